@@ -1,0 +1,351 @@
+"""CPU fp64 oracle for the AWQ per-layer scale search and its W4A16 contraction.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no code
+with the HIP library (no kernels, headers, helpers or constants); the two agree
+only through the arithmetic contract written out below.
+
+Pages (cited by title / address and section; nothing here is quoted):
+
+  [P1] "AWQ (Activation-aware Weight Quantization)", builderai.tools/tool/awq
+  [P3] "AWQ", robotsatlas.com/ai-technologies/awq
+  [P4] AWQ project page, sourcepulse.org/projects/1842286
+  [P5] "What is AWQ?", aquanode.io/gpu-glossary/awq
+
+What the pages fix: a calibration pass measures how large the activations are
+at each linear layer's input ([P3] "How it works", "Key mechanisms",
+"Components"); each input channel gets a factor that multiplies the weight and
+divides the activation, which leaves the product unchanged ([P3] "How it works",
+"Components" / per-channel scaling; [P5] "The core idea"); the factor is picked
+by a grid search that minimises the layer's output error ([P3] "How it works",
+"Key mechanisms"); then weights are quantized group-wise (groups of 128) to 4 or
+3 bits with a per-group scale ([P3] "Components" / group-wise 4-bit
+quantization, "Hyperparameters"; [P4] opening paragraph) and written as real
+packed INT4 ([P1] "About").
+
+Where the pages are silent the following readings are used (each one is also a
+contract the GPU library implements):
+
+  statistic        a[k] = mean over tokens of |x[m,k]|
+  grid             alpha_i = i / n_grid, i = 0..n_grid-1  (includes 0, excludes 1)
+  candidate        r = max(a^alpha, 1e-4);  s = r / sqrt(max_k r * min_k r)
+  quantizer        asymmetric, per (row, group of `group` input channels):
+                   range extended to include 0; step = range / qmax
+                   (1.0 when that is zero); zero z = rint(-min/step);
+                   q = clamp(rint(ws/step) + z, 0, qmax); rint = half-to-even
+  packing          qweight[n][t] = sum_i q[n, 8t+i] << 4i  (u32, sequential
+                   nibbles along K; 3-bit codes use the same 4-bit containers)
+                   scales f32 [N][K/group], zeros u8 [N][K/group]
+  dequantized B    B[n,k] = bf16( f32( f32((q - z) * step) * inv_s[k] ) )
+                   (1/s folded into the weight operand; the activation operand
+                   is the caller's bf16 X, unchanged)
+  loss             MSE over all M*N outputs of X.B^T against X.W^T, fp64
+  selection        first index of the minimum loss (NaN never wins; all-NaN
+                   gives -1)
+
+Every "f32(...)" marks one IEEE fp32 operation of the contract.  The oracle
+evaluates the exact operation in fp64 and rounds the result to fp32; for +, -,
+x and / this equals the correctly rounded fp32 result because 53 >= 2*24 + 2
+(double rounding is innocuous; S. Figueroa, "When is double rounding
+innocuous?", 1995).  Products of two fp32 values are exact in fp64.
+
+Parity unpinned (convention only, no value on the pages can fix them): the
+normalising constant sqrt(max*min), the 1e-4 floor, the nibble order of the
+packed layout and the 4-bit container used for INT3 codes.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Floor applied after the power in the candidate scale (a reading: guards dead
+# channels, whose 0^alpha would make 1/s infinite).
+SCALE_FLOOR = 1e-4
+
+
+# --------------------------------------------------------------------------
+# Number formats.  bf16 is the top 16 bits of an IEEE binary32.
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f32(x) -> np.ndarray:
+    """Round float64 values to the nearest binary32 (ties to even); back as float64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def bf16_rne_bits(x) -> np.ndarray:
+    """Round values that are already binary32 to bf16, nearest with ties to even.
+
+    Written out as the definition: the two bf16 neighbours of x are the value
+    with the low 16 bits cleared (towards zero) and the next one away from
+    zero; the closer one wins and an exact tie goes to the one whose last
+    kept mantissa bit is 0.  NaN maps to a quiet NaN.
+    """
+    v = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = v.view(np.uint32)
+    lo = u & np.uint32(0xFFFF0000)                     # towards zero
+    hi = lo + np.uint32(0x10000)                       # away from zero
+    vlo = lo.view(np.float32).astype(np.float64)
+    vhi = hi.view(np.float32).astype(np.float64)
+    # Past the largest finite bf16 the upper neighbour is 2^128 in an unbounded
+    # exponent range (IEEE 754 overflow rule); it is stored as infinity.
+    vhi = np.where(np.isinf(vhi), np.copysign(2.0 ** 128, vhi), vhi)
+    vx = v.astype(np.float64)
+    dlo = np.abs(vx - vlo)
+    with np.errstate(invalid="ignore"):
+        dhi = np.abs(vhi - vx)
+    lo_even = ((lo >> np.uint32(16)) & np.uint32(1)) == 0
+    take_lo = (dlo < dhi) | ((dlo == dhi) & lo_even)
+    out = np.where(take_lo, lo, hi)
+    exact = (u & np.uint32(0xFFFF)) == 0
+    out = np.where(exact, u, out)
+    nan = np.isnan(v)
+    out = np.where(nan, (u | np.uint32(0x00400000)) & np.uint32(0xFFFF0000), out)
+    return (out >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_round(x) -> np.ndarray:
+    """Value after RNE rounding of binary32 values to bf16, as float64."""
+    return bf16_bits_to_f64(bf16_rne_bits(x))
+
+
+# --------------------------------------------------------------------------
+# Step 1: activation statistics.
+# [P3] "How it works" and "Components" / activation saliency analysis: the
+# calibration set is run through the model and activation magnitudes are
+# measured at each linear layer's input.  Reading: mean |x| per input channel.
+# --------------------------------------------------------------------------
+
+def act_stats(x_bits, chunk_rows: int = 8192):
+    """Per-input-channel mean |x| over all M calibration tokens.
+
+    x_bits: uint16 bf16 patterns [M][K].  Returns (a64, a32): the fp64 mean and
+    that mean rounded to fp32 (the value the scale step consumes).
+    """
+    x_bits = np.asarray(x_bits)
+    M, K = x_bits.shape
+    total = np.zeros(K, dtype=np.float64)
+    for r0 in range(0, M, chunk_rows):
+        total += np.abs(bf16_bits_to_f64(x_bits[r0:r0 + chunk_rows])).sum(axis=0)
+    a64 = total / M
+    return a64, f32(a64)
+
+
+# --------------------------------------------------------------------------
+# Step 2: candidate per-channel scales.
+# [P3] "How it works": a factor per input channel, weight multiplied and
+# activation divided by it; the factor comes from the activation statistic.
+# Reading: s = a^alpha on an n_grid-point grid in [0, 1), floored, normalised.
+# --------------------------------------------------------------------------
+
+def alpha_grid(n_grid: int) -> np.ndarray:
+    return np.arange(n_grid, dtype=np.float64) / float(n_grid)
+
+
+def candidate_scales(a32, n_grid: int):
+    """(s32, inv32), each [n_grid][K]: s rounded to fp32 and fp32(1 / s32)."""
+    a32 = np.asarray(a32, dtype=np.float64)
+    K = a32.shape[0]
+    s32 = np.empty((n_grid, K), dtype=np.float64)
+    inv32 = np.empty((n_grid, K), dtype=np.float64)
+    for i, alpha in enumerate(alpha_grid(n_grid)):
+        r = np.maximum(np.power(a32, alpha), SCALE_FLOOR)   # 0^0 = 1
+        s = r / np.sqrt(r.max() * r.min())
+        s32[i] = f32(s)
+        inv32[i] = f32(1.0 / s32[i])
+    return s32, inv32
+
+
+# --------------------------------------------------------------------------
+# Step 3: group-wise asymmetric quantization of W.diag(s).
+# [P3] "How it works" (quantized group-wise after the scales are set),
+# "Components" (groups of 128, per-group scale), "Hyperparameters" (4 or 3
+# bits, group 128).  Reading: asymmetric, with a per-group integer zero.
+# --------------------------------------------------------------------------
+
+def quantize(w, s32, bits: int, group: int):
+    """Quantize ws = f32(W * s) group-wise along K.
+
+    w: bf16 bit patterns (uint16) or float64 values [N][K]; s32: [K] or None
+    (None means s = 1).  Returns (q int64 [N][K], z int64 [N][K/group],
+    step float64 [N][K/group] holding fp32 values).
+    """
+    W = bf16_bits_to_f64(w) if np.asarray(w).dtype == np.uint16 else np.asarray(w, np.float64)
+    N, K = W.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    qmax = float((1 << bits) - 1)
+    ws = f32(W * (1.0 if s32 is None else np.asarray(s32, np.float64)[None, :]))
+    G = ws.reshape(N, K // group, group)
+    mx = np.maximum(G.max(axis=2), 0.0)
+    mn = np.minimum(G.min(axis=2), 0.0)
+    rng = f32(mx - mn)
+    step = f32(rng / qmax)
+    step = np.where(step > 0.0, step, 1.0)
+    z = np.clip(np.rint(f32(-mn / step)), 0.0, qmax)
+    q = np.clip(np.rint(f32(G / step[:, :, None])) + z[:, :, None], 0.0, qmax)
+    return q.reshape(N, K).astype(np.int64), z.astype(np.int64), step
+
+
+# --------------------------------------------------------------------------
+# Step 3b: packing ("writes real INT4 weights", [P1] "About").
+# --------------------------------------------------------------------------
+
+def pack(q, z, step):
+    """(qweight u32 [N][K/8], scales f32 [N][K/g], zeros u8 [N][K/g])."""
+    q = np.asarray(q, dtype=np.uint64)
+    N, K = q.shape
+    words = np.zeros((N, K // 8), dtype=np.uint64)
+    for i in range(8):
+        words |= q[:, i::8] << np.uint64(4 * i)
+    return (words.astype(np.uint32), np.asarray(step, np.float64).astype(np.float32),
+            np.asarray(z).astype(np.uint8))
+
+
+def unpack(qweight):
+    """Codes [N][K] from packed words (inverse of pack's nibble order)."""
+    w = np.asarray(qweight, dtype=np.uint32)
+    N, T = w.shape
+    q = np.empty((N, T * 8), dtype=np.int64)
+    for i in range(8):
+        q[:, i::8] = (w >> np.uint32(4 * i)) & np.uint32(0xF)
+    return q
+
+
+def packed_bytes(N: int, K: int, group: int) -> int:
+    """Storage of the packed form: 4-bit codes + fp32 scale + u8 zero per group."""
+    return N * K // 2 + N * (K // group) * (4 + 1)
+
+
+# --------------------------------------------------------------------------
+# Step 4: the weight operand of the contraction and the per-candidate loss.
+# [P3] "How it works" / "Key mechanisms": the scale is chosen by a grid search
+# that minimises the layer's output error.  The activation divided by s is the
+# same product as the weight multiplied by 1/s ([P3] "Components" / per-channel
+# scaling), so 1/s is applied to the dequantized weight.
+# --------------------------------------------------------------------------
+
+def dequant_operand(q, z, step, group: int, inv32=None) -> np.ndarray:
+    """B[n,k] = bf16(f32(f32((q - z) * step) * inv_s[k])) as float64 values.
+
+    With inv32 None the last multiply is skipped (deployment form, s folded
+    upstream): B = bf16(f32((q - z) * step)).
+    """
+    q = np.asarray(q, np.float64)
+    zz = np.repeat(np.asarray(z, np.float64), group, axis=1)
+    st = np.repeat(np.asarray(step, np.float64), group, axis=1)
+    d = f32((q - zz) * st)
+    if inv32 is not None:
+        d = f32(d * np.asarray(inv32, np.float64)[None, :])
+    return bf16_round(d)
+
+
+def gemm(x_bits, b_values) -> np.ndarray:
+    """Y = X . B^T in fp64 (X given as bf16 patterns, B as float64 values)."""
+    return bf16_bits_to_f64(x_bits) @ np.asarray(b_values, np.float64).T
+
+
+def output_mse(x_bits, w_bits, b_values, chunk_rows: int = 4096) -> float:
+    """mean over m, n of (X.B^T - X.W^T)^2, evaluated as ||X (B - W)^T||^2 / (M N).
+
+    X.B^T - X.W^T = X.(B - W)^T by distributivity; B - W is exact in fp64
+    because both are bf16 values.
+    """
+    x_bits = np.asarray(x_bits)
+    M = x_bits.shape[0]
+    D = np.asarray(b_values, np.float64) - bf16_bits_to_f64(w_bits)
+    N = D.shape[0]
+    sse = 0.0
+    for r0 in range(0, M, chunk_rows):
+        E = bf16_bits_to_f64(x_bits[r0:r0 + chunk_rows]) @ D.T
+        sse += float(np.einsum("ij,ij->", E, E))
+    return sse / (M * N)
+
+
+def gram(x_bits, chunk_rows: int = 8192) -> np.ndarray:
+    """G = X^T X in fp64."""
+    x_bits = np.asarray(x_bits)
+    M, K = x_bits.shape
+    G = np.zeros((K, K), dtype=np.float64)
+    for r0 in range(0, M, chunk_rows):
+        Xc = bf16_bits_to_f64(x_bits[r0:r0 + chunk_rows])
+        G += Xc.T @ Xc
+    return G
+
+
+def output_mse_gram(G, M: int, w_bits, b_values) -> float:
+    """Same MSE from the Gram matrix: sum_n D_n G D_n^T / (M N), D = B - W."""
+    D = np.asarray(b_values, np.float64) - bf16_bits_to_f64(w_bits)
+    N = D.shape[0]
+    return float(np.einsum("nk,nk->", D @ G, D)) / (M * N)
+
+
+def first_argmin(losses) -> int:
+    """First index of the smallest loss; NaN never wins; -1 if all are NaN."""
+    losses = np.asarray(losses, np.float64)
+    best, best_v = -1, None
+    for i, v in enumerate(losses):
+        if np.isnan(v):
+            continue
+        if best_v is None or v < best_v:
+            best, best_v = i, v
+    return best
+
+
+# --------------------------------------------------------------------------
+# The whole per-layer search.
+# --------------------------------------------------------------------------
+
+def search(x_bits, w_bits, bits: int = 4, group: int = 128, n_grid: int = 20,
+           loss_form: str = "direct", timings: dict | None = None):
+    """AWQ per-layer scale search.  Returns a dict with every intermediate.
+
+    loss_form "direct" evaluates each loss over the tokens; "gram" forms
+    G = X^T X once and evaluates sum_n D_n G D_n^T (same value).
+    """
+    import time
+    t0 = time.perf_counter()
+    x_bits = np.asarray(x_bits)
+    w_bits = np.asarray(w_bits)
+    M = x_bits.shape[0]
+    a64, a32 = act_stats(x_bits)
+    s32, inv32 = candidate_scales(a32, n_grid)
+    t1 = time.perf_counter()
+    G = gram(x_bits) if loss_form == "gram" else None
+    losses = np.empty(n_grid, dtype=np.float64)
+    t_quant = 0.0
+    for i in range(n_grid):
+        tq = time.perf_counter()
+        q, z, step = quantize(w_bits, s32[i], bits, group)
+        B = dequant_operand(q, z, step, group, inv32[i])
+        t_quant += time.perf_counter() - tq
+        if G is None:
+            losses[i] = output_mse(x_bits, w_bits, B)
+        else:
+            losses[i] = output_mse_gram(G, M, w_bits, B)
+    t2 = time.perf_counter()
+    best = first_argmin(losses)
+    sel = best if best >= 0 else 0
+    q, z, step = quantize(w_bits, s32[sel], bits, group)
+    qweight, scales, zeros = pack(q, z, step)
+    t3 = time.perf_counter()
+    if timings is not None:
+        timings.update(stats_and_scales=t1 - t0, quantize=t_quant,
+                       loss=(t2 - t1) - t_quant, final_pack=t3 - t2)
+    return dict(mean_abs64=a64, mean_abs=a32, s=s32, inv_s=inv32, alphas=alpha_grid(n_grid),
+                losses=losses, best_idx=best, best_s=s32[sel].copy(),
+                q=q, z=z, step=step, qweight=qweight, scales=scales, zeros=zeros)
+
+
+def deploy_gemm(a_bits, qweight, scales, zeros, group: int, inv32=None) -> np.ndarray:
+    """Y = A . B^T with B dequantized from packed codes ([P4] "Highlighted
+    Details": 4-bit linear layers; [P1] "About": W4A16 kernels)."""
+    q = unpack(qweight)
+    B = dequant_operand(q, np.asarray(zeros, np.int64), np.asarray(scales, np.float64),
+                        group, inv32)
+    return gemm(a_bits, B)

@@ -1,0 +1,103 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that the pins
+in test_oracle_pins catch every one of them."""
+
+import numpy as np
+import pytest
+
+import oracle.awq_oracle as OA
+import test_oracle_pins as P
+
+
+class _NumpyWith:
+    """numpy, except for the attributes overridden."""
+
+    def __init__(self, **over):
+        self._over = over
+
+    def __getattr__(self, name):
+        return self._over.get(name, getattr(np, name))
+
+
+def _mut_floor_instead_of_rint(mp):
+    mp.setattr(OA, "np", _NumpyWith(rint=np.floor))
+
+
+def _mut_drop_inv_s(mp):
+    orig = OA.dequant_operand
+    mp.setattr(OA, "dequant_operand", lambda q, z, st, g, inv32=None: orig(q, z, st, g, None))
+
+
+def _mut_alpha_grid_closed(mp):
+    mp.setattr(OA, "alpha_grid", lambda n: np.arange(n, dtype=np.float64) / max(n - 1, 1))
+
+
+def _mut_scale_index_reversed(mp):
+    orig = OA.quantize
+    mp.setattr(OA, "quantize", lambda w, s, b, g: orig(w, None if s is None else np.asarray(s)[::-1], b, g))
+
+
+def _mut_zero_added_before_rounding(mp):
+    def q2(w, s32, bits, group):
+        q, z, step = orig(w, s32, bits, group)
+        W = OA.bf16_bits_to_f64(w) if np.asarray(w).dtype == np.uint16 else w
+        ws = OA.f32(W * (1.0 if s32 is None else np.asarray(s32)[None, :]))
+        N, K = ws.shape
+        qmax = (1 << bits) - 1
+        G = ws.reshape(N, K // group, group)
+        qq = np.clip(np.floor(OA.f32(G / step[:, :, None]) + z[:, :, None] + 0.5), 0, qmax)
+        return qq.reshape(N, K).astype(np.int64), z, step
+    orig = OA.quantize
+    mp.setattr(OA, "quantize", q2)
+
+
+def _mut_loss_sign(mp):
+    def mse(x_bits, w_bits, b_values, chunk_rows=4096):
+        X = OA.bf16_bits_to_f64(x_bits)
+        D = np.asarray(b_values) + OA.bf16_bits_to_f64(w_bits)
+        E = X @ D.T
+        return float((E * E).sum()) / E.size
+    mp.setattr(OA, "output_mse", mse)
+
+
+def _mut_no_range_extension(mp):
+    mp.setattr(OA, "np", _NumpyWith(maximum=lambda a, b, *r: a if np.isscalar(b) else np.maximum(a, b, *r),
+                                    minimum=lambda a, b, *r: a if np.isscalar(b) else np.minimum(a, b, *r)))
+
+
+def _mut_stats_mean_without_abs(mp):
+    mp.setattr(OA, "np", _NumpyWith(abs=lambda a: a))
+
+
+def _mut_normaliser_max_only(mp):
+    orig_sqrt = np.sqrt
+    mp.setattr(OA, "np", _NumpyWith(sqrt=lambda v: orig_sqrt(v) * 1.5))
+
+
+MUTATIONS = [_mut_floor_instead_of_rint, _mut_drop_inv_s, _mut_alpha_grid_closed,
+             _mut_scale_index_reversed, _mut_zero_added_before_rounding, _mut_loss_sign,
+             _mut_no_range_extension, _mut_stats_mean_without_abs, _mut_normaliser_max_only]
+
+PINS = [
+    P.test_quantizer_worked_group,
+    P.test_quantizer_special_groups,
+    P.test_stats_closed_form_constant_columns,
+    P.test_alpha_grid_and_alpha0_is_identity,
+    P.test_candidates_closed_form,
+    P.test_candidates_floor_on_dead_channel,
+    lambda: P.test_alpha0_loss_is_plain_rtn(4),
+    lambda: P.test_whole_search_brute_force_tiny(24, 8, 128, 4, 20),
+    lambda: P.test_whole_search_brute_force_tiny(16, 6, 256, 3, 21),
+]
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__[5:])
+def test_pins_catch_planted_mistake(mutation, monkeypatch):
+    # The unmutated oracle passes every pin here.
+    mutation(monkeypatch)
+    caught = 0
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            caught += 1
+    assert caught >= 1, f"no pin caught {mutation.__name__}"

@@ -1,0 +1,446 @@
+"""Pins for the CPU oracle: closed forms, invariants, special cases, library
+routines and brute force, each independent of the oracle's own code.
+
+Citations are to the pages by address and section:
+  builderai.tools AWQ page ("About"), robotsatlas.com AWQ page ("How it works",
+  "Key mechanisms", "Components", "Hyperparameters", "Computational
+  complexity", "Benchmark notes"), vectordb.ever.works AWQ page ("Features",
+  "Comparison"), aquanode.io "What is AWQ?" ("The core idea").
+"""
+
+import json
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bits_of(values):
+    """bf16 patterns of values that are exactly representable in bf16."""
+    v = np.asarray(values, dtype=np.float32)
+    u = v.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exactly bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------- pure Python
+
+def py_f32(x: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def py_bf16(x: float) -> float:
+    """RNE to bf16 by integer arithmetic on the fp32 pattern (not the oracle's method)."""
+    u = struct.unpack("<I", struct.pack("<f", x))[0]
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return struct.unpack("<f", struct.pack("<I", (u << 16) & 0xFFFFFFFF))[0]
+
+
+def py_rint(x: float) -> float:
+    f = math.floor(x)
+    d = x - f
+    if d > 0.5 or (d == 0.5 and f % 2 == 1):
+        f += 1
+    return float(f)
+
+
+def py_search(X, W, bits, group, n_grid):
+    """The whole search in pure Python loops on lists of floats (tiny sizes)."""
+    M, K, N = len(X), len(X[0]), len(W)
+    qmax = (1 << bits) - 1
+    a = [py_f32(sum(abs(X[m][k]) for m in range(M)) / M) for k in range(K)]
+    losses, S = [], []
+    for i in range(n_grid):
+        alpha = i / n_grid
+        r = [max(a[k] ** alpha, 1e-4) for k in range(K)]
+        c = math.sqrt(max(r) * min(r))
+        s = [py_f32(r[k] / c) for k in range(K)]
+        inv = [py_f32(1.0 / s[k]) for k in range(K)]
+        S.append(s)
+        B = [[0.0] * K for _ in range(N)]
+        for n in range(N):
+            for g0 in range(0, K, group):
+                ws = [py_f32(W[n][k] * s[k]) for k in range(g0, g0 + group)]
+                mx, mn = max(max(ws), 0.0), min(min(ws), 0.0)
+                step = py_f32(py_f32(mx - mn) / qmax)
+                if step == 0.0:
+                    step = 1.0
+                z = min(max(py_rint(py_f32(-mn / step)), 0.0), qmax)
+                for j, k in enumerate(range(g0, g0 + group)):
+                    q = min(max(py_rint(py_f32(ws[j] / step)) + z, 0.0), qmax)
+                    B[n][k] = py_bf16(py_f32(py_f32((q - z) * step) * inv[k]))
+        sse = 0.0
+        for m in range(M):
+            for n in range(N):
+                yq = math.fsum(X[m][k] * B[n][k] for k in range(K))
+                y = math.fsum(X[m][k] * W[n][k] for k in range(K))
+                sse += (yq - y) ** 2
+        losses.append(sse / (M * N))
+    best = min(range(n_grid), key=lambda i: (losses[i], i))
+    return a, S, losses, best
+
+
+# ------------------------------------------------------------ number formats
+
+def test_bf16_rounding_matches_torch_cast():
+    """Library-routine pin: the oracle's bf16 RNE equals torch's CPU cast."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1)
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    edge = (hi[:, None] | lows[None, :]).ravel()
+    rand = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    u = np.concatenate([edge, rand])
+    x = u.view(np.float32)
+    finite = np.isfinite(x)
+    got = O.bf16_rne_bits(x[finite])
+    ref = torch.from_numpy(x[finite].copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+    # NaN stays NaN
+    assert np.isnan(O.bf16_round(np.array([np.nan], np.float32)))[0]
+
+
+def test_bf16_rounding_matches_integer_rne():
+    """Second method: integer RNE on the fp32 pattern, pure Python."""
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal(3000) * 10.0 ** rng.integers(-6, 6, 3000)).astype(np.float32)
+    got = O.bf16_round(x)
+    ref = np.array([py_bf16(float(v)) for v in x])
+    assert np.array_equal(got, ref)
+
+
+def test_f32_ops_match_numpy_float32():
+    """Library-routine pin: fp64-evaluate-then-round equals numpy's fp32 ops."""
+    rng = np.random.default_rng(3)
+    a = (rng.standard_normal(200000) * 10.0 ** rng.integers(-8, 8, 200000)).astype(np.float32)
+    b = (rng.standard_normal(200000) * 10.0 ** rng.integers(-8, 8, 200000)).astype(np.float32)
+    b[b == 0] = 1.0
+    A, B = a.astype(np.float64), b.astype(np.float64)
+    assert np.array_equal(O.f32(A / B), (a / b).astype(np.float64))
+    assert np.array_equal(O.f32(A * B), (a * b).astype(np.float64))
+    assert np.array_equal(O.f32(A - B), (a - b).astype(np.float64))
+
+
+# ------------------------------------------------------------- stats (step 1)
+
+def test_stats_closed_form_constant_columns():
+    """Constant column c gives mean |x| = |c|; +-c alternation too."""
+    cols = np.array([0.5, -3.0, 0.0, 1.25, -0.0078125, 96.0, 2.0, -2.0], np.float32)
+    M = 64
+    X = np.tile(cols, (M, 1))
+    X[1::2, 6] *= -1  # alternating signs
+    a64, a32 = O.act_stats(bits_of(X))
+    assert np.array_equal(a32, np.abs(cols).astype(np.float64))
+
+
+def test_stats_row_permutation_and_power_of_two_scaling():
+    x, _ = synth.random_layer(96, 256, 8, seed=4, n_outlier=3)
+    _, a = O.act_stats(x)
+    perm = np.random.default_rng(5).permutation(96)
+    _, ap = O.act_stats(x[perm])
+    assert np.array_equal(a, ap)
+    x4 = bits_of(synth.bf16_bits_to_f32(x) * np.float32(4.0))
+    _, a4 = O.act_stats(x4)
+    assert np.array_equal(a4, 4.0 * a)
+
+
+def test_stats_brute_force():
+    x, _ = synth.random_layer(17, 128, 8, seed=6)
+    X = synth.bf16_bits_to_f32(x).astype(np.float64)
+    ref = [py_f32(math.fsum(abs(X[m, k]) for m in range(17)) / 17) for k in range(128)]
+    assert np.array_equal(O.act_stats(x)[1], np.array(ref))
+
+
+# ------------------------------------------------------ candidates (step 2)
+
+def test_alpha_grid_and_alpha0_is_identity():
+    """alpha = i/20 over [0,1): includes 0 (plain rounding), excludes 1."""
+    g = O.alpha_grid(20)
+    assert g[0] == 0.0 and g[-1] == 0.95 and len(g) == 20
+    a = np.array([0.3, 2.0, 7.5, 0.0], dtype=np.float64)
+    s, inv = O.candidate_scales(a, 20)
+    assert np.all(s[0] == 1.0) and np.all(inv[0] == 1.0)
+
+
+def test_candidates_closed_form():
+    """a = [1, 4], alpha = 1/2: r = [1, 2], s = r / sqrt(2)."""
+    s, inv = O.candidate_scales(np.array([1.0, 4.0]), 2)
+    assert s[1, 0] == py_f32(1.0 / math.sqrt(2.0))
+    assert s[1, 1] == py_f32(2.0 / math.sqrt(2.0))
+    assert inv[1, 1] == py_f32(1.0 / s[1, 1])
+
+
+def test_candidates_floor_on_dead_channel():
+    s, inv = O.candidate_scales(np.array([0.0, 1.0, 100.0]), 4)
+    # alpha = 0.5: r = [1e-4, 1, 10]; normaliser sqrt(10 * 1e-4) = 0.1
+    assert s[2, 0] == py_f32(1e-4 / math.sqrt(10.0 * 1e-4))
+    assert s[2, 2] == py_f32(10.0 / math.sqrt(10.0 * 1e-4))
+    assert np.all(np.isfinite(inv))
+
+
+def test_candidates_invariant_under_activation_scaling():
+    """X -> 2^p X leaves s unchanged: the normaliser removes 2^(p alpha)."""
+    rng = np.random.default_rng(7)
+    a = O.f32(np.abs(rng.standard_normal(4096)) + 0.05)
+    s1, _ = O.candidate_scales(a, 20)
+    s2, _ = O.candidate_scales(a * 8.0, 20)
+    rel = np.abs(s1 - s2) / s1
+    assert rel.max() <= 2.0 ** -23
+    assert np.mean(s1 == s2) > 0.999
+
+
+def test_candidates_normalised_and_monotone():
+    rng = np.random.default_rng(8)
+    a = O.f32(np.abs(rng.standard_normal(512)) + 0.01)
+    s, _ = O.candidate_scales(a, 20)
+    for i in range(1, 20):
+        assert abs(s[i].max() * s[i].min() - 1.0) < 1e-6
+        order = np.argsort(a, kind="stable")
+        assert np.all(np.diff(s[i][order]) >= 0)
+
+
+# ------------------------------------------------------ quantizer (step 3)
+
+def test_quantizer_worked_group():
+    with open(os.path.join(GOLDEN, "quant_group_worked.json")) as f:
+        g = json.load(f)
+    vals = np.full(g["group"], g["tail_value"], np.float32)
+    vals[:len(g["values_head"])] = g["values_head"]
+    q, z, step = O.quantize(bits_of(vals[None, :]), None, g["bits"], g["group"])
+    assert step[0, 0] == g["expected_step"]
+    assert z[0, 0] == g["expected_zero"]
+    assert list(q[0, :8]) == g["expected_codes_head"]
+    assert np.all(q[0, 8:] == g["expected_code_tail"])
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_quantizer_codes_range_and_half_step_bound(bits):
+    """Codes in [0, qmax]; |ws - (q - z) step| <= step/2 (plus one fp32 rounding)."""
+    x, w = synth.random_layer(64, 512, 48, seed=9, n_outlier=5)
+    _, a = O.act_stats(x)
+    s, _ = O.candidate_scales(a, 20)
+    qmax = (1 << bits) - 1
+    W = O.bf16_bits_to_f64(w)
+    for i in (0, 7, 19):
+        q, z, step = O.quantize(w, s[i], bits, 128)
+        assert q.min() >= 0 and q.max() <= qmax and z.min() >= 0 and z.max() <= qmax
+        ws = O.f32(W * s[i][None, :])
+        st = np.repeat(step, 128, axis=1)
+        err = np.abs(ws - (q - np.repeat(z, 128, axis=1)) * st)
+        assert np.all(err <= st / 2 * (1 + 2.0 ** -20))
+
+
+def test_quantizer_brute_force_nearest_grid_point():
+    """Each code is the nearest of the qmax+1 levels to ws/step + z (ties: even rint)."""
+    x, w = synth.random_layer(32, 256, 12, seed=10, n_outlier=2)
+    s = O.candidate_scales(O.act_stats(x)[1], 20)[0][13]
+    for bits in (3, 4):
+        qmax = (1 << bits) - 1
+        q, z, step = O.quantize(w, s, bits, 128)
+        W = synth.bf16_bits_to_f32(w).astype(np.float64)
+        for n in range(12):
+            for g in range(2):
+                ws = [py_f32(W[n, k] * s[k]) for k in range(128 * g, 128 * g + 128)]
+                st, zz = step[n, g], z[n, g]
+                for j, v in enumerate(ws):
+                    t = py_f32(v / st)
+                    best = min(range(qmax + 1),
+                               key=lambda c: (abs(t - (c - zz)), (c - zz) % 2))
+                    assert q[n, 128 * g + j] == best
+
+
+def test_quantizer_special_groups():
+    """All-zero group: step 1, codes = zero = 0.  All-positive group: zero 0."""
+    vals = np.zeros((2, 128), np.float32)
+    vals[1] = np.linspace(0.5, 3.0, 128, dtype=np.float32)
+    vals[1] = synth.bf16_bits_to_f32(synth.to_bf16_bits(vals[1]))
+    q, z, step = O.quantize(synth.to_bf16_bits(vals), None, 4, 128)
+    assert step[0, 0] == 1.0 and z[0, 0] == 0 and np.all(q[0] == 0)
+    # all-positive: the range runs from 0 to the max, so step = max / 15
+    assert z[1, 0] == 0 and q[1].max() == 15
+    assert step[1, 0] == py_f32(float(vals[1].max()) / 15.0)
+    assert np.all(np.abs(vals[1] - q[1] * step[1, 0]) <= step[1, 0] / 2)
+
+
+def test_quantizer_power_of_two_weight_scaling():
+    _, w = synth.random_layer(8, 256, 16, seed=11)
+    q1, z1, st1 = O.quantize(w, None, 4, 128)
+    w2 = bits_of(synth.bf16_bits_to_f32(w) * np.float32(0.25))
+    q2, z2, st2 = O.quantize(w2, None, 4, 128)
+    assert np.array_equal(q1, q2) and np.array_equal(z1, z2)
+    assert np.array_equal(st2, st1 * 0.25)
+
+
+def test_quantizer_group_min_maps_to_zero_code():
+    _, w = synth.random_layer(8, 256, 16, seed=12)
+    q, z, _ = O.quantize(w, None, 4, 128)
+    W = synth.bf16_bits_to_f32(w).reshape(16, 2, 128)
+    qq = q.reshape(16, 2, 128)
+    idx = W.argmin(axis=2)
+    assert np.all(np.take_along_axis(qq, idx[:, :, None], 2) == 0)
+
+
+# ---------------------------------------------------------------- packing
+
+def test_pack_worked_and_roundtrip():
+    with open(os.path.join(GOLDEN, "pack_worked.json")) as f:
+        g = json.load(f)
+    q = np.array([g["codes"]], np.int64)
+    words, _, _ = O.pack(q, np.zeros((1, 1), np.int64), np.ones((1, 1)))
+    assert [hex(int(v)) for v in words[0]] == g["expected_words_hex"]
+    rng = np.random.default_rng(13)
+    q = rng.integers(0, 16, size=(7, 256))
+    assert np.array_equal(O.unpack(O.pack(q, np.zeros((7, 2)), np.ones((7, 2)))[0]), q)
+
+
+def test_storage_about_four_times_smaller():
+    """~4x smaller than 16-bit and ~4.x bits per weight (vectordb 'Features',
+    robotsatlas 'Computational complexity')."""
+    N, K = 12288, 4096
+    nbytes = O.packed_bytes(N, K, 128)
+    ratio = 2 * N * K / nbytes
+    bits_per_weight = 8 * nbytes / (N * K)
+    assert 3.5 < ratio < 4.0 and ratio == pytest.approx(3.7101, abs=1e-3)
+    assert 4.0 < bits_per_weight < 5.0 and bits_per_weight == 4.3125
+
+
+# ------------------------------------------------------------- loss (step 4)
+
+def test_scaling_preserves_product_before_rounding():
+    """(W diag(s)) (X diag(1/s))^T = W X^T exactly in real arithmetic
+    (robotsatlas 'How it works' / 'Components')."""
+    x, w = synth.random_layer(64, 256, 32, seed=14, n_outlier=3)
+    X, W = O.bf16_bits_to_f64(x), O.bf16_bits_to_f64(w)
+    s = O.candidate_scales(O.act_stats(x)[1], 20)[0][11]
+    Y = X @ W.T
+    Ys = (X / s[None, :]) @ (W * s[None, :]).T
+    assert np.max(np.abs(Ys - Y)) <= 1e-12 * np.max(np.abs(Y))
+
+
+def test_loss_two_forms_and_literal_difference():
+    x, w = synth.random_layer(200, 384, 40, seed=15, n_outlier=4)
+    s, inv = O.candidate_scales(O.act_stats(x)[1], 20)
+    G = O.gram(x)
+    for i in (0, 9, 19):
+        q, z, st = O.quantize(w, s[i], 4, 128)
+        B = O.dequant_operand(q, z, st, 128, inv[i])
+        direct = O.output_mse(x, w, B)
+        g = O.output_mse_gram(G, 200, w, B)
+        literal = np.mean((O.gemm(x, B) - O.gemm(x, O.bf16_bits_to_f64(w))) ** 2)
+        assert g == pytest.approx(direct, rel=1e-10)
+        assert literal == pytest.approx(direct, rel=1e-9)
+
+
+def rtn_mse(x_bits, w_bits, bits, group):
+    """Plain round-to-nearest, written separately: no scale, per-group asymmetric
+    min/max quantization in fp32 (numpy float32 arithmetic)."""
+    W = synth.bf16_bits_to_f32(w_bits)
+    X = synth.bf16_bits_to_f32(x_bits).astype(np.float64)
+    qmax = np.float32((1 << bits) - 1)
+    N, K = W.shape
+    Bq = np.empty_like(W)
+    for n in range(N):
+        for g0 in range(0, K, group):
+            v = W[n, g0:g0 + group]
+            hi = max(v.max(), np.float32(0))
+            lo = min(v.min(), np.float32(0))
+            step = np.float32(hi - lo) / qmax
+            if step == 0:
+                step = np.float32(1)
+            zero = np.clip(np.rint(-lo / step), 0, qmax)
+            code = np.clip(np.rint(v / step) + zero, 0, qmax)
+            Bq[n, g0:g0 + group] = np.float32(code - zero) * step
+    Bq = synth.bf16_bits_to_f32(synth.to_bf16_bits(Bq)).astype(np.float64)
+    return float(np.mean((X @ Bq.T - X @ W.astype(np.float64).T) ** 2))
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_alpha0_loss_is_plain_rtn(bits):
+    x, w = synth.random_layer(128, 256, 24, seed=16, n_outlier=3)
+    res = O.search(x, w, bits=bits, group=128, n_grid=20)
+    assert res["losses"][0] == pytest.approx(rtn_mse(x, w, bits, 128), rel=1e-12)
+    assert res["losses"].min() <= res["losses"][0]   # never worse than RTN
+
+
+def test_grid_exact_weights_have_zero_rtn_loss():
+    """Weights already on each group's 16-level grid quantize exactly at alpha 0."""
+    rng = np.random.default_rng(17)
+    N, K = 16, 256
+    codes = rng.integers(0, 16, size=(N, K))
+    codes[:, 0::128] = 0
+    codes[:, 1::128] = 15
+    W = ((codes - 5) * 2.0 ** -6).astype(np.float32)
+    x, _ = synth.random_layer(64, K, 4, seed=18, n_outlier=2)
+    res = O.search(x, bits_of(W), 4, 128, 20)
+    assert res["losses"][0] == 0.0 and res["best_idx"] == 0
+    assert np.array_equal(res["q"], codes)
+
+
+def test_losses_scale_by_four_to_the_p():
+    x, w = synth.random_layer(96, 256, 16, seed=19, n_outlier=3)
+    r1 = O.search(x, w, 4, 128, 20)
+    x2 = bits_of(synth.bf16_bits_to_f32(x) * np.float32(2.0))
+    r2 = O.search(x2, w, 4, 128, 20)
+    w2 = bits_of(synth.bf16_bits_to_f32(w) * np.float32(0.5))
+    r3 = O.search(x, w2, 4, 128, 20)
+    assert r2["best_idx"] == r1["best_idx"] == r3["best_idx"]
+    assert np.allclose(r2["losses"], 4.0 * r1["losses"], rtol=1e-6, atol=0)
+    assert np.array_equal(r3["losses"], r1["losses"] / 4.0)
+
+
+@pytest.mark.parametrize("M,N,K,bits,seed", [(24, 8, 128, 4, 20), (16, 6, 256, 3, 21),
+                                             (40, 4, 128, 4, 22)])
+def test_whole_search_brute_force_tiny(M, N, K, bits, seed):
+    """Every step recomputed in pure Python loops on a tiny layer."""
+    x, w = synth.random_layer(M, K, N, seed=seed, n_outlier=2, outlier_factor=15.0)
+    n_grid = 10
+    res = O.search(x, w, bits, 128, n_grid)
+    X = synth.bf16_bits_to_f32(x).astype(np.float64).tolist()
+    W = synth.bf16_bits_to_f32(w).astype(np.float64).tolist()
+    a, S, losses, best = py_search(X, W, bits, 128, n_grid)
+    assert np.array_equal(res["mean_abs"], np.array(a))
+    assert np.array_equal(res["s"], np.array(S))
+    assert np.allclose(res["losses"], losses, rtol=1e-12, atol=0)
+    assert res["best_idx"] == best
+
+
+def test_outlier_channels_get_the_largest_scales():
+    """~1% salient channels (builderai 'About', aquanode 'The core idea'): on the
+    outlier recipe the search picks alpha > 0 and s peaks on the outliers."""
+    x, w, spec = synth.make_layer("single_linear_512")
+    res = O.search(x, w, 4, 128, 20)
+    cols, _ = synth.outlier_columns(spec)
+    assert res["best_idx"] > 0
+    top = np.argsort(res["best_s"])[-len(cols):]
+    assert set(top) == set(cols)
+    assert res["losses"][res["best_idx"]] < 0.9 * res["losses"][0]
+
+
+def test_first_argmin_ties_and_nan():
+    assert O.first_argmin([3.0, 1.0, 1.0, 2.0]) == 1
+    assert O.first_argmin([np.nan, 2.0, np.nan, 1.5]) == 3
+    assert O.first_argmin([np.nan, np.nan]) == -1
+
+
+# ------------------------------------------------------------ deploy GEMM
+
+def test_deploy_gemm_exact_sums():
+    x, w = synth.random_layer(5, 256, 7, seed=23)
+    q, z, st = O.quantize(w, None, 4, 128)
+    qw, sc, ze = O.pack(q, z, st)
+    Y = O.deploy_gemm(x, qw, sc, ze, 128)
+    X = synth.bf16_bits_to_f32(x).astype(np.float64)
+    for m in range(5):
+        for n in range(7):
+            terms = []
+            for k in range(256):
+                d = py_bf16(py_f32((q[n, k] - z[n, k // 128]) * float(st[n, k // 128])))
+                terms.append(X[m, k] * d)
+            assert Y[m, n] == pytest.approx(math.fsum(terms), rel=1e-13, abs=1e-300)
