@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Throughput of the AWQ per-layer scale search on one MI355X.
+
+One step = one whole search over one layer (activation statistics, 20
+candidate scales, the fp32 reference product, 20 x (quantize + W4A16 GEMM
+with fused squared error), loss reduction, argmin, final quantize + pack)
+with the inputs already resident in HBM.  Default workload: a Llama-2-7B
+shaped fused QKV layer, 65536 calibration tokens, K=4096 -> N=12288, INT4,
+group 128, 20 grid points, seeded synthetic data.
+
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
+the stream the kernels are launched on; the roofline block uses the W4A16
+GEMM (the dominant kernel).  cpu_baseline times the CPU oracle on a bounded
+sample of the same layer and scales it to the full layer.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "AWQ search: layers/s + W4A16 GEMM TFLOP/s (% MFMA peak), quant GB/s (% HBM)"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def event_time_ms(fn, reps: int, stream) -> float:
+    """Average duration of fn() over reps launches, HIP events on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def cpu_baseline(x_bits, w_bits, spec, m_sample: int, n_sample: int) -> dict:
+    """Oracle (numpy fp64) on a token prefix x output-row prefix; each phase is
+    scaled to the full layer by the dimension it is linear in."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    xs = np.ascontiguousarray(x_bits[:m_sample])
+    ws = np.ascontiguousarray(w_bits[:n_sample])
+    t = {}
+    t0 = time.perf_counter()
+    O.search(xs, ws, spec.bits[-1], spec.group, spec.n_grid, loss_form="direct", timings=t)
+    wall = time.perf_counter() - t0
+    M, N = spec.M, spec.N
+    full = (t["stats_and_scales"] * (M / m_sample) + t["quantize"] * (N / n_sample) +
+            t["loss"] * (M / m_sample) * (N / n_sample) + t["final_pack"] * (N / n_sample))
+    return {"value": 1.0 / full, "unit": "layers/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"full {spec.n_grid}-point search on the first {m_sample} tokens x first "
+                       f"{n_sample} output rows (K={spec.K}) in {wall:.1f} s; phases scaled to "
+                       f"M={M}, N={N} (stats by M, quantize by N, loss by M*N)"),
+            "seconds_sample": wall, "seconds_full_layer_est": full}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama2_7b_qkv")
+    ap.add_argument("--layer", default=None)
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-m", type=int, default=1024)
+    ap.add_argument("--cpu-n", type=int, default=1024)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import post_weight_quantization_stats_amd as awq
+    import synth
+
+    dev = torch.device("cuda:0")
+    spec = synth.layer_spec(args.workload, args.layer)
+    bits = spec.bits[-1]
+    M, K, N, G = spec.M, spec.K, spec.N, spec.n_grid
+    log(f"workload {spec.workload}/{spec.name}: M={M} K={K} N={N} bits={bits} grid={G}")
+    t0 = time.perf_counter()
+    x_bits, w_bits, _ = synth.make_layer(spec.workload, spec.name)
+    log(f"synthetic inputs in {time.perf_counter() - t0:.1f} s")
+    xd = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    wd = torch.from_numpy(w_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    ws_bytes = awq.workspace_size(awq.OP_SEARCH_SCALE, M, N, K, bits, spec.group, G)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    log(f"warmup {args.warmup}")
+    out = None
+    for _ in range(args.warmup):
+        out = awq.search_scale(xd, wd, bits, spec.group, G, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        out = awq.search_scale(xd, wd, bits, spec.group, G, workspace=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    log(f"search: {ms_per_step:.2f} ms/layer; alpha*={int(out['best_idx'].item()) / G:.2f}")
+
+    # ---- per-kernel durations (HIP events on the launch stream) ----
+    reps = args.kernel_reps
+    mean_abs = awq.act_stats(xd)
+    s_all, inv_all = awq.candidate_scales(mean_abs, G)
+    i_mid = G // 2
+    qw, sc, ze = awq.quantize_pack(wd, s_all[i_mid], bits, spec.group)
+    yref = awq.reference_gemm(xd, wd)
+    gemm_ws = torch.empty(max(awq.workspace_size(awq.OP_W4A16_GEMM, M, N, K), 256),
+                          dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    t_gemm = event_time_ms(lambda: awq.w4a16_gemm(xd, qw, sc, ze, bits, spec.group,
+                                                  inv_s=inv_all[i_mid], y_ref=yref,
+                                                  return_y=False, workspace=gemm_ws), reps, stream)
+    t_ref = event_time_ms(lambda: awq.reference_gemm(xd, wd), max(2, reps // 2), stream)
+    t_stats = event_time_ms(lambda: awq.act_stats(xd), reps, stream)
+    t_quant = event_time_ms(lambda: awq.quantize_pack(wd, s_all[i_mid], bits, spec.group),
+                            reps * 5, stream)
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (t_gemm * 1e-3) / 1e12
+    ref_tflops = flops / (t_ref * 1e-3) / 1e12
+    stats_bytes = 2.0 * M * K + 4.0 * K
+    quant_bytes = 2.0 * N * K + 4.0 * K + N * K / 2 + 5.0 * N * K / spec.group
+    stats_gbs = stats_bytes / (t_stats * 1e-3) / 1e9
+    quant_gbs = quant_bytes / (t_quant * 1e-3) / 1e9
+    log(f"w4a16 gemm {t_gemm:.3f} ms = {gemm_tflops:.1f} TFLOP/s; reference gemm {t_ref:.3f} ms "
+        f"= {ref_tflops:.1f} TFLOP/s; stats {t_stats * 1e3:.1f} us = {stats_gbs:.0f} GB/s; "
+        f"quantize {t_quant * 1e3:.1f} us = {quant_gbs:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": 1e3 / ms_per_step,
+        "unit": "layers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.workload}/{spec.name}", "M": M, "K": K, "N": N,
+                   "bits": bits, "group": spec.group, "n_grid": G},
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None, "kernel": "w4a16 gemm + fused squared error",
+                     "flops_per_launch": flops, "ms_per_launch": t_gemm},
+        "kernels": {
+            "w4a16_gemm_sse": {"ms": t_gemm, "tflops": gemm_tflops,
+                               "frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS},
+            "reference_gemm": {"ms": t_ref, "tflops": ref_tflops,
+                               "frac_mfma_peak": ref_tflops / PEAK_BF16_TFLOPS},
+            "act_stats": {"us": t_stats * 1e3, "gbs": stats_gbs,
+                          "frac_hbm_peak": stats_gbs / PEAK_HBM_GBS},
+            "quantize_pack": {"us": t_quant * 1e3, "gbs": quant_gbs,
+                              "frac_hbm_peak": quant_gbs / PEAK_HBM_GBS},
+        },
+        "cpu_baseline": None,
+    }
+    del ws, gemm_ws, yref
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_m} tokens x {args.cpu_n} rows")
+        result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, spec, args.cpu_m, args.cpu_n)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,198 @@
+/*
+ * awq_mi355x.h -- C ABI of the AWQ per-layer scale search on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * AWQ (activation-aware weight quantization) picks, for each linear layer, a
+ * per-input-channel scale s from calibration activation statistics, multiplies
+ * the weight by s and divides the activation by it (the product is unchanged),
+ * chooses s by a grid search that minimises the layer's output error, then
+ * quantizes the scaled weight group-wise to 4 (or 3) bits and writes the
+ * packed integers.  Sources, by page and section:
+ *   robotsatlas.com AWQ page: "How it works", "Key mechanisms", "Components",
+ *     "Hyperparameters", "Computational complexity";
+ *   builderai.tools AWQ page: "About" (real INT4 weights, W4A16 kernels);
+ *   aquanode.io "What is AWQ?": "The core idea".
+ *
+ * Conventions for every call
+ *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense,
+ *     row-major, contiguous.  X is [M][K] (tokens x input channels), W is
+ *     [N][K] (output channels x input channels, so Y = X . W^T).
+ *   - Every pointer except `stream` is a DEVICE pointer.  `stream` is a
+ *     hipStream_t passed as void* (NULL = the default stream).
+ *   - The caller owns all memory: inputs, outputs and the workspace.  The
+ *     library never allocates, frees or synchronises.  A call validates its
+ *     arguments on the host, enqueues kernels on `stream` and returns; outputs
+ *     are valid once the stream has completed; inputs must stay unchanged
+ *     until then.  Calls on different streams that share an output race.
+ *   - On any validation error nothing is enqueued and no HIP call is made.
+ *   - Pointers to bf16/f32/u32 tensors with more than one element must be
+ *     16-byte aligned (AWQ_ERR_ALIGN otherwise).
+ *   - group must be 128 and bits 3 or 4 (AWQ_ERR_UNSUPPORTED otherwise); K must
+ *     be a positive multiple of group (AWQ_ERR_SHAPE).
+ *   - Inputs must be finite; NaN/Inf in X or W give unspecified codes and
+ *     non-finite losses (the search then never selects a NaN loss).
+ *   - No C++ exception crosses this boundary.  awq_last_error() returns a
+ *     thread-local message for the last failing call on this thread.
+ *
+ * Packed weight format (the "real INT4 weights")
+ *   qweight u32 [N][K/8]: code of (n, k) in word k/8 at bits 4*(k%8);
+ *                         3-bit codes use the same 4-bit containers.
+ *   scales  f32 [N][K/group]: quantization step of each group.
+ *   zeros   u8  [N][K/group]: integer zero point of each group.
+ *   Dequantized weight: (code - zero) * step.
+ */
+#ifndef AWQ_MI355X_H
+#define AWQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AWQ_ABI_VERSION 1
+
+typedef enum awq_status {
+  AWQ_OK = 0,
+  AWQ_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  AWQ_ERR_SHAPE = 2,        /* a size is out of range or inconsistent              */
+  AWQ_ERR_UNSUPPORTED = 3,  /* bits, group or n_grid outside the supported set     */
+  AWQ_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned             */
+  AWQ_ERR_WORKSPACE = 5,    /* workspace missing or smaller than awq_workspace_size */
+  AWQ_ERR_LAUNCH = 6,       /* the HIP runtime reported an error (see awq_last_error) */
+} awq_status;
+
+typedef enum awq_op {
+  AWQ_OP_ACT_STATS = 0,
+  AWQ_OP_W4A16_GEMM = 1,
+  AWQ_OP_SEARCH_SCALE = 2,
+  AWQ_OP_CANDIDATE_SCALES = 3,
+} awq_op;
+
+/* Version of this ABI (AWQ_ABI_VERSION). */
+int32_t awq_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* awq_status_string(int32_t status);
+
+/* Message for the last failing call on the calling thread ("" if none). */
+const char* awq_last_error(void);
+
+/*
+ * Bytes of device workspace a call needs (0 means ws may be NULL).
+ *   op AWQ_OP_ACT_STATS:    uses M, K.
+ *   op AWQ_OP_W4A16_GEMM:   uses M, N, K (needed only when sse is requested).
+ *   op AWQ_OP_SEARCH_SCALE: uses M, N, K, bits, group, n_grid.
+ *   op AWQ_OP_CANDIDATE_SCALES: uses K, n_grid.
+ * Errors: AWQ_ERR_NULL (bytes NULL), AWQ_ERR_SHAPE, AWQ_ERR_UNSUPPORTED.
+ */
+awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t bits,
+                              int32_t group, int32_t n_grid, size_t* bytes);
+
+/*
+ * Activation statistics (robotsatlas "How it works", "Components" / activation
+ * saliency analysis: activation magnitudes measured at the layer input over a
+ * calibration set).  Statistic: mean_abs[k] = (1/M) sum_m |x[m,k]|, summed in
+ * fp64 in a fixed order, returned rounded to fp32.
+ *   x        bf16 [M][K]  calibration activations (M >= 1, K % 8 == 0)
+ *   mean_abs f32  [K]     output
+ *   ws       device workspace of awq_workspace_size(AWQ_OP_ACT_STATS) bytes
+ */
+awq_status awq_act_stats(const uint16_t* x, int64_t M, int64_t K, float* mean_abs, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * Candidate scales of the grid search (robotsatlas "How it works": a scaling
+ * factor per input channel derived from the activation statistic; "Key
+ * mechanisms": grid search over scales).  For i = 0..n_grid-1, alpha = i/n_grid:
+ *   r[k] = max(mean_abs[k]^alpha, 1e-4)        (fp64; 0^0 = 1)
+ *   s[i][k] = fp32(r[k] / sqrt(max_k r * min_k r))
+ *   inv_s[i][k] = fp32(1 / s[i][k])
+ *   mean_abs f32 [K] (non-negative); s, inv_s f32 [n_grid][K] outputs.
+ *   1 <= n_grid <= 64.  ws: awq_workspace_size(AWQ_OP_CANDIDATE_SCALES) bytes.
+ */
+awq_status awq_candidate_scales(const float* mean_abs, int64_t K, int32_t n_grid, float* s,
+                                float* inv_s, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Group-wise asymmetric quantization and packing of W . diag(s) (robotsatlas
+ * "How it works": weights quantized group-wise after the scales are set;
+ * "Components": groups of 128 with a per-group scale; "Hyperparameters": 4 or
+ * 3 bits; builderai "About": real INT4 weights are written).  Per row n and
+ * group j (input channels j*group .. j*group+group-1), each step one IEEE
+ * fp32 operation:
+ *   ws   = w[n,k] * s[k]                     (s NULL means s = 1)
+ *   mx   = max(max ws, 0);  mn = min(min ws, 0)
+ *   step = (mx - mn) / qmax, replaced by 1 when it is 0   (qmax = 2^bits - 1)
+ *   z    = clamp(rint(-mn / step), 0, qmax)
+ *   q    = clamp(rint(ws / step) + z, 0, qmax)     (rint: ties to even)
+ *   w     bf16 [N][K];  s f32 [K] or NULL
+ *   qweight u32 [N][K/8], scales f32 [N][K/group], zeros u8 [N][K/group]
+ * N == 0 is a no-op (pointers are then ignored).
+ */
+awq_status awq_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const float* s, int32_t bits,
+                             int32_t group, uint32_t* qweight, float* scales, uint8_t* zeros,
+                             void* stream);
+
+/*
+ * Dense reference product Y = X . W^T (robotsatlas "How it works": the output
+ * error is measured against the layer's unquantized output).  bf16 operands,
+ * fp32 accumulation on the matrix cores, fp32 output.
+ *   x bf16 [M][K], w bf16 [N][K], y f32 [M][N].  M == 0 or N == 0 is a no-op
+ *   (pointers are then ignored).
+ */
+awq_status awq_reference_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                              const uint16_t* w, float* y, void* stream);
+
+/*
+ * W4A16 contraction with the packed weights (builderai "About": kernels for
+ * 4-bit weights with 16-bit activations; robotsatlas "Implementation
+ * pitfalls": dequantization stays inside the kernel).  The weight operand is
+ *   B[n,k] = bf16( fp32( fp32((q - z) * step) * inv_s[k] ) )
+ * (inv_s NULL: B = bf16(fp32((q - z) * step))), dequantized on chip and never
+ * written to memory; Y = X . B^T with bf16 inputs and fp32 accumulation.
+ *   x       bf16 [M][K];  qweight/scales/zeros as from awq_quantize_pack
+ *   inv_s   f32 [K] or NULL
+ *   y       f32 [M][N] output, or NULL
+ *   y_ref   f32 [M][N] or NULL;  sse f64 [1] or NULL.  If sse is given, y_ref
+ *           is required and sse = sum over m,n of (Y[m,n] - y_ref[m,n])^2,
+ *           reduced in fp64 in a fixed order (bit-reproducible).
+ *   ws      workspace of awq_workspace_size(AWQ_OP_W4A16_GEMM) bytes when sse
+ *           is requested, else may be NULL.
+ * At least one of y and sse must be non-NULL.  When M or N is 0 every pointer
+ * but sse is ignored and sse (if given) is set to 0.
+ */
+awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                          const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                          int32_t bits, int32_t group, const float* inv_s, const float* y_ref,
+                          float* y, double* sse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole per-layer search (robotsatlas "How it works", "Key mechanisms";
+ * "Computational complexity": cost grows with layers x grid points x
+ * calibration tokens).  Steps, all on `stream` with no host synchronisation:
+ *   1. mean_abs = awq_act_stats(x)
+ *   2. s, inv_s = awq_candidate_scales(mean_abs, n_grid)
+ *   3. y_ref = X . W^T (fp32, kept in the workspace)
+ *   4. for each candidate i: quantize W . diag(s_i), then
+ *      loss[i] = sum (X . B_i^T - y_ref)^2 / (M N)   (fp64, fixed order)
+ *   5. best = first index of the smallest loss (NaN never wins; -1 if every
+ *      loss is NaN, in which case candidate 0 is written below)
+ *   6. best_s = s[best]; qweight/scales/zeros = quantize_pack(w, best_s)
+ *   x bf16 [M][K] (M >= 1), w bf16 [N][K] (N >= 1)
+ *   mean_abs f32 [K], losses f64 [n_grid], best_idx i32 [1], best_s f32 [K],
+ *   qweight u32 [N][K/8], scales f32 [N][K/group], zeros u8 [N][K/group]
+ *   ws: awq_workspace_size(AWQ_OP_SEARCH_SCALE) bytes (it holds y_ref, 4*M*N).
+ */
+awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
+                            int32_t bits, int32_t group, int32_t n_grid, float* mean_abs,
+                            double* losses, int32_t* best_idx, float* best_s, uint32_t* qweight,
+                            float* scales, uint8_t* zeros, void* ws, size_t ws_bytes,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_MI355X_H */

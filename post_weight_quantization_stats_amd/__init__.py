@@ -1,0 +1,225 @@
+"""AWQ per-layer scale search on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over libawq_mi355x.so (C ABI in include/awq_mi355x.h).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensors, allocates outputs with torch on the tensors' device and
+passes raw device pointers plus the current HIP stream.  There is no CPU
+fallback: if the library cannot be loaded the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+__all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "quantize_pack",
+           "reference_gemm", "w4a16_gemm", "search_scale", "workspace_size",
+           "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES"]
+
+OP_ACT_STATS, OP_W4A16_GEMM, OP_SEARCH_SCALE, OP_CANDIDATE_SCALES = 0, 1, 2, 3
+
+_c_void_p, _i64, _i32, _size_t = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+
+# name -> argtypes (restype is int32 status unless noted)
+_SIGNATURES = {
+    "awq_abi_version": ([], _i32),
+    "awq_status_string": ([_i32], ctypes.c_char_p),
+    "awq_last_error": ([], ctypes.c_char_p),
+    "awq_workspace_size": ([_i32, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.POINTER(_size_t)], _i32),
+    "awq_act_stats": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
+    "awq_candidate_scales": ([_c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _size_t,
+                              _c_void_p], _i32),
+    "awq_quantize_pack": ([_c_void_p, _i64, _i64, _c_void_p, _i32, _i32, _c_void_p, _c_void_p,
+                           _c_void_p, _c_void_p], _i32),
+    "awq_reference_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p], _i32),
+    "awq_w4a16_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
+                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
+                        _c_void_p], _i32),
+    "awq_search_scale": ([_c_void_p, _i64, _i64, _c_void_p, _i64, _i32, _i32, _i32, _c_void_p,
+                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                          _c_void_p, _size_t, _c_void_p], _i32),
+}
+
+_LIB = None
+
+
+class AwqError(RuntimeError):
+    def __init__(self, status: int, func: str, message: str):
+        self.status = status
+        super().__init__(f"{func}: {lib().awq_status_string(status).decode()} ({message})")
+
+
+def library_path() -> str:
+    return _build.LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (building it first only if no build exists)."""
+    global _LIB
+    if _LIB is None:
+        path = _build.LIB_PATH
+        if not os.path.exists(path):
+            _build.build()
+        handle = ctypes.CDLL(path)
+        for name, (argtypes, restype) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = argtypes
+            fn.restype = restype
+        _LIB = handle
+    return _LIB
+
+
+def _check(status: int, func: str) -> None:
+    if status != 0:
+        raise AwqError(status, func, lib().awq_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _bf16(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 values (got {t.dtype})")
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D tensor")
+    return t
+
+
+def _f32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous float32 GPU tensor")
+    return t
+
+
+def workspace_size(op: int, M: int = 0, N: int = 0, K: int = 0, bits: int = 4, group: int = 128,
+                   n_grid: int = 20) -> int:
+    out = _size_t(0)
+    _check(lib().awq_workspace_size(op, M, N, K, bits, group, n_grid, ctypes.byref(out)),
+           "awq_workspace_size")
+    return int(out.value)
+
+
+def _workspace(nbytes: int, device, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def act_stats(x: torch.Tensor) -> torch.Tensor:
+    """mean |x| per input channel, float32 [K]."""
+    x = _bf16(x, "x")
+    M, K = x.shape
+    out = torch.empty(K, dtype=torch.float32, device=x.device)
+    ws = _workspace(workspace_size(OP_ACT_STATS, M, 0, K), x.device)
+    _check(lib().awq_act_stats(_ptr(x), M, K, _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)),
+           "awq_act_stats")
+    return out
+
+
+def candidate_scales(mean_abs: torch.Tensor, n_grid: int = 20):
+    """(s, inv_s), each float32 [n_grid][K]."""
+    mean_abs = _f32(mean_abs, "mean_abs")
+    K = mean_abs.numel()
+    s = torch.empty((n_grid, K), dtype=torch.float32, device=mean_abs.device)
+    inv = torch.empty_like(s)
+    ws = _workspace(workspace_size(OP_CANDIDATE_SCALES, 0, 0, K, n_grid=n_grid), mean_abs.device)
+    _check(lib().awq_candidate_scales(_ptr(mean_abs), K, n_grid, _ptr(s), _ptr(inv), _ptr(ws),
+                                      ws.numel(), _stream(mean_abs.device)), "awq_candidate_scales")
+    return s, inv
+
+
+def quantize_pack(w: torch.Tensor, s: torch.Tensor | None = None, bits: int = 4, group: int = 128):
+    """(qweight int32 [N][K/8] holding u32 words, scales float32 [N][K/g], zeros uint8 [N][K/g])."""
+    w = _bf16(w, "w")
+    N, K = w.shape
+    if s is not None:
+        s = _f32(s, "s")
+        if s.numel() != K:
+            raise ValueError("s must have K elements")
+    dev = w.device
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    scales = torch.empty((N, K // group), dtype=torch.float32, device=dev)
+    zeros = torch.empty((N, K // group), dtype=torch.uint8, device=dev)
+    _check(lib().awq_quantize_pack(_ptr(w), N, K, _ptr(s), bits, group, _ptr(qweight), _ptr(scales),
+                                   _ptr(zeros), _stream(dev)), "awq_quantize_pack")
+    return qweight, scales, zeros
+
+
+def reference_gemm(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """Y = X . W^T in fp32 [M][N] (bf16 operands, fp32 accumulation)."""
+    x, w = _bf16(x, "x"), _bf16(w, "w")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("x and w disagree on K")
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(lib().awq_reference_gemm(_ptr(x), M, N, K, _ptr(w), _ptr(y), _stream(x.device)),
+           "awq_reference_gemm")
+    return y
+
+
+def w4a16_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+               bits: int = 4, group: int = 128, inv_s: torch.Tensor | None = None,
+               y_ref: torch.Tensor | None = None, return_y: bool = True,
+               workspace: torch.Tensor | None = None):
+    """Y = X . dequant(Q)^T (fp32).  With y_ref also returns sse = sum (Y - y_ref)^2
+    as a float64 [1] device tensor: returns (y or None, sse)."""
+    x = _bf16(x, "x")
+    M, K = x.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 8 != K:
+        raise ValueError("qweight must be [N][K/8]")
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if return_y else None
+    sse = None
+    ws = None
+    if y_ref is not None:
+        y_ref = _f32(y_ref, "y_ref")
+        sse = torch.empty(1, dtype=torch.float64, device=dev)
+        ws = _workspace(workspace_size(OP_W4A16_GEMM, M, N, K), dev, workspace)
+    if inv_s is not None:
+        inv_s = _f32(inv_s, "inv_s")
+    _check(lib().awq_w4a16_gemm(_ptr(x), M, N, K, _ptr(qweight), _ptr(scales), _ptr(zeros), bits,
+                                group, _ptr(inv_s), _ptr(y_ref), _ptr(y), _ptr(sse), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(dev)), "awq_w4a16_gemm")
+    if y_ref is None:
+        return y
+    return y, sse
+
+
+def search_scale(x: torch.Tensor, w: torch.Tensor, bits: int = 4, group: int = 128,
+                 n_grid: int = 20, workspace: torch.Tensor | None = None) -> dict:
+    """The whole per-layer AWQ search; every output stays on the GPU."""
+    x, w = _bf16(x, "x"), _bf16(w, "w")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("x and w disagree on K")
+    dev = x.device
+    out = dict(
+        mean_abs=torch.empty(K, dtype=torch.float32, device=dev),
+        losses=torch.empty(n_grid, dtype=torch.float64, device=dev),
+        best_idx=torch.empty(1, dtype=torch.int32, device=dev),
+        best_s=torch.empty(K, dtype=torch.float32, device=dev),
+        qweight=torch.empty((N, K // 8), dtype=torch.int32, device=dev),
+        scales=torch.empty((N, K // group), dtype=torch.float32, device=dev),
+        zeros=torch.empty((N, K // group), dtype=torch.uint8, device=dev),
+    )
+    ws = _workspace(workspace_size(OP_SEARCH_SCALE, M, N, K, bits, group, n_grid), dev, workspace)
+    _check(lib().awq_search_scale(_ptr(x), M, K, _ptr(w), N, bits, group, n_grid,
+                                  _ptr(out["mean_abs"]), _ptr(out["losses"]), _ptr(out["best_idx"]),
+                                  _ptr(out["best_s"]), _ptr(out["qweight"]), _ptr(out["scales"]),
+                                  _ptr(out["zeros"]), _ptr(ws), ws.numel(), _stream(dev)),
+           "awq_search_scale")
+    return out

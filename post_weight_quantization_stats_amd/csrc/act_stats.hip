@@ -1,0 +1,102 @@
+// Activation statistics: mean |x| per input channel over the calibration
+// tokens (robotsatlas AWQ page, "How it works" and "Components" / activation
+// saliency analysis).
+//
+// HBM-bound column reduction of X bf16 [M][K].  Each wave streams 1 KiB
+// contiguous row segments (64 lanes x 16 B); lanes accumulate |x| of their 8
+// columns in fp64 (the partial sums of bf16 magnitudes stay exact in
+// practice), the four waves of a block are combined in a fixed order, and a
+// second kernel adds the per-block partials in row-block order.
+#include "awq_internal.h"
+#include "device_common.h"
+
+namespace awq {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kColsPerBlock = 512;  // 64 lanes x 8 bf16
+
+__device__ __forceinline__ void acc_abs8(double (&acc)[8], uint4 v) {
+  acc[0] += (double)fabsf(bf16_lo(v.x));
+  acc[1] += (double)fabsf(bf16_hi(v.x));
+  acc[2] += (double)fabsf(bf16_lo(v.y));
+  acc[3] += (double)fabsf(bf16_hi(v.y));
+  acc[4] += (double)fabsf(bf16_lo(v.z));
+  acc[5] += (double)fabsf(bf16_hi(v.z));
+  acc[6] += (double)fabsf(bf16_lo(v.w));
+  acc[7] += (double)fabsf(bf16_hi(v.w));
+}
+
+__global__ __launch_bounds__(kThreads) void act_stats_partial_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t rows_per_block,
+    double* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t col0 = (int64_t)blockIdx.x * kColsPerBlock + lane * 8;
+  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_block;
+  const int64_t r_end = min(M, r_begin + rows_per_block);
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (col0 < K) {
+    const uint16_t* p = x + col0;
+    int64_t r = r_begin + wave;
+    // four rows in flight per lane
+    for (; r + 12 < r_end; r += 16) {
+      const uint4 v0 = load_stream16((p + r * K));
+      const uint4 v1 = load_stream16((p + (r + 4) * K));
+      const uint4 v2 = load_stream16((p + (r + 8) * K));
+      const uint4 v3 = load_stream16((p + (r + 12) * K));
+      acc_abs8(acc, v0);
+      acc_abs8(acc, v1);
+      acc_abs8(acc, v2);
+      acc_abs8(acc, v3);
+    }
+    for (; r < r_end; r += 4) acc_abs8(acc, *(const uint4*)(p + r * K));
+  }
+  __shared__ double red[4][kColsPerBlock];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[wave][lane * 8 + j] = acc[j];
+  __syncthreads();
+  for (int c = threadIdx.x; c < kColsPerBlock; c += kThreads) {
+    const int64_t col = (int64_t)blockIdx.x * kColsPerBlock + c;
+    if (col < K)
+      partial[(int64_t)blockIdx.y * K + col] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void act_stats_finalize_kernel(
+    const double* __restrict__ partial, int64_t R, int64_t K, int64_t M, float* __restrict__ out) {
+  const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (k >= K) return;
+  double s = 0.0;
+  for (int64_t r = 0; r < R; ++r) s += partial[r * K + k];
+  out[k] = (float)(s / (double)M);
+}
+
+}  // namespace
+
+StatsPlan stats_plan(int64_t M) {
+  // At least 256 rows per block; at most 1024 row blocks.
+  int64_t R = ceil_div(M, 256);
+  if (R > 1024) R = 1024;
+  if (R < 1) R = 1;
+  int64_t rpb = ceil_div(M, R);
+  rpb = ceil_div(rpb, 4) * 4;
+  R = ceil_div(M, rpb);
+  if (R < 1) R = 1;
+  return StatsPlan{rpb, R};
+}
+
+hipError_t launch_act_stats(const uint16_t* x, int64_t M, int64_t K, float* mean_abs,
+                            double* partial, hipStream_t stream) {
+  const StatsPlan plan = stats_plan(M);
+  dim3 grid((unsigned)ceil_div(K, kColsPerBlock), (unsigned)plan.row_blocks);
+  act_stats_partial_kernel<<<grid, kThreads, 0, stream>>>(x, M, K, plan.rows_per_block, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  act_stats_finalize_kernel<<<(unsigned)ceil_div(K, kThreads), kThreads, 0, stream>>>(
+      partial, plan.row_blocks, K, M, mean_abs);
+  return hipGetLastError();
+}
+
+}  // namespace awq

@@ -1,0 +1,348 @@
+// Host side of libawq_mi355x: argument validation, workspace layout and the
+// launch sequence of each C-ABI entry point (declared in awq_mi355x.h).
+// Validation happens before any HIP call; kernels are enqueued on the
+// caller's stream and nothing here synchronises or allocates device memory.
+#include "awq_mi355x.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "awq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+awq_status fail(awq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+awq_status ok() {
+  g_last_error.clear();
+  return AWQ_OK;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+#define AWQ_TRY_LAUNCH(expr)                                                          \
+  do {                                                                                \
+    hipError_t e_ = (expr);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(AWQ_ERR_LAUNCH, "%s: %s", #expr, hipGetErrorString(e_));            \
+  } while (0)
+
+awq_status check_quant_params(int32_t bits, int32_t group) {
+  if (bits != 3 && bits != 4) return fail(AWQ_ERR_UNSUPPORTED, "bits must be 3 or 4 (got %d)", bits);
+  if (group != awq::kGroup)
+    return fail(AWQ_ERR_UNSUPPORTED, "group must be %d (got %d)", awq::kGroup, group);
+  return AWQ_OK;
+}
+
+awq_status check_k(int64_t K, int32_t group) {
+  if (K <= 0 || K % group != 0)
+    return fail(AWQ_ERR_SHAPE, "K must be a positive multiple of the group size (K=%lld)", (long long)K);
+  if (K > (int64_t(1) << 30)) return fail(AWQ_ERR_SHAPE, "K too large (%lld)", (long long)K);
+  return AWQ_OK;
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+// ---- workspace layouts ----
+struct SearchLayout {
+  size_t yref, s, inv, scales_ws, stats_ws, qtmp, sctmp, ztmp, partials, total;
+};
+
+SearchLayout search_layout(int64_t M, int64_t N, int64_t K, int n_grid) {
+  using awq::align_up;
+  SearchLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  L.yref = take((size_t)M * N * sizeof(float));
+  L.s = take((size_t)n_grid * K * sizeof(float));
+  L.inv = take((size_t)n_grid * K * sizeof(float));
+  L.scales_ws = take(awq::scales_ws_bytes(K, n_grid));
+  L.stats_ws = take(awq::stats_ws_bytes(M, K));
+  L.qtmp = take((size_t)N * (K / 8) * sizeof(uint32_t));
+  L.sctmp = take((size_t)N * (K / awq::kGroup) * sizeof(float));
+  L.ztmp = take((size_t)N * (K / awq::kGroup));
+  L.partials = take((size_t)n_grid * awq::gemm_tiles(M, N) * sizeof(double));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t awq_abi_version(void) { return AWQ_ABI_VERSION; }
+
+const char* awq_status_string(int32_t status) {
+  switch (status) {
+    case AWQ_OK: return "AWQ_OK";
+    case AWQ_ERR_NULL: return "AWQ_ERR_NULL";
+    case AWQ_ERR_SHAPE: return "AWQ_ERR_SHAPE";
+    case AWQ_ERR_UNSUPPORTED: return "AWQ_ERR_UNSUPPORTED";
+    case AWQ_ERR_ALIGN: return "AWQ_ERR_ALIGN";
+    case AWQ_ERR_WORKSPACE: return "AWQ_ERR_WORKSPACE";
+    case AWQ_ERR_LAUNCH: return "AWQ_ERR_LAUNCH";
+    default: return "AWQ_ERR_UNKNOWN";
+  }
+}
+
+const char* awq_last_error(void) { return g_last_error.c_str(); }
+
+awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t bits,
+                              int32_t group, int32_t n_grid, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return fail(AWQ_ERR_NULL, "bytes is NULL");
+    *bytes = 0;
+    switch (op) {
+      case AWQ_OP_ACT_STATS:
+        if (M <= 0 || K <= 0 || K % 8 != 0 || M >= kMaxDim || K >= kMaxDim)
+          return fail(AWQ_ERR_SHAPE, "act_stats needs M >= 1 and K a positive multiple of 8");
+        *bytes = awq::stats_ws_bytes(M, K);
+        return ok();
+      case AWQ_OP_W4A16_GEMM:
+        if (M < 0 || N < 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim)
+          return fail(AWQ_ERR_SHAPE, "bad GEMM shape");
+        *bytes = awq::align_up((size_t)awq::gemm_tiles(M, N) * sizeof(double));
+        return ok();
+      case AWQ_OP_SEARCH_SCALE: {
+        awq_status st = check_quant_params(bits, group);
+        if (st != AWQ_OK) return st;
+        if ((st = check_k(K, group)) != AWQ_OK) return st;
+        if (M <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim)
+          return fail(AWQ_ERR_SHAPE, "search needs M >= 1 and N >= 1");
+        if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_UNSUPPORTED, "n_grid must be in [1, 64]");
+        *bytes = search_layout(M, N, K, n_grid).total;
+        return ok();
+      }
+      case AWQ_OP_CANDIDATE_SCALES:
+        if (K <= 0 || K >= kMaxDim) return fail(AWQ_ERR_SHAPE, "K must be positive");
+        if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_UNSUPPORTED, "n_grid must be in [1, 64]");
+        *bytes = awq::scales_ws_bytes(K, n_grid);
+        return ok();
+      default:
+        return fail(AWQ_ERR_UNSUPPORTED, "unknown op %d", op);
+    }
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_act_stats(const uint16_t* x, int64_t M, int64_t K, float* mean_abs, void* ws,
+                         size_t ws_bytes, void* stream) {
+  try {
+    if (x == nullptr || mean_abs == nullptr) return fail(AWQ_ERR_NULL, "x and mean_abs are required");
+    if (M <= 0 || K <= 0 || K % 8 != 0 || M >= kMaxDim || K >= kMaxDim)
+      return fail(AWQ_ERR_SHAPE, "act_stats needs M >= 1 and K a positive multiple of 8");
+    if (misaligned(x) || misaligned(mean_abs) || misaligned(ws))
+      return fail(AWQ_ERR_ALIGN, "x, mean_abs and ws must be 16-byte aligned");
+    if (ws == nullptr || ws_bytes < awq::stats_ws_bytes(M, K))
+      return fail(AWQ_ERR_WORKSPACE, "act_stats needs %zu workspace bytes", awq::stats_ws_bytes(M, K));
+    AWQ_TRY_LAUNCH(awq::launch_act_stats(x, M, K, mean_abs, (double*)ws, (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_candidate_scales(const float* mean_abs, int64_t K, int32_t n_grid, float* s,
+                                float* inv_s, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (mean_abs == nullptr || s == nullptr || inv_s == nullptr)
+      return fail(AWQ_ERR_NULL, "mean_abs, s and inv_s are required");
+    if (K <= 0 || K >= kMaxDim) return fail(AWQ_ERR_SHAPE, "K must be positive");
+    if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_UNSUPPORTED, "n_grid must be in [1, 64]");
+    if (misaligned(mean_abs) || misaligned(s) || misaligned(inv_s) || misaligned(ws))
+      return fail(AWQ_ERR_ALIGN, "pointers must be 16-byte aligned");
+    if (ws == nullptr || ws_bytes < awq::scales_ws_bytes(K, n_grid))
+      return fail(AWQ_ERR_WORKSPACE, "candidate_scales needs %zu workspace bytes",
+                  awq::scales_ws_bytes(K, n_grid));
+    AWQ_TRY_LAUNCH(awq::launch_candidate_scales(mean_abs, K, n_grid, s, inv_s, ws, (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const float* s, int32_t bits,
+                             int32_t group, uint32_t* qweight, float* scales, uint8_t* zeros,
+                             void* stream) {
+  try {
+    awq_status st = check_quant_params(bits, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (N < 0 || N >= kMaxDim) return fail(AWQ_ERR_SHAPE, "N out of range");
+    if (N == 0) return ok();
+    if (w == nullptr || qweight == nullptr || scales == nullptr || zeros == nullptr)
+      return fail(AWQ_ERR_NULL, "w, qweight, scales and zeros are required");
+    if (misaligned(w) || misaligned(qweight) || (s != nullptr && misaligned(s)) ||
+        ((uintptr_t)scales & 3u))
+      return fail(AWQ_ERR_ALIGN, "w, qweight, s must be 16-byte aligned, scales 4-byte");
+    AWQ_TRY_LAUNCH(awq::launch_quantize_pack(w, N, K, s, nullptr, bits, qweight, scales, zeros,
+                                             (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_reference_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                              const uint16_t* w, float* y, void* stream) {
+  try {
+    awq_status st = check_k(K, awq::kGroup);
+    if (st != AWQ_OK) return st;
+    if (M < 0 || N < 0 || M >= kMaxDim || N >= kMaxDim) return fail(AWQ_ERR_SHAPE, "M, N out of range");
+    if (M == 0 || N == 0) return ok();
+    if (x == nullptr || w == nullptr || y == nullptr) return fail(AWQ_ERR_NULL, "x, w and y are required");
+    if (misaligned(x) || misaligned(w) || misaligned(y))
+      return fail(AWQ_ERR_ALIGN, "x, w and y must be 16-byte aligned");
+    awq::GemmOperands op{};
+    op.x = x;
+    op.M = M;
+    op.N = N;
+    op.K = K;
+    op.w = w;
+    op.y = y;
+    AWQ_TRY_LAUNCH(awq::launch_gemm(op, (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                          const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                          int32_t bits, int32_t group, const float* inv_s, const float* y_ref,
+                          float* y, double* sse, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    awq_status st = check_quant_params(bits, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (M < 0 || N < 0 || M >= kMaxDim || N >= kMaxDim) return fail(AWQ_ERR_SHAPE, "M, N out of range");
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0 || N == 0) {  // empty product: only sse (if given) is written
+      if (sse != nullptr) {
+        if ((uintptr_t)sse & 7u) return fail(AWQ_ERR_ALIGN, "sse must be 8-byte aligned");
+        AWQ_TRY_LAUNCH(awq::launch_fill_f64(sse, 1, 0.0, s));
+      }
+      return ok();
+    }
+    if (x == nullptr || qweight == nullptr || scales == nullptr || zeros == nullptr)
+      return fail(AWQ_ERR_NULL, "x, qweight, scales and zeros are required");
+    if (y == nullptr && sse == nullptr) return fail(AWQ_ERR_NULL, "one of y and sse is required");
+    if (sse != nullptr && y_ref == nullptr) return fail(AWQ_ERR_NULL, "sse needs y_ref");
+    if (misaligned(x) || misaligned(qweight) || misaligned(y) || misaligned(y_ref) ||
+        misaligned(inv_s) || misaligned(ws) || ((uintptr_t)scales & 3u) || ((uintptr_t)sse & 7u))
+      return fail(AWQ_ERR_ALIGN, "tensor pointers must be 16-byte aligned (scales 4, sse 8)");
+    const size_t need = awq::align_up((size_t)awq::gemm_tiles(M, N) * sizeof(double));
+    if (sse != nullptr && (ws == nullptr || ws_bytes < need))
+      return fail(AWQ_ERR_WORKSPACE, "w4a16_gemm with sse needs %zu workspace bytes", need);
+    awq::GemmOperands op{};
+    op.x = x;
+    op.M = M;
+    op.N = N;
+    op.K = K;
+    op.qweight = qweight;
+    op.scales = scales;
+    op.zeros = zeros;
+    op.inv_s = inv_s;
+    op.y_ref = sse != nullptr ? y_ref : nullptr;
+    op.y = y;
+    op.partials = sse != nullptr ? (double*)ws : nullptr;
+    AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
+    if (sse != nullptr)
+      AWQ_TRY_LAUNCH(awq::launch_loss_reduce((const double*)ws, awq::gemm_tiles(M, N), 1, 1.0, sse, s));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
+                            int32_t bits, int32_t group, int32_t n_grid, float* mean_abs,
+                            double* losses, int32_t* best_idx, float* best_s, uint32_t* qweight,
+                            float* scales, uint8_t* zeros, void* ws, size_t ws_bytes,
+                            void* stream) {
+  try {
+    if (x == nullptr || w == nullptr || mean_abs == nullptr || losses == nullptr ||
+        best_idx == nullptr || best_s == nullptr || qweight == nullptr || scales == nullptr ||
+        zeros == nullptr)
+      return fail(AWQ_ERR_NULL, "all tensor arguments are required");
+    awq_status st = check_quant_params(bits, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (M <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim)
+      return fail(AWQ_ERR_SHAPE, "search needs M >= 1 and N >= 1");
+    if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_UNSUPPORTED, "n_grid must be in [1, 64]");
+    if (misaligned(x) || misaligned(w) || misaligned(mean_abs) || misaligned(best_s) ||
+        misaligned(qweight) || misaligned(ws) || ((uintptr_t)scales & 3u) ||
+        ((uintptr_t)losses & 7u) || ((uintptr_t)best_idx & 3u))
+      return fail(AWQ_ERR_ALIGN, "tensor pointers must be 16-byte aligned (scales/best_idx 4, losses 8)");
+    const SearchLayout L = search_layout(M, N, K, n_grid);
+    if (ws == nullptr || ws_bytes < L.total)
+      return fail(AWQ_ERR_WORKSPACE, "search_scale needs %zu workspace bytes", L.total);
+
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
+    float* yref = (float*)(base + L.yref);
+    float* sc = (float*)(base + L.s);
+    float* inv = (float*)(base + L.inv);
+    uint32_t* qtmp = (uint32_t*)(base + L.qtmp);
+    float* sctmp = (float*)(base + L.sctmp);
+    uint8_t* ztmp = (uint8_t*)(base + L.ztmp);
+    double* partials = (double*)(base + L.partials);
+    const int64_t T = awq::gemm_tiles(M, N);
+
+    AWQ_TRY_LAUNCH(awq::launch_act_stats(x, M, K, mean_abs, (double*)(base + L.stats_ws), s));
+    AWQ_TRY_LAUNCH(awq::launch_candidate_scales(mean_abs, K, n_grid, sc, inv, base + L.scales_ws, s));
+    {
+      awq::GemmOperands op{};
+      op.x = x;
+      op.M = M;
+      op.N = N;
+      op.K = K;
+      op.w = w;
+      op.y = yref;
+      AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
+    }
+    for (int i = 0; i < n_grid; ++i) {
+      AWQ_TRY_LAUNCH(awq::launch_quantize_pack(w, N, K, sc + (int64_t)i * K, nullptr, bits, qtmp,
+                                               sctmp, ztmp, s));
+      awq::GemmOperands op{};
+      op.x = x;
+      op.M = M;
+      op.N = N;
+      op.K = K;
+      op.qweight = qtmp;
+      op.scales = sctmp;
+      op.zeros = ztmp;
+      op.inv_s = inv + (int64_t)i * K;
+      op.y_ref = yref;
+      op.partials = partials + (int64_t)i * T;
+      AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
+    }
+    AWQ_TRY_LAUNCH(awq::launch_loss_reduce(partials, T, n_grid, (double)M * (double)N, losses, s));
+    AWQ_TRY_LAUNCH(awq::launch_argmin(losses, n_grid, best_idx, s));
+    AWQ_TRY_LAUNCH(awq::launch_select_row(sc, best_idx, K, best_s, s));
+    AWQ_TRY_LAUNCH(awq::launch_quantize_pack(w, N, K, sc, best_idx, bits, qweight, scales, zeros, s));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of libawq_mi355x.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace awq {
+
+// Only group size supported by the kernels (K is tiled in 128-wide groups).
+constexpr int kGroup = 128;
+
+// ---- W4A16 / reference GEMM tiling (also used to size SSE partials) ----
+constexpr int kGemmBM = 256;
+constexpr int kGemmBN = 256;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+inline int64_t gemm_tiles(int64_t M, int64_t N) {
+  return ceil_div(M, kGemmBM) * ceil_div(N, kGemmBN);
+}
+
+// ---- activation statistics partition: R row chunks x K fp64 partials ----
+struct StatsPlan {
+  int64_t rows_per_block;
+  int64_t row_blocks;
+};
+StatsPlan stats_plan(int64_t M);
+inline size_t stats_ws_bytes(int64_t M, int64_t K) {
+  return align_up((size_t)stats_plan(M).row_blocks * (size_t)K * sizeof(double));
+}
+
+// ---- candidate scales: r (fp64) + per-block min/max partials ----
+constexpr int kScaleThreads = 256;
+inline size_t scales_ws_bytes(int64_t K, int n_grid) {
+  const int64_t nb = ceil_div(K, kScaleThreads);
+  return align_up((size_t)n_grid * K * sizeof(double)) +
+         align_up((size_t)n_grid * nb * 2 * sizeof(double));
+}
+
+// ---- launchers (each returns the launch's hipError_t) ----
+hipError_t launch_act_stats(const uint16_t* x, int64_t M, int64_t K, float* mean_abs,
+                            double* partial, hipStream_t stream);
+
+hipError_t launch_candidate_scales(const float* mean_abs, int64_t K, int n_grid, float* s,
+                                   float* inv_s, void* ws, hipStream_t stream);
+
+// s_sel: when non-NULL, the scale row used is s + max(*s_sel, 0) * K.
+hipError_t launch_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                                const int32_t* s_sel, int bits, uint32_t* qweight,
+                                float* scales, uint8_t* zeros, hipStream_t stream);
+
+struct GemmOperands {
+  const uint16_t* x;        // bf16 [M][K]
+  int64_t M, N, K;
+  // exactly one of: w (bf16 [N][K]) or the packed triple
+  const uint16_t* w;
+  const uint32_t* qweight;
+  const float* scales;
+  const uint8_t* zeros;
+  const float* inv_s;       // [K] or NULL
+  const float* y_ref;       // [M][N] or NULL
+  float* y;                 // [M][N] or NULL
+  double* partials;         // [tiles] fp64 SSE per tile, or NULL
+};
+hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream);
+
+// losses[i] = (sum_t partials[i*T + t]) / divisor, fixed summation order.
+hipError_t launch_loss_reduce(const double* partials, int64_t T, int n_grid, double divisor,
+                              double* losses, hipStream_t stream);
+hipError_t launch_argmin(const double* losses, int n_grid, int32_t* best, hipStream_t stream);
+hipError_t launch_select_row(const float* s, const int32_t* sel, int64_t K, float* out,
+                             hipStream_t stream);
+hipError_t launch_fill_f64(double* p, int64_t n, double v, hipStream_t stream);
+
+}  // namespace awq

@@ -1,0 +1,163 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/*.h, and rejects invalid arguments on the host before
+making any HIP call (so these run on a machine without a GPU)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import post_weight_quantization_stats_amd as awq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, SHAPE, UNSUPPORTED, ALIGN, WORKSPACE = 0, 1, 2, 3, 4, 5
+FAKE = 0x10000          # 16-byte aligned, never dereferenced on error paths
+FAKE_MIS = 0x10004      # misaligned
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(awq_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("awq_act_stats", "awq_search_scale", "awq_quantize_pack", "awq_w4a16_gemm"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = awq.lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(declared_functions()) <= set(awq._SIGNATURES)
+
+
+def test_version_and_status_strings():
+    lib = awq.lib()
+    assert lib.awq_abi_version() == 1
+    assert lib.awq_status_string(0) == b"AWQ_OK"
+    assert lib.awq_status_string(5) == b"AWQ_ERR_WORKSPACE"
+    assert lib.awq_status_string(99) == b"AWQ_ERR_UNKNOWN"
+
+
+def ws_size(op, M, N, K, bits=4, group=128, n_grid=20):
+    out = ctypes.c_size_t(0)
+    st = awq.lib().awq_workspace_size(op, M, N, K, bits, group, n_grid, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_sizes():
+    st, b = ws_size(awq.OP_SEARCH_SCALE, 65536, 12288, 4096)
+    assert st == OK
+    assert b >= 65536 * 12288 * 4          # holds the fp32 reference output
+    assert b < 65536 * 12288 * 4 + 200 * 2 ** 20
+    assert ws_size(awq.OP_ACT_STATS, 256, 0, 512)[0] == OK
+    assert ws_size(awq.OP_W4A16_GEMM, 0, 0, 128) == (OK, 0)
+    assert ws_size(awq.OP_SEARCH_SCALE, 256, 512, 500)[0] == SHAPE
+    assert ws_size(awq.OP_SEARCH_SCALE, 256, 512, 512, bits=2)[0] == UNSUPPORTED
+    assert ws_size(awq.OP_SEARCH_SCALE, 256, 512, 512, group=64)[0] == UNSUPPORTED
+    assert ws_size(awq.OP_SEARCH_SCALE, 256, 512, 512, n_grid=0)[0] == UNSUPPORTED
+    assert ws_size(awq.OP_SEARCH_SCALE, 256, 512, 512, n_grid=65)[0] == UNSUPPORTED
+    assert ws_size(awq.OP_SEARCH_SCALE, 0, 512, 512)[0] == SHAPE
+    assert ws_size(99, 1, 1, 128)[0] == UNSUPPORTED
+    assert awq.lib().awq_workspace_size(0, 1, 1, 8, 4, 128, 20, None) == NULL
+
+
+def test_act_stats_errors():
+    lib = awq.lib()
+    f = lib.awq_act_stats
+    assert f(None, 4, 8, FAKE, FAKE, 1 << 20, None) == NULL
+    assert f(FAKE, 0, 8, FAKE, FAKE, 1 << 20, None) == SHAPE
+    assert f(FAKE, 4, 12, FAKE, FAKE, 1 << 20, None) == SHAPE
+    assert f(FAKE_MIS, 4, 8, FAKE, FAKE, 1 << 20, None) == ALIGN
+    assert f(FAKE, 4, 8, FAKE, None, 0, None) == WORKSPACE
+    assert f(FAKE, 4, 8, FAKE, FAKE, 8, None) == WORKSPACE
+    assert b"workspace" in lib.awq_last_error()
+
+
+def test_candidate_scales_errors():
+    f = awq.lib().awq_candidate_scales
+    assert f(None, 8, 20, FAKE, FAKE, FAKE, 1 << 20, None) == NULL
+    assert f(FAKE, 0, 20, FAKE, FAKE, FAKE, 1 << 20, None) == SHAPE
+    assert f(FAKE, 8, 0, FAKE, FAKE, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert f(FAKE, 8, 65, FAKE, FAKE, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert f(FAKE, 8, 20, FAKE_MIS, FAKE, FAKE, 1 << 20, None) == ALIGN
+    assert f(FAKE, 8, 20, FAKE, FAKE, FAKE, 16, None) == WORKSPACE
+
+
+def test_quantize_pack_errors():
+    f = awq.lib().awq_quantize_pack
+    assert f(None, 4, 128, None, 4, 128, FAKE, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 4, 128, None, 4, 128, None, FAKE, FAKE, None) == NULL
+    assert f(FAKE, 4, 128, None, 5, 128, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 4, 128, None, 2, 128, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 4, 256, None, 4, 64, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 4, 200, None, 4, 128, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 4, 0, None, 4, 128, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, -1, 128, None, 4, 128, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE_MIS, 4, 128, None, 4, 128, FAKE, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, 4, 128, FAKE_MIS, 4, 128, FAKE, FAKE, FAKE, None) == ALIGN
+    # N == 0 is a valid no-op and makes no HIP call
+    assert f(FAKE, 0, 128, None, 4, 128, FAKE, FAKE, FAKE, None) == OK
+
+
+def test_gemm_errors():
+    f = awq.lib().awq_w4a16_gemm
+    args = dict(x=FAKE, M=4, N=8, K=128, q=FAKE, sc=FAKE, z=FAKE, bits=4, group=128, inv=None,
+                yref=None, y=FAKE, sse=None, ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["x"], a["M"], a["N"], a["K"], a["q"], a["sc"], a["z"], a["bits"], a["group"],
+                 a["inv"], a["yref"], a["y"], a["sse"], a["ws"], a["wsb"], None)
+
+    assert call(x=None) == NULL
+    assert call(y=None) == NULL                       # neither y nor sse
+    assert call(sse=FAKE) == NULL                     # sse without y_ref
+    assert call(bits=8) == UNSUPPORTED
+    assert call(K=100) == SHAPE
+    assert call(M=-1) == SHAPE
+    assert call(x=FAKE_MIS) == ALIGN
+    assert call(inv=FAKE_MIS) == ALIGN
+    assert call(sse=FAKE, yref=FAKE) == WORKSPACE
+    assert call(sse=FAKE, yref=FAKE, ws=FAKE, wsb=8) == WORKSPACE
+    r = awq.lib().awq_reference_gemm
+    assert r(None, 4, 8, 128, FAKE, FAKE, None) == NULL
+    assert r(FAKE, 4, 8, 100, FAKE, FAKE, None) == SHAPE
+    assert r(FAKE, 4, 8, 128, FAKE_MIS, FAKE, None) == ALIGN
+
+
+def test_search_errors():
+    f = awq.lib().awq_search_scale
+
+    def call(x=FAKE, M=256, K=512, w=FAKE, N=512, bits=4, group=128, n_grid=20, ws=FAKE, wsb=1 << 40,
+             best=FAKE):
+        return f(x, M, K, w, N, bits, group, n_grid, FAKE, FAKE, best, FAKE, FAKE, FAKE, FAKE, ws,
+                 wsb, None)
+
+    assert call(x=None) == NULL
+    assert call(best=None) == NULL
+    assert call(M=0) == SHAPE
+    assert call(N=0) == SHAPE
+    assert call(K=384 + 8) == SHAPE
+    assert call(bits=1) == UNSUPPORTED
+    assert call(n_grid=0) == UNSUPPORTED
+    assert call(w=FAKE_MIS) == ALIGN
+    assert call(ws=None) == WORKSPACE
+    need = ws_size(awq.OP_SEARCH_SCALE, 256, 512, 512)[1]
+    assert call(wsb=need - 1) == WORKSPACE
+    assert str(need) in awq.lib().awq_last_error().decode()
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        awq.act_stats(torch.zeros((4, 8), dtype=torch.bfloat16))

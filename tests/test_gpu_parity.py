@@ -1,0 +1,214 @@
+"""GPU parity: every step of the HIP path against the CPU fp64 oracle on the
+same seeded inputs, element by element.
+
+Tolerances: codes, zeros, scales and packed words bit-exact given the
+oracle's s; GEMM within 1e-3 relative (|d| <= 1e-3 max(|y|, rms Y) and
+Frobenius); per-candidate losses within 1e-4 relative; the chosen candidate
+equal, or (ties) within 1e-4 of the oracle's minimum; statistics within 1e-6
+relative (fp64 sums of bf16 magnitudes are normally exact, so bit equality is
+also counted).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import post_weight_quantization_stats_amd as awq
+import synth
+from gpu_util import (announce, gemm_close, require_gpu, to_dev_bf16, to_dev_f32, u32,
+                      ulp_distance_f32)
+
+pytestmark = pytest.mark.gpu
+
+# (M, K, N, seed, n_outlier): several 256x256 tiles, ragged M / N tails,
+# one group, a single token.
+SHAPES = [
+    (256, 512, 512, 0, 5),
+    (300, 384, 200, 1, 4),
+    (513, 256, 520, 2, 3),
+    (1, 128, 64, 3, 1),
+    (77, 1024, 264, 4, 10),
+    (1024, 640, 768, 5, 6),
+]
+
+
+def layer(shape):
+    M, K, N, seed, n_out = shape
+    if (M, K, N) == (256, 512, 512):
+        x, w, _ = synth.make_layer("single_linear_512")
+        return x, w
+    return synth.random_layer(M, K, N, seed=seed, n_outlier=n_out, outlier_factor=20.0)
+
+
+def ids(s):
+    return f"M{s[0]}_K{s[1]}_N{s[2]}"
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_act_stats(dev, shape):
+    announce("act_stats", ids(shape))
+    x, _ = layer(shape)
+    got = awq.act_stats(to_dev_bf16(x, dev)).cpu().numpy().astype(np.float64)
+    _, ref = O.act_stats(x)
+    rel = np.abs(got - ref) / np.maximum(ref, 1e-30)
+    assert rel.max() <= 1e-6
+    assert np.mean(got == ref) > 0.99
+
+
+def test_act_stats_long_and_ragged(dev):
+    announce("act_stats long ragged")
+    x, _ = synth.random_layer(5003, 1032, 8, seed=7, n_outlier=9)
+    got = awq.act_stats(to_dev_bf16(x, dev)).cpu().numpy().astype(np.float64)
+    _, ref = O.act_stats(x)
+    assert (np.abs(got - ref) / ref).max() <= 1e-6
+
+
+@pytest.mark.parametrize("K,n_grid", [(512, 20), (4096, 20), (1000, 7), (128, 1), (300, 64)])
+def test_candidate_scales(dev, K, n_grid):
+    announce("candidate_scales", K, n_grid)
+    rng = np.random.default_rng(K + n_grid)
+    a = O.f32(np.abs(rng.standard_normal(K)) * 0.8 + 0.01)
+    a[rng.choice(K, size=max(1, K // 100), replace=False)] *= 30.0
+    a[0] = 0.0   # a dead channel hits the floor
+    a = O.f32(a)
+    s, inv = awq.candidate_scales(to_dev_f32(a, dev), n_grid)
+    s_ref, inv_ref = O.candidate_scales(a, n_grid)
+    ds = ulp_distance_f32(s.cpu().numpy(), s_ref)
+    di = ulp_distance_f32(inv.cpu().numpy(), inv_ref)
+    # fp64 pow may differ from the host's in its last bit; that flips the
+    # fp32 rounding with probability ~2^-29 per element.
+    assert ds.max() <= 1 and di.max() <= 1
+    assert np.mean(ds == 0) > 0.999
+    assert np.all(s.cpu().numpy()[0] == 1.0)
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_quantize_pack_bit_exact(dev, shape, bits):
+    announce("quantize_pack", ids(shape), bits)
+    x, w = layer(shape)
+    _, a = O.act_stats(x)
+    s_ref, _ = O.candidate_scales(a, 20)
+    wd = to_dev_bf16(w, dev)
+    for i in (None, 0, 6, 13, 19):
+        s_row = None if i is None else s_ref[i]
+        qw, sc, ze = awq.quantize_pack(wd, None if s_row is None else to_dev_f32(s_row, dev), bits)
+        q, z, st = O.quantize(w, s_row, bits, 128)
+        rq, rs, rz = O.pack(q, z, st)
+        assert np.array_equal(u32(qw), rq), f"codes differ at candidate {i}"
+        assert np.array_equal(sc.cpu().numpy(), rs), f"scales differ at candidate {i}"
+        assert np.array_equal(ze.cpu().numpy(), rz), f"zeros differ at candidate {i}"
+
+
+def test_quantize_special_groups(dev):
+    announce("quantize special groups")
+    N, K = 6, 256
+    W = np.zeros((N, K), np.float32)
+    W[1] = np.linspace(0.5, 3.0, K)                    # all positive
+    W[2] = -np.linspace(0.5, 3.0, K)                   # all negative
+    rng = np.random.default_rng(0)
+    codes = rng.integers(0, 16, size=K)
+    codes[0], codes[1], codes[128], codes[129] = 0, 15, 0, 15
+    W[3] = (codes - 5) * 2.0 ** -6                      # on the 16-level grid
+    W[4] = 1e-3 * rng.standard_normal(K)               # tiny values
+    W[5, :128] = 7.0                                   # constant group
+    w = synth.to_bf16_bits(W)
+    for bits in (3, 4):
+        qw, sc, ze = awq.quantize_pack(to_dev_bf16(w, dev), None, bits)
+        rq, rs, rz = O.pack(*O.quantize(w, None, bits, 128))
+        assert np.array_equal(u32(qw), rq)
+        assert np.array_equal(sc.cpu().numpy(), rs)
+        assert np.array_equal(ze.cpu().numpy(), rz)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_reference_gemm(dev, shape):
+    announce("reference_gemm", ids(shape))
+    x, w = layer(shape)
+    y = awq.reference_gemm(to_dev_bf16(x, dev), to_dev_bf16(w, dev)).cpu().numpy()
+    gemm_close(y, O.gemm(x, O.bf16_bits_to_f64(w)))
+
+
+@pytest.mark.parametrize("use_inv_s", [True, False])
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_w4a16_gemm_and_sse(dev, shape, use_inv_s):
+    announce("w4a16_gemm", ids(shape), use_inv_s)
+    x, w = layer(shape)
+    M, N = x.shape[0], w.shape[0]
+    _, a = O.act_stats(x)
+    s_ref, inv_ref = O.candidate_scales(a, 20)
+    i = 11
+    q, z, st = O.quantize(w, s_ref[i], 4, 128)
+    qw, sc, ze = O.pack(q, z, st)
+    inv = inv_ref[i] if use_inv_s else None
+    B = O.dequant_operand(q, z, st, 128, inv)
+    y_oracle = O.gemm(x, B)
+    y_ref32 = O.f32(O.gemm(x, O.bf16_bits_to_f64(w)))
+    xd = to_dev_bf16(x, dev)
+    qwd = torch.from_numpy(qw.view(np.int32)).to(dev)
+    scd = torch.from_numpy(sc).to(dev)
+    zed = torch.from_numpy(ze).to(dev)
+    invd = None if inv is None else to_dev_f32(inv, dev)
+    y, sse = awq.w4a16_gemm(xd, qwd, scd, zed, 4, 128, inv_s=invd, y_ref=to_dev_f32(y_ref32, dev))
+    gemm_close(y.cpu().numpy(), y_oracle)
+    sse_ref = float(np.sum((y_oracle - y_ref32) ** 2))
+    assert float(sse.item()) == pytest.approx(sse_ref, rel=1e-4)
+    # y-only call gives the same numbers as the fused call
+    y2 = awq.w4a16_gemm(xd, qwd, scd, zed, 4, 128, inv_s=invd)
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_search_scale(dev, shape, bits):
+    announce("search_scale", ids(shape), bits)
+    x, w = layer(shape)
+    n_grid = 20
+    out = awq.search_scale(to_dev_bf16(x, dev), to_dev_bf16(w, dev), bits, 128, n_grid)
+    torch.cuda.synchronize()
+    ref = O.search(x, w, bits, 128, n_grid)
+    mean_abs = out["mean_abs"].cpu().numpy().astype(np.float64)
+    assert (np.abs(mean_abs - ref["mean_abs"]) / np.maximum(ref["mean_abs"], 1e-30)).max() <= 1e-6
+    losses = out["losses"].cpu().numpy()
+    np.testing.assert_allclose(losses, ref["losses"], rtol=1e-4, atol=0)
+    best = int(out["best_idx"].item())
+    assert 0 <= best < n_grid
+    assert ref["losses"][best] <= (1 + 1e-4) * ref["losses"].min()
+    best_s = out["best_s"].cpu().numpy().astype(np.float64)
+    assert ulp_distance_f32(best_s, ref["s"][best]).max() <= 1
+    # the written weights are the quantization of W . diag(best_s), bit-exact
+    rq, rs, rz = O.pack(*O.quantize(w, best_s, bits, 128))
+    assert np.array_equal(u32(out["qweight"]), rq)
+    assert np.array_equal(out["scales"].cpu().numpy(), rs)
+    assert np.array_equal(out["zeros"].cpu().numpy(), rz)
+
+
+def test_search_is_bit_reproducible(dev):
+    announce("search determinism")
+    x, w = layer(SHAPES[2])
+    xd, wd = to_dev_bf16(x, dev), to_dev_bf16(w, dev)
+    a = awq.search_scale(xd, wd)
+    b = awq.search_scale(xd, wd)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_gemm_empty_and_degenerate(dev):
+    announce("gemm empty")
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device=dev)
+    qw = torch.zeros((8, 16), dtype=torch.int32, device=dev)
+    sc = torch.ones((8, 1), dtype=torch.float32, device=dev)
+    ze = torch.zeros((8, 1), dtype=torch.uint8, device=dev)
+    yref = torch.zeros((0, 8), dtype=torch.float32, device=dev)
+    y, sse = awq.w4a16_gemm(x, qw, sc, ze, y_ref=yref)
+    assert y.shape == (0, 8) and float(sse.item()) == 0.0
+    w0 = torch.zeros((0, 128), dtype=torch.bfloat16, device=dev)
+    q0, s0, z0 = awq.quantize_pack(w0)
+    assert q0.shape == (0, 16)
