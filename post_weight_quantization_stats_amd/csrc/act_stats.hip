@@ -6,7 +6,7 @@
 // contiguous row segments (64 lanes x 16 B); lanes accumulate |x| of their 8
 // columns in fp64 (the partial sums of bf16 magnitudes stay exact in
 // practice), the four waves of a block are combined in a fixed order, and a
-// second kernel adds the per-block partials in row-block order.
+// second kernel adds the per-block partials in a fixed order.
 #include "awq_internal.h"
 #include "device_common.h"
 
@@ -64,13 +64,23 @@ __global__ __launch_bounds__(kThreads) void act_stats_partial_kernel(
   }
 }
 
+// Column k's partials are split over 4 row-block strides (one wave each,
+// 64 columns per block) and combined in a fixed order.
 __global__ __launch_bounds__(kThreads) void act_stats_finalize_kernel(
     const double* __restrict__ partial, int64_t R, int64_t K, int64_t M, float* __restrict__ out) {
-  const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (k >= K) return;
+  const int c = threadIdx.x & 63;
+  const int g = threadIdx.x >> 6;
+  const int64_t k = (int64_t)blockIdx.x * 64 + c;
   double s = 0.0;
-  for (int64_t r = 0; r < R; ++r) s += partial[r * K + k];
-  out[k] = (float)(s / (double)M);
+  if (k < K) {
+#pragma unroll 8
+    for (int64_t r = g; r < R; r += 4) s += partial[r * K + k];
+  }
+  __shared__ double red[4][64];
+  red[g][c] = s;
+  __syncthreads();
+  if (g == 0 && k < K)
+    out[k] = (float)((((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]) / (double)M);
 }
 
 }  // namespace
@@ -94,7 +104,7 @@ hipError_t launch_act_stats(const uint16_t* x, int64_t M, int64_t K, float* mean
   act_stats_partial_kernel<<<grid, kThreads, 0, stream>>>(x, M, K, plan.rows_per_block, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  act_stats_finalize_kernel<<<(unsigned)ceil_div(K, kThreads), kThreads, 0, stream>>>(
+  act_stats_finalize_kernel<<<(unsigned)ceil_div(K, 64), kThreads, 0, stream>>>(
       partial, plan.row_blocks, K, M, mean_abs);
   return hipGetLastError();
 }
