@@ -31,6 +31,37 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "AWQ search: layers/s + W4A16 GEMM TFLOP/s (% MFMA peak), quant GB/s (% HBM)"
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "w4a16_gemm_llama2_7b_qkv_traffic.txt")
+GEMM_SOURCES = ["w4a16_gemm.hip", "device_common.h", "awq_internal.h"]
+
+
+def gemm_source_hash() -> str:
+    """Hash of the W4A16 GEMM kernel sources (ties counter data to a kernel version)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "post_weight_quantization_stats_amd", "csrc")
+    for name in GEMM_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per W4A16 GEMM launch from the committed rocprofv3 counter
+    summary, or None when the kernel source changed since it was taken."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_hash") != gemm_source_hash():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -84,7 +115,7 @@ def main() -> int:
     ap.add_argument("--layer", default=None)
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-m", type=int, default=1024)
+    ap.add_argument("--cpu-m", type=int, default=2048)
     ap.add_argument("--cpu-n", type=int, default=1024)
     args = ap.parse_args()
 
@@ -112,6 +143,13 @@ def main() -> int:
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+
+    # Calibration copy of known size for scaling the FETCH_SIZE / WRITE_SIZE
+    # counters: reads 2*M*K bytes of bf16, writes 4*M*K bytes of fp32.
+    calib = xd.to(torch.float32)
+    torch.cuda.synchronize()
+    log(f"calibration copy: read {2 * M * K} B, write {4 * M * K} B")
+    del calib
 
     log(f"warmup {args.warmup}")
     out = None
@@ -172,8 +210,11 @@ def main() -> int:
                    "bits": bits, "group": spec.group, "n_grid": G},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None, "kernel": "w4a16 gemm + fused squared error",
-                     "flops_per_launch": flops, "ms_per_launch": t_gemm},
+                     "traffic": committed_traffic(), "kernel": "w4a16 gemm + fused squared error",
+                     "flops_per_launch": flops, "ms_per_launch": t_gemm,
+                     "algorithmic_bytes_per_launch": 2.0 * M * K + N * K / 2 +
+                     5.0 * N * K / spec.group + 4.0 * K + 4.0 * M * N,
+                     "kernel_source_hash": gemm_source_hash()},
         "kernels": {
             "w4a16_gemm_sse": {"ms": t_gemm, "tflops": gemm_tflops,
                                "frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS},

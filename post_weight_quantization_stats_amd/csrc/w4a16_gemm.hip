@@ -16,17 +16,21 @@
 //   * The activation tile (and the bf16 weight tile of the reference product)
 //     is copied global -> LDS by the buffer unit (buffer_load_dwordx4 ... lds)
 //     into a ring of 4 stages, three k-steps ahead; no VGPRs are involved.
-//     Before the barrier that publishes a stage, each wave waits for its own
-//     copy into it (other waves read it after the barrier).
 //     Each stage is its own __shared__ array and the k-loop is unrolled by 4,
 //     so the compiler sees which stage every DMA and every read touches and
 //     waits (vmcnt) only for the copy a read depends on.
+//   * Stages are published two k-steps ahead: before the barrier that ends
+//     step k each wave waits for its own copy into stage k+2 (other waves
+//     read it after the barrier).  So the fragments of step k+1's first k16
+//     substep are read before that barrier, and those of the second substep
+//     during the first substep's MFMAs; LDS latency never sits between a
+//     barrier and the next MFMA.
 //   * INT4 path: thread t owns weight row t of the tile.  Its 16 bytes of codes
-//     for a k-step (plus the group's step and zero) are loaded two k-steps
+//     for a k-step (plus the group's step and zero) are loaded three k-steps
 //     ahead into one of two register sets; the dequantized bf16 values
 //     B = bf16(f32(f32((q - z) * step) * inv_s[k])) are written into a
-//     two-stage B ring one k-step ahead, between the MFMAs of the current
-//     step.  inv_s[k] is uniform and comes from SGPRs.  The dequantized
+//     4-stage B ring two k-steps ahead, interleaved with the current step's
+//     MFMAs.  inv_s[k] is uniform and comes from SGPRs.  The dequantized
 //     operand is never written to HBM.
 //   * Buffer resources: 32-bit per-lane offsets, the k offset in an SGPR,
 //     and rows past M / N read as zero, so the loads need no branches.
@@ -147,9 +151,9 @@ template <bool kInt4, bool kInvS>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __restrict__ inv_s) {
   // Separate objects per stage: the compiler tracks LDS-DMA writes per object.
   __shared__ uint4 sa0[kSlots], sa1[kSlots], sa2[kSlots], sa3[kSlots];
-  __shared__ uint4 sb0[kSlots], sb1[kSlots], sb2[kInt4 ? 1 : kSlots], sb3[kInt4 ? 1 : kSlots];
+  __shared__ uint4 sb0[kSlots], sb1[kSlots], sb2[kSlots], sb3[kSlots];
   uint4* const SA[4] = {sa0, sa1, sa2, sa3};
-  uint4* const SB[4] = {sb0, sb1, sb2, sb3};   // INT4 uses a 2-stage B ring
+  uint4* const SB[4] = {sb0, sb1, sb2, sb3};
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -229,25 +233,31 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto mfma_substep = [&](const uint4* la, const uint4* lb, int s) {
-    bf16x8 af[4], bfr[4];
+  struct Frags {
+    bf16x8 a[4], b[4];
+  };
+  auto read_frags = [&](Frags& F, const uint4* la, const uint4* lb, int s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      af[i] = __builtin_bit_cast(bf16x8, la[swz(wm * 128 + i * 32 + lr, 2 * s + lk)]);
+      F.a[i] = __builtin_bit_cast(bf16x8, la[swz(wm * 128 + i * 32 + lr, 2 * s + lk)]);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      bfr[j] = __builtin_bit_cast(bf16x8, lb[swz(wn * 128 + j * 32 + lr, 2 * s + lk)]);
+      F.b[j] = __builtin_bit_cast(bf16x8, lb[swz(wn * 128 + j * 32 + lr, 2 * s + lk)]);
+  };
+  auto mfma16 = [&](const Frags& F) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[i], F.b[j], acc[i][j], 0, 0, 0);
   };
 
   const int64_t KT = K / BK;   // multiple of 4 (K is a multiple of 128)
   CodeRegs C[2];
+  Frags F0, F1;
 
-  // Prologue: A(0..2) in flight, B(0) ready in LDS.
+  // Prologue: A(0..2) [and bf16 B(0..2)] in flight; INT4 B(0), B(1)
+  // dequantized; stages 0 and 1 published; step 0's first fragments read.
   dma_tile(ra, SA[0], 0);
   dma_tile(ra, SA[1], BK);
   dma_tile(ra, SA[2], 2 * BK);
@@ -256,14 +266,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
     load_codes(C[1], BK);
     dequant_half(C[0], SB[0], 0, 0);
     dequant_half(C[0], SB[0], 0, 2);
+    dequant_half(C[1], SB[1], BK, 0);
+    dequant_half(C[1], SB[1], BK, 2);
+    load_codes(C[0], 2 * BK);
   } else {
     dma_tile(rb, SB[0], 0);
     dma_tile(rb, SB[1], BK);
     dma_tile(rb, SB[2], 2 * BK);
     own_dma_done(SB[0]);
+    own_dma_done(SB[1]);
   }
   own_dma_done(SA[0]);
+  own_dma_done(SA[1]);
   barrier_lds();
+  read_frags(F0, SA[0], SB[0], 0);
 
   // One k-step; every stage index is a compile-time constant.  The loads are
   // issued unconditionally (also past the end of K, where they read other
@@ -271,23 +287,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
   // wait counts are exact on every path.
   auto step = [&](int64_t k, auto I) {
     constexpr int i = decltype(I)::value;      // k % 4
-    uint4* const a_cur = SA[i];
     dma_tile(ra, SA[(i + 3) & 3], (k + 3) * BK);
     if constexpr (kInt4) {
-      uint4* const b_cur = SB[i & 1];
-      uint4* const b_next = SB[(i + 1) & 1];
-      load_codes(C[i & 1], (k + 2) * BK);
-      mfma_substep(a_cur, b_cur, 0);
-      dequant_half(C[(i + 1) & 1], b_next, (k + 1) * BK, 0);
-      mfma_substep(a_cur, b_cur, 1);
-      dequant_half(C[(i + 1) & 1], b_next, (k + 1) * BK, 2);
+      load_codes(C[(i + 1) & 1], (k + 3) * BK);
     } else {
       dma_tile(rb, SB[(i + 3) & 3], (k + 3) * BK);
-      mfma_substep(a_cur, SB[i], 0);
-      mfma_substep(a_cur, SB[i], 1);
-      own_dma_done(SB[(i + 1) & 3]);
     }
-    own_dma_done(SA[(i + 1) & 3]);
+    read_frags(F1, SA[i], SB[i], 1);
+    mfma16(F0);
+    if constexpr (kInt4) dequant_half(C[i & 1], SB[(i + 2) & 3], (k + 2) * BK, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma16(F1);
+    if constexpr (kInt4) dequant_half(C[i & 1], SB[(i + 2) & 3], (k + 2) * BK, 2);
+    read_frags(F0, SA[(i + 1) & 3], SB[(i + 1) & 3], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    own_dma_done(SA[(i + 2) & 3]);
+    if constexpr (!kInt4) own_dma_done(SB[(i + 2) & 3]);
     barrier_lds();
   };
 
@@ -300,30 +315,77 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
 
   // Epilogue.  32x32 block layout: lane holds column (lane & 31) and rows
   // 8*(r/4) + 4*(lane/32) + r%4 for accumulator register r.
-  double sse = 0.0;
-  const int64_t row0 = m0 + wm * 128 + 4 * lk;
+  const int64_t row0 = wm * 128 + 4 * lk;        // within the tile
   const int64_t col0 = n0 + wn * 128 + lr;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  if (p.y != nullptr) {
+    // Rows past M fall outside the buffer resource and are dropped.
+    const rsrc_t ro = make_rsrc(p.y + m0 * N + n0, ((uint64_t)(M - m0) * N - n0) * 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int64_t gn = col0 + j * 32;
+      if (n0 + wn * 128 + j * 32 + lr < N) {
+        const uint32_t cbase = (uint32_t)((row0 * N + wn * 128 + j * 32 + lr) * 4);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t gm = row0 + i * 32 + 8 * (r >> 2) + (r & 3);
-        if (gm < M && gn < N) {
-          const float v = acc[i][j][r];
-          if (p.y != nullptr) p.y[gm * N + gn] = v;
-          if (p.partials != nullptr) {
-            const float d = v - p.y_ref[gm * N + gn];
-            sse += (double)d * (double)d;
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t roff = (uint32_t)((i * 32 + 8 * (r >> 2) + (r & 3)) * N * 4);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ro, cbase + roff, 0, 0);
           }
         }
       }
     }
   }
   if (p.partials != nullptr) {
+    // Sum of (acc - y_ref)^2.  The wave's 128 x 128 block of y_ref is staged
+    // through LDS (the k-loop's stage buffers are free now) by the buffer
+    // unit, 64 rows at a time, so the whole block is in flight at once; each
+    // wave copies and reads only its own rows, so no barrier is needed
+    // between the copy and the reads.  Rows past M read 0 through the buffer
+    // resource (their accumulators are 0 too); columns past N are masked.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stray prefetches into LDS
+    barrier_lds();                                      // every wave is done with the stages
+    float* const reg_w[8] = {(float*)sa0, (float*)sa1, (float*)sa2, (float*)sa3,
+                             (float*)sb0, (float*)sb1, (float*)sb2, (float*)sb3};
+    float* const mine0 = wave == 0 ? reg_w[0] : wave == 1 ? reg_w[2] : wave == 2 ? reg_w[4] : reg_w[6];
+    float* const mine1 = wave == 0 ? reg_w[1] : wave == 1 ? reg_w[3] : wave == 2 ? reg_w[5] : reg_w[7];
+    const rsrc_t ry = make_rsrc(p.y_ref + m0 * N + n0, ((uint64_t)(M - m0) * N - n0) * 4);
+    // DMA q of a phase: rows 2q, 2q+1 of the phase's 64 rows; lane L -> row
+    // 2q + L/32, columns 4*(L%32) .. +3 of the wave's 128 columns.
+    const uint32_t ybase = (uint32_t)((((int64_t)wm * 128 + (lane >> 5)) * N + wn * 128 + 4 * (lane & 31)) * 4);
+    bool col_ok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) col_ok[j] = n0 + wn * 128 + j * 32 + lr < N;
+    double sse = 0.0;
+#pragma unroll
+    for (int phase = 0; phase < 2; ++phase) {
+      if (phase == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of phase 0 done
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        float* dst = (q < 16 ? mine0 : mine1) + (q & 15) * 256;
+        const uint32_t roff = (uint32_t)(((int64_t)phase * 64 + 2 * q) * N * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void*)dst, 16, ybase + roff, 0, 0, 0);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * phase + ii;
+        double dpart = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rho = ii * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);   // row within the phase
+            const float yv = (rho < 32 ? mine0 : mine1)[(rho & 31) * 128 + j * 32 + lr];
+            float d = acc[i][j][r] - yv;
+            d = col_ok[j] ? d : 0.f;
+            dpart += (double)d * (double)d;
+          }
+        }
+        sse += dpart;
+      }
+    }
     sse = wave_sum_f64(sse);
     __shared__ double wsum[NT / 64];
     if (lane == 0) wsum[wave] = sse;
