@@ -7,9 +7,10 @@
 // with a bf16 weight operand computes that unquantized output Y = X . W^T.
 //
 // gfx950 design
-//   * 256x256 output tile per workgroup, BK = 32, 4 waves in a 2x2 grid; each
-//     wave owns 128x128 = 4x4 v_mfma_f32_32x32x16_bf16 blocks (256 fp32
-//     accumulators per lane, held in AGPRs).
+//   * 256x256 output tile per workgroup, BK = 32.  INT4 path: 4 waves in a
+//     2x2 grid, each owning 128x128 = 4x4 v_mfma_f32_32x32x16_bf16 blocks
+//     (256 fp32 accumulators per lane, held in AGPRs).  bf16 path: 8 waves in
+//     a 2x4 grid of 128x64 (two waves per SIMD).
 //   * LDS tiles are [row][4 x 16 B chunks] with an XOR swizzle of the chunk
 //     index that keeps ds_read_b128 of the MFMA fragment pattern free of bank
 //     conflicts (8- and 16-lane phases alike).
@@ -47,16 +48,29 @@
 
 namespace awq {
 
-namespace {
+namespace gemm_detail {
 
 constexpr int BM = kGemmBM;
 constexpr int BN = kGemmBN;
 constexpr int BK = 32;
-constexpr int NT = 256;
 constexpr int kChunks = BK / 8;             // 16-byte chunks per tile row
 constexpr int kSlots = 256 * kChunks;       // 16-byte slots per operand tile (16 KiB)
-constexpr int kDmaPerWave = 4;              // 1 KiB per DMA instruction, 4 KiB per wave
-static_assert(BM == 256 && BN == 256 && NT == 256, "mapping assumes 256x256 tiles, 256 threads");
+static_assert(BM == 256 && BN == 256, "mapping assumes 256x256 tiles");
+
+// Wave grid: 2 waves along M (128 rows each) by WN waves along N.  WN = 2:
+// 4 waves of 128x128 (one per SIMD); WN = 4: 8 waves of 128x64 (two per
+// SIMD, so one wave's waits are covered by the other's MFMAs).
+template <int WN>
+struct Cfg {
+  static constexpr int kWaves = 2 * WN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kTN = 256 / WN;              // wave tile columns
+  static constexpr int kBJ = kTN / 32;              // 32x32 blocks along N per wave
+  static constexpr int kDma = kSlots / 64 / kWaves; // 1 KiB DMA instructions per wave per tile
+  static constexpr int kTPR = kThreads / 256;       // threads per weight row (INT4 dequant)
+  static constexpr int kWPT = 4 / kTPR;             // code words per thread per k-step
+  static constexpr int kFragReads = 4 + kBJ;        // ds_read_b128 per k16 substep
+};
 static_assert(kGroup % BK == 0, "a k-step must not straddle a quantization group");
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -85,6 +99,26 @@ __device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// One wave's share of an operand tile: DPW buffer->LDS copies of 1 KiB.
+template <int DPW>
+__device__ __forceinline__ void dma_tile_wave(rsrc_t r, uint4* dst, const uint32_t (&off)[DPW],
+                                              uint32_t soff) {
+#pragma unroll
+  for (int i = 0; i < DPW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 64 * i), 16, off[i], soff, 0, 0);
+}
+
+// Copy of 16 bytes per lane from a buffer into LDS at dst + 16 * lane.
+__device__ __forceinline__ void dma16(rsrc_t r, float* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint2 ld8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v.x, v.y);
+}
+
 // Swizzle of a row's chunk index: rows r, r+2, r+4, r+6 and rows r, r+4, r+8,
 // r+12 all get different values, so 8-lane and 16-lane phases of a
 // ds_read_b128 that walk consecutive rows at one chunk hit distinct banks.
@@ -95,6 +129,19 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Barrier that waits only for this wave's LDS operations older than its last
+// N (LDS operations of a wave complete in order): the last N are fragment
+// reads for the next step, which need not land before the barrier.
+template <int N>
+__device__ __forceinline__ void barrier_lds_keep() {
+  if constexpr (N == 8)
+    asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 6)
+    asm volatile("s_waitcnt lgkmcnt(6)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_barrier" ::: "memory");
 }
 
 // Tile of workgroup `bid`: ids are dealt round-robin over the 8 XCDs, so give
@@ -141,14 +188,22 @@ __device__ __forceinline__ uint4 dequant8(uint32_t qw, float step, float zero, c
   return r;
 }
 
+template <int WPT>
 struct CodeRegs {
-  uint4 q;            // 32 codes of this thread's row for one k-step
+  uint32_t q[WPT];    // this thread's code words of its row for one k-step
   uint32_t step_bits; // raw; converted when used so the load stays in flight
   uint32_t zero;
 };
 
-template <bool kInt4, bool kInvS>
-__global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __restrict__ inv_s) {
+template <bool kInt4, bool kInvS, int WN>
+__global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
+                                                                    const float* __restrict__ inv_s) {
+  // The body exists only in the device pass; the host pass needs just the
+  // signature to emit the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C_ = Cfg<WN>;
+  constexpr int NW = C_::kWaves, BJ = C_::kBJ, TN = C_::kTN, DPW = C_::kDma;
+  constexpr int TPR = C_::kTPR, WPT = C_::kWPT;
   // Separate objects per stage: the compiler tracks LDS-DMA writes per object.
   __shared__ uint4 sa0[kSlots], sa1[kSlots], sa2[kSlots], sa3[kSlots];
   __shared__ uint4 sb0[kSlots], sb1[kSlots], sb2[kSlots], sb3[kSlots];
@@ -158,7 +213,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, lk = lane >> 5;
 
   int64_t tm, tn;
@@ -167,16 +222,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t G = K / kGroup;
 
-  // DMA mapping: instruction i of wave w fills slots [(4w+i)*64, +64): lane L
-  // -> row 64w + 16i + L/4, physical chunk L%4 = logical chunk ^ swizzle.
-  uint32_t dma_off[kDmaPerWave];
+  // DMA mapping: instruction i of wave w fills slots [(DPW*w+i)*64, +64):
+  // lane L -> row 16*(DPW*w+i) + L/4, physical chunk L%4 = logical ^ swizzle.
+  uint32_t dma_off[DPW];
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const int row = 64 * wave + 16 * i + (lane >> 2);
+  for (int i = 0; i < DPW; ++i) {
+    const int row = 16 * (DPW * wave + i) + (lane >> 2);
     const int chunk = (lane & 3) ^ chunk_swz(row);
     dma_off[i] = (uint32_t)(row * K * 2 + chunk * 16);
   }
-  const int dma_slot = wave * (kDmaPerWave * 64);
+  const int dma_slot = wave * (DPW * 64);
 
   const rsrc_t ra = make_rsrc(p.x + m0 * K, (uint64_t)(M - m0) * K * 2);
   rsrc_t rb, rq, rsc, rz;
@@ -187,36 +242,53 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
   } else {
     rb = make_rsrc(p.w + n0 * K, (uint64_t)(N - n0) * K * 2);
   }
-  const uint32_t q_off = (uint32_t)(t * (K / 2));
-  const uint32_t sc_off = (uint32_t)(t * G * 4);
-  const uint32_t z_off = (uint32_t)(t * G);
+  // INT4 dequant mapping: thread t owns words [wq0, wq0 + WPT) of row brow.
+  const int brow = t / TPR;
+  const int wq0 = (t % TPR) * WPT;
+  const uint32_t q_off = (uint32_t)(brow * (K / 2) + wq0 * 4);
+  const uint32_t sc_off = (uint32_t)(brow * G * 4);
+  const uint32_t z_off = (uint32_t)(brow * G);
 
   auto dma_tile = [&](rsrc_t r, uint4* stage, int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(stage + dma_slot + 64 * i), 16,
-                                               dma_off[i], (uint32_t)(k0 * 2), 0, 0);
+    dma_tile_wave<DPW>(r, stage + dma_slot, dma_off, (uint32_t)(k0 * 2));
   };
-  auto load_codes = [&](CodeRegs& C, int64_t k0) {
-    C.q = ld16(rq, q_off, (uint32_t)(k0 / 2));
+  auto load_codes = [&](CodeRegs<WPT>& C, int64_t k0) {
+    if constexpr (WPT == 4) {
+      const uint4 v = ld16(rq, q_off, (uint32_t)(k0 / 2));
+      C.q[0] = v.x; C.q[1] = v.y; C.q[2] = v.z; C.q[3] = v.w;
+    } else {
+      const uint2 v = ld8(rq, q_off, (uint32_t)(k0 / 2));
+      C.q[0] = v.x; C.q[1] = v.y;
+    }
     const uint32_t g = (uint32_t)(k0 / kGroup);
     C.step_bits = __builtin_amdgcn_raw_buffer_load_b32(rsc, sc_off, g * 4, 0);
     C.zero = __builtin_amdgcn_raw_buffer_load_b8(rz, z_off, g, 0);
   };
-  // Dequantize the codes into row t of a B stage.  The empty asm statements
-  // pin the first use of each loaded register to this point (after the
-  // previous barrier); otherwise the scheduler hoists the conversion up to the
-  // load and the wait for it drains every later prefetch.
-  auto dequant_half = [&](const CodeRegs& C, uint4* stage, int64_t k0, int w0) {
+  // Dequantization of one k-step's codes, one word (8 codes, one 16-byte LDS
+  // write) at a time.  pin() is an empty asm that fixes the first use of the
+  // loaded registers at the start of the step that dequantizes them;
+  // otherwise the scheduler hoists the conversion up to the load and the
+  // wait for it drains every later prefetch.
+  struct Unpacked {
+    uint32_t words[WPT];
+    float step, zero;
+  };
+  auto pin = [&](const CodeRegs<WPT>& C) {
+    Unpacked U;
     uint32_t sbits = C.step_bits, zraw = C.zero;
-    uint32_t words[2] = {w0 == 0 ? C.q.x : C.q.z, w0 == 0 ? C.q.y : C.q.w};
-    asm volatile("" : "+v"(sbits), "+v"(zraw), "+v"(words[0]), "+v"(words[1]));
-    const float step = __uint_as_float(sbits);
-    const float zero = (float)zraw;
 #pragma unroll
-    for (int w = 0; w < 2; ++w)
-      stage[swz(t, w0 + w)] = dequant8<kInvS>(words[w], step, zero,
-                                              kInvS ? inv_s + k0 + 8 * (w0 + w) : nullptr);
+    for (int w = 0; w < WPT; ++w) U.words[w] = C.q[w];
+    asm volatile("" : "+v"(sbits), "+v"(zraw));
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) asm volatile("" : "+v"(U.words[w]));
+    U.step = __uint_as_float(sbits);
+    U.zero = (float)zraw;
+    return U;
+  };
+  auto dequant_word = [&](const Unpacked& U, uint4* stage, int64_t k0, int w) {
+    const int c = wq0 + w;   // chunk of the row = code word index within the k-step
+    stage[swz(brow, c)] = dequant8<kInvS>(U.words[w], U.step, U.zero,
+                                          kInvS ? inv_s + k0 + 8 * c : nullptr);
   };
   // Wait until this wave's DMA into `stage` has landed (the compiler inserts
   // the exact vmcnt for a read of an object with a pending DMA write).
@@ -225,35 +297,36 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
     asm volatile("" ::"v"(v));
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][BJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < BJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   struct Frags {
-    bf16x8 a[4], b[4];
+    bf16x8 a[4], b[BJ];
   };
   auto read_frags = [&](Frags& F, const uint4* la, const uint4* lb, int s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       F.a[i] = __builtin_bit_cast(bf16x8, la[swz(wm * 128 + i * 32 + lr, 2 * s + lk)]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      F.b[j] = __builtin_bit_cast(bf16x8, lb[swz(wn * 128 + j * 32 + lr, 2 * s + lk)]);
+    for (int j = 0; j < BJ; ++j)
+      F.b[j] = __builtin_bit_cast(bf16x8, lb[swz(wn * TN + j * 32 + lr, 2 * s + lk)]);
   };
-  auto mfma16 = [&](const Frags& F) {
+  // Half of the wave's blocks (rows i = 2h, 2h+1).
+  auto mfma_half = [&](const Frags& F, int h) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 2 * h; i < 2 * h + 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < BJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[i], F.b[j], acc[i][j], 0, 0, 0);
   };
 
   const int64_t KT = K / BK;   // multiple of 4 (K is a multiple of 128)
-  CodeRegs C[2];
+  CodeRegs<WPT> C[2];
   Frags F0, F1;
 
   // Prologue: A(0..2) [and bf16 B(0..2)] in flight; INT4 B(0), B(1)
@@ -264,10 +337,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
   if constexpr (kInt4) {
     load_codes(C[0], 0);
     load_codes(C[1], BK);
-    dequant_half(C[0], SB[0], 0, 0);
-    dequant_half(C[0], SB[0], 0, 2);
-    dequant_half(C[1], SB[1], BK, 0);
-    dequant_half(C[1], SB[1], BK, 2);
+    {
+      const Unpacked U0 = pin(C[0]);
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) dequant_word(U0, SB[0], 0, w);
+      const Unpacked U1 = pin(C[1]);
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) dequant_word(U1, SB[1], BK, w);
+    }
     load_codes(C[0], 2 * BK);
   } else {
     dma_tile(rb, SB[0], 0);
@@ -281,29 +358,72 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
   barrier_lds();
   read_frags(F0, SA[0], SB[0], 0);
 
-  // One k-step; every stage index is a compile-time constant.  The loads are
-  // issued unconditionally (also past the end of K, where they read other
-  // rows' data or zeros into stages that are never read), so the compiler's
-  // wait counts are exact on every path.
+  // Interleave MFMAs with other work in the current scheduling region:
+  // nm groups of {1 MFMA, v VALU, d DS-read}.
+  auto interleave = [&](auto NM, auto V, auto D) {
+    constexpr int nm = decltype(NM)::value, v = decltype(V)::value, d = decltype(D)::value;
+#pragma unroll
+    for (int q = 0; q < nm; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
+      if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x002, v, 0);   // VALU
+      if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);   // DS read
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using IH = std::integral_constant<int, 2 * BJ>;        // MFMAs per half substep
+  using IS = std::integral_constant<int, 4 * BJ>;        // MFMAs per substep
+  // VALU per MFMA for the dequant words placed in a region
+  using IV1 = std::integral_constant<int, (WPT / 2) * 40 / (4 * BJ)>;
+  using IV2 = std::integral_constant<int, (WPT / 2) * 40 / (2 * BJ)>;
+
+  // One k-step (the loads are issued unconditionally, also past the end of K,
+  // where they read other rows' data or zeros into stages that are never
+  // read, so the compiler's wait counts are exact on every path).
   auto step = [&](int64_t k, auto I) {
     constexpr int i = decltype(I)::value;      // k % 4
     dma_tile(ra, SA[(i + 3) & 3], (k + 3) * BK);
     if constexpr (kInt4) {
+      uint4* const bq = SB[(i + 2) & 3];
+      const int64_t kq = (k + 2) * BK;
+      const Unpacked U = pin(C[i & 1]);      // codes of step k+2
       load_codes(C[(i + 1) & 1], (k + 3) * BK);
+      read_frags(F1, SA[i], SB[i], 1);
+      mfma_half(F0, 0);
+      mfma_half(F0, 1);
+#pragma unroll
+      for (int w = 0; w < WPT / 2; ++w) dequant_word(U, bq, kq, w);
+      interleave(IS{}, IV1{}, I0{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(F1, 0);
+#pragma unroll
+      for (int w = WPT / 2; w < WPT; ++w) dequant_word(U, bq, kq, w);
+      own_dma_done(SA[(i + 2) & 3]);
+      interleave(IH{}, IV2{}, I0{});
+      // Every LDS write and DMA-completion read of this step is issued above;
+      // the fragment reads below are the wave's youngest LDS operations.
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(F1, 1);
+      read_frags(F0, SA[(i + 1) & 3], SB[(i + 1) & 3], 0);
+      interleave(IH{}, I0{}, I1{});
+      __builtin_amdgcn_sched_barrier(0);
+      barrier_lds_keep<C_::kFragReads>();
     } else {
       dma_tile(rb, SB[(i + 3) & 3], (k + 3) * BK);
+      read_frags(F1, SA[i], SB[i], 1);
+      mfma_half(F0, 0);
+      mfma_half(F0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(F1, 0);
+      own_dma_done(SA[(i + 2) & 3]);
+      own_dma_done(SB[(i + 2) & 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(F1, 1);
+      read_frags(F0, SA[(i + 1) & 3], SB[(i + 1) & 3], 0);
+      interleave(IH{}, I0{}, I1{});
+      __builtin_amdgcn_sched_barrier(0);
+      barrier_lds_keep<0>();
     }
-    read_frags(F1, SA[i], SB[i], 1);
-    mfma16(F0);
-    if constexpr (kInt4) dequant_half(C[i & 1], SB[(i + 2) & 3], (k + 2) * BK, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma16(F1);
-    if constexpr (kInt4) dequant_half(C[i & 1], SB[(i + 2) & 3], (k + 2) * BK, 2);
-    read_frags(F0, SA[(i + 1) & 3], SB[(i + 1) & 3], 0);
-    __builtin_amdgcn_sched_barrier(0);
-    own_dma_done(SA[(i + 2) & 3]);
-    if constexpr (!kInt4) own_dma_done(SB[(i + 2) & 3]);
-    barrier_lds();
   };
 
   for (int64_t k = 0; k < KT; k += 4) {
@@ -316,14 +436,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
   // Epilogue.  32x32 block layout: lane holds column (lane & 31) and rows
   // 8*(r/4) + 4*(lane/32) + r%4 for accumulator register r.
   const int64_t row0 = wm * 128 + 4 * lk;        // within the tile
-  const int64_t col0 = n0 + wn * 128 + lr;
   if (p.y != nullptr) {
     // Rows past M fall outside the buffer resource and are dropped.
     const rsrc_t ro = make_rsrc(p.y + m0 * N + n0, ((uint64_t)(M - m0) * N - n0) * 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (n0 + wn * 128 + j * 32 + lr < N) {
-        const uint32_t cbase = (uint32_t)((row0 * N + wn * 128 + j * 32 + lr) * 4);
+    for (int j = 0; j < BJ; ++j) {
+      if (n0 + wn * TN + j * 32 + lr < N) {
+        const uint32_t cbase = (uint32_t)((row0 * N + wn * TN + j * 32 + lr) * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_barrier(0);
@@ -337,34 +456,50 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
     }
   }
   if (p.partials != nullptr) {
-    // Sum of (acc - y_ref)^2.  The wave's 128 x 128 block of y_ref is staged
+    // Sum of (acc - y_ref)^2.  The wave's 128 x TN block of y_ref is staged
     // through LDS (the k-loop's stage buffers are free now) by the buffer
-    // unit, 64 rows at a time, so the whole block is in flight at once; each
-    // wave copies and reads only its own rows, so no barrier is needed
+    // unit, 64 rows at a time, so a whole half-block is in flight at once;
+    // each wave copies and reads only its own rows, so no barrier is needed
     // between the copy and the reads.  Rows past M read 0 through the buffer
     // resource (their accumulators are 0 too); columns past N are masked.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // stray prefetches into LDS
     barrier_lds();                                      // every wave is done with the stages
-    float* const reg_w[8] = {(float*)sa0, (float*)sa1, (float*)sa2, (float*)sa3,
-                             (float*)sb0, (float*)sb1, (float*)sb2, (float*)sb3};
-    float* const mine0 = wave == 0 ? reg_w[0] : wave == 1 ? reg_w[2] : wave == 2 ? reg_w[4] : reg_w[6];
-    float* const mine1 = wave == 0 ? reg_w[1] : wave == 1 ? reg_w[3] : wave == 2 ? reg_w[5] : reg_w[7];
+    // The wave's 16 KiB (8 waves) or 2 x 16 KiB (4 waves) of LDS for a phase.
+    constexpr int kArrs = 8 / NW;
+    auto arr = [&](int a) -> float* {
+      switch (a & 7) {
+        case 0: return (float*)sa0;
+        case 1: return (float*)sa1;
+        case 2: return (float*)sa2;
+        case 3: return (float*)sa3;
+        case 4: return (float*)sb0;
+        case 5: return (float*)sb1;
+        case 6: return (float*)sb2;
+        default: return (float*)sb3;
+      }
+    };
+    float* const mine0 = arr(wave * kArrs);
+    float* const mine1 = arr(wave * kArrs + kArrs - 1);
+    constexpr int kRowsPerArr = 16384 / 4 / TN;         // rows of a wave's block per array
+    constexpr int kLanesPerRow = TN / 4;                // 16-byte pieces per row
+    constexpr int kRowsPerDma = 64 / kLanesPerRow;
+    constexpr int kDmaPerPhase = 64 / kRowsPerDma;
     const rsrc_t ry = make_rsrc(p.y_ref + m0 * N + n0, ((uint64_t)(M - m0) * N - n0) * 4);
-    // DMA q of a phase: rows 2q, 2q+1 of the phase's 64 rows; lane L -> row
-    // 2q + L/32, columns 4*(L%32) .. +3 of the wave's 128 columns.
-    const uint32_t ybase = (uint32_t)((((int64_t)wm * 128 + (lane >> 5)) * N + wn * 128 + 4 * (lane & 31)) * 4);
-    bool col_ok[4];
+    const uint32_t ybase = (uint32_t)((((int64_t)wm * 128 + lane / kLanesPerRow) * N + wn * TN +
+                                       4 * (lane % kLanesPerRow)) * 4);
+    bool col_ok[BJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) col_ok[j] = n0 + wn * 128 + j * 32 + lr < N;
+    for (int j = 0; j < BJ; ++j) col_ok[j] = n0 + wn * TN + j * 32 + lr < N;
     double sse = 0.0;
 #pragma unroll
     for (int phase = 0; phase < 2; ++phase) {
       if (phase == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of phase 0 done
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
-        float* dst = (q < 16 ? mine0 : mine1) + (q & 15) * 256;
-        const uint32_t roff = (uint32_t)(((int64_t)phase * 64 + 2 * q) * N * 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void*)dst, 16, ybase + roff, 0, 0, 0);
+      for (int q = 0; q < kDmaPerPhase; ++q) {
+        const int rr = q * kRowsPerDma;                   // first row of this DMA within the phase
+        float* dst = (rr < kRowsPerArr ? mine0 : mine1) + (rr % kRowsPerArr) * TN;
+        const uint32_t roff = (uint32_t)(((int64_t)phase * 64 + rr) * N * 4);
+        dma16(ry, dst, ybase + roff);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
@@ -372,12 +507,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
         const int i = 2 * phase + ii;
         double dpart = 0.0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < BJ; ++j) {
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rho = ii * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);   // row within the phase
-            const float yv = (rho < 32 ? mine0 : mine1)[(rho & 31) * 128 + j * 32 + lr];
+            const float yv = (rho < kRowsPerArr ? mine0 : mine1)[(rho % kRowsPerArr) * TN + j * 32 + lr];
             float d = acc[i][j][r] - yv;
             d = col_ok[j] ? d : 0.f;
             dpart += (double)d * (double)d;
@@ -387,14 +522,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p, const float* __re
       }
     }
     sse = wave_sum_f64(sse);
-    __shared__ double wsum[NT / 64];
+    __shared__ double wsum[NW];
     if (lane == 0) wsum[wave] = sse;
     __syncthreads();
-    if (t == 0) p.partials[tm * p.tiles_n + tn] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    if (t == 0) {
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += wsum[w];
+      p.partials[tm * p.tiles_n + tn] = tot;
+    }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
-}  // namespace
+}  // namespace gemm_detail
+
+using namespace gemm_detail;
 
 hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream) {
   if (op.M == 0 || op.N == 0) return hipSuccess;
@@ -413,12 +556,14 @@ hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream) {
   p.tiles_m = ceil_div(op.M, BM);
   p.tiles_n = ceil_div(op.N, BN);
   const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n);
+  // bf16 operand: 8 waves (two per SIMD) measured faster; INT4: the dequant
+  // VALU work favours 4 waves with 128x128 tiles each.
   if (op.qweight == nullptr)
-    gemm_kernel<false, false><<<blocks, NT, 0, stream>>>(p, nullptr);
+    gemm_kernel<false, false, 4><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
   else if (op.inv_s != nullptr)
-    gemm_kernel<true, true><<<blocks, NT, 0, stream>>>(p, op.inv_s);
+    gemm_kernel<true, true, 2><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, op.inv_s);
   else
-    gemm_kernel<true, false><<<blocks, NT, 0, stream>>>(p, nullptr);
+    gemm_kernel<true, false, 2><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, nullptr);
   return hipGetLastError();
 }
 
