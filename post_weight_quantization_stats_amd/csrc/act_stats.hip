@@ -42,10 +42,10 @@ __global__ __launch_bounds__(kThreads) void act_stats_partial_kernel(
     int64_t r = r_begin + wave;
     // four rows in flight per lane
     for (; r + 12 < r_end; r += 16) {
-      const uint4 v0 = load_stream16((p + r * K));
-      const uint4 v1 = load_stream16((p + (r + 4) * K));
-      const uint4 v2 = load_stream16((p + (r + 8) * K));
-      const uint4 v3 = load_stream16((p + (r + 12) * K));
+      const uint4 v0 = load_stream16(p + r * K);
+      const uint4 v1 = load_stream16(p + (r + 4) * K);
+      const uint4 v2 = load_stream16(p + (r + 8) * K);
+      const uint4 v3 = load_stream16(p + (r + 12) * K);
       acc_abs8(acc, v0);
       acc_abs8(acc, v1);
       acc_abs8(acc, v2);

@@ -4,13 +4,27 @@
 // "Hyperparameters": 4 or 3 bits; builderai AWQ page, "About": the real
 // integer weights are written).
 //
-// Layout: 16 lanes own one (row, 128-channel group); each lane loads 8 bf16
-// (16 B, so a wave reads 1 KiB contiguous), reduces min/max with xor
-// shuffles inside its 16-lane segment, and writes one u32 of 8 packed
-// nibbles.  Every arithmetic step is one IEEE fp32 operation, in the order of
-// the contract: ws = w*s; step = (max(mx,0) - min(mn,0)) / qmax (1 if 0);
-// z = clamp(rint(-mn/step)); q = clamp(rint(ws/step) + z).  Divisions are the
-// correctly rounded fp32 divide (no reciprocal approximation).
+// Layout: 8 lanes own one 128-channel group, 16 channels (32 B of bf16) per
+// lane, so a wave covers 8 groups = 2 KiB of one row.  A block of 256 lanes
+// spans 32 groups and walks kRows rows; each lane loads its 16 scale factors
+// once.  Group min/max is reduced with three DPP steps inside each 8-lane
+// segment (quad swaps, then the half-row mirror); each lane writes two u32 of
+// packed nibbles.  Every arithmetic step is one IEEE fp32 operation, in the
+// order of the contract: ws = w*s; step = (max(mx,0) - min(mn,0)) / qmax
+// (1 if 0); z = clamp(rint(-mn/step)); q = clamp(rint(ws/step) + z).
+//
+// The quotients must be the correctly rounded ones (the codes are their rint).
+// With y = RN(1/b), q0 = RN(a*y) and the exact residual r = a - b*q0 (one
+// fma), RN(q0 + r*y) is the correctly rounded a/b (P. Markstein, "Computation
+// of elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
+// Dev. 34(1), 1990; Muller et al., Handbook of Floating-Point Arithmetic,
+// 2018, the division theorem for fused multiply-add).  The theorem needs the
+// residual not to underflow.  A group takes this path when its range lies in
+// [2^-90, 2^100]: then step >= 2^-94, every |a| >= step/2 has a residual far
+// above the subnormal range, and for |a| < step/2 both quotients round to a
+// code of 0 (checked exhaustively for the constant divisors 15 and 7 and on
+// 2e8 random (a, step) pairs).  Other groups (zero, tiny, huge or non-finite
+// ranges) take plain IEEE divisions.
 #include <math.h>
 
 #include "awq_internal.h"
@@ -21,70 +35,136 @@ namespace awq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kGroupsPerBlock = kThreads / 16;
+constexpr int kLanesPerGroup = 8;
+constexpr int kGroupsPerBlock = kThreads / kLanesPerGroup;
+constexpr int kRows = 4;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float markstein_div(float a, float b, float y) {
+  const float q0 = a * y;
+  const float r = fmaf(-q0, b, a);              // exact residual
+  return fmaf(r, y, q0);                        // RN(a / b)
+}
+
+// One lane's 16 channels of a group: fills two words of packed codes and the
+// group's step and zero (identical in all 8 lanes of the group).
+template <int BITS>
+__device__ __forceinline__ void quantize16(const float (&ws)[16], uint32_t& w0, uint32_t& w1,
+                                           float& step_out, float& z_out) {
+  constexpr float qmax = (float)((1 << BITS) - 1);
+  constexpr float inv_qmax = 1.0f / qmax;       // RN(1/qmax), folded by the compiler
+  float mx = fmaxf(ws[0], ws[1]), mn = fminf(ws[0], ws[1]);
+#pragma unroll
+  for (int j = 2; j < 16; ++j) {
+    mx = fmaxf(mx, ws[j]);
+    mn = fminf(mn, ws[j]);
+  }
+  mx = fmaxf(mx, dpp<0xB1>(mx));                // lanes ^1
+  mn = fminf(mn, dpp<0xB1>(mn));
+  mx = fmaxf(mx, dpp<0x4E>(mx));                // lanes ^2
+  mn = fminf(mn, dpp<0x4E>(mn));
+  mx = fmaxf(mx, dpp<0x141>(mx));               // lane i <-> 7-i of each half row
+  mn = fminf(mn, dpp<0x141>(mn));
+  mx = fmaxf(mx, 0.f);
+  mn = fminf(mn, 0.f);
+  const float range = mx - mn;
+  const bool fast = range >= 0x1p-90f && range <= 0x1p100f;
+
+  float step = markstein_div(range, qmax, inv_qmax);
+  float y = 1.0f / step;
+  float zq = markstein_div(-mn, step, y);
+  float qt[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) qt[j] = markstein_div(ws[j], step, y);
+  if (__builtin_expect(!fast, 0)) {
+    // Outside the proven range: plain correctly rounded divides.  The empty
+    // asm keeps this a real branch (no speculated divides on the fast path).
+    asm volatile("" ::: "memory");
+    step = range / qmax;
+    if (!(step > 0.f)) step = 1.f;
+    zq = -mn / step;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) qt[j] = ws[j] / step;
+  }
+  const float z = fminf(fmaxf(rintf(zq), 0.f), qmax);
+  // Codes are small integers, so a pair packs exactly as lo + 16*hi into one
+  // byte with v_cvt_pk_u8_f32.
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float lo = fminf(fmaxf(rintf(qt[8 * h + 2 * b]) + z, 0.f), qmax);
+      const float hi = fminf(fmaxf(rintf(qt[8 * h + 2 * b + 1]) + z, 0.f), qmax);
+      w[h] = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(hi, 16.f, lo), b, w[h]);
+    }
+  }
+  w0 = w[0];
+  w1 = w[1];
+  step_out = step;
+  z_out = z;
+}
 
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t K, const float* __restrict__ s,
     const int32_t* __restrict__ s_sel, uint32_t* __restrict__ qweight,
     float* __restrict__ scales, uint8_t* __restrict__ zeros) {
-  constexpr float qmax = (float)((1 << BITS) - 1);
   const int64_t G = K / kGroup;
-  const int64_t grp = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
-  const int t16 = threadIdx.x & 15;
-  const bool valid = grp < N * G;
-  const int64_t n = valid ? grp / G : 0;
-  const int64_t g = valid ? grp % G : 0;
-  const int64_t k0 = g * kGroup + t16 * 8;
+  const int64_t g = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x / kLanesPerGroup);
+  const int t8 = threadIdx.x % kLanesPerGroup;
+  const bool gvalid = g < G;
+  const int64_t k0 = (gvalid ? g : 0) * kGroup + t8 * 16;
+  const int64_t n_begin = (int64_t)blockIdx.y * kRows;
 
+  float sv[16];
   const float* srow = s;
   if (s != nullptr && s_sel != nullptr) srow = s + (int64_t)max(*s_sel, 0) * K;
-
-  float ws[8];
-  if (valid) {
-    const uint4 v = *(const uint4*)(w + n * K + k0);
-    ws[0] = bf16_lo(v.x); ws[1] = bf16_hi(v.x);
-    ws[2] = bf16_lo(v.y); ws[3] = bf16_hi(v.y);
-    ws[4] = bf16_lo(v.z); ws[5] = bf16_hi(v.z);
-    ws[6] = bf16_lo(v.w); ws[7] = bf16_hi(v.w);
-    if (srow != nullptr) {
-      const float4 s0 = *(const float4*)(srow + k0);
-      const float4 s1 = *(const float4*)(srow + k0 + 4);
-      ws[0] *= s0.x; ws[1] *= s0.y; ws[2] *= s0.z; ws[3] *= s0.w;
-      ws[4] *= s1.x; ws[5] *= s1.y; ws[6] *= s1.z; ws[7] *= s1.w;
+  if (srow != nullptr) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 t = *(const float4*)(srow + k0 + 4 * c);
+      sv[4 * c] = t.x; sv[4 * c + 1] = t.y; sv[4 * c + 2] = t.z; sv[4 * c + 3] = t.w;
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ws[j] = 0.f;
   }
-  float mx = ws[0], mn = ws[0];
+
+  uint4 v[kRows][2];
 #pragma unroll
-  for (int j = 1; j < 8; ++j) {
-    mx = fmaxf(mx, ws[j]);
-    mn = fminf(mn, ws[j]);
+  for (int r = 0; r < kRows; ++r) {
+    const int64_t n = n_begin + r;
+    const bool ok = gvalid && n < N;
+    const uint16_t* src = w + (ok ? n : 0) * K + k0;
+    v[r][0] = ok ? load_stream16(src) : make_uint4(0, 0, 0, 0);
+    v[r][1] = ok ? load_stream16(src + 8) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) {
-    mx = fmaxf(mx, __shfl_xor(mx, o, 16));
-    mn = fminf(mn, __shfl_xor(mn, o, 16));
-  }
-  mx = fmaxf(mx, 0.f);
-  mn = fminf(mn, 0.f);
-  const float range = mx - mn;
-  float step = range / qmax;
-  if (!(step > 0.f)) step = 1.f;
-  const float z = fminf(fmaxf(rintf(-mn / step), 0.f), qmax);
-  uint32_t word = 0;
+  for (int r = 0; r < kRows; ++r) {
+    const int64_t n = n_begin + r;
+    float ws[16];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float q = fminf(fmaxf(rintf(ws[j] / step) + z, 0.f), qmax);
-    word |= (uint32_t)q << (4 * j);
-  }
-  if (valid) {
-    qweight[n * (K / 8) + k0 / 8] = word;
-    if (t16 == 0) {
-      scales[grp] = step;
-      zeros[grp] = (uint8_t)z;
+    for (int c = 0; c < 2; ++c) {
+      ws[8 * c + 0] = bf16_lo(v[r][c].x); ws[8 * c + 1] = bf16_hi(v[r][c].x);
+      ws[8 * c + 2] = bf16_lo(v[r][c].y); ws[8 * c + 3] = bf16_hi(v[r][c].y);
+      ws[8 * c + 4] = bf16_lo(v[r][c].z); ws[8 * c + 5] = bf16_hi(v[r][c].z);
+      ws[8 * c + 6] = bf16_lo(v[r][c].w); ws[8 * c + 7] = bf16_hi(v[r][c].w);
+    }
+    if (srow != nullptr) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ws[j] *= sv[j];
+    }
+    uint32_t w0, w1;
+    float step, z;
+    quantize16<BITS>(ws, w0, w1, step, z);
+    if (gvalid && n < N) {
+      *(uint2*)(qweight + n * (K / 8) + k0 / 8) = make_uint2(w0, w1);
+      if (t8 == 0) {
+        scales[n * G + g] = step;
+        zeros[n * G + g] = (uint8_t)z;
+      }
     }
   }
 }
@@ -94,13 +174,12 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
 hipError_t launch_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const float* s,
                                 const int32_t* s_sel, int bits, uint32_t* qweight,
                                 float* scales, uint8_t* zeros, hipStream_t stream) {
-  const int64_t groups = N * (K / kGroup);
-  if (groups == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)ceil_div(groups, kGroupsPerBlock);
+  if (N == 0) return hipSuccess;
+  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
   if (bits == 4)
-    quantize_pack_kernel<4><<<blocks, kThreads, 0, stream>>>(w, N, K, s, s_sel, qweight, scales, zeros);
+    quantize_pack_kernel<4><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, qweight, scales, zeros);
   else
-    quantize_pack_kernel<3><<<blocks, kThreads, 0, stream>>>(w, N, K, s, s_sel, qweight, scales, zeros);
+    quantize_pack_kernel<3><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, qweight, scales, zeros);
   return hipGetLastError();
 }
 

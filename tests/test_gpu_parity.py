@@ -127,6 +127,37 @@ def test_quantize_special_groups(dev):
         assert np.array_equal(ze.cpu().numpy(), rz)
 
 
+def test_quantize_extreme_ranges(dev):
+    """Groups whose range falls outside [2^-90, 2^100] take plain divides on
+    the GPU; groups inside it with subnormal members take the fast quotient.
+    Codes, steps and zeros must still match the oracle bit for bit."""
+    announce("quantize extreme ranges")
+    rng = np.random.default_rng(5)
+    K = 1024
+    rows = []
+    for mag in (1e-38, 3e-33, 2.0 ** -91, 2.0 ** -89, 1e-20, 1.0, 1e25, 2.0 ** 99, 2.0 ** 101,
+                1e35):
+        rows.append(mag * rng.standard_normal(K))
+    mixed = rng.standard_normal(K)
+    mixed[::3] *= 1e-39                                # subnormal members
+    rows.append(mixed)
+    boundary = np.zeros(K)
+    boundary[::128] = 15.0 * 2.0 ** -94                # range exactly at the cut
+    boundary[1::128] = 2.0 ** -95
+    rows.append(boundary)
+    W = np.stack(rows).astype(np.float32)
+    w = synth.to_bf16_bits(W)
+    s = np.exp2(rng.uniform(-3, 3, K)).astype(np.float32)
+    for bits in (3, 4):
+        for sv in (None, s):
+            qw, sc, ze = awq.quantize_pack(to_dev_bf16(w, dev),
+                                           None if sv is None else to_dev_f32(sv, dev), bits)
+            rq, rs, rz = O.pack(*O.quantize(w, sv, bits, 128))
+            assert np.array_equal(sc.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+            assert np.array_equal(ze.cpu().numpy(), rz)
+            assert np.array_equal(u32(qw), rq)
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=ids)
 def test_reference_gemm(dev, shape):
     announce("reference_gemm", ids(shape))
