@@ -64,6 +64,130 @@ def committed_traffic():
         return None
 
 
+# ---- rocprofv3 output summaries (run on the host after a profiled bench) ----
+
+KERNEL_LABELS = [
+    ("gemm_kernel<true, true", "w4a16_gemm_sse (INT4 operand, 1/s folded, squared-error epilogue)"),
+    ("gemm_kernel<true, false", "w4a16_gemm (INT4 operand, plain)"),
+    ("gemm_kernel<false", "reference_gemm (bf16 operand, fp32 Y_ref)"),
+    ("decode_gemm", "decode W4A16 GEMM"),
+    ("act_stats_partial", "act_stats partial sums"),
+    ("act_stats_finalize", "act_stats finalize"),
+    ("quantize_pack_kernel", "quantize_pack"),
+    ("scales_r_kernel", "candidate scales (powers)"),
+    ("scales_norm_kernel", "candidate scales (normalise)"),
+    ("loss_reduce_kernel", "loss reduce"),
+    ("argmin_kernel", "argmin"),
+    ("select_row_kernel", "select s*"),
+    ("fill_f64_kernel", "fill"),
+]
+
+
+def _label(name: str) -> str:
+    for key, label in KERNEL_LABELS:
+        if key in name:
+            return label
+    return name[:60]
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d: str, suffix: str) -> str:
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def _bench_line(log_path):
+    try:
+        with open(log_path) as f:
+            for line in f:
+                if line.startswith("{"):
+                    return json.loads(line)
+    except OSError:
+        pass
+    return None
+
+
+def summarize_trace(trace_dir: str, command: str, log_path: str | None) -> str:
+    rows = _read_csv(_find(trace_dir, "kernel_stats.csv"))
+    out = ["# rocprofv3 kernel-trace statistics", f"# command: {command}", ""]
+    out.append(f"{'kernel':<62} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}")
+    for r in rows:
+        name = r["Name"]
+        if "awq::" not in name:
+            continue
+        out.append(f"{_label(name):<62} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.1f} "
+                   f"{float(r['MinNs']) / 1e3:>10.1f} {float(r['MaxNs']) / 1e3:>10.1f} "
+                   f"{float(r['Percentage']):>6.2f}")
+    line = _bench_line(log_path) if log_path else None
+    if line:
+        rf = line["roofline"]
+        out += ["", "# same run, bench.py HIP-event figures:",
+                f"search ms/layer: {line['ms_per_step']:.2f}",
+                f"w4a16_gemm_sse ms_per_launch (events): {rf['ms_per_launch']:.3f}",
+                f"kernel_source_hash: {rf['kernel_source_hash']}"]
+        for k, v in line["kernels"].items():
+            out.append(f"{k}: " + ", ".join(f"{a}={b:.4g}" for a, b in v.items()))
+    return "\n".join(out) + "\n"
+
+
+def _per_kernel_counter(rows, counter):
+    """Counter value per dispatch, grouped by kernel label."""
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, commands: str, M: int, K: int) -> str:
+    """HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the counter reads for the calibration copy (bf16 X ->
+    fp32: 2MK bytes read, 4MK bytes written)."""
+    fetch = _per_kernel_counter(_read_csv(_find(fetch_dir, "counter_collection.csv")), "FETCH_SIZE")
+    write = _per_kernel_counter(_read_csv(_find(write_dir, "counter_collection.csv")), "WRITE_SIZE")
+
+    def calib(per, nbytes):
+        cands = [(max(v), k) for k, v in per.items() if "copy" in k and "awq::" not in k]
+        if not cands:
+            raise SystemExit("calibration copy kernel not found")
+        kib, _ = max(cands)
+        return nbytes / (kib * 1024.0), kib
+
+    f_read, kib_r = calib(fetch, 2.0 * M * K)
+    f_write, kib_w = calib(write, 4.0 * M * K)
+    out = ["# rocprofv3 HBM traffic per dispatch (FETCH_SIZE and WRITE_SIZE, separate runs)",
+           f"# commands: {commands}",
+           f"# calibration copy (bf16 X -> fp32, M={M} K={K}): FETCH_SIZE {kib_r:.0f} KiB for "
+           f"{2 * M * K} B read -> read factor {f_read:.4f}; WRITE_SIZE {kib_w:.0f} KiB for "
+           f"{4 * M * K} B written -> write factor {f_write:.4f}", ""]
+    gemm_bytes = None
+    for name in sorted(set(fetch) | set(write), key=_label):
+        if "awq::" not in name:
+            continue
+        fr = fetch.get(name, [float("nan")])
+        wr = write.get(name, [float("nan")])
+        rb = float(np.median(fr)) * 1024.0 * f_read
+        wb = float(np.median(wr)) * 1024.0 * f_write
+        out.append(f"{_label(name):<62} read {rb / 2**20:>10.1f} MiB  write {wb / 2**20:>9.1f} MiB  "
+                   f"(dispatches {len(fr)}/{len(wr)})")
+        if "gemm_kernel<true, true" in name:
+            gemm_bytes = rb + wb
+    out.append("")
+    out.append(f"kernel_source_hash: {gemm_source_hash()}")
+    if gemm_bytes is not None:
+        out.append(f"hbm_bytes_per_launch: {gemm_bytes:.0f}")
+    return "\n".join(out) + "\n"
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -117,7 +241,27 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-m", type=int, default=2048)
     ap.add_argument("--cpu-n", type=int, default=1024)
+    ap.add_argument("--summarize-trace", metavar="DIR", default=None,
+                    help="write a summary of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="write HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE runs and exit")
+    ap.add_argument("--bench-log", default=None, help="log of the profiled bench run")
+    ap.add_argument("--profile-command", default="", help="command text recorded in a summary")
+    ap.add_argument("--summary-out", default=None)
     args = ap.parse_args()
+
+    if args.summarize_trace or args.summarize_pmc:
+        import synth
+        spec = synth.layer_spec(args.workload, args.layer)
+        if args.summarize_trace:
+            text = summarize_trace(args.summarize_trace, args.profile_command, args.bench_log)
+        else:
+            text = summarize_pmc(*args.summarize_pmc, args.profile_command, spec.M, spec.K)
+        if args.summary_out:
+            with open(args.summary_out, "w") as f:
+                f.write(text)
+        print(text, end="")
+        return 0
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
