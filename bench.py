@@ -70,7 +70,8 @@ KERNEL_LABELS = [
     ("gemm_kernel<true, true", "w4a16_gemm_sse (INT4 operand, 1/s folded, squared-error epilogue)"),
     ("gemm_kernel<true, false", "w4a16_gemm (INT4 operand, plain)"),
     ("gemm_kernel<false", "reference_gemm (bf16 operand, fp32 Y_ref)"),
-    ("decode_gemm", "decode W4A16 GEMM"),
+    ("decode_gemm", "decode W4A16 GEMM (M <= 16)"),
+    ("decode_reduce", "decode split-K reduce"),
     ("act_stats_partial", "act_stats partial sums"),
     ("act_stats_finalize", "act_stats finalize"),
     ("quantize_pack_kernel", "quantize_pack"),
@@ -205,6 +206,49 @@ def event_time_ms(fn, reps: int, stream) -> float:
     return start.elapsed_time(end) / reps
 
 
+def bench_decode(awq, dev, stream, reps: int = 100) -> dict:
+    """Decode-shaped W4A16 contraction on the Llama-3-8B block's layers
+    (M = 1 and 16 tokens, random packed INT4 weights).  Each figure is the
+    average over `reps` launches captured in one HIP graph and replayed, so
+    host launch overhead is not in it."""
+    import torch
+
+    import synth
+    out = {}
+    for name in ("qkv", "o_proj", "gate_up", "down"):
+        spec = synth.layer_spec("llama3_8b_block", name)
+        N, K = spec.N, spec.K
+        gen = torch.Generator(device=dev).manual_seed(7)
+        qw = torch.randint(-2 ** 31, 2 ** 31 - 1, (N, K // 8), dtype=torch.int32, device=dev,
+                           generator=gen)
+        sc = torch.rand((N, K // 128), device=dev, generator=gen) * 0.003 + 0.001
+        ze = torch.randint(0, 16, (N, K // 128), dtype=torch.uint8, device=dev, generator=gen)
+        for M in (1, 16):
+            a = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            need = awq.workspace_size(awq.OP_DECODE_GEMM, M, N, K)
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+            def fn():
+                awq.decode_gemm(a, qw, sc, ze, 4, out=y, workspace=ws)
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            ms = event_time_ms(g.replay, 5, stream) / reps
+            nbytes = N * K / 2 + 5.0 * N * K / 128 + 2.0 * M * K + 4.0 * M * N
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            out[f"{name}_M{M}"] = {"N": N, "K": K, "us": ms * 1e3, "gbs": gbs,
+                                   "frac_hbm_peak": gbs / PEAK_HBM_GBS, "bytes": nbytes}
+            log(f"decode {name} M={M} N={N} K={K}: {ms * 1e3:.2f} us = {gbs:.0f} GB/s")
+            del g
+    return out
+
+
 def cpu_baseline(x_bits, w_bits, spec, m_sample: int, n_sample: int) -> dict:
     """Oracle (numpy fp64) on a token prefix x output-row prefix; each phase is
     scaled to the full layer by the dimension it is linear in."""
@@ -239,6 +283,7 @@ def main() -> int:
     ap.add_argument("--layer", default=None)
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped GEMM figures")
     ap.add_argument("--cpu-m", type=int, default=2048)
     ap.add_argument("--cpu-n", type=int, default=1024)
     ap.add_argument("--summarize-trace", metavar="DIR", default=None,
@@ -371,6 +416,8 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if not args.no_decode:
+        result["kernels"]["decode_gemm_llama3_8b"] = bench_decode(awq, dev, stream)
     del ws, gemm_ws, yref
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

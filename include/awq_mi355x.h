@@ -28,7 +28,9 @@
  *   - Pointers to bf16/f32/u32 tensors with more than one element must be
  *     16-byte aligned (AWQ_ERR_ALIGN otherwise).
  *   - group must be 128 and bits 3 or 4 (AWQ_ERR_UNSUPPORTED otherwise); K must
- *     be a positive multiple of group (AWQ_ERR_SHAPE).
+ *     be a positive multiple of group, at most 2^22, and the contractions
+ *     take N <= 2^22 (AWQ_ERR_SHAPE otherwise: tiles are addressed with 32-bit
+ *     byte offsets).
  *   - Inputs must be finite; NaN/Inf in X or W give unspecified codes and
  *     non-finite losses (the search then never selects a NaN loss).
  *   - No C++ exception crosses this boundary.  awq_last_error() returns a
@@ -68,6 +70,7 @@ typedef enum awq_op {
   AWQ_OP_W4A16_GEMM = 1,
   AWQ_OP_SEARCH_SCALE = 2,
   AWQ_OP_CANDIDATE_SCALES = 3,
+  AWQ_OP_DECODE_GEMM = 4,
 } awq_op;
 
 /* Version of this ABI (AWQ_ABI_VERSION). */
@@ -85,6 +88,8 @@ const char* awq_last_error(void);
  *   op AWQ_OP_W4A16_GEMM:   uses M, N, K (needed only when sse is requested).
  *   op AWQ_OP_SEARCH_SCALE: uses M, N, K, bits, group, n_grid.
  *   op AWQ_OP_CANDIDATE_SCALES: uses K, n_grid.
+ *   op AWQ_OP_DECODE_GEMM:  uses M, N, K, bits, group (0 bytes when K is not
+ *                           split across workgroups).
  * Errors: AWQ_ERR_NULL (bytes NULL), AWQ_ERR_SHAPE, AWQ_ERR_UNSUPPORTED.
  */
 awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t bits,
@@ -167,6 +172,29 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                           const uint32_t* qweight, const float* scales, const uint8_t* zeros,
                           int32_t bits, int32_t group, const float* inv_s, const float* y_ref,
                           float* y, double* sse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Decode-shaped W4A16 contraction for 1 <= M <= 16 tokens, the deployment
+ * case (builderai "About": kernels for 4-bit weights with 16-bit activations;
+ * robotsatlas "Implementation pitfalls": the speedup needs a kernel that reads
+ * the packed weights directly; "Limitations": the benefit depends on matched
+ * INT4 kernels).  Streams the packed weights once:
+ *   y[m][n] = sum_k a[m][k] * (q[n][k] - zeros[n][k/group]) * scales[n][k/group]
+ * The dequantized weight is the exact product (q - z) * step (not rounded to
+ * bf16); products are exact and sums are fp32.
+ *   a       bf16 [M][K] activations (already divided by the search's s, as
+ *           the caller folds it)
+ *   qweight/scales/zeros as from awq_quantize_pack, bits 3 or 4
+ *   y       f32 [M][N] output
+ *   ws      awq_workspace_size(AWQ_OP_DECODE_GEMM) bytes (fp32 partials of
+ *           the K splits; may be NULL when that size is 0).
+ * M > 16 gives AWQ_ERR_SHAPE (use awq_w4a16_gemm).  M == 0 or N == 0 is a
+ * no-op.  Results are bit-reproducible for a given (M, N, K).
+ */
+awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                 const uint32_t* qweight, const float* scales,
+                                 const uint8_t* zeros, int32_t bits, int32_t group, float* y,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
  * The whole per-layer search (robotsatlas "How it works", "Key mechanisms";

@@ -42,6 +42,9 @@ contract the GPU library implements):
   loss             MSE over all M*N outputs of X.B^T against X.W^T, fp64
   selection        first index of the minimum loss (NaN never wins; all-NaN
                    gives -1)
+  decode product   for the deployment contraction with few tokens, the
+                   dequantized weight is the exact (q - z) * step (no bf16
+                   rounding): Y = A . ((q - z) * step)^T
 
 Every "f32(...)" marks one IEEE fp32 operation of the contract.  The oracle
 evaluates the exact operation in fp64 and rounds the result to fp32; for +, -,
@@ -349,3 +352,16 @@ def deploy_gemm(a_bits, qweight, scales, zeros, group: int, inv32=None) -> np.nd
     B = dequant_operand(q, np.asarray(zeros, np.int64), np.asarray(scales, np.float64),
                         group, inv32)
     return gemm(a_bits, B)
+
+
+def decode_gemm(a_bits, qweight, scales, zeros, group: int) -> np.ndarray:
+    """Deployment contraction with packed weights ([P1] "About": 4-bit weights
+    with 16-bit activations; [P3] "Implementation pitfalls": the packed form
+    is read directly): Y = A . Wd^T with Wd = (q - z) * step exactly.  (q - z)
+    is a small integer and step a binary32, so every Wd and every product with
+    a bf16 activation is exact in fp64; only the K-sum rounds."""
+    q = unpack(qweight).astype(np.float64)
+    z = np.repeat(np.asarray(zeros, np.float64), group, axis=1)
+    step = np.repeat(np.asarray(scales, np.float32).astype(np.float64), group, axis=1)
+    wd = (q - z) * step
+    return bf16_bits_to_f64(a_bits) @ wd.T

@@ -20,7 +20,7 @@ __all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "
            "reference_gemm", "w4a16_gemm", "search_scale", "workspace_size",
            "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES"]
 
-OP_ACT_STATS, OP_W4A16_GEMM, OP_SEARCH_SCALE, OP_CANDIDATE_SCALES = 0, 1, 2, 3
+OP_ACT_STATS, OP_W4A16_GEMM, OP_SEARCH_SCALE, OP_CANDIDATE_SCALES, OP_DECODE_GEMM = 0, 1, 2, 3, 4
 
 _c_void_p, _i64, _i32, _size_t = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 
@@ -39,6 +39,8 @@ _SIGNATURES = {
     "awq_w4a16_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
                         _c_void_p], _i32),
+    "awq_w4a16_decode_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
+                               _i32, _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
     "awq_search_scale": ([_c_void_p, _i64, _i64, _c_void_p, _i64, _i32, _i32, _i32, _c_void_p,
                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                           _c_void_p, _size_t, _c_void_p], _i32),
@@ -196,6 +198,26 @@ def w4a16_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zer
     if y_ref is None:
         return y
     return y, sse
+
+
+def decode_gemm(a: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                bits: int = 4, group: int = 128, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = A . ((q - z) * step)^T for 1 <= M <= 16 tokens (fp32 [M][N])."""
+    a = _bf16(a, "a")
+    M, K = a.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 8 != K:
+        raise ValueError("qweight must be [N][K/8]")
+    dev = a.device
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if out is None else _f32(out, "out")
+    need = workspace_size(OP_DECODE_GEMM, M, N, K, bits, group)
+    ws = _workspace(need, dev, workspace) if need > 0 else None
+    _check(lib().awq_w4a16_decode_gemm(_ptr(a), M, N, K, _ptr(qweight), _ptr(scales), _ptr(zeros),
+                                       bits, group, _ptr(y), _ptr(ws),
+                                       0 if ws is None else ws.numel(), _stream(dev)),
+           "awq_w4a16_decode_gemm")
+    return y
 
 
 def search_scale(x: torch.Tensor, w: torch.Tensor, bits: int = 4, group: int = 128,

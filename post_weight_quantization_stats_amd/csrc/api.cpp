@@ -49,11 +49,14 @@ awq_status check_quant_params(int32_t bits, int32_t group) {
 awq_status check_k(int64_t K, int32_t group) {
   if (K <= 0 || K % group != 0)
     return fail(AWQ_ERR_SHAPE, "K must be a positive multiple of the group size (K=%lld)", (long long)K);
-  if (K > (int64_t(1) << 30)) return fail(AWQ_ERR_SHAPE, "K too large (%lld)", (long long)K);
+  // Kernels address a tile's rows with 32-bit byte offsets (up to 256 rows of K bf16).
+  if (K > (int64_t(1) << 22)) return fail(AWQ_ERR_SHAPE, "K too large (%lld > 2^22)", (long long)K);
   return AWQ_OK;
 }
 
 constexpr int64_t kMaxDim = int64_t(1) << 31;
+// Output rows of a 256-row tile are addressed with 32-bit byte offsets (row * N * 4).
+constexpr int64_t kMaxGemmN = int64_t(1) << 22;
 
 // ---- workspace layouts ----
 struct SearchLayout {
@@ -115,7 +118,7 @@ awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32
         *bytes = awq::stats_ws_bytes(M, K);
         return ok();
       case AWQ_OP_W4A16_GEMM:
-        if (M < 0 || N < 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim)
+        if (M < 0 || N < 0 || K <= 0 || M >= kMaxDim || N > kMaxGemmN)
           return fail(AWQ_ERR_SHAPE, "bad GEMM shape");
         *bytes = awq::align_up((size_t)awq::gemm_tiles(M, N) * sizeof(double));
         return ok();
@@ -123,10 +126,19 @@ awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32
         awq_status st = check_quant_params(bits, group);
         if (st != AWQ_OK) return st;
         if ((st = check_k(K, group)) != AWQ_OK) return st;
-        if (M <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim)
-          return fail(AWQ_ERR_SHAPE, "search needs M >= 1 and N >= 1");
+        if (M <= 0 || N <= 0 || M >= kMaxDim || N > kMaxGemmN)
+          return fail(AWQ_ERR_SHAPE, "search needs M >= 1 and 1 <= N <= 2^22");
         if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_UNSUPPORTED, "n_grid must be in [1, 64]");
         *bytes = search_layout(M, N, K, n_grid).total;
+        return ok();
+      }
+      case AWQ_OP_DECODE_GEMM: {
+        awq_status st = check_quant_params(bits, group);
+        if (st != AWQ_OK) return st;
+        if ((st = check_k(K, group)) != AWQ_OK) return st;
+        if (M < 0 || M > awq::kDecodeMaxM || N < 0 || N > kMaxGemmN)
+          return fail(AWQ_ERR_SHAPE, "decode GEMM needs 0 <= M <= %lld", (long long)awq::kDecodeMaxM);
+        *bytes = (M == 0 || N == 0) ? 0 : awq::decode_plan(M, N, K).ws_bytes;
         return ok();
       }
       case AWQ_OP_CANDIDATE_SCALES:
@@ -205,7 +217,7 @@ awq_status awq_reference_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K
   try {
     awq_status st = check_k(K, awq::kGroup);
     if (st != AWQ_OK) return st;
-    if (M < 0 || N < 0 || M >= kMaxDim || N >= kMaxDim) return fail(AWQ_ERR_SHAPE, "M, N out of range");
+    if (M < 0 || N < 0 || M >= kMaxDim || N > kMaxGemmN) return fail(AWQ_ERR_SHAPE, "M, N out of range");
     if (M == 0 || N == 0) return ok();
     if (x == nullptr || w == nullptr || y == nullptr) return fail(AWQ_ERR_NULL, "x, w and y are required");
     if (misaligned(x) || misaligned(w) || misaligned(y))
@@ -232,7 +244,7 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
     awq_status st = check_quant_params(bits, group);
     if (st != AWQ_OK) return st;
     if ((st = check_k(K, group)) != AWQ_OK) return st;
-    if (M < 0 || N < 0 || M >= kMaxDim || N >= kMaxDim) return fail(AWQ_ERR_SHAPE, "M, N out of range");
+    if (M < 0 || N < 0 || M >= kMaxDim || N > kMaxGemmN) return fail(AWQ_ERR_SHAPE, "M, N out of range");
     hipStream_t s = (hipStream_t)stream;
     if (M == 0 || N == 0) {  // empty product: only sse (if given) is written
       if (sse != nullptr) {
@@ -272,6 +284,34 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
   }
 }
 
+awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                 const uint32_t* qweight, const float* scales,
+                                 const uint8_t* zeros, int32_t bits, int32_t group, float* y,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  try {
+    awq_status st = check_quant_params(bits, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (M < 0 || M > awq::kDecodeMaxM || N < 0 || N > kMaxGemmN)
+      return fail(AWQ_ERR_SHAPE, "decode GEMM needs 0 <= M <= %lld and 0 <= N <= 2^22",
+                  (long long)awq::kDecodeMaxM);
+    if (M == 0 || N == 0) return ok();
+    if (a == nullptr || qweight == nullptr || scales == nullptr || zeros == nullptr || y == nullptr)
+      return fail(AWQ_ERR_NULL, "a, qweight, scales, zeros and y are required");
+    if (misaligned(a) || misaligned(qweight) || misaligned(y) || misaligned(ws) ||
+        ((uintptr_t)scales & 3u))
+      return fail(AWQ_ERR_ALIGN, "a, qweight, y and ws must be 16-byte aligned, scales 4-byte");
+    const awq::DecodePlan plan = awq::decode_plan(M, N, K);
+    if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes))
+      return fail(AWQ_ERR_WORKSPACE, "decode GEMM needs %zu workspace bytes", plan.ws_bytes);
+    AWQ_TRY_LAUNCH(awq::launch_decode_gemm(a, M, N, K, qweight, scales, zeros, y, ws,
+                                           (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
 awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
                             int32_t bits, int32_t group, int32_t n_grid, float* mean_abs,
                             double* losses, int32_t* best_idx, float* best_s, uint32_t* qweight,
@@ -285,8 +325,8 @@ awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint1
     awq_status st = check_quant_params(bits, group);
     if (st != AWQ_OK) return st;
     if ((st = check_k(K, group)) != AWQ_OK) return st;
-    if (M <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim)
-      return fail(AWQ_ERR_SHAPE, "search needs M >= 1 and N >= 1");
+    if (M <= 0 || N <= 0 || M >= kMaxDim || N > kMaxGemmN)
+      return fail(AWQ_ERR_SHAPE, "search needs M >= 1 and 1 <= N <= 2^22");
     if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_UNSUPPORTED, "n_grid must be in [1, 64]");
     if (misaligned(x) || misaligned(w) || misaligned(mean_abs) || misaligned(best_s) ||
         misaligned(qweight) || misaligned(ws) || ((uintptr_t)scales & 3u) ||

@@ -67,6 +67,18 @@ struct GemmOperands {
 };
 hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream);
 
+// ---- decode-shaped W4A16 contraction (M <= 16) ----
+constexpr int64_t kDecodeMaxM = 16;
+struct DecodePlan {
+  int64_t groups_per_split;
+  int64_t splits;
+  size_t ws_bytes;          // fp32 partials [splits][M][N] when splits > 1
+};
+DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                              const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                              float* y, void* ws, hipStream_t stream);
+
 // losses[i] = (sum_t partials[i*T + t]) / divisor, fixed summation order.
 hipError_t launch_loss_reduce(const double* partials, int64_t T, int n_grid, double divisor,
                               double* losses, hipStream_t stream);

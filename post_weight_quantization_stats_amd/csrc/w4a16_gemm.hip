@@ -377,17 +377,19 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
   using IV1 = std::integral_constant<int, (WPT / 2) * 40 / (4 * BJ)>;
   using IV2 = std::integral_constant<int, (WPT / 2) * 40 / (2 * BJ)>;
 
-  // One k-step (the loads are issued unconditionally, also past the end of K,
-  // where they read other rows' data or zeros into stages that are never
-  // read, so the compiler's wait counts are exact on every path).
+  // One k-step.  The loads are issued unconditionally so the compiler's wait
+  // counts are exact on every path; the prefetches of the three steps past
+  // the end of K are clamped to the last k-step (they fill stages that are
+  // never read), which keeps every address inside its row.
   auto step = [&](int64_t k, auto I) {
     constexpr int i = decltype(I)::value;      // k % 4
-    dma_tile(ra, SA[(i + 3) & 3], (k + 3) * BK);
+    const int64_t kpre = min(k + 3, KT - 1) * BK;
+    dma_tile(ra, SA[(i + 3) & 3], kpre);
     if constexpr (kInt4) {
       uint4* const bq = SB[(i + 2) & 3];
       const int64_t kq = (k + 2) * BK;
       const Unpacked U = pin(C[i & 1]);      // codes of step k+2
-      load_codes(C[(i + 1) & 1], (k + 3) * BK);
+      load_codes(C[(i + 1) & 1], kpre);
       read_frags(F1, SA[i], SB[i], 1);
       mfma_half(F0, 0);
       mfma_half(F0, 1);
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
       __builtin_amdgcn_sched_barrier(0);
       barrier_lds_keep<C_::kFragReads>();
     } else {
-      dma_tile(rb, SB[(i + 3) & 3], (k + 3) * BK);
+      dma_tile(rb, SB[(i + 3) & 3], kpre);
       read_frags(F1, SA[i], SB[i], 1);
       mfma_half(F0, 0);
       mfma_half(F0, 1);

@@ -161,3 +161,32 @@ def test_python_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         awq.act_stats(torch.zeros((4, 8), dtype=torch.bfloat16))
+
+
+def test_decode_gemm_errors_and_plan():
+    f = awq.lib().awq_w4a16_decode_gemm
+    args = dict(a=FAKE, M=4, N=128, K=4096, q=FAKE, sc=FAKE, z=FAKE, bits=4, group=128, y=FAKE,
+                ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["a"], a["M"], a["N"], a["K"], a["q"], a["sc"], a["z"], a["bits"], a["group"],
+                 a["y"], a["ws"], a["wsb"], None)
+
+    assert call(a=None) == NULL
+    assert call(y=None) == NULL
+    assert call(M=17) == SHAPE                       # larger M: awq_w4a16_gemm
+    assert call(M=-1) == SHAPE
+    assert call(K=100) == SHAPE
+    assert call(bits=2) == UNSUPPORTED
+    assert call(group=64) == UNSUPPORTED
+    assert call(a=FAKE_MIS) == ALIGN
+    assert call(y=FAKE_MIS) == ALIGN
+    assert call(M=0) == OK and call(N=0) == OK       # empty: no-op
+    # A narrow layer is split along K: the partials need workspace.
+    need = awq.workspace_size(awq.OP_DECODE_GEMM, 4, 128, 4096)
+    assert need >= 4 * 128 * 4 * 2
+    assert call() == WORKSPACE
+    assert call(ws=FAKE, wsb=need - 1) == WORKSPACE
+    # A wide layer fills the GPU without splitting K: no workspace at all.
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 65536, 4096) == 0

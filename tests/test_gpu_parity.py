@@ -243,3 +243,78 @@ def test_gemm_empty_and_degenerate(dev):
     w0 = torch.zeros((0, 128), dtype=torch.bfloat16, device=dev)
     q0, s0, z0 = awq.quantize_pack(w0)
     assert q0.shape == (0, 16)
+
+
+# ---------------------------------------------------------------- decode GEMM
+
+def random_packed(N, K, bits, seed):
+    """Seeded packed weights: random code words (codes < 2^bits in 4-bit
+    containers), positive steps, zeros in [0, qmax]."""
+    rng = np.random.default_rng(seed)
+    qw = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    if bits == 3:
+        qw &= np.uint32(0x77777777)
+    G = K // 128
+    sc = (0.02 / 7.5 * rng.uniform(0.5, 1.5, size=(N, G))).astype(np.float32)
+    ze = rng.integers(0, 2 ** bits, size=(N, G)).astype(np.uint8)
+    return qw, sc, ze
+
+
+def run_decode(dev, M, N, K, bits, seed):
+    a = synth.decode_activations(K, M, seed=seed)
+    qw, sc, ze = random_packed(N, K, bits, seed)
+    y = awq.decode_gemm(to_dev_bf16(a, dev), torch.from_numpy(qw.view(np.int32)).to(dev),
+                        to_dev_f32(sc, dev), torch.from_numpy(ze).to(dev), bits)
+    return y.cpu().numpy(), (a, qw, sc, ze)
+
+
+# (M, N, K): split-K and unsplit, ragged N, one group, odd token counts.
+DECODE_SHAPES = [(1, 64, 128), (2, 200, 256), (3, 1000, 1024), (4, 4096, 4096), (8, 520, 2048),
+                 (13, 4104, 384), (16, 6144, 4096), (16, 40960, 512), (5, 16, 1152)]
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda s: f"M{s[0]}_N{s[1]}_K{s[2]}")
+def test_decode_gemm(dev, shape, bits):
+    M, N, K = shape
+    announce("decode_gemm", shape, bits)
+    y, (a, qw, sc, ze) = run_decode(dev, M, N, K, bits, seed=M * 7 + bits)
+    ref = O.decode_gemm(a, qw, sc, ze, 128)
+    _, fro = gemm_close(y, ref)
+    assert fro <= 1e-5     # fp32 sums of exact products: far inside the contract
+
+
+@pytest.mark.parametrize("name", ["qkv", "o_proj", "gate_up", "down"])
+def test_decode_gemm_llama3_block_shapes(dev, name):
+    """The Llama-3-8B block's layers at their full sizes, M = 1 and 16."""
+    spec = synth.layer_spec("llama3_8b_block", name)
+    for M in (1, 16):
+        announce("decode_gemm full size", name, M)
+        y, (a, qw, sc, ze) = run_decode(dev, M, spec.N, spec.K, 4, seed=M)
+        gemm_close(y, O.decode_gemm(a, qw, sc, ze, 128))
+
+
+def test_decode_gemm_is_bit_reproducible(dev):
+    announce("decode_gemm determinism")
+    y1, _ = run_decode(dev, 16, 4096, 14336, 4, seed=9)
+    y2, _ = run_decode(dev, 16, 4096, 14336, 4, seed=9)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_decode_gemm_matches_search_operand_when_exact(dev):
+    """Power-of-two steps make (q - z) * step exact in bf16: the decode kernel
+    and the general W4A16 kernel then compute the same products."""
+    announce("decode vs general w4a16")
+    M, N, K = 16, 512, 1024
+    a = synth.decode_activations(K, M, seed=4)
+    qw, _, ze = random_packed(N, K, 4, seed=4)
+    rng = np.random.default_rng(4)
+    sc = np.exp2(rng.integers(-10, -4, size=(N, K // 128))).astype(np.float32)
+    ad = to_dev_bf16(a, dev)
+    qd = torch.from_numpy(qw.view(np.int32)).to(dev)
+    sd, zd = to_dev_f32(sc, dev), torch.from_numpy(ze).to(dev)
+    y_dec = awq.decode_gemm(ad, qd, sd, zd, 4).cpu().numpy()
+    y_gen = awq.w4a16_gemm(ad, qd, sd, zd, 4).cpu().numpy()
+    ref = O.decode_gemm(a, qw, sc, ze, 128)
+    gemm_close(y_dec, ref)
+    gemm_close(y_gen, ref)

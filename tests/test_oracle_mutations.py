@@ -4,6 +4,7 @@ in test_oracle_pins catch every one of them."""
 import numpy as np
 import pytest
 
+import oracle
 import oracle.awq_oracle as OA
 import test_oracle_pins as P
 
@@ -73,9 +74,24 @@ def _mut_normaliser_max_only(mp):
     mp.setattr(OA, "np", _NumpyWith(sqrt=lambda v: orig_sqrt(v) * 1.5))
 
 
+def _mut_decode_zero_of_first_group(mp):
+    def dec(a_bits, qweight, scales, zeros, group):
+        q = OA.unpack(qweight).astype(np.float64)
+        z = np.asarray(zeros, np.float64)[:, :1]
+        step = np.repeat(np.asarray(scales, np.float64), group, axis=1)
+        return OA.bf16_bits_to_f64(a_bits) @ ((q - z) * step).T
+    # The pins call the package's name for it.
+    mp.setattr(oracle, "decode_gemm", dec)
+
+
+def _mut_decode_rounds_weight_to_bf16(mp):
+    mp.setattr(oracle, "decode_gemm", lambda a, qw, sc, ze, g: OA.deploy_gemm(a, qw, sc, ze, g))
+
+
 MUTATIONS = [_mut_floor_instead_of_rint, _mut_drop_inv_s, _mut_alpha_grid_closed,
              _mut_scale_index_reversed, _mut_zero_added_before_rounding, _mut_loss_sign,
-             _mut_no_range_extension, _mut_stats_mean_without_abs, _mut_normaliser_max_only]
+             _mut_no_range_extension, _mut_stats_mean_without_abs, _mut_normaliser_max_only,
+             _mut_decode_zero_of_first_group, _mut_decode_rounds_weight_to_bf16]
 
 PINS = [
     P.test_quantizer_worked_group,
@@ -87,6 +103,8 @@ PINS = [
     lambda: P.test_alpha0_loss_is_plain_rtn(4),
     lambda: P.test_whole_search_brute_force_tiny(24, 8, 128, 4, 20),
     lambda: P.test_whole_search_brute_force_tiny(16, 6, 256, 3, 21),
+    P.test_decode_gemm_brute_force_from_words,
+    P.test_decode_gemm_unit_codes_closed_form,
 ]
 
 

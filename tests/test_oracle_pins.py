@@ -444,3 +444,66 @@ def test_deploy_gemm_exact_sums():
                 d = py_bf16(py_f32((q[n, k] - z[n, k // 128]) * float(st[n, k // 128])))
                 terms.append(X[m, k] * d)
             assert Y[m, n] == pytest.approx(math.fsum(terms), rel=1e-13, abs=1e-300)
+
+
+# ------------------------------------------------------------ decode contraction
+
+def test_decode_gemm_brute_force_from_words():
+    """Nibbles decoded bit by bit from the packed words in pure Python; the
+    dequantized weight (q - z) * step is exact in binary64."""
+    rng = np.random.default_rng(31)
+    M, N, K = 3, 8, 256
+    x, w = synth.random_layer(M, K, N, seed=31)
+    q, z, st = O.quantize(w, None, 4, 128)
+    qw, sc, ze = O.pack(q, z, st)
+    Y = O.decode_gemm(x, qw, sc, ze, 128)
+    X = synth.bf16_bits_to_f32(x).astype(np.float64)
+    words = qw.astype(np.uint64)
+    for m in range(M):
+        for n in range(N):
+            terms = []
+            for k in range(K):
+                code = (int(words[n, k // 8]) >> (4 * (k % 8))) & 15
+                g = k // 128
+                terms.append(X[m, k] * ((code - int(ze[n, g])) * float(sc[n, g])))
+            assert Y[m, n] == pytest.approx(math.fsum(terms), rel=1e-13, abs=1e-300)
+    del rng
+
+
+def test_decode_gemm_codes_at_zero_point_give_zero():
+    M, N, K = 4, 16, 384
+    x, _ = synth.random_layer(M, K, N, seed=32)
+    rng = np.random.default_rng(32)
+    ze = rng.integers(0, 16, size=(N, K // 128)).astype(np.uint8)
+    q = np.repeat(ze.astype(np.int64), 128, axis=1)
+    qw = O.pack(q, ze, np.ones((N, K // 128), np.float32))[0]
+    sc = rng.uniform(0.01, 2.0, size=(N, K // 128)).astype(np.float32)
+    assert np.all(O.decode_gemm(x, qw, sc, ze, 128) == 0.0)
+
+
+def test_decode_gemm_unit_codes_closed_form():
+    """q = z + 1 everywhere: Y[m][n] = sum_g step[n][g] * (sum of A[m] over group g)."""
+    M, N, K = 5, 8, 512
+    x, _ = synth.random_layer(M, K, N, seed=33)
+    rng = np.random.default_rng(33)
+    ze = rng.integers(0, 15, size=(N, K // 128)).astype(np.uint8)
+    q = np.repeat(ze.astype(np.int64) + 1, 128, axis=1)
+    qw = O.pack(q, ze, np.ones((N, K // 128), np.float32))[0]
+    sc = rng.uniform(0.01, 2.0, size=(N, K // 128)).astype(np.float32)
+    A = synth.bf16_bits_to_f32(x).astype(np.float64)
+    colsum = A.reshape(M, K // 128, 128).sum(axis=2)            # [M][G]
+    ref = colsum @ sc.astype(np.float64).T
+    np.testing.assert_allclose(O.decode_gemm(x, qw, sc, ze, 128), ref, rtol=1e-13, atol=1e-12)
+
+
+def test_decode_gemm_equals_deploy_when_dequant_is_bf16_exact():
+    """With power-of-two steps, (q - z) * step is exact in bf16, so the exact
+    decode product and the bf16-operand product coincide bit for bit."""
+    M, N, K = 4, 24, 256
+    x, _ = synth.random_layer(M, K, N, seed=34)
+    rng = np.random.default_rng(34)
+    q = rng.integers(0, 16, size=(N, K)).astype(np.int64)
+    ze = rng.integers(0, 16, size=(N, K // 128)).astype(np.uint8)
+    sc = np.exp2(rng.integers(-12, 4, size=(N, K // 128))).astype(np.float32)
+    qw = O.pack(q, ze, sc)[0]
+    assert np.array_equal(O.decode_gemm(x, qw, sc, ze, 128), O.deploy_gemm(x, qw, sc, ze, 128))
