@@ -13,15 +13,24 @@
 //     takes codes k and k+4 of a packed word; the activation operand is
 //     permuted the same way (slot order 0,4,1,5,2,6,3,7 within each 8 codes).
 //   * v_mfma_f32_16x16x32_bf16 sums S = sum_k A[m][k] * (128 + q) over one
-//     128-channel group (four MFMAs), and one more set of four MFMAs with an
-//     all-ones operand gives sum_k A[m][k] for the same group.
+//     128-channel group (four MFMAs per 16 output channels).
 //   * The group is then folded once per output: y += step * (S - (128 + z) *
-//     sum A).  The products A * (128 + q) are exact in fp32, so the result is
-//     the fp32-accumulated value of sum_k A * (q - z) * step.
+//     sum A), with sum A per (token, group) computed once per workgroup.  The
+//     products A * (128 + q) are exact in fp32, so the result is the
+//     fp32-accumulated value of sum_k A * (q - z) * step.
+// Memory: the workgroup's slice of A (at most 16 rows x 2048 channels) is
+// copied into LDS once by the buffer unit (XOR-swizzled 16-byte chunks, so the
+// 16 rows of a fragment read hit distinct banks).  Each wave also loads the
+// (step, 128 + zero) pairs of its 32 rows for the whole slice into an LDS
+// table up front, one distinct element per lane: loaded per group and per
+// lane they would touch 16 cache lines for 64 useful bytes per instruction,
+// which measured slower than the code stream itself.  The codes stream
+// through a ring of kDepth groups of registers per wave (deeper rings
+// measured no faster: the streams of the resident waves already cover the
+// latency).
 // Work split: a workgroup of 4 waves owns 128 output channels (two 16-column
-// blocks per wave) and one range of groups along K.  When the output alone
-// gives too few waves to keep enough loads in flight, K is split and each
-// split writes an fp32 partial; a second kernel sums the partials in split
+// blocks per wave) and one range of at most 16 groups along K.  Each split
+// of K writes an fp32 partial; a second kernel sums the partials in split
 // order, so results do not depend on timing.
 #include <algorithm>
 
@@ -36,9 +45,13 @@ constexpr int kNB = 2;                        // 16-column blocks per wave
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileN = 16 * kNB * kWaves;     // output channels per workgroup
-constexpr int kTargetWaves = 2048;            // two waves per SIMD
+constexpr int kDepth = 2;                     // groups of codes in flight per wave
+constexpr int kMaxSliceGroups = 16;           // A slice: 16 rows x 2048 channels
+constexpr int kRowChunks = kMaxSliceGroups * kGroup / 8;   // 16-byte chunks per LDS row
+constexpr int kTargetWaves = 1024;            // one wave per SIMD
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct DecodeParams {
   const uint16_t* a;
@@ -80,68 +93,124 @@ __device__ __forceinline__ bf16x8 codes_b(uint32_t w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// LDS chunk of A (row, logical 16-byte chunk c): the low three bits of the
+// chunk index are XOR-ed with the row, so one chunk column of rows 0..7
+// spreads over all banks.
+__device__ __forceinline__ int a_slot(int row, int c) { return row * kRowChunks + (c ^ (row & 7)); }
+
 struct GroupLoads {
-  uint4 a[4];          // 32 activations of this lane's row (k = 32*(lane/16) .. +32)
   uint4 q[kNB];        // 4 code words of this lane's column per block
-  uint32_t step[kNB];  // raw fp32 bits
-  uint32_t zero[kNB];
 };
 
 __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  extern __shared__ uint4 sa[];                         // A slice: M rows x kRowChunks
+  __shared__ float4 ssum[kMaxSliceGroups * 4];          // sum A [group][row], 1 KiB
+  __shared__ float2 ssz[kWaves][16 * kNB][kMaxSliceGroups];   // (step, 128 + z), 16 KiB
+
   const int lane = threadIdx.x & 63;
   // Wave index in an SGPR, so the buffer resources below are scalar.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15;        // MFMA row (A) and column (B, output)
   const int g4 = lane >> 4;         // quarter of the 128-channel group
   const int64_t M = p.M, N = p.N, K = p.K;
+  // A rows past M repeat row M-1 (their outputs are never stored), so every
+  // LDS read stays inside the M rows allocated.
+  const int arow = min(c16, (int)M - 1);
   const int64_t G = K / kGroup;
   const int64_t n_wave = (int64_t)blockIdx.x * kTileN + wave * (16 * kNB);
   const int64_t g_begin = (int64_t)blockIdx.y * p.groups_per_split;
-  const int64_t g_end = min(G, g_begin + p.groups_per_split);
+  const int gs = (int)(min(G, g_begin + p.groups_per_split) - g_begin);   // groups here
+  const int64_t k_begin = g_begin * kGroup;
 
-  // Rows past M (activations) and N (weights) read as zero.
   const rsrc_t ra = make_rsrc(p.a, M * K * 2);
+  // Rows past N read as zero.
   const rsrc_t rq = make_rsrc(p.qweight + n_wave * (K / 8), (N - n_wave) * (K / 2));
   const rsrc_t rs = make_rsrc(p.scales + n_wave * G, (N - n_wave) * G * 4);
   const rsrc_t rz = make_rsrc(p.zeros + n_wave * G, (N - n_wave) * G);
-  const uint32_t a_off = (uint32_t)(c16 * K * 2 + g4 * 64);
-  uint32_t q_off[kNB], s_off[kNB], z_off[kNB];
+  uint32_t q_off[kNB];
 #pragma unroll
-  for (int b = 0; b < kNB; ++b) {
-    const int row = b * 16 + c16;
-    q_off[b] = (uint32_t)(row * (K / 2) + g4 * 16);
-    s_off[b] = (uint32_t)(row * G * 4);
-    z_off[b] = (uint32_t)(row * G);
-  }
-
-  // Loads of group g.  The prefetch of the group after the last is clamped to
-  // the last group (data never used), so every address stays inside its
-  // buffer and the loads need no branch.
-  auto load = [&](GroupLoads& L, int64_t g) {
+  for (int b = 0; b < kNB; ++b)
+    q_off[b] = (uint32_t)((b * 16 + c16) * (K / 2) + k_begin / 2 + g4 * 16);
+  // Code loads of local group gl.  Past the last group the offset points
+  // outside the buffer: the load returns zeros without a memory access.
+  auto load = [&](GroupLoads& L, int gl) {
+    const bool in = gl < gs;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) L.a[c] = ld16(ra, a_off + c * 16, (uint32_t)(g * 256));
-#pragma unroll
-    for (int b = 0; b < kNB; ++b) {
-      L.q[b] = ld16(rq, q_off[b], (uint32_t)(g * 64));
-      L.step[b] = __builtin_amdgcn_raw_buffer_load_b32(rs, s_off[b], (uint32_t)(g * 4), 0);
-      L.zero[b] = __builtin_amdgcn_raw_buffer_load_b8(rz, z_off[b], (uint32_t)g, 0);
-    }
+    for (int b = 0; b < kNB; ++b)
+      L.q[b] = ld16(rq, in ? q_off[b] + (uint32_t)gl * 64 : 0xFFFFFFF0u, 0);
   };
 
-  const u32x4 ones_bits = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_bits);
+  // (step, zero) of the wave's 32 rows x gs groups: element e -> row e / gs,
+  // group e % gs (consecutive lanes read consecutive groups of a row).
+  constexpr int kSzIters = 16 * kNB * kMaxSliceGroups / 64;
+  uint32_t sz_step[kSzIters], sz_zero[kSzIters];
+#pragma unroll
+  for (int i = 0; i < kSzIters; ++i) {
+    const int e = i * 64 + lane;
+    const int row = e / gs, gl = e - row * gs;
+    const bool ok = row < 16 * kNB;   // past the wave's rows: offsets outside the buffers
+    sz_step[i] = __builtin_amdgcn_raw_buffer_load_b32(
+        rs, ok ? (uint32_t)((row * G + g_begin + gl) * 4) : 0xFFFFFFF0u, 0, 0);
+    sz_zero[i] = __builtin_amdgcn_raw_buffer_load_b8(
+        rz, ok ? (uint32_t)(row * G + g_begin + gl) : 0xFFFFFFF0u, 0, 0);
+  }
+
+  GroupLoads R[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) load(R[d], d);
+
+  // A slice -> LDS: instruction `it` copies row it/4, chunks (it%4)*64 + lane.
+  // Only the M rows in use are copied; chunks past the slice read as zero
+  // (offset outside the buffer).
+  {
+    const int rc = gs * (kGroup / 8);                   // chunks in use per row
+    for (int it = wave; it < (int)M * (kRowChunks / 64); it += kWaves) {
+      const int row = it / (kRowChunks / 64);
+      const int pc = (it % (kRowChunks / 64)) * 64 + lane;   // physical chunk
+      const int c = pc ^ (row & 7);
+      const uint32_t voff = pc < rc ? (uint32_t)(row * K * 2 + (k_begin + c * 8) * 2) : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + row * kRowChunks +
+                                                               (it % (kRowChunks / 64)) * 64),
+                                               16, voff, 0, 0, 0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < kSzIters; ++i) {
+    const int e = i * 64 + lane;
+    const int row = e / gs, gl = e - row * gs;
+    if (row < 16 * kNB) ssz[wave][row][gl] = make_float2(__uint_as_float(sz_step[i]),
+                                                          128.f + (float)sz_zero[i]);
+  }
+  __syncthreads();
+
+  // sum A per (group, row) for this slice: thread t -> group t/16, row t%16.
+  {
+    const int gl = threadIdx.x >> 4, row = threadIdx.x & 15;
+    if (gl < gs && row < M) {
+      float sum = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < kGroup / 8; ++c) {
+        const uint4 v = sa[a_slot(row, gl * 16 + c)];
+        sum += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) +
+               bf16_lo(v.z) + bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
+      }
+      ((float*)ssum)[gl * 16 + row] = sum;
+    }
+  }
+  __syncthreads();
+
   f32x4 y[kNB];
 #pragma unroll
   for (int b = 0; b < kNB; ++b) y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const GroupLoads& L) {
+  auto compute = [&](const GroupLoads& L, int gl) {
     bf16x8 af[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) af[j] = permute_a(L.a[j]);
-    f32x4 sum_a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sum_a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], ones, sum_a, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) af[j] = permute_a(sa[a_slot(arow, gl * 16 + 4 * g4 + j)]);
+    const float4 sv = ssum[gl * 4 + g4];                // rows 4*g4 .. 4*g4+3
+    const float sum_a[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       const uint32_t words[4] = {L.q[b].x, L.q[b].y, L.q[b].z, L.q[b].w};
@@ -149,25 +218,22 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], codes_b(words[j]), acc, 0, 0, 0);
-      const float step = __uint_as_float(L.step[b]);
-      const float off = 128.f + (float)L.zero[b];
+      const float2 sz = ssz[wave][b * 16 + c16][gl];
+      const float step = sz.x, off = sz.y;
 #pragma unroll
       for (int i = 0; i < 4; ++i) y[b][i] = fmaf(step, fmaf(-off, sum_a[i], acc[i]), y[b][i]);
     }
   };
 
-  // Two register sets in turn (a copy between them would wait for the
-  // prefetch to land).
-  GroupLoads L0, L1;
-  load(L0, g_begin);
-  int64_t g = g_begin;
-  for (; g + 1 < g_end; g += 2) {
-    load(L1, g + 1);
-    compute(L0);
-    load(L0, min(g + 2, g_end - 1));
-    compute(L1);
+  // Ring of kDepth register sets, unrolled so every index is static.  Loads
+  // are unconditional, so the compiler's wait counts stay exact.
+  for (int gl = 0; gl < gs; gl += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      if (gl + d < gs) compute(R[d], gl + d);
+      load(R[d], gl + d + kDepth);
+    }
   }
-  if (g < g_end) compute(L0);
 
   // Output: lane holds column c16 of each block and rows 4*g4 + i.
   float* out = p.out + (int64_t)blockIdx.y * M * N;
@@ -203,8 +269,10 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t G = K / kGroup;
   const int64_t waves = ceil_div(N, kTileN) * kWaves;
   int64_t splits = waves >= kTargetWaves ? 1 : ceil_div(kTargetWaves, waves);
-  // At least two groups per split: each split also writes M*N partials.
+  // At least two groups per split (each split also writes M*N partials), and
+  // at most kMaxSliceGroups (the A slice in LDS).
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, G / 2));
+  splits = std::max<int64_t>(splits, ceil_div(G, kMaxSliceGroups));
   d.groups_per_split = ceil_div(G, splits);
   d.splits = ceil_div(G, d.groups_per_split);
   d.ws_bytes = d.splits > 1 ? align_up((size_t)d.splits * M * N * sizeof(float)) : 0;
@@ -227,7 +295,12 @@ hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K
   p.K = K;
   p.groups_per_split = d.groups_per_split;
   dim3 grid((unsigned)ceil_div(N, kTileN), (unsigned)d.splits);
-  decode_gemm_kernel<<<grid, kThreads, 0, stream>>>(p);
+  const size_t lds = (size_t)M * kRowChunks * 16;
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)decode_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)(kDecodeMaxM * kRowChunks * 16));
+  if (attr != hipSuccess) return attr;
+  decode_gemm_kernel<<<grid, kThreads, lds, stream>>>(p);
   if (d.splits > 1) {
     const int64_t count = M * N;
     decode_reduce_kernel<<<(unsigned)ceil_div(count, 256), 256, 0, stream>>>(
