@@ -2,15 +2,18 @@
 """Throughput of the AWQ per-layer scale search on one MI355X.
 
 One step = one whole search over one layer (activation statistics, 20
-candidate scales, the fp32 reference product, 20 x (quantize + W4A16 GEMM
-with fused squared error), loss reduction, argmin, final quantize + pack)
-with the inputs already resident in HBM.  Default workload: a Llama-2-7B
+candidate scales, the fp32 reference product, 20 x (quantize to the
+candidate's bf16 operand + contraction with fused squared error), loss
+reduction, argmin, final quantize + pack) with the inputs already resident
+in HBM.  Default workload: a Llama-2-7B
 shaped fused QKV layer, 65536 calibration tokens, K=4096 -> N=12288, INT4,
 group 128, 20 grid points, seeded synthetic data.
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
-the stream the kernels are launched on; the roofline block uses the W4A16
-GEMM (the dominant kernel).  cpu_baseline times the CPU oracle on a bounded
+the stream the kernels are launched on; the roofline block uses the
+per-candidate contraction with the squared-error epilogue (the dominant
+kernel).  The packed W4A16 contraction and the decode-shaped W4A16 kernel are
+timed beside it.  cpu_baseline times the CPU oracle on a bounded
 sample of the same layer and scales it to the full layer.
 """
 
@@ -32,12 +35,14 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "AWQ search: layers/s + W4A16 GEMM TFLOP/s (% MFMA peak), quant GB/s (% HBM)"
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "w4a16_gemm_llama2_7b_qkv_traffic.txt")
+TRAFFIC_FILE = os.path.join(PROFILES, "candidate_sse_llama2_7b_qkv_traffic.txt")
+# The search's per-candidate contraction with the squared-error epilogue.
+DOMINANT_KERNEL = "gemm_kernel<false, false, 4, false, true>"
 GEMM_SOURCES = ["w4a16_gemm.hip", "device_common.h", "awq_internal.h"]
 
 
 def gemm_source_hash() -> str:
-    """Hash of the W4A16 GEMM kernel sources (ties counter data to a kernel version)."""
+    """Hash of the contraction kernel sources (ties counter data to a kernel version)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "post_weight_quantization_stats_amd", "csrc")
@@ -48,8 +53,9 @@ def gemm_source_hash() -> str:
 
 
 def committed_traffic():
-    """HBM bytes per W4A16 GEMM launch from the committed rocprofv3 counter
-    summary, or None when the kernel source changed since it was taken."""
+    """HBM bytes per launch of the search's dominant contraction from the
+    committed rocprofv3 counter summary, or None when the kernel source
+    changed since it was taken."""
     try:
         fields = {}
         with open(TRAFFIC_FILE) as f:
@@ -67,14 +73,17 @@ def committed_traffic():
 # ---- rocprofv3 output summaries (run on the host after a profiled bench) ----
 
 KERNEL_LABELS = [
-    ("gemm_kernel<true, true", "w4a16_gemm_sse (INT4 operand, 1/s folded, squared-error epilogue)"),
-    ("gemm_kernel<true, false", "w4a16_gemm (INT4 operand, plain)"),
-    ("gemm_kernel<false", "reference_gemm (bf16 operand, fp32 Y_ref)"),
+    ("gemm_kernel<false, false, 4, false, true>", "candidate_sse (bf16 operand, squared-error epilogue)"),
+    ("gemm_kernel<false, false, 4, true, false>", "reference_gemm (bf16 operand, fp32 Y_ref)"),
+    ("gemm_kernel<true, true, 2, false, true>", "w4a16_gemm_sse (INT4 operand, 1/s folded, SSE epilogue)"),
+    ("gemm_kernel<true", "w4a16_gemm (INT4 operand, other epilogues)"),
+    ("quantize_kernel<4, true>", "dequant_operand (quantize -> bf16 operand)"),
+    ("quantize_kernel<3, true>", "dequant_operand (quantize -> bf16 operand)"),
     ("decode_gemm", "decode W4A16 GEMM (M <= 16)"),
     ("decode_reduce", "decode split-K reduce"),
     ("act_stats_partial", "act_stats partial sums"),
     ("act_stats_finalize", "act_stats finalize"),
-    ("quantize_pack_kernel", "quantize_pack"),
+    ("quantize_kernel", "quantize_pack"),
     ("scales_r_kernel", "candidate scales (powers)"),
     ("scales_norm_kernel", "candidate scales (normalise)"),
     ("loss_reduce_kernel", "loss reduce"),
@@ -180,7 +189,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, commands: str, M: int, K: int)
         wb = float(np.median(wr)) * 1024.0 * f_write
         out.append(f"{_label(name):<62} read {rb / 2**20:>10.1f} MiB  write {wb / 2**20:>9.1f} MiB  "
                    f"(dispatches {len(fr)}/{len(wr)})")
-        if "gemm_kernel<true, true" in name:
+        if DOMINANT_KERNEL in name:
             gemm_bytes = rb + wb
     out.append("")
     out.append(f"kernel_source_hash: {gemm_source_hash()}")
@@ -377,27 +386,41 @@ def main() -> int:
     s_all, inv_all = awq.candidate_scales(mean_abs, G)
     i_mid = G // 2
     qw, sc, ze = awq.quantize_pack(wd, s_all[i_mid], bits, spec.group)
+    b_mid = awq.dequant_operand(wd, s_all[i_mid], inv_all[i_mid], bits, spec.group)
     yref = awq.reference_gemm(xd, wd)
     gemm_ws = torch.empty(max(awq.workspace_size(awq.OP_W4A16_GEMM, M, N, K), 256),
                           dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    t_gemm = event_time_ms(lambda: awq.w4a16_gemm(xd, qw, sc, ze, bits, spec.group,
-                                                  inv_s=inv_all[i_mid], y_ref=yref,
-                                                  return_y=False, workspace=gemm_ws), reps, stream)
+    t_sse = event_time_ms(lambda: awq.candidate_sse(xd, b_mid, yref, workspace=gemm_ws), reps,
+                          stream)
+    t_w4 = event_time_ms(lambda: awq.w4a16_gemm(xd, qw, sc, ze, bits, spec.group,
+                                                inv_s=inv_all[i_mid], y_ref=yref,
+                                                return_y=False, workspace=gemm_ws),
+                         max(2, reps // 2), stream)
     t_ref = event_time_ms(lambda: awq.reference_gemm(xd, wd), max(2, reps // 2), stream)
     t_stats = event_time_ms(lambda: awq.act_stats(xd), reps, stream)
     t_quant = event_time_ms(lambda: awq.quantize_pack(wd, s_all[i_mid], bits, spec.group),
                             reps * 5, stream)
+    t_deq = event_time_ms(lambda: awq.dequant_operand(wd, s_all[i_mid], inv_all[i_mid], bits,
+                                                      spec.group), reps * 5, stream)
     flops = 2.0 * M * N * K
-    gemm_tflops = flops / (t_gemm * 1e-3) / 1e12
-    ref_tflops = flops / (t_ref * 1e-3) / 1e12
+    tf = lambda ms: flops / (ms * 1e-3) / 1e12
     stats_bytes = 2.0 * M * K + 4.0 * K
     quant_bytes = 2.0 * N * K + 4.0 * K + N * K / 2 + 5.0 * N * K / spec.group
-    stats_gbs = stats_bytes / (t_stats * 1e-3) / 1e9
-    quant_gbs = quant_bytes / (t_quant * 1e-3) / 1e9
-    log(f"w4a16 gemm {t_gemm:.3f} ms = {gemm_tflops:.1f} TFLOP/s; reference gemm {t_ref:.3f} ms "
-        f"= {ref_tflops:.1f} TFLOP/s; stats {t_stats * 1e3:.1f} us = {stats_gbs:.0f} GB/s; "
-        f"quantize {t_quant * 1e3:.1f} us = {quant_gbs:.0f} GB/s")
+    deq_bytes = 2.0 * N * K + 8.0 * K + 2.0 * N * K
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    log(f"candidate sse {t_sse:.3f} ms = {tf(t_sse):.1f} TFLOP/s; packed w4a16+sse {t_w4:.3f} ms "
+        f"= {tf(t_w4):.1f} TFLOP/s; reference {t_ref:.3f} ms = {tf(t_ref):.1f} TFLOP/s")
+    log(f"stats {t_stats * 1e3:.1f} us = {gbs(stats_bytes, t_stats):.0f} GB/s; quantize+pack "
+        f"{t_quant * 1e3:.1f} us = {gbs(quant_bytes, t_quant):.0f} GB/s; dequant operand "
+        f"{t_deq * 1e3:.1f} us = {gbs(deq_bytes, t_deq):.0f} GB/s")
+
+    def mfma_entry(ms):
+        return {"ms": ms, "tflops": tf(ms), "frac_mfma_peak": tf(ms) / PEAK_BF16_TFLOPS}
+
+    def hbm_entry(nbytes, ms):
+        return {"us": ms * 1e3, "gbs": gbs(nbytes, ms), "frac_hbm_peak": gbs(nbytes, ms) / PEAK_HBM_GBS,
+                "bytes": nbytes}
 
     result = {
         "metric": METRIC,
@@ -414,28 +437,26 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{spec.workload}/{spec.name}", "M": M, "K": K, "N": N,
                    "bits": bits, "group": spec.group, "n_grid": G},
-        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": committed_traffic(), "kernel": "w4a16 gemm + fused squared error",
-                     "flops_per_launch": flops, "ms_per_launch": t_gemm,
-                     "algorithmic_bytes_per_launch": 2.0 * M * K + N * K / 2 +
-                     5.0 * N * K / spec.group + 4.0 * K + 4.0 * M * N,
+        "roofline": {"bound": "mfma", "achieved": tf(t_sse), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tf(t_sse) / PEAK_BF16_TFLOPS,
+                     "traffic": committed_traffic(),
+                     "kernel": "per-candidate contraction X.B^T with fused squared error",
+                     "flops_per_launch": flops, "ms_per_launch": t_sse,
+                     "algorithmic_bytes_per_launch": 2.0 * M * K + 2.0 * N * K + 4.0 * M * N,
                      "kernel_source_hash": gemm_source_hash()},
         "kernels": {
-            "w4a16_gemm_sse": {"ms": t_gemm, "tflops": gemm_tflops,
-                               "frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS},
-            "reference_gemm": {"ms": t_ref, "tflops": ref_tflops,
-                               "frac_mfma_peak": ref_tflops / PEAK_BF16_TFLOPS},
-            "act_stats": {"us": t_stats * 1e3, "gbs": stats_gbs,
-                          "frac_hbm_peak": stats_gbs / PEAK_HBM_GBS},
-            "quantize_pack": {"us": t_quant * 1e3, "gbs": quant_gbs,
-                              "frac_hbm_peak": quant_gbs / PEAK_HBM_GBS},
+            "candidate_sse": mfma_entry(t_sse),
+            "w4a16_gemm_sse": mfma_entry(t_w4),
+            "reference_gemm": mfma_entry(t_ref),
+            "act_stats": hbm_entry(stats_bytes, t_stats),
+            "quantize_pack": hbm_entry(quant_bytes, t_quant),
+            "dequant_operand": hbm_entry(deq_bytes, t_deq),
         },
         "cpu_baseline": None,
     }
     if not args.no_decode:
         result["kernels"]["decode_gemm_llama3_8b"] = bench_decode(awq, dev, stream)
-    del ws, gemm_ws, yref
+    del ws, gemm_ws, yref, b_mid
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_m} tokens x {args.cpu_n} rows")

@@ -71,6 +71,7 @@ typedef enum awq_op {
   AWQ_OP_SEARCH_SCALE = 2,
   AWQ_OP_CANDIDATE_SCALES = 3,
   AWQ_OP_DECODE_GEMM = 4,
+  AWQ_OP_CANDIDATE_SSE = 5,
 } awq_op;
 
 /* Version of this ABI (AWQ_ABI_VERSION). */
@@ -90,6 +91,7 @@ const char* awq_last_error(void);
  *   op AWQ_OP_CANDIDATE_SCALES: uses K, n_grid.
  *   op AWQ_OP_DECODE_GEMM:  uses M, N, K, bits, group (0 bytes when K is not
  *                           split across workgroups).
+ *   op AWQ_OP_CANDIDATE_SSE: uses M, N.
  * Errors: AWQ_ERR_NULL (bytes NULL), AWQ_ERR_SHAPE, AWQ_ERR_UNSUPPORTED.
  */
 awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t bits,
@@ -141,6 +143,20 @@ awq_status awq_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const floa
                              void* stream);
 
 /*
+ * Dequantized weight operand of one candidate scale, the search's inner step
+ * (robotsatlas "How it works": the weight is scaled by s, quantized
+ * group-wise, and the activation divided by s; here 1/s is folded into the
+ * dequantized weight, which leaves the product unchanged).  Quantizes
+ * W . diag(s) exactly as awq_quantize_pack does and writes
+ *   b[n][k] = bf16( f32( f32((q - z) * step) * inv_s[k] ) )   (RNE to bf16)
+ * (inv_s NULL: no factor).  w bf16 [N][K]; s, inv_s f32 [K] (s NULL means 1);
+ * b bf16 [N][K] output.  N == 0 is a no-op (pointers are then ignored).
+ */
+awq_status awq_dequant_operand(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                               const float* inv_s, int32_t bits, int32_t group, uint16_t* b,
+                               void* stream);
+
+/*
  * Dense reference product Y = X . W^T (robotsatlas "How it works": the output
  * error is measured against the layer's unquantized output).  bf16 operands,
  * fp32 accumulation on the matrix cores, fp32 output.
@@ -149,6 +165,21 @@ awq_status awq_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const floa
  */
 awq_status awq_reference_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                               const uint16_t* w, float* y, void* stream);
+
+/*
+ * Squared output error of one candidate (robotsatlas "How it works": the
+ * scale is chosen by a grid search that minimises the layer's output error):
+ *   sse = sum over m, n of ( (X . B^T)[m, n] - y_ref[m, n] )^2
+ * with bf16 X [M][K] and B [N][K] (a candidate's operand from
+ * awq_dequant_operand), fp32 accumulation on the matrix cores, and the error
+ * reduced in fp64 in a fixed order (bit-reproducible).  The product is never
+ * written to memory.  y_ref f32 [M][N]; sse f64 [1];
+ * ws: awq_workspace_size(AWQ_OP_CANDIDATE_SSE) bytes.  M == 0 or N == 0 sets
+ * sse to 0.
+ */
+awq_status awq_candidate_sse(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint16_t* b,
+                             const float* y_ref, double* sse, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /*
  * W4A16 contraction with the packed weights (builderai "About": kernels for
@@ -211,7 +242,8 @@ awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_
  *   x bf16 [M][K] (M >= 1), w bf16 [N][K] (N >= 1)
  *   mean_abs f32 [K], losses f64 [n_grid], best_idx i32 [1], best_s f32 [K],
  *   qweight u32 [N][K/8], scales f32 [N][K/group], zeros u8 [N][K/group]
- *   ws: awq_workspace_size(AWQ_OP_SEARCH_SCALE) bytes (it holds y_ref, 4*M*N).
+ *   ws: awq_workspace_size(AWQ_OP_SEARCH_SCALE) bytes (it holds y_ref, 4*M*N,
+ *       and one candidate's bf16 weight operand, 2*N*K).
  */
 awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
                             int32_t bits, int32_t group, int32_t n_grid, float* mean_abs,

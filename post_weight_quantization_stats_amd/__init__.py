@@ -20,7 +20,8 @@ __all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "
            "reference_gemm", "w4a16_gemm", "search_scale", "workspace_size",
            "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES"]
 
-OP_ACT_STATS, OP_W4A16_GEMM, OP_SEARCH_SCALE, OP_CANDIDATE_SCALES, OP_DECODE_GEMM = 0, 1, 2, 3, 4
+(OP_ACT_STATS, OP_W4A16_GEMM, OP_SEARCH_SCALE, OP_CANDIDATE_SCALES, OP_DECODE_GEMM,
+ OP_CANDIDATE_SSE) = 0, 1, 2, 3, 4, 5
 
 _c_void_p, _i64, _i32, _size_t = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 
@@ -35,6 +36,10 @@ _SIGNATURES = {
                               _c_void_p], _i32),
     "awq_quantize_pack": ([_c_void_p, _i64, _i64, _c_void_p, _i32, _i32, _c_void_p, _c_void_p,
                            _c_void_p, _c_void_p], _i32),
+    "awq_dequant_operand": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
+                             _c_void_p], _i32),
+    "awq_candidate_sse": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                           _size_t, _c_void_p], _i32),
     "awq_reference_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p], _i32),
     "awq_w4a16_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
@@ -198,6 +203,36 @@ def w4a16_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zer
     if y_ref is None:
         return y
     return y, sse
+
+
+def dequant_operand(w: torch.Tensor, s: torch.Tensor | None, inv_s: torch.Tensor | None,
+                    bits: int = 4, group: int = 128) -> torch.Tensor:
+    """One candidate's bf16 weight operand bf16(f32(f32((q - z) * step) * inv_s[k]))."""
+    w = _bf16(w, "w")
+    N, K = w.shape
+    if s is not None:
+        s = _f32(s, "s")
+    if inv_s is not None:
+        inv_s = _f32(inv_s, "inv_s")
+    b = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+    _check(lib().awq_dequant_operand(_ptr(w), N, K, _ptr(s), _ptr(inv_s), bits, group, _ptr(b),
+                                     _stream(w.device)), "awq_dequant_operand")
+    return b
+
+
+def candidate_sse(x: torch.Tensor, b: torch.Tensor, y_ref: torch.Tensor,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """sum (X . B^T - y_ref)^2 as a float64 [1] device tensor (product never stored)."""
+    x, b, y_ref = _bf16(x, "x"), _bf16(b, "b"), _f32(y_ref, "y_ref")
+    M, K = x.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("x and b disagree on K")
+    sse = torch.empty(1, dtype=torch.float64, device=x.device)
+    ws = _workspace(workspace_size(OP_CANDIDATE_SSE, M, N, K), x.device, workspace)
+    _check(lib().awq_candidate_sse(_ptr(x), M, N, K, _ptr(b), _ptr(y_ref), _ptr(sse), _ptr(ws),
+                                   ws.numel(), _stream(x.device)), "awq_candidate_sse")
+    return sse
 
 
 def decode_gemm(a: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,

@@ -60,7 +60,7 @@ constexpr int64_t kMaxGemmN = int64_t(1) << 22;
 
 // ---- workspace layouts ----
 struct SearchLayout {
-  size_t yref, s, inv, scales_ws, stats_ws, qtmp, sctmp, ztmp, partials, total;
+  size_t yref, s, inv, scales_ws, stats_ws, btmp, partials, total;
 };
 
 SearchLayout search_layout(int64_t M, int64_t N, int64_t K, int n_grid) {
@@ -77,9 +77,7 @@ SearchLayout search_layout(int64_t M, int64_t N, int64_t K, int n_grid) {
   L.inv = take((size_t)n_grid * K * sizeof(float));
   L.scales_ws = take(awq::scales_ws_bytes(K, n_grid));
   L.stats_ws = take(awq::stats_ws_bytes(M, K));
-  L.qtmp = take((size_t)N * (K / 8) * sizeof(uint32_t));
-  L.sctmp = take((size_t)N * (K / awq::kGroup) * sizeof(float));
-  L.ztmp = take((size_t)N * (K / awq::kGroup));
+  L.btmp = take((size_t)N * K * sizeof(uint16_t));   // one candidate's bf16 weight operand
   L.partials = take((size_t)n_grid * awq::gemm_tiles(M, N) * sizeof(double));
   L.total = off;
   return L;
@@ -132,6 +130,11 @@ awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32
         *bytes = search_layout(M, N, K, n_grid).total;
         return ok();
       }
+      case AWQ_OP_CANDIDATE_SSE:
+        if (M < 0 || N < 0 || M >= kMaxDim || N > kMaxGemmN)
+          return fail(AWQ_ERR_SHAPE, "bad GEMM shape");
+        *bytes = awq::align_up((size_t)awq::gemm_tiles(M, N) * sizeof(double));
+        return ok();
       case AWQ_OP_DECODE_GEMM: {
         awq_status st = check_quant_params(bits, group);
         if (st != AWQ_OK) return st;
@@ -206,6 +209,25 @@ awq_status awq_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const floa
       return fail(AWQ_ERR_ALIGN, "w, qweight, s must be 16-byte aligned, scales 4-byte");
     AWQ_TRY_LAUNCH(awq::launch_quantize_pack(w, N, K, s, nullptr, bits, qweight, scales, zeros,
                                              (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_dequant_operand(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                               const float* inv_s, int32_t bits, int32_t group, uint16_t* b,
+                               void* stream) {
+  try {
+    awq_status st = check_quant_params(bits, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (N < 0 || N >= kMaxDim) return fail(AWQ_ERR_SHAPE, "N out of range");
+    if (N == 0) return ok();
+    if (w == nullptr || b == nullptr) return fail(AWQ_ERR_NULL, "w and b are required");
+    if (misaligned(w) || misaligned(b) || misaligned(s) || misaligned(inv_s))
+      return fail(AWQ_ERR_ALIGN, "w, b, s and inv_s must be 16-byte aligned");
+    AWQ_TRY_LAUNCH(awq::launch_quantize_dequant(w, N, K, s, inv_s, bits, b, (hipStream_t)stream));
     return ok();
   } catch (...) {
     return fail(AWQ_ERR_LAUNCH, "internal error");
@@ -312,6 +334,43 @@ awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_
   }
 }
 
+awq_status awq_candidate_sse(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint16_t* b,
+                             const float* y_ref, double* sse, void* ws, size_t ws_bytes,
+                             void* stream) {
+  try {
+    if (K <= 0 || K % awq::kGroup != 0 || K > (int64_t(1) << 22))
+      return fail(AWQ_ERR_SHAPE, "K must be a positive multiple of %d, at most 2^22", awq::kGroup);
+    if (M < 0 || N < 0 || M >= kMaxDim || N > kMaxGemmN) return fail(AWQ_ERR_SHAPE, "M, N out of range");
+    if (sse == nullptr) return fail(AWQ_ERR_NULL, "sse is required");
+    if ((uintptr_t)sse & 7u) return fail(AWQ_ERR_ALIGN, "sse must be 8-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0 || N == 0) {
+      AWQ_TRY_LAUNCH(awq::launch_fill_f64(sse, 1, 0.0, s));
+      return ok();
+    }
+    if (x == nullptr || b == nullptr || y_ref == nullptr)
+      return fail(AWQ_ERR_NULL, "x, b and y_ref are required");
+    if (misaligned(x) || misaligned(b) || misaligned(y_ref) || misaligned(ws))
+      return fail(AWQ_ERR_ALIGN, "x, b, y_ref and ws must be 16-byte aligned");
+    const size_t need = awq::align_up((size_t)awq::gemm_tiles(M, N) * sizeof(double));
+    if (ws == nullptr || ws_bytes < need)
+      return fail(AWQ_ERR_WORKSPACE, "candidate_sse needs %zu workspace bytes", need);
+    awq::GemmOperands op{};
+    op.x = x;
+    op.M = M;
+    op.N = N;
+    op.K = K;
+    op.w = b;
+    op.y_ref = y_ref;
+    op.partials = (double*)ws;
+    AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
+    AWQ_TRY_LAUNCH(awq::launch_loss_reduce((const double*)ws, awq::gemm_tiles(M, N), 1, 1.0, sse, s));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
 awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
                             int32_t bits, int32_t group, int32_t n_grid, float* mean_abs,
                             double* losses, int32_t* best_idx, float* best_s, uint32_t* qweight,
@@ -341,9 +400,7 @@ awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint1
     float* yref = (float*)(base + L.yref);
     float* sc = (float*)(base + L.s);
     float* inv = (float*)(base + L.inv);
-    uint32_t* qtmp = (uint32_t*)(base + L.qtmp);
-    float* sctmp = (float*)(base + L.sctmp);
-    uint8_t* ztmp = (uint8_t*)(base + L.ztmp);
+    uint16_t* btmp = (uint16_t*)(base + L.btmp);
     double* partials = (double*)(base + L.partials);
     const int64_t T = awq::gemm_tiles(M, N);
 
@@ -359,18 +416,20 @@ awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint1
       op.y = yref;
       AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
     }
+    // Per candidate: quantize W*s_i and write its dequantized operand
+    // B_i = bf16(f32(f32((q - z) * step) * inv_s_i[k])) once, then contract
+    // X . B_i^T with the squared error against Y_ref in the epilogue.  (The
+    // packed W4A16 contraction would dequantize B_i again for every 256-row
+    // tile of X; with many calibration tokens writing it once is cheaper.)
     for (int i = 0; i < n_grid; ++i) {
-      AWQ_TRY_LAUNCH(awq::launch_quantize_pack(w, N, K, sc + (int64_t)i * K, nullptr, bits, qtmp,
-                                               sctmp, ztmp, s));
+      AWQ_TRY_LAUNCH(awq::launch_quantize_dequant(w, N, K, sc + (int64_t)i * K,
+                                                  inv + (int64_t)i * K, bits, btmp, s));
       awq::GemmOperands op{};
       op.x = x;
       op.M = M;
       op.N = N;
       op.K = K;
-      op.qweight = qtmp;
-      op.scales = sctmp;
-      op.zeros = ztmp;
-      op.inv_s = inv + (int64_t)i * K;
+      op.w = btmp;
       op.y_ref = yref;
       op.partials = partials + (int64_t)i * T;
       AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));

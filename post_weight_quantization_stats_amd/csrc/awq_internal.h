@@ -52,6 +52,12 @@ hipError_t launch_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const f
                                 const int32_t* s_sel, int bits, uint32_t* qweight,
                                 float* scales, uint8_t* zeros, hipStream_t stream);
 
+// The search's bf16 weight operand for one candidate:
+// b_out[n][k] = bf16(f32(f32((q - z) * step) * inv_s[k])) (inv_s NULL: no factor).
+hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                                   const float* inv_s, int bits, uint16_t* b_out,
+                                   hipStream_t stream);
+
 struct GemmOperands {
   const uint16_t* x;        // bf16 [M][K]
   int64_t M, N, K;

@@ -50,10 +50,10 @@ __device__ __forceinline__ float markstein_div(float a, float b, float y) {
   return fmaf(r, y, q0);                        // RN(a / b)
 }
 
-// One lane's 16 channels of a group: fills two words of packed codes and the
-// group's step and zero (identical in all 8 lanes of the group).
+// One lane's 16 channels of a group: their codes (as floats) and the group's
+// step and zero (identical in all 8 lanes of the group).
 template <int BITS>
-__device__ __forceinline__ void quantize16(const float (&ws)[16], uint32_t& w0, uint32_t& w1,
+__device__ __forceinline__ void quantize16(const float (&ws)[16], float (&q)[16],
                                            float& step_out, float& z_out) {
   constexpr float qmax = (float)((1 << BITS) - 1);
   constexpr float inv_qmax = 1.0f / qmax;       // RN(1/qmax), folded by the compiler
@@ -91,29 +91,32 @@ __device__ __forceinline__ void quantize16(const float (&ws)[16], uint32_t& w0, 
     for (int j = 0; j < 16; ++j) qt[j] = ws[j] / step;
   }
   const float z = fminf(fmaxf(rintf(zq), 0.f), qmax);
-  // Codes are small integers, so a pair packs exactly as lo + 16*hi into one
-  // byte with v_cvt_pk_u8_f32.
-  uint32_t w[2] = {0u, 0u};
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float lo = fminf(fmaxf(rintf(qt[8 * h + 2 * b]) + z, 0.f), qmax);
-      const float hi = fminf(fmaxf(rintf(qt[8 * h + 2 * b + 1]) + z, 0.f), qmax);
-      w[h] = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(hi, 16.f, lo), b, w[h]);
-    }
-  }
-  w0 = w[0];
-  w1 = w[1];
+  for (int j = 0; j < 16; ++j) q[j] = fminf(fmaxf(rintf(qt[j]) + z, 0.f), qmax);
   step_out = step;
   z_out = z;
 }
 
-template <int BITS>
-__global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
+// Eight codes -> one u32 (code j at bits 4j).  Codes are small integers, so
+// a pair packs exactly as lo + 16*hi into one byte with v_cvt_pk_u8_f32.
+__device__ __forceinline__ uint32_t pack8(const float* q) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[2 * b + 1], 16.f, q[2 * b]), b, w);
+  return w;
+}
+
+// kDequant = false: packed codes, steps and zeros.  kDequant = true: the
+// search's weight operand B = bf16(f32(f32((q - z) * step) * inv_s[k])) as a
+// bf16 [N][K] matrix, written once per candidate so that the contraction
+// reads a plain bf16 operand instead of dequantizing it again for every tile
+// of calibration tokens.
+template <int BITS, bool kDequant>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t K, const float* __restrict__ s,
-    const int32_t* __restrict__ s_sel, uint32_t* __restrict__ qweight,
-    float* __restrict__ scales, uint8_t* __restrict__ zeros) {
+    const int32_t* __restrict__ s_sel, const float* __restrict__ inv_s,
+    uint32_t* __restrict__ qweight, float* __restrict__ scales, uint8_t* __restrict__ zeros,
+    uint16_t* __restrict__ bout) {
   const int64_t G = K / kGroup;
   const int64_t g = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x / kLanesPerGroup);
   const int t8 = threadIdx.x % kLanesPerGroup;
@@ -121,15 +124,19 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
   const int64_t k0 = (gvalid ? g : 0) * kGroup + t8 * 16;
   const int64_t n_begin = (int64_t)blockIdx.y * kRows;
 
-  float sv[16];
-  const float* srow = s;
-  if (s != nullptr && s_sel != nullptr) srow = s + (int64_t)max(*s_sel, 0) * K;
-  if (srow != nullptr) {
+  auto load16 = [&](const float* row, float (&v)[16]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float4 t = *(const float4*)(srow + k0 + 4 * c);
-      sv[4 * c] = t.x; sv[4 * c + 1] = t.y; sv[4 * c + 2] = t.z; sv[4 * c + 3] = t.w;
+      const float4 t = *(const float4*)(row + k0 + 4 * c);
+      v[4 * c] = t.x; v[4 * c + 1] = t.y; v[4 * c + 2] = t.z; v[4 * c + 3] = t.w;
     }
+  };
+  float sv[16], iv[16];
+  const float* srow = s;
+  if (s != nullptr && s_sel != nullptr) srow = s + (int64_t)max(*s_sel, 0) * K;
+  if (srow != nullptr) load16(srow, sv);
+  if constexpr (kDequant) {
+    if (inv_s != nullptr) load16(inv_s, iv);
   }
 
   uint4 v[kRows][2];
@@ -156,11 +163,26 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
 #pragma unroll
       for (int j = 0; j < 16; ++j) ws[j] *= sv[j];
     }
-    uint32_t w0, w1;
-    float step, z;
-    quantize16<BITS>(ws, w0, w1, step, z);
-    if (gvalid && n < N) {
-      *(uint2*)(qweight + n * (K / 8) + k0 / 8) = make_uint2(w0, w1);
+    float q[16], step, z;
+    quantize16<BITS>(ws, q, step, z);
+    if (!(gvalid && n < N)) continue;
+    if constexpr (kDequant) {
+      uint32_t d[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float lo = (q[2 * j] - z) * step;            // exact difference, one rounding
+        float hi = (q[2 * j + 1] - z) * step;
+        if (inv_s != nullptr) {
+          lo *= iv[2 * j];
+          hi *= iv[2 * j + 1];
+        }
+        d[j] = pack_bf16x2(lo, hi);
+      }
+      uint4* dst = (uint4*)(bout + n * K + k0);
+      dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
+      dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
+    } else {
+      *(uint2*)(qweight + n * (K / 8) + k0 / 8) = make_uint2(pack8(q), pack8(q + 8));
       if (t8 == 0) {
         scales[n * G + g] = step;
         zeros[n * G + g] = (uint8_t)z;
@@ -177,9 +199,25 @@ hipError_t launch_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const f
   if (N == 0) return hipSuccess;
   dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
   if (bits == 4)
-    quantize_pack_kernel<4><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, qweight, scales, zeros);
+    quantize_kernel<4, false><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, nullptr, qweight,
+                                                             scales, zeros, nullptr);
   else
-    quantize_pack_kernel<3><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, qweight, scales, zeros);
+    quantize_kernel<3, false><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, nullptr, qweight,
+                                                             scales, zeros, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                                   const float* inv_s, int bits, uint16_t* b_out,
+                                   hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
+  if (bits == 4)
+    quantize_kernel<4, true><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
+                                                            nullptr, nullptr, b_out);
+  else
+    quantize_kernel<3, true><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
+                                                            nullptr, nullptr, b_out);
   return hipGetLastError();
 }
 

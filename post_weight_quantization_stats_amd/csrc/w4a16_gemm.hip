@@ -195,7 +195,8 @@ struct CodeRegs {
   uint32_t zero;
 };
 
-template <bool kInt4, bool kInvS, int WN>
+// kStoreY: write the fp32 product; kSse: fp64 sum of (Y - Y_ref)^2 per tile.
+template <bool kInt4, bool kInvS, int WN, bool kStoreY, bool kSse>
 __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
                                                                     const float* __restrict__ inv_s) {
   // The body exists only in the device pass; the host pass needs just the
@@ -438,7 +439,7 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
   // Epilogue.  32x32 block layout: lane holds column (lane & 31) and rows
   // 8*(r/4) + 4*(lane/32) + r%4 for accumulator register r.
   const int64_t row0 = wm * 128 + 4 * lk;        // within the tile
-  if (p.y != nullptr) {
+  if constexpr (kStoreY) {
     // Rows past M fall outside the buffer resource and are dropped.
     const rsrc_t ro = make_rsrc(p.y + m0 * N + n0, ((uint64_t)(M - m0) * N - n0) * 4);
 #pragma unroll
@@ -457,7 +458,7 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
       }
     }
   }
-  if (p.partials != nullptr) {
+  if constexpr (kSse) {
     // Sum of (acc - y_ref)^2.  The wave's 128 x TN block of y_ref is staged
     // through LDS (the k-loop's stage buffers are free now) by the buffer
     // unit, 64 rows at a time, so a whole half-block is in flight at once;
@@ -560,12 +561,28 @@ hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream) {
   const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n);
   // bf16 operand: 8 waves (two per SIMD) measured faster; INT4: the dequant
   // VALU work favours 4 waves with 128x128 tiles each.
-  if (op.qweight == nullptr)
-    gemm_kernel<false, false, 4><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
-  else if (op.inv_s != nullptr)
-    gemm_kernel<true, true, 2><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, op.inv_s);
-  else
-    gemm_kernel<true, false, 2><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, nullptr);
+  const bool y = op.y != nullptr, sse = op.partials != nullptr;
+  if (op.qweight == nullptr) {
+    if (sse)
+      gemm_kernel<false, false, 4, false, true><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
+    else
+      gemm_kernel<false, false, 4, true, false><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
+  } else {
+    auto go = [&](auto kInv) {
+      constexpr bool inv = decltype(kInv)::value;
+      const float* is = inv ? op.inv_s : nullptr;
+      if (y && sse)
+        gemm_kernel<true, inv, 2, true, true><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, is);
+      else if (sse)
+        gemm_kernel<true, inv, 2, false, true><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, is);
+      else
+        gemm_kernel<true, inv, 2, true, false><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, is);
+    };
+    if (op.inv_s != nullptr)
+      go(std::true_type{});
+    else
+      go(std::false_type{});
+  }
   return hipGetLastError();
 }
 

@@ -188,5 +188,30 @@ def test_decode_gemm_errors_and_plan():
     assert need >= 4 * 128 * 4 * 2
     assert call() == WORKSPACE
     assert call(ws=FAKE, wsb=need - 1) == WORKSPACE
-    # A wide layer fills the GPU without splitting K: no workspace at all.
-    assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 65536, 4096) == 0
+    # A wide layer whose K fits one slice fills the GPU unsplit: no workspace.
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 65536, 2048) == 0
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 65536, 4096) > 0
+
+
+def test_dequant_operand_errors():
+    f = awq.lib().awq_dequant_operand
+    assert f(None, 4, 128, None, None, 4, 128, FAKE, None) == NULL
+    assert f(FAKE, 4, 128, None, None, 4, 128, None, None) == NULL
+    assert f(FAKE, 4, 128, None, None, 5, 128, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 4, 100, None, None, 4, 128, FAKE, None) == SHAPE
+    assert f(FAKE, -1, 128, None, None, 4, 128, FAKE, None) == SHAPE
+    assert f(FAKE, 4, 128, FAKE_MIS, None, 4, 128, FAKE, None) == ALIGN
+    assert f(FAKE, 4, 128, None, None, 4, 128, FAKE_MIS, None) == ALIGN
+    assert f(None, 0, 128, None, None, 4, 128, None, None) == OK
+
+
+def test_candidate_sse_errors():
+    f = awq.lib().awq_candidate_sse
+    assert f(FAKE, 4, 8, 128, FAKE, FAKE, None, FAKE, 1 << 20, None) == NULL
+    assert f(None, 4, 8, 128, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == NULL
+    assert f(FAKE, 4, 8, 100, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == SHAPE
+    assert f(FAKE, -1, 8, 128, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == SHAPE
+    assert f(FAKE_MIS, 4, 8, 128, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == ALIGN
+    assert f(FAKE, 4, 8, 128, FAKE, FAKE, FAKE + 4, FAKE, 1 << 20, None) == ALIGN
+    assert f(FAKE, 4, 8, 128, FAKE, FAKE, FAKE, None, 0, None) == WORKSPACE
+    assert f(FAKE, 4, 8, 128, FAKE, FAKE, FAKE, FAKE, 8, None) == WORKSPACE

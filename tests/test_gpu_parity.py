@@ -158,6 +158,45 @@ def test_quantize_extreme_ranges(dev):
             assert np.array_equal(u32(qw), rq)
 
 
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_dequant_operand_bit_exact(dev, shape, bits):
+    """The search's per-candidate bf16 weight operand, bit for bit."""
+    announce("dequant_operand", ids(shape), bits)
+    x, w = layer(shape)
+    _, a = O.act_stats(x)
+    s_all, inv_all = O.candidate_scales(a, 20)
+    wd = to_dev_bf16(w, dev)
+    for i in (0, 7, 19):
+        b = awq.dequant_operand(wd, to_dev_f32(s_all[i], dev), to_dev_f32(inv_all[i], dev), bits)
+        q, z, st = O.quantize(w, s_all[i], bits, 128)
+        ref = O.dequant_operand(q, z, st, 128, inv_all[i])
+        got = b.float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref)
+    b = awq.dequant_operand(wd, None, None, bits)
+    q, z, st = O.quantize(w, None, bits, 128)
+    assert np.array_equal(b.float().cpu().numpy().astype(np.float64),
+                          O.dequant_operand(q, z, st, 128, None))
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_candidate_sse(dev, shape):
+    """The search's per-candidate loss numerator from the bf16 operand."""
+    announce("candidate_sse", ids(shape))
+    x, w = layer(shape)
+    M, N = x.shape[0], w.shape[0]
+    _, a = O.act_stats(x)
+    s_all, inv_all = O.candidate_scales(a, 20)
+    xd, wd = to_dev_bf16(x, dev), to_dev_bf16(w, dev)
+    y_ref = awq.reference_gemm(xd, wd)
+    for i in (0, 11):
+        b = awq.dequant_operand(wd, to_dev_f32(s_all[i], dev), to_dev_f32(inv_all[i], dev), 4)
+        got = float(awq.candidate_sse(xd, b, y_ref).item()) / (M * N)
+        q, z, st = O.quantize(w, s_all[i], 4, 128)
+        ref = O.output_mse(x, w, O.dequant_operand(q, z, st, 128, inv_all[i]))
+        assert abs(got - ref) <= 1e-4 * ref
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=ids)
 def test_reference_gemm(dev, shape):
     announce("reference_gemm", ids(shape))
