@@ -141,7 +141,7 @@ def summarize_trace(trace_dir: str, command: str, log_path: str | None) -> str:
         rf = line["roofline"]
         out += ["", "# same run, bench.py HIP-event figures:",
                 f"search ms/layer: {line['ms_per_step']:.2f}",
-                f"w4a16_gemm_sse ms_per_launch (events): {rf['ms_per_launch']:.3f}",
+                f"dominant kernel ms_per_launch (events): {rf['ms_per_launch']:.3f}",
                 f"kernel_source_hash: {rf['kernel_source_hash']}"]
         for k, v in line["kernels"].items():
             out.append(f"{k}: " + ", ".join(f"{a}={b:.4g}" for a, b in v.items()))
