@@ -307,8 +307,8 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped GEMM figures")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode-shaped GEMM figures (prints them as JSON)")
-    ap.add_argument("--cpu-m", type=int, default=2048)
-    ap.add_argument("--cpu-n", type=int, default=1024)
+    ap.add_argument("--cpu-m", type=int, default=4096)
+    ap.add_argument("--cpu-n", type=int, default=2048)
     ap.add_argument("--summarize-trace", metavar="DIR", default=None,
                     help="write a summary of a rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,

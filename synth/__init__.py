@@ -130,9 +130,12 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32)
 
 
-def make_weight(spec: LayerSpec, seed: int = 0) -> np.ndarray:
+def make_weight(spec: LayerSpec, seed: int = 0, rows: int | None = None) -> np.ndarray:
+    """W (bf16 bit patterns [N][K]); `rows` draws only the first rows, which
+    equal the first rows of the full draw (the stream is row-major)."""
     rng = _rng(seed, spec.workload_id, spec.layer_id, TENSOR_W)
-    w = rng.standard_normal((spec.N, spec.K), dtype=np.float32)
+    n = spec.N if rows is None else min(rows, spec.N)
+    w = rng.standard_normal((n, spec.K), dtype=np.float32)
     w *= np.float32(spec.w_std)
     return to_bf16_bits(w)
 
@@ -193,9 +196,10 @@ def make_activations(spec: LayerSpec, M: int | None = None, seed: int = 0,
     return out
 
 
-def make_layer(workload: str, name: str | None = None, M: int | None = None, seed: int = 0):
+def make_layer(workload: str, name: str | None = None, M: int | None = None, seed: int = 0,
+               rows: int | None = None):
     spec = layer_spec(workload, name)
-    return make_activations(spec, M, seed), make_weight(spec, seed), spec
+    return make_activations(spec, M, seed), make_weight(spec, seed, rows), spec
 
 
 def decode_activations(K: int, M: int, seed: int = 0) -> np.ndarray:

@@ -1,0 +1,160 @@
+"""GPU parity at the bench configuration's full size (Llama-2-7B fused QKV:
+65536 calibration tokens, K = 4096 -> N = 12288, INT4, group 128, 20 grid
+points), in the launch configuration bench.py times, plus every other
+workload's layer shapes at a reduced token count.
+
+At full size the oracle checks what it can compute: the statistics in full,
+the candidate operands and the written weights on sampled rows (bit-exact),
+the product on a sampled block; for the reductions, properties that hold at
+any size (a candidate's squared error against its own product is exactly
+zero; the search's losses are exactly the standalone per-candidate squared
+errors; the chosen index is the first minimum).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import post_weight_quantization_stats_amd as awq
+import synth
+from gpu_util import announce, gemm_close, require_gpu, to_dev_bf16, to_dev_f32, u32, ulp_distance_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+@pytest.fixture(scope="module")
+def qkv(dev):
+    announce("full-size inputs llama2_7b_qkv")
+    x, w, spec = synth.make_layer("llama2_7b_qkv")
+    return x, w, spec, to_dev_bf16(x, dev), to_dev_bf16(w, dev)
+
+
+@pytest.fixture(scope="module")
+def qkv_stats(qkv):
+    x = qkv[0]
+    return O.act_stats(x)
+
+
+def sample_rows(n, k, seed):
+    return np.sort(np.random.default_rng(seed).choice(n, size=k, replace=False))
+
+
+def test_fullsize_stats(qkv, qkv_stats):
+    announce("full-size act_stats")
+    _, _, _, xd, _ = qkv
+    got = awq.act_stats(xd).cpu().numpy().astype(np.float64)
+    _, ref = qkv_stats
+    assert (np.abs(got - ref) / np.maximum(ref, 1e-30)).max() <= 1e-6
+
+
+def test_fullsize_candidates_and_operands(dev, qkv, qkv_stats):
+    announce("full-size candidate scales + operands")
+    x, w, spec, xd, wd = qkv
+    a_gpu = awq.act_stats(xd)
+    s_gpu, inv_gpu = awq.candidate_scales(a_gpu, spec.n_grid)
+    s_ref, inv_ref = O.candidate_scales(qkv_stats[1], spec.n_grid)
+    assert ulp_distance_f32(s_gpu.cpu().numpy(), s_ref).max() <= 1
+    rows = sample_rows(spec.N, 48, 1)
+    for i in (0, 9, 19):
+        s_i, inv_i = s_gpu[i].cpu().numpy(), inv_gpu[i].cpu().numpy()
+        b = awq.dequant_operand(wd, s_gpu[i], inv_gpu[i], 4).float().cpu().numpy()[rows]
+        q, z, st = O.quantize(w[rows], s_i, 4, 128)
+        assert np.array_equal(b.astype(np.float64), O.dequant_operand(q, z, st, 128, inv_i))
+        qw, sc, ze = awq.quantize_pack(wd, s_gpu[i], 4)
+        rq, rs, rz = O.pack(q, z, st)
+        assert np.array_equal(u32(qw)[rows], rq)
+        assert np.array_equal(sc.cpu().numpy()[rows], rs)
+        assert np.array_equal(ze.cpu().numpy()[rows], rz)
+
+
+def test_fullsize_products_sampled(dev, qkv):
+    announce("full-size products, sampled block")
+    x, w, spec, xd, wd = qkv
+    ms = sample_rows(spec.M, 24, 2)
+    ns = sample_rows(spec.N, 40, 3)
+    y = awq.reference_gemm(xd, wd)
+    gemm_close(y[ms][:, ns].cpu().numpy(), O.gemm(x[ms], O.bf16_bits_to_f64(w[ns])))
+    del y
+    s, inv = O.candidate_scales(O.act_stats(x[:4096])[1], 20)
+    qw, sc, ze = awq.quantize_pack(wd, to_dev_f32(s[13], dev), 4)
+    yq = awq.w4a16_gemm(xd, qw, sc, ze, 4, inv_s=to_dev_f32(inv[13], dev))
+    q, z, st = O.quantize(w[ns], s[13], 4, 128)
+    ref = O.gemm(x[ms], O.dequant_operand(q, z, st, 128, inv[13]))
+    gemm_close(yq[ms][:, ns].cpu().numpy(), ref)
+
+
+def test_fullsize_candidate_sse_properties(dev, qkv):
+    announce("full-size candidate_sse properties")
+    x, w, spec, xd, wd = qkv
+    a = awq.act_stats(xd)
+    s, inv = awq.candidate_scales(a, spec.n_grid)
+    b = awq.dequant_operand(wd, s[6], inv[6], 4)
+    y_b = awq.reference_gemm(xd, b)                      # the candidate's own product
+    assert float(awq.candidate_sse(xd, b, y_b).item()) == 0.0
+    y_ref = awq.reference_gemm(xd, wd)
+    sse = float(awq.candidate_sse(xd, b, y_ref).item())
+    direct = float(((y_b.double() - y_ref.double()) ** 2).sum().item())
+    assert abs(sse - direct) <= 1e-9 * direct
+
+
+def test_fullsize_search(dev, qkv, qkv_stats):
+    """The bench's whole search at full size."""
+    announce("full-size search_scale")
+    x, w, spec, xd, wd = qkv
+    out = awq.search_scale(xd, wd, 4, 128, spec.n_grid)
+    losses = out["losses"].cpu().numpy()
+    best = int(out["best_idx"].item())
+    assert best == int(np.argmin(losses)) and np.isfinite(losses).all()
+    a_gpu = out["mean_abs"]
+    _, a_ref = qkv_stats
+    assert (np.abs(a_gpu.cpu().numpy() - a_ref) / a_ref).max() <= 1e-6
+    s, inv = awq.candidate_scales(a_gpu, spec.n_grid)
+    y_ref = awq.reference_gemm(xd, wd)
+    MN = float(spec.M) * spec.N
+    for i in range(spec.n_grid):
+        b = awq.dequant_operand(wd, s[i], inv[i], 4)
+        assert float(awq.candidate_sse(xd, b, y_ref).item()) / MN == losses[i], i
+    s_ref, _ = O.candidate_scales(a_ref, spec.n_grid)
+    best_s = out["best_s"].cpu().numpy()
+    assert ulp_distance_f32(best_s, s_ref[best]).max() <= 1
+    rows = sample_rows(spec.N, 48, 4)
+    rq, rs, rz = O.pack(*O.quantize(w[rows], best_s, 4, 128))
+    assert np.array_equal(u32(out["qweight"])[rows], rq)
+    assert np.array_equal(out["scales"].cpu().numpy()[rows], rs)
+    assert np.array_equal(out["zeros"].cpu().numpy()[rows], rz)
+    # the outlier channels carry the largest scales (salient channels, 1%)
+    cols, _ = synth.outlier_columns(spec)
+    if best > 0:
+        assert np.all(best_s[cols] > np.median(best_s))
+
+
+# Every other workload's layer shapes (real K, dtype and activation recipe),
+# at 384 tokens and the first 256 output rows, against the oracle's search.
+OTHER_LAYERS = [("llama2_7b_mlp", "gate_up", 4), ("llama2_7b_mlp", "down", 4),
+                ("llama3_8b_block", "qkv", 4), ("llama3_8b_block", "o_proj", 4),
+                ("llama3_8b_block", "gate_up", 4), ("llama3_8b_block", "down", 4),
+                ("llama2_70b_mlp", "down", 3), ("llama2_70b_mlp", "down", 4),
+                ("llama2_70b_mlp", "gate_up", 3)]
+
+
+@pytest.mark.parametrize("workload,name,bits", OTHER_LAYERS,
+                         ids=lambda v: str(v))
+def test_workload_layers_reduced(dev, workload, name, bits):
+    announce("search reduced", workload, name, bits)
+    x, w, spec = synth.make_layer(workload, name, M=384, rows=256)
+    out = awq.search_scale(to_dev_bf16(x, dev), to_dev_bf16(w, dev), bits, 128, spec.n_grid)
+    ref = O.search(x, w, bits, 128, spec.n_grid)
+    np.testing.assert_allclose(out["losses"].cpu().numpy(), ref["losses"], rtol=1e-4, atol=0)
+    best = int(out["best_idx"].item())
+    assert ref["losses"][best] <= (1 + 1e-4) * ref["losses"].min()
+    best_s = out["best_s"].cpu().numpy().astype(np.float64)
+    rq, rs, rz = O.pack(*O.quantize(w, best_s, bits, 128))
+    assert np.array_equal(u32(out["qweight"]), rq)
+    assert np.array_equal(out["scales"].cpu().numpy(), rs)
+    assert np.array_equal(out["zeros"].cpu().numpy(), rz)
