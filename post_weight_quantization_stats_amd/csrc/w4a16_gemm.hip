@@ -418,8 +418,11 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
       mfma_half(F0, 1);
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F1, 0);
-      own_dma_done(SA[(i + 2) & 3]);
-      own_dma_done(SB[(i + 2) & 3]);
+      // This wave's copies into stage k+2 were issued one step ago; only this
+      // step's 2 x DPW copies may still be in flight.  (An explicit count: a
+      // dummy LDS read of the stage would also wait for every LDS read.)
+      static_assert(DPW == 2, "the count below assumes 2 copies per operand per step");
+      asm volatile("s_waitcnt vmcnt(4)");
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F1, 1);
       read_frags(F0, SA[(i + 1) & 3], SB[(i + 1) & 3], 0);
