@@ -270,6 +270,34 @@ def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
     return out
 
 
+def bench_gram(awq, xd, wd, spec, bits: int, direct: dict, steps: int, direct_ms: float) -> dict:
+    """The same search with Gram-form losses (G = X^T X once, then per
+    candidate D G D^T on a bf16 x 3 split): a second workload with the same
+    result, reported beside the headline, never in its place."""
+    import torch
+
+    M, K, N, G = spec.M, spec.K, spec.N, spec.n_grid
+    ws = torch.empty(awq.workspace_size(awq.OP_SEARCH_SCALE_GRAM, M, N, K, bits, spec.group, G),
+                     dtype=torch.uint8, device=xd.device)
+    g = awq.search_scale_gram(xd, wd, bits, spec.group, G, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g = awq.search_scale_gram(xd, wd, bits, spec.group, G, workspace=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    la, lg = direct["losses"].double(), g["losses"].double()
+    rel = float(((lg - la).abs() / la.abs()).max().item())
+    same = int(direct["best_idx"].item()) == int(g["best_idx"].item())
+    flops = 2.0 * M * K * K + G * 6.0 * N * K * K
+    log(f"gram-form search: {ms:.2f} ms/layer ({direct_ms / ms:.2f}x the direct form); "
+        f"max relative loss difference {rel:.2e}; same choice {same}")
+    del ws
+    return {"ms_per_layer": ms, "layers_per_s": 1e3 / ms, "speedup_vs_direct": direct_ms / ms,
+            "contraction_flops_per_layer": flops, "max_rel_loss_diff_vs_direct": rel,
+            "same_choice": same}
+
+
 def cpu_baseline(x_bits, w_bits, spec, m_sample: int, n_sample: int) -> dict:
     """Oracle (numpy fp64) on a token prefix x output-row prefix; each phase is
     scaled to the full layer by the dimension it is linear in."""
@@ -305,6 +333,7 @@ def main() -> int:
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped GEMM figures")
+    ap.add_argument("--no-gram", action="store_true", help="skip the Gram-form search figure")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode-shaped GEMM figures (prints them as JSON)")
     ap.add_argument("--cpu-m", type=int, default=4096)
@@ -458,6 +487,10 @@ def main() -> int:
         result["kernels"]["decode_gemm_llama3_8b"] = bench_decode(awq, dev, stream)
     del ws, gemm_ws, yref, b_mid
     torch.cuda.empty_cache()
+    if not args.no_gram:
+        result["variants"] = {"gram_form": bench_gram(awq, xd, wd, spec, bits, out, args.steps,
+                                                      ms_per_step)}
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_m} tokens x {args.cpu_n} rows")
         result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, spec, args.cpu_m, args.cpu_n)

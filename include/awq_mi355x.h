@@ -72,6 +72,7 @@ typedef enum awq_op {
   AWQ_OP_CANDIDATE_SCALES = 3,
   AWQ_OP_DECODE_GEMM = 4,
   AWQ_OP_CANDIDATE_SSE = 5,
+  AWQ_OP_SEARCH_SCALE_GRAM = 6,
 } awq_op;
 
 /* Version of this ABI (AWQ_ABI_VERSION). */
@@ -92,6 +93,7 @@ const char* awq_last_error(void);
  *   op AWQ_OP_DECODE_GEMM:  uses M, N, K, bits, group (0 bytes when K is not
  *                           split across workgroups).
  *   op AWQ_OP_CANDIDATE_SSE: uses M, N.
+ *   op AWQ_OP_SEARCH_SCALE_GRAM: uses M, N, K, bits, group, n_grid.
  * Errors: AWQ_ERR_NULL (bytes NULL), AWQ_ERR_SHAPE, AWQ_ERR_UNSUPPORTED.
  */
 awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t bits,
@@ -250,6 +252,27 @@ awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint1
                             double* losses, int32_t* best_idx, float* best_s, uint32_t* qweight,
                             float* scales, uint8_t* zeros, void* ws, size_t ws_bytes,
                             void* stream);
+
+/*
+ * The same search with the losses in Gram form (an exact identity under the
+ * fold of 1/s into the weight operand):
+ *   loss_i = sum_n D_n G D_n^T / (M N),  D = B_i - W,  G = X^T X,
+ * with G formed once per layer (fp32 sums of exact bf16 products) and D G
+ * evaluated on the matrix cores as a bf16 x 3 split ([hi D | hi D | lo D] .
+ * [hi G | lo G | hi G]^T, about 2^-16 relative).  Per candidate it costs
+ * 6 N K^2 flops instead of 2 M N K, so it pays when 3 K < M (many
+ * calibration tokens); G costs 2 M K^2 once.  Arguments and outputs as in
+ * awq_search_scale (losses agree with it to about 1e-5 relative; the chosen
+ * index can differ only between candidates whose losses tie to that
+ * precision).  Limits: M rounded up to 128 and 3 K at most 2^22.
+ *   ws: awq_workspace_size(AWQ_OP_SEARCH_SCALE_GRAM) bytes (X^T, G and its
+ *       split, one candidate's split difference and D in fp32).
+ */
+awq_status awq_search_scale_gram(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w,
+                                 int64_t N, int32_t bits, int32_t group, int32_t n_grid,
+                                 float* mean_abs, double* losses, int32_t* best_idx, float* best_s,
+                                 uint32_t* qweight, float* scales, uint8_t* zeros, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,11 +17,13 @@ import torch
 from . import build as _build
 
 __all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "quantize_pack",
-           "reference_gemm", "w4a16_gemm", "search_scale", "workspace_size",
-           "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES"]
+           "reference_gemm", "w4a16_gemm", "search_scale", "search_scale_gram", "decode_gemm",
+           "dequant_operand", "candidate_sse", "workspace_size",
+           "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES",
+           "OP_DECODE_GEMM", "OP_CANDIDATE_SSE", "OP_SEARCH_SCALE_GRAM"]
 
 (OP_ACT_STATS, OP_W4A16_GEMM, OP_SEARCH_SCALE, OP_CANDIDATE_SCALES, OP_DECODE_GEMM,
- OP_CANDIDATE_SSE) = 0, 1, 2, 3, 4, 5
+ OP_CANDIDATE_SSE, OP_SEARCH_SCALE_GRAM) = 0, 1, 2, 3, 4, 5, 6
 
 _c_void_p, _i64, _i32, _size_t = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 
@@ -46,6 +48,9 @@ _SIGNATURES = {
                         _c_void_p], _i32),
     "awq_w4a16_decode_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
                                _i32, _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
+    "awq_search_scale_gram": ([_c_void_p, _i64, _i64, _c_void_p, _i64, _i32, _i32, _i32,
+                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                               _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
     "awq_search_scale": ([_c_void_p, _i64, _i64, _c_void_p, _i64, _i32, _i32, _i32, _c_void_p,
                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                           _c_void_p, _size_t, _c_void_p], _i32),
@@ -279,4 +284,33 @@ def search_scale(x: torch.Tensor, w: torch.Tensor, bits: int = 4, group: int = 1
                                   _ptr(out["best_s"]), _ptr(out["qweight"]), _ptr(out["scales"]),
                                   _ptr(out["zeros"]), _ptr(ws), ws.numel(), _stream(dev)),
            "awq_search_scale")
+    return out
+
+
+def search_scale_gram(x: torch.Tensor, w: torch.Tensor, bits: int = 4, group: int = 128,
+                      n_grid: int = 20, workspace: torch.Tensor | None = None) -> dict:
+    """The per-layer search with Gram-form losses (pays when 3K < M); outputs as search_scale."""
+    x, w = _bf16(x, "x"), _bf16(w, "w")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("x and w disagree on K")
+    dev = x.device
+    out = dict(
+        mean_abs=torch.empty(K, dtype=torch.float32, device=dev),
+        losses=torch.empty(n_grid, dtype=torch.float64, device=dev),
+        best_idx=torch.empty(1, dtype=torch.int32, device=dev),
+        best_s=torch.empty(K, dtype=torch.float32, device=dev),
+        qweight=torch.empty((N, K // 8), dtype=torch.int32, device=dev),
+        scales=torch.empty((N, K // group), dtype=torch.float32, device=dev),
+        zeros=torch.empty((N, K // group), dtype=torch.uint8, device=dev),
+    )
+    ws = _workspace(workspace_size(OP_SEARCH_SCALE_GRAM, M, N, K, bits, group, n_grid), dev,
+                    workspace)
+    _check(lib().awq_search_scale_gram(_ptr(x), M, K, _ptr(w), N, bits, group, n_grid,
+                                       _ptr(out["mean_abs"]), _ptr(out["losses"]),
+                                       _ptr(out["best_idx"]), _ptr(out["best_s"]),
+                                       _ptr(out["qweight"]), _ptr(out["scales"]),
+                                       _ptr(out["zeros"]), _ptr(ws), ws.numel(), _stream(dev)),
+           "awq_search_scale_gram")
     return out

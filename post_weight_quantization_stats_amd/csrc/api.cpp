@@ -83,6 +83,34 @@ SearchLayout search_layout(int64_t M, int64_t N, int64_t K, int n_grid) {
   return L;
 }
 
+struct GramLayout {
+  size_t s, inv, scales_ws, stats_ws, xt, g32, gsplit, asplit, d32, partials, total;
+};
+
+GramLayout gram_layout(int64_t M, int64_t N, int64_t K, int n_grid) {
+  using awq::align_up;
+  GramLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const int64_t Mp = awq::gram_padded_m(M);
+  L.s = take((size_t)n_grid * K * sizeof(float));
+  L.inv = take((size_t)n_grid * K * sizeof(float));
+  L.scales_ws = take(awq::scales_ws_bytes(K, n_grid));
+  L.stats_ws = take(awq::stats_ws_bytes(M, K));
+  L.xt = take((size_t)K * Mp * sizeof(uint16_t));              // X^T, zero-padded
+  L.g32 = take((size_t)K * K * sizeof(float));                 // G = X^T X
+  L.gsplit = take((size_t)K * 3 * K * sizeof(uint16_t));       // [hi G | lo G | hi G]
+  L.asplit = take((size_t)N * 3 * K * sizeof(uint16_t));       // [hi D | hi D | lo D]
+  L.d32 = take((size_t)N * K * sizeof(float));                 // D = B - W
+  L.partials = take((size_t)n_grid * awq::gemm_tiles(N, K) * sizeof(double));
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,6 +170,17 @@ awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32
         if (M < 0 || M > awq::kDecodeMaxM || N < 0 || N > kMaxGemmN)
           return fail(AWQ_ERR_SHAPE, "decode GEMM needs 0 <= M <= %lld", (long long)awq::kDecodeMaxM);
         *bytes = (M == 0 || N == 0) ? 0 : awq::decode_plan(M, N, K).ws_bytes;
+        return ok();
+      }
+      case AWQ_OP_SEARCH_SCALE_GRAM: {
+        awq_status st = check_quant_params(bits, group);
+        if (st != AWQ_OK) return st;
+        if ((st = check_k(K, group)) != AWQ_OK) return st;
+        if (M <= 0 || N <= 0 || awq::gram_padded_m(M) > (int64_t(1) << 22) || N > kMaxGemmN ||
+            3 * K > (int64_t(1) << 22))
+          return fail(AWQ_ERR_SHAPE, "Gram search needs 1 <= M <= 2^22, 1 <= N <= 2^22, 3K <= 2^22");
+        if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_UNSUPPORTED, "n_grid must be in [1, 64]");
+        *bytes = gram_layout(M, N, K, n_grid).total;
         return ok();
       }
       case AWQ_OP_CANDIDATE_SCALES:
@@ -365,6 +404,85 @@ awq_status awq_candidate_sse(const uint16_t* x, int64_t M, int64_t N, int64_t K,
     op.partials = (double*)ws;
     AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
     AWQ_TRY_LAUNCH(awq::launch_loss_reduce((const double*)ws, awq::gemm_tiles(M, N), 1, 1.0, sse, s));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_search_scale_gram(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w,
+                                 int64_t N, int32_t bits, int32_t group, int32_t n_grid,
+                                 float* mean_abs, double* losses, int32_t* best_idx, float* best_s,
+                                 uint32_t* qweight, float* scales, uint8_t* zeros, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  try {
+    if (x == nullptr || w == nullptr || mean_abs == nullptr || losses == nullptr ||
+        best_idx == nullptr || best_s == nullptr || qweight == nullptr || scales == nullptr ||
+        zeros == nullptr)
+      return fail(AWQ_ERR_NULL, "all tensor arguments are required");
+    awq_status st = check_quant_params(bits, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (M <= 0 || N <= 0 || awq::gram_padded_m(M) > (int64_t(1) << 22) || N > kMaxGemmN ||
+        3 * K > (int64_t(1) << 22))
+      return fail(AWQ_ERR_SHAPE, "Gram search needs 1 <= M <= 2^22, 1 <= N <= 2^22, 3K <= 2^22");
+    if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_UNSUPPORTED, "n_grid must be in [1, 64]");
+    if (misaligned(x) || misaligned(w) || misaligned(mean_abs) || misaligned(best_s) ||
+        misaligned(qweight) || misaligned(ws) || ((uintptr_t)scales & 3u) ||
+        ((uintptr_t)losses & 7u) || ((uintptr_t)best_idx & 3u))
+      return fail(AWQ_ERR_ALIGN, "tensor pointers must be 16-byte aligned (scales/best_idx 4, losses 8)");
+    const GramLayout L = gram_layout(M, N, K, n_grid);
+    if (ws == nullptr || ws_bytes < L.total)
+      return fail(AWQ_ERR_WORKSPACE, "search_scale_gram needs %zu workspace bytes", L.total);
+
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
+    float* sc = (float*)(base + L.s);
+    float* inv = (float*)(base + L.inv);
+    uint16_t* xt = (uint16_t*)(base + L.xt);
+    float* g32 = (float*)(base + L.g32);
+    uint16_t* gsplit = (uint16_t*)(base + L.gsplit);
+    uint16_t* asplit = (uint16_t*)(base + L.asplit);
+    float* d32 = (float*)(base + L.d32);
+    double* partials = (double*)(base + L.partials);
+    const int64_t Mp = awq::gram_padded_m(M);
+    const int64_t T = awq::gemm_tiles(N, K);
+
+    AWQ_TRY_LAUNCH(awq::launch_act_stats(x, M, K, mean_abs, (double*)(base + L.stats_ws), s));
+    AWQ_TRY_LAUNCH(awq::launch_candidate_scales(mean_abs, K, n_grid, sc, inv, base + L.scales_ws, s));
+    // G = X^T X once per layer (fp32 accumulation of exact bf16 products).
+    AWQ_TRY_LAUNCH(awq::launch_transpose_pad(x, M, K, xt, s));
+    {
+      awq::GemmOperands op{};
+      op.x = xt;
+      op.M = K;
+      op.N = K;
+      op.K = Mp;
+      op.w = xt;
+      op.y = g32;
+      AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
+    }
+    AWQ_TRY_LAUNCH(awq::launch_gram_split(g32, K, gsplit, s));
+    // Per candidate: D = B_i - W, then sum_n D_n G D_n^T as the dot of
+    // [hi D | hi D | lo D] . [hi G | lo G | hi G]^T with D in the epilogue.
+    for (int i = 0; i < n_grid; ++i) {
+      AWQ_TRY_LAUNCH(awq::launch_quantize_diff(w, N, K, sc + (int64_t)i * K, inv + (int64_t)i * K,
+                                               bits, asplit, d32, s));
+      awq::GemmOperands op{};
+      op.x = asplit;
+      op.M = N;
+      op.N = K;
+      op.K = 3 * K;
+      op.w = gsplit;
+      op.y_ref = d32;
+      op.partials = partials + (int64_t)i * T;
+      op.dot = true;
+      AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
+    }
+    AWQ_TRY_LAUNCH(awq::launch_loss_reduce(partials, T, n_grid, (double)M * (double)N, losses, s));
+    AWQ_TRY_LAUNCH(awq::launch_argmin(losses, n_grid, best_idx, s));
+    AWQ_TRY_LAUNCH(awq::launch_select_row(sc, best_idx, K, best_s, s));
+    AWQ_TRY_LAUNCH(awq::launch_quantize_pack(w, N, K, sc, best_idx, bits, qweight, scales, zeros, s));
     return ok();
   } catch (...) {
     return fail(AWQ_ERR_LAUNCH, "internal error");

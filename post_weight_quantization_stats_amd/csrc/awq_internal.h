@@ -58,6 +58,18 @@ hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, cons
                                    const float* inv_s, int bits, uint16_t* b_out,
                                    hipStream_t stream);
 
+// Candidate difference for the Gram-form loss: d32[n][k] = B - W (fp32) and
+// a_split[n] = [hi(D) | hi(D) | lo(D)] (bf16 [N][3K]).
+hipError_t launch_quantize_diff(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                                const float* inv_s, int bits, uint16_t* a_split, float* d32,
+                                hipStream_t stream);
+
+// ---- Gram form: X^T (bf16 [K][Mp], zero-padded) and the split G operand ----
+int64_t gram_padded_m(int64_t M);
+hipError_t launch_transpose_pad(const uint16_t* x, int64_t M, int64_t K, uint16_t* xt,
+                                hipStream_t stream);
+hipError_t launch_gram_split(const float* g, int64_t K, uint16_t* out, hipStream_t stream);
+
 struct GemmOperands {
   const uint16_t* x;        // bf16 [M][K]
   int64_t M, N, K;
@@ -70,6 +82,7 @@ struct GemmOperands {
   const float* y_ref;       // [M][N] or NULL
   float* y;                 // [M][N] or NULL
   double* partials;         // [tiles] fp64 SSE per tile, or NULL
+  bool dot;                 // bf16 operand: partials hold sum(Y * y_ref) instead
 };
 hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream);
 

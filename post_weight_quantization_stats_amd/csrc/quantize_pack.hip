@@ -106,17 +106,22 @@ __device__ __forceinline__ uint32_t pack8(const float* q) {
   return w;
 }
 
-// kDequant = false: packed codes, steps and zeros.  kDequant = true: the
+// Output modes.  kPack: packed codes, steps and zeros.  kOperand: the
 // search's weight operand B = bf16(f32(f32((q - z) * step) * inv_s[k])) as a
 // bf16 [N][K] matrix, written once per candidate so that the contraction
 // reads a plain bf16 operand instead of dequantizing it again for every tile
-// of calibration tokens.
-template <int BITS, bool kDequant>
+// of calibration tokens.  kDiff: D = B - W (exact in fp32: two bf16 values of
+// similar size) as fp32 [N][K], and the split operand [hi(D) | hi(D) | lo(D)]
+// as bf16 [N][3K] (hi = RNE to bf16, lo = RNE of the exact remainder) for the
+// Gram-form loss D G D^T.
+enum QuantMode { kPack = 0, kOperand = 1, kDiff = 2 };
+
+template <int BITS, int kMode>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t K, const float* __restrict__ s,
     const int32_t* __restrict__ s_sel, const float* __restrict__ inv_s,
     uint32_t* __restrict__ qweight, float* __restrict__ scales, uint8_t* __restrict__ zeros,
-    uint16_t* __restrict__ bout) {
+    uint16_t* __restrict__ bout, float* __restrict__ dout) {
   const int64_t G = K / kGroup;
   const int64_t g = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x / kLanesPerGroup);
   const int t8 = threadIdx.x % kLanesPerGroup;
@@ -135,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   const float* srow = s;
   if (s != nullptr && s_sel != nullptr) srow = s + (int64_t)max(*s_sel, 0) * K;
   if (srow != nullptr) load16(srow, sv);
-  if constexpr (kDequant) {
+  if constexpr (kMode != kPack) {
     if (inv_s != nullptr) load16(inv_s, iv);
   }
 
@@ -159,6 +164,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       ws[8 * c + 4] = bf16_lo(v[r][c].z); ws[8 * c + 5] = bf16_hi(v[r][c].z);
       ws[8 * c + 6] = bf16_lo(v[r][c].w); ws[8 * c + 7] = bf16_hi(v[r][c].w);
     }
+    float wv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) wv[j] = ws[j];
     if (srow != nullptr) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) ws[j] *= sv[j];
@@ -166,21 +174,47 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     float q[16], step, z;
     quantize16<BITS>(ws, q, step, z);
     if (!(gvalid && n < N)) continue;
-    if constexpr (kDequant) {
+    if constexpr (kMode != kPack) {
+      float bv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        bv[j] = (q[j] - z) * step;                  // exact difference, one rounding
+        if (inv_s != nullptr) bv[j] *= iv[j];
+      }
       uint32_t d[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float lo = (q[2 * j] - z) * step;            // exact difference, one rounding
-        float hi = (q[2 * j + 1] - z) * step;
-        if (inv_s != nullptr) {
-          lo *= iv[2 * j];
-          hi *= iv[2 * j + 1];
+      for (int j = 0; j < 8; ++j) d[j] = pack_bf16x2(bv[2 * j], bv[2 * j + 1]);
+      if constexpr (kMode == kOperand) {
+        uint4* dst = (uint4*)(bout + n * K + k0);
+        dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
+        dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
+      } else {
+        float dd[16];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          dd[2 * j] = bf16_lo(d[j]) - wv[2 * j];
+          dd[2 * j + 1] = bf16_hi(d[j]) - wv[2 * j + 1];
         }
-        d[j] = pack_bf16x2(lo, hi);
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          hi[j] = pack_bf16x2(dd[2 * j], dd[2 * j + 1]);
+          lo[j] = pack_bf16x2(dd[2 * j] - bf16_lo(hi[j]), dd[2 * j + 1] - bf16_hi(hi[j]));
+        }
+        float4* df = (float4*)(dout + n * K + k0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          df[c] = make_float4(dd[4 * c], dd[4 * c + 1], dd[4 * c + 2], dd[4 * c + 3]);
+        uint16_t* arow = bout + n * 3 * K;
+        const uint4 h0 = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        const uint4 h1 = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+        ((uint4*)(arow + k0))[0] = h0;
+        ((uint4*)(arow + k0))[1] = h1;
+        ((uint4*)(arow + K + k0))[0] = h0;
+        ((uint4*)(arow + K + k0))[1] = h1;
+        ((uint4*)(arow + 2 * K + k0))[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        ((uint4*)(arow + 2 * K + k0))[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
       }
-      uint4* dst = (uint4*)(bout + n * K + k0);
-      dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
-      dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
     } else {
       *(uint2*)(qweight + n * (K / 8) + k0 / 8) = make_uint2(pack8(q), pack8(q + 8));
       if (t8 == 0) {
@@ -199,11 +233,11 @@ hipError_t launch_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const f
   if (N == 0) return hipSuccess;
   dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
   if (bits == 4)
-    quantize_kernel<4, false><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, nullptr, qweight,
-                                                             scales, zeros, nullptr);
+    quantize_kernel<4, kPack><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, nullptr, qweight,
+                                                             scales, zeros, nullptr, nullptr);
   else
-    quantize_kernel<3, false><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, nullptr, qweight,
-                                                             scales, zeros, nullptr);
+    quantize_kernel<3, kPack><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, nullptr, qweight,
+                                                             scales, zeros, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -213,11 +247,25 @@ hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, cons
   if (N == 0) return hipSuccess;
   dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
   if (bits == 4)
-    quantize_kernel<4, true><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
-                                                            nullptr, nullptr, b_out);
+    quantize_kernel<4, kOperand><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
+                                                                nullptr, nullptr, b_out, nullptr);
   else
-    quantize_kernel<3, true><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
-                                                            nullptr, nullptr, b_out);
+    quantize_kernel<3, kOperand><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
+                                                                nullptr, nullptr, b_out, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_diff(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                                const float* inv_s, int bits, uint16_t* a_split, float* d32,
+                                hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
+  if (bits == 4)
+    quantize_kernel<4, kDiff><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
+                                                             nullptr, nullptr, a_split, d32);
+  else
+    quantize_kernel<3, kDiff><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
+                                                             nullptr, nullptr, a_split, d32);
   return hipGetLastError();
 }
 

@@ -195,8 +195,9 @@ struct CodeRegs {
   uint32_t zero;
 };
 
-// kStoreY: write the fp32 product; kSse: fp64 sum of (Y - Y_ref)^2 per tile.
-template <bool kInt4, bool kInvS, int WN, bool kStoreY, bool kSse>
+// kStoreY: write the fp32 product; kSse: fp64 sum of (Y - Y_ref)^2 per tile,
+// or with kDot the fp64 sum of Y * Y_ref (a quadratic form's last factor).
+template <bool kInt4, bool kInvS, int WN, bool kStoreY, bool kSse, bool kDot = false>
 __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
                                                                     const float* __restrict__ inv_s) {
   // The body exists only in the device pass; the host pass needs just the
@@ -519,9 +520,14 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
           for (int r = 0; r < 16; ++r) {
             const int rho = ii * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);   // row within the phase
             const float yv = (rho < kRowsPerArr ? mine0 : mine1)[(rho % kRowsPerArr) * TN + j * 32 + lr];
-            float d = acc[i][j][r] - yv;
-            d = col_ok[j] ? d : 0.f;
-            dpart += (double)d * (double)d;
+            if constexpr (kDot) {
+              const double prod = (double)acc[i][j][r] * (double)yv;   // exact
+              dpart += col_ok[j] ? prod : 0.0;
+            } else {
+              float d = acc[i][j][r] - yv;
+              d = col_ok[j] ? d : 0.f;
+              dpart += (double)d * (double)d;
+            }
           }
         }
         sse += dpart;
@@ -565,7 +571,9 @@ hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream) {
   // bf16 operand: 8 waves (two per SIMD) measured faster; INT4: the dequant
   // VALU work favours 4 waves with 128x128 tiles each.
   const bool y = op.y != nullptr, sse = op.partials != nullptr;
-  if (op.qweight == nullptr) {
+  if (op.qweight == nullptr && op.dot) {
+    gemm_kernel<false, false, 4, false, true, true><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
+  } else if (op.qweight == nullptr) {
     if (sse)
       gemm_kernel<false, false, 4, false, true><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
     else

@@ -215,3 +215,34 @@ def test_candidate_sse_errors():
     assert f(FAKE, 4, 8, 128, FAKE, FAKE, FAKE + 4, FAKE, 1 << 20, None) == ALIGN
     assert f(FAKE, 4, 8, 128, FAKE, FAKE, FAKE, None, 0, None) == WORKSPACE
     assert f(FAKE, 4, 8, 128, FAKE, FAKE, FAKE, FAKE, 8, None) == WORKSPACE
+
+
+def test_search_gram_errors_and_workspace():
+    f = awq.lib().awq_search_scale_gram
+
+    def call(x=FAKE, M=256, K=512, w=FAKE, N=512, bits=4, group=128, n_grid=20, ws=FAKE, wsb=1 << 40,
+             best=FAKE):
+        return f(x, M, K, w, N, bits, group, n_grid, FAKE, FAKE, best, FAKE, FAKE, FAKE, FAKE, ws,
+                 wsb, None)
+
+    assert call(x=None) == NULL
+    assert call(best=None) == NULL
+    assert call(M=0) == SHAPE
+    assert call(N=0) == SHAPE
+    assert call(K=384 + 8) == SHAPE
+    assert call(M=(1 << 22) + 1) == SHAPE          # padded token count above the limit
+    assert call(bits=1) == UNSUPPORTED
+    assert call(n_grid=65) == UNSUPPORTED
+    assert call(w=FAKE_MIS) == ALIGN
+    assert call(ws=None) == WORKSPACE
+    need = ws_size(awq.OP_SEARCH_SCALE_GRAM, 256, 512, 512)[1]
+    assert call(wsb=need - 1) == WORKSPACE
+    assert str(need) in awq.lib().awq_last_error().decode()
+    # the workspace holds X^T (padded), G in fp32, both split operands and D
+    M, N, K = 65536, 12288, 4096
+    st, b = ws_size(awq.OP_SEARCH_SCALE_GRAM, M, N, K)
+    assert st == OK
+    core = K * M * 2 + K * K * 4 + K * 3 * K * 2 + N * 3 * K * 2 + N * K * 4
+    assert core <= b < core + 64 * 2 ** 20
+    assert ws_size(awq.OP_SEARCH_SCALE_GRAM, 300, 200, 384)[1] >= 384 * 384 * 2
+    assert ws_size(awq.OP_SEARCH_SCALE_GRAM, 256, 512, 500)[0] == SHAPE

@@ -134,6 +134,26 @@ def test_fullsize_search(dev, qkv, qkv_stats):
         assert np.all(best_s[cols] > np.median(best_s))
 
 
+def test_fullsize_search_gram(dev, qkv):
+    """The Gram-form search at full size against the direct one: same
+    statistics and scales, losses within 2e-5 relative, the same choice
+    unless two losses tie to that precision."""
+    announce("full-size search_scale_gram")
+    x, w, spec, xd, wd = qkv
+    a = awq.search_scale(xd, wd, 4, 128, spec.n_grid)
+    g = awq.search_scale_gram(xd, wd, 4, 128, spec.n_grid)
+    torch.cuda.synchronize()
+    assert torch.equal(a["mean_abs"], g["mean_abs"])
+    la, lg = a["losses"].cpu().numpy(), g["losses"].cpu().numpy()
+    np.testing.assert_allclose(lg, la, rtol=2e-5, atol=0)
+    ib, gb = int(a["best_idx"].item()), int(g["best_idx"].item())
+    assert gb == int(np.argmin(lg))
+    assert ib == gb or abs(la[ib] - la[gb]) <= 2e-5 * la[ib]
+    if ib == gb:
+        for k in ("best_s", "qweight", "scales", "zeros"):
+            assert torch.equal(a[k], g[k]), k
+
+
 # Every other workload's layer shapes (real K, dtype and activation recipe),
 # at 384 tokens and the first 256 output rows, against the oracle's search.
 OTHER_LAYERS = [("llama2_7b_mlp", "gate_up", 4), ("llama2_7b_mlp", "down", 4),

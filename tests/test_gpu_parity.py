@@ -259,6 +259,43 @@ def test_search_scale(dev, shape, bits):
     assert np.array_equal(out["zeros"].cpu().numpy(), rz)
 
 
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_search_scale_gram(dev, shape, bits):
+    """Gram-form losses against the oracle's (fp64, Gram form), 1e-4 relative."""
+    announce("search_scale_gram", ids(shape), bits)
+    x, w = layer(shape)
+    n_grid = 20
+    out = awq.search_scale_gram(to_dev_bf16(x, dev), to_dev_bf16(w, dev), bits, 128, n_grid)
+    torch.cuda.synchronize()
+    ref = O.search(x, w, bits, 128, n_grid, loss_form="gram")
+    losses = out["losses"].cpu().numpy()
+    np.testing.assert_allclose(losses, ref["losses"], rtol=1e-4, atol=0)
+    best = int(out["best_idx"].item())
+    assert ref["losses"][best] <= (1 + 1e-4) * ref["losses"].min()
+    best_s = out["best_s"].cpu().numpy().astype(np.float64)
+    assert ulp_distance_f32(best_s, ref["s"][best]).max() <= 1
+    rq, rs, rz = O.pack(*O.quantize(w, best_s, bits, 128))
+    assert np.array_equal(u32(out["qweight"]), rq)
+    assert np.array_equal(out["scales"].cpu().numpy(), rs)
+    assert np.array_equal(out["zeros"].cpu().numpy(), rz)
+
+
+def test_search_gram_matches_direct(dev):
+    """Both forms on one layer: same statistics, losses within 2e-5 relative."""
+    announce("search gram vs direct")
+    x, w = layer(SHAPES[5])
+    xd, wd = to_dev_bf16(x, dev), to_dev_bf16(w, dev)
+    a = awq.search_scale(xd, wd)
+    g = awq.search_scale_gram(xd, wd)
+    torch.cuda.synchronize()
+    assert torch.equal(a["mean_abs"], g["mean_abs"])
+    la, lg = a["losses"].cpu().numpy(), g["losses"].cpu().numpy()
+    np.testing.assert_allclose(lg, la, rtol=2e-5, atol=0)
+    ib, gb = int(a["best_idx"].item()), int(g["best_idx"].item())
+    assert ib == gb or abs(la[ib] - la[gb]) <= 2e-5 * la[ib]
+
+
 def test_search_is_bit_reproducible(dev):
     announce("search determinism")
     x, w = layer(SHAPES[2])
