@@ -35,9 +35,9 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "AWQ search: layers/s + W4A16 GEMM TFLOP/s (% MFMA peak), quant GB/s (% HBM)"
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "candidate_sse_llama2_7b_qkv_traffic.txt")
-# The search's per-candidate contraction with the squared-error epilogue.
-DOMINANT_KERNEL = "gemm_kernel<false, false, 4, false, true>"
+TRAFFIC_FILE = os.path.join(PROFILES, "search_contraction_llama2_7b_qkv_traffic.txt")
+# The search's per-candidate contraction X . D^T with the sum-of-squares epilogue.
+DOMINANT_KERNEL = "gemm_kernel<false, false, 4, false, true, false, true>"
 GEMM_SOURCES = ["w4a16_gemm.hip", "device_common.h", "awq_internal.h"]
 
 
@@ -73,12 +73,23 @@ def committed_traffic():
 # ---- rocprofv3 output summaries (run on the host after a profiled bench) ----
 
 KERNEL_LABELS = [
-    ("gemm_kernel<false, false, 4, false, true>", "candidate_sse (bf16 operand, squared-error epilogue)"),
-    ("gemm_kernel<false, false, 4, true, false>", "reference_gemm (bf16 operand, fp32 Y_ref)"),
-    ("gemm_kernel<true, true, 2, false, true>", "w4a16_gemm_sse (INT4 operand, 1/s folded, SSE epilogue)"),
+    ("gemm_kernel<false, false, 4, false, true, false, true>",
+     "search contraction X.D^T (difference operand, sum of squares)"),
+    ("gemm_kernel<false, false, 4, false, true, true, false>",
+     "Gram-form contraction (split D . split G, dot epilogue)"),
+    ("gemm_kernel<false, false, 4, false, true, false, false>",
+     "candidate_sse vs y_ref (bf16 operand, squared-error epilogue)"),
+    ("gemm_kernel<false, false, 4, true, false", "reference_gemm / Gram matrix (bf16, fp32 out)"),
+    ("gemm_kernel<true, true, 2, false, true", "w4a16_gemm_sse (INT4 operand, 1/s folded, SSE epilogue)"),
     ("gemm_kernel<true", "w4a16_gemm (INT4 operand, other epilogues)"),
-    ("quantize_kernel<4, true>", "dequant_operand (quantize -> bf16 operand)"),
-    ("quantize_kernel<3, true>", "dequant_operand (quantize -> bf16 operand)"),
+    ("quantize_kernel<4, 1>", "dequant_operand (quantize -> bf16 B)"),
+    ("quantize_kernel<3, 1>", "dequant_operand (quantize -> bf16 B)"),
+    ("quantize_kernel<4, 2>", "Gram-form quantize (split D, fp32 D)"),
+    ("quantize_kernel<3, 2>", "Gram-form quantize (split D, fp32 D)"),
+    ("quantize_kernel<4, 3>", "diff_operand (quantize -> bf16 B - W)"),
+    ("quantize_kernel<3, 3>", "diff_operand (quantize -> bf16 B - W)"),
+    ("transpose_pad_kernel", "X^T (Gram form)"),
+    ("gram_split_kernel", "G split (Gram form)"),
     ("decode_gemm", "decode W4A16 GEMM (M <= 16)"),
     ("decode_reduce", "decode split-K reduce"),
     ("act_stats_partial", "act_stats partial sums"),
@@ -416,12 +427,15 @@ def main() -> int:
     i_mid = G // 2
     qw, sc, ze = awq.quantize_pack(wd, s_all[i_mid], bits, spec.group)
     b_mid = awq.dequant_operand(wd, s_all[i_mid], inv_all[i_mid], bits, spec.group)
+    d_mid = awq.diff_operand(wd, s_all[i_mid], inv_all[i_mid], bits, spec.group)
     yref = awq.reference_gemm(xd, wd)
     gemm_ws = torch.empty(max(awq.workspace_size(awq.OP_W4A16_GEMM, M, N, K), 256),
                           dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    t_sse = event_time_ms(lambda: awq.candidate_sse(xd, b_mid, yref, workspace=gemm_ws), reps,
+    t_sse = event_time_ms(lambda: awq.candidate_sse(xd, d_mid, None, workspace=gemm_ws), reps,
                           stream)
+    t_sse_y = event_time_ms(lambda: awq.candidate_sse(xd, b_mid, yref, workspace=gemm_ws),
+                            max(2, reps // 2), stream)
     t_w4 = event_time_ms(lambda: awq.w4a16_gemm(xd, qw, sc, ze, bits, spec.group,
                                                 inv_s=inv_all[i_mid], y_ref=yref,
                                                 return_y=False, workspace=gemm_ws),
@@ -432,17 +446,21 @@ def main() -> int:
                             reps * 5, stream)
     t_deq = event_time_ms(lambda: awq.dequant_operand(wd, s_all[i_mid], inv_all[i_mid], bits,
                                                       spec.group), reps * 5, stream)
+    t_diff = event_time_ms(lambda: awq.diff_operand(wd, s_all[i_mid], inv_all[i_mid], bits,
+                                                    spec.group), reps * 5, stream)
     flops = 2.0 * M * N * K
     tf = lambda ms: flops / (ms * 1e-3) / 1e12
     stats_bytes = 2.0 * M * K + 4.0 * K
     quant_bytes = 2.0 * N * K + 4.0 * K + N * K / 2 + 5.0 * N * K / spec.group
     deq_bytes = 2.0 * N * K + 8.0 * K + 2.0 * N * K
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
-    log(f"candidate sse {t_sse:.3f} ms = {tf(t_sse):.1f} TFLOP/s; packed w4a16+sse {t_w4:.3f} ms "
+    log(f"search contraction {t_sse:.3f} ms = {tf(t_sse):.1f} TFLOP/s; against y_ref "
+        f"{t_sse_y:.3f} ms = {tf(t_sse_y):.1f} TFLOP/s; packed w4a16+sse {t_w4:.3f} ms "
         f"= {tf(t_w4):.1f} TFLOP/s; reference {t_ref:.3f} ms = {tf(t_ref):.1f} TFLOP/s")
     log(f"stats {t_stats * 1e3:.1f} us = {gbs(stats_bytes, t_stats):.0f} GB/s; quantize+pack "
         f"{t_quant * 1e3:.1f} us = {gbs(quant_bytes, t_quant):.0f} GB/s; dequant operand "
-        f"{t_deq * 1e3:.1f} us = {gbs(deq_bytes, t_deq):.0f} GB/s")
+        f"{t_deq * 1e3:.1f} us = {gbs(deq_bytes, t_deq):.0f} GB/s; difference operand "
+        f"{t_diff * 1e3:.1f} us = {gbs(deq_bytes, t_diff):.0f} GB/s")
 
     def mfma_entry(ms):
         return {"ms": ms, "tflops": tf(ms), "frac_mfma_peak": tf(ms) / PEAK_BF16_TFLOPS}
@@ -469,23 +487,25 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": tf(t_sse), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": tf(t_sse) / PEAK_BF16_TFLOPS,
                      "traffic": committed_traffic(),
-                     "kernel": "per-candidate contraction X.B^T with fused squared error",
+                     "kernel": "per-candidate contraction X.D^T (D = B - W) with fused sum of squares",
                      "flops_per_launch": flops, "ms_per_launch": t_sse,
-                     "algorithmic_bytes_per_launch": 2.0 * M * K + 2.0 * N * K + 4.0 * M * N,
+                     "algorithmic_bytes_per_launch": 2.0 * M * K + 2.0 * N * K,
                      "kernel_source_hash": gemm_source_hash()},
         "kernels": {
-            "candidate_sse": mfma_entry(t_sse),
+            "search_contraction": mfma_entry(t_sse),
+            "candidate_sse_vs_yref": mfma_entry(t_sse_y),
             "w4a16_gemm_sse": mfma_entry(t_w4),
             "reference_gemm": mfma_entry(t_ref),
             "act_stats": hbm_entry(stats_bytes, t_stats),
             "quantize_pack": hbm_entry(quant_bytes, t_quant),
             "dequant_operand": hbm_entry(deq_bytes, t_deq),
+            "diff_operand": hbm_entry(deq_bytes, t_diff),
         },
         "cpu_baseline": None,
     }
     if not args.no_decode:
         result["kernels"]["decode_gemm_llama3_8b"] = bench_decode(awq, dev, stream)
-    del ws, gemm_ws, yref, b_mid
+    del ws, gemm_ws, yref, b_mid, d_mid
     torch.cuda.empty_cache()
     if not args.no_gram:
         result["variants"] = {"gram_form": bench_gram(awq, xd, wd, spec, bits, out, args.steps,

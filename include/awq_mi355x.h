@@ -159,6 +159,22 @@ awq_status awq_dequant_operand(const uint16_t* w, int64_t N, int64_t K, const fl
                                void* stream);
 
 /*
+ * Difference operand of one candidate scale: the search's weight operand
+ * minus the original weight, so that X . D^T is the candidate's output error
+ * X . B^T - X . W^T directly (robotsatlas "How it works": the scale minimises
+ * the error between the quantized and the original layer outputs).
+ *   d[n][k] = bf16( f32(b[n][k] - w[n][k]) )   (RNE to bf16)
+ * with b exactly as awq_dequant_operand writes it.  The rounding is exact: a
+ * nonzero b has |w s| >= step / 2, so b and w share a sign and b / w lies in
+ * [1/2, 2] (up to the roundings of s and 1/s); by Sterbenz's lemma their
+ * difference is a bf16 value.  Arguments as for awq_dequant_operand; d bf16
+ * [N][K] output.  N == 0 is a no-op (pointers are then ignored).
+ */
+awq_status awq_diff_operand(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                            const float* inv_s, int32_t bits, int32_t group, uint16_t* d,
+                            void* stream);
+
+/*
  * Dense reference product Y = X . W^T (robotsatlas "How it works": the output
  * error is measured against the layer's unquantized output).  bf16 operands,
  * fp32 accumulation on the matrix cores, fp32 output.
@@ -175,7 +191,9 @@ awq_status awq_reference_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K
  * with bf16 X [M][K] and B [N][K] (a candidate's operand from
  * awq_dequant_operand), fp32 accumulation on the matrix cores, and the error
  * reduced in fp64 in a fixed order (bit-reproducible).  The product is never
- * written to memory.  y_ref f32 [M][N]; sse f64 [1];
+ * written to memory.  y_ref f32 [M][N], or NULL for sse = sum (X . B^T)^2
+ * (B then a difference operand from awq_diff_operand: the search's form);
+ * sse f64 [1];
  * ws: awq_workspace_size(AWQ_OP_CANDIDATE_SSE) bytes.  M == 0 or N == 0 sets
  * sse to 0.
  */
@@ -235,17 +253,19 @@ awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_
  * calibration tokens).  Steps, all on `stream` with no host synchronisation:
  *   1. mean_abs = awq_act_stats(x)
  *   2. s, inv_s = awq_candidate_scales(mean_abs, n_grid)
- *   3. y_ref = X . W^T (fp32, kept in the workspace)
- *   4. for each candidate i: quantize W . diag(s_i), then
- *      loss[i] = sum (X . B_i^T - y_ref)^2 / (M N)   (fp64, fixed order)
+ *   3. for each candidate i: quantize W . diag(s_i), write the difference
+ *      operand D_i = B_i - W (awq_diff_operand; exact in bf16), then
+ *      loss[i] = sum (X . D_i^T)^2 / (M N)   (fp64, fixed order)
+ *      X . D_i^T equals X . B_i^T - X . W^T, the output error against the
+ *      unquantized layer, so no reference output is formed.
  *   5. best = first index of the smallest loss (NaN never wins; -1 if every
  *      loss is NaN, in which case candidate 0 is written below)
  *   6. best_s = s[best]; qweight/scales/zeros = quantize_pack(w, best_s)
  *   x bf16 [M][K] (M >= 1), w bf16 [N][K] (N >= 1)
  *   mean_abs f32 [K], losses f64 [n_grid], best_idx i32 [1], best_s f32 [K],
  *   qweight u32 [N][K/8], scales f32 [N][K/group], zeros u8 [N][K/group]
- *   ws: awq_workspace_size(AWQ_OP_SEARCH_SCALE) bytes (it holds y_ref, 4*M*N,
- *       and one candidate's bf16 weight operand, 2*N*K).
+ *   ws: awq_workspace_size(AWQ_OP_SEARCH_SCALE) bytes (it holds one
+ *       candidate's bf16 difference operand, 2*N*K, and per-tile partials).
  */
 awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
                             int32_t bits, int32_t group, int32_t n_grid, float* mean_abs,

@@ -39,6 +39,10 @@ contract the GPU library implements):
   dequantized B    B[n,k] = bf16( f32( f32((q - z) * step) * inv_s[k] ) )
                    (1/s folded into the weight operand; the activation operand
                    is the caller's bf16 X, unchanged)
+  difference       D = bf16(f32(B - W)), the operand whose product with X is
+                   the output error X.B^T - X.W^T; no rounding happens there:
+                   a nonzero B has |W s| >= step/2, so B/W lies in [1/2, 2]
+                   and by Sterbenz's lemma B - W is a bf16 value
   loss             MSE over all M*N outputs of X.B^T against X.W^T, fp64
   selection        first index of the minimum loss (NaN never wins; all-NaN
                    gives -1)
@@ -246,6 +250,15 @@ def dequant_operand(q, z, step, group: int, inv32=None) -> np.ndarray:
     if inv32 is not None:
         d = f32(d * np.asarray(inv32, np.float64)[None, :])
     return bf16_round(d)
+
+
+def diff_operand(w_bits, b_values) -> np.ndarray:
+    """D[n,k] = bf16(f32(B[n,k] - W[n,k])) as float64 values (B from dequant_operand).
+
+    B - W is exact in fp64 (two bf16 values); the f32 then bf16 roundings are
+    the contract's, and for the quantizer's B they change nothing (Sterbenz).
+    """
+    return bf16_round(f32(np.asarray(b_values, np.float64) - bf16_bits_to_f64(w_bits)))
 
 
 def gemm(x_bits, b_values) -> np.ndarray:

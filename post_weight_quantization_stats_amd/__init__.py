@@ -18,7 +18,7 @@ from . import build as _build
 
 __all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "quantize_pack",
            "reference_gemm", "w4a16_gemm", "search_scale", "search_scale_gram", "decode_gemm",
-           "dequant_operand", "candidate_sse", "workspace_size",
+           "dequant_operand", "diff_operand", "candidate_sse", "workspace_size",
            "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES",
            "OP_DECODE_GEMM", "OP_CANDIDATE_SSE", "OP_SEARCH_SCALE_GRAM"]
 
@@ -40,6 +40,8 @@ _SIGNATURES = {
                            _c_void_p, _c_void_p], _i32),
     "awq_dequant_operand": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
                              _c_void_p], _i32),
+    "awq_diff_operand": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
+                          _c_void_p], _i32),
     "awq_candidate_sse": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                            _size_t, _c_void_p], _i32),
     "awq_reference_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p], _i32),
@@ -225,14 +227,34 @@ def dequant_operand(w: torch.Tensor, s: torch.Tensor | None, inv_s: torch.Tensor
     return b
 
 
-def candidate_sse(x: torch.Tensor, b: torch.Tensor, y_ref: torch.Tensor,
+def diff_operand(w: torch.Tensor, s: torch.Tensor | None, inv_s: torch.Tensor | None,
+                 bits: int = 4, group: int = 128) -> torch.Tensor:
+    """One candidate's bf16 difference operand bf16(B - W) (B as dequant_operand writes it)."""
+    w = _bf16(w, "w")
+    N, K = w.shape
+    if s is not None:
+        s = _f32(s, "s")
+    if inv_s is not None:
+        inv_s = _f32(inv_s, "inv_s")
+    d = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+    _check(lib().awq_diff_operand(_ptr(w), N, K, _ptr(s), _ptr(inv_s), bits, group, _ptr(d),
+                                  _stream(w.device)), "awq_diff_operand")
+    return d
+
+
+def candidate_sse(x: torch.Tensor, b: torch.Tensor, y_ref: torch.Tensor | None,
                   workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """sum (X . B^T - y_ref)^2 as a float64 [1] device tensor (product never stored)."""
-    x, b, y_ref = _bf16(x, "x"), _bf16(b, "b"), _f32(y_ref, "y_ref")
+    """sum (X . B^T - y_ref)^2 (y_ref None: sum (X . B^T)^2) as a float64 [1]
+    device tensor; the product is never stored."""
+    x, b = _bf16(x, "x"), _bf16(b, "b")
     M, K = x.shape
     N = b.shape[0]
     if b.shape[1] != K:
         raise ValueError("x and b disagree on K")
+    if y_ref is not None:
+        y_ref = _f32(y_ref, "y_ref")
+        if tuple(y_ref.shape) != (M, N):
+            raise ValueError("y_ref must be [M][N]")
     sse = torch.empty(1, dtype=torch.float64, device=x.device)
     ws = _workspace(workspace_size(OP_CANDIDATE_SSE, M, N, K), x.device, workspace)
     _check(lib().awq_candidate_sse(_ptr(x), M, N, K, _ptr(b), _ptr(y_ref), _ptr(sse), _ptr(ws),

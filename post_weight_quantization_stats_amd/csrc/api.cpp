@@ -60,7 +60,7 @@ constexpr int64_t kMaxGemmN = int64_t(1) << 22;
 
 // ---- workspace layouts ----
 struct SearchLayout {
-  size_t yref, s, inv, scales_ws, stats_ws, btmp, partials, total;
+  size_t s, inv, scales_ws, stats_ws, dtmp, partials, total;
 };
 
 SearchLayout search_layout(int64_t M, int64_t N, int64_t K, int n_grid) {
@@ -72,12 +72,11 @@ SearchLayout search_layout(int64_t M, int64_t N, int64_t K, int n_grid) {
     off += align_up(bytes);
     return o;
   };
-  L.yref = take((size_t)M * N * sizeof(float));
   L.s = take((size_t)n_grid * K * sizeof(float));
   L.inv = take((size_t)n_grid * K * sizeof(float));
   L.scales_ws = take(awq::scales_ws_bytes(K, n_grid));
   L.stats_ws = take(awq::stats_ws_bytes(M, K));
-  L.btmp = take((size_t)N * K * sizeof(uint16_t));   // one candidate's bf16 weight operand
+  L.dtmp = take((size_t)N * K * sizeof(uint16_t));   // one candidate's bf16 difference operand
   L.partials = take((size_t)n_grid * awq::gemm_tiles(M, N) * sizeof(double));
   L.total = off;
   return L;
@@ -273,6 +272,25 @@ awq_status awq_dequant_operand(const uint16_t* w, int64_t N, int64_t K, const fl
   }
 }
 
+awq_status awq_diff_operand(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                            const float* inv_s, int32_t bits, int32_t group, uint16_t* d,
+                            void* stream) {
+  try {
+    awq_status st = check_quant_params(bits, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (N < 0 || N >= kMaxDim) return fail(AWQ_ERR_SHAPE, "N out of range");
+    if (N == 0) return ok();
+    if (w == nullptr || d == nullptr) return fail(AWQ_ERR_NULL, "w and d are required");
+    if (misaligned(w) || misaligned(d) || misaligned(s) || misaligned(inv_s))
+      return fail(AWQ_ERR_ALIGN, "w, d, s and inv_s must be 16-byte aligned");
+    AWQ_TRY_LAUNCH(awq::launch_quantize_diff_operand(w, N, K, s, inv_s, bits, d, (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
 awq_status awq_reference_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                               const uint16_t* w, float* y, void* stream) {
   try {
@@ -387,8 +405,7 @@ awq_status awq_candidate_sse(const uint16_t* x, int64_t M, int64_t N, int64_t K,
       AWQ_TRY_LAUNCH(awq::launch_fill_f64(sse, 1, 0.0, s));
       return ok();
     }
-    if (x == nullptr || b == nullptr || y_ref == nullptr)
-      return fail(AWQ_ERR_NULL, "x, b and y_ref are required");
+    if (x == nullptr || b == nullptr) return fail(AWQ_ERR_NULL, "x and b are required");
     if (misaligned(x) || misaligned(b) || misaligned(y_ref) || misaligned(ws))
       return fail(AWQ_ERR_ALIGN, "x, b, y_ref and ws must be 16-byte aligned");
     const size_t need = awq::align_up((size_t)awq::gemm_tiles(M, N) * sizeof(double));
@@ -401,6 +418,7 @@ awq_status awq_candidate_sse(const uint16_t* x, int64_t M, int64_t N, int64_t K,
     op.K = K;
     op.w = b;
     op.y_ref = y_ref;
+    op.sq = y_ref == nullptr;
     op.partials = (double*)ws;
     AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
     AWQ_TRY_LAUNCH(awq::launch_loss_reduce((const double*)ws, awq::gemm_tiles(M, N), 1, 1.0, sse, s));
@@ -515,40 +533,31 @@ awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint1
 
     hipStream_t s = (hipStream_t)stream;
     char* base = (char*)ws;
-    float* yref = (float*)(base + L.yref);
     float* sc = (float*)(base + L.s);
     float* inv = (float*)(base + L.inv);
-    uint16_t* btmp = (uint16_t*)(base + L.btmp);
+    uint16_t* dtmp = (uint16_t*)(base + L.dtmp);
     double* partials = (double*)(base + L.partials);
     const int64_t T = awq::gemm_tiles(M, N);
 
     AWQ_TRY_LAUNCH(awq::launch_act_stats(x, M, K, mean_abs, (double*)(base + L.stats_ws), s));
     AWQ_TRY_LAUNCH(awq::launch_candidate_scales(mean_abs, K, n_grid, sc, inv, base + L.scales_ws, s));
-    {
-      awq::GemmOperands op{};
-      op.x = x;
-      op.M = M;
-      op.N = N;
-      op.K = K;
-      op.w = w;
-      op.y = yref;
-      AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
-    }
-    // Per candidate: quantize W*s_i and write its dequantized operand
-    // B_i = bf16(f32(f32((q - z) * step) * inv_s_i[k])) once, then contract
-    // X . B_i^T with the squared error against Y_ref in the epilogue.  (The
-    // packed W4A16 contraction would dequantize B_i again for every 256-row
-    // tile of X; with many calibration tokens writing it once is cheaper.)
+    // Per candidate: quantize W*s_i, form its dequantized operand
+    // B_i = bf16(f32(f32((q - z) * step) * inv_s_i[k])) and write the
+    // difference D_i = B_i - W once (exact in bf16), then contract X . D_i^T,
+    // which is the output error X B_i^T - X W^T itself, and sum its squares
+    // in the epilogue.  No reference output is formed or read.  (The packed
+    // W4A16 contraction would dequantize B_i again for every 256-row tile of
+    // X; with many calibration tokens writing the operand once is cheaper.)
     for (int i = 0; i < n_grid; ++i) {
-      AWQ_TRY_LAUNCH(awq::launch_quantize_dequant(w, N, K, sc + (int64_t)i * K,
-                                                  inv + (int64_t)i * K, bits, btmp, s));
+      AWQ_TRY_LAUNCH(awq::launch_quantize_diff_operand(w, N, K, sc + (int64_t)i * K,
+                                                       inv + (int64_t)i * K, bits, dtmp, s));
       awq::GemmOperands op{};
       op.x = x;
       op.M = M;
       op.N = N;
       op.K = K;
-      op.w = btmp;
-      op.y_ref = yref;
+      op.w = dtmp;
+      op.sq = true;
       op.partials = partials + (int64_t)i * T;
       AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
     }

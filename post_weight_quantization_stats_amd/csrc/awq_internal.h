@@ -60,6 +60,10 @@ hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, cons
 
 // Candidate difference for the Gram-form loss: d32[n][k] = B - W (fp32) and
 // a_split[n] = [hi(D) | hi(D) | lo(D)] (bf16 [N][3K]).
+// bf16(B - W) as bf16 [N][K] (exact: see quantize_pack.hip).
+hipError_t launch_quantize_diff_operand(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                                        const float* inv_s, int bits, uint16_t* d_out,
+                                        hipStream_t stream);
 hipError_t launch_quantize_diff(const uint16_t* w, int64_t N, int64_t K, const float* s,
                                 const float* inv_s, int bits, uint16_t* a_split, float* d32,
                                 hipStream_t stream);
@@ -83,6 +87,7 @@ struct GemmOperands {
   float* y;                 // [M][N] or NULL
   double* partials;         // [tiles] fp64 SSE per tile, or NULL
   bool dot;                 // bf16 operand: partials hold sum(Y * y_ref) instead
+  bool sq;                  // bf16 operand: partials hold sum(Y^2); y_ref unused
 };
 hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream);
 

@@ -113,8 +113,12 @@ __device__ __forceinline__ uint32_t pack8(const float* q) {
 // of calibration tokens.  kDiff: D = B - W (exact in fp32: two bf16 values of
 // similar size) as fp32 [N][K], and the split operand [hi(D) | hi(D) | lo(D)]
 // as bf16 [N][3K] (hi = RNE to bf16, lo = RNE of the exact remainder) for the
-// Gram-form loss D G D^T.
-enum QuantMode { kPack = 0, kOperand = 1, kDiff = 2 };
+// Gram-form loss D G D^T.  kDiffOp: D as bf16 [N][K], the operand whose
+// product with X is the output error X B^T - X W^T itself.  That rounding is
+// exact: B is nonzero only where |W s| >= step / 2, so B and W share a sign
+// and B / W lies in [1/2, 2] (up to the roundings of s and 1/s), and by
+// Sterbenz's lemma the difference of two such bf16 values is a bf16 value.
+enum QuantMode { kPack = 0, kOperand = 1, kDiff = 2, kDiffOp = 3 };
 
 template <int BITS, int kMode>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
@@ -188,6 +192,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         uint4* dst = (uint4*)(bout + n * K + k0);
         dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
         dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
+      } else if constexpr (kMode == kDiffOp) {
+        uint32_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          e[j] = pack_bf16x2(bf16_lo(d[j]) - wv[2 * j], bf16_hi(d[j]) - wv[2 * j + 1]);
+        uint4* dst = (uint4*)(bout + n * K + k0);
+        dst[0] = make_uint4(e[0], e[1], e[2], e[3]);
+        dst[1] = make_uint4(e[4], e[5], e[6], e[7]);
       } else {
         float dd[16];
 #pragma unroll
@@ -252,6 +264,20 @@ hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, cons
   else
     quantize_kernel<3, kOperand><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
                                                                 nullptr, nullptr, b_out, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_diff_operand(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                                        const float* inv_s, int bits, uint16_t* d_out,
+                                        hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
+  if (bits == 4)
+    quantize_kernel<4, kDiffOp><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
+                                                               nullptr, nullptr, d_out, nullptr);
+  else
+    quantize_kernel<3, kDiffOp><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
+                                                               nullptr, nullptr, d_out, nullptr);
   return hipGetLastError();
 }
 

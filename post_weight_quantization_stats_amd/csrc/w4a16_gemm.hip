@@ -197,7 +197,8 @@ struct CodeRegs {
 
 // kStoreY: write the fp32 product; kSse: fp64 sum of (Y - Y_ref)^2 per tile,
 // or with kDot the fp64 sum of Y * Y_ref (a quadratic form's last factor).
-template <bool kInt4, bool kInvS, int WN, bool kStoreY, bool kSse, bool kDot = false>
+template <bool kInt4, bool kInvS, int WN, bool kStoreY, bool kSse, bool kDot = false,
+          bool kSq = false>
 __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
                                                                     const float* __restrict__ inv_s) {
   // The body exists only in the device pass; the host pass needs just the
@@ -462,7 +463,36 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
       }
     }
   }
-  if constexpr (kSse) {
+  if constexpr (kSse && kSq) {
+    // Sum of acc^2 (the operand is a difference, so acc is the output error
+    // itself).  Squares and sums in fp64; rows past M are 0, columns past N
+    // are masked.
+    double sse = 0.0;
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) {
+      const bool ok = n0 + wn * TN + j * 32 + lr < N;
+      double dpart = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const double a = (double)acc[i][j][r];
+          dpart = fma(a, a, dpart);
+        }
+      }
+      sse += ok ? dpart : 0.0;
+    }
+    sse = wave_sum_f64(sse);
+    __shared__ double wsq[NW];
+    if (lane == 0) wsq[wave] = sse;
+    __syncthreads();
+    if (t == 0) {
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += wsq[w];
+      p.partials[tm * p.tiles_n + tn] = tot;
+    }
+  } else if constexpr (kSse) {
     // Sum of (acc - y_ref)^2.  The wave's 128 x TN block of y_ref is staged
     // through LDS (the k-loop's stage buffers are free now) by the buffer
     // unit, 64 rows at a time, so a whole half-block is in flight at once;
@@ -571,7 +601,9 @@ hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream) {
   // bf16 operand: 8 waves (two per SIMD) measured faster; INT4: the dequant
   // VALU work favours 4 waves with 128x128 tiles each.
   const bool y = op.y != nullptr, sse = op.partials != nullptr;
-  if (op.qweight == nullptr && op.dot) {
+  if (op.qweight == nullptr && op.sq) {
+    gemm_kernel<false, false, 4, false, true, false, true><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
+  } else if (op.qweight == nullptr && op.dot) {
     gemm_kernel<false, false, 4, false, true, true><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
   } else if (op.qweight == nullptr) {
     if (sse)

@@ -57,8 +57,8 @@ def ws_size(op, M, N, K, bits=4, group=128, n_grid=20):
 def test_workspace_sizes():
     st, b = ws_size(awq.OP_SEARCH_SCALE, 65536, 12288, 4096)
     assert st == OK
-    assert b >= 65536 * 12288 * 4          # holds the fp32 reference output
-    assert b < 65536 * 12288 * 4 + 200 * 2 ** 20
+    assert b >= 12288 * 4096 * 2           # one candidate's bf16 difference operand
+    assert b < 12288 * 4096 * 2 + 64 * 2 ** 20   # and no fp32 reference output
     assert ws_size(awq.OP_ACT_STATS, 256, 0, 512)[0] == OK
     assert ws_size(awq.OP_W4A16_GEMM, 0, 0, 128) == (OK, 0)
     assert ws_size(awq.OP_SEARCH_SCALE, 256, 512, 500)[0] == SHAPE
@@ -195,6 +195,18 @@ def test_decode_gemm_errors_and_plan():
 
 def test_dequant_operand_errors():
     f = awq.lib().awq_dequant_operand
+    assert f(None, 4, 128, None, None, 4, 128, FAKE, None) == NULL
+    assert f(FAKE, 4, 128, None, None, 4, 128, None, None) == NULL
+    assert f(FAKE, 4, 128, None, None, 5, 128, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 4, 100, None, None, 4, 128, FAKE, None) == SHAPE
+    assert f(FAKE, -1, 128, None, None, 4, 128, FAKE, None) == SHAPE
+    assert f(FAKE, 4, 128, FAKE_MIS, None, 4, 128, FAKE, None) == ALIGN
+    assert f(FAKE, 4, 128, None, None, 4, 128, FAKE_MIS, None) == ALIGN
+    assert f(None, 0, 128, None, None, 4, 128, None, None) == OK
+
+
+def test_diff_operand_errors():
+    f = awq.lib().awq_diff_operand
     assert f(None, 4, 128, None, None, 4, 128, FAKE, None) == NULL
     assert f(FAKE, 4, 128, None, None, 4, 128, None, None) == NULL
     assert f(FAKE, 4, 128, None, None, 5, 128, FAKE, None) == UNSUPPORTED

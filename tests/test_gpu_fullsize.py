@@ -7,8 +7,10 @@ At full size the oracle checks what it can compute: the statistics in full,
 the candidate operands and the written weights on sampled rows (bit-exact),
 the product on a sampled block; for the reductions, properties that hold at
 any size (a candidate's squared error against its own product is exactly
-zero; the search's losses are exactly the standalone per-candidate squared
-errors; the chosen index is the first minimum).
+zero; the difference operand is B - W exactly and its squared product equals
+the error against the reference output; the search's losses are exactly the
+standalone per-candidate squared errors; the chosen index is the first
+minimum).
 """
 
 import numpy as np
@@ -101,6 +103,11 @@ def test_fullsize_candidate_sse_properties(dev, qkv):
     sse = float(awq.candidate_sse(xd, b, y_ref).item())
     direct = float(((y_b.double() - y_ref.double()) ** 2).sum().item())
     assert abs(sse - direct) <= 1e-9 * direct
+    # the difference form measures the same error without y_ref
+    d = awq.diff_operand(wd, s[6], inv[6], 4)
+    assert torch.equal(d.float(), b.float() - wd.float())        # exact in bf16
+    sq = float(awq.candidate_sse(xd, d, None).item())
+    assert abs(sq - sse) <= 1e-5 * sse
 
 
 def test_fullsize_search(dev, qkv, qkv_stats):
@@ -115,11 +122,10 @@ def test_fullsize_search(dev, qkv, qkv_stats):
     _, a_ref = qkv_stats
     assert (np.abs(a_gpu.cpu().numpy() - a_ref) / a_ref).max() <= 1e-6
     s, inv = awq.candidate_scales(a_gpu, spec.n_grid)
-    y_ref = awq.reference_gemm(xd, wd)
     MN = float(spec.M) * spec.N
     for i in range(spec.n_grid):
-        b = awq.dequant_operand(wd, s[i], inv[i], 4)
-        assert float(awq.candidate_sse(xd, b, y_ref).item()) / MN == losses[i], i
+        d = awq.diff_operand(wd, s[i], inv[i], 4)
+        assert float(awq.candidate_sse(xd, d, None).item()) / MN == losses[i], i
     s_ref, _ = O.candidate_scales(a_ref, spec.n_grid)
     best_s = out["best_s"].cpu().numpy()
     assert ulp_distance_f32(best_s, s_ref[best]).max() <= 1

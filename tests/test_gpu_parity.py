@@ -179,6 +179,43 @@ def test_dequant_operand_bit_exact(dev, shape, bits):
                           O.dequant_operand(q, z, st, 128, None))
 
 
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_diff_operand_bit_exact(dev, shape, bits):
+    """The search's per-candidate difference operand bf16(B - W), bit for bit."""
+    announce("diff_operand", ids(shape), bits)
+    x, w = layer(shape)
+    _, a = O.act_stats(x)
+    s_all, inv_all = O.candidate_scales(a, 20)
+    wd = to_dev_bf16(w, dev)
+    for i in (0, 7, 19):
+        d = awq.diff_operand(wd, to_dev_f32(s_all[i], dev), to_dev_f32(inv_all[i], dev), bits)
+        q, z, st = O.quantize(w, s_all[i], bits, 128)
+        ref = O.diff_operand(w, O.dequant_operand(q, z, st, 128, inv_all[i]))
+        assert np.array_equal(d.float().cpu().numpy().astype(np.float64), ref)
+    d = awq.diff_operand(wd, None, None, bits)
+    q, z, st = O.quantize(w, None, bits, 128)
+    assert np.array_equal(d.float().cpu().numpy().astype(np.float64),
+                          O.diff_operand(w, O.dequant_operand(q, z, st, 128, None)))
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_candidate_sse_difference_form(dev, shape):
+    """sum (X . D^T)^2 with the difference operand: the search's loss numerator."""
+    announce("candidate_sse difference form", ids(shape))
+    x, w = layer(shape)
+    M, N = x.shape[0], w.shape[0]
+    _, a = O.act_stats(x)
+    s_all, inv_all = O.candidate_scales(a, 20)
+    xd, wd = to_dev_bf16(x, dev), to_dev_bf16(w, dev)
+    for i in (0, 11, 19):
+        d = awq.diff_operand(wd, to_dev_f32(s_all[i], dev), to_dev_f32(inv_all[i], dev), 4)
+        got = float(awq.candidate_sse(xd, d, None).item()) / (M * N)
+        q, z, st = O.quantize(w, s_all[i], 4, 128)
+        ref = O.output_mse(x, w, O.dequant_operand(q, z, st, 128, inv_all[i]))
+        assert abs(got - ref) <= 1e-5 * ref
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=ids)
 def test_candidate_sse(dev, shape):
     """The search's per-candidate loss numerator from the bf16 operand."""

@@ -88,10 +88,22 @@ def _mut_decode_rounds_weight_to_bf16(mp):
     mp.setattr(oracle, "decode_gemm", lambda a, qw, sc, ze, g: OA.deploy_gemm(a, qw, sc, ze, g))
 
 
+def _mut_diff_sign(mp):
+    orig = OA.diff_operand
+    mp.setattr(oracle, "diff_operand", lambda w, b: -orig(w, b))
+
+
+def _mut_diff_off_by_half_ulp(mp):
+    # The difference left slightly off its bf16 value (a stray factor).
+    mp.setattr(oracle, "diff_operand",
+               lambda w, b: OA.f32(np.asarray(b, np.float64) - OA.bf16_bits_to_f64(w)) * (1 + 2.0 ** -9))
+
+
 MUTATIONS = [_mut_floor_instead_of_rint, _mut_drop_inv_s, _mut_alpha_grid_closed,
              _mut_scale_index_reversed, _mut_zero_added_before_rounding, _mut_loss_sign,
              _mut_no_range_extension, _mut_stats_mean_without_abs, _mut_normaliser_max_only,
-             _mut_decode_zero_of_first_group, _mut_decode_rounds_weight_to_bf16]
+             _mut_decode_zero_of_first_group, _mut_decode_rounds_weight_to_bf16, _mut_diff_sign,
+             _mut_diff_off_by_half_ulp]
 
 PINS = [
     P.test_quantizer_worked_group,
@@ -105,6 +117,7 @@ PINS = [
     lambda: P.test_whole_search_brute_force_tiny(16, 6, 256, 3, 21),
     P.test_decode_gemm_brute_force_from_words,
     P.test_decode_gemm_unit_codes_closed_form,
+    lambda: P.test_difference_operand_is_exact(4),
 ]
 
 

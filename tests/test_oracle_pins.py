@@ -338,6 +338,38 @@ def test_loss_two_forms_and_literal_difference():
         assert literal == pytest.approx(direct, rel=1e-9)
 
 
+@pytest.mark.parametrize("bits", [3, 4])
+def test_difference_operand_is_exact(bits):
+    """B - W needs no rounding in bf16: every nonzero B lies within a factor
+    of two of W with the same sign (Sterbenz's lemma then makes the
+    difference of the two bf16 values a bf16 value), and X . D^T is the
+    output error against the literal products X . B^T - X . W^T."""
+    x, w = synth.random_layer(96, 512, 64, seed=21, n_outlier=5, outlier_factor=30.0)
+    X, W = O.bf16_bits_to_f64(x), O.bf16_bits_to_f64(w)
+    s, inv = O.candidate_scales(O.act_stats(x)[1], 20)
+    for i in range(20):
+        q, z, st = O.quantize(w, s[i], bits, 128)
+        B = O.dequant_operand(q, z, st, 128, inv[i])
+        nz = B != 0
+        ratio = B[nz] / W[nz]
+        assert ratio.min() >= 0.5 and ratio.max() <= 2.0
+        D = O.diff_operand(w, B)
+        assert np.array_equal(D, B - W)
+        err = X @ B.T - X @ W.T
+        assert np.abs(X @ D.T - err).max() <= 1e-12 * np.abs(X @ B.T).max()
+
+
+def test_difference_operand_rounds_where_inexact():
+    """Away from the quantizer's grid the contract still rounds: a difference
+    that needs more than 8 significant bits goes to the nearest bf16."""
+    b = np.array([[1.0, 0.0, 2.0 ** -10]])
+    w = synth.to_bf16_bits(np.array([[2.0 ** -9, 0.5, 1.0]], np.float32))
+    D = O.diff_operand(w, b)
+    assert D[0, 1] == -0.5
+    assert D[0, 2] == -1.0                    # 2^-10 - 1 rounds back to -1
+    assert D[0, 0] == 1.0                     # 1 - 2^-9: a tie, to the even neighbour
+
+
 def rtn_mse(x_bits, w_bits, bits, group):
     """Plain round-to-nearest, written separately: no scale, per-group asymmetric
     min/max quantization in fp32 (numpy float32 arithmetic)."""
