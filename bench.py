@@ -136,6 +136,44 @@ def _bench_line(log_path):
     return None
 
 
+N_XCD, N_CU, SIMD_PER_CU = 8, 256, 4
+
+
+def summarize_mfma(pmc_dir: str, command: str) -> str:
+    """Clock and matrix-core occupancy per kernel from one counter pass
+    (GRBM_GUI_ACTIVE summed over the XCDs, SQ_BUSY_CU_CYCLES over the CUs,
+    SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs, SQ_INSTS_VALU_MFMA_MOPS_BF16 in
+    units of 512 flops)."""
+    rows = _read_csv(_find(pmc_dir, "counter_collection.csv"))
+    per = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "awq::" not in name:
+            continue
+        key = (r["Dispatch_Id"], name)
+        d = per.setdefault(key, {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    by = {}
+    for (_, name), d in per.items():
+        by.setdefault(_label(name), []).append(d)
+    out = ["# rocprofv3 counters: clock and matrix-core occupancy per kernel (medians over dispatches)",
+           f"# command: {command}",
+           "# clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES /",
+           "# (4 SIMDs x SQ_BUSY_CU_CYCLES); tflops = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 / duration",
+           "# (the clock is meaningful only for kernels much longer than the counter window)", ""]
+    out.append(f"{'kernel':<62} {'n':>3} {'dur_ms':>8} {'clock_GHz':>9} {'mfma_busy':>9} {'tflops':>8}")
+    for label, ds in sorted(by.items()):
+        if not all("GRBM_GUI_ACTIVE" in d and "SQ_VALU_MFMA_BUSY_CYCLES" in d for d in ds):
+            continue
+        med = lambda f: float(np.median([f(d) for d in ds]))
+        dur = med(lambda d: d["dur"])
+        clock = med(lambda d: d["GRBM_GUI_ACTIVE"] / N_XCD / d["dur"] / 1e9)
+        busy = med(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMD_PER_CU * max(d["SQ_BUSY_CU_CYCLES"], 1)))
+        tfl = med(lambda d: 512.0 * d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) / d["dur"] / 1e12)
+        out.append(f"{label:<62} {len(ds):>3} {dur * 1e3:>8.3f} {clock:>9.2f} {busy:>9.1%} {tfl:>8.0f}")
+    return "\n".join(out) + "\n"
+
+
 def summarize_trace(trace_dir: str, command: str, log_path: str | None) -> str:
     rows = _read_csv(_find(trace_dir, "kernel_stats.csv"))
     out = ["# rocprofv3 kernel-trace statistics", f"# command: {command}", ""]
@@ -155,7 +193,8 @@ def summarize_trace(trace_dir: str, command: str, log_path: str | None) -> str:
                 f"dominant kernel ms_per_launch (events): {rf['ms_per_launch']:.3f}",
                 f"kernel_source_hash: {rf['kernel_source_hash']}"]
         for k, v in line["kernels"].items():
-            out.append(f"{k}: " + ", ".join(f"{a}={b:.4g}" for a, b in v.items()))
+            if isinstance(v, dict) and all(isinstance(b, (int, float)) for b in v.values()):
+                out.append(f"{k}: " + ", ".join(f"{a}={b:.4g}" for a, b in v.items()))
     return "\n".join(out) + "\n"
 
 
@@ -283,8 +322,8 @@ def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
 
 def bench_gram(awq, xd, wd, spec, bits: int, direct: dict, steps: int, direct_ms: float) -> dict:
     """The same search with Gram-form losses (G = X^T X once, then per
-    candidate D G D^T on a bf16 x 3 split): a second workload with the same
-    result, reported beside the headline, never in its place."""
+    candidate D G D^T against a two-term bf16 split of G): a second workload
+    with the same result, reported beside the headline, never in its place."""
     import torch
 
     M, K, N, G = spec.M, spec.K, spec.N, spec.n_grid
@@ -300,7 +339,7 @@ def bench_gram(awq, xd, wd, spec, bits: int, direct: dict, steps: int, direct_ms
     la, lg = direct["losses"].double(), g["losses"].double()
     rel = float(((lg - la).abs() / la.abs()).max().item())
     same = int(direct["best_idx"].item()) == int(g["best_idx"].item())
-    flops = 2.0 * M * K * K + G * 6.0 * N * K * K
+    flops = 2.0 * M * K * K + G * 4.0 * N * K * K
     log(f"gram-form search: {ms:.2f} ms/layer ({direct_ms / ms:.2f}x the direct form); "
         f"max relative loss difference {rel:.2e}; same choice {same}")
     del ws
@@ -345,6 +384,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped GEMM figures")
     ap.add_argument("--no-gram", action="store_true", help="skip the Gram-form search figure")
+    ap.add_argument("--no-power-probe", action="store_true",
+                    help="skip the constant-operand launch (keeps profiles to the synthetic data)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode-shaped GEMM figures (prints them as JSON)")
     ap.add_argument("--cpu-m", type=int, default=4096)
@@ -353,15 +394,19 @@ def main() -> int:
                     help="write a summary of a rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="write HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE runs and exit")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR", default=None,
+                    help="write clock / matrix-core occupancy from a counter pass and exit")
     ap.add_argument("--bench-log", default=None, help="log of the profiled bench run")
     ap.add_argument("--profile-command", default="", help="command text recorded in a summary")
     ap.add_argument("--summary-out", default=None)
     args = ap.parse_args()
 
-    if args.summarize_trace or args.summarize_pmc:
+    if args.summarize_trace or args.summarize_pmc or args.summarize_mfma:
         import synth
         spec = synth.layer_spec(args.workload, args.layer)
-        if args.summarize_trace:
+        if args.summarize_mfma:
+            text = summarize_mfma(args.summarize_mfma, args.profile_command)
+        elif args.summarize_trace:
             text = summarize_trace(args.summarize_trace, args.profile_command, args.bench_log)
         else:
             text = summarize_pmc(*args.summarize_pmc, args.profile_command, spec.M, spec.K)
@@ -436,6 +481,15 @@ def main() -> int:
                           stream)
     t_sse_y = event_time_ms(lambda: awq.candidate_sse(xd, b_mid, yref, workspace=gemm_ws),
                             max(2, reps // 2), stream)
+    # The same launch on constant operands: identical instructions and memory
+    # traffic, almost no bit toggling in the matrix cores.  The gap to the
+    # synthetic data is the chip's power limit, not the kernel's schedule.
+    t_sse_c = None
+    if not args.no_power_probe:
+        x_one, d_one = torch.ones_like(xd), torch.ones_like(d_mid)
+        t_sse_c = event_time_ms(lambda: awq.candidate_sse(x_one, d_one, None, workspace=gemm_ws),
+                                max(2, reps // 2), stream)
+        del x_one, d_one
     t_w4 = event_time_ms(lambda: awq.w4a16_gemm(xd, qw, sc, ze, bits, spec.group,
                                                 inv_s=inv_all[i_mid], y_ref=yref,
                                                 return_y=False, workspace=gemm_ws),
@@ -455,7 +509,8 @@ def main() -> int:
     deq_bytes = 2.0 * N * K + 8.0 * K + 2.0 * N * K
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
     log(f"search contraction {t_sse:.3f} ms = {tf(t_sse):.1f} TFLOP/s; against y_ref "
-        f"{t_sse_y:.3f} ms = {tf(t_sse_y):.1f} TFLOP/s; packed w4a16+sse {t_w4:.3f} ms "
+        f"{t_sse_y:.3f} ms = {tf(t_sse_y):.1f} TFLOP/s; on constant operands "
+        f"{(t_sse_c or float('nan')):.3f} ms; packed w4a16+sse {t_w4:.3f} ms "
         f"= {tf(t_w4):.1f} TFLOP/s; reference {t_ref:.3f} ms = {tf(t_ref):.1f} TFLOP/s")
     log(f"stats {t_stats * 1e3:.1f} us = {gbs(stats_bytes, t_stats):.0f} GB/s; quantize+pack "
         f"{t_quant * 1e3:.1f} us = {gbs(quant_bytes, t_quant):.0f} GB/s; dequant operand "
@@ -494,6 +549,7 @@ def main() -> int:
         "kernels": {
             "search_contraction": mfma_entry(t_sse),
             "candidate_sse_vs_yref": mfma_entry(t_sse_y),
+            "search_contraction_constant_operands": mfma_entry(t_sse_c) if t_sse_c else None,
             "w4a16_gemm_sse": mfma_entry(t_w4),
             "reference_gemm": mfma_entry(t_ref),
             "act_stats": hbm_entry(stats_bytes, t_stats),

@@ -278,13 +278,13 @@ awq_status awq_search_scale(const uint16_t* x, int64_t M, int64_t K, const uint1
  * fold of 1/s into the weight operand):
  *   loss_i = sum_n D_n G D_n^T / (M N),  D = B_i - W,  G = X^T X,
  * with G formed once per layer (fp32 sums of exact bf16 products) and D G
- * evaluated on the matrix cores as a bf16 x 3 split ([hi D | hi D | lo D] .
- * [hi G | lo G | hi G]^T, about 2^-16 relative).  Per candidate it costs
- * 6 N K^2 flops instead of 2 M N K, so it pays when 3 K < M (many
- * calibration tokens); G costs 2 M K^2 once.  Arguments and outputs as in
+ * evaluated on the matrix cores against a two-term split of G ([D | D] .
+ * [hi G | lo G]^T; D is exact in bf16 as in awq_diff_operand; about 2^-16
+ * relative).  Per candidate it costs 4 N K^2 flops instead of 2 M N K, so it
+ * pays when 2 K < M (many calibration tokens); G costs 2 M K^2 once.  Arguments and outputs as in
  * awq_search_scale (losses agree with it to about 1e-5 relative; the chosen
  * index can differ only between candidates whose losses tie to that
- * precision).  Limits: M rounded up to 128 and 3 K at most 2^22.
+ * precision).  Limits: M rounded up to 128 and 2 K at most 2^22.
  *   ws: awq_workspace_size(AWQ_OP_SEARCH_SCALE_GRAM) bytes (X^T, G and its
  *       split, one candidate's split difference and D in fp32).
  */

@@ -102,8 +102,8 @@ GramLayout gram_layout(int64_t M, int64_t N, int64_t K, int n_grid) {
   L.stats_ws = take(awq::stats_ws_bytes(M, K));
   L.xt = take((size_t)K * Mp * sizeof(uint16_t));              // X^T, zero-padded
   L.g32 = take((size_t)K * K * sizeof(float));                 // G = X^T X
-  L.gsplit = take((size_t)K * 3 * K * sizeof(uint16_t));       // [hi G | lo G | hi G]
-  L.asplit = take((size_t)N * 3 * K * sizeof(uint16_t));       // [hi D | hi D | lo D]
+  L.gsplit = take((size_t)K * 2 * K * sizeof(uint16_t));       // [hi G | lo G]
+  L.asplit = take((size_t)N * 2 * K * sizeof(uint16_t));       // [D | D]
   L.d32 = take((size_t)N * K * sizeof(float));                 // D = B - W
   L.partials = take((size_t)n_grid * awq::gemm_tiles(N, K) * sizeof(double));
   L.total = off;
@@ -176,8 +176,8 @@ awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32
         if (st != AWQ_OK) return st;
         if ((st = check_k(K, group)) != AWQ_OK) return st;
         if (M <= 0 || N <= 0 || awq::gram_padded_m(M) > (int64_t(1) << 22) || N > kMaxGemmN ||
-            3 * K > (int64_t(1) << 22))
-          return fail(AWQ_ERR_SHAPE, "Gram search needs 1 <= M <= 2^22, 1 <= N <= 2^22, 3K <= 2^22");
+            2 * K > (int64_t(1) << 22))
+          return fail(AWQ_ERR_SHAPE, "Gram search needs 1 <= M <= 2^22, 1 <= N <= 2^22, 2K <= 2^22");
         if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_UNSUPPORTED, "n_grid must be in [1, 64]");
         *bytes = gram_layout(M, N, K, n_grid).total;
         return ok();
@@ -442,8 +442,8 @@ awq_status awq_search_scale_gram(const uint16_t* x, int64_t M, int64_t K, const 
     if (st != AWQ_OK) return st;
     if ((st = check_k(K, group)) != AWQ_OK) return st;
     if (M <= 0 || N <= 0 || awq::gram_padded_m(M) > (int64_t(1) << 22) || N > kMaxGemmN ||
-        3 * K > (int64_t(1) << 22))
-      return fail(AWQ_ERR_SHAPE, "Gram search needs 1 <= M <= 2^22, 1 <= N <= 2^22, 3K <= 2^22");
+        2 * K > (int64_t(1) << 22))
+      return fail(AWQ_ERR_SHAPE, "Gram search needs 1 <= M <= 2^22, 1 <= N <= 2^22, 2K <= 2^22");
     if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_UNSUPPORTED, "n_grid must be in [1, 64]");
     if (misaligned(x) || misaligned(w) || misaligned(mean_abs) || misaligned(best_s) ||
         misaligned(qweight) || misaligned(ws) || ((uintptr_t)scales & 3u) ||
@@ -481,8 +481,8 @@ awq_status awq_search_scale_gram(const uint16_t* x, int64_t M, int64_t K, const 
       AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
     }
     AWQ_TRY_LAUNCH(awq::launch_gram_split(g32, K, gsplit, s));
-    // Per candidate: D = B_i - W, then sum_n D_n G D_n^T as the dot of
-    // [hi D | hi D | lo D] . [hi G | lo G | hi G]^T with D in the epilogue.
+    // Per candidate: D = B_i - W (exact in bf16), then sum_n D_n G D_n^T as
+    // the dot of [D | D] . [hi G | lo G]^T with D in the epilogue.
     for (int i = 0; i < n_grid; ++i) {
       AWQ_TRY_LAUNCH(awq::launch_quantize_diff(w, N, K, sc + (int64_t)i * K, inv + (int64_t)i * K,
                                                bits, asplit, d32, s));
@@ -490,7 +490,7 @@ awq_status awq_search_scale_gram(const uint16_t* x, int64_t M, int64_t K, const 
       op.x = asplit;
       op.M = N;
       op.N = K;
-      op.K = 3 * K;
+      op.K = 2 * K;
       op.w = gsplit;
       op.y_ref = d32;
       op.partials = partials + (int64_t)i * T;

@@ -58,12 +58,12 @@ hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, cons
                                    const float* inv_s, int bits, uint16_t* b_out,
                                    hipStream_t stream);
 
-// Candidate difference for the Gram-form loss: d32[n][k] = B - W (fp32) and
-// a_split[n] = [hi(D) | hi(D) | lo(D)] (bf16 [N][3K]).
 // bf16(B - W) as bf16 [N][K] (exact: see quantize_pack.hip).
 hipError_t launch_quantize_diff_operand(const uint16_t* w, int64_t N, int64_t K, const float* s,
                                         const float* inv_s, int bits, uint16_t* d_out,
                                         hipStream_t stream);
+// Candidate difference for the Gram-form loss: d32[n][k] = B - W (fp32) and
+// a_split[n] = [D | D] (bf16 [N][2K]).
 hipError_t launch_quantize_diff(const uint16_t* w, int64_t N, int64_t K, const float* s,
                                 const float* inv_s, int bits, uint16_t* a_split, float* d32,
                                 hipStream_t stream);

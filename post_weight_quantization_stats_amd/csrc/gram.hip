@@ -8,11 +8,12 @@
 //   * transpose_pad_kernel writes X^T (bf16 [K][Mp], Mp = M rounded up to the
 //     contraction's k-step granularity, zero columns past M) so that G is the
 //     same K-contiguous bf16 contraction as every other product here.
-//   * gram_split_kernel turns fp32 G into the operand [hi(G) | lo(G) | hi(G)]
-//     (bf16 [K][3K]; hi = RNE to bf16, lo = RNE of the exact remainder).  With
-//     the candidate's [hi(D) | hi(D) | lo(D)] one contraction of length 3K
-//     gives hi(D) hi(G) + hi(D) lo(G) + lo(D) hi(G), i.e. D G to about 2^-16
-//     relative, with bf16 matrix cores.
+//   * gram_split_kernel turns fp32 G into the operand [hi(G) | lo(G)] (bf16
+//     [K][2K]; hi = RNE to bf16, lo = RNE of the exact remainder).  D = B - W
+//     is a bf16 value (the quantizer's grid keeps B within a factor of two of
+//     W), so with the candidate's [D | D] one contraction of length 2K gives
+//     D hi(G) + D lo(G), i.e. D G to about 2^-16 relative, on bf16 matrix
+//     cores.
 #include "awq_internal.h"
 #include "device_common.h"
 
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
   }
 }
 
-// Eight fp32 values of G per thread -> three 16-byte pieces of the split operand.
+// Eight fp32 values of G per thread -> two 16-byte pieces of the split operand.
 __global__ __launch_bounds__(256) void gram_split_kernel(const float* __restrict__ g, int64_t K,
                                                          uint16_t* __restrict__ out) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;   // element index in G
@@ -74,11 +75,9 @@ __global__ __launch_bounds__(256) void gram_split_kernel(const float* __restrict
     hi[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
     lo[j] = pack_bf16x2(v[2 * j] - bf16_lo(hi[j]), v[2 * j + 1] - bf16_hi(hi[j]));
   }
-  uint16_t* r = out + row * 3 * K + col;
-  const uint4 h = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  *(uint4*)r = h;
+  uint16_t* r = out + row * 2 * K + col;
+  *(uint4*)r = make_uint4(hi[0], hi[1], hi[2], hi[3]);
   *(uint4*)(r + K) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-  *(uint4*)(r + 2 * K) = h;
 }
 
 }  // namespace

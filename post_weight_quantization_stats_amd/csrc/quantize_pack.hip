@@ -110,14 +110,13 @@ __device__ __forceinline__ uint32_t pack8(const float* q) {
 // search's weight operand B = bf16(f32(f32((q - z) * step) * inv_s[k])) as a
 // bf16 [N][K] matrix, written once per candidate so that the contraction
 // reads a plain bf16 operand instead of dequantizing it again for every tile
-// of calibration tokens.  kDiff: D = B - W (exact in fp32: two bf16 values of
-// similar size) as fp32 [N][K], and the split operand [hi(D) | hi(D) | lo(D)]
-// as bf16 [N][3K] (hi = RNE to bf16, lo = RNE of the exact remainder) for the
-// Gram-form loss D G D^T.  kDiffOp: D as bf16 [N][K], the operand whose
+// of calibration tokens.  kDiffOp: D = B - W as bf16 [N][K], the operand whose
 // product with X is the output error X B^T - X W^T itself.  That rounding is
 // exact: B is nonzero only where |W s| >= step / 2, so B and W share a sign
 // and B / W lies in [1/2, 2] (up to the roundings of s and 1/s), and by
 // Sterbenz's lemma the difference of two such bf16 values is a bf16 value.
+// kDiff: for the Gram-form loss D G D^T, D as fp32 [N][K] and the operand
+// [D | D] as bf16 [N][2K] (against [hi(G) | lo(G)]).
 enum QuantMode { kPack = 0, kOperand = 1, kDiff = 2, kDiffOp = 3 };
 
 template <int BITS, int kMode>
@@ -202,30 +201,24 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         dst[1] = make_uint4(e[4], e[5], e[6], e[7]);
       } else {
         float dd[16];
+        uint32_t e[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           dd[2 * j] = bf16_lo(d[j]) - wv[2 * j];
           dd[2 * j + 1] = bf16_hi(d[j]) - wv[2 * j + 1];
-        }
-        uint32_t hi[8], lo[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          hi[j] = pack_bf16x2(dd[2 * j], dd[2 * j + 1]);
-          lo[j] = pack_bf16x2(dd[2 * j] - bf16_lo(hi[j]), dd[2 * j + 1] - bf16_hi(hi[j]));
+          e[j] = pack_bf16x2(dd[2 * j], dd[2 * j + 1]);
         }
         float4* df = (float4*)(dout + n * K + k0);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           df[c] = make_float4(dd[4 * c], dd[4 * c + 1], dd[4 * c + 2], dd[4 * c + 3]);
-        uint16_t* arow = bout + n * 3 * K;
-        const uint4 h0 = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        const uint4 h1 = make_uint4(hi[4], hi[5], hi[6], hi[7]);
-        ((uint4*)(arow + k0))[0] = h0;
-        ((uint4*)(arow + k0))[1] = h1;
-        ((uint4*)(arow + K + k0))[0] = h0;
-        ((uint4*)(arow + K + k0))[1] = h1;
-        ((uint4*)(arow + 2 * K + k0))[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        ((uint4*)(arow + 2 * K + k0))[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+        uint16_t* arow = bout + n * 2 * K;
+        const uint4 e0 = make_uint4(e[0], e[1], e[2], e[3]);
+        const uint4 e1 = make_uint4(e[4], e[5], e[6], e[7]);
+        ((uint4*)(arow + k0))[0] = e0;
+        ((uint4*)(arow + k0))[1] = e1;
+        ((uint4*)(arow + K + k0))[0] = e0;
+        ((uint4*)(arow + K + k0))[1] = e1;
       }
     } else {
       *(uint2*)(qweight + n * (K / 8) + k0 / 8) = make_uint2(pack8(q), pack8(q + 8));

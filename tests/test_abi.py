@@ -254,7 +254,7 @@ def test_search_gram_errors_and_workspace():
     M, N, K = 65536, 12288, 4096
     st, b = ws_size(awq.OP_SEARCH_SCALE_GRAM, M, N, K)
     assert st == OK
-    core = K * M * 2 + K * K * 4 + K * 3 * K * 2 + N * 3 * K * 2 + N * K * 4
+    core = K * M * 2 + K * K * 4 + K * 2 * K * 2 + N * 2 * K * 2 + N * K * 4
     assert core <= b < core + 64 * 2 ** 20
     assert ws_size(awq.OP_SEARCH_SCALE_GRAM, 300, 200, 384)[1] >= 384 * 384 * 2
     assert ws_size(awq.OP_SEARCH_SCALE_GRAM, 256, 512, 500)[0] == SHAPE

@@ -414,6 +414,26 @@ def test_decode_gemm_is_bit_reproducible(dev):
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
+def test_decode_gemm_workspace_reuse(dev):
+    """One workspace shared by a sequence of calls (different shapes and
+    split counts, repeated) gives results bit-identical to fresh workspaces:
+    nothing a call leaves in it changes a later call."""
+    announce("decode_gemm workspace reuse")
+    shapes = [(1, 6144, 4096), (16, 4096, 14336), (3, 1000, 1024), (1, 6144, 4096), (8, 520, 2048)]
+    need = max(awq.workspace_size(awq.OP_DECODE_GEMM, M, N, K) for M, N, K in shapes)
+    assert need > 0
+    shared = torch.full((need,), 0x7F, dtype=torch.uint8, device=dev)
+    for rep in range(2):
+        for i, (M, N, K) in enumerate(shapes):
+            a = synth.decode_activations(K, M, seed=i)
+            qw, sc, ze = random_packed(N, K, 4, seed=i)
+            args = (to_dev_bf16(a, dev), torch.from_numpy(qw.view(np.int32)).to(dev),
+                    to_dev_f32(sc, dev), torch.from_numpy(ze).to(dev), 4)
+            y_shared = awq.decode_gemm(*args, workspace=shared).cpu().numpy()
+            y_fresh = awq.decode_gemm(*args).cpu().numpy()
+            assert np.array_equal(y_shared.view(np.uint32), y_fresh.view(np.uint32)), (rep, i)
+
+
 def test_decode_gemm_matches_search_operand_when_exact(dev):
     """Power-of-two steps make (q - z) * step exact in bf16: the decode kernel
     and the general W4A16 kernel then compute the same products."""
