@@ -484,6 +484,12 @@ def main() -> int:
     # The same launch on constant operands: identical instructions and memory
     # traffic, almost no bit toggling in the matrix cores.  The gap to the
     # synthetic data is the chip's power limit, not the kernel's schedule.
+    # The vendor library's plain bf16 GEMM on the same operands (hipBLASLt via
+    # torch.mm, bf16 out): a yardstick for the contraction, not part of the path.
+    d_t = d_mid.t().contiguous()
+    y_mm = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    t_mm = event_time_ms(lambda: torch.mm(xd, d_t, out=y_mm), max(2, reps // 2), stream)
+    del d_t, y_mm
     t_sse_c = None
     if not args.no_power_probe:
         x_one, d_one = torch.ones_like(xd), torch.ones_like(d_mid)
@@ -510,7 +516,8 @@ def main() -> int:
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
     log(f"search contraction {t_sse:.3f} ms = {tf(t_sse):.1f} TFLOP/s; against y_ref "
         f"{t_sse_y:.3f} ms = {tf(t_sse_y):.1f} TFLOP/s; on constant operands "
-        f"{(t_sse_c or float('nan')):.3f} ms; packed w4a16+sse {t_w4:.3f} ms "
+        f"{(t_sse_c or float('nan')):.3f} ms; hipBLASLt bf16 mm {t_mm:.3f} ms = {tf(t_mm):.1f} "
+        f"TFLOP/s; packed w4a16+sse {t_w4:.3f} ms "
         f"= {tf(t_w4):.1f} TFLOP/s; reference {t_ref:.3f} ms = {tf(t_ref):.1f} TFLOP/s")
     log(f"stats {t_stats * 1e3:.1f} us = {gbs(stats_bytes, t_stats):.0f} GB/s; quantize+pack "
         f"{t_quant * 1e3:.1f} us = {gbs(quant_bytes, t_quant):.0f} GB/s; dequant operand "
@@ -550,6 +557,7 @@ def main() -> int:
             "search_contraction": mfma_entry(t_sse),
             "candidate_sse_vs_yref": mfma_entry(t_sse_y),
             "search_contraction_constant_operands": mfma_entry(t_sse_c) if t_sse_c else None,
+            "vendor_bf16_gemm_same_shape": mfma_entry(t_mm),
             "w4a16_gemm_sse": mfma_entry(t_w4),
             "reference_gemm": mfma_entry(t_ref),
             "act_stats": hbm_entry(stats_bytes, t_stats),
