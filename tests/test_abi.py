@@ -183,14 +183,15 @@ def test_decode_gemm_errors_and_plan():
     assert call(a=FAKE_MIS) == ALIGN
     assert call(y=FAKE_MIS) == ALIGN
     assert call(M=0) == OK and call(N=0) == OK       # empty: no-op
-    # A narrow layer is split along K: the partials need workspace.
-    need = awq.workspace_size(awq.OP_DECODE_GEMM, 4, 128, 4096)
-    assert need >= 4 * 128 * 4 * 2
-    assert call() == WORKSPACE
-    assert call(ws=FAKE, wsb=need - 1) == WORKSPACE
-    # A wide layer whose K fits one slice fills the GPU unsplit: no workspace.
-    assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 65536, 2048) == 0
-    assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 65536, 4096) > 0
+    # Up to K = 8192 one workgroup's waves cover K: no workspace.  Beyond,
+    # K is split across workgroups and the partials need workspace.
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 4, 128, 4096) == 0
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 4096, 8192) == 0
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 4096, 8320) > 0
+    need = awq.workspace_size(awq.OP_DECODE_GEMM, 4, 128, 32768)
+    assert need >= 2 * 4 * 128 * 4
+    assert call(K=32768) == WORKSPACE
+    assert call(K=32768, ws=FAKE, wsb=need - 1) == WORKSPACE
 
 
 def test_dequant_operand_errors():

@@ -381,9 +381,12 @@ def run_decode(dev, M, N, K, bits, seed):
     return y.cpu().numpy(), (a, qw, sc, ze)
 
 
-# (M, N, K): split-K and unsplit, ragged N, one group, odd token counts.
+# (M, N, K): K within one workgroup (waves with one, several or no groups)
+# and split across workgroups (K > 8192), ragged N, one group, odd token
+# counts, narrow and wide layers (16-, 32- and 64-column workgroups).
 DECODE_SHAPES = [(1, 64, 128), (2, 200, 256), (3, 1000, 1024), (4, 4096, 4096), (8, 520, 2048),
-                 (13, 4104, 384), (16, 6144, 4096), (16, 40960, 512), (5, 16, 1152)]
+                 (13, 4104, 384), (16, 6144, 4096), (16, 40960, 512), (5, 16, 1152),
+                 (2, 520, 16512), (1, 72, 32768), (16, 8200, 16384)]
 
 
 @pytest.mark.parametrize("bits", [4, 3])
@@ -419,7 +422,7 @@ def test_decode_gemm_workspace_reuse(dev):
     split counts, repeated) gives results bit-identical to fresh workspaces:
     nothing a call leaves in it changes a later call."""
     announce("decode_gemm workspace reuse")
-    shapes = [(1, 6144, 4096), (16, 4096, 14336), (3, 1000, 1024), (1, 6144, 4096), (8, 520, 2048)]
+    shapes = [(1, 6144, 4096), (2, 520, 33024), (3, 1000, 1024), (1, 72, 32768), (8, 520, 2048)]
     need = max(awq.workspace_size(awq.OP_DECODE_GEMM, M, N, K) for M, N, K in shapes)
     assert need > 0
     shared = torch.full((need,), 0x7F, dtype=torch.uint8, device=dev)
