@@ -90,7 +90,7 @@ KERNEL_LABELS = [
     ("quantize_kernel<3, 3>", "diff_operand (quantize -> bf16 B - W)"),
     ("transpose_pad_kernel", "X^T (Gram form)"),
     ("gram_split_kernel", "G split (Gram form)"),
-    ("decode_gemm", "decode W4A16 GEMM (M <= 16)"),
+    ("decode_gemm", "decode W4A16 GEMM (M <= 64)"),
     ("decode_reduce", "decode split-K reduce"),
     ("act_stats_partial", "act_stats partial sums"),
     ("act_stats_finalize", "act_stats finalize"),
@@ -267,7 +267,7 @@ def event_time_ms(fn, reps: int, stream) -> float:
 
 def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
     """Decode-shaped W4A16 contraction on the Llama-3-8B block's layers
-    (M = 1 and 16 tokens, random packed INT4 weights).  Launches cycle through
+    (M = 1, 16 and 64 tokens, random packed INT4 weights).  Launches cycle through
     enough copies of the packed weights (>= 768 MiB in all) that each one
     streams from HBM rather than the 256 MiB last-level cache.  Each figure
     is the average over `reps` launches captured in one HIP graph and
@@ -289,7 +289,7 @@ def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
             sc = torch.rand((N, K // 128), device=dev, generator=gen) * 0.003 + 0.001
             ze = torch.randint(0, 16, (N, K // 128), dtype=torch.uint8, device=dev, generator=gen)
             packs.append((qw, sc, ze))
-        for M in (1, 16):
+        for M in (1, 16, 64):
             a = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
             need = awq.workspace_size(awq.OP_DECODE_GEMM, M, N, K)

@@ -225,7 +225,7 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                           float* y, double* sse, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Decode-shaped W4A16 contraction for 1 <= M <= 16 tokens, the deployment
+ * Decode-shaped W4A16 contraction for 1 <= M <= 64 tokens, the deployment
  * case (builderai "About": kernels for 4-bit weights with 16-bit activations;
  * robotsatlas "Implementation pitfalls": the speedup needs a kernel that reads
  * the packed weights directly; "Limitations": the benefit depends on matched
@@ -237,9 +237,10 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
  *           the caller folds it)
  *   qweight/scales/zeros as from awq_quantize_pack, bits 3 or 4
  *   y       f32 [M][N] output
- *   ws      awq_workspace_size(AWQ_OP_DECODE_GEMM) bytes (fp32 partials of
- *           the K splits; may be NULL when that size is 0).
- * M > 16 gives AWQ_ERR_SHAPE (use awq_w4a16_gemm).  M == 0 or N == 0 is a
+ *   ws      awq_workspace_size(AWQ_OP_DECODE_GEMM) bytes (fp32 partials
+ *           when K > 8192 is split across workgroups; 0 otherwise, and ws may
+ *           then be NULL).
+ * M > 64 gives AWQ_ERR_SHAPE (use awq_w4a16_gemm).  M == 0 or N == 0 is a
  * no-op.  Results are bit-reproducible for a given (M, N, K).
  */
 awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,

@@ -265,7 +265,7 @@ def candidate_sse(x: torch.Tensor, b: torch.Tensor, y_ref: torch.Tensor | None,
 def decode_gemm(a: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
                 bits: int = 4, group: int = 128, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = A . ((q - z) * step)^T for 1 <= M <= 16 tokens (fp32 [M][N])."""
+    """Y = A . ((q - z) * step)^T for 1 <= M <= 64 tokens (fp32 [M][N])."""
     a = _bf16(a, "a")
     M, K = a.shape
     N = qweight.shape[0]

@@ -92,7 +92,7 @@ struct GemmOperands {
 hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream);
 
 // ---- decode-shaped W4A16 contraction (M <= 16) ----
-constexpr int64_t kDecodeMaxM = 16;
+constexpr int64_t kDecodeMaxM = 64;
 struct DecodePlan {
   int64_t groups_per_split;
   int64_t splits;

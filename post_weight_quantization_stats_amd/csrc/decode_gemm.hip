@@ -1,10 +1,10 @@
-// Decode-shaped W4A16 contraction: Y[M][N] = A . Wd^T for M <= 16 tokens, with
+// Decode-shaped W4A16 contraction: Y[M][N] = A . Wd^T for M <= 64 tokens, with
 // Wd[n][k] = (q[n][k] - z[n][g]) * step[n][g] taken from the packed weights
 // (builderai AWQ page, "About": kernels for 4-bit weights and 16-bit
 // activations; robotsatlas AWQ page, "Implementation pitfalls": without a
 // matched INT4 kernel, dequantizing first throws the speedup away).
 //
-// At M <= 16 the contraction streams the packed weights once (0.54 bytes per
+// At M <= 64 the contraction streams the packed weights once (0.54 bytes per
 // weight) and does 2*M flops per weight, so it is bound by HBM, and the VALU
 // work per weight has to stay near one instruction.  The kernel never forms
 // (q - z) * step per weight:
@@ -19,6 +19,9 @@
 //   * The group is then folded once per output: y += step * (S - (128 + z) *
 //     sum A).  The products are exact in fp32, so the result is the
 //     fp32-accumulated value of sum_k A * (q - z) * step.
+//
+// Up to 64 tokens: MB 16-row blocks of A per workgroup; each group's codes
+// are turned into bf16 once and feed every row block.
 //
 // Work split.  At these sizes a call is dominated by fixed latency (a kernel
 // costs several microseconds before it streams a byte), so the layer should be
@@ -37,6 +40,7 @@
 // table up front, one distinct element per lane: loaded per group and per
 // lane they would touch 16 cache lines for 64 useful bytes per instruction.
 #include <algorithm>
+#include <type_traits>
 
 #include "awq_internal.h"
 #include "device_common.h"
@@ -94,20 +98,22 @@ __device__ __forceinline__ bf16x8 codes_b(uint32_t w) {
 }
 
 // One group's loads for one lane: its 16 bytes of codes per 16-column block
-// and its 64 bytes of activations (channels 32*g4 .. 32*g4+31 of the group).
-template <int NB>
+// and, per 16-row block of tokens, its 64 bytes of activations (channels
+// 32*g4 .. 32*g4+31 of the group).
+template <int NB, int MB>
 struct GroupLoads {
   uint4 q[NB];
-  uint4 a[4];
+  uint4 a[MB][4];
 };
 
-// NB 16-column blocks per workgroup (all of its waves work on them).
-template <int NB>
+// NB 16-column blocks per workgroup (all of its waves work on them) and MB
+// 16-row blocks of tokens (M <= 16 * MB).
+template <int NB, int MB>
 __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int kCols = 16 * NB;
   __shared__ float2 ssz[kWaves][kCols][kWaveGroups];    // (step, 128 + z), 8 to 32 KiB
-  __shared__ f32x4 red[kWaves - 1][NB][64];              // partial outputs of waves 1..3
+  __shared__ f32x4 red[kWaves - 1][MB][NB][64];          // partial outputs of waves 1..3
 
   const int lane = threadIdx.x & 63;
   // Wave index in an SGPR, so the buffer resources below are scalar.
@@ -116,7 +122,9 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
   const int g4 = lane >> 4;         // quarter of the 128-channel group
   const int64_t M = p.M, N = p.N, K = p.K;
   // A rows past M repeat row M-1 (their outputs are never stored).
-  const int arow = min(c16, (int)M - 1);
+  int arow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) arow[mb] = min(16 * mb + c16, (int)M - 1);
   const int64_t G = K / kGroup;
   const int64_t n_blk = (int64_t)blockIdx.x * kCols;
   // This workgroup's groups [gb0, gb1); this wave's [g0, g0 + gn).
@@ -153,19 +161,24 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
 #pragma unroll
   for (int b = 0; b < NB; ++b)
     q_off[b] = (uint32_t)((b * 16 + c16) * (K / 2) + g0 * 64 + g4 * 16);
-  const uint32_t a_off = (uint32_t)((arow * K + g0 * kGroup + 32 * g4) * 2);
+  uint32_t a_off[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    a_off[mb] = (uint32_t)((arow[mb] * K + g0 * kGroup + 32 * g4) * 2);
   // Loads of local group gl.  Past the wave's last group the offset points
   // outside the buffer: the load returns zeros without a memory access.
-  auto load = [&](GroupLoads<NB>& L, int gl) {
+  auto load = [&](GroupLoads<NB, MB>& L, int gl) {
     const bool in = gl < gn;
 #pragma unroll
     for (int b = 0; b < NB; ++b) L.q[b] = ld16(rq, in ? q_off[b] + (uint32_t)gl * 64 : 0xFFFFFFF0u);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      L.a[j] = ld16(ra, in ? a_off + (uint32_t)gl * (kGroup * 2) + 16 * j : 0xFFFFFFF0u);
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        L.a[mb][j] = ld16(ra, in ? a_off[mb] + (uint32_t)gl * (kGroup * 2) + 16 * j : 0xFFFFFFF0u);
   };
 
-  GroupLoads<NB> R[kDepth];
+  GroupLoads<NB, MB> R[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) load(R[d], d);
 
@@ -180,27 +193,41 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
 
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
                                                        0x3F803F80u});
-  f32x4 y[NB];
+  f32x4 y[MB][NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) y[mb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const GroupLoads<NB>& L, int gl) {
-    bf16x8 af[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) af[j] = permute_a(L.a[j]);
-    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};               // sum A, rows 4*g4 .. 4*g4+3
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], ones, sa, 0, 0, 0);
+  auto compute = [&](const GroupLoads<NB, MB>& L, int gl) {
+    // The codes as bf16 128 + q, once per group for every row block.
+    bf16x8 bq[NB][4];
+    float2 sz[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const uint32_t words[4] = {L.q[b].x, L.q[b].y, L.q[b].z, L.q[b].w};
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], codes_b(words[j]), acc, 0, 0, 0);
-      const float2 sz = ssz[wave][b * 16 + c16][gl];
+      for (int j = 0; j < 4; ++j) bq[b][j] = codes_b(words[j]);
+      sz[b] = ssz[wave][b * 16 + c16][gl];
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[b][i] = fmaf(sz.x, fmaf(-sz.y, sa[i], acc[i]), y[b][i]);
+    for (int mb = 0; mb < MB; ++mb) {
+      bf16x8 af[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) af[j] = permute_a(L.a[mb][j]);
+      f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};             // sum A, rows 16mb + 4*g4 .. +3
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], ones, sa, 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bq[b][j], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          y[mb][b][i] = fmaf(sz[b].x, fmaf(-sz[b].y, sa[i], acc[i]), y[mb][b][i]);
+      }
     }
   };
 
@@ -217,26 +244,32 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
   // Sum the waves' partial outputs in wave order.
   if (wave > 0) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) red[wave - 1][b][lane] = y[b];
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) red[wave - 1][mb][b][lane] = y[mb][b];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int w = 0; w < kWaves - 1; ++w)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) y[b] += red[w][b][lane];
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) y[mb][b] += red[w][mb][b][lane];
 
-  // Output: lane holds column c16 of each block and rows 4*g4 + i.
+  // Output: lane holds column c16 of each block and rows 16mb + 4*g4 + i.
   float* out = p.out + (int64_t)blockIdx.y * M * N;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int64_t n = n_blk + b * 16 + c16;
     if (n < N) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = 4 * g4 + i;
-        if (m < M) out[m * N + n] = y[b][i];
-      }
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = 16 * mb + 4 * g4 + i;
+          if (m < M) out[m * N + n] = y[mb][b][i];
+        }
     }
   }
 #endif
@@ -253,13 +286,15 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
   y[i] = acc;
 }
 
-// 16-column blocks per workgroup.  Measured (4 waves, ring of 2) on the
-// Llama-3-8B layers at M = 1 and 16: one block for few tokens on layers up to
-// 16K wide; two when M > 4 on layers of at least 4096 columns, or on wider
-// layers at any M; four for M > 8 on layers of at least 16K columns.
-int decode_blocks_per_group(int64_t M, int64_t N) {
-  if (M > 8 && ceil_div(N, (int64_t)64) >= 256) return 4;
-  if ((M > 4 && ceil_div(N, (int64_t)32) >= 128) || ceil_div(N, (int64_t)32) >= 512) return 2;
+// 16-column blocks per workgroup, from the number of workgroups one block
+// each would give (b1, K splits included).  Measured (4 waves, ring of 2) on
+// the Llama-3-8B layers at M = 1, 16, 32 and 64: more columns let an
+// activation fragment feed more codes, which pays once M > 4 if at least 192
+// workgroups remain, and at any M on the widest layers.
+int decode_blocks_per_group(int64_t M, int64_t N, int64_t splits) {
+  const int64_t b1 = ceil_div(N, (int64_t)16) * splits;
+  if (M > 8 && b1 >= 1024) return 4;
+  if ((M > 4 && b1 >= 384) || b1 >= 1024) return 2;
   return 1;
 }
 
@@ -289,14 +324,26 @@ hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K
   p.N = N;
   p.K = K;
   p.groups_per_split = d.groups_per_split;
-  const int nb = decode_blocks_per_group(M, N);
+  const int nb = decode_blocks_per_group(M, N, d.splits);
+  const int mb = (int)ceil_div(M, (int64_t)16);
   dim3 grid((unsigned)ceil_div(N, (int64_t)16 * nb), (unsigned)d.splits);
+  auto go = [&](auto NBc, auto MBc) {
+    decode_gemm_kernel<decltype(NBc)::value, decltype(MBc)::value><<<grid, kThreads, 0, stream>>>(p);
+  };
+  auto go_mb = [&](auto NBc) {
+    if (mb == 1)
+      go(NBc, std::integral_constant<int, 1>{});
+    else if (mb == 2)
+      go(NBc, std::integral_constant<int, 2>{});
+    else
+      go(NBc, std::integral_constant<int, 4>{});
+  };
   if (nb == 4)
-    decode_gemm_kernel<4><<<grid, kThreads, 0, stream>>>(p);
+    go_mb(std::integral_constant<int, 4>{});
   else if (nb == 2)
-    decode_gemm_kernel<2><<<grid, kThreads, 0, stream>>>(p);
+    go_mb(std::integral_constant<int, 2>{});
   else
-    decode_gemm_kernel<1><<<grid, kThreads, 0, stream>>>(p);
+    go_mb(std::integral_constant<int, 1>{});
   if (d.splits > 1) {
     const int64_t count = M * N;
     decode_reduce_kernel<<<(unsigned)ceil_div(count, (int64_t)256), 256, 0, stream>>>(

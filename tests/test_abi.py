@@ -175,7 +175,7 @@ def test_decode_gemm_errors_and_plan():
 
     assert call(a=None) == NULL
     assert call(y=None) == NULL
-    assert call(M=17) == SHAPE                       # larger M: awq_w4a16_gemm
+    assert call(M=65) == SHAPE                       # larger M: awq_w4a16_gemm
     assert call(M=-1) == SHAPE
     assert call(K=100) == SHAPE
     assert call(bits=2) == UNSUPPORTED

@@ -386,7 +386,9 @@ def run_decode(dev, M, N, K, bits, seed):
 # counts, narrow and wide layers (16-, 32- and 64-column workgroups).
 DECODE_SHAPES = [(1, 64, 128), (2, 200, 256), (3, 1000, 1024), (4, 4096, 4096), (8, 520, 2048),
                  (13, 4104, 384), (16, 6144, 4096), (16, 40960, 512), (5, 16, 1152),
-                 (2, 520, 16512), (1, 72, 32768), (16, 8200, 16384)]
+                 (2, 520, 16512), (1, 72, 32768), (16, 8200, 16384),
+                 (17, 1000, 1024), (32, 6144, 4096), (48, 520, 16512), (64, 4096, 4096),
+                 (64, 20000, 640), (33, 40, 128)]
 
 
 @pytest.mark.parametrize("bits", [4, 3])
@@ -404,7 +406,7 @@ def test_decode_gemm(dev, shape, bits):
 def test_decode_gemm_llama3_block_shapes(dev, name):
     """The Llama-3-8B block's layers at their full sizes, M = 1 and 16."""
     spec = synth.layer_spec("llama3_8b_block", name)
-    for M in (1, 16):
+    for M in (1, 16, 64):
         announce("decode_gemm full size", name, M)
         y, (a, qw, sc, ze) = run_decode(dev, M, spec.N, spec.K, 4, seed=M)
         gemm_close(y, O.decode_gemm(a, qw, sc, ze, 128))
