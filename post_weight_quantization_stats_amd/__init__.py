@@ -336,3 +336,8 @@ def search_scale_gram(x: torch.Tensor, w: torch.Tensor, bits: int = 4, group: in
                                        _ptr(out["zeros"]), _ptr(ws), ws.numel(), _stream(dev)),
            "awq_search_scale_gram")
     return out
+
+
+from .linear import W4A16Linear, fold_inverse_scale  # noqa: E402  (needs the names above)
+
+__all__ += ["W4A16Linear", "fold_inverse_scale"]
