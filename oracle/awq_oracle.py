@@ -36,6 +36,8 @@ contract the GPU library implements):
   packing          qweight[n][t] = sum_i q[n, 8t+i] << 4i  (u32, sequential
                    nibbles along K; 3-bit codes use the same 4-bit containers)
                    scales f32 [N][K/group], zeros u8 [N][K/group]
+  dense INT3       qweight3[n][3c .. 3c+2] = the 96-bit little-endian value
+                   sum_i q[n, 32c+i] << 3i of each run of 32 codes
   dequantized B    B[n,k] = bf16( f32( f32((q - z) * step) * inv_s[k] ) )
                    (1/s folded into the weight operand; the activation operand
                    is the caller's bf16 X, unchanged)
@@ -58,7 +60,8 @@ innocuous?", 1995).  Products of two fp32 values are exact in fp64.
 
 Parity unpinned (convention only, no value on the pages can fix them): the
 normalising constant sqrt(max*min), the 1e-4 floor, the nibble order of the
-packed layout and the 4-bit container used for INT3 codes.
+packed layout, the 4-bit container used for INT3 codes and the bit order of the
+dense INT3 layout.
 """
 
 from __future__ import annotations
@@ -229,6 +232,35 @@ def packed_bytes(N: int, K: int, group: int) -> int:
     return N * K // 2 + N * (K // group) * (4 + 1)
 
 
+def pack3(q):
+    """Dense INT3 codes ([P4] opening paragraph: 3- and 4-bit weights): each
+    run of 32 codes along K is one 96-bit little-endian value with code i at
+    bits 3i .. 3i+2, stored as three u32 words.  qweight3 u32 [N][3K/32]."""
+    q = np.asarray(q, dtype=np.int64)
+    N, K = q.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    if q.min(initial=0) < 0 or q.max(initial=0) > 7:
+        raise ValueError("codes must lie in [0, 7]")
+    bits = ((q.reshape(N, K // 32, 32, 1) >> np.arange(3)) & 1).astype(np.uint8)
+    by = np.packbits(bits.reshape(N, K // 32, 96), axis=-1, bitorder="little")   # 12 bytes
+    return np.ascontiguousarray(by).view("<u4").reshape(N, 3 * K // 32).astype(np.uint32)
+
+
+def unpack3(qweight3):
+    """Codes [N][K] from dense INT3 words (inverse of pack3)."""
+    w = np.ascontiguousarray(np.asarray(qweight3, dtype="<u4"))
+    N, T = w.shape
+    bits = np.unpackbits(w.view(np.uint8).reshape(N, T // 3, 12), axis=-1, bitorder="little")
+    b3 = bits.reshape(N, T // 3, 32, 3).astype(np.int64)
+    return (b3[..., 0] | (b3[..., 1] << 1) | (b3[..., 2] << 2)).reshape(N, T // 3 * 32)
+
+
+def packed3_bytes(N: int, K: int, group: int) -> int:
+    """Storage of the dense INT3 form: 3-bit codes + fp32 scale + u8 zero per group."""
+    return N * 3 * K // 8 + N * (K // group) * (4 + 1)
+
+
 # --------------------------------------------------------------------------
 # Step 4: the weight operand of the contraction and the per-candidate loss.
 # [P3] "How it works" / "Key mechanisms": the scale is chosen by a grid search
@@ -367,13 +399,25 @@ def deploy_gemm(a_bits, qweight, scales, zeros, group: int, inv32=None) -> np.nd
     return gemm(a_bits, B)
 
 
+def decode_gemm3(a_bits, qweight3, scales, zeros, group: int) -> np.ndarray:
+    """The deployment contraction on dense INT3 weights: decode_gemm's
+    product with the codes read through unpack3."""
+    q = unpack3(qweight3)
+    return _decode_product(a_bits, q, scales, zeros, group)
+
+
 def decode_gemm(a_bits, qweight, scales, zeros, group: int) -> np.ndarray:
     """Deployment contraction with packed weights ([P1] "About": 4-bit weights
     with 16-bit activations; [P3] "Implementation pitfalls": the packed form
     is read directly): Y = A . Wd^T with Wd = (q - z) * step exactly.  (q - z)
     is a small integer and step a binary32, so every Wd and every product with
     a bf16 activation is exact in fp64; only the K-sum rounds."""
-    q = unpack(qweight).astype(np.float64)
+    return _decode_product(a_bits, unpack(qweight), scales, zeros, group)
+
+
+def _decode_product(a_bits, q, scales, zeros, group: int) -> np.ndarray:
+    """A . ((q - z) * step)^T in fp64 from codes [N][K]."""
+    q = np.asarray(q, np.float64)
     z = np.repeat(np.asarray(zeros, np.float64), group, axis=1)
     step = np.repeat(np.asarray(scales, np.float32).astype(np.float64), group, axis=1)
     wd = (q - z) * step

@@ -99,11 +99,32 @@ def _mut_diff_off_by_half_ulp(mp):
                lambda w, b: OA.f32(np.asarray(b, np.float64) - OA.bf16_bits_to_f64(w)) * (1 + 2.0 ** -9))
 
 
+def _mut_pack3_code_bits_reversed(mp):
+    orig = OA.pack3
+
+    def p3(q):
+        q = np.asarray(q, np.int64)
+        rev = ((q & 1) << 2) | (q & 2) | ((q >> 2) & 1)      # bit order inside each code
+        return orig(rev)
+    mp.setattr(oracle, "pack3", p3)
+
+
+def _mut_pack3_runs_of_16(mp):
+    orig = OA.pack3
+
+    def p3(q):
+        q = np.asarray(q, np.int64)
+        N, K = q.shape
+        perm = np.arange(K).reshape(K // 32, 2, 16)[:, ::-1, :].reshape(K)   # halves swapped
+        return orig(q[:, perm])
+    mp.setattr(oracle, "pack3", p3)
+
+
 MUTATIONS = [_mut_floor_instead_of_rint, _mut_drop_inv_s, _mut_alpha_grid_closed,
              _mut_scale_index_reversed, _mut_zero_added_before_rounding, _mut_loss_sign,
              _mut_no_range_extension, _mut_stats_mean_without_abs, _mut_normaliser_max_only,
              _mut_decode_zero_of_first_group, _mut_decode_rounds_weight_to_bf16, _mut_diff_sign,
-             _mut_diff_off_by_half_ulp]
+             _mut_diff_off_by_half_ulp, _mut_pack3_code_bits_reversed, _mut_pack3_runs_of_16]
 
 PINS = [
     P.test_quantizer_worked_group,
@@ -118,6 +139,8 @@ PINS = [
     P.test_decode_gemm_brute_force_from_words,
     P.test_decode_gemm_unit_codes_closed_form,
     lambda: P.test_difference_operand_is_exact(4),
+    P.test_pack3_worked_words,
+    P.test_pack3_big_integer_brute_force,
 ]
 
 

@@ -300,6 +300,46 @@ def test_pack_worked_and_roundtrip():
     assert np.array_equal(O.unpack(O.pack(q, np.zeros((7, 2)), np.ones((7, 2)))[0]), q)
 
 
+def test_pack3_worked_words():
+    with open(os.path.join(GOLDEN, "pack3_worked.json")) as f:
+        g = json.load(f)
+    q = np.array(g["codes"], dtype=np.int64)[None, :]
+    words = O.pack3(q)
+    assert [hex(int(x)) for x in words[0]] == g["expected_words_hex"]
+    assert np.array_equal(O.unpack3(words), q)
+
+
+def test_pack3_big_integer_brute_force():
+    """Each 32-code run as one Python integer, built code by code."""
+    rng = np.random.default_rng(31)
+    q = rng.integers(0, 8, size=(7, 256))
+    words = O.pack3(q)
+    assert words.shape == (7, 24) and words.dtype == np.uint32
+    for n in range(7):
+        for c in range(8):
+            v = 0
+            for i in range(32):
+                v += int(q[n, 32 * c + i]) * 8 ** i
+            assert [int(x) for x in words[n, 3 * c:3 * c + 3]] == [v % 2 ** 32, (v >> 32) % 2 ** 32,
+                                                                   v >> 64]
+    assert np.array_equal(O.unpack3(words), q)
+    with pytest.raises(ValueError):
+        O.pack3(np.full((1, 32), 8))
+
+
+def test_dense_int3_storage_and_product():
+    """Dense INT3 takes 3 bits per weight plus 40 bits per group (3.31 bits,
+    4.83x smaller than bf16), and the product from its words equals the
+    product from the 4-bit containers for the same codes."""
+    assert O.packed3_bytes(64, 4096, 128) * 8 / (64 * 4096) == 3 + 40 / 128
+    assert 16 / (3 + 40 / 128) == pytest.approx(4.83, abs=0.01)
+    x, w = synth.random_layer(5, 256, 24, seed=17)
+    q, z, st = O.quantize(w, None, 3, 128)
+    qw, sc, ze = O.pack(q, z, st)
+    a = x[:5]
+    assert np.array_equal(O.decode_gemm3(a, O.pack3(q), sc, ze, 128), O.decode_gemm(a, qw, sc, ze, 128))
+
+
 def test_storage_about_four_times_smaller():
     """~4x smaller than 16-bit and ~4.x bits per weight (vectordb 'Features',
     robotsatlas 'Computational complexity')."""
