@@ -145,6 +145,20 @@ awq_status awq_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const floa
                              void* stream);
 
 /*
+ * The same quantization with 3-bit codes written densely (sourcepulse AWQ
+ * project page, opening paragraph: 3- and 4-bit weights), so the codes take
+ * 3 bits per weight instead of a 4-bit container: each run of 32 codes along
+ * K is one 96-bit little-endian value, code i at bits 3i .. 3i+2, stored as
+ * three u32 words.  Steps and zeros as awq_quantize_pack with bits = 3.
+ *   w bf16 [N][K], s f32 [K] or NULL (s = 1)
+ *   qweight3 u32 [N][3K/32] (4-byte aligned), scales f32 [N][K/group],
+ *   zeros u8 [N][K/group].  N == 0 is a no-op.
+ */
+awq_status awq_quantize_pack3(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                              int32_t group, uint32_t* qweight3, float* scales, uint8_t* zeros,
+                              void* stream);
+
+/*
  * Dequantized weight operand of one candidate scale, the search's inner step
  * (robotsatlas "How it works": the weight is scaled by s, quantized
  * group-wise, and the activation divided by s; here 1/s is folded into the
@@ -247,6 +261,19 @@ awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_
                                  const uint32_t* qweight, const float* scales,
                                  const uint8_t* zeros, int32_t bits, int32_t group, float* y,
                                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The same decode-shaped contraction on dense INT3 weights (the layout of
+ * awq_quantize_pack3): 0.375 bytes of codes per weight instead of 0.5.
+ * Arguments, limits, workspace (awq_workspace_size(AWQ_OP_DECODE_GEMM)) and
+ * results as awq_w4a16_decode_gemm with bits = 3; qweight3 u32 [N][3K/32],
+ * 4-byte aligned.  For the same codes the result is bit-identical to
+ * awq_w4a16_decode_gemm on the 4-bit containers.
+ */
+awq_status awq_w3a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                 const uint32_t* qweight3, const float* scales,
+                                 const uint8_t* zeros, int32_t group, float* y, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /*
  * The whole per-layer search (robotsatlas "How it works", "Key mechanisms";

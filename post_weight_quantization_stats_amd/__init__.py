@@ -18,7 +18,7 @@ from . import build as _build
 
 __all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "quantize_pack",
            "reference_gemm", "w4a16_gemm", "search_scale", "search_scale_gram", "decode_gemm",
-           "dequant_operand", "diff_operand", "candidate_sse", "workspace_size",
+           "dequant_operand", "diff_operand", "candidate_sse", "quantize_pack3", "decode_gemm3", "workspace_size",
            "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES",
            "OP_DECODE_GEMM", "OP_CANDIDATE_SSE", "OP_SEARCH_SCALE_GRAM"]
 
@@ -40,6 +40,10 @@ _SIGNATURES = {
                            _c_void_p, _c_void_p], _i32),
     "awq_dequant_operand": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
                              _c_void_p], _i32),
+    "awq_quantize_pack3": ([_c_void_p, _i64, _i64, _c_void_p, _i32, _c_void_p, _c_void_p,
+                            _c_void_p, _c_void_p], _i32),
+    "awq_w3a16_decode_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
+                               _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
     "awq_diff_operand": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
                           _c_void_p], _i32),
     "awq_candidate_sse": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -279,6 +283,40 @@ def decode_gemm(a: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, ze
                                        bits, group, _ptr(y), _ptr(ws),
                                        0 if ws is None else ws.numel(), _stream(dev)),
            "awq_w4a16_decode_gemm")
+    return y
+
+
+def quantize_pack3(w: torch.Tensor, s: torch.Tensor | None, group: int = 128):
+    """Dense INT3 codes of W . diag(s): (qweight3 int32 [N][3K/32], scales f32, zeros u8)."""
+    w = _bf16(w, "w")
+    N, K = w.shape
+    if s is not None:
+        s = _f32(s, "s")
+    dev = w.device
+    qw = torch.empty((N, 3 * K // 32), dtype=torch.int32, device=dev)
+    sc = torch.empty((N, K // group), dtype=torch.float32, device=dev)
+    ze = torch.empty((N, K // group), dtype=torch.uint8, device=dev)
+    _check(lib().awq_quantize_pack3(_ptr(w), N, K, _ptr(s), group, _ptr(qw), _ptr(sc), _ptr(ze),
+                                    _stream(dev)), "awq_quantize_pack3")
+    return qw, sc, ze
+
+
+def decode_gemm3(a: torch.Tensor, qweight3: torch.Tensor, scales: torch.Tensor,
+                 zeros: torch.Tensor, group: int = 128, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = A . ((q - z) * step)^T from dense INT3 weights, 1 <= M <= 64 (fp32 [M][N])."""
+    a = _bf16(a, "a")
+    M, K = a.shape
+    N = qweight3.shape[0]
+    if qweight3.shape[1] * 32 != 3 * K:
+        raise ValueError("qweight3 must be [N][3K/32]")
+    dev = a.device
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if out is None else _f32(out, "out")
+    need = workspace_size(OP_DECODE_GEMM, M, N, K, 3, group)
+    ws = _workspace(need, dev, workspace) if need > 0 else None
+    _check(lib().awq_w3a16_decode_gemm(_ptr(a), M, N, K, _ptr(qweight3), _ptr(scales), _ptr(zeros),
+                                       group, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                       _stream(dev)), "awq_w3a16_decode_gemm")
     return y
 
 

@@ -253,6 +253,28 @@ awq_status awq_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const floa
   }
 }
 
+awq_status awq_quantize_pack3(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                              int32_t group, uint32_t* qweight3, float* scales, uint8_t* zeros,
+                              void* stream) {
+  try {
+    awq_status st = check_quant_params(3, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (N < 0 || N >= kMaxDim) return fail(AWQ_ERR_SHAPE, "N out of range");
+    if (N == 0) return ok();
+    if (w == nullptr || qweight3 == nullptr || scales == nullptr || zeros == nullptr)
+      return fail(AWQ_ERR_NULL, "w, qweight3, scales and zeros are required");
+    if (misaligned(w) || (s != nullptr && misaligned(s)) || ((uintptr_t)qweight3 & 3u) ||
+        ((uintptr_t)scales & 3u))
+      return fail(AWQ_ERR_ALIGN, "w and s must be 16-byte aligned, qweight3 and scales 4-byte");
+    AWQ_TRY_LAUNCH(awq::launch_quantize_pack3(w, N, K, s, qweight3, scales, zeros,
+                                              (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
 awq_status awq_dequant_operand(const uint16_t* w, int64_t N, int64_t K, const float* s,
                                const float* inv_s, int32_t bits, int32_t group, uint16_t* b,
                                void* stream) {
@@ -363,10 +385,10 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
   }
 }
 
-awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
-                                 const uint32_t* qweight, const float* scales,
-                                 const uint8_t* zeros, int32_t bits, int32_t group, float* y,
-                                 void* ws, size_t ws_bytes, void* stream) {
+static awq_status decode_entry(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                               const uint32_t* qweight, const float* scales,
+                               const uint8_t* zeros, int32_t bits, int32_t group, float* y,
+                               void* ws, size_t ws_bytes, void* stream, bool int3_dense) {
   try {
     awq_status st = check_quant_params(bits, group);
     if (st != AWQ_OK) return st;
@@ -377,18 +399,35 @@ awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_
     if (M == 0 || N == 0) return ok();
     if (a == nullptr || qweight == nullptr || scales == nullptr || zeros == nullptr || y == nullptr)
       return fail(AWQ_ERR_NULL, "a, qweight, scales, zeros and y are required");
-    if (misaligned(a) || misaligned(qweight) || misaligned(y) || misaligned(ws) ||
-        ((uintptr_t)scales & 3u))
-      return fail(AWQ_ERR_ALIGN, "a, qweight, y and ws must be 16-byte aligned, scales 4-byte");
+    if (misaligned(a) || misaligned(y) || misaligned(ws) || ((uintptr_t)scales & 3u) ||
+        (int3_dense ? ((uintptr_t)qweight & 3u) != 0 : misaligned(qweight)))
+      return fail(AWQ_ERR_ALIGN, "a, y and ws must be 16-byte aligned, qweight 16-byte (4-byte "
+                                 "for dense INT3), scales 4-byte");
     const awq::DecodePlan plan = awq::decode_plan(M, N, K);
     if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes))
       return fail(AWQ_ERR_WORKSPACE, "decode GEMM needs %zu workspace bytes", plan.ws_bytes);
     AWQ_TRY_LAUNCH(awq::launch_decode_gemm(a, M, N, K, qweight, scales, zeros, y, ws,
-                                           (hipStream_t)stream));
+                                           (hipStream_t)stream, int3_dense));
     return ok();
   } catch (...) {
     return fail(AWQ_ERR_LAUNCH, "internal error");
   }
+}
+
+awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                 const uint32_t* qweight, const float* scales,
+                                 const uint8_t* zeros, int32_t bits, int32_t group, float* y,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  return decode_entry(a, M, N, K, qweight, scales, zeros, bits, group, y, ws, ws_bytes, stream,
+                      false);
+}
+
+awq_status awq_w3a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                 const uint32_t* qweight3, const float* scales,
+                                 const uint8_t* zeros, int32_t group, float* y, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  return decode_entry(a, M, N, K, qweight3, scales, zeros, 3, group, y, ws, ws_bytes, stream,
+                      true);
 }
 
 awq_status awq_candidate_sse(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint16_t* b,

@@ -52,6 +52,11 @@ hipError_t launch_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const f
                                 const int32_t* s_sel, int bits, uint32_t* qweight,
                                 float* scales, uint8_t* zeros, hipStream_t stream);
 
+// INT3 codes of W . diag(s) in the dense layout (32 codes in three u32 words).
+hipError_t launch_quantize_pack3(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                                 uint32_t* qweight3, float* scales, uint8_t* zeros,
+                                 hipStream_t stream);
+
 // The search's bf16 weight operand for one candidate:
 // b_out[n][k] = bf16(f32(f32((q - z) * step) * inv_s[k])) (inv_s NULL: no factor).
 hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, const float* s,
@@ -99,9 +104,11 @@ struct DecodePlan {
   size_t ws_bytes;          // fp32 partials [splits][M][N] when splits > 1
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
+// int3_dense: qweight holds dense INT3 words [N][3K/32] instead of 4-bit
+// containers [N][K/8].
 hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
                               const uint32_t* qweight, const float* scales, const uint8_t* zeros,
-                              float* y, void* ws, hipStream_t stream);
+                              float* y, void* ws, hipStream_t stream, bool int3_dense = false);
 
 // losses[i] = (sum_t partials[i*T + t]) / divisor, fixed summation order.
 hipError_t launch_loss_reduce(const double* partials, int64_t T, int n_grid, double divisor,

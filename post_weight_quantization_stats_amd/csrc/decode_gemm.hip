@@ -97,6 +97,25 @@ __device__ __forceinline__ bf16x8 codes_b(uint32_t w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Dense INT3 (32 codes in three u32 words, code i at bit 3i): the lane's 32
+// codes of a group come as 12 bytes; each 24-bit run of 8 codes is spread to
+// 4-bit fields (code i at bit 4i) so the 4-bit path below applies unchanged.
+__device__ __forceinline__ uint32_t spread3(uint32_t f) {
+  const uint32_t y = (f & 0xFFFu) | ((f & 0xFFF000u) << 4);   // codes 0-3 | codes 4-7 << 16
+  return (y & 0x00070007u) | ((y & 0x00380038u) << 1) | ((y & 0x01C001C0u) << 2) |
+         ((y & 0x0E000E00u) << 3);
+}
+__device__ __forceinline__ uint4 nibbles_from_int3(uint4 v) {
+  return make_uint4(spread3(v.x & 0xFFFFFFu), spread3((v.x >> 24) | ((v.y & 0xFFFFu) << 8)),
+                    spread3((v.y >> 16) | ((v.z & 0xFFu) << 16)), spread3(v.z >> 8));
+}
+
+__device__ __forceinline__ uint4 ld12(rsrc_t r, uint32_t voff) {
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+  const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, 0);
+  return make_uint4(v.x, v.y, v.z, 0u);
+}
+
 // One group's loads for one lane: its 16 bytes of codes per 16-column block
 // and, per 16-row block of tokens, its 64 bytes of activations (channels
 // 32*g4 .. 32*g4+31 of the group).
@@ -107,8 +126,8 @@ struct GroupLoads {
 };
 
 // NB 16-column blocks per workgroup (all of its waves work on them) and MB
-// 16-row blocks of tokens (M <= 16 * MB).
-template <int NB, int MB>
+// 16-row blocks of tokens (M <= 16 * MB); I3: dense INT3 codes.
+template <int NB, int MB, bool I3>
 __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int kCols = 16 * NB;
@@ -135,8 +154,9 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
   const int gn = (int)max((int64_t)0, min(gb1, g0 + per) - g0);
 
   const rsrc_t ra = make_rsrc(p.a, M * K * 2);
-  // Rows past N read as zero.
-  const rsrc_t rq = make_rsrc(p.qweight + n_blk * (K / 8), (N - n_blk) * (K / 2));
+  // Rows past N read as zero.  Words per row: K/8 (4-bit) or 3K/32 (INT3).
+  const int64_t row_words = I3 ? 3 * K / 32 : K / 8;
+  const rsrc_t rq = make_rsrc(p.qweight + n_blk * row_words, (N - n_blk) * row_words * 4);
   const rsrc_t rs = make_rsrc(p.scales + n_blk * G, (N - n_blk) * G * 4);
   const rsrc_t rz = make_rsrc(p.zeros + n_blk * G, (N - n_blk) * G);
 
@@ -157,10 +177,12 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
         rz, ok ? (uint32_t)(row * G + g0 + gl) : 0xFFFFFFF0u, 0, 0);
   }
 
+  // A lane's codes of group g: bytes 64g + 16*g4 (4-bit) or 48g + 12*g4 (INT3).
+  constexpr uint32_t kGroupBytes = I3 ? 48 : 64, kLaneBytes = I3 ? 12 : 16;
   uint32_t q_off[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
-    q_off[b] = (uint32_t)((b * 16 + c16) * (K / 2) + g0 * 64 + g4 * 16);
+    q_off[b] = (uint32_t)((b * 16 + c16) * row_words * 4 + g0 * kGroupBytes + g4 * kLaneBytes);
   uint32_t a_off[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -170,7 +192,10 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
   auto load = [&](GroupLoads<NB, MB>& L, int gl) {
     const bool in = gl < gn;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) L.q[b] = ld16(rq, in ? q_off[b] + (uint32_t)gl * 64 : 0xFFFFFFF0u);
+    for (int b = 0; b < NB; ++b) {
+      const uint32_t off = in ? q_off[b] + (uint32_t)gl * kGroupBytes : 0xFFFFFFF0u;
+      L.q[b] = I3 ? ld12(rq, off) : ld16(rq, off);
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -205,7 +230,8 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
     float2 sz[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const uint32_t words[4] = {L.q[b].x, L.q[b].y, L.q[b].z, L.q[b].w};
+      const uint4 qw = I3 ? nibbles_from_int3(L.q[b]) : L.q[b];
+      const uint32_t words[4] = {qw.x, qw.y, qw.z, qw.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) bq[b][j] = codes_b(words[j]);
       sz[b] = ssz[wave][b * 16 + c16][gl];
@@ -311,7 +337,7 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
                               const uint32_t* qweight, const float* scales, const uint8_t* zeros,
-                              float* y, void* ws, hipStream_t stream) {
+                              float* y, void* ws, hipStream_t stream, bool int3_dense) {
   if (M == 0 || N == 0) return hipSuccess;
   const DecodePlan d = decode_plan(M, N, K);
   DecodeParams p;
@@ -328,7 +354,11 @@ hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K
   const int mb = (int)ceil_div(M, (int64_t)16);
   dim3 grid((unsigned)ceil_div(N, (int64_t)16 * nb), (unsigned)d.splits);
   auto go = [&](auto NBc, auto MBc) {
-    decode_gemm_kernel<decltype(NBc)::value, decltype(MBc)::value><<<grid, kThreads, 0, stream>>>(p);
+    constexpr int nbv = decltype(NBc)::value, mbv = decltype(MBc)::value;
+    if (int3_dense)
+      decode_gemm_kernel<nbv, mbv, true><<<grid, kThreads, 0, stream>>>(p);
+    else
+      decode_gemm_kernel<nbv, mbv, false><<<grid, kThreads, 0, stream>>>(p);
   };
   auto go_mb = [&](auto NBc) {
     if (mb == 1)

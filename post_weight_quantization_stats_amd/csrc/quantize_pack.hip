@@ -116,8 +116,32 @@ __device__ __forceinline__ uint32_t pack8(const float* q) {
 // and B / W lies in [1/2, 2] (up to the roundings of s and 1/s), and by
 // Sterbenz's lemma the difference of two such bf16 values is a bf16 value.
 // kDiff: for the Gram-form loss D G D^T, D as fp32 [N][K] and the operand
-// [D | D] as bf16 [N][2K] (against [hi(G) | lo(G)]).
-enum QuantMode { kPack = 0, kOperand = 1, kDiff = 2, kDiffOp = 3 };
+// [D | D] as bf16 [N][2K] (against [hi(G) | lo(G)]).  kPack3: INT3 codes in
+// the dense layout (each run of 32 codes along K is one 96-bit little-endian
+// value, code i at bits 3i, in three u32 words), steps and zeros.
+enum QuantMode { kPack = 0, kOperand = 1, kDiff = 2, kDiffOp = 3, kPack3 = 4 };
+// Modes that write codes (the rest write a dequantized operand).
+constexpr bool writes_codes(int mode) { return mode == kPack || mode == kPack3; }
+
+// Sixteen 3-bit codes (as floats) -> the 48-bit value sum q_i << 3i, split
+// into bits 0..31 and 32..47.
+__device__ __forceinline__ void pack48(const float (&q)[16], uint32_t& lo, uint32_t& hi) {
+  lo = 0;
+  hi = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t c = (uint32_t)q[i];
+    const int b = 3 * i;
+    if (b + 3 <= 32) {
+      lo |= c << b;
+    } else if (b >= 32) {
+      hi |= c << (b - 32);
+    } else {
+      lo |= c << b;
+      hi |= c >> (32 - b);
+    }
+  }
+}
 
 template <int BITS, int kMode>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
@@ -143,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   const float* srow = s;
   if (s != nullptr && s_sel != nullptr) srow = s + (int64_t)max(*s_sel, 0) * K;
   if (srow != nullptr) load16(srow, sv);
-  if constexpr (kMode != kPack) {
+  if constexpr (!writes_codes(kMode)) {
     if (inv_s != nullptr) load16(inv_s, iv);
   }
 
@@ -176,8 +200,18 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     }
     float q[16], step, z;
     quantize16<BITS>(ws, q, step, z);
+    uint32_t p_lo = 0, p_hi = 0, o_lo = 0, o_hi = 0;
+    if constexpr (kMode == kPack3) {
+      // Lanes 2m and 2m+1 hold the two halves of one 32-code run; the even
+      // lane takes its neighbour's 48 bits (quad_perm [1,0,3,2]) and writes
+      // the run's three words.  Both lanes of a pair are active or inactive
+      // together (same group and row).
+      pack48(q, p_lo, p_hi);
+      o_lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p_lo, 0xB1, 0xF, 0xF, false);
+      o_hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p_hi, 0xB1, 0xF, 0xF, false);
+    }
     if (!(gvalid && n < N)) continue;
-    if constexpr (kMode != kPack) {
+    if constexpr (!writes_codes(kMode)) {
       float bv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -200,6 +234,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         dst[0] = make_uint4(e[0], e[1], e[2], e[3]);
         dst[1] = make_uint4(e[4], e[5], e[6], e[7]);
       } else {
+        static_assert(kMode == kDiff, "unhandled operand mode");
         float dd[16];
         uint32_t e[8];
 #pragma unroll
@@ -221,7 +256,17 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         ((uint4*)(arow + K + k0))[1] = e1;
       }
     } else {
-      *(uint2*)(qweight + n * (K / 8) + k0 / 8) = make_uint2(pack8(q), pack8(q + 8));
+      static_assert(writes_codes(kMode), "unhandled code mode");
+      if constexpr (kMode == kPack3) {
+        if ((t8 & 1) == 0) {
+          uint32_t* dst = qweight + n * (3 * K / 32) + (k0 / 32) * 3;
+          dst[0] = p_lo;
+          dst[1] = p_hi | (o_lo << 16);
+          dst[2] = (o_lo >> 16) | (o_hi << 16);
+        }
+      } else {
+        *(uint2*)(qweight + n * (K / 8) + k0 / 8) = make_uint2(pack8(q), pack8(q + 8));
+      }
       if (t8 == 0) {
         scales[n * G + g] = step;
         zeros[n * G + g] = (uint8_t)z;
@@ -243,6 +288,16 @@ hipError_t launch_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const f
   else
     quantize_kernel<3, kPack><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, nullptr, qweight,
                                                              scales, zeros, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_pack3(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                                 uint32_t* qweight3, float* scales, uint8_t* zeros,
+                                 hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
+  quantize_kernel<3, kPack3><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, nullptr, qweight3,
+                                                            scales, zeros, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -259,3 +259,26 @@ def test_search_gram_errors_and_workspace():
     assert core <= b < core + 64 * 2 ** 20
     assert ws_size(awq.OP_SEARCH_SCALE_GRAM, 300, 200, 384)[1] >= 384 * 384 * 2
     assert ws_size(awq.OP_SEARCH_SCALE_GRAM, 256, 512, 500)[0] == SHAPE
+
+
+def test_dense_int3_entry_errors():
+    pk = awq.lib().awq_quantize_pack3
+    assert pk(None, 4, 128, None, 128, FAKE, FAKE, FAKE, None) == NULL
+    assert pk(FAKE, 4, 128, None, 128, None, FAKE, FAKE, None) == NULL
+    assert pk(FAKE, 4, 100, None, 128, FAKE, FAKE, FAKE, None) == SHAPE
+    assert pk(FAKE, 4, 128, None, 64, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert pk(FAKE, 4, 128, None, 128, FAKE + 2, FAKE, FAKE, None) == ALIGN
+    assert pk(FAKE_MIS, 4, 128, None, 128, FAKE, FAKE, FAKE, None) == ALIGN
+    assert pk(None, 0, 128, None, 128, None, None, None, None) == OK
+    dg = awq.lib().awq_w3a16_decode_gemm
+
+    def call(a=FAKE, M=4, N=128, K=4096, q=FAKE, group=128, y=FAKE, ws=None, wsb=0):
+        return dg(a, M, N, K, q, FAKE, FAKE, group, y, ws, wsb, None)
+
+    assert call(a=None) == NULL
+    assert call(M=65) == SHAPE
+    assert call(K=100) == SHAPE
+    assert call(group=64) == UNSUPPORTED
+    assert call(q=FAKE + 2) == ALIGN
+    assert call(K=32768) == WORKSPACE
+    assert call(M=0) == OK and call(N=0) == OK

@@ -160,6 +160,33 @@ def test_fullsize_search_gram(dev, qkv):
             assert torch.equal(a[k], g[k]), k
 
 
+@pytest.mark.parametrize("name", ["down", "gate_up"])
+def test_fullsize_int3_dense_llama2_70b(dev, name):
+    """The 70B-shaped INT3 layers at full size: dense words on sampled rows
+    against the oracle, and the dense-INT3 decode contraction bit-identical to
+    the 4-bit-container one at M = 1 and 16, with a sampled oracle block."""
+    announce("full-size dense INT3", name)
+    spec = synth.layer_spec("llama2_70b_mlp", name)
+    w = synth.make_weight(spec, 0)
+    wd = to_dev_bf16(w, dev)
+    s = np.exp(np.random.default_rng(2).uniform(-0.5, 0.5, spec.K)).astype(np.float32)
+    qw3, sc, ze = awq.quantize_pack3(wd, to_dev_f32(s, dev))
+    qw4, sc4, ze4 = awq.quantize_pack(wd, to_dev_f32(s, dev), 3)
+    assert torch.equal(sc, sc4) and torch.equal(ze, ze4)
+    rows = sample_rows(spec.N, 16, 5)
+    q, z, st = O.quantize(w[rows], s, 3, 128)
+    assert np.array_equal(u32(qw3)[rows], O.pack3(q))
+    for M in (1, 16):
+        a = synth.decode_activations(spec.K, M, seed=M)
+        ad = to_dev_bf16(a, dev)
+        y3 = awq.decode_gemm3(ad, qw3, sc, ze)
+        y4 = awq.decode_gemm(ad, qw4, sc4, ze4, 3)
+        assert torch.equal(y3, y4), M
+        cols = sample_rows(spec.N, 24, M)
+        ref = O.decode_gemm3(a, u32(qw3)[cols], sc.cpu().numpy()[cols], ze.cpu().numpy()[cols], 128)
+        gemm_close(y3.cpu().numpy()[:, cols], ref)
+
+
 # Every other workload's layer shapes (real K, dtype and activation recipe),
 # at 384 tokens and the first 256 output rows, against the oracle's search.
 OTHER_LAYERS = [("llama2_7b_mlp", "gate_up", 4), ("llama2_7b_mlp", "down", 4),

@@ -439,6 +439,46 @@ def test_decode_gemm_workspace_reuse(dev):
             assert np.array_equal(y_shared.view(np.uint32), y_fresh.view(np.uint32)), (rep, i)
 
 
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_quantize_pack3_bit_exact(dev, shape):
+    """Dense INT3 words, steps and zeros, bit for bit, given the oracle's s."""
+    announce("quantize_pack3", ids(shape))
+    x, w = layer(shape)
+    _, a = O.act_stats(x)
+    s_all, _ = O.candidate_scales(a, 20)
+    wd = to_dev_bf16(w, dev)
+    for s in (None, s_all[13]):
+        qw, sc, ze = awq.quantize_pack3(wd, None if s is None else to_dev_f32(s, dev))
+        q, z, st = O.quantize(w, s, 3, 128)
+        _, rs, rz = O.pack(q, z, st)
+        assert np.array_equal(u32(qw), O.pack3(q))
+        assert np.array_equal(sc.cpu().numpy(), rs)
+        assert np.array_equal(ze.cpu().numpy(), rz)
+
+
+INT3_DECODE_SHAPES = [(1, 64, 128), (3, 1000, 1024), (16, 6144, 4096), (16, 40960, 512),
+                      (2, 520, 16512), (64, 4096, 4096), (33, 40, 128), (1, 72, 32768)]
+
+
+@pytest.mark.parametrize("shape", INT3_DECODE_SHAPES, ids=lambda s: f"M{s[0]}_N{s[1]}_K{s[2]}")
+def test_decode_gemm3(dev, shape):
+    """The dense-INT3 contraction: bit-identical to the 4-bit-container one on
+    the same codes, and against the oracle's product from the dense words."""
+    M, N, K = shape
+    announce("decode_gemm3", shape)
+    a = synth.decode_activations(K, M, seed=M + 3)
+    qw4, sc, ze = random_packed(N, K, 3, seed=M + 5)
+    q = O.unpack(qw4)
+    qw3 = O.pack3(q)
+    ad, sd, zd = to_dev_bf16(a, dev), to_dev_f32(sc, dev), torch.from_numpy(ze).to(dev)
+    y3 = awq.decode_gemm3(ad, torch.from_numpy(qw3.view(np.int32)).to(dev), sd, zd)
+    y4 = awq.decode_gemm(ad, torch.from_numpy(qw4.view(np.int32)).to(dev), sd, zd, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(y3, y4)
+    _, fro = gemm_close(y3.cpu().numpy(), O.decode_gemm3(a, qw3, sc, ze, 128))
+    assert fro <= 1e-5
+
+
 def test_decode_gemm_matches_search_operand_when_exact(dev):
     """Power-of-two steps make (q - z) * step exact in bf16: the decode kernel
     and the general W4A16 kernel then compute the same products."""
