@@ -38,6 +38,8 @@ contract the GPU library implements):
                    scales f32 [N][K/group], zeros u8 [N][K/group]
   dense INT3       qweight3[n][3c .. 3c+2] = the 96-bit little-endian value
                    sum_i q[n, 32c+i] << 3i of each run of 32 codes
+  decode tiles     the words of rows 16b..16b+15 and group g as tile b*G+g,
+                   row r's piece for channels 32q.. at byte P*(r + 16q)
   dequantized B    B[n,k] = bf16( f32( f32((q - z) * step) * inv_s[k] ) )
                    (1/s folded into the weight operand; the activation operand
                    is the caller's bf16 X, unchanged)
@@ -61,7 +63,7 @@ innocuous?", 1995).  Products of two fp32 values are exact in fp64.
 Parity unpinned (convention only, no value on the pages can fix them): the
 normalising constant sqrt(max*min), the 1e-4 floor, the nibble order of the
 packed layout, the 4-bit container used for INT3 codes and the bit order of the
-dense INT3 layout.
+dense INT3 layout and the order of the decode tiles.
 """
 
 from __future__ import annotations
@@ -254,6 +256,25 @@ def unpack3(qweight3):
     bits = np.unpackbits(w.view(np.uint8).reshape(N, T // 3, 12), axis=-1, bitorder="little")
     b3 = bits.reshape(N, T // 3, 32, 3).astype(np.int64)
     return (b3[..., 0] | (b3[..., 1] << 1) | (b3[..., 2] << 2)).reshape(N, T // 3 * 32)
+
+
+def decode_tiles(qweight, K: int, dense3: bool = False, group: int = 128) -> np.ndarray:
+    """The packed words rearranged for streaming by 16-row blocks (a layout of
+    this library, for the deployment contraction): rows 16b .. 16b+15 (zero
+    rows past N) and one group g form tile b*G + g; inside it the P bytes of
+    row r covering the group's channels 32q .. 32q+31 sit at byte P*(r + 16q),
+    with P = 16 for 4-bit containers and 12 for dense INT3.  Returns bytes,
+    uint8 [ceil(N/16) * G * 16 * 4P]."""
+    w = np.ascontiguousarray(np.asarray(qweight, dtype="<u4"))
+    N = w.shape[0]
+    G = K // group
+    P = 12 if dense3 else 16
+    rows = w.view(np.uint8).reshape(N, G, 4, P)            # [n][g][q][P bytes]
+    NB = -(-N // 16)
+    padded = np.zeros((NB * 16, G, 4, P), dtype=np.uint8)
+    padded[:N] = rows
+    t = padded.reshape(NB, 16, G, 4, P).transpose(0, 2, 3, 1, 4)   # [b][g][q][r][P]
+    return np.ascontiguousarray(t).reshape(-1)
 
 
 def packed3_bytes(N: int, K: int, group: int) -> int:

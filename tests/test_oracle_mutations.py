@@ -120,11 +120,26 @@ def _mut_pack3_runs_of_16(mp):
     mp.setattr(oracle, "pack3", p3)
 
 
+def _mut_tiles_row_major_inside(mp):
+    """Pieces inside a tile ordered row by row (r*4 + q) instead of lane order."""
+    def tiles(qweight, K, dense3=False, group=128):
+        w = np.ascontiguousarray(np.asarray(qweight, dtype="<u4"))
+        N = w.shape[0]
+        G, P = K // group, (12 if dense3 else 16)
+        rows = w.view(np.uint8).reshape(N, G, 4, P)
+        NB = -(-N // 16)
+        padded = np.zeros((NB * 16, G, 4, P), dtype=np.uint8)
+        padded[:N] = rows
+        return np.ascontiguousarray(padded.reshape(NB, 16, G, 4, P).transpose(0, 2, 1, 3, 4)).reshape(-1)
+    mp.setattr(oracle, "decode_tiles", tiles)
+
+
 MUTATIONS = [_mut_floor_instead_of_rint, _mut_drop_inv_s, _mut_alpha_grid_closed,
              _mut_scale_index_reversed, _mut_zero_added_before_rounding, _mut_loss_sign,
              _mut_no_range_extension, _mut_stats_mean_without_abs, _mut_normaliser_max_only,
              _mut_decode_zero_of_first_group, _mut_decode_rounds_weight_to_bf16, _mut_diff_sign,
-             _mut_diff_off_by_half_ulp, _mut_pack3_code_bits_reversed, _mut_pack3_runs_of_16]
+             _mut_diff_off_by_half_ulp, _mut_pack3_code_bits_reversed, _mut_pack3_runs_of_16,
+             _mut_tiles_row_major_inside]
 
 PINS = [
     P.test_quantizer_worked_group,
@@ -141,6 +156,7 @@ PINS = [
     lambda: P.test_difference_operand_is_exact(4),
     P.test_pack3_worked_words,
     P.test_pack3_big_integer_brute_force,
+    lambda: P.test_decode_tiles_brute_force(False),
 ]
 
 

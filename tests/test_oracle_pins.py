@@ -340,6 +340,30 @@ def test_dense_int3_storage_and_product():
     assert np.array_equal(O.decode_gemm3(a, O.pack3(q), sc, ze, 128), O.decode_gemm(a, qw, sc, ze, 128))
 
 
+@pytest.mark.parametrize("dense3", [False, True])
+def test_decode_tiles_brute_force(dense3):
+    """Every byte of the tile layout, found by walking the definition: tile
+    b*G + g holds rows 16b .. 16b+15 of group g, row r's piece for channels
+    32q .. 32q+31 at byte P*(r + 16q); rows past N are zero."""
+    rng = np.random.default_rng(41)
+    N, K = 37, 384
+    G, P = K // 128, (12 if dense3 else 16)
+    words = 3 * K // 32 if dense3 else K // 8
+    qw = rng.integers(0, 2 ** 32, size=(N, words), dtype=np.uint64).astype(np.uint32)
+    raw = qw.astype("<u4").view(np.uint8).reshape(N, words * 4)
+    tiles = O.decode_tiles(qw, K, dense3)
+    NB = -(-N // 16)
+    assert tiles.size == NB * G * 64 * P
+    for b in range(NB):
+        for g in range(G):
+            for q in range(4):
+                for r in range(16):
+                    n = 16 * b + r
+                    got = tiles[(b * G + g) * 64 * P + P * (r + 16 * q):][:P]
+                    want = raw[n, g * 4 * P + q * P:][:P] if n < N else np.zeros(P, np.uint8)
+                    assert np.array_equal(got, want), (b, g, q, r)
+
+
 def test_storage_about_four_times_smaller():
     """~4x smaller than 16-bit and ~4.x bits per weight (vectordb 'Features',
     robotsatlas 'Computational complexity')."""
