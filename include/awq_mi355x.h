@@ -75,6 +75,12 @@ typedef enum awq_op {
   AWQ_OP_SEARCH_SCALE_GRAM = 6,
 } awq_op;
 
+/* Packed code layouts of the deployment contraction. */
+typedef enum {
+  AWQ_LAYOUT_NIBBLE = 0,      /* awq_quantize_pack: codes in 4-bit fields, [N][K/8] words */
+  AWQ_LAYOUT_INT3_DENSE = 1,  /* awq_quantize_pack3: 32 codes in 3 words, [N][3K/32] words */
+} awq_layout;
+
 /* Version of this ABI (AWQ_ABI_VERSION). */
 int32_t awq_abi_version(void);
 
@@ -273,6 +279,36 @@ awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_
 awq_status awq_w3a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
                                  const uint32_t* qweight3, const float* scales,
                                  const uint8_t* zeros, int32_t group, float* y, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
+ * Decode tiles: the packed words rearranged once, at load time, for the
+ * deployment contraction (robotsatlas "Limitations": the benefit depends on
+ * matched INT4 kernels).  Rows 16b .. 16b+15 of group g (rows past N are
+ * zero) form tile b*G + g; inside it, row r's piece covering the group's
+ * channels 32q .. 32q+31 (P = 16 bytes for AWQ_LAYOUT_NIBBLE, 12 for
+ * AWQ_LAYOUT_INT3_DENSE) sits at byte P*(r + 16q), so one wave's load of a
+ * tile is one contiguous piece in lane order.
+ *   awq_decode_tiles_size: *bytes = ceil(N/16) * 16 * (K/2 or 3K/8).
+ *   awq_decode_tiles: qweight as written by awq_quantize_pack (layout
+ *     NIBBLE, any bits) or awq_quantize_pack3 (INT3_DENSE), 4-byte aligned;
+ *     tiles output of that size, 16-byte aligned.  N == 0 is a no-op.
+ */
+awq_status awq_decode_tiles_size(int64_t N, int64_t K, int32_t layout, int32_t group,
+                                 size_t* bytes);
+awq_status awq_decode_tiles(const uint32_t* qweight, int64_t N, int64_t K, int32_t layout,
+                            int32_t group, uint32_t* tiles, void* stream);
+
+/*
+ * The decode-shaped contraction reading decode tiles: arguments, limits,
+ * workspace and results as awq_w4a16_decode_gemm (layout NIBBLE) or
+ * awq_w3a16_decode_gemm (INT3_DENSE), bit-identical to them for the same
+ * codes.  The tiles must be at most 4 GiB (32-bit offsets); larger gives
+ * AWQ_ERR_SHAPE.
+ */
+awq_status awq_decode_gemm_tiled(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                 const uint32_t* tiles, const float* scales, const uint8_t* zeros,
+                                 int32_t layout, int32_t group, float* y, void* ws,
                                  size_t ws_bytes, void* stream);
 
 /*

@@ -18,7 +18,8 @@ from . import build as _build
 
 __all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "quantize_pack",
            "reference_gemm", "w4a16_gemm", "search_scale", "search_scale_gram", "decode_gemm",
-           "dequant_operand", "diff_operand", "candidate_sse", "quantize_pack3", "decode_gemm3", "workspace_size",
+           "dequant_operand", "diff_operand", "candidate_sse", "quantize_pack3", "decode_gemm3",
+           "decode_tiles", "decode_gemm_tiled", "LAYOUT_NIBBLE", "LAYOUT_INT3_DENSE", "workspace_size",
            "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES",
            "OP_DECODE_GEMM", "OP_CANDIDATE_SSE", "OP_SEARCH_SCALE_GRAM"]
 
@@ -44,6 +45,10 @@ _SIGNATURES = {
                             _c_void_p, _c_void_p], _i32),
     "awq_w3a16_decode_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
                                _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
+    "awq_decode_tiles_size": ([_i64, _i64, _i32, _i32, _c_void_p], _i32),
+    "awq_decode_tiles": ([_c_void_p, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p], _i32),
+    "awq_decode_gemm_tiled": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
+                               _i32, _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
     "awq_diff_operand": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
                           _c_void_p], _i32),
     "awq_candidate_sse": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -317,6 +322,41 @@ def decode_gemm3(a: torch.Tensor, qweight3: torch.Tensor, scales: torch.Tensor,
     _check(lib().awq_w3a16_decode_gemm(_ptr(a), M, N, K, _ptr(qweight3), _ptr(scales), _ptr(zeros),
                                        group, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
                                        _stream(dev)), "awq_w3a16_decode_gemm")
+    return y
+
+
+LAYOUT_NIBBLE, LAYOUT_INT3_DENSE = 0, 1
+
+
+def decode_tiles(qweight: torch.Tensor, K: int, layout: int = LAYOUT_NIBBLE,
+                 group: int = 128) -> torch.Tensor:
+    """The packed words as decode tiles (int32, flat), for decode_gemm_tiled."""
+    N = qweight.shape[0]
+    nbytes = _size_t(0)
+    _check(lib().awq_decode_tiles_size(N, K, layout, group, ctypes.byref(nbytes)),
+           "awq_decode_tiles_size")
+    tiles = torch.empty(nbytes.value // 4, dtype=torch.int32, device=qweight.device)
+    _check(lib().awq_decode_tiles(_ptr(qweight.contiguous()), N, K, layout, group, _ptr(tiles),
+                                  _stream(qweight.device)), "awq_decode_tiles")
+    return tiles
+
+
+def decode_gemm_tiled(a: torch.Tensor, tiles: torch.Tensor, scales: torch.Tensor,
+                      zeros: torch.Tensor, layout: int = LAYOUT_NIBBLE, group: int = 128,
+                      out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_gemm / decode_gemm3 reading decode tiles (fp32 [M][N])."""
+    a = _bf16(a, "a")
+    M, K = a.shape
+    N = scales.shape[0]
+    dev = a.device
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if out is None else _f32(out, "out")
+    need = workspace_size(OP_DECODE_GEMM, M, N, K, 3 if layout == LAYOUT_INT3_DENSE else 4, group)
+    ws = _workspace(need, dev, workspace) if need > 0 else None
+    _check(lib().awq_decode_gemm_tiled(_ptr(a), M, N, K, _ptr(tiles), _ptr(scales), _ptr(zeros),
+                                       layout, group, _ptr(y), _ptr(ws),
+                                       0 if ws is None else ws.numel(), _stream(dev)),
+           "awq_decode_gemm_tiled")
     return y
 
 

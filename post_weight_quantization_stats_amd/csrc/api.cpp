@@ -388,7 +388,8 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
 static awq_status decode_entry(const uint16_t* a, int64_t M, int64_t N, int64_t K,
                                const uint32_t* qweight, const float* scales,
                                const uint8_t* zeros, int32_t bits, int32_t group, float* y,
-                               void* ws, size_t ws_bytes, void* stream, bool int3_dense) {
+                               void* ws, size_t ws_bytes, void* stream, bool int3_dense,
+                               bool tiled = false) {
   try {
     awq_status st = check_quant_params(bits, group);
     if (st != AWQ_OK) return st;
@@ -406,8 +407,10 @@ static awq_status decode_entry(const uint16_t* a, int64_t M, int64_t N, int64_t 
     const awq::DecodePlan plan = awq::decode_plan(M, N, K);
     if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes))
       return fail(AWQ_ERR_WORKSPACE, "decode GEMM needs %zu workspace bytes", plan.ws_bytes);
+    if (tiled && awq::decode_tiles_bytes(N, K, int3_dense) > 0xFFFFFFFFull)
+      return fail(AWQ_ERR_SHAPE, "decode tiles are addressed with 32-bit offsets: at most 4 GiB");
     AWQ_TRY_LAUNCH(awq::launch_decode_gemm(a, M, N, K, qweight, scales, zeros, y, ws,
-                                           (hipStream_t)stream, int3_dense));
+                                           (hipStream_t)stream, int3_dense, tiled));
     return ok();
   } catch (...) {
     return fail(AWQ_ERR_LAUNCH, "internal error");
@@ -428,6 +431,48 @@ awq_status awq_w3a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_
                                  size_t ws_bytes, void* stream) {
   return decode_entry(a, M, N, K, qweight3, scales, zeros, 3, group, y, ws, ws_bytes, stream,
                       true);
+}
+
+awq_status awq_decode_tiles_size(int64_t N, int64_t K, int32_t layout, int32_t group,
+                                 size_t* bytes) {
+  if (bytes == nullptr) return fail(AWQ_ERR_NULL, "bytes is required");
+  if (layout != AWQ_LAYOUT_NIBBLE && layout != AWQ_LAYOUT_INT3_DENSE)
+    return fail(AWQ_ERR_UNSUPPORTED, "unknown layout %d", layout);
+  awq_status st = check_quant_params(layout == AWQ_LAYOUT_INT3_DENSE ? 3 : 4, group);
+  if (st != AWQ_OK) return st;
+  if ((st = check_k(K, group)) != AWQ_OK) return st;
+  if (N < 0 || N > kMaxGemmN) return fail(AWQ_ERR_SHAPE, "N out of range");
+  *bytes = awq::decode_tiles_bytes(N, K, layout == AWQ_LAYOUT_INT3_DENSE);
+  return ok();
+}
+
+awq_status awq_decode_tiles(const uint32_t* qweight, int64_t N, int64_t K, int32_t layout,
+                            int32_t group, uint32_t* tiles, void* stream) {
+  try {
+    size_t bytes = 0;
+    awq_status st = awq_decode_tiles_size(N, K, layout, group, &bytes);
+    if (st != AWQ_OK) return st;
+    if (N == 0) return ok();
+    if (qweight == nullptr || tiles == nullptr) return fail(AWQ_ERR_NULL, "qweight and tiles are required");
+    if (((uintptr_t)qweight & 3u) || ((uintptr_t)tiles & 15u))
+      return fail(AWQ_ERR_ALIGN, "qweight must be 4-byte aligned, tiles 16-byte");
+    AWQ_TRY_LAUNCH(awq::launch_decode_tiles(qweight, N, K, layout == AWQ_LAYOUT_INT3_DENSE, tiles,
+                                            (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_decode_gemm_tiled(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                 const uint32_t* tiles, const float* scales, const uint8_t* zeros,
+                                 int32_t layout, int32_t group, float* y, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (layout != AWQ_LAYOUT_NIBBLE && layout != AWQ_LAYOUT_INT3_DENSE)
+    return fail(AWQ_ERR_UNSUPPORTED, "unknown layout %d", layout);
+  const bool dense = layout == AWQ_LAYOUT_INT3_DENSE;
+  return decode_entry(a, M, N, K, tiles, scales, zeros, dense ? 3 : 4, group, y, ws, ws_bytes,
+                      stream, dense, true);
 }
 
 awq_status awq_candidate_sse(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint16_t* b,

@@ -106,9 +106,16 @@ struct DecodePlan {
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);
 // int3_dense: qweight holds dense INT3 words [N][3K/32] instead of 4-bit
 // containers [N][K/8].
+// tiled: qweight holds decode tiles (launch_decode_tiles) instead of row-major words.
 hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
                               const uint32_t* qweight, const float* scales, const uint8_t* zeros,
-                              float* y, void* ws, hipStream_t stream, bool int3_dense = false);
+                              float* y, void* ws, hipStream_t stream, bool int3_dense = false,
+                              bool tiled = false);
+// Decode tiles: rows 16b .. 16b+15 (zero past N) x group g as tile b*G + g,
+// row r's piece for channels 32q .. 32q+31 at byte P*(r + 16q) (P = 16 or 12).
+size_t decode_tiles_bytes(int64_t N, int64_t K, bool int3_dense);
+hipError_t launch_decode_tiles(const uint32_t* qweight, int64_t N, int64_t K, bool int3_dense,
+                               uint32_t* tiles, hipStream_t stream);
 
 // losses[i] = (sum_t partials[i*T + t]) / divisor, fixed summation order.
 hipError_t launch_loss_reduce(const double* partials, int64_t T, int n_grid, double divisor,

@@ -4,8 +4,9 @@ A thin torch.nn.Module: it holds the packed codes, steps and zeros as
 buffers and routes each call to a HIP contraction by token count, so
 nothing of the product runs in PyTorch.
 
-  * M <= 64 tokens: the decode contraction (weights streamed once from HBM;
-    dequantized weight (q - z) * step exactly).
+  * M <= 64 tokens: the decode contraction on decode tiles (made once per
+    device on first use; weights streamed once from HBM; dequantized weight
+    (q - z) * step exactly).
   * M > 64: the general W4A16 contraction (dequantized weight rounded to
     bf16 in LDS, the search's operand contract).
 
@@ -21,7 +22,8 @@ from __future__ import annotations
 
 import torch
 
-from . import OP_DECODE_GEMM, decode_gemm, w4a16_gemm, workspace_size
+from . import (LAYOUT_NIBBLE, OP_DECODE_GEMM, decode_gemm_tiled, decode_tiles, w4a16_gemm,
+               workspace_size)
 
 DECODE_MAX_M = 64
 
@@ -43,6 +45,7 @@ class W4A16Linear(torch.nn.Module):
         self.register_buffer("scales", scales.to(torch.float32).contiguous())
         self.register_buffer("zeros", zeros.to(torch.uint8).contiguous())
         self._ws = None
+        self._tiles = None
 
     @classmethod
     def from_search(cls, result: dict, bits: int = 4, group: int = 128) -> "W4A16Linear":
@@ -65,8 +68,10 @@ class W4A16Linear(torch.nn.Module):
                 if self._ws is None or self._ws.numel() < need or self._ws.device != x.device:
                     self._ws = torch.empty(need, dtype=torch.uint8, device=x.device)
                 ws = self._ws
-            y = decode_gemm(x2, self.qweight, self.scales, self.zeros, self.bits, self.group,
-                            workspace=ws)
+            if self._tiles is None or self._tiles.device != self.qweight.device:
+                self._tiles = decode_tiles(self.qweight, self.in_features, LAYOUT_NIBBLE, self.group)
+            y = decode_gemm_tiled(x2, self._tiles, self.scales, self.zeros, LAYOUT_NIBBLE,
+                                  self.group, workspace=ws)
         else:
             y = w4a16_gemm(x2, self.qweight, self.scales, self.zeros, self.bits, self.group)
         return y.reshape(*lead, self.out_features)

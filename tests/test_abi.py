@@ -282,3 +282,25 @@ def test_dense_int3_entry_errors():
     assert call(q=FAKE + 2) == ALIGN
     assert call(K=32768) == WORKSPACE
     assert call(M=0) == OK and call(N=0) == OK
+
+
+def test_decode_tiles_entry_errors():
+    lib = awq.lib()
+    out = ctypes.c_size_t(0)
+    assert lib.awq_decode_tiles_size(40, 384, 0, 128, None) == NULL
+    assert lib.awq_decode_tiles_size(40, 384, 2, 128, ctypes.byref(out)) == UNSUPPORTED
+    assert lib.awq_decode_tiles_size(40, 100, 0, 128, ctypes.byref(out)) == SHAPE
+    assert lib.awq_decode_tiles_size(40, 384, 0, 128, ctypes.byref(out)) == OK
+    assert out.value == 48 * 384 // 2
+    assert lib.awq_decode_tiles_size(40, 384, 1, 128, ctypes.byref(out)) == OK
+    assert out.value == 48 * 3 * 384 // 8
+    assert lib.awq_decode_tiles(None, 40, 384, 0, 128, FAKE, None) == NULL
+    assert lib.awq_decode_tiles(FAKE, 40, 384, 0, 128, FAKE + 4, None) == ALIGN
+    assert lib.awq_decode_tiles(FAKE, 0, 384, 0, 128, None, None) == OK
+    f = lib.awq_decode_gemm_tiled
+    assert f(FAKE, 4, 128, 4096, FAKE, FAKE, FAKE, 5, 128, FAKE, None, 0, None) == UNSUPPORTED
+    assert f(FAKE, 65, 128, 4096, FAKE, FAKE, FAKE, 0, 128, FAKE, None, 0, None) == SHAPE
+    assert f(None, 4, 128, 4096, FAKE, FAKE, FAKE, 0, 128, FAKE, None, 0, None) == NULL
+    assert f(FAKE, 4, 128, 4096, FAKE + 4, FAKE, FAKE, 0, 128, FAKE, None, 0, None) == ALIGN
+    # tiles beyond 4 GiB cannot be addressed
+    assert f(FAKE, 4, 1 << 22, 1 << 13, FAKE, FAKE, FAKE, 0, 128, FAKE, FAKE, 1 << 40, None) == SHAPE

@@ -479,6 +479,40 @@ def test_decode_gemm3(dev, shape):
     assert fro <= 1e-5
 
 
+@pytest.mark.parametrize("dense3", [False, True], ids=["nibble", "int3dense"])
+def test_decode_tiles_bit_exact(dev, dense3):
+    """Decode tiles against the oracle's layout (ragged N, several groups)."""
+    announce("decode_tiles", dense3)
+    for N, K in ((37, 384), (520, 2048), (16, 128)):
+        qw4, _, _ = random_packed(N, K, 3 if dense3 else 4, seed=N)
+        qw = O.pack3(O.unpack(qw4)) if dense3 else qw4
+        t = awq.decode_tiles(torch.from_numpy(qw.view(np.int32)).to(dev), K,
+                             awq.LAYOUT_INT3_DENSE if dense3 else awq.LAYOUT_NIBBLE)
+        got = t.cpu().numpy().view(np.uint8)
+        assert np.array_equal(got, O.decode_tiles(qw, K, dense3)), (N, K)
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda s: f"M{s[0]}_N{s[1]}_K{s[2]}")
+def test_decode_gemm_tiled_matches_row_major(dev, shape):
+    """The tiled contraction is bit-identical to the row-major one, for the
+    4-bit containers and for dense INT3."""
+    M, N, K = shape
+    announce("decode_gemm_tiled", shape)
+    a = synth.decode_activations(K, M, seed=M + 9)
+    qw4, sc, ze = random_packed(N, K, 3, seed=M + 11)
+    qw3 = O.pack3(O.unpack(qw4))
+    ad, sd, zd = to_dev_bf16(a, dev), to_dev_f32(sc, dev), torch.from_numpy(ze).to(dev)
+    q4d = torch.from_numpy(qw4.view(np.int32)).to(dev)
+    q3d = torch.from_numpy(qw3.view(np.int32)).to(dev)
+    y4 = awq.decode_gemm(ad, q4d, sd, zd, 3)
+    y4t = awq.decode_gemm_tiled(ad, awq.decode_tiles(q4d, K), sd, zd, awq.LAYOUT_NIBBLE)
+    y3t = awq.decode_gemm_tiled(ad, awq.decode_tiles(q3d, K, awq.LAYOUT_INT3_DENSE), sd, zd,
+                                awq.LAYOUT_INT3_DENSE)
+    torch.cuda.synchronize()
+    assert torch.equal(y4t, y4)
+    assert torch.equal(y3t, y4)
+
+
 def test_decode_gemm_matches_search_operand_when_exact(dev):
     """Power-of-two steps make (q - z) * step exact in bf16: the decode kernel
     and the general W4A16 kernel then compute the same products."""
