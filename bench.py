@@ -265,13 +265,29 @@ def event_time_ms(fn, reps: int, stream) -> float:
     return start.elapsed_time(end) / reps
 
 
+def _graph_time_ms(fn, reps: int, stream) -> float:
+    """Average time of fn(i), i = 0..reps-1, captured in one HIP graph and
+    replayed (host launch overhead excluded)."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    ms = event_time_ms(g.replay, 5, stream) / reps
+    del g
+    return ms
+
+
 def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
     """Decode-shaped W4A16 contraction on the Llama-3-8B block's layers
-    (M = 1, 16 and 64 tokens, random packed INT4 weights).  Launches cycle through
-    enough copies of the packed weights (>= 768 MiB in all) that each one
-    streams from HBM rather than the 256 MiB last-level cache.  Each figure
-    is the average over `reps` launches captured in one HIP graph and
-    replayed, so host launch overhead is not in it."""
+    (M = 1, 16 and 64 tokens, random packed INT4 weights), on decode tiles
+    (the deployment path) and on the row-major packed words.  Launches cycle
+    through enough copies of the packed weights (>= 768 MiB in all) that each
+    one streams from HBM rather than the 256 MiB last-level cache."""
     import torch
 
     import synth
@@ -288,35 +304,83 @@ def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
                                generator=gen)
             sc = torch.rand((N, K // 128), device=dev, generator=gen) * 0.003 + 0.001
             ze = torch.randint(0, 16, (N, K // 128), dtype=torch.uint8, device=dev, generator=gen)
-            packs.append((qw, sc, ze))
+            packs.append((qw, awq.decode_tiles(qw, K), sc, ze))
         for M in (1, 16, 64):
             a = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
             need = awq.workspace_size(awq.OP_DECODE_GEMM, M, N, K)
             ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
-            def fn(i):
-                qw, sc, ze = packs[i % copies]
+            def tiled(i):
+                _, tl, sc, ze = packs[i % copies]
+                awq.decode_gemm_tiled(a, tl, sc, ze, awq.LAYOUT_NIBBLE, out=y, workspace=ws)
+
+            def row_major(i):
+                qw, _, sc, ze = packs[i % copies]
                 awq.decode_gemm(a, qw, sc, ze, 4, out=y, workspace=ws)
-            fn(0)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(reps):
-                    fn(i)
-            g.replay()
-            torch.cuda.synchronize()
-            ms = event_time_ms(g.replay, 5, stream) / reps
+            ms = _graph_time_ms(tiled, reps, stream)
+            ms_rm = _graph_time_ms(row_major, reps, stream)
             nbytes = wbytes + 2.0 * M * K + 4.0 * M * N
             gbs = nbytes / (ms * 1e-3) / 1e9
             out[f"{name}_M{M}"] = {"N": N, "K": K, "us": ms * 1e3, "gbs": gbs,
                                    "frac_hbm_peak": gbs / PEAK_HBM_GBS, "bytes": nbytes,
-                                   "weight_copies": copies}
-            log(f"decode {name} M={M} N={N} K={K}: {ms * 1e3:.2f} us = {gbs:.0f} GB/s "
-                f"({copies} weight copies)")
-            del g
+                                   "row_major_us": ms_rm * 1e3, "weight_copies": copies}
+            log(f"decode {name} M={M} N={N} K={K}: tiles {ms * 1e3:.2f} us = {gbs:.0f} GB/s; "
+                f"row-major {ms_rm * 1e3:.2f} us ({copies} weight copies)")
         del packs
         torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode_int3(awq, dev, stream, reps: int = 64) -> dict:
+    """Decode-shaped contraction on the Llama-2-70B MLP's INT3 layers, dense
+    INT3 words (3 bits per weight) beside the same codes in 4-bit containers,
+    both as decode tiles, M = 1 and 16, weights rotated beyond the last-level
+    cache."""
+    import torch
+
+    import synth
+    out = {}
+    for name in ("down", "gate_up"):
+        spec = synth.layer_spec("llama2_70b_mlp", name)
+        N, K = spec.N, spec.K
+        gen = torch.Generator(device=dev).manual_seed(11)
+        sz_bytes = 5.0 * N * K / 128
+        for layout in ("dense", "container"):
+            wbytes = (3.0 * N * K / 8 if layout == "dense" else N * K / 2) + sz_bytes
+            copies = int(min(16, max(2, -(-(768 << 20) // int(wbytes)))))
+            packs = []
+            for _ in range(copies):
+                words = 3 * K // 32 if layout == "dense" else K // 8
+                qw = torch.randint(-2 ** 31, 2 ** 31 - 1, (N, words), dtype=torch.int32,
+                                   device=dev, generator=gen)
+                if layout == "container":
+                    qw &= 0x77777777          # 3-bit codes in 4-bit fields
+                sc = torch.rand((N, K // 128), device=dev, generator=gen) * 0.003 + 0.001
+                ze = torch.randint(0, 8, (N, K // 128), dtype=torch.uint8, device=dev,
+                                   generator=gen)
+                lay = awq.LAYOUT_INT3_DENSE if layout == "dense" else awq.LAYOUT_NIBBLE
+                packs.append((awq.decode_tiles(qw, K, lay), sc, ze))
+                del qw
+            for M in (1, 16):
+                a = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
+                y = torch.empty((M, N), dtype=torch.float32, device=dev)
+                need = awq.workspace_size(awq.OP_DECODE_GEMM, M, N, K, 3)
+                ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+                def fn(i):
+                    tl, sc, ze = packs[i % copies]
+                    awq.decode_gemm_tiled(a, tl, sc, ze, lay, out=y, workspace=ws)
+                ms = _graph_time_ms(fn, reps, stream)
+                nbytes = wbytes + 2.0 * M * K + 4.0 * M * N
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                out[f"{name}_{layout}_M{M}"] = {"N": N, "K": K, "us": ms * 1e3, "gbs": gbs,
+                                                "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+                                                "bytes": nbytes, "weight_copies": copies}
+                log(f"decode int3 {layout} (tiles) {name} M={M} N={N} K={K}: {ms * 1e3:.2f} us = "
+                    f"{gbs:.0f} GB/s")
+            del packs
+            torch.cuda.empty_cache()
     return out
 
 
@@ -428,7 +492,9 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     if args.decode_only:
-        print(json.dumps(bench_decode(awq, dev, torch.cuda.current_stream(dev))), flush=True)
+        st = torch.cuda.current_stream(dev)
+        print(json.dumps({"int4": bench_decode(awq, dev, st), "int3": bench_decode_int3(awq, dev, st)}),
+              flush=True)
         return 0
     spec = synth.layer_spec(args.workload, args.layer)
     bits = spec.bits[-1]
@@ -569,6 +635,7 @@ def main() -> int:
     }
     if not args.no_decode:
         result["kernels"]["decode_gemm_llama3_8b"] = bench_decode(awq, dev, stream)
+        result["kernels"]["decode_gemm_int3_llama2_70b"] = bench_decode_int3(awq, dev, stream)
     del ws, gemm_ws, yref, b_mid, d_mid
     torch.cuda.empty_cache()
     if not args.no_gram:
