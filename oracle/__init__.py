@@ -4,4 +4,5 @@ from .awq_oracle import (SCALE_FLOOR, act_stats, alpha_grid, bf16_bits_to_f64,
                          bf16_rne_bits, bf16_round, candidate_scales, decode_gemm, decode_gemm3, decode_tiles, deploy_gemm,
                          dequant_operand, diff_operand, f32, first_argmin, gemm, gram,
                          output_mse, output_mse_gram, pack, pack3, packed3_bytes, packed_bytes, quantize,
-                         search, unpack, unpack3)
+                         search, unpack, unpack3, rmsnorm, silu_mul, divide_rows,
+                         residual_add, mlp_block)

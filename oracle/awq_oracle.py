@@ -50,6 +50,11 @@ contract the GPU library implements):
   loss             MSE over all M*N outputs of X.B^T against X.W^T, fp64
   selection        first index of the minimum loss (NaN never wins; all-NaN
                    gives -1)
+  block pipeline   a Llama-shaped feed-forward sublayer searched in order:
+                   u = bf16(f32(f32(x * r) * gamma)), r = f32(1/sqrt(mean x^2 + eps));
+                   H = bf16(f32(silu(g) * v)) in fp64; 1/s folds into gamma
+                   (gate_up) and into the up rows' steps (down) as f32(v / s);
+                   the residual x + y rounds to f32, then to bf16
   decode product   for the deployment contraction with few tokens, the
                    dequantized weight is the exact (q - z) * step (no bf16
                    rounding): Y = A . ((q - z) * step)^T
@@ -443,3 +448,79 @@ def _decode_product(a_bits, q, scales, zeros, group: int) -> np.ndarray:
     step = np.repeat(np.asarray(scales, np.float32).astype(np.float64), group, axis=1)
     wd = (q - z) * step
     return bf16_bits_to_f64(a_bits) @ wd.T
+
+
+# --------------------------------------------------------------------------
+# The synthetic block pipeline around the search: a Llama-shaped feed-forward
+# sublayer, searched layer after layer with each scale folded into the op
+# before it ([P3] "How it works": the activation is divided by the same
+# per-channel factor that multiplies the weight, which a deployment folds
+# into the preceding operation; "Computational complexity": one search per
+# layer, over the layers in order).  Every "bf16(...)" and "f32(...)" is a
+# rounding point of the contract.
+# --------------------------------------------------------------------------
+
+def rmsnorm(x_bits, gamma32, eps: float):
+    """u[m,k] = bf16(f32(f32(x[m,k] * r_m) * gamma[k])) with
+    r_m = f32(1 / sqrt(sum_k x[m,k]^2 / K + eps)) evaluated in fp64.
+    Returns (u bf16 bit patterns, r32)."""
+    X = bf16_bits_to_f64(x_bits)
+    K = X.shape[1]
+    r32 = f32(1.0 / np.sqrt((X * X).sum(axis=1) / K + eps))
+    u = f32(f32(X * r32[:, None]) * np.asarray(gamma32, np.float64)[None, :])
+    return bf16_rne_bits(u), r32
+
+
+def silu_mul(y32, F: int):
+    """H = bf16(f32(silu(g) * v)) for y = [g | v] ([M][2F] fp32), with
+    silu(g) = g / (1 + exp(-g)) and the product in fp64."""
+    Y = np.asarray(y32, np.float64)
+    g, v = Y[:, :F], Y[:, F:2 * F]
+    with np.errstate(over="ignore"):
+        h = g / (1.0 + np.exp(-g)) * v
+    return bf16_rne_bits(f32(h))
+
+
+def divide_rows(v32, s32):
+    """out[r][c] = f32(v[r][c] / s[r]): 1/s folded into a gain (C = 1) or into
+    the per-group steps of a quantized layer's output rows."""
+    v = np.asarray(v32, np.float64)
+    s = np.asarray(s32, np.float64)
+    return f32(v / s.reshape((-1,) + (1,) * (v.ndim - 1)))
+
+
+def residual_add(x_bits, y32):
+    """x_next = bf16(f32(x + y))."""
+    return bf16_rne_bits(f32(bf16_bits_to_f64(x_bits) + np.asarray(y32, np.float64)))
+
+
+def mlp_block(x_bits, gamma32, wgu_bits, wdown_bits, eps: float = 1e-5, bits: int = 4,
+              group: int = 128, n_grid: int = 20, upstream=None):
+    """One feed-forward sublayer through the search, in order:
+
+      u = rmsnorm(x, gamma);  search gate_up on u -> s1, Q_gu;  gamma' = gamma / s1
+      [g | v] = rmsnorm(x, gamma') . dequant(Q_gu)^T (the deployed product)
+      H = silu_mul(g, v);  search down on H -> s2, Q_down
+      up rows' steps /= s2;  H' = silu_mul(g, v / s2 as deployed)
+      x_next = residual_add(x, H' . dequant(Q_down)^T)
+
+    `upstream` may supply the GPU's own intermediates (keys "u", "y_gu", "h",
+    "h2", "y_down") so each step can be checked on identical inputs; the
+    returned dict holds every intermediate the oracle computed."""
+    up = upstream or {}
+    F = np.asarray(wgu_bits).shape[0] // 2
+    u, _ = rmsnorm(x_bits, gamma32, eps)
+    r1 = search(up.get("u", u), wgu_bits, bits, group, n_grid)
+    gamma_f = divide_rows(gamma32, r1["best_s"])
+    u_f, _ = rmsnorm(x_bits, gamma_f, eps)
+    y_gu = deploy_gemm(up.get("u_f", u_f), r1["qweight"], r1["scales"], r1["zeros"], group)
+    h = silu_mul(up.get("y_gu", y_gu), F)
+    r2 = search(up.get("h", h), wdown_bits, bits, group, n_grid)
+    scales_f = np.asarray(r1["scales"], np.float32).copy()
+    scales_f[F:] = divide_rows(scales_f[F:], r2["best_s"])
+    y_gu2 = deploy_gemm(up.get("u_f", u_f), r1["qweight"], scales_f, r1["zeros"], group)
+    h2 = silu_mul(up.get("y_gu2", y_gu2), F)
+    y_down = deploy_gemm(up.get("h2", h2), r2["qweight"], r2["scales"], r2["zeros"], group)
+    x_next = residual_add(x_bits, up.get("y_down", y_down))
+    return dict(u=u, gate_up=r1, gamma_folded=gamma_f, u_f=u_f, y_gu=y_gu, h=h, down=r2,
+                scales_gu_folded=scales_f, y_gu2=y_gu2, h2=h2, y_down=y_down, x_next=x_next)

@@ -134,12 +134,37 @@ def _mut_tiles_row_major_inside(mp):
     mp.setattr(oracle, "decode_tiles", tiles)
 
 
+def _mut_rmsnorm_without_mean(mp):
+    def rms(x_bits, gamma32, eps):
+        X = OA.bf16_bits_to_f64(x_bits)
+        r32 = OA.f32(1.0 / np.sqrt((X * X).sum(axis=1) + eps))       # sum, not mean
+        u = OA.f32(OA.f32(X * r32[:, None]) * np.asarray(gamma32, np.float64)[None, :])
+        return OA.bf16_rne_bits(u), r32
+    mp.setattr(oracle, "rmsnorm", rms)
+
+
+def _mut_silu_is_sigmoid(mp):
+    def sm(y32, F):
+        Y = np.asarray(y32, np.float64)
+        with np.errstate(over="ignore"):
+            h = 1.0 / (1.0 + np.exp(-Y[:, :F])) * Y[:, F:2 * F]
+        return OA.bf16_rne_bits(OA.f32(h))
+    mp.setattr(oracle, "silu_mul", sm)
+
+
+def _mut_fold_multiplies(mp):
+    mp.setattr(oracle, "divide_rows",
+               lambda v, s: OA.f32(np.asarray(v, np.float64) *
+                                   np.asarray(s, np.float64).reshape((-1,) + (1,) * (np.ndim(v) - 1))))
+
+
 MUTATIONS = [_mut_floor_instead_of_rint, _mut_drop_inv_s, _mut_alpha_grid_closed,
              _mut_scale_index_reversed, _mut_zero_added_before_rounding, _mut_loss_sign,
              _mut_no_range_extension, _mut_stats_mean_without_abs, _mut_normaliser_max_only,
              _mut_decode_zero_of_first_group, _mut_decode_rounds_weight_to_bf16, _mut_diff_sign,
              _mut_diff_off_by_half_ulp, _mut_pack3_code_bits_reversed, _mut_pack3_runs_of_16,
-             _mut_tiles_row_major_inside]
+             _mut_tiles_row_major_inside, _mut_rmsnorm_without_mean, _mut_silu_is_sigmoid,
+             _mut_fold_multiplies]
 
 PINS = [
     P.test_quantizer_worked_group,
@@ -157,6 +182,9 @@ PINS = [
     P.test_pack3_worked_words,
     P.test_pack3_big_integer_brute_force,
     lambda: P.test_decode_tiles_brute_force(False),
+    P.test_rmsnorm_closed_form_and_scaling,
+    P.test_silu_mul_against_torch_and_identities,
+    P.test_divide_rows_and_residual_against_library,
 ]
 
 

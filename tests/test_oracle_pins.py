@@ -603,3 +603,99 @@ def test_decode_gemm_equals_deploy_when_dequant_is_bf16_exact():
     sc = np.exp2(rng.integers(-12, 4, size=(N, K // 128))).astype(np.float32)
     qw = O.pack(q, ze, sc)[0]
     assert np.array_equal(O.decode_gemm(x, qw, sc, ze, 128), O.deploy_gemm(x, qw, sc, ze, 128))
+
+
+# ------------------------------------------------- the synthetic block pipeline
+
+def test_rmsnorm_closed_form_and_scaling():
+    """A constant row c = +-2^p with eps = 0 normalises to exactly +-gamma;
+    with eps = 0 scaling the row by 2^p changes nothing; the normalised
+    row's mean square is ms / (ms + eps)."""
+    gamma = np.array([0.75, 1.25, 1.0, 1.5] * 32, np.float32)
+    for c in (4.0, -0.5, 2.0 ** -6):
+        x = synth.to_bf16_bits(np.full((1, 128), c, np.float32))
+        u, r = O.rmsnorm(x, gamma, 0.0)
+        assert r[0] == 1.0 / abs(c)
+        assert np.array_equal(O.bf16_bits_to_f64(u)[0], np.sign(c) * O.bf16_round(gamma))
+    x, _ = synth.random_layer(9, 256, 8, seed=23, n_outlier=3)
+    u0, _ = O.rmsnorm(x, gamma[:1].repeat(256), 0.0)
+    x8 = synth.to_bf16_bits((O.bf16_bits_to_f64(x) * 8).astype(np.float32))
+    u8, _ = O.rmsnorm(x8, gamma[:1].repeat(256), 0.0)
+    assert np.array_equal(u0, u8)
+    X = O.bf16_bits_to_f64(x)
+    ms = (X * X).mean(axis=1)
+    _, r = O.rmsnorm(x, np.ones(256, np.float32), 1e-2)
+    np.testing.assert_allclose(ms * r.astype(np.float64) ** 2, ms / (ms + 1e-2), rtol=2e-7)
+
+
+def test_silu_mul_against_torch_and_identities():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(29)
+    F = 64
+    y = (rng.standard_normal((5, 2 * F)) * 4).astype(np.float32)
+    y[0, :4] = [0.0, 60.0, -60.0, -800.0]
+    h = O.silu_mul(y, F)
+    ref = torch.nn.functional.silu(torch.from_numpy(y[:, :F]).double()) * torch.from_numpy(y[:, F:]).double()
+    assert np.array_equal(h, O.bf16_rne_bits(ref.float().numpy()))
+    H = O.bf16_bits_to_f64(h)
+    assert H[0, 0] == 0.0 and H[0, 3] == 0.0
+    assert H[0, 1] == O.bf16_round(O.f32(60.0 * np.float64(y[0, F + 1])))
+
+
+def test_divide_rows_and_residual_against_library():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(31)
+    v = rng.uniform(1e-4, 1e-2, (12, 5)).astype(np.float32)
+    s = rng.uniform(0.2, 5.0, 12).astype(np.float32)
+    assert np.array_equal(O.divide_rows(v, s), v / s[:, None])
+    assert np.array_equal(O.divide_rows(v[:, 0], s), v[:, 0] / s)
+    x, _ = synth.random_layer(4, 128, 8, seed=31)
+    y = rng.standard_normal((4, 128)).astype(np.float32)
+    xt = torch.from_numpy(O.bf16_bits_to_f64(x).astype(np.float32))
+    ref = (xt + torch.from_numpy(y)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.residual_add(x, y), ref)
+
+
+def test_folds_move_the_scale_into_the_preceding_op():
+    """The method's premise for the folds: dividing the preceding op's output
+    by s and multiplying the weight by s leaves the product; after the
+    roundings, rmsnorm with gamma / s times s is rmsnorm with gamma to within
+    two bf16 steps, and silu(g) * (v / s) is silu(g) * v / s."""
+    x, _ = synth.random_layer(16, 256, 8, seed=37, n_outlier=4)
+    rng = np.random.default_rng(37)
+    gamma = rng.uniform(0.5, 1.5, 256).astype(np.float32)
+    s = np.exp(rng.uniform(-1, 1, 256)).astype(np.float32)
+    u, _ = O.rmsnorm(x, gamma, 1e-5)
+    uf, _ = O.rmsnorm(x, O.divide_rows(gamma, s), 1e-5)
+    U, UF = O.bf16_bits_to_f64(u), O.bf16_bits_to_f64(uf) * s[None, :]
+    assert np.all(np.abs(UF - U) <= 2 * 2.0 ** -8 * np.abs(U) + 1e-30)
+    F = 256
+    y = (rng.standard_normal((16, 2 * F)) * 3).astype(np.float32)
+    yf = y.copy()
+    yf[:, F:] = (y[:, F:].astype(np.float64) / s[None, :]).astype(np.float32)
+    H = O.bf16_bits_to_f64(O.silu_mul(y, F))
+    HF = O.bf16_bits_to_f64(O.silu_mul(yf, F)) * s[None, :]
+    assert np.all(np.abs(HF - H) <= 3 * 2.0 ** -8 * np.abs(H) + 1e-30)
+
+
+def test_mlp_block_steps_and_fold_of_the_up_rows():
+    """One block: the searches are the plain search on the block's own
+    activations, gamma and the up rows' steps carry 1/s, and the deployed
+    up output equals the undeployed one divided by s2 (to the roundings)."""
+    rng = np.random.default_rng(43)
+    d, F = 256, 384
+    x, _ = synth.random_layer(48, d, 8, seed=43, n_outlier=3)
+    gamma = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    wgu = synth.to_bf16_bits((rng.standard_normal((2 * F, d)) * 0.02).astype(np.float32))
+    wd = synth.to_bf16_bits((rng.standard_normal((d, F)) * 0.02).astype(np.float32))
+    r = O.mlp_block(x, gamma, wgu, wd, n_grid=6)
+    ref1 = O.search(r["u"], wgu, 4, 128, 6)
+    assert np.array_equal(r["gate_up"]["losses"], ref1["losses"])
+    assert np.array_equal(r["gamma_folded"], O.divide_rows(gamma, ref1["best_s"]))
+    ref2 = O.search(r["h"], wd, 4, 128, 6)
+    assert np.array_equal(r["down"]["losses"], ref2["losses"])
+    s2 = ref2["best_s"].astype(np.float64)
+    assert np.array_equal(r["scales_gu_folded"][:F], r["gate_up"]["scales"][:F])
+    v1, v2 = r["y_gu"][:, F:], r["y_gu2"][:, F:]
+    assert np.abs(v2 * s2[None, :] - v1).max() <= 2e-2 * np.abs(v1).max()
+    assert r["x_next"].shape == x.shape and r["x_next"].dtype == np.uint16
