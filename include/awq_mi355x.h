@@ -358,6 +358,36 @@ awq_status awq_search_scale_gram(const uint16_t* x, int64_t M, int64_t K, const 
                                  uint32_t* qweight, float* scales, uint8_t* zeros, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/*
+ * Ops of the synthetic feed-forward block around the search: a Llama-shaped
+ * sublayer x -> x + down(silu(gate(u)) * up(u)), u = RMSNorm(x), searched
+ * layer after layer with each 1/s folded into the op before the layer
+ * (robotsatlas "How it works": the activation is divided by the same
+ * per-channel factor that multiplies the weight; a deployment folds it into
+ * the preceding operation).  Streams on `stream`; no host synchronisation.
+ *
+ * awq_rmsnorm: u[m][k] = bf16(f32(f32(x[m][k] * r_m) * gamma[k])),
+ *   r_m = f32(1 / sqrt(sum_k x[m][k]^2 / K + eps)) in fp64 (sum in a fixed
+ *   order).  x, u bf16 [M][K] (K a multiple of 8), gamma f32 [K], r f32 [M]
+ *   output or NULL; eps >= 0.
+ * awq_silu_mul: h[m][f] = bf16(f32(silu(g) * v)) with g = y[m][f],
+ *   v = y[m][F + f], silu(g) = g / (1 + exp(-g)), in fp64.  y f32 [M][2F]
+ *   (the fused gate/up output), h bf16 [M][F], F a multiple of 4.
+ * awq_divide_rows: out[r][c] = f32(v[r][c] / s[r]) (IEEE division): 1/s
+ *   folded into a gain (C = 1) or into the steps of a quantized layer's
+ *   output rows (v = its scales [R][K/group]).  out may equal v.
+ * awq_residual_add: out = bf16(f32(x + y)), x bf16 [M][K], y f32 [M][K],
+ *   out bf16 [M][K], K a multiple of 8.
+ * M == 0 (or F, C == 0) is a no-op.
+ */
+awq_status awq_rmsnorm(const uint16_t* x, int64_t M, int64_t K, const float* gamma, double eps,
+                       uint16_t* u, float* r, void* stream);
+awq_status awq_silu_mul(const float* y, int64_t M, int64_t F, uint16_t* h, void* stream);
+awq_status awq_divide_rows(const float* v, int64_t R, int64_t C, const float* s, float* out,
+                           void* stream);
+awq_status awq_residual_add(const uint16_t* x, const float* y, int64_t M, int64_t K,
+                            uint16_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,8 @@ from . import build as _build
 __all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "quantize_pack",
            "reference_gemm", "w4a16_gemm", "search_scale", "search_scale_gram", "decode_gemm",
            "dequant_operand", "diff_operand", "candidate_sse", "quantize_pack3", "decode_gemm3",
-           "decode_tiles", "decode_gemm_tiled", "LAYOUT_NIBBLE", "LAYOUT_INT3_DENSE", "workspace_size",
+           "decode_tiles", "decode_gemm_tiled", "LAYOUT_NIBBLE", "LAYOUT_INT3_DENSE",
+           "rmsnorm", "silu_mul", "divide_rows", "residual_add", "workspace_size",
            "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES",
            "OP_DECODE_GEMM", "OP_CANDIDATE_SSE", "OP_SEARCH_SCALE_GRAM"]
 
@@ -49,6 +50,11 @@ _SIGNATURES = {
     "awq_decode_tiles": ([_c_void_p, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p], _i32),
     "awq_decode_gemm_tiled": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
                                _i32, _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
+    "awq_rmsnorm": ([_c_void_p, _i64, _i64, _c_void_p, ctypes.c_double, _c_void_p, _c_void_p,
+                     _c_void_p], _i32),
+    "awq_silu_mul": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p], _i32),
+    "awq_divide_rows": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p], _i32),
+    "awq_residual_add": ([_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p], _i32),
     "awq_diff_operand": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
                           _c_void_p], _i32),
     "awq_candidate_sse": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -325,6 +331,47 @@ def decode_gemm3(a: torch.Tensor, qweight3: torch.Tensor, scales: torch.Tensor,
     return y
 
 
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, return_r: bool = False):
+    """u = bf16(f32(f32(x * r) * gamma)), r = f32(1/sqrt(mean x^2 + eps)) per token."""
+    x, gamma = _bf16(x, "x"), _f32(gamma, "gamma")
+    M, K = x.shape
+    u = torch.empty_like(x)
+    r = torch.empty(M, dtype=torch.float32, device=x.device) if return_r else None
+    _check(lib().awq_rmsnorm(_ptr(x), M, K, _ptr(gamma), float(eps), _ptr(u), _ptr(r),
+                             _stream(x.device)), "awq_rmsnorm")
+    return (u, r) if return_r else u
+
+
+def silu_mul(y: torch.Tensor) -> torch.Tensor:
+    """H = bf16(f32(silu(g) * v)) for y = [g | v] fp32 [M][2F]."""
+    y = _f32(y, "y")
+    M, F2 = y.shape
+    h = torch.empty((M, F2 // 2), dtype=torch.bfloat16, device=y.device)
+    _check(lib().awq_silu_mul(_ptr(y), M, F2 // 2, _ptr(h), _stream(y.device)), "awq_silu_mul")
+    return h
+
+
+def divide_rows(v: torch.Tensor, s: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """out[r][...] = f32(v[r][...] / s[r])."""
+    v, s = _f32(v, "v"), _f32(s, "s")
+    R = v.shape[0]
+    C = v.numel() // max(R, 1)
+    out = torch.empty_like(v) if out is None else _f32(out, "out")
+    _check(lib().awq_divide_rows(_ptr(v), R, C, _ptr(s), _ptr(out), _stream(v.device)),
+           "awq_divide_rows")
+    return out
+
+
+def residual_add(x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+    """bf16(f32(x + y)) for bf16 x and fp32 y of the same shape [M][K]."""
+    x, y = _bf16(x, "x"), _f32(y, "y")
+    M, K = x.shape
+    out = torch.empty_like(x)
+    _check(lib().awq_residual_add(_ptr(x), _ptr(y), M, K, _ptr(out), _stream(x.device)),
+           "awq_residual_add")
+    return out
+
+
 LAYOUT_NIBBLE, LAYOUT_INT3_DENSE = 0, 1
 
 
@@ -419,3 +466,7 @@ def search_scale_gram(x: torch.Tensor, w: torch.Tensor, bits: int = 4, group: in
 from .linear import W4A16Linear, fold_inverse_scale  # noqa: E402  (needs the names above)
 
 __all__ += ["W4A16Linear", "fold_inverse_scale"]
+
+from .pipeline import quantize_mlp_block, quantize_mlp_blocks  # noqa: E402
+
+__all__ += ["quantize_mlp_block", "quantize_mlp_blocks"]

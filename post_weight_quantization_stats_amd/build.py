@@ -20,7 +20,7 @@ LIB_NAME = "libawq_mi355x.so"
 LIB_PATH = os.path.join(OUT_DIR, LIB_NAME)
 
 SOURCES = ["act_stats.hip", "candidate_scales.hip", "quantize_pack.hip", "w4a16_gemm.hip",
-           "decode_gemm.hip", "gram.hip", "loss_argmin.hip", "api.cpp"]
+           "decode_gemm.hip", "gram.hip", "block_ops.hip", "loss_argmin.hip", "api.cpp"]
 
 ARCH = "gfx950"
 

@@ -512,6 +512,72 @@ awq_status awq_candidate_sse(const uint16_t* x, int64_t M, int64_t N, int64_t K,
   }
 }
 
+awq_status awq_rmsnorm(const uint16_t* x, int64_t M, int64_t K, const float* gamma, double eps,
+                       uint16_t* u, float* r, void* stream) {
+  try {
+    if (M < 0 || M >= kMaxDim || K <= 0 || K % 8 != 0 || K > (int64_t(1) << 22))
+      return fail(AWQ_ERR_SHAPE, "rmsnorm needs 0 <= M, 8 <= K <= 2^22 with K a multiple of 8");
+    if (!(eps >= 0.0)) return fail(AWQ_ERR_UNSUPPORTED, "eps must be >= 0");
+    if (M == 0) return ok();
+    if (x == nullptr || gamma == nullptr || u == nullptr)
+      return fail(AWQ_ERR_NULL, "x, gamma and u are required");
+    if (misaligned(x) || misaligned(gamma) || misaligned(u) || ((uintptr_t)r & 3u))
+      return fail(AWQ_ERR_ALIGN, "x, gamma and u must be 16-byte aligned, r 4-byte");
+    AWQ_TRY_LAUNCH(awq::launch_rmsnorm(x, M, K, gamma, eps, u, r, (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_silu_mul(const float* y, int64_t M, int64_t F, uint16_t* h, void* stream) {
+  try {
+    if (M < 0 || M >= kMaxDim || F < 0 || F % 4 != 0 || F > (int64_t(1) << 22))
+      return fail(AWQ_ERR_SHAPE, "silu_mul needs F a multiple of 4, at most 2^22");
+    if (M == 0 || F == 0) return ok();
+    if (y == nullptr || h == nullptr) return fail(AWQ_ERR_NULL, "y and h are required");
+    if (misaligned(y) || ((uintptr_t)h & 7u))
+      return fail(AWQ_ERR_ALIGN, "y must be 16-byte aligned, h 8-byte");
+    AWQ_TRY_LAUNCH(awq::launch_silu_mul(y, M, F, h, (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_divide_rows(const float* v, int64_t R, int64_t C, const float* s, float* out,
+                           void* stream) {
+  try {
+    if (R < 0 || C < 0 || R >= kMaxDim || C >= kMaxDim) return fail(AWQ_ERR_SHAPE, "R, C out of range");
+    if (R == 0 || C == 0) return ok();
+    if (v == nullptr || s == nullptr || out == nullptr)
+      return fail(AWQ_ERR_NULL, "v, s and out are required");
+    if (((uintptr_t)v & 3u) || ((uintptr_t)s & 3u) || ((uintptr_t)out & 3u))
+      return fail(AWQ_ERR_ALIGN, "v, s and out must be 4-byte aligned");
+    AWQ_TRY_LAUNCH(awq::launch_divide_rows(v, R, C, s, out, (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_residual_add(const uint16_t* x, const float* y, int64_t M, int64_t K,
+                            uint16_t* out, void* stream) {
+  try {
+    if (M < 0 || M >= kMaxDim || K < 0 || K % 8 != 0 || K > (int64_t(1) << 22))
+      return fail(AWQ_ERR_SHAPE, "residual_add needs K a multiple of 8, at most 2^22");
+    if (M == 0 || K == 0) return ok();
+    if (x == nullptr || y == nullptr || out == nullptr)
+      return fail(AWQ_ERR_NULL, "x, y and out are required");
+    if (misaligned(x) || misaligned(y) || misaligned(out))
+      return fail(AWQ_ERR_ALIGN, "x, y and out must be 16-byte aligned");
+    AWQ_TRY_LAUNCH(awq::launch_residual_add(x, y, M * K, out, (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
 awq_status awq_search_scale_gram(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w,
                                  int64_t N, int32_t bits, int32_t group, int32_t n_grid,
                                  float* mean_abs, double* losses, int32_t* best_idx, float* best_s,

@@ -79,6 +79,15 @@ hipError_t launch_transpose_pad(const uint16_t* x, int64_t M, int64_t K, uint16_
                                 hipStream_t stream);
 hipError_t launch_gram_split(const float* g, int64_t K, uint16_t* out, hipStream_t stream);
 
+// ---- ops of the synthetic feed-forward block around the search ----
+hipError_t launch_rmsnorm(const uint16_t* x, int64_t M, int64_t K, const float* gamma,
+                          double eps, uint16_t* u, float* r, hipStream_t stream);
+hipError_t launch_silu_mul(const float* y, int64_t M, int64_t F, uint16_t* h, hipStream_t stream);
+hipError_t launch_divide_rows(const float* v, int64_t R, int64_t C, const float* s, float* out,
+                              hipStream_t stream);
+hipError_t launch_residual_add(const uint16_t* x, const float* y, int64_t n, uint16_t* out,
+                               hipStream_t stream);
+
 struct GemmOperands {
   const uint16_t* x;        // bf16 [M][K]
   int64_t M, N, K;

@@ -1,0 +1,149 @@
+// The ops either side of the search in a Llama-shaped feed-forward sublayer,
+// for running the search layer after layer (robotsatlas AWQ page, "How it
+// works": the activation is divided by the same per-channel factor that
+// multiplies the weight, which a deployment folds into the preceding
+// operation; "Computational complexity": one search per layer, in order).
+//
+//   rmsnorm      u = bf16(f32(f32(x * r) * gamma)), r = f32(1/sqrt(mean x^2 + eps))
+//   silu_mul     H = bf16(f32(silu(g) * v)) for y = [g | v], in fp64
+//   divide_rows  out[r][c] = f32(v[r][c] / s[r])  (the folds of 1/s)
+//   residual     x_next = bf16(f32(x + y))
+//
+// All are HBM-bound streams; each rounding point is the contract's, so the
+// results match the CPU reference bit for bit up to the last-ulp accuracy of
+// fp64 exp and the order of an fp64 sum.
+#include "awq_internal.h"
+#include "device_common.h"
+
+namespace awq {
+
+namespace {
+
+// Round-to-nearest-even of an fp32 value to bf16 (bit pattern).
+__device__ __forceinline__ uint16_t bf16_rne(float v) {
+  return (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+}
+
+// One workgroup per token row: fixed-order fp64 sum of squares, then the
+// normalised row.  K is a multiple of 8.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x, int64_t K,
+                                                      const float* __restrict__ gamma, double eps,
+                                                      uint16_t* __restrict__ u,
+                                                      float* __restrict__ r_out) {
+  const int64_t m = blockIdx.x;
+  const uint16_t* row = x + m * K;
+  double ss = 0.0;
+  for (int64_t c = (int64_t)threadIdx.x * 8; c < K; c += 256 * 8) {
+    const uint4 v = *(const uint4*)(row + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double a = bf16_lo(w[j]), b = bf16_hi(w[j]);
+      ss += a * a;          // exact square; the sum rounds in fp64
+      ss += b * b;
+    }
+  }
+  ss = wave_sum_f64(ss);
+  __shared__ double part[4];
+  __shared__ float r_sh;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double tot = ((part[0] + part[1]) + part[2]) + part[3];
+    r_sh = (float)(1.0 / sqrt(tot / (double)K + eps));
+    if (r_out != nullptr) r_out[m] = r_sh;
+  }
+  __syncthreads();
+  const float r = r_sh;
+  uint16_t* out = u + m * K;
+  for (int64_t c = (int64_t)threadIdx.x * 8; c < K; c += 256 * 8) {
+    const uint4 v = *(const uint4*)(row + c);
+    const float4 g0 = *(const float4*)(gamma + c);
+    const float4 g1 = *(const float4*)(gamma + c + 4);
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = bf16_lo(w[j]) * r, b = bf16_hi(w[j]) * r;
+      o[j] = pack_bf16x2(a * gv[2 * j], b * gv[2 * j + 1]);
+    }
+    *(uint4*)(out + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Four outputs per thread; F is a multiple of 4.
+__global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ y, int64_t M,
+                                                       int64_t F, uint16_t* __restrict__ h) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // element of H
+  if (i >= M * F) return;
+  const int64_t m = i / F, f = i - m * F;
+  const float4 g = *(const float4*)(y + m * 2 * F + f);
+  const float4 v = *(const float4*)(y + m * 2 * F + F + f);
+  const float gs[4] = {g.x, g.y, g.z, g.w}, vs[4] = {v.x, v.y, v.z, v.w};
+  uint16_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double gd = gs[j];
+    const double hv = gd / (1.0 + exp(-gd)) * (double)vs[j];
+    o[j] = bf16_rne((float)hv);
+  }
+  *(uint2*)(h + i) = make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+}
+
+__global__ __launch_bounds__(256) void divide_rows_kernel(const float* __restrict__ v, int64_t R,
+                                                          int64_t C, const float* __restrict__ s,
+                                                          float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= R * C) return;
+  out[i] = v[i] / s[i / C];          // IEEE division, one rounding
+}
+
+// Eight elements per thread; K is a multiple of 8.
+__global__ __launch_bounds__(256) void residual_kernel(const uint16_t* __restrict__ x,
+                                                       const float* __restrict__ y, int64_t n,
+                                                       uint16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  const uint4 xv = *(const uint4*)(x + i);
+  const float4 y0 = *(const float4*)(y + i);
+  const float4 y1 = *(const float4*)(y + i + 4);
+  const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+  const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(bf16_lo(w[j]) + yv[2 * j], bf16_hi(w[j]) + yv[2 * j + 1]);
+  *(uint4*)(out + i) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const uint16_t* x, int64_t M, int64_t K, const float* gamma,
+                          double eps, uint16_t* u, float* r, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  rmsnorm_kernel<<<(unsigned)M, 256, 0, stream>>>(x, K, gamma, eps, u, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul(const float* y, int64_t M, int64_t F, uint16_t* h, hipStream_t stream) {
+  if (M == 0 || F == 0) return hipSuccess;
+  silu_mul_kernel<<<(unsigned)ceil_div(M * F / 4, (int64_t)256), 256, 0, stream>>>(y, M, F, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_divide_rows(const float* v, int64_t R, int64_t C, const float* s, float* out,
+                              hipStream_t stream) {
+  if (R == 0 || C == 0) return hipSuccess;
+  divide_rows_kernel<<<(unsigned)ceil_div(R * C, (int64_t)256), 256, 0, stream>>>(v, R, C, s, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_add(const uint16_t* x, const float* y, int64_t n, uint16_t* out,
+                               hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  residual_kernel<<<(unsigned)ceil_div(n / 8, (int64_t)256), 256, 0, stream>>>(x, y, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace awq

@@ -24,7 +24,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-TENSOR_W, TENSOR_X, TENSOR_COLS, TENSOR_FACTORS, TENSOR_DECODE = 0, 1, 2, 3, 4
+TENSOR_W, TENSOR_X, TENSOR_COLS, TENSOR_FACTORS, TENSOR_DECODE, TENSOR_GAIN = 0, 1, 2, 3, 4, 5
+BLOCK_STREAM = 7          # workload id of the synthetic feed-forward blocks
 
 
 @dataclass(frozen=True)
@@ -218,3 +219,19 @@ def random_layer(M: int, K: int, N: int, seed: int, w_std: float = 0.02,
         cols = rng.choice(K, size=n_outlier, replace=False)
         x[:, cols] *= np.float32(outlier_factor)
     return to_bf16_bits(x), to_bf16_bits(w)
+
+
+def make_mlp_blocks(M: int, d: int, F: int, n_blocks: int, seed: int = 0, w_std: float = 0.02):
+    """Synthetic Llama-shaped feed-forward blocks for the layer-by-layer
+    pipeline: the first block's input x0 (bf16 [M][d], Student-t with nu = 4:
+    heavy-tailed hidden states) and per block (gamma f32 [d] ~ U(0.5, 1.5),
+    w_gu bf16 [2F][d] (gate rows, then up rows), w_down bf16 [d][F]),
+    weights ~ N(0, w_std^2)."""
+    x = _rng(seed, BLOCK_STREAM, 0, TENSOR_X).standard_t(4.0, size=(M, d)).astype(np.float32)
+    blocks = []
+    for b in range(n_blocks):
+        gamma = _rng(seed, BLOCK_STREAM, 100 + b, TENSOR_GAIN).uniform(0.5, 1.5, d).astype(np.float32)
+        wgu = _rng(seed, BLOCK_STREAM, 100 + b, TENSOR_W).standard_normal((2 * F, d), dtype=np.float32)
+        wd = _rng(seed, BLOCK_STREAM, 200 + b, TENSOR_W).standard_normal((d, F), dtype=np.float32)
+        blocks.append((gamma, to_bf16_bits(wgu * np.float32(w_std)), to_bf16_bits(wd * np.float32(w_std))))
+    return to_bf16_bits(x), blocks

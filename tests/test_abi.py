@@ -304,3 +304,21 @@ def test_decode_tiles_entry_errors():
     assert f(FAKE, 4, 128, 4096, FAKE + 4, FAKE, FAKE, 0, 128, FAKE, None, 0, None) == ALIGN
     # tiles beyond 4 GiB cannot be addressed
     assert f(FAKE, 4, 1 << 22, 1 << 13, FAKE, FAKE, FAKE, 0, 128, FAKE, FAKE, 1 << 40, None) == SHAPE
+
+
+def test_block_op_errors():
+    lib = awq.lib()
+    assert lib.awq_rmsnorm(None, 4, 128, FAKE, ctypes.c_double(1e-5), FAKE, None, None) == NULL
+    assert lib.awq_rmsnorm(FAKE, 4, 100, FAKE, ctypes.c_double(1e-5), FAKE, None, None) == SHAPE
+    assert lib.awq_rmsnorm(FAKE, 4, 128, FAKE, ctypes.c_double(-1.0), FAKE, None, None) == UNSUPPORTED
+    assert lib.awq_rmsnorm(FAKE_MIS, 4, 128, FAKE, ctypes.c_double(1e-5), FAKE, None, None) == ALIGN
+    assert lib.awq_rmsnorm(None, 0, 128, None, ctypes.c_double(1e-5), None, None, None) == OK
+    assert lib.awq_silu_mul(None, 4, 128, FAKE, None) == NULL
+    assert lib.awq_silu_mul(FAKE, 4, 126, FAKE, None) == SHAPE
+    assert lib.awq_silu_mul(FAKE, 4, 128, FAKE + 4, None) == ALIGN
+    assert lib.awq_divide_rows(FAKE, 4, 3, None, FAKE, None) == NULL
+    assert lib.awq_divide_rows(FAKE, 4, 3, FAKE + 2, FAKE, None) == ALIGN
+    assert lib.awq_divide_rows(None, 0, 3, None, None, None) == OK
+    assert lib.awq_residual_add(FAKE, None, 4, 128, FAKE, None) == NULL
+    assert lib.awq_residual_add(FAKE, FAKE, 4, 12, FAKE, None) == SHAPE
+    assert lib.awq_residual_add(FAKE, FAKE_MIS, 4, 128, FAKE, None) == ALIGN

@@ -31,3 +31,15 @@ def test_outlier_recipe():
     mean_abs = np.abs(x).mean(axis=0)
     others = np.setdiff1d(np.arange(spec.K), cols)
     assert mean_abs[cols].min() > 5 * mean_abs[others].max()
+
+
+def test_mlp_blocks_deterministic_and_shaped():
+    x, blocks = synth.make_mlp_blocks(32, 256, 384, 2, seed=3)
+    x2, blocks2 = synth.make_mlp_blocks(32, 256, 384, 2, seed=3)
+    assert x.shape == (32, 256) and x.dtype == np.uint16 and np.array_equal(x, x2)
+    assert len(blocks) == 2
+    for (g, wgu, wd), (g2, wgu2, wd2) in zip(blocks, blocks2):
+        assert g.shape == (256,) and g.dtype == np.float32 and 0.5 <= g.min() and g.max() <= 1.5
+        assert wgu.shape == (768, 256) and wd.shape == (256, 384)
+        assert np.array_equal(g, g2) and np.array_equal(wgu, wgu2) and np.array_equal(wd, wd2)
+    assert not np.array_equal(blocks[0][1], blocks[1][1])
