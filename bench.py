@@ -253,8 +253,11 @@ def log(*a):
 
 
 def event_time_ms(fn, reps: int, stream) -> float:
-    """Average duration of fn() over reps launches, HIP events on `stream`."""
+    """Average duration of fn() over reps launches, HIP events on `stream`,
+    after one untimed call (first-use setup, e.g. a library's kernel load)."""
     import torch
+    fn()
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -412,6 +415,50 @@ def bench_gram(awq, xd, wd, spec, bits: int, direct: dict, steps: int, direct_ms
             "same_choice": same}
 
 
+def bench_pipeline(awq, dev, stream, n_blocks: int = 2, M: int = 65536, d: int = 4096,
+                   F: int = 11008) -> dict:
+    """The search layer after layer through synthetic feed-forward blocks at
+    the Llama-2-7B widths (each block: gate_up 4096 -> 2 x 11008 and down
+    11008 -> 4096 searched, the scales folded, the quantized layers run as
+    deployed), plus the block ops' own kernels against HBM."""
+    import torch
+
+    import synth
+    t0 = time.perf_counter()
+    x0, blocks = synth.make_mlp_blocks(M, d, F, n_blocks, seed=0)
+    log(f"pipeline inputs ({n_blocks} blocks, {M} tokens) in {time.perf_counter() - t0:.1f} s")
+    xd = torch.from_numpy(x0.view(np.int16)).to(dev).view(torch.bfloat16)
+    bd = [(torch.from_numpy(g).to(dev),
+           torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16),
+           torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)) for g, a, b in blocks]
+    awq.quantize_mlp_blocks(xd, bd)            # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = awq.quantize_mlp_blocks(xd, bd)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3
+    alphas = [(int(r["gate_up"]["best_idx"].item()), int(r["down"]["best_idx"].item())) for r in res]
+    log(f"pipeline: {n_blocks} blocks in {ms:.1f} ms ({ms / n_blocks:.1f} ms per block, "
+        f"{2 * n_blocks * 1e3 / ms:.2f} layers/s); alpha indices {alphas}")
+    # the block ops on their own
+    gamma = bd[0][0]
+    y = torch.randn((M, 2 * F), device=dev)
+    yd = torch.randn((M, d), device=dev)
+    t_rms = event_time_ms(lambda: awq.rmsnorm(xd, gamma), 10, stream)
+    t_silu = event_time_ms(lambda: awq.silu_mul(y), 10, stream)
+    t_res = event_time_ms(lambda: awq.residual_add(xd, yd), 10, stream)
+    del y, yd
+    gbs = lambda nbytes, t: nbytes / (t * 1e-3) / 1e9
+    ops = {"rmsnorm": (4.0 * M * d + 4.0 * d, t_rms), "silu_mul": (10.0 * M * F, t_silu),
+           "residual_add": (8.0 * M * d, t_res)}
+    for k, (nb, t) in ops.items():
+        log(f"{k}: {t * 1e3:.1f} us = {gbs(nb, t):.0f} GB/s")
+    return {"blocks": n_blocks, "M": M, "d": d, "F": F, "ms": ms, "ms_per_block": ms / n_blocks,
+            "layers_per_s": 2 * n_blocks * 1e3 / ms, "alpha_indices": alphas,
+            "ops": {k: {"us": t * 1e3, "gbs": gbs(nb, t), "frac_hbm_peak": gbs(nb, t) / PEAK_HBM_GBS,
+                        "bytes": nb} for k, (nb, t) in ops.items()}}
+
+
 def cpu_baseline(x_bits, w_bits, spec, m_sample: int, n_sample: int) -> dict:
     """Oracle (numpy fp64) on a token prefix x output-row prefix; each phase is
     scaled to the full layer by the dimension it is linear in."""
@@ -448,6 +495,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped GEMM figures")
     ap.add_argument("--no-gram", action="store_true", help="skip the Gram-form search figure")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="skip the layer-by-layer block pipeline figure")
     ap.add_argument("--no-power-probe", action="store_true",
                     help="skip the constant-operand launch (keeps profiles to the synthetic data)")
     ap.add_argument("--decode-only", action="store_true",
@@ -638,9 +687,15 @@ def main() -> int:
         result["kernels"]["decode_gemm_int3_llama2_70b"] = bench_decode_int3(awq, dev, stream)
     del ws, gemm_ws, yref, b_mid, d_mid
     torch.cuda.empty_cache()
+    result["variants"] = {}
     if not args.no_gram:
-        result["variants"] = {"gram_form": bench_gram(awq, xd, wd, spec, bits, out, args.steps,
-                                                      ms_per_step)}
+        result["variants"]["gram_form"] = bench_gram(awq, xd, wd, spec, bits, out, args.steps,
+                                                     ms_per_step)
+        torch.cuda.empty_cache()
+    if not args.no_pipeline:
+        del xd, wd, out
+        torch.cuda.empty_cache()
+        result["variants"]["block_pipeline_llama2_7b_mlp"] = bench_pipeline(awq, dev, stream)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_m} tokens x {args.cpu_n} rows")
