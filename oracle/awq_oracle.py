@@ -38,6 +38,11 @@ contract the GPU library implements):
                    scales f32 [N][K/group], zeros u8 [N][K/group]
   dense INT3       qweight3[n][3c .. 3c+2] = the 96-bit little-endian value
                    sum_i q[n, 32c+i] << 3i of each run of 32 codes
+  compact format   for deployment: the fp32 step limited to [2^-24, 65504]
+                   and rounded to binary16 (nearest, ties to even) before the
+                   zero and the codes are computed; steps stored as binary16
+                   [N][G], zeros two per byte (even group in the low nibble)
+                   [N][ceil(G/2)]
   decode tiles     the words of rows 16b..16b+15 and group g as tile b*G+g,
                    row r's piece for channels 32q.. at byte P*(r + 16q)
   dequantized B    B[n,k] = bf16( f32( f32((q - z) * step) * inv_s[k] ) )
@@ -68,7 +73,8 @@ innocuous?", 1995).  Products of two fp32 values are exact in fp64.
 Parity unpinned (convention only, no value on the pages can fix them): the
 normalising constant sqrt(max*min), the 1e-4 floor, the nibble order of the
 packed layout, the 4-bit container used for INT3 codes and the bit order of the
-dense INT3 layout and the order of the decode tiles.
+dense INT3 layout, the order of the decode tiles, and the compact format's
+step range limits and zero nibble order.
 """
 
 from __future__ import annotations
@@ -192,6 +198,20 @@ def quantize(w, s32, bits: int, group: int):
     (None means s = 1).  Returns (q int64 [N][K], z int64 [N][K/group],
     step float64 [N][K/group] holding fp32 values).
     """
+    return _quantize(w, s32, bits, group, half_steps=False)
+
+
+def quantize16(w, s32, bits: int, group: int):
+    """The quantizer for the compact deployment format (16-bit steps): as
+    quantize, except that the fp32 step is first limited to the binary16
+    range [2^-24, 65504] (fmax/fmin, so NaN becomes 2^-24) and rounded to
+    binary16; the zero and the codes are then computed with that step, so
+    the stored step is the one the codes were rounded against.  Returns
+    (q, z, step) with step holding binary16 values."""
+    return _quantize(w, s32, bits, group, half_steps=True)
+
+
+def _quantize(w, s32, bits: int, group: int, half_steps: bool):
     W = bf16_bits_to_f64(w) if np.asarray(w).dtype == np.uint16 else np.asarray(w, np.float64)
     N, K = W.shape
     if K % group:
@@ -204,9 +224,64 @@ def quantize(w, s32, bits: int, group: int):
     rng = f32(mx - mn)
     step = f32(rng / qmax)
     step = np.where(step > 0.0, step, 1.0)
+    if half_steps:
+        step = f16_bits_to_f64(f16_rne_bits(np.fmin(np.fmax(step, F16_MIN), F16_MAX)))
     z = np.clip(np.rint(f32(-mn / step)), 0.0, qmax)
     q = np.clip(np.rint(f32(G / step[:, :, None])) + z[:, :, None], 0.0, qmax)
     return q.reshape(N, K).astype(np.int64), z.astype(np.int64), step
+
+
+# IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+F16_MIN = 2.0 ** -24          # smallest positive (subnormal) value
+F16_MAX = 65504.0             # largest finite value
+
+
+def f16_bits_to_f64(bits) -> np.ndarray:
+    """Exact value of binary16 bit patterns (uint16), from the format's
+    definition: (-1)^s * 2^(e-15) * (1 + f/1024) for 0 < e < 31,
+    (-1)^s * 2^-14 * f/1024 for e = 0, infinity or NaN for e = 31."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    normal = (1.0 + f / 1024.0) * np.exp2(e.astype(np.float64) - 15.0)
+    sub = f / 1024.0 * 2.0 ** -14
+    mag = np.where(e == 0, sub, normal)
+    mag = np.where(e == 31, np.where(f == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+def f16_rne_bits(x) -> np.ndarray:
+    """Round binary32 values to binary16, nearest with ties to even, as bit
+    patterns.  Written out from the definition: in the binade of |x| (the
+    subnormal binade below 2^-14) the spacing is u = 2^(E-10); |x| / u is
+    rounded to the nearest integer, an exact half going to the even one, and
+    the result re-encoded; a result above 65504 is infinity (IEEE 754
+    overflow: |x| >= 65520).  NaN maps to a quiet NaN."""
+    with np.errstate(invalid="ignore", over="ignore"):
+        v = np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    neg = np.signbit(v)
+    a = np.abs(v)
+    finite = np.isfinite(a)
+    af = np.where(finite & (a > 0), a, 1.0)
+    _, ex = np.frexp(af)                        # af = m * 2^ex, m in [1/2, 1)
+    E = np.maximum(ex - 1, -14)                 # binade exponent, floored at the subnormals
+    u = np.exp2((E - 10).astype(np.float64))
+    n = af / u                                  # exact: a power-of-two scaling
+    lo = np.floor(n)
+    frac = n - lo
+    up = (frac > 0.5) | ((frac == 0.5) & (np.mod(lo, 2.0) == 1.0))
+    m = (lo + up) * u                           # the rounded magnitude
+    m = np.where(finite & (a > 0), m, np.where(finite, 0.0, np.inf))
+    _, ex2 = np.frexp(np.where(m > 0, m, 1.0))
+    e_field = np.where(m >= 2.0 ** -14, ex2 - 1 + 15, 0)
+    frac_field = np.where(m >= 2.0 ** -14, (m / np.exp2((ex2 - 1).astype(np.float64)) - 1.0) * 1024.0,
+                          m / 2.0 ** -24)
+    out = (e_field.astype(np.int64) << 10) | np.rint(np.where(np.isfinite(frac_field), frac_field, 0.0)).astype(np.int64)
+    out = np.where(m > F16_MAX, 0x7C00, out)
+    out = np.where(np.isnan(v), 0x7E00, out)
+    out = out | np.where(neg, 0x8000, 0)
+    return out.astype(np.uint16)
 
 
 # --------------------------------------------------------------------------
@@ -237,6 +312,36 @@ def unpack(qweight):
 def packed_bytes(N: int, K: int, group: int) -> int:
     """Storage of the packed form: 4-bit codes + fp32 scale + u8 zero per group."""
     return N * K // 2 + N * (K // group) * (4 + 1)
+
+
+def pack_meta16(z, step16):
+    """The compact per-group metadata of the deployment format: steps as
+    binary16 bit patterns uint16 [N][G], and zeros two per byte, group 2j in
+    the low nibble of byte j and group 2j+1 in the high nibble (a zero past
+    the last group is 0), uint8 [N][ceil(G/2)]."""
+    z = np.asarray(z, dtype=np.int64)
+    N, G = z.shape
+    if z.min(initial=0) < 0 or z.max(initial=0) > 15:
+        raise ValueError("zeros must lie in [0, 15]")
+    zp = np.zeros((N, 2 * ((G + 1) // 2)), dtype=np.int64)
+    zp[:, :G] = z
+    zeros4 = (zp[:, 0::2] | (zp[:, 1::2] << 4)).astype(np.uint8)
+    return f16_rne_bits(step16), zeros4
+
+
+def unpack_meta16(steps16, zeros4, G: int):
+    """(step float64 [N][G], z int64 [N][G]) from the compact metadata."""
+    zb = np.asarray(zeros4, dtype=np.int64)
+    z = np.empty((zb.shape[0], 2 * zb.shape[1]), dtype=np.int64)
+    z[:, 0::2] = zb & 0xF
+    z[:, 1::2] = zb >> 4
+    return f16_bits_to_f64(steps16), z[:, :G]
+
+
+def packed16_bytes(N: int, K: int, group: int, code_bits: int = 4) -> int:
+    """Storage of the compact form: codes + binary16 step + 4-bit zero per group."""
+    G = K // group
+    return N * code_bits * K // 8 + N * G * 2 + N * ((G + 1) // 2)
 
 
 def pack3(q):
@@ -439,6 +544,16 @@ def decode_gemm(a_bits, qweight, scales, zeros, group: int) -> np.ndarray:
     is a small integer and step a binary32, so every Wd and every product with
     a bf16 activation is exact in fp64; only the K-sum rounds."""
     return _decode_product(a_bits, unpack(qweight), scales, zeros, group)
+
+
+def decode_gemm16(a_bits, qweight, steps16, zeros4, group: int, dense3: bool = False) -> np.ndarray:
+    """The deployment contraction on the compact format: decode_gemm's
+    product with (step, zero) read from binary16 steps and 4-bit zeros
+    (every binary16 value is a binary32 value, so Wd = (q - z) * step stays
+    exact)."""
+    q = unpack3(qweight) if dense3 else unpack(qweight)
+    step, z = unpack_meta16(steps16, zeros4, q.shape[1] // group)
+    return _decode_product(a_bits, q, step, z, group)
 
 
 def _decode_product(a_bits, q, scales, zeros, group: int) -> np.ndarray:

@@ -158,13 +158,48 @@ def _mut_fold_multiplies(mp):
                                    np.asarray(s, np.float64).reshape((-1,) + (1,) * (np.ndim(v) - 1))))
 
 
+def _mut_f16_ties_away(mp):
+    orig = OA.f16_rne_bits
+
+    def ties_away(x):
+        # one binary32 ulp away from zero first: exact ties round away from zero
+        v = np.asarray(x, np.float64).astype(np.float32)
+        return orig(np.nextafter(v, np.copysign(np.float32(np.inf), v)))
+    mp.setattr(OA, "f16_rne_bits", ties_away)
+    mp.setattr(oracle, "f16_rne_bits", ties_away)
+
+
+def _mut_quantize16_codes_with_fp32_step(mp):
+    def q16(w, s32, bits, group):
+        q, z, _ = OA._quantize(w, s32, bits, group, half_steps=False)
+        _, _, step = OA._quantize(w, s32, bits, group, half_steps=True)
+        return q, z, step
+    mp.setattr(OA, "quantize16", q16)
+    mp.setattr(oracle, "quantize16", q16)
+
+
+def _mut_zero_nibbles_swapped(mp):
+    orig = OA.pack_meta16
+
+    def swapped(z, step16):
+        sb, zb = orig(z, step16)
+        return sb, ((zb >> 4) | (zb << 4)).astype(np.uint8)
+    mp.setattr(OA, "pack_meta16", swapped)
+    mp.setattr(oracle, "pack_meta16", swapped)
+
+
+def _mut_half_step_no_clamp(mp):
+    mp.setattr(OA, "F16_MIN", 0.0)
+
+
 MUTATIONS = [_mut_floor_instead_of_rint, _mut_drop_inv_s, _mut_alpha_grid_closed,
              _mut_scale_index_reversed, _mut_zero_added_before_rounding, _mut_loss_sign,
              _mut_no_range_extension, _mut_stats_mean_without_abs, _mut_normaliser_max_only,
              _mut_decode_zero_of_first_group, _mut_decode_rounds_weight_to_bf16, _mut_diff_sign,
              _mut_diff_off_by_half_ulp, _mut_pack3_code_bits_reversed, _mut_pack3_runs_of_16,
              _mut_tiles_row_major_inside, _mut_rmsnorm_without_mean, _mut_silu_is_sigmoid,
-             _mut_fold_multiplies]
+             _mut_fold_multiplies, _mut_f16_ties_away, _mut_quantize16_codes_with_fp32_step,
+             _mut_zero_nibbles_swapped, _mut_half_step_no_clamp]
 
 PINS = [
     P.test_quantizer_worked_group,
@@ -185,6 +220,10 @@ PINS = [
     P.test_rmsnorm_closed_form_and_scaling,
     P.test_silu_mul_against_torch_and_identities,
     P.test_divide_rows_and_residual_against_library,
+    P.test_f16_format_against_libraries,
+    P.test_quantize16_brute_force_nearest_level,
+    P.test_quantize16_clamped_and_subnormal_steps,
+    P.test_meta16_pack_brute_force_and_roundtrip,
 ]
 
 

@@ -605,6 +605,173 @@ def test_decode_gemm_equals_deploy_when_dequant_is_bf16_exact():
     assert np.array_equal(O.decode_gemm(x, qw, sc, ze, 128), O.deploy_gemm(x, qw, sc, ze, 128))
 
 
+# ------------------------------------------- compact format: 16-bit steps, 4-bit zeros
+
+def py_f16_bits(x: float) -> int:
+    """binary16 pattern of x by Python's struct 'e' format (round half to even)."""
+    try:
+        return struct.unpack("<H", struct.pack("<e", x))[0]
+    except OverflowError:
+        return 0x7C00 if x > 0 else 0xFC00
+
+
+def test_f16_format_against_libraries():
+    """The oracle's binary16 decode and rounding, written from the format's
+    definition, against numpy's float16 and Python's struct 'e' format:
+    every bit pattern, random binary32 values, exact ties and the overflow
+    boundary."""
+    b = np.arange(65536, dtype=np.uint16)
+    ref = b.view(np.float16).astype(np.float64)
+    got = O.f16_bits_to_f64(b)
+    assert np.all((got == ref) | (np.isnan(got) & np.isnan(ref)))
+    rng = np.random.default_rng(40)
+    u = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    v = u.view(np.float32)
+    v = v[~np.isnan(v)]
+    with np.errstate(over="ignore"):
+        assert np.array_equal(O.f16_rne_bits(v), v.astype(np.float16).view(np.uint16))
+    # exact midpoints between neighbouring binary16 values (all exact in binary32)
+    h = np.arange(0, 0x7BFF, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    mid = ((lo + hi) / 2).astype(np.float32)
+    want = np.where(h % 2 == 0, h, h + 1).astype(np.uint16)       # to the even pattern
+    assert np.array_equal(O.f16_rne_bits(mid), want)
+    assert np.array_equal(O.f16_rne_bits(-mid), want | np.uint16(0x8000))
+    for x in (65504.0, 65519.99, 65520.0, 2.0 ** -25, 2.0 ** -25 * (1 + 2 ** -23), 3e-8, 1e-3, 0.1):
+        x32 = float(np.float32(x))
+        assert int(O.f16_rne_bits(np.float32(x32))) == py_f16_bits(x32), x
+
+
+def _grid_layer(N, G, group, qmax, seed):
+    """bf16 weights k * 2^-7 whose every group has range qmax * j * 2^-7
+    (j in 1..8), so the fp32 step j * 2^-7 is a binary16 value."""
+    rng = np.random.default_rng(seed)
+    k = np.empty((N, G, group), np.int64)
+    for n in range(N):
+        for g in range(G):
+            j = int(rng.integers(1, 9))
+            lo = -int(rng.integers(0, qmax * j + 1))
+            hi = lo + qmax * j
+            k[n, g] = rng.integers(lo, hi + 1, size=group)
+            k[n, g, rng.integers(0, group)] = lo
+            k[n, g, rng.integers(0, group)] = hi
+    return bits_of(k.reshape(N, G * group).astype(np.float32) * np.float32(2.0 ** -7))
+
+
+def test_quantize16_equals_quantize_when_steps_are_binary16():
+    for bits in (3, 4):
+        w = _grid_layer(6, 3, 128, (1 << bits) - 1, seed=41 + bits)
+        q1, z1, st1 = O.quantize(w, None, bits, 128)
+        q2, z2, st2 = O.quantize16(w, None, bits, 128)
+        assert np.array_equal(q1, q2) and np.array_equal(z1, z2) and np.array_equal(st1, st2)
+
+
+def test_quantize16_brute_force_nearest_level():
+    """Each step is the binary16 nearest the fp32 step (struct 'e'), and each
+    code is the nearest of the qmax+1 levels to f32(ws/step) + z (ties: even)."""
+    x, w = synth.random_layer(32, 256, 6, seed=42, n_outlier=2)
+    s = O.candidate_scales(O.act_stats(x)[1], 20)[0][11]
+    W = synth.bf16_bits_to_f32(w).astype(np.float64)
+    for bits in (3, 4):
+        qmax = (1 << bits) - 1
+        q, z, step = O.quantize16(w, s, bits, 128)
+        _, _, step32 = O.quantize(w, s, bits, 128)
+        for n in range(6):
+            for g in range(2):
+                st = float(step[n, g])
+                assert py_f16_bits(st) == py_f16_bits(float(step32[n, g]))
+                assert struct.unpack("<e", struct.pack("<e", st))[0] == st
+                ws = [py_f32(W[n, k] * s[k]) for k in range(128 * g, 128 * g + 128)]
+                mn = min(min(ws), 0.0)
+                zz = min(max(round(py_f32(-mn / st)), 0), qmax)
+                assert z[n, g] == zz
+                for j, v in enumerate(ws):
+                    t = py_f32(v / st)
+                    best = min(range(qmax + 1), key=lambda c: (abs(t - (c - zz)), (c - zz) % 2))
+                    assert q[n, 128 * g + j] == best
+
+
+def test_quantize16_clamped_and_subnormal_steps():
+    """Tiny ranges take the smallest binary16 step 2^-24 (codes and zero 0);
+    ranges past 15 * 65504 take 65504 and saturate the codes; a zero group
+    keeps step 1; binary16-subnormal steps are multiples of 2^-24 within
+    2^-25 of the fp32 step."""
+    vals = np.zeros((4, 128), np.float32)
+    vals[0, :64], vals[0, 64:] = 1e-9, -1e-9
+    vals[1, 0], vals[1, 1], vals[1, 2] = 2.0 ** 20, -(2.0 ** 20), 65536.0
+    vals[3] = np.linspace(-3e-4, 2e-4, 128, dtype=np.float32)
+    w = synth.to_bf16_bits(vals)
+    q, z, step = O.quantize16(w, None, 4, 128)
+    assert step[0, 0] == 2.0 ** -24 and z[0, 0] == 0 and np.all(q[0] == 0)
+    assert step[1, 0] == 65504.0 and z[1, 0] == 15
+    assert q[1, 0] == 15 and q[1, 1] == 0 and q[1, 2] == 15 and q[1, 3] == 15
+    assert step[2, 0] == 1.0 and z[2, 0] == 0 and np.all(q[2] == 0)
+    _, _, s32 = O.quantize(w, None, 4, 128)
+    assert s32[3, 0] < 2.0 ** -14
+    n = step[3, 0] / 2.0 ** -24
+    assert n == int(n) and abs(step[3, 0] - s32[3, 0]) <= 2.0 ** -25
+
+
+def test_meta16_pack_brute_force_and_roundtrip():
+    rng = np.random.default_rng(43)
+    for G in (1, 5, 8):
+        z = rng.integers(0, 16, size=(3, G))
+        st = np.array([[struct.unpack("<e", struct.pack("<e", float(v)))[0] for v in row]
+                       for row in rng.uniform(1e-3, 2.0, size=(3, G))])
+        sb, zb = O.pack_meta16(z, st)
+        assert sb.dtype == np.uint16 and zb.dtype == np.uint8 and zb.shape == (3, (G + 1) // 2)
+        for n in range(3):
+            for g in range(G):
+                assert int(sb[n, g]) == py_f16_bits(float(st[n, g]))
+            for j in range((G + 1) // 2):
+                lo = int(z[n, 2 * j])
+                hi = int(z[n, 2 * j + 1]) if 2 * j + 1 < G else 0
+                assert int(zb[n, j]) == lo + 16 * hi
+        st2, z2 = O.unpack_meta16(sb, zb, G)
+        assert np.array_equal(z2, z) and np.array_equal(st2, st)
+
+
+def test_decode_gemm16_brute_force_from_bytes():
+    """Codes, zeros and steps decoded from the stored words and bytes in pure
+    Python (nibbles by shifting, steps by struct 'e'); the dequantized weight
+    (q - z) * step is exact in binary64.  The dense INT3 container gives the
+    same product."""
+    M, N, K = 3, 6, 384
+    x, w = synth.random_layer(M, K, N, seed=44)
+    X = synth.bf16_bits_to_f32(x).astype(np.float64)
+    for bits in (4, 3):
+        q, z, st = O.quantize16(w, None, bits, 128)
+        qw = O.pack(q, z, st)[0]
+        sb, zb = O.pack_meta16(z, st)
+        Y = O.decode_gemm16(x, qw, sb, zb, 128)
+        words = qw.astype(np.uint64)
+        for m in range(M):
+            for n in range(N):
+                terms = []
+                for k in range(K):
+                    g = k // 128
+                    code = (int(words[n, k // 8]) >> (4 * (k % 8))) & 15
+                    zero = (int(zb[n, g // 2]) >> (4 * (g % 2))) & 15
+                    stv = struct.unpack("<e", struct.pack("<H", int(sb[n, g])))[0]
+                    terms.append(X[m, k] * ((code - zero) * stv))
+                assert Y[m, n] == pytest.approx(math.fsum(terms), rel=1e-13, abs=1e-300)
+        if bits == 3:
+            Y3 = O.decode_gemm16(x, O.pack3(q), sb, zb, 128, dense3=True)
+            assert np.array_equal(Y3, Y)
+
+
+def test_compact_storage_bytes():
+    """4-bit codes + 2-byte step + half-byte zero per group of 128: 4.156
+    bits per weight, 3.85 times smaller than bf16 (the pages' "about four
+    times")."""
+    N, K = 4096, 4096
+    assert O.packed16_bytes(N, K, 128) == N * K // 2 + N * 32 * 2 + N * 16
+    assert O.packed16_bytes(N, K, 128, code_bits=3) == N * K * 3 // 8 + N * 32 * 2 + N * 16
+    ratio = 2 * N * K / O.packed16_bytes(N, K, 128)
+    assert 3.8 < ratio < 3.9
+
+
 # ------------------------------------------------- the synthetic block pipeline
 
 def test_rmsnorm_closed_form_and_scaling():
