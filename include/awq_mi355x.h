@@ -312,6 +312,48 @@ awq_status awq_decode_gemm_tiled(const uint16_t* a, int64_t M, int64_t N, int64_
                                  size_t ws_bytes, void* stream);
 
 /*
+ * Compact deployment format: 16-bit steps and 4-bit zeros (2.5 bytes of
+ * metadata per group instead of 5; robotsatlas "Components": a scale per
+ * group of 128; builderai "About": real low-bit weights are written).  The
+ * final pack at the chosen s, with the step rounded before the codes:
+ *   step  = as awq_quantize_pack, then limited to [2^-24, 65504] (a NaN step
+ *           becomes 2^-24) and rounded to IEEE binary16 (nearest, ties to
+ *           even)
+ *   z, q  = as awq_quantize_pack, computed with that step
+ *   w bf16 [N][K]; s f32 [K] or NULL (s = 1); bits 3 or 4
+ *   layout AWQ_LAYOUT_NIBBLE: qweight u32 [N][K/8] (16-byte aligned) as
+ *     awq_quantize_pack; AWQ_LAYOUT_INT3_DENSE (bits 3): qweight u32
+ *     [N][3K/32] (4-byte aligned) as awq_quantize_pack3
+ *   steps16 binary16 bit patterns [N][K/group] (2-byte aligned)
+ *   zeros4  u8 [N][ceil(G/2)], G = K/group: group 2j in the low nibble of
+ *     byte j, group 2j+1 in the high nibble (0 past the last group)
+ * N == 0 is a no-op.
+ */
+awq_status awq_quantize_pack16(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                               int32_t bits, int32_t group, int32_t layout, uint32_t* qweight,
+                               uint16_t* steps16, uint8_t* zeros4, void* stream);
+
+/*
+ * Compact metadata -> scales f32 [N][K/group] and zeros u8 [N][K/group]
+ * (exact), for the contractions that take those (awq_w4a16_gemm with many
+ * tokens).  N == 0 is a no-op.
+ */
+awq_status awq_expand_meta16(const uint16_t* steps16, const uint8_t* zeros4, int64_t N, int64_t K,
+                             int32_t group, float* scales, uint8_t* zeros, void* stream);
+
+/*
+ * The decode-shaped contraction on decode tiles with the compact metadata
+ * (awq_quantize_pack16): arguments, limits, workspace and results as
+ * awq_decode_gemm_tiled, with steps16 (2-byte aligned) and zeros4 in place
+ * of scales and zeros.  Bit-identical to awq_decode_gemm_tiled on the
+ * expanded metadata.
+ */
+awq_status awq_decode_gemm_tiled16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                   const uint32_t* tiles, const uint16_t* steps16,
+                                   const uint8_t* zeros4, int32_t layout, int32_t group, float* y,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
  * The whole per-layer search (robotsatlas "How it works", "Key mechanisms";
  * "Computational complexity": cost grows with layers x grid points x
  * calibration tokens).  Steps, all on `stream` with no host synchronisation:

@@ -20,6 +20,7 @@ __all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "
            "reference_gemm", "w4a16_gemm", "search_scale", "search_scale_gram", "decode_gemm",
            "dequant_operand", "diff_operand", "candidate_sse", "quantize_pack3", "decode_gemm3",
            "decode_tiles", "decode_gemm_tiled", "LAYOUT_NIBBLE", "LAYOUT_INT3_DENSE",
+           "quantize_pack16", "expand_meta16", "decode_gemm_tiled16",
            "rmsnorm", "silu_mul", "divide_rows", "residual_add", "workspace_size",
            "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES",
            "OP_DECODE_GEMM", "OP_CANDIDATE_SSE", "OP_SEARCH_SCALE_GRAM"]
@@ -50,6 +51,12 @@ _SIGNATURES = {
     "awq_decode_tiles": ([_c_void_p, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p], _i32),
     "awq_decode_gemm_tiled": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
                                _i32, _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
+    "awq_quantize_pack16": ([_c_void_p, _i64, _i64, _c_void_p, _i32, _i32, _i32, _c_void_p,
+                             _c_void_p, _c_void_p, _c_void_p], _i32),
+    "awq_expand_meta16": ([_c_void_p, _c_void_p, _i64, _i64, _i32, _c_void_p, _c_void_p,
+                           _c_void_p], _i32),
+    "awq_decode_gemm_tiled16": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                 _i32, _i32, _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
     "awq_rmsnorm": ([_c_void_p, _i64, _i64, _c_void_p, ctypes.c_double, _c_void_p, _c_void_p,
                      _c_void_p], _i32),
     "awq_silu_mul": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p], _i32),
@@ -404,6 +411,70 @@ def decode_gemm_tiled(a: torch.Tensor, tiles: torch.Tensor, scales: torch.Tensor
                                        layout, group, _ptr(y), _ptr(ws),
                                        0 if ws is None else ws.numel(), _stream(dev)),
            "awq_decode_gemm_tiled")
+    return y
+
+
+def quantize_pack16(w: torch.Tensor, s: torch.Tensor | None, bits: int = 4, group: int = 128,
+                    layout: int = LAYOUT_NIBBLE):
+    """The compact deployment format of W . diag(s): (qweight int32, steps16
+    float16 [N][K/group], zeros4 uint8 [N][ceil(G/2)], two zeros per byte).
+    qweight is [N][K/8] (LAYOUT_NIBBLE) or [N][3K/32] (LAYOUT_INT3_DENSE, bits 3)."""
+    w = _bf16(w, "w")
+    N, K = w.shape
+    if s is not None:
+        s = _f32(s, "s")
+    dev = w.device
+    G = K // group
+    words = 3 * K // 32 if layout == LAYOUT_INT3_DENSE else K // 8
+    qw = torch.empty((N, words), dtype=torch.int32, device=dev)
+    st = torch.empty((N, G), dtype=torch.float16, device=dev)
+    ze = torch.empty((N, (G + 1) // 2), dtype=torch.uint8, device=dev)
+    _check(lib().awq_quantize_pack16(_ptr(w), N, K, _ptr(s), bits, group, layout, _ptr(qw),
+                                     _ptr(st), _ptr(ze), _stream(dev)), "awq_quantize_pack16")
+    return qw, st, ze
+
+
+def _f16(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.float16:
+        raise ValueError(f"{name} must be float16 (binary16 steps)")
+    return t.contiguous()
+
+
+def expand_meta16(steps16: torch.Tensor, zeros4: torch.Tensor, group: int = 128):
+    """(scales f32 [N][G], zeros u8 [N][G]) from the compact metadata (exact)."""
+    steps16 = _f16(steps16, "steps16")
+    N, G = steps16.shape
+    if zeros4.dtype != torch.uint8 or tuple(zeros4.shape) != (N, (G + 1) // 2):
+        raise ValueError("zeros4 must be uint8 [N][ceil(G/2)]")
+    dev = steps16.device
+    sc = torch.empty((N, G), dtype=torch.float32, device=dev)
+    ze = torch.empty((N, G), dtype=torch.uint8, device=dev)
+    _check(lib().awq_expand_meta16(_ptr(steps16), _ptr(zeros4.contiguous()), N, G * group, group,
+                                   _ptr(sc), _ptr(ze), _stream(dev)), "awq_expand_meta16")
+    return sc, ze
+
+
+def decode_gemm_tiled16(a: torch.Tensor, tiles: torch.Tensor, steps16: torch.Tensor,
+                        zeros4: torch.Tensor, layout: int = LAYOUT_NIBBLE, group: int = 128,
+                        out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_gemm_tiled with the compact metadata (fp32 [M][N])."""
+    a = _bf16(a, "a")
+    M, K = a.shape
+    steps16 = _f16(steps16, "steps16")
+    N, G = steps16.shape
+    if G * group != K:
+        raise ValueError("steps16 must be [N][K/group]")
+    if zeros4.dtype != torch.uint8 or tuple(zeros4.shape) != (N, (G + 1) // 2):
+        raise ValueError("zeros4 must be uint8 [N][ceil(G/2)]")
+    dev = a.device
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if out is None else _f32(out, "out")
+    need = workspace_size(OP_DECODE_GEMM, M, N, K, 3 if layout == LAYOUT_INT3_DENSE else 4, group)
+    ws = _workspace(need, dev, workspace) if need > 0 else None
+    _check(lib().awq_decode_gemm_tiled16(_ptr(a), M, N, K, _ptr(tiles), _ptr(steps16),
+                                         _ptr(zeros4.contiguous()), layout, group, _ptr(y),
+                                         _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)),
+           "awq_decode_gemm_tiled16")
     return y
 
 

@@ -275,6 +275,53 @@ awq_status awq_quantize_pack3(const uint16_t* w, int64_t N, int64_t K, const flo
   }
 }
 
+awq_status awq_quantize_pack16(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                               int32_t bits, int32_t group, int32_t layout, uint32_t* qweight,
+                               uint16_t* steps16, uint8_t* zeros4, void* stream) {
+  try {
+    if (layout != AWQ_LAYOUT_NIBBLE && layout != AWQ_LAYOUT_INT3_DENSE)
+      return fail(AWQ_ERR_UNSUPPORTED, "unknown layout %d", layout);
+    const bool dense = layout == AWQ_LAYOUT_INT3_DENSE;
+    if (dense && bits != 3) return fail(AWQ_ERR_UNSUPPORTED, "the dense INT3 layout holds 3-bit codes");
+    awq_status st = check_quant_params(bits, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (N < 0 || N >= kMaxDim) return fail(AWQ_ERR_SHAPE, "N out of range");
+    if (N == 0) return ok();
+    if (w == nullptr || qweight == nullptr || steps16 == nullptr || zeros4 == nullptr)
+      return fail(AWQ_ERR_NULL, "w, qweight, steps16 and zeros4 are required");
+    if (misaligned(w) || (s != nullptr && misaligned(s)) ||
+        (dense ? ((uintptr_t)qweight & 3u) != 0 : misaligned(qweight)) || ((uintptr_t)steps16 & 1u))
+      return fail(AWQ_ERR_ALIGN, "w, s must be 16-byte aligned, qweight 16-byte (4-byte for dense "
+                                 "INT3), steps16 2-byte");
+    AWQ_TRY_LAUNCH(awq::launch_quantize_pack16(w, N, K, s, bits, dense, qweight, steps16, zeros4,
+                                               (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_expand_meta16(const uint16_t* steps16, const uint8_t* zeros4, int64_t N, int64_t K,
+                             int32_t group, float* scales, uint8_t* zeros, void* stream) {
+  try {
+    awq_status st = check_quant_params(4, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (N < 0 || N >= kMaxDim) return fail(AWQ_ERR_SHAPE, "N out of range");
+    if (N == 0) return ok();
+    if (steps16 == nullptr || zeros4 == nullptr || scales == nullptr || zeros == nullptr)
+      return fail(AWQ_ERR_NULL, "steps16, zeros4, scales and zeros are required");
+    if (((uintptr_t)steps16 & 1u) || ((uintptr_t)scales & 3u))
+      return fail(AWQ_ERR_ALIGN, "steps16 must be 2-byte aligned, scales 4-byte");
+    AWQ_TRY_LAUNCH(awq::launch_expand_meta16(steps16, zeros4, N, K / group, scales, zeros,
+                                             (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
 awq_status awq_dequant_operand(const uint16_t* w, int64_t N, int64_t K, const float* s,
                                const float* inv_s, int32_t bits, int32_t group, uint16_t* b,
                                void* stream) {
@@ -385,11 +432,13 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
   }
 }
 
+// Exactly one of scales (fp32 steps, u8 zeros) and steps16 (binary16 steps,
+// zeros two per byte; tiled codes only) is given.
 static awq_status decode_entry(const uint16_t* a, int64_t M, int64_t N, int64_t K,
                                const uint32_t* qweight, const float* scales,
-                               const uint8_t* zeros, int32_t bits, int32_t group, float* y,
-                               void* ws, size_t ws_bytes, void* stream, bool int3_dense,
-                               bool tiled = false) {
+                               const uint16_t* steps16, const uint8_t* zeros, int32_t bits,
+                               int32_t group, float* y, void* ws, size_t ws_bytes, void* stream,
+                               bool int3_dense, bool tiled = false) {
   try {
     awq_status st = check_quant_params(bits, group);
     if (st != AWQ_OK) return st;
@@ -398,19 +447,27 @@ static awq_status decode_entry(const uint16_t* a, int64_t M, int64_t N, int64_t 
       return fail(AWQ_ERR_SHAPE, "decode GEMM needs 0 <= M <= %lld and 0 <= N <= 2^22",
                   (long long)awq::kDecodeMaxM);
     if (M == 0 || N == 0) return ok();
-    if (a == nullptr || qweight == nullptr || scales == nullptr || zeros == nullptr || y == nullptr)
-      return fail(AWQ_ERR_NULL, "a, qweight, scales, zeros and y are required");
-    if (misaligned(a) || misaligned(y) || misaligned(ws) || ((uintptr_t)scales & 3u) ||
+    const bool half = steps16 != nullptr;
+    if (a == nullptr || qweight == nullptr || (half ? steps16 : (const void*)scales) == nullptr ||
+        zeros == nullptr || y == nullptr)
+      return fail(AWQ_ERR_NULL, "a, qweight, %s, zeros and y are required",
+                  half ? "steps16" : "scales");
+    if (misaligned(a) || misaligned(y) || misaligned(ws) ||
+        (half ? ((uintptr_t)steps16 & 1u) : ((uintptr_t)scales & 3u)) ||
         (int3_dense ? ((uintptr_t)qweight & 3u) != 0 : misaligned(qweight)))
       return fail(AWQ_ERR_ALIGN, "a, y and ws must be 16-byte aligned, qweight 16-byte (4-byte "
-                                 "for dense INT3), scales 4-byte");
+                                 "for dense INT3), scales 4-byte, steps16 2-byte");
     const awq::DecodePlan plan = awq::decode_plan(M, N, K);
     if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes))
       return fail(AWQ_ERR_WORKSPACE, "decode GEMM needs %zu workspace bytes", plan.ws_bytes);
     if (tiled && awq::decode_tiles_bytes(N, K, int3_dense) > 0xFFFFFFFFull)
       return fail(AWQ_ERR_SHAPE, "decode tiles are addressed with 32-bit offsets: at most 4 GiB");
-    AWQ_TRY_LAUNCH(awq::launch_decode_gemm(a, M, N, K, qweight, scales, zeros, y, ws,
-                                           (hipStream_t)stream, int3_dense, tiled));
+    if (half)
+      AWQ_TRY_LAUNCH(awq::launch_decode_gemm16(a, M, N, K, qweight, steps16, zeros, y, ws,
+                                               (hipStream_t)stream, int3_dense));
+    else
+      AWQ_TRY_LAUNCH(awq::launch_decode_gemm(a, M, N, K, qweight, scales, zeros, y, ws,
+                                             (hipStream_t)stream, int3_dense, tiled));
     return ok();
   } catch (...) {
     return fail(AWQ_ERR_LAUNCH, "internal error");
@@ -421,16 +478,16 @@ awq_status awq_w4a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_
                                  const uint32_t* qweight, const float* scales,
                                  const uint8_t* zeros, int32_t bits, int32_t group, float* y,
                                  void* ws, size_t ws_bytes, void* stream) {
-  return decode_entry(a, M, N, K, qweight, scales, zeros, bits, group, y, ws, ws_bytes, stream,
-                      false);
+  return decode_entry(a, M, N, K, qweight, scales, nullptr, zeros, bits, group, y, ws, ws_bytes,
+                      stream, false);
 }
 
 awq_status awq_w3a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
                                  const uint32_t* qweight3, const float* scales,
                                  const uint8_t* zeros, int32_t group, float* y, void* ws,
                                  size_t ws_bytes, void* stream) {
-  return decode_entry(a, M, N, K, qweight3, scales, zeros, 3, group, y, ws, ws_bytes, stream,
-                      true);
+  return decode_entry(a, M, N, K, qweight3, scales, nullptr, zeros, 3, group, y, ws, ws_bytes,
+                      stream, true);
 }
 
 awq_status awq_decode_tiles_size(int64_t N, int64_t K, int32_t layout, int32_t group,
@@ -471,8 +528,21 @@ awq_status awq_decode_gemm_tiled(const uint16_t* a, int64_t M, int64_t N, int64_
   if (layout != AWQ_LAYOUT_NIBBLE && layout != AWQ_LAYOUT_INT3_DENSE)
     return fail(AWQ_ERR_UNSUPPORTED, "unknown layout %d", layout);
   const bool dense = layout == AWQ_LAYOUT_INT3_DENSE;
-  return decode_entry(a, M, N, K, tiles, scales, zeros, dense ? 3 : 4, group, y, ws, ws_bytes,
-                      stream, dense, true);
+  if (scales == nullptr) return fail(AWQ_ERR_NULL, "scales is required");
+  return decode_entry(a, M, N, K, tiles, scales, nullptr, zeros, dense ? 3 : 4, group, y, ws,
+                      ws_bytes, stream, dense, true);
+}
+
+awq_status awq_decode_gemm_tiled16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                   const uint32_t* tiles, const uint16_t* steps16,
+                                   const uint8_t* zeros4, int32_t layout, int32_t group, float* y,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (layout != AWQ_LAYOUT_NIBBLE && layout != AWQ_LAYOUT_INT3_DENSE)
+    return fail(AWQ_ERR_UNSUPPORTED, "unknown layout %d", layout);
+  const bool dense = layout == AWQ_LAYOUT_INT3_DENSE;
+  if (steps16 == nullptr) return fail(AWQ_ERR_NULL, "steps16 is required");
+  return decode_entry(a, M, N, K, tiles, nullptr, steps16, zeros4, dense ? 3 : 4, group, y, ws,
+                      ws_bytes, stream, dense, true);
 }
 
 awq_status awq_candidate_sse(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint16_t* b,

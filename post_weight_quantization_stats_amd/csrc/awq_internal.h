@@ -57,6 +57,17 @@ hipError_t launch_quantize_pack3(const uint16_t* w, int64_t N, int64_t K, const 
                                  uint32_t* qweight3, float* scales, uint8_t* zeros,
                                  hipStream_t stream);
 
+// Compact deployment format: the fp32 step limited to [2^-24, 65504] and
+// rounded to binary16 before zero and codes; steps16 [N][G] binary16, zeros4
+// [N][ceil(G/2)] two per byte (even group low).  Codes as launch_quantize_pack
+// (4-bit containers, bits 3 or 4) or, int3_dense, as launch_quantize_pack3.
+hipError_t launch_quantize_pack16(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                                  int bits, bool int3_dense, uint32_t* qweight, uint16_t* steps16,
+                                  uint8_t* zeros4, hipStream_t stream);
+// Compact metadata -> fp32 steps and u8 zeros [N][G] (exact).
+hipError_t launch_expand_meta16(const uint16_t* steps16, const uint8_t* zeros4, int64_t N,
+                                int64_t G, float* scales, uint8_t* zeros, hipStream_t stream);
+
 // The search's bf16 weight operand for one candidate:
 // b_out[n][k] = bf16(f32(f32((q - z) * step) * inv_s[k])) (inv_s NULL: no factor).
 hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, const float* s,
@@ -120,6 +131,11 @@ hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K
                               const uint32_t* qweight, const float* scales, const uint8_t* zeros,
                               float* y, void* ws, hipStream_t stream, bool int3_dense = false,
                               bool tiled = false);
+// The decode contraction on decode tiles with the compact metadata.
+hipError_t launch_decode_gemm16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                const uint32_t* tiles, const uint16_t* steps16,
+                                const uint8_t* zeros4, float* y, void* ws, hipStream_t stream,
+                                bool int3_dense);
 // Decode tiles: rows 16b .. 16b+15 (zero past N) x group g as tile b*G + g,
 // row r's piece for channels 32q .. 32q+31 at byte P*(r + 16q) (P = 16 or 12).
 size_t decode_tiles_bytes(int64_t N, int64_t K, bool int3_dense);

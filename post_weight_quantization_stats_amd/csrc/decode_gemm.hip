@@ -67,8 +67,9 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 struct DecodeParams {
   const uint16_t* a;
   const uint32_t* qweight;
-  const float* scales;
-  const uint8_t* zeros;
+  const float* scales;        // fp32 steps [N][G] (unless H16)
+  const uint16_t* steps16;    // H16: binary16 steps [N][G]
+  const uint8_t* zeros;       // u8 [N][G], or H16: two per byte [N][ceil(G/2)]
   float* out;                 // y, or partials [splits][M][N]
   int64_t M, N, K;
   int64_t groups_per_split;
@@ -133,8 +134,9 @@ struct GroupLoads {
 };
 
 // NB 16-column blocks per workgroup (all of its waves work on them) and MB
-// 16-row blocks of tokens (M <= 16 * MB); I3: dense INT3 codes; TL: tiled.
-template <int NB, int MB, bool I3, bool TL>
+// 16-row blocks of tokens (M <= 16 * MB); I3: dense INT3 codes; TL: tiled;
+// H16: the compact metadata (binary16 steps, 4-bit zeros).
+template <int NB, int MB, bool I3, bool TL, bool H16 = false>
 __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int kCols = 16 * NB;
@@ -166,8 +168,10 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
   const int64_t row_blocks = (N + 15) / 16;
   const rsrc_t rq = TL ? make_rsrc(p.qweight, row_blocks * 16 * row_words * 4)
                        : make_rsrc(p.qweight + n_blk * row_words, (N - n_blk) * row_words * 4);
-  const rsrc_t rs = make_rsrc(p.scales + n_blk * G, (N - n_blk) * G * 4);
-  const rsrc_t rz = make_rsrc(p.zeros + n_blk * G, (N - n_blk) * G);
+  const int64_t zrow = H16 ? (G + 1) / 2 : G;                // zero bytes per row
+  const rsrc_t rs = H16 ? make_rsrc(p.steps16 + n_blk * G, (N - n_blk) * G * 2)
+                        : make_rsrc(p.scales + n_blk * G, (N - n_blk) * G * 4);
+  const rsrc_t rz = make_rsrc(p.zeros + n_blk * zrow, (N - n_blk) * zrow);
 
   // (step, zero) of the workgroup's kCols rows x this wave's gn groups:
   // element e -> row e / gn, group e % gn (consecutive lanes read consecutive
@@ -180,10 +184,17 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
     const int e = i * 64 + lane;
     const int row = gn > 0 ? e / gn : kCols, gl = gn > 0 ? e - row * gn : 0;
     const bool ok = row < kCols;
-    sz_step[i] = __builtin_amdgcn_raw_buffer_load_b32(
-        rs, ok ? (uint32_t)((row * G + g0 + gl) * 4) : 0xFFFFFFF0u, 0, 0);
-    sz_zero[i] = __builtin_amdgcn_raw_buffer_load_b8(
-        rz, ok ? (uint32_t)(row * G + g0 + gl) : 0xFFFFFFF0u, 0, 0);
+    if constexpr (H16) {
+      sz_step[i] = __builtin_amdgcn_raw_buffer_load_b16(
+          rs, ok ? (uint32_t)((row * G + g0 + gl) * 2) : 0xFFFFFFF0u, 0, 0);
+      sz_zero[i] = __builtin_amdgcn_raw_buffer_load_b8(
+          rz, ok ? (uint32_t)(row * zrow + (g0 + gl) / 2) : 0xFFFFFFF0u, 0, 0);
+    } else {
+      sz_step[i] = __builtin_amdgcn_raw_buffer_load_b32(
+          rs, ok ? (uint32_t)((row * G + g0 + gl) * 4) : 0xFFFFFFF0u, 0, 0);
+      sz_zero[i] = __builtin_amdgcn_raw_buffer_load_b8(
+          rz, ok ? (uint32_t)(row * G + g0 + gl) : 0xFFFFFFF0u, 0, 0);
+    }
   }
 
   // A lane's codes of group g: bytes 64g + 16*g4 (4-bit) or 48g + 12*g4 (INT3)
@@ -223,8 +234,15 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
   for (int i = 0; i < kSzIters; ++i) {
     const int e = i * 64 + lane;
     const int row = gn > 0 ? e / gn : kCols, gl = gn > 0 ? e - row * gn : 0;
-    if (row < kCols) ssz[wave][row][gl] = make_float2(__uint_as_float(sz_step[i]),
-                                                      128.f + (float)sz_zero[i]);
+    if (row < kCols) {
+      if constexpr (H16) {
+        const uint32_t zq = (sz_zero[i] >> (4 * ((g0 + gl) & 1))) & 15u;
+        ssz[wave][row][gl] = make_float2(
+            (float)__builtin_bit_cast(_Float16, (uint16_t)sz_step[i]), 128.f + (float)zq);
+      } else {
+        ssz[wave][row][gl] = make_float2(__uint_as_float(sz_step[i]), 128.f + (float)sz_zero[i]);
+      }
+    }
   }
   __syncthreads();
 
@@ -382,35 +400,33 @@ hipError_t launch_decode_tiles(const uint32_t* qweight, int64_t N, int64_t K, bo
   return hipGetLastError();
 }
 
-hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
-                              const uint32_t* qweight, const float* scales, const uint8_t* zeros,
-                              float* y, void* ws, hipStream_t stream, bool int3_dense,
-                              bool tiled) {
-  if (M == 0 || N == 0) return hipSuccess;
-  const DecodePlan d = decode_plan(M, N, K);
-  DecodeParams p;
-  p.a = a;
-  p.qweight = qweight;
-  p.scales = scales;
-  p.zeros = zeros;
-  p.out = d.splits > 1 ? (float*)ws : y;
-  p.M = M;
-  p.N = N;
-  p.K = K;
-  p.groups_per_split = d.groups_per_split;
+namespace {
+
+template <bool H16>
+hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* ws,
+                           hipStream_t stream, bool int3_dense, bool tiled) {
+  const int64_t M = p.M, N = p.N;
   const int nb = decode_blocks_per_group(M, N, d.splits);
   const int mb = (int)ceil_div(M, (int64_t)16);
   dim3 grid((unsigned)ceil_div(N, (int64_t)16 * nb), (unsigned)d.splits);
   auto go = [&](auto NBc, auto MBc) {
     constexpr int nbv = decltype(NBc)::value, mbv = decltype(MBc)::value;
-    if (int3_dense && tiled)
-      decode_gemm_kernel<nbv, mbv, true, true><<<grid, kThreads, 0, stream>>>(p);
-    else if (int3_dense)
-      decode_gemm_kernel<nbv, mbv, true, false><<<grid, kThreads, 0, stream>>>(p);
-    else if (tiled)
-      decode_gemm_kernel<nbv, mbv, false, true><<<grid, kThreads, 0, stream>>>(p);
-    else
-      decode_gemm_kernel<nbv, mbv, false, false><<<grid, kThreads, 0, stream>>>(p);
+    if constexpr (H16) {
+      // The compact metadata is read with tiled codes only.
+      if (int3_dense)
+        decode_gemm_kernel<nbv, mbv, true, true, true><<<grid, kThreads, 0, stream>>>(p);
+      else
+        decode_gemm_kernel<nbv, mbv, false, true, true><<<grid, kThreads, 0, stream>>>(p);
+    } else {
+      if (int3_dense && tiled)
+        decode_gemm_kernel<nbv, mbv, true, true><<<grid, kThreads, 0, stream>>>(p);
+      else if (int3_dense)
+        decode_gemm_kernel<nbv, mbv, true, false><<<grid, kThreads, 0, stream>>>(p);
+      else if (tiled)
+        decode_gemm_kernel<nbv, mbv, false, true><<<grid, kThreads, 0, stream>>>(p);
+      else
+        decode_gemm_kernel<nbv, mbv, false, false><<<grid, kThreads, 0, stream>>>(p);
+    }
   };
   auto go_mb = [&](auto NBc) {
     if (mb == 1)
@@ -432,6 +448,48 @@ hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K
         (const float*)ws, count, (int)d.splits, y);
   }
   return hipGetLastError();
+}
+
+DecodeParams decode_params(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                           const uint32_t* qweight, const DecodePlan& d, float* y, void* ws) {
+  DecodeParams p;
+  p.a = a;
+  p.qweight = qweight;
+  p.scales = nullptr;
+  p.steps16 = nullptr;
+  p.zeros = nullptr;
+  p.out = d.splits > 1 ? (float*)ws : y;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.groups_per_split = d.groups_per_split;
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                              const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                              float* y, void* ws, hipStream_t stream, bool int3_dense,
+                              bool tiled) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const DecodePlan d = decode_plan(M, N, K);
+  DecodeParams p = decode_params(a, M, N, K, qweight, d, y, ws);
+  p.scales = scales;
+  p.zeros = zeros;
+  return decode_dispatch<false>(p, d, y, ws, stream, int3_dense, tiled);
+}
+
+hipError_t launch_decode_gemm16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                const uint32_t* tiles, const uint16_t* steps16,
+                                const uint8_t* zeros4, float* y, void* ws, hipStream_t stream,
+                                bool int3_dense) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const DecodePlan d = decode_plan(M, N, K);
+  DecodeParams p = decode_params(a, M, N, K, tiles, d, y, ws);
+  p.steps16 = steps16;
+  p.zeros = zeros4;
+  return decode_dispatch<true>(p, d, y, ws, stream, int3_dense, true);
 }
 
 }  // namespace awq

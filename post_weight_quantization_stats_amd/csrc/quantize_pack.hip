@@ -52,7 +52,7 @@ __device__ __forceinline__ float markstein_div(float a, float b, float y) {
 
 // One lane's 16 channels of a group: their codes (as floats) and the group's
 // step and zero (identical in all 8 lanes of the group).
-template <int BITS>
+template <int BITS, bool kHalf = false>
 __device__ __forceinline__ void quantize16(const float (&ws)[16], float (&q)[16],
                                            float& step_out, float& z_out) {
   constexpr float qmax = (float)((1 << BITS) - 1);
@@ -73,6 +73,34 @@ __device__ __forceinline__ void quantize16(const float (&ws)[16], float (&q)[16]
   mn = fminf(mn, 0.f);
   const float range = mx - mn;
   const bool fast = range >= 0x1p-90f && range <= 0x1p100f;
+
+  if constexpr (kHalf) {
+    // Compact format: the fp32 step limited to [2^-24, 65504] and rounded to
+    // binary16 (v_cvt_f16_f32, nearest even); zero and codes use that step.
+    // It is >= 2^-24 (far above the bound above) and, below the upper limit,
+    // within a binary16 rounding of range / qmax, so the quotients keep the
+    // same correctly rounded fast path.
+    float step = fast ? markstein_div(range, qmax, inv_qmax) : range / qmax;
+    if (!(step > 0.f)) step = 1.f;
+    step = (float)(_Float16)fminf(fmaxf(step, 0x1p-24f), 65504.f);
+    const float y = 1.0f / step;
+    float zq = markstein_div(-mn, step, y);
+    float qt[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) qt[j] = markstein_div(ws[j], step, y);
+    if (__builtin_expect(!fast, 0)) {
+      asm volatile("" ::: "memory");
+      zq = -mn / step;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) qt[j] = ws[j] / step;
+    }
+    const float z = fminf(fmaxf(rintf(zq), 0.f), qmax);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) q[j] = fminf(fmaxf(rintf(qt[j]) + z, 0.f), qmax);
+    step_out = step;
+    z_out = z;
+    return;
+  }
 
   float step = markstein_div(range, qmax, inv_qmax);
   float y = 1.0f / step;
@@ -143,12 +171,16 @@ __device__ __forceinline__ void pack48(const float (&q)[16], uint32_t& lo, uint3
   }
 }
 
-template <int BITS, int kMode>
+// kHalf (code modes only): the compact format, binary16 steps in steps16
+// [N][G] and zeros two per byte in zeros [N][ceil(G/2)] (even group in the
+// low nibble; the high nibble past the last group is 0).
+template <int BITS, int kMode, bool kHalf = false>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t K, const float* __restrict__ s,
     const int32_t* __restrict__ s_sel, const float* __restrict__ inv_s,
     uint32_t* __restrict__ qweight, float* __restrict__ scales, uint8_t* __restrict__ zeros,
-    uint16_t* __restrict__ bout, float* __restrict__ dout) {
+    uint16_t* __restrict__ bout, float* __restrict__ dout, uint16_t* __restrict__ steps16) {
+  static_assert(!kHalf || writes_codes(kMode), "the compact format is a code mode");
   const int64_t G = K / kGroup;
   const int64_t g = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x / kLanesPerGroup);
   const int t8 = threadIdx.x % kLanesPerGroup;
@@ -199,7 +231,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       for (int j = 0; j < 16; ++j) ws[j] *= sv[j];
     }
     float q[16], step, z;
-    quantize16<BITS>(ws, q, step, z);
+    quantize16<BITS, kHalf>(ws, q, step, z);
+    // The zero of the neighbouring group (lanes ^ 8: same row, group g ^ 1).
+    uint32_t z_next = 0u;
+    if constexpr (kHalf) z_next = (uint32_t)__shfl_xor((int)z, kLanesPerGroup);
     uint32_t p_lo = 0, p_hi = 0, o_lo = 0, o_hi = 0;
     if constexpr (kMode == kPack3) {
       // Lanes 2m and 2m+1 hold the two halves of one 32-code run; the even
@@ -268,14 +303,58 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         *(uint2*)(qweight + n * (K / 8) + k0 / 8) = make_uint2(pack8(q), pack8(q + 8));
       }
       if (t8 == 0) {
-        scales[n * G + g] = step;
-        zeros[n * G + g] = (uint8_t)z;
+        if constexpr (kHalf) {
+          steps16[n * G + g] = __builtin_bit_cast(uint16_t, (_Float16)step);   // exact
+          if ((g & 1) == 0)
+            zeros[n * ((G + 1) / 2) + g / 2] = (uint8_t)((uint32_t)z | (g + 1 < G ? z_next << 4 : 0u));
+        } else {
+          scales[n * G + g] = step;
+          zeros[n * G + g] = (uint8_t)z;
+        }
       }
     }
   }
 }
 
+// Compact metadata -> fp32 steps and u8 zeros, one thread per (row, group).
+__global__ __launch_bounds__(256) void expand_meta16_kernel(const uint16_t* __restrict__ steps16,
+                                                            const uint8_t* __restrict__ zeros4,
+                                                            int64_t N, int64_t G,
+                                                            float* __restrict__ scales,
+                                                            uint8_t* __restrict__ zeros) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= N * G) return;
+  const int64_t n = i / G, g = i - n * G;
+  scales[i] = (float)__builtin_bit_cast(_Float16, steps16[i]);
+  zeros[i] = (uint8_t)((zeros4[n * ((G + 1) / 2) + g / 2] >> (4 * (g & 1))) & 15);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_pack16(const uint16_t* w, int64_t N, int64_t K, const float* s,
+                                  int bits, bool int3_dense, uint32_t* qweight, uint16_t* steps16,
+                                  uint8_t* zeros4, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
+  if (int3_dense)
+    quantize_kernel<3, kPack3, true><<<grid, kThreads, 0, stream>>>(
+        w, N, K, s, nullptr, nullptr, qweight, nullptr, zeros4, nullptr, nullptr, steps16);
+  else if (bits == 4)
+    quantize_kernel<4, kPack, true><<<grid, kThreads, 0, stream>>>(
+        w, N, K, s, nullptr, nullptr, qweight, nullptr, zeros4, nullptr, nullptr, steps16);
+  else
+    quantize_kernel<3, kPack, true><<<grid, kThreads, 0, stream>>>(
+        w, N, K, s, nullptr, nullptr, qweight, nullptr, zeros4, nullptr, nullptr, steps16);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_meta16(const uint16_t* steps16, const uint8_t* zeros4, int64_t N,
+                                int64_t G, float* scales, uint8_t* zeros, hipStream_t stream) {
+  if (N == 0 || G == 0) return hipSuccess;
+  expand_meta16_kernel<<<(unsigned)ceil_div(N * G, (int64_t)256), 256, 0, stream>>>(
+      steps16, zeros4, N, G, scales, zeros);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const float* s,
                                 const int32_t* s_sel, int bits, uint32_t* qweight,
@@ -284,10 +363,10 @@ hipError_t launch_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const f
   dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
   if (bits == 4)
     quantize_kernel<4, kPack><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, nullptr, qweight,
-                                                             scales, zeros, nullptr, nullptr);
+                                                             scales, zeros, nullptr, nullptr, nullptr);
   else
     quantize_kernel<3, kPack><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, nullptr, qweight,
-                                                             scales, zeros, nullptr, nullptr);
+                                                             scales, zeros, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -297,7 +376,7 @@ hipError_t launch_quantize_pack3(const uint16_t* w, int64_t N, int64_t K, const 
   if (N == 0) return hipSuccess;
   dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
   quantize_kernel<3, kPack3><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, nullptr, qweight3,
-                                                            scales, zeros, nullptr, nullptr);
+                                                            scales, zeros, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -308,10 +387,10 @@ hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, cons
   dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
   if (bits == 4)
     quantize_kernel<4, kOperand><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
-                                                                nullptr, nullptr, b_out, nullptr);
+                                                                nullptr, nullptr, b_out, nullptr, nullptr);
   else
     quantize_kernel<3, kOperand><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
-                                                                nullptr, nullptr, b_out, nullptr);
+                                                                nullptr, nullptr, b_out, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -322,10 +401,10 @@ hipError_t launch_quantize_diff_operand(const uint16_t* w, int64_t N, int64_t K,
   dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
   if (bits == 4)
     quantize_kernel<4, kDiffOp><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
-                                                               nullptr, nullptr, d_out, nullptr);
+                                                               nullptr, nullptr, d_out, nullptr, nullptr);
   else
     quantize_kernel<3, kDiffOp><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
-                                                               nullptr, nullptr, d_out, nullptr);
+                                                               nullptr, nullptr, d_out, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -336,10 +415,10 @@ hipError_t launch_quantize_diff(const uint16_t* w, int64_t N, int64_t K, const f
   dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
   if (bits == 4)
     quantize_kernel<4, kDiff><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
-                                                             nullptr, nullptr, a_split, d32);
+                                                             nullptr, nullptr, a_split, d32, nullptr);
   else
     quantize_kernel<3, kDiff><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
-                                                             nullptr, nullptr, a_split, d32);
+                                                             nullptr, nullptr, a_split, d32, nullptr);
   return hipGetLastError();
 }
 

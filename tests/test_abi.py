@@ -322,3 +322,40 @@ def test_block_op_errors():
     assert lib.awq_residual_add(FAKE, None, 4, 128, FAKE, None) == NULL
     assert lib.awq_residual_add(FAKE, FAKE, 4, 12, FAKE, None) == SHAPE
     assert lib.awq_residual_add(FAKE, FAKE_MIS, 4, 128, FAKE, None) == ALIGN
+
+
+def test_compact_format_entry_errors():
+    lib = awq.lib()
+    pk = lib.awq_quantize_pack16
+
+    def pack(w=FAKE, N=4, K=256, s=None, bits=4, group=128, layout=0, q=FAKE, st=FAKE, z=FAKE):
+        return pk(w, N, K, s, bits, group, layout, q, st, z, None)
+
+    assert pack(w=None) == NULL and pack(st=None) == NULL and pack(z=None) == NULL
+    assert pack(layout=2) == UNSUPPORTED
+    assert pack(layout=1, bits=4) == UNSUPPORTED
+    assert pack(bits=5) == UNSUPPORTED and pack(group=64) == UNSUPPORTED
+    assert pack(K=100) == SHAPE and pack(N=-1) == SHAPE
+    assert pack(st=FAKE + 1) == ALIGN
+    assert pack(q=FAKE + 4) == ALIGN                  # nibble codes: 16-byte
+    assert pack(w=FAKE_MIS) == ALIGN
+    assert pack(N=0, w=None, q=None, st=None, z=None) == OK
+    ex = lib.awq_expand_meta16
+    assert ex(None, FAKE, 4, 256, 128, FAKE, FAKE, None) == NULL
+    assert ex(FAKE, FAKE, 4, 100, 128, FAKE, FAKE, None) == SHAPE
+    assert ex(FAKE + 1, FAKE, 4, 256, 128, FAKE, FAKE, None) == ALIGN
+    assert ex(FAKE, FAKE, 4, 256, 128, FAKE + 2, FAKE, None) == ALIGN
+    assert ex(None, None, 0, 256, 128, None, None, None) == OK
+    f = lib.awq_decode_gemm_tiled16
+
+    def dec(a=FAKE, M=4, N=128, K=4096, t=FAKE, st=FAKE, z=FAKE, layout=0, group=128, y=FAKE,
+            ws=None, wsb=0):
+        return f(a, M, N, K, t, st, z, layout, group, y, ws, wsb, None)
+
+    assert dec(layout=5) == UNSUPPORTED
+    assert dec(st=None) == NULL and dec(a=None) == NULL and dec(z=None) == NULL
+    assert dec(M=65) == SHAPE and dec(K=100) == SHAPE
+    assert dec(st=FAKE + 1) == ALIGN and dec(t=FAKE + 4) == ALIGN
+    assert dec(K=32768) == WORKSPACE
+    assert dec(N=1 << 22, K=1 << 13, ws=FAKE, wsb=1 << 40) == SHAPE
+    assert dec(M=0) == OK and dec(N=0) == OK
