@@ -288,7 +288,8 @@ def _graph_time_ms(fn, reps: int, stream) -> float:
 def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
     """Decode-shaped W4A16 contraction on the Llama-3-8B block's layers
     (M = 1, 16 and 64 tokens, random packed INT4 weights), on decode tiles
-    (the deployment path) and on the row-major packed words.  Launches cycle
+    (the deployment path), on the row-major packed words, and on decode
+    tiles with the compact metadata (binary16 steps, 4-bit zeros).  Launches cycle
     through enough copies of the packed weights (>= 768 MiB in all) that each
     one streams from HBM rather than the 256 MiB last-level cache."""
     import torch
@@ -307,7 +308,9 @@ def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
                                generator=gen)
             sc = torch.rand((N, K // 128), device=dev, generator=gen) * 0.003 + 0.001
             ze = torch.randint(0, 16, (N, K // 128), dtype=torch.uint8, device=dev, generator=gen)
-            packs.append((qw, awq.decode_tiles(qw, K), sc, ze))
+            z4 = torch.randint(0, 256, (N, (K // 128 + 1) // 2), dtype=torch.uint8, device=dev,
+                               generator=gen)
+            packs.append((qw, awq.decode_tiles(qw, K), sc, ze, sc.half(), z4))
         for M in (1, 16, 64):
             a = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -315,21 +318,32 @@ def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
             ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
             def tiled(i):
-                _, tl, sc, ze = packs[i % copies]
+                _, tl, sc, ze, _, _ = packs[i % copies]
                 awq.decode_gemm_tiled(a, tl, sc, ze, awq.LAYOUT_NIBBLE, out=y, workspace=ws)
 
             def row_major(i):
-                qw, _, sc, ze = packs[i % copies]
+                qw, _, sc, ze, _, _ = packs[i % copies]
                 awq.decode_gemm(a, qw, sc, ze, 4, out=y, workspace=ws)
+
+            def compact(i):
+                _, tl, _, _, st16, z4 = packs[i % copies]
+                awq.decode_gemm_tiled16(a, tl, st16, z4, awq.LAYOUT_NIBBLE, out=y, workspace=ws)
             ms = _graph_time_ms(tiled, reps, stream)
             ms_rm = _graph_time_ms(row_major, reps, stream)
-            nbytes = wbytes + 2.0 * M * K + 4.0 * M * N
+            ms_c = _graph_time_ms(compact, reps, stream)
+            io = 2.0 * M * K + 4.0 * M * N
+            nbytes = wbytes + io
             gbs = nbytes / (ms * 1e-3) / 1e9
+            cbytes = N * K / 2 + 2.5 * N * K / 128 + io
+            cgbs = cbytes / (ms_c * 1e-3) / 1e9
             out[f"{name}_M{M}"] = {"N": N, "K": K, "us": ms * 1e3, "gbs": gbs,
                                    "frac_hbm_peak": gbs / PEAK_HBM_GBS, "bytes": nbytes,
-                                   "row_major_us": ms_rm * 1e3, "weight_copies": copies}
+                                   "row_major_us": ms_rm * 1e3, "compact_us": ms_c * 1e3,
+                                   "compact_bytes": cbytes, "compact_gbs": cgbs,
+                                   "weight_copies": copies}
             log(f"decode {name} M={M} N={N} K={K}: tiles {ms * 1e3:.2f} us = {gbs:.0f} GB/s; "
-                f"row-major {ms_rm * 1e3:.2f} us ({copies} weight copies)")
+                f"row-major {ms_rm * 1e3:.2f} us; compact metadata {ms_c * 1e3:.2f} us = "
+                f"{cgbs:.0f} GB/s ({copies} weight copies)")
         del packs
         torch.cuda.empty_cache()
     return out
