@@ -43,8 +43,10 @@ contract the GPU library implements):
                    zero and the codes are computed; steps stored as binary16
                    [N][G], zeros two per byte (even group in the low nibble)
                    [N][ceil(G/2)]
-  decode tiles     the words of rows 16b..16b+15 and group g as tile b*G+g,
-                   row r's piece for channels 32q.. at byte P*(r + 16q)
+  decode tiles     the codes of rows 16b..16b+15 and group g as tile b*G+g,
+                   row r's piece for channels 32q.. at byte P*(r + 16q);
+                   inside a piece channels 2p, 2p+1 form pair p, placed
+                   for a one-mask lift into a 32-bit word's two halves
   dequantized B    B[n,k] = bf16( f32( f32((q - z) * step) * inv_s[k] ) )
                    (1/s folded into the weight operand; the activation operand
                    is the caller's bf16 X, unchanged)
@@ -369,22 +371,45 @@ def unpack3(qweight3):
 
 
 def decode_tiles(qweight, K: int, dense3: bool = False, group: int = 128) -> np.ndarray:
-    """The packed words rearranged for streaming by 16-row blocks (a layout of
+    """The packed codes rearranged for streaming by 16-row blocks (a layout of
     this library, for the deployment contraction): rows 16b .. 16b+15 (zero
-    rows past N) and one group g form tile b*G + g; inside it the P bytes of
-    row r covering the group's channels 32q .. 32q+31 sit at byte P*(r + 16q),
-    with P = 16 for 4-bit containers and 12 for dense INT3.  Returns bytes,
-    uint8 [ceil(N/16) * G * 16 * 4P]."""
-    w = np.ascontiguousarray(np.asarray(qweight, dtype="<u4"))
-    N = w.shape[0]
+    rows past N) and one group g form tile b*G + g; inside it the P-byte
+    piece of row r covering the group's channels 32q .. 32q+31 sits at byte
+    P*(r + 16q), with P = 16 for 4-bit containers and 12 for dense INT3.
+    Inside a piece, channels 2p and 2p+1 form pair p (p = 0..15), placed so
+    that one mask lifts a pair into the two halves of a 32-bit word:
+      4-bit containers: u32 word j holds pairs 4j..4j+3, pair 4j+t's first
+        code in nibble t and its second in nibble 4+t;
+      dense INT3: pair p < 15 sits in u32 word p // 5, first code at bits
+        3(p % 5), second at bits 16 + 3(p % 5); pair 15 is spread over the
+        free bits: bit i of channel 30's code at bit 15 of word i, bit i of
+        channel 31's code at bit 31 of word i.
+    Returns bytes (little-endian words), uint8 [ceil(N/16) * G * 16 * 4P]."""
+    codes = unpack3(qweight) if dense3 else unpack(qweight)
+    N = codes.shape[0]
     G = K // group
-    P = 12 if dense3 else 16
-    rows = w.view(np.uint8).reshape(N, G, 4, P)            # [n][g][q][P bytes]
     NB = -(-N // 16)
-    padded = np.zeros((NB * 16, G, 4, P), dtype=np.uint8)
-    padded[:N] = rows
-    t = padded.reshape(NB, 16, G, 4, P).transpose(0, 2, 3, 1, 4)   # [b][g][q][r][P]
-    return np.ascontiguousarray(t).reshape(-1)
+    c = np.zeros((NB * 16, K), dtype=np.uint64)
+    c[:N] = codes
+    pieces = c.reshape(NB, 16, G, 4, 32)                  # [b][r][g][q][channel]
+    first, second = pieces[..., 0::2], pieces[..., 1::2]  # [b][r][g][q][pair]
+    if dense3:
+        words = np.zeros(pieces.shape[:4] + (3,), dtype=np.uint64)
+        for p in range(15):
+            sh = np.uint64(3 * (p % 5))
+            words[..., p // 5] |= (first[..., p] << sh) | (second[..., p] << (sh + np.uint64(16)))
+        for i in range(3):
+            bit = np.uint64(i)
+            words[..., i] |= (((first[..., 15] >> bit) & np.uint64(1)) << np.uint64(15)) | \
+                             (((second[..., 15] >> bit) & np.uint64(1)) << np.uint64(31))
+    else:
+        words = np.zeros(pieces.shape[:4] + (4,), dtype=np.uint64)
+        for j in range(4):
+            for t in range(4):
+                words[..., j] |= (first[..., 4 * j + t] << np.uint64(4 * t)) | \
+                                 (second[..., 4 * j + t] << np.uint64(16 + 4 * t))
+    t = words.transpose(0, 2, 3, 1, 4)                    # [b][g][q][r][word]
+    return np.ascontiguousarray(t.astype("<u4")).reshape(-1).view(np.uint8)
 
 
 def packed3_bytes(N: int, K: int, group: int) -> int:

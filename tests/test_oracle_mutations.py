@@ -122,6 +122,17 @@ def _mut_pack3_runs_of_16(mp):
 
 def _mut_tiles_row_major_inside(mp):
     """Pieces inside a tile ordered row by row (r*4 + q) instead of lane order."""
+    orig = OA.decode_tiles
+
+    def tiles(qweight, K, dense3=False, group=128):
+        t = orig(qweight, K, dense3, group)
+        P = 12 if dense3 else 16
+        return np.ascontiguousarray(t.reshape(-1, 4, 16, P).transpose(0, 2, 1, 3)).reshape(-1)
+    mp.setattr(oracle, "decode_tiles", tiles)
+
+
+def _mut_tiles_codes_in_pack_order(mp):
+    """Pieces copied from the packed words unchanged (no pairing inside)."""
     def tiles(qweight, K, dense3=False, group=128):
         w = np.ascontiguousarray(np.asarray(qweight, dtype="<u4"))
         N = w.shape[0]
@@ -130,7 +141,7 @@ def _mut_tiles_row_major_inside(mp):
         NB = -(-N // 16)
         padded = np.zeros((NB * 16, G, 4, P), dtype=np.uint8)
         padded[:N] = rows
-        return np.ascontiguousarray(padded.reshape(NB, 16, G, 4, P).transpose(0, 2, 1, 3, 4)).reshape(-1)
+        return np.ascontiguousarray(padded.reshape(NB, 16, G, 4, P).transpose(0, 2, 3, 1, 4)).reshape(-1)
     mp.setattr(oracle, "decode_tiles", tiles)
 
 
@@ -197,7 +208,7 @@ MUTATIONS = [_mut_floor_instead_of_rint, _mut_drop_inv_s, _mut_alpha_grid_closed
              _mut_no_range_extension, _mut_stats_mean_without_abs, _mut_normaliser_max_only,
              _mut_decode_zero_of_first_group, _mut_decode_rounds_weight_to_bf16, _mut_diff_sign,
              _mut_diff_off_by_half_ulp, _mut_pack3_code_bits_reversed, _mut_pack3_runs_of_16,
-             _mut_tiles_row_major_inside, _mut_rmsnorm_without_mean, _mut_silu_is_sigmoid,
+             _mut_tiles_row_major_inside, _mut_tiles_codes_in_pack_order, _mut_rmsnorm_without_mean, _mut_silu_is_sigmoid,
              _mut_fold_multiplies, _mut_f16_ties_away, _mut_quantize16_codes_with_fp32_step,
              _mut_zero_nibbles_swapped, _mut_half_step_no_clamp]
 
@@ -217,6 +228,7 @@ PINS = [
     P.test_pack3_worked_words,
     P.test_pack3_big_integer_brute_force,
     lambda: P.test_decode_tiles_brute_force(False),
+    lambda: P.test_decode_tiles_brute_force(True),
     P.test_rmsnorm_closed_form_and_scaling,
     P.test_silu_mul_against_torch_and_identities,
     P.test_divide_rows_and_residual_against_library,

@@ -342,15 +342,23 @@ def test_dense_int3_storage_and_product():
 
 @pytest.mark.parametrize("dense3", [False, True])
 def test_decode_tiles_brute_force(dense3):
-    """Every byte of the tile layout, found by walking the definition: tile
-    b*G + g holds rows 16b .. 16b+15 of group g, row r's piece for channels
-    32q .. 32q+31 at byte P*(r + 16q); rows past N are zero."""
+    """Every byte of the tile layout, found by walking the definition in pure
+    Python: tile b*G + g holds rows 16b .. 16b+15 of group g, row r's piece
+    for channels 32q .. 32q+31 at byte P*(r + 16q), rows past N zero; inside
+    a piece, pair p = (channel 2p, channel 2p+1) goes to nibbles (t, 4+t) of
+    word j for p = 4j + t (4-bit containers) or to bits (3(p%5), 16+3(p%5))
+    of word p//5, pair 15 to bits 15 and 31 of the three words (dense INT3).
+    The codes are read from the packed words bit by bit."""
     rng = np.random.default_rng(41)
     N, K = 37, 384
     G, P = K // 128, (12 if dense3 else 16)
-    words = 3 * K // 32 if dense3 else K // 8
-    qw = rng.integers(0, 2 ** 32, size=(N, words), dtype=np.uint64).astype(np.uint32)
-    raw = qw.astype("<u4").view(np.uint8).reshape(N, words * 4)
+    nwords = 3 * K // 32 if dense3 else K // 8
+    qw = rng.integers(0, 2 ** 32, size=(N, nwords), dtype=np.uint64).astype(np.uint32)
+    if dense3:
+        big = [int.from_bytes(qw[n].astype("<u4").tobytes(), "little") for n in range(N)]
+        code = lambda n, k: (big[n] >> (3 * k)) & 7
+    else:
+        code = lambda n, k: (int(qw[n, k // 8]) >> (4 * (k % 8))) & 15
     tiles = O.decode_tiles(qw, K, dense3)
     NB = -(-N // 16)
     assert tiles.size == NB * G * 64 * P
@@ -359,9 +367,20 @@ def test_decode_tiles_brute_force(dense3):
             for q in range(4):
                 for r in range(16):
                     n = 16 * b + r
-                    got = tiles[(b * G + g) * 64 * P + P * (r + 16 * q):][:P]
-                    want = raw[n, g * 4 * P + q * P:][:P] if n < N else np.zeros(P, np.uint8)
-                    assert np.array_equal(got, want), (b, g, q, r)
+                    c = [code(n, 128 * g + 32 * q + i) if n < N else 0 for i in range(32)]
+                    words = [0] * (P // 4)
+                    for p in range(16):
+                        lo, hi = c[2 * p], c[2 * p + 1]
+                        if not dense3:
+                            words[p // 4] |= (lo << (4 * (p % 4))) | (hi << (16 + 4 * (p % 4)))
+                        elif p < 15:
+                            words[p // 5] |= (lo << (3 * (p % 5))) | (hi << (16 + 3 * (p % 5)))
+                        else:
+                            for i in range(3):
+                                words[i] |= (((lo >> i) & 1) << 15) | (((hi >> i) & 1) << 31)
+                    want = b"".join(w.to_bytes(4, "little") for w in words)
+                    got = tiles[(b * G + g) * 64 * P + P * (r + 16 * q):][:P].tobytes()
+                    assert got == want, (b, g, q, r)
 
 
 def test_storage_about_four_times_smaller():
