@@ -34,6 +34,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source additions.  decode_gemm.hip: the matrix-core accumulators live in
+# ordinary VGPRs (the fold after every group reads them; in AGPRs each read is
+# an extra v_accvgpr_read per element).
+SOURCE_FLAGS = {
+    "decode_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -42,7 +50,8 @@ def hipcc() -> str:
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [hipcc(), *COMMON_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

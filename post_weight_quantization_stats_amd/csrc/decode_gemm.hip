@@ -35,13 +35,17 @@
 // fragment feed more codes, which pays when M is large or the layer is wide
 // enough to keep every CU busy anyway (the rule in decode_blocks_per_group
 // was measured on the Llama-3-8B block's layers).
-// Tiled weights (TL): the packed words rearranged once so that a wave's
+// Tiled weights (TL): the packed codes rearranged once so that a wave's
 // code load for one 16-column block and one group is a single contiguous
 // 1 KiB (768 B for dense INT3) piece in lane order: tile b*G + g holds rows
 // 16b .. 16b+15 of group g, row r's piece for channels 32q .. 32q+31 at byte
 // P*(r + 16q).  Row-strided loads touch 16 cache lines for 64 useful bytes
 // each; the tiles stream whole lines in order (10-27% faster from HBM on the
-// largest layers).
+// largest layers).  Inside a piece channels 2p and 2p+1 (pair p) sit where
+// one mask lifts them into the two bf16 halves of a word (nibbles t and 4+t
+// of word p/4; dense INT3: bits 3t and 16+3t of word p/5, t = p%5, pair 15
+// in bits 15 and 31 of the three words), so the MFMA slots hold channels in
+// their natural order and the activations are used as loaded.
 // The activations come from L2 (every workgroup reads the same few KiB).  The
 // (step, 128 + zero) pairs of a wave's rows and groups are loaded into an LDS
 // table up front, one distinct element per lane: loaded per group and per
@@ -96,12 +100,15 @@ __device__ __forceinline__ bf16x8 permute_a(uint4 d) {
 }
 
 // Eight codes (code i at bits 4i) -> bf16 128 + code in slots 0,4,1,5,2,6,3,7.
-__device__ __forceinline__ bf16x8 codes_b(uint32_t w) {
+// kc = 0x43004300 (bf16 128 in both halves), held in a VGPR: with the mask
+// in an SGPR each mask-and-or is then one v_and_or_b32 (a VOP3 takes no
+// literal here, and only one scalar operand).
+__device__ __forceinline__ bf16x8 codes_b(uint32_t w, uint32_t kc) {
   u32x4 r;
-  r.x = (w & 0x000F000Fu) | 0x43004300u;
-  r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  r.x = (w & 0x000F000Fu) | kc;
+  r.y = ((w >> 4) & 0x000F000Fu) | kc;
+  r.z = ((w >> 8) & 0x000F000Fu) | kc;
+  r.w = ((w >> 12) & 0x000F000Fu) | kc;
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -116,6 +123,20 @@ __device__ __forceinline__ uint32_t spread3(uint32_t f) {
 __device__ __forceinline__ uint4 nibbles_from_int3(uint4 v) {
   return make_uint4(spread3(v.x & 0xFFFFFFu), spread3((v.x >> 24) | ((v.y & 0xFFFFu) << 8)),
                     spread3((v.y >> 16) | ((v.z & 0xFFu) << 16)), spread3(v.z >> 8));
+}
+
+// A dense-INT3 tile piece (three words) -> the four bf16x8 operands of its
+// 32 channels in natural order: pair p as bf16 (128 + code) halves.
+__device__ __forceinline__ void lift_pairs3(uint4 v, bf16x8 (&out)[4], uint32_t kc) {
+  const uint32_t w[3] = {v.x, v.y, v.z};
+  uint32_t r[16];
+#pragma unroll
+  for (int p = 0; p < 15; ++p) r[p] = ((w[p / 5] >> (3 * (p % 5))) & 0x00070007u) | kc;
+  r[15] = ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) |
+          ((w[2] >> 13) & 0x00040004u) | kc;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    out[j] = __builtin_bit_cast(bf16x8, u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]});
 }
 
 __device__ __forceinline__ uint4 ld12(rsrc_t r, uint32_t voff) {
@@ -246,6 +267,8 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
   }
   __syncthreads();
 
+  uint32_t kc;   // see codes_b; an opaque VGPR value, so it is not folded back into a literal
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(kc));
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
                                                        0x3F803F80u});
   f32x4 y[MB][NB];
@@ -260,17 +283,31 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
     float2 sz[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const uint4 qw = I3 ? nibbles_from_int3(L.q[b]) : L.q[b];
-      const uint32_t words[4] = {qw.x, qw.y, qw.z, qw.w};
+      if constexpr (I3 && TL) {
+        lift_pairs3(L.q[b], bq[b], kc);
+      } else {
+        // Row-major words: codes k and k+4 of each word pair up (slot order
+        // 0,4,1,5,2,6,3,7, matched by permute_a).  Tiles: the pairs are
+        // channels 2p, 2p+1 (natural order).
+        const uint4 qw = I3 ? nibbles_from_int3(L.q[b]) : L.q[b];
+        const uint32_t words[4] = {qw.x, qw.y, qw.z, qw.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bq[b][j] = codes_b(words[j]);
+        for (int j = 0; j < 4; ++j) bq[b][j] = codes_b(words[j], kc);
+      }
       sz[b] = ssz[wave][b * 16 + c16][gl];
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       bf16x8 af[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) af[j] = permute_a(L.a[mb][j]);
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (TL) {
+          const uint4 d = L.a[mb][j];
+          af[j] = __builtin_bit_cast(bf16x8, u32x4{d.x, d.y, d.z, d.w});
+        } else {
+          af[j] = permute_a(L.a[mb][j]);
+        }
+      }
       f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};             // sum A, rows 16mb + 4*g4 .. +3
 #pragma unroll
       for (int j = 0; j < 4; ++j) sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], ones, sa, 0, 0, 0);
@@ -332,6 +369,11 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
 }
 
 // Decode tiles from row-major packed words: one thread per W-word piece.
+// 4-bit containers (W = 4): each word's nibbles 0..7 (channels 8j .. 8j+7)
+// go to nibbles 0,4,1,5,2,6,3,7, so channels 2p, 2p+1 land in nibbles t,
+// 4+t.  Dense INT3 (W = 3): the piece's 32 codes (code i at bit 3i of the
+// 96-bit run) are re-placed by pair: pair p < 15 at bits 3(p%5) and
+// 16 + 3(p%5) of word p/5, pair 15 bit by bit in bits 15 and 31.
 template <int W>
 __global__ __launch_bounds__(256) void decode_tiles_kernel(const uint32_t* __restrict__ qw,
                                                            int64_t N, int64_t G,
@@ -345,8 +387,35 @@ __global__ __launch_bounds__(256) void decode_tiles_kernel(const uint32_t* __res
   uint32_t v[W];
 #pragma unroll
   for (int i = 0; i < W; ++i) v[i] = n < N ? qw[n * row_words + (g * 4 + q) * W + i] : 0u;
+  uint32_t o[W];
+  if constexpr (W == 4) {
 #pragma unroll
-  for (int i = 0; i < W; ++i) tiles[e * W + i] = v[i];
+    for (int j = 0; j < 4; ++j) {
+      uint32_t x = 0u;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        x |= ((v[j] >> (8 * u)) & 0xFu) << (4 * u) | ((v[j] >> (8 * u + 4)) & 0xFu) << (16 + 4 * u);
+      o[j] = x;
+    }
+  } else {
+    const uint64_t lo = (uint64_t)v[0] | ((uint64_t)v[1] << 32);
+    const uint64_t hi = v[2];
+    auto code = [&](int i) -> uint32_t {
+      const int bit = 3 * i;
+      if (bit + 3 <= 64) return (uint32_t)(lo >> bit) & 7u;
+      if (bit >= 64) return (uint32_t)(hi >> (bit - 64)) & 7u;
+      return (uint32_t)((lo >> bit) | (hi << (64 - bit))) & 7u;   // straddles bit 64
+    };
+    o[0] = o[1] = o[2] = 0u;
+#pragma unroll
+    for (int p = 0; p < 15; ++p)
+      o[p / 5] |= code(2 * p) << (3 * (p % 5)) | code(2 * p + 1) << (16 + 3 * (p % 5));
+    const uint32_t c30 = code(30), c31 = code(31);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) o[i] |= ((c30 >> i) & 1u) << 15 | ((c31 >> i) & 1u) << 31;
+  }
+#pragma unroll
+  for (int i = 0; i < W; ++i) tiles[e * W + i] = o[i];
 }
 
 // y[i] = sum over s of part[s][i], s ascending.
