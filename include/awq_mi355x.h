@@ -288,7 +288,11 @@ awq_status awq_w3a16_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_
  * zero) form tile b*G + g; inside it, row r's piece covering the group's
  * channels 32q .. 32q+31 (P = 16 bytes for AWQ_LAYOUT_NIBBLE, 12 for
  * AWQ_LAYOUT_INT3_DENSE) sits at byte P*(r + 16q), so one wave's load of a
- * tile is one contiguous piece in lane order.
+ * tile is one contiguous piece in lane order.  Inside a piece channels 2p
+ * and 2p+1 form pair p: AWQ_LAYOUT_NIBBLE puts pair 4j+t in nibbles t and
+ * 4+t of u32 word j; AWQ_LAYOUT_INT3_DENSE puts pair p < 15 at bits 3(p%5)
+ * and 16+3(p%5) of word p/5, and bit i of channel 30's and 31's codes at
+ * bits 15 and 31 of word i.
  *   awq_decode_tiles_size: *bytes = ceil(N/16) * 16 * (K/2 or 3K/8).
  *   awq_decode_tiles: qweight as written by awq_quantize_pack (layout
  *     NIBBLE, any bits) or awq_quantize_pack3 (INT3_DENSE), 4-byte aligned;
