@@ -82,12 +82,18 @@ KERNEL_LABELS = [
     ("gemm_kernel<false, false, 4, true, false", "reference_gemm / Gram matrix (bf16, fp32 out)"),
     ("gemm_kernel<true, true, 2, false, true", "w4a16_gemm_sse (INT4 operand, 1/s folded, SSE epilogue)"),
     ("gemm_kernel<true", "w4a16_gemm (INT4 operand, other epilogues)"),
-    ("quantize_kernel<4, 1>", "dequant_operand (quantize -> bf16 B)"),
-    ("quantize_kernel<3, 1>", "dequant_operand (quantize -> bf16 B)"),
-    ("quantize_kernel<4, 2>", "Gram-form quantize (split D, fp32 D)"),
-    ("quantize_kernel<3, 2>", "Gram-form quantize (split D, fp32 D)"),
-    ("quantize_kernel<4, 3>", "diff_operand (quantize -> bf16 B - W)"),
-    ("quantize_kernel<3, 3>", "diff_operand (quantize -> bf16 B - W)"),
+    ("quantize_kernel<4, 1,", "dequant_operand (quantize -> bf16 B)"),
+    ("quantize_kernel<3, 1,", "dequant_operand (quantize -> bf16 B)"),
+    ("quantize_kernel<4, 2,", "Gram-form quantize (split D, fp32 D)"),
+    ("quantize_kernel<3, 2,", "Gram-form quantize (split D, fp32 D)"),
+    ("quantize_kernel<4, 3,", "diff_operand (quantize -> bf16 B - W)"),
+    ("quantize_kernel<3, 3,", "diff_operand (quantize -> bf16 B - W)"),
+    ("quantize_kernel<4, 0, true>", "quantize_pack16 (compact format)"),
+    ("quantize_kernel<3, 0, true>", "quantize_pack16 (compact format)"),
+    ("quantize_kernel<3, 4, true>", "quantize_pack16 (compact format, dense INT3)"),
+    ("quantize_kernel<3, 4,", "quantize_pack3 (dense INT3)"),
+    ("expand_meta16", "compact metadata expansion"),
+    ("decode_tiles_kernel", "decode tiles"),
     ("transpose_pad_kernel", "X^T (Gram form)"),
     ("gram_split_kernel", "G split (Gram form)"),
     ("decode_gemm", "decode W4A16 GEMM (M <= 64)"),
@@ -101,6 +107,7 @@ KERNEL_LABELS = [
     ("argmin_kernel", "argmin"),
     ("select_row_kernel", "select s*"),
     ("fill_f64_kernel", "fill"),
+    ("Cijk_", "hipBLASLt bf16 GEMM (vendor yardstick, same operands)"),
 ]
 
 
@@ -148,7 +155,7 @@ def summarize_mfma(pmc_dir: str, command: str) -> str:
     per = {}
     for r in rows:
         name = r["Kernel_Name"]
-        if "awq::" not in name:
+        if "awq::" not in name and "Cijk_" not in name:
             continue
         key = (r["Dispatch_Id"], name)
         d = per.setdefault(key, {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
@@ -180,7 +187,7 @@ def summarize_trace(trace_dir: str, command: str, log_path: str | None) -> str:
     out.append(f"{'kernel':<62} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}")
     for r in rows:
         name = r["Name"]
-        if "awq::" not in name:
+        if "awq::" not in name and "Cijk_" not in name:
             continue
         out.append(f"{_label(name):<62} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.1f} "
                    f"{float(r['MinNs']) / 1e3:>10.1f} {float(r['MaxNs']) / 1e3:>10.1f} "
@@ -231,7 +238,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, commands: str, M: int, K: int)
            f"{4 * M * K} B written -> write factor {f_write:.4f}", ""]
     gemm_bytes = None
     for name in sorted(set(fetch) | set(write), key=_label):
-        if "awq::" not in name:
+        if "awq::" not in name and "Cijk_" not in name:
             continue
         fr = fetch.get(name, [float("nan")])
         wr = write.get(name, [float("nan")])
