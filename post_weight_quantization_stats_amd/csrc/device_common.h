@@ -21,12 +21,13 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 
-// Two binary32 values -> packed bf16 pair, round to nearest even
-// (v_cvt_pk_bf16_f32 on gfx950).  `lo` lands in bits 0..15.
+// Two binary32 values -> packed bf16 pair, round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950 (converting the halves separately costs two
+// converts and an or).  `lo` lands in bits 0..15.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo;
-  const __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
