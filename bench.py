@@ -644,6 +644,11 @@ def main() -> int:
                                                       spec.group), reps * 5, stream)
     t_diff = event_time_ms(lambda: awq.diff_operand(wd, s_all[i_mid], inv_all[i_mid], bits,
                                                     spec.group), reps * 5, stream)
+    # Yardstick for the read-and-write kernels: a plain device copy (torch)
+    # moving as many bytes as the difference operand's kernel (read W, write D).
+    cp_src, cp_dst = wd.clone(), torch.empty_like(wd)
+    t_copy = event_time_ms(lambda: cp_dst.copy_(cp_src), reps * 5, stream)
+    del cp_src, cp_dst
     flops = 2.0 * M * N * K
     tf = lambda ms: flops / (ms * 1e-3) / 1e12
     stats_bytes = 2.0 * M * K + 4.0 * K
@@ -658,7 +663,8 @@ def main() -> int:
     log(f"stats {t_stats * 1e3:.1f} us = {gbs(stats_bytes, t_stats):.0f} GB/s; quantize+pack "
         f"{t_quant * 1e3:.1f} us = {gbs(quant_bytes, t_quant):.0f} GB/s; dequant operand "
         f"{t_deq * 1e3:.1f} us = {gbs(deq_bytes, t_deq):.0f} GB/s; difference operand "
-        f"{t_diff * 1e3:.1f} us = {gbs(deq_bytes, t_diff):.0f} GB/s")
+        f"{t_diff * 1e3:.1f} us = {gbs(deq_bytes, t_diff):.0f} GB/s; plain device copy of W "
+        f"{t_copy * 1e3:.1f} us = {gbs(4.0 * N * K, t_copy):.0f} GB/s")
 
     def mfma_entry(ms):
         return {"ms": ms, "tflops": tf(ms), "frac_mfma_peak": tf(ms) / PEAK_BF16_TFLOPS}
@@ -700,6 +706,7 @@ def main() -> int:
             "quantize_pack": hbm_entry(quant_bytes, t_quant),
             "dequant_operand": hbm_entry(deq_bytes, t_deq),
             "diff_operand": hbm_entry(deq_bytes, t_diff),
+            "device_copy_same_bytes": hbm_entry(4.0 * N * K, t_copy),
         },
         "cpu_baseline": None,
     }

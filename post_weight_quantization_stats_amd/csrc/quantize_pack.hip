@@ -51,8 +51,11 @@ __device__ __forceinline__ float markstein_div(float a, float b, float y) {
 }
 
 // One lane's 16 channels of a group: their codes (as floats) and the group's
-// step and zero (identical in all 8 lanes of the group).
-template <int BITS, bool kHalf = false>
+// step and zero (identical in all 8 lanes of the group).  kCentred: q[j] holds
+// the centred code q - z instead, formed as clamp(rint(ws/step), -z, qmax - z)
+// (equal to clamp(rint(ws/step) + z, 0, qmax) - z: every value is a small
+// integer), one median instead of an add, a clamp and a subtract.
+template <int BITS, bool kHalf = false, bool kCentred = false>
 __device__ __forceinline__ void quantize16(const float (&ws)[16], float (&q)[16],
                                            float& step_out, float& z_out) {
   constexpr float qmax = (float)((1 << BITS) - 1);
@@ -94,6 +97,7 @@ __device__ __forceinline__ void quantize16(const float (&ws)[16], float (&q)[16]
 #pragma unroll
       for (int j = 0; j < 16; ++j) qt[j] = ws[j] / step;
     }
+    static_assert(!kCentred, "the compact format writes codes");
     const float z = fminf(fmaxf(rintf(zq), 0.f), qmax);
 #pragma unroll
     for (int j = 0; j < 16; ++j) q[j] = fminf(fmaxf(rintf(qt[j]) + z, 0.f), qmax);
@@ -119,8 +123,14 @@ __device__ __forceinline__ void quantize16(const float (&ws)[16], float (&q)[16]
     for (int j = 0; j < 16; ++j) qt[j] = ws[j] / step;
   }
   const float z = fminf(fmaxf(rintf(zq), 0.f), qmax);
+  if constexpr (kCentred) {
+    const float lo = -z, hi = qmax - z;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) q[j] = fminf(fmaxf(rintf(qt[j]) + z, 0.f), qmax);
+    for (int j = 0; j < 16; ++j) q[j] = __builtin_amdgcn_fmed3f(rintf(qt[j]), lo, hi);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) q[j] = fminf(fmaxf(rintf(qt[j]) + z, 0.f), qmax);
+  }
   step_out = step;
   z_out = z;
 }
@@ -200,7 +210,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   if (s != nullptr && s_sel != nullptr) srow = s + (int64_t)max(*s_sel, 0) * K;
   if (srow != nullptr) load16(srow, sv);
   if constexpr (!writes_codes(kMode)) {
-    if (inv_s != nullptr) load16(inv_s, iv);
+    // No inverse scale: a factor of 1, which every multiply keeps exactly,
+    // so the loop below multiplies unconditionally (no per-element select).
+    if (inv_s != nullptr) {
+      load16(inv_s, iv);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) iv[j] = 1.0f;
+    }
   }
 
   uint4 v[kRows][2];
@@ -231,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       for (int j = 0; j < 16; ++j) ws[j] *= sv[j];
     }
     float q[16], step, z;
-    quantize16<BITS, kHalf>(ws, q, step, z);
+    quantize16<BITS, kHalf, !writes_codes(kMode)>(ws, q, step, z);
     // The zero of the neighbouring group (lanes ^ 8: same row, group g ^ 1).
     uint32_t z_next = 0u;
     if constexpr (kHalf) z_next = (uint32_t)__shfl_xor((int)z, kLanesPerGroup);
@@ -250,8 +267,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       float bv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        bv[j] = (q[j] - z) * step;                  // exact difference, one rounding
-        if (inv_s != nullptr) bv[j] *= iv[j];
+        bv[j] = q[j] * step * iv[j];                // q holds q - z: two roundings
       }
       uint32_t d[8];
 #pragma unroll
