@@ -96,6 +96,11 @@ KERNEL_LABELS = [
     ("decode_tiles_kernel", "decode tiles"),
     ("transpose_pad_kernel", "X^T (Gram form)"),
     ("gram_split_kernel", "G split (Gram form)"),
+    (("decode_gemm_kernel<", ", true, true>"), "decode GEMM, tiles, compact metadata"),
+    (("decode_gemm_kernel<", ", false, true, false>"), "decode GEMM, tiles"),
+    (("decode_gemm_kernel<", ", true, true, false>"), "decode GEMM, dense INT3 tiles"),
+    (("decode_gemm_kernel<", ", false, false, false>"), "decode GEMM, row-major words"),
+    (("decode_gemm_kernel<", ", true, false, false>"), "decode GEMM, dense INT3 row-major"),
     ("decode_gemm", "decode W4A16 GEMM (M <= 64)"),
     ("decode_reduce", "decode split-K reduce"),
     ("act_stats_partial", "act_stats partial sums"),
@@ -113,7 +118,8 @@ KERNEL_LABELS = [
 
 def _label(name: str) -> str:
     for key, label in KERNEL_LABELS:
-        if key in name:
+        keys = key if isinstance(key, tuple) else (key,)
+        if all(k in name for k in keys):
             return label
     return name[:60]
 
@@ -193,7 +199,13 @@ def summarize_trace(trace_dir: str, command: str, log_path: str | None) -> str:
                    f"{float(r['MinNs']) / 1e3:>10.1f} {float(r['MaxNs']) / 1e3:>10.1f} "
                    f"{float(r['Percentage']):>6.2f}")
     line = _bench_line(log_path) if log_path else None
-    if line:
+    if line and "int4" in line:
+        out += ["", "# same run, bench.py figures (HIP-graph replays, weights rotated beyond the LLC):"]
+        for case, v in line["int4"].items():
+            out.append(f"{case}: tiles {v['us']:.2f} us ({v['gbs']:.0f} GB/s), row-major "
+                       f"{v['row_major_us']:.2f} us, compact metadata {v['compact_us']:.2f} us "
+                       f"({v['compact_gbs']:.0f} GB/s)")
+    elif line:
         rf = line["roofline"]
         out += ["", "# same run, bench.py HIP-event figures:",
                 f"search ms/layer: {line['ms_per_step']:.2f}",
@@ -292,7 +304,8 @@ def _graph_time_ms(fn, reps: int, stream) -> float:
     return ms
 
 
-def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
+def bench_decode(awq, dev, stream, reps: int = 96, layers=("qkv", "o_proj", "gate_up", "down"),
+                 token_counts=(1, 16, 64)) -> dict:
     """Decode-shaped W4A16 contraction on the Llama-3-8B block's layers
     (M = 1, 16 and 64 tokens, random packed INT4 weights), on decode tiles
     (the deployment path), on the row-major packed words, and on decode
@@ -303,7 +316,7 @@ def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
 
     import synth
     out = {}
-    for name in ("qkv", "o_proj", "gate_up", "down"):
+    for name in layers:
         spec = synth.layer_spec("llama3_8b_block", name)
         N, K = spec.N, spec.K
         wbytes = N * K / 2 + 5.0 * N * K / 128
@@ -318,7 +331,7 @@ def bench_decode(awq, dev, stream, reps: int = 96) -> dict:
             z4 = torch.randint(0, 256, (N, (K // 128 + 1) // 2), dtype=torch.uint8, device=dev,
                                generator=gen)
             packs.append((qw, awq.decode_tiles(qw, K), sc, ze, sc.half(), z4))
-        for M in (1, 16, 64):
+        for M in token_counts:
             a = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
             need = awq.workspace_size(awq.OP_DECODE_GEMM, M, N, K)
@@ -522,6 +535,8 @@ def main() -> int:
                     help="skip the constant-operand launch (keeps profiles to the synthetic data)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode-shaped GEMM figures (prints them as JSON)")
+    ap.add_argument("--decode-case", default=None, metavar="LAYER:M",
+                    help="only one decode case of the Llama-3-8B block, e.g. gate_up:1")
     ap.add_argument("--cpu-m", type=int, default=4096)
     ap.add_argument("--cpu-n", type=int, default=2048)
     ap.add_argument("--summarize-trace", metavar="DIR", default=None,
@@ -561,6 +576,13 @@ def main() -> int:
     import synth
 
     dev = torch.device("cuda:0")
+    if args.decode_case:
+        # One decode case only (for a profiler run): layer name and token count.
+        st = torch.cuda.current_stream(dev)
+        name, m = args.decode_case.split(":")
+        print(json.dumps({"int4": bench_decode(awq, dev, st, layers=(name,),
+                                               token_counts=(int(m),))}), flush=True)
+        return 0
     if args.decode_only:
         st = torch.cuda.current_stream(dev)
         print(json.dumps({"int4": bench_decode(awq, dev, st), "int3": bench_decode_int3(awq, dev, st)}),
