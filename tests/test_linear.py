@@ -24,6 +24,19 @@ def test_module_rejects_bad_shapes():
         m(torch.zeros((2, 64), dtype=torch.bfloat16))
 
 
+def test_module_compact_format_shapes():
+    """float16 steps select the compact format: zeros two per byte, [N][ceil(G/2)]."""
+    qw = torch.zeros((8, 48), dtype=torch.int32)                  # K = 384, G = 3
+    st = torch.zeros((8, 3), dtype=torch.float16)
+    m = awq.W4A16Linear(qw, st, torch.zeros((8, 2), dtype=torch.uint8))
+    assert m.compact and m.scales.dtype == torch.float16
+    with pytest.raises(ValueError):
+        awq.W4A16Linear(qw, st, torch.zeros((8, 3), dtype=torch.uint8))
+    m32 = awq.W4A16Linear(qw, st.float(), torch.zeros((8, 3), dtype=torch.uint8))
+    assert not m32.compact and m32.scales.dtype == torch.float32
+    assert "compact=True" in repr(m)
+
+
 def test_fold_inverse_scale():
     """Folding 1/s into a gain or into a previous layer's rows makes its
     output X / s: (diag(g) X) / s = diag(g / s) X, exactly in fp64."""
