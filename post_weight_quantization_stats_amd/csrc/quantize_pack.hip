@@ -27,6 +27,8 @@
 // ranges) take plain IEEE divisions.
 #include <math.h>
 
+#include <algorithm>
+
 #include "awq_internal.h"
 #include "device_common.h"
 
@@ -196,7 +198,6 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   const int t8 = threadIdx.x % kLanesPerGroup;
   const bool gvalid = g < G;
   const int64_t k0 = (gvalid ? g : 0) * kGroup + t8 * 16;
-  const int64_t n_begin = (int64_t)blockIdx.y * kRows;
 
   auto load16 = [&](const float* row, float (&v)[16]) {
 #pragma unroll
@@ -220,115 +221,135 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     }
   }
 
-  uint4 v[kRows][2];
+  // Rows in a grid-stride loop: each block takes kRows rows at a time and
+  // issues the loads of its next kRows before quantizing the current ones,
+  // so the memory pipe stays busy through the arithmetic (a block that loads,
+  // then computes, then stores leaves it idle for much of its life).
+  auto load_rows = [&](uint4 (&v)[kRows][2], int64_t nb) {
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    const int64_t n = n_begin + r;
-    const bool ok = gvalid && n < N;
-    const uint16_t* src = w + (ok ? n : 0) * K + k0;
-    v[r][0] = ok ? load_stream16(src) : make_uint4(0, 0, 0, 0);
-    v[r][1] = ok ? load_stream16(src + 8) : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    const int64_t n = n_begin + r;
-    float ws[16];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      ws[8 * c + 0] = bf16_lo(v[r][c].x); ws[8 * c + 1] = bf16_hi(v[r][c].x);
-      ws[8 * c + 2] = bf16_lo(v[r][c].y); ws[8 * c + 3] = bf16_hi(v[r][c].y);
-      ws[8 * c + 4] = bf16_lo(v[r][c].z); ws[8 * c + 5] = bf16_hi(v[r][c].z);
-      ws[8 * c + 6] = bf16_lo(v[r][c].w); ws[8 * c + 7] = bf16_hi(v[r][c].w);
+    for (int r = 0; r < kRows; ++r) {
+      const int64_t n = nb + r;
+      const bool ok = gvalid && n < N;
+      const uint16_t* src = w + (ok ? n : 0) * K + k0;
+      v[r][0] = ok ? load_stream16(src) : make_uint4(0, 0, 0, 0);
+      v[r][1] = ok ? load_stream16(src + 8) : make_uint4(0, 0, 0, 0);
     }
-    float wv[16];
+  };
+  auto process_rows = [&](const uint4 (&v)[kRows][2], int64_t n_begin) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) wv[j] = ws[j];
-    if (srow != nullptr) {
+    for (int r = 0; r < kRows; ++r) {
+      const int64_t n = n_begin + r;
+      float ws[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) ws[j] *= sv[j];
-    }
-    float q[16], step, z;
-    quantize16<BITS, kHalf, !writes_codes(kMode)>(ws, q, step, z);
-    // The zero of the neighbouring group (lanes ^ 8: same row, group g ^ 1).
-    uint32_t z_next = 0u;
-    if constexpr (kHalf) z_next = (uint32_t)__shfl_xor((int)z, kLanesPerGroup);
-    uint32_t p_lo = 0, p_hi = 0, o_lo = 0, o_hi = 0;
-    if constexpr (kMode == kPack3) {
-      // Lanes 2m and 2m+1 hold the two halves of one 32-code run; the even
-      // lane takes its neighbour's 48 bits (quad_perm [1,0,3,2]) and writes
-      // the run's three words.  Both lanes of a pair are active or inactive
-      // together (same group and row).
-      pack48(q, p_lo, p_hi);
-      o_lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p_lo, 0xB1, 0xF, 0xF, false);
-      o_hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p_hi, 0xB1, 0xF, 0xF, false);
-    }
-    if (!(gvalid && n < N)) continue;
-    if constexpr (!writes_codes(kMode)) {
-      float bv[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        bv[j] = q[j] * step * iv[j];                // q holds q - z: two roundings
+      for (int c = 0; c < 2; ++c) {
+        ws[8 * c + 0] = bf16_lo(v[r][c].x); ws[8 * c + 1] = bf16_hi(v[r][c].x);
+        ws[8 * c + 2] = bf16_lo(v[r][c].y); ws[8 * c + 3] = bf16_hi(v[r][c].y);
+        ws[8 * c + 4] = bf16_lo(v[r][c].z); ws[8 * c + 5] = bf16_hi(v[r][c].z);
+        ws[8 * c + 6] = bf16_lo(v[r][c].w); ws[8 * c + 7] = bf16_hi(v[r][c].w);
       }
-      uint32_t d[8];
+      float wv[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) d[j] = pack_bf16x2(bv[2 * j], bv[2 * j + 1]);
-      if constexpr (kMode == kOperand) {
-        uint4* dst = (uint4*)(bout + n * K + k0);
-        dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
-        dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
-      } else if constexpr (kMode == kDiffOp) {
-        uint32_t e[8];
+      for (int j = 0; j < 16; ++j) wv[j] = ws[j];
+      if (srow != nullptr) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          e[j] = pack_bf16x2(bf16_lo(d[j]) - wv[2 * j], bf16_hi(d[j]) - wv[2 * j + 1]);
-        uint4* dst = (uint4*)(bout + n * K + k0);
-        dst[0] = make_uint4(e[0], e[1], e[2], e[3]);
-        dst[1] = make_uint4(e[4], e[5], e[6], e[7]);
-      } else {
-        static_assert(kMode == kDiff, "unhandled operand mode");
-        float dd[16];
-        uint32_t e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          dd[2 * j] = bf16_lo(d[j]) - wv[2 * j];
-          dd[2 * j + 1] = bf16_hi(d[j]) - wv[2 * j + 1];
-          e[j] = pack_bf16x2(dd[2 * j], dd[2 * j + 1]);
-        }
-        float4* df = (float4*)(dout + n * K + k0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          df[c] = make_float4(dd[4 * c], dd[4 * c + 1], dd[4 * c + 2], dd[4 * c + 3]);
-        uint16_t* arow = bout + n * 2 * K;
-        const uint4 e0 = make_uint4(e[0], e[1], e[2], e[3]);
-        const uint4 e1 = make_uint4(e[4], e[5], e[6], e[7]);
-        ((uint4*)(arow + k0))[0] = e0;
-        ((uint4*)(arow + k0))[1] = e1;
-        ((uint4*)(arow + K + k0))[0] = e0;
-        ((uint4*)(arow + K + k0))[1] = e1;
+        for (int j = 0; j < 16; ++j) ws[j] *= sv[j];
       }
-    } else {
-      static_assert(writes_codes(kMode), "unhandled code mode");
+      float q[16], step, z;
+      quantize16<BITS, kHalf, !writes_codes(kMode)>(ws, q, step, z);
+      // The zero of the neighbouring group (lanes ^ 8: same row, group g ^ 1).
+      uint32_t z_next = 0u;
+      if constexpr (kHalf) z_next = (uint32_t)__shfl_xor((int)z, kLanesPerGroup);
+      uint32_t p_lo = 0, p_hi = 0, o_lo = 0, o_hi = 0;
       if constexpr (kMode == kPack3) {
-        if ((t8 & 1) == 0) {
-          uint32_t* dst = qweight + n * (3 * K / 32) + (k0 / 32) * 3;
-          dst[0] = p_lo;
-          dst[1] = p_hi | (o_lo << 16);
-          dst[2] = (o_lo >> 16) | (o_hi << 16);
+        // Lanes 2m and 2m+1 hold the two halves of one 32-code run; the even
+        // lane takes its neighbour's 48 bits (quad_perm [1,0,3,2]) and writes
+        // the run's three words.  Both lanes of a pair are active or inactive
+        // together (same group and row).
+        pack48(q, p_lo, p_hi);
+        o_lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p_lo, 0xB1, 0xF, 0xF, false);
+        o_hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p_hi, 0xB1, 0xF, 0xF, false);
+      }
+      if (!(gvalid && n < N)) continue;
+      if constexpr (!writes_codes(kMode)) {
+        float bv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          bv[j] = q[j] * step * iv[j];                // q holds q - z: two roundings
+        }
+        uint32_t d[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d[j] = pack_bf16x2(bv[2 * j], bv[2 * j + 1]);
+        if constexpr (kMode == kOperand) {
+          uint4* dst = (uint4*)(bout + n * K + k0);
+          dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
+          dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
+        } else if constexpr (kMode == kDiffOp) {
+          uint32_t e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            e[j] = pack_bf16x2(bf16_lo(d[j]) - wv[2 * j], bf16_hi(d[j]) - wv[2 * j + 1]);
+          uint4* dst = (uint4*)(bout + n * K + k0);
+          dst[0] = make_uint4(e[0], e[1], e[2], e[3]);
+          dst[1] = make_uint4(e[4], e[5], e[6], e[7]);
+        } else {
+          static_assert(kMode == kDiff, "unhandled operand mode");
+          float dd[16];
+          uint32_t e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            dd[2 * j] = bf16_lo(d[j]) - wv[2 * j];
+            dd[2 * j + 1] = bf16_hi(d[j]) - wv[2 * j + 1];
+            e[j] = pack_bf16x2(dd[2 * j], dd[2 * j + 1]);
+          }
+          float4* df = (float4*)(dout + n * K + k0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            df[c] = make_float4(dd[4 * c], dd[4 * c + 1], dd[4 * c + 2], dd[4 * c + 3]);
+          uint16_t* arow = bout + n * 2 * K;
+          const uint4 e0 = make_uint4(e[0], e[1], e[2], e[3]);
+          const uint4 e1 = make_uint4(e[4], e[5], e[6], e[7]);
+          ((uint4*)(arow + k0))[0] = e0;
+          ((uint4*)(arow + k0))[1] = e1;
+          ((uint4*)(arow + K + k0))[0] = e0;
+          ((uint4*)(arow + K + k0))[1] = e1;
         }
       } else {
-        *(uint2*)(qweight + n * (K / 8) + k0 / 8) = make_uint2(pack8(q), pack8(q + 8));
-      }
-      if (t8 == 0) {
-        if constexpr (kHalf) {
-          steps16[n * G + g] = __builtin_bit_cast(uint16_t, (_Float16)step);   // exact
-          if ((g & 1) == 0)
-            zeros[n * ((G + 1) / 2) + g / 2] = (uint8_t)((uint32_t)z | (g + 1 < G ? z_next << 4 : 0u));
+        static_assert(writes_codes(kMode), "unhandled code mode");
+        if constexpr (kMode == kPack3) {
+          if ((t8 & 1) == 0) {
+            uint32_t* dst = qweight + n * (3 * K / 32) + (k0 / 32) * 3;
+            dst[0] = p_lo;
+            dst[1] = p_hi | (o_lo << 16);
+            dst[2] = (o_lo >> 16) | (o_hi << 16);
+          }
         } else {
-          scales[n * G + g] = step;
-          zeros[n * G + g] = (uint8_t)z;
+          *(uint2*)(qweight + n * (K / 8) + k0 / 8) = make_uint2(pack8(q), pack8(q + 8));
+        }
+        if (t8 == 0) {
+          if constexpr (kHalf) {
+            steps16[n * G + g] = __builtin_bit_cast(uint16_t, (_Float16)step);   // exact
+            if ((g & 1) == 0)
+              zeros[n * ((G + 1) / 2) + g / 2] = (uint8_t)((uint32_t)z | (g + 1 < G ? z_next << 4 : 0u));
+          } else {
+            scales[n * G + g] = step;
+            zeros[n * G + g] = (uint8_t)z;
+          }
         }
       }
     }
+  };
+  const int64_t stride = (int64_t)gridDim.y * kRows;
+  int64_t nb = (int64_t)blockIdx.y * kRows;
+  uint4 va[kRows][2], vb[kRows][2];
+  load_rows(va, nb);
+  while (nb < N) {                       // uniform across the block
+    load_rows(vb, nb + stride);
+    process_rows(va, nb);
+    nb += stride;
+    if (nb >= N) break;
+    load_rows(va, nb + stride);
+    process_rows(vb, nb);
+    nb += stride;
   }
 }
 
@@ -345,13 +366,21 @@ __global__ __launch_bounds__(256) void expand_meta16_kernel(const uint16_t* __re
   zeros[i] = (uint8_t)((zeros4[n * ((G + 1) / 2) + g / 2] >> (4 * (g & 1))) & 15);
 }
 
+// Blocks along K cover kGroupsPerBlock groups each; along N, enough row
+// slots for about eight blocks per CU (the rest is the grid-stride loop).
+dim3 quant_grid(int64_t N, int64_t K) {
+  const int64_t gx = ceil_div(K / kGroup, (int64_t)kGroupsPerBlock);
+  const int64_t gy = std::min(ceil_div(N, (int64_t)kRows), std::max((int64_t)1, (int64_t)2048 / gx));
+  return dim3((unsigned)gx, (unsigned)gy);
+}
+
 }  // namespace
 
 hipError_t launch_quantize_pack16(const uint16_t* w, int64_t N, int64_t K, const float* s,
                                   int bits, bool int3_dense, uint32_t* qweight, uint16_t* steps16,
                                   uint8_t* zeros4, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
+  const dim3 grid = quant_grid(N, K);
   if (int3_dense)
     quantize_kernel<3, kPack3, true><<<grid, kThreads, 0, stream>>>(
         w, N, K, s, nullptr, nullptr, qweight, nullptr, zeros4, nullptr, nullptr, steps16);
@@ -376,7 +405,7 @@ hipError_t launch_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const f
                                 const int32_t* s_sel, int bits, uint32_t* qweight,
                                 float* scales, uint8_t* zeros, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
+  const dim3 grid = quant_grid(N, K);
   if (bits == 4)
     quantize_kernel<4, kPack><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, nullptr, qweight,
                                                              scales, zeros, nullptr, nullptr, nullptr);
@@ -390,7 +419,7 @@ hipError_t launch_quantize_pack3(const uint16_t* w, int64_t N, int64_t K, const 
                                  uint32_t* qweight3, float* scales, uint8_t* zeros,
                                  hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
+  const dim3 grid = quant_grid(N, K);
   quantize_kernel<3, kPack3><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, nullptr, qweight3,
                                                             scales, zeros, nullptr, nullptr, nullptr);
   return hipGetLastError();
@@ -400,7 +429,7 @@ hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, cons
                                    const float* inv_s, int bits, uint16_t* b_out,
                                    hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
+  const dim3 grid = quant_grid(N, K);
   if (bits == 4)
     quantize_kernel<4, kOperand><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
                                                                 nullptr, nullptr, b_out, nullptr, nullptr);
@@ -414,7 +443,7 @@ hipError_t launch_quantize_diff_operand(const uint16_t* w, int64_t N, int64_t K,
                                         const float* inv_s, int bits, uint16_t* d_out,
                                         hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
+  const dim3 grid = quant_grid(N, K);
   if (bits == 4)
     quantize_kernel<4, kDiffOp><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
                                                                nullptr, nullptr, d_out, nullptr, nullptr);
@@ -428,7 +457,7 @@ hipError_t launch_quantize_diff(const uint16_t* w, int64_t N, int64_t K, const f
                                 const float* inv_s, int bits, uint16_t* a_split, float* d32,
                                 hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  dim3 grid((unsigned)ceil_div(K / kGroup, kGroupsPerBlock), (unsigned)ceil_div(N, kRows));
+  const dim3 grid = quant_grid(N, K);
   if (bits == 4)
     quantize_kernel<4, kDiff><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
                                                              nullptr, nullptr, a_split, d32, nullptr);
