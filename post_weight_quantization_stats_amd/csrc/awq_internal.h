@@ -27,9 +27,9 @@ struct StatsPlan {
   int64_t rows_per_block;
   int64_t row_blocks;
 };
-StatsPlan stats_plan(int64_t M);
+StatsPlan stats_plan(int64_t M, int64_t K);
 inline size_t stats_ws_bytes(int64_t M, int64_t K) {
-  return align_up((size_t)stats_plan(M).row_blocks * (size_t)K * sizeof(double));
+  return align_up((size_t)stats_plan(M, K).row_blocks * (size_t)K * sizeof(double));
 }
 
 // ---- candidate scales: r (fp64) + per-block min/max partials ----
