@@ -474,6 +474,18 @@ def bench_pipeline(awq, dev, stream, n_blocks: int = 2, M: int = 65536, d: int =
     alphas = [(int(r["gate_up"]["best_idx"].item()), int(r["down"]["best_idx"].item())) for r in res]
     log(f"pipeline: {n_blocks} blocks in {ms:.1f} ms ({ms / n_blocks:.1f} ms per block, "
         f"{2 * n_blocks * 1e3 / ms:.2f} layers/s); alpha indices {alphas}")
+    # The same blocks with Gram-form losses in both searches.
+    awq.quantize_mlp_blocks(xd, bd, gram=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res_g = awq.quantize_mlp_blocks(xd, bd, gram=True)
+    torch.cuda.synchronize()
+    ms_g = (time.perf_counter() - t0) * 1e3
+    alphas_g = [(int(r["gate_up"]["best_idx"].item()), int(r["down"]["best_idx"].item()))
+                for r in res_g]
+    del res_g
+    log(f"pipeline, Gram-form searches: {ms_g / n_blocks:.1f} ms per block "
+        f"({2 * n_blocks * 1e3 / ms_g:.2f} layers/s); alpha indices {alphas_g}")
     # the block ops on their own
     gamma = bd[0][0]
     y = torch.randn((M, 2 * F), device=dev)
@@ -489,6 +501,8 @@ def bench_pipeline(awq, dev, stream, n_blocks: int = 2, M: int = 65536, d: int =
         log(f"{k}: {t * 1e3:.1f} us = {gbs(nb, t):.0f} GB/s")
     return {"blocks": n_blocks, "M": M, "d": d, "F": F, "ms": ms, "ms_per_block": ms / n_blocks,
             "layers_per_s": 2 * n_blocks * 1e3 / ms, "alpha_indices": alphas,
+            "gram_form": {"ms_per_block": ms_g / n_blocks, "layers_per_s": 2 * n_blocks * 1e3 / ms_g,
+                          "alpha_indices": alphas_g},
             "ops": {k: {"us": t * 1e3, "gbs": gbs(nb, t), "frac_hbm_peak": gbs(nb, t) / PEAK_HBM_GBS,
                         "bytes": nb} for k, (nb, t) in ops.items()}}
 

@@ -66,12 +66,13 @@ def test_silu_mul_divide_residual(dev):
                           O.residual_add(x, yy))
 
 
-def check_block_steps(dev, x, gamma, wgu, wd, n_grid, F):
+def check_block_steps(dev, x, gamma, wgu, wd, n_grid, F, gram=False):
     """Run one block on the GPU and check each step against the oracle on the
     GPU's own inputs; returns the GPU's x_next (bit patterns)."""
     xd = to_dev_bf16(x, dev)
     r = awq.quantize_mlp_block(xd, to_dev_f32(gamma, dev), to_dev_bf16(wgu, dev),
-                               to_dev_bf16(wd, dev), n_grid=n_grid, keep_intermediates=True)
+                               to_dev_bf16(wd, dev), n_grid=n_grid, keep_intermediates=True,
+                               gram=gram)
     torch.cuda.synchronize()
     u = bits(r["u"])
     close_bf16(u, O.rmsnorm(x, gamma, 1e-5)[0])
@@ -114,6 +115,15 @@ def test_two_blocks_step_by_step(dev):
     for b, (gamma, wgu, wd) in enumerate(blocks):
         announce("pipeline block", b)
         x, _ = check_block_steps(dev, x, gamma, wgu, wd, 20, F)
+
+
+def test_two_blocks_step_by_step_gram_form(dev):
+    """The same steps with both searches in the Gram form."""
+    M, d, F = 512, 256, 384
+    x, blocks = synth.make_mlp_blocks(M, d, F, 2, seed=3)
+    for b, (gamma, wgu, wd) in enumerate(blocks):
+        announce("pipeline block, Gram form", b)
+        x, _ = check_block_steps(dev, x, gamma, wgu, wd, 20, F, gram=True)
 
 
 def test_block_full_width_reduced_tokens(dev):
