@@ -187,6 +187,37 @@ def test_fullsize_int3_dense_llama2_70b(dev, name):
         gemm_close(y3.cpu().numpy()[:, cols], ref)
 
 
+@pytest.mark.parametrize("name,bits,dense3", [("gate_up", 4, False), ("down", 3, True)])
+def test_fullsize_compact_format_llama2_70b(dev, name, bits, dense3):
+    """The compact deployment format on the 70B-shaped layers at full size:
+    codes, binary16 steps and zero nibbles on sampled rows against the
+    oracle, and the compact decode contraction on tiles bit-identical to the
+    fp32-metadata one on the expanded metadata (M = 1 and 16)."""
+    announce("full-size compact format", name, bits, dense3)
+    spec = synth.layer_spec("llama2_70b_mlp", name)
+    w = synth.make_weight(spec, 0)
+    wd = to_dev_bf16(w, dev)
+    s = np.exp(np.random.default_rng(3).uniform(-0.5, 0.5, spec.K)).astype(np.float32)
+    layout = awq.LAYOUT_INT3_DENSE if dense3 else awq.LAYOUT_NIBBLE
+    qw, st, z4 = awq.quantize_pack16(wd, to_dev_f32(s, dev), bits, 128, layout)
+    rows = sample_rows(spec.N, 16, 7)
+    q, z, stp = O.quantize16(w[rows], s, bits, 128)
+    sb, zb = O.pack_meta16(z, stp)
+    words = O.pack3(q) if dense3 else O.pack(q, z, stp)[0]
+    assert np.array_equal(u32(qw)[rows], words)
+    assert np.array_equal(st.cpu().numpy().view(np.uint16)[rows], sb)
+    assert np.array_equal(z4.cpu().numpy()[rows], zb)
+    tiles = awq.decode_tiles(qw, spec.K, layout)
+    sc, ze = awq.expand_meta16(st, z4)
+    del wd, qw
+    for M in (1, 16):
+        ad = to_dev_bf16(synth.decode_activations(spec.K, M, seed=M), dev)
+        y16 = awq.decode_gemm_tiled16(ad, tiles, st, z4, layout)
+        y32 = awq.decode_gemm_tiled(ad, tiles, sc, ze, layout)
+        torch.cuda.synchronize()
+        assert torch.equal(y16, y32), M
+
+
 # Every other workload's layer shapes (real K, dtype and activation recipe),
 # at 384 tokens and the first 256 output rows, against the oracle's search.
 OTHER_LAYERS = [("llama2_7b_mlp", "gate_up", 4), ("llama2_7b_mlp", "down", 4),
