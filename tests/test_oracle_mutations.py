@@ -233,6 +233,7 @@ PINS = [
     P.test_silu_mul_against_torch_and_identities,
     P.test_divide_rows_and_residual_against_library,
     P.test_f16_format_against_libraries,
+    P.test_compact_worked_groups,
     P.test_quantize16_brute_force_nearest_level,
     P.test_quantize16_clamped_and_subnormal_steps,
     P.test_meta16_pack_brute_force_and_roundtrip,

@@ -678,6 +678,28 @@ def _grid_layer(N, G, group, qmax, seed):
     return bits_of(k.reshape(N, G * group).astype(np.float32) * np.float32(2.0 ** -7))
 
 
+def test_compact_worked_groups():
+    """Hand-worked groups whose fp32 steps sit exactly between two binary16
+    values (tests/golden/compact_worked.json): one tie goes down to an even
+    fraction, the other up."""
+    with open(os.path.join(GOLDEN, "compact_worked.json")) as f:
+        g = json.load(f)
+    K = g["K"]
+    W = np.zeros((1, K), np.float32)
+    for k, v in g["w_nonzero"]:
+        W[0, k] = v
+    s = np.ones(K, np.float32)
+    for k, v in g["s_nonzero"]:
+        s[k] = v
+        assert float(np.float32(v)) == v
+    q, z, st = O.quantize16(synth.to_bf16_bits(W), s, g["bits"], g["group"])
+    sb, zb = O.pack_meta16(z, st)
+    assert [hex(int(v)) for v in sb[0]] == g["expected_steps16_hex"]
+    assert zb[0].tolist() == g["expected_zeros4"]
+    nz = [[int(k), int(q[0, k])] for k in np.flatnonzero(q[0])]
+    assert nz == g["expected_codes_nonzero"]
+
+
 def test_quantize16_equals_quantize_when_steps_are_binary16():
     for bits in (3, 4):
         w = _grid_layer(6, 3, 128, (1 << bits) - 1, seed=41 + bits)
