@@ -359,3 +359,32 @@ def test_compact_format_entry_errors():
     assert dec(K=32768) == WORKSPACE
     assert dec(N=1 << 22, K=1 << 13, ws=FAKE, wsb=1 << 40) == SHAPE
     assert dec(M=0) == OK and dec(N=0) == OK
+
+
+def test_last_error_is_per_thread():
+    """Each thread sees the message of its own last failing call."""
+    import threading
+    lib = awq.lib()
+    seen = {}
+
+    def worker(name, call):
+        for _ in range(200):
+            st = call()
+            msg = lib.awq_last_error()
+            if name in seen and seen[name] != (st, msg):
+                seen[name] = None
+                return
+            seen[name] = (st, msg)
+
+    calls = {
+        "shape": lambda: lib.awq_act_stats(FAKE, 4, 100, FAKE, FAKE, 1 << 20, None),
+        "unsupported": lambda: lib.awq_quantize_pack(FAKE, 4, 128, None, 5, 128, FAKE, FAKE, FAKE, None),
+    }
+    threads = [threading.Thread(target=worker, args=(k, c)) for k, c in calls.items()]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert seen["shape"] is not None and seen["shape"][0] == SHAPE
+    assert seen["unsupported"] is not None and seen["unsupported"][0] == UNSUPPORTED
+    assert seen["shape"][1] != seen["unsupported"][1]
