@@ -160,6 +160,35 @@ def test_fullsize_search_gram(dev, qkv):
             assert torch.equal(a[k], g[k]), k
 
 
+@pytest.mark.parametrize("bits", [3, 4])
+def test_fullsize_search_llama2_70b_down(dev, bits):
+    """The largest layer of the workloads at full size (Llama-2-70B down
+    projection: 16384 tokens x 28672 -> 8192): the direct and Gram-form
+    searches agree (losses within 2e-5 relative, the same choice up to such
+    ties), the statistics match the oracle's, and sampled rows of the final
+    pack are bit-exact against the oracle given the chosen s."""
+    announce("full-size search, Llama-2-70B down", bits)
+    x, w, spec = synth.make_layer("llama2_70b_mlp", "down")
+    xd, wd = to_dev_bf16(x, dev), to_dev_bf16(w, dev)
+    a = awq.search_scale(xd, wd, bits, 128, spec.n_grid)
+    g = awq.search_scale_gram(xd, wd, bits, 128, spec.n_grid)
+    torch.cuda.synchronize()
+    la, lg = a["losses"].cpu().numpy(), g["losses"].cpu().numpy()
+    assert np.isfinite(la).all()
+    np.testing.assert_allclose(lg, la, rtol=2e-5, atol=0)
+    ib, gb = int(a["best_idx"].item()), int(g["best_idx"].item())
+    assert ib == int(np.argmin(la))
+    assert ib == gb or abs(la[ib] - la[gb]) <= 2e-5 * la[ib]
+    a_ref = O.act_stats(x)[1]
+    assert (np.abs(a["mean_abs"].cpu().numpy() - a_ref) / a_ref).max() <= 1e-6
+    best_s = a["best_s"].cpu().numpy()
+    rows = sample_rows(spec.N, 16, 9)
+    rq, rs, rz = O.pack(*O.quantize(w[rows], best_s, bits, 128))
+    assert np.array_equal(u32(a["qweight"])[rows], rq)
+    assert np.array_equal(a["scales"].cpu().numpy()[rows], rs)
+    assert np.array_equal(a["zeros"].cpu().numpy()[rows], rz)
+
+
 @pytest.mark.parametrize("name", ["down", "gate_up"])
 def test_fullsize_int3_dense_llama2_70b(dev, name):
     """The 70B-shaped INT3 layers at full size: dense words on sampled rows
