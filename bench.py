@@ -449,6 +449,40 @@ def bench_gram(awq, xd, wd, spec, bits: int, direct: dict, steps: int, direct_ms
             "same_choice": same}
 
 
+def bench_largest_layer(awq, dev, steps: int = 3) -> dict:
+    """The search on the workloads' largest layer, the Llama-2-70B down
+    projection (16384 tokens x 28672 -> 8192), INT3 and INT4, direct and
+    Gram form (here 3K > M, so the Gram form costs as much as the direct)."""
+    import torch
+
+    import synth
+    spec = synth.layer_spec("llama2_70b_mlp", "down")
+    x_bits, w_bits, _ = synth.make_layer(spec.workload, spec.name)
+    xd = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    wd = torch.from_numpy(w_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    del x_bits, w_bits
+    out = {"M": spec.M, "K": spec.K, "N": spec.N}
+    flops = 2.0 * spec.M * spec.N * spec.K * spec.n_grid
+    for bits in spec.bits:
+        for form, fn in (("direct", awq.search_scale), ("gram", awq.search_scale_gram)):
+            fn(xd, wd, bits, spec.group, spec.n_grid)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                r = fn(xd, wd, bits, spec.group, spec.n_grid)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / steps
+            out[f"int{bits}_{form}"] = {"ms_per_layer": ms, "layers_per_s": 1e3 / ms,
+                                        "best_idx": int(r["best_idx"].item())}
+            extra = f", {flops / (ms * 1e-3) / 1e12:.0f} TFLOP/s in the candidate products" \
+                if form == "direct" else ""
+            log(f"largest layer (Llama-2-70B down) INT{bits} {form}: {ms:.1f} ms/layer{extra}; "
+                f"alpha index {out[f'int{bits}_{form}']['best_idx']}")
+    del xd, wd
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_pipeline(awq, dev, stream, n_blocks: int = 2, M: int = 65536, d: int = 4096,
                    F: int = 11008) -> dict:
     """The search layer after layer through synthetic feed-forward blocks at
@@ -549,6 +583,8 @@ def main() -> int:
                     help="skip the constant-operand launch (keeps profiles to the synthetic data)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode-shaped GEMM figures (prints them as JSON)")
+    ap.add_argument("--no-largest", action="store_true",
+                    help="skip the search on the workloads' largest layer (Llama-2-70B down)")
     ap.add_argument("--decode-case", default=None, metavar="LAYER:M",
                     help="only one decode case of the Llama-3-8B block, e.g. gate_up:1")
     ap.add_argument("--cpu-m", type=int, default=4096)
@@ -761,6 +797,8 @@ def main() -> int:
         torch.cuda.empty_cache()
         result["variants"]["block_pipeline_llama2_7b_mlp"] = bench_pipeline(awq, dev, stream)
         torch.cuda.empty_cache()
+    if not args.no_largest:
+        result["variants"]["search_llama2_70b_down"] = bench_largest_layer(awq, dev)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_m} tokens x {args.cpu_n} rows")
         result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, spec, args.cpu_m, args.cpu_n)
