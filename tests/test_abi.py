@@ -188,6 +188,9 @@ def test_decode_gemm_errors_and_plan():
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 4, 128, 4096) == 0
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 4096, 8192) == 0
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 4096, 8320) > 0
+    # Above 16 tokens a workgroup takes at most 32 groups (4096 channels).
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 17, 4096, 4096) == 0
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 17, 4096, 4224) >= 2 * 17 * 4096 * 4
     need = awq.workspace_size(awq.OP_DECODE_GEMM, 4, 128, 32768)
     assert need >= 2 * 4 * 128 * 4
     assert call(K=32768) == WORKSPACE
