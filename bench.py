@@ -483,6 +483,60 @@ def bench_largest_layer(awq, dev, steps: int = 3) -> dict:
     return out
 
 
+def bench_llama3_block(awq, dev, steps: int = 2) -> dict:
+    """The search over the four layers of the Llama-3-8B-shaped decoder block
+    (32768 calibration tokens; qkv 4096 -> 6144, o_proj 4096 -> 4096, gate/up
+    4096 -> 2 x 14336, down 14336 -> 4096), reported per layer and as blocks/s.
+    The down layer's input H = silu(X . Wg^T) * (X . Wu^T) from the unquantized
+    gate/up weights is formed in fp64 on the GPU (torch) and rounded to bf16,
+    the generator's own formula, so the host does not spend a minute on it."""
+    import torch
+
+    import synth
+    res, total = {}, 0.0
+    gate_up = None
+    for name in ("qkv", "o_proj", "gate_up", "down"):
+        spec = synth.layer_spec("llama3_8b_block", name)
+        w_bits = synth.make_weight(spec, 0)
+        wd = torch.from_numpy(w_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        if name == "down":
+            xg, wg = gate_up
+            F = spec.K
+            h = torch.empty((spec.M, F), dtype=torch.bfloat16, device=dev)
+            for r0 in range(0, spec.M, 8192):
+                xc = xg[r0:r0 + 8192].double()
+                g = xc @ wg[:F].double().T
+                u = xc @ wg[F:].double().T
+                h[r0:r0 + 8192] = (g * torch.sigmoid(g) * u).float().to(torch.bfloat16)
+                del xc, g, u
+            xd = h
+            gate_up = None
+        else:
+            x_bits = synth.make_activations(spec, seed=0)
+            xd = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+            if name == "gate_up":
+                gate_up = (xd, wd)
+        awq.search_scale(xd, wd, 4, spec.group, spec.n_grid)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            r = awq.search_scale(xd, wd, 4, spec.group, spec.n_grid)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        total += ms
+        tflops = 2.0 * spec.M * spec.N * spec.K * spec.n_grid / (ms * 1e-3) / 1e12
+        res[name] = {"M": spec.M, "K": spec.K, "N": spec.N, "ms_per_layer": ms,
+                     "best_idx": int(r["best_idx"].item()), "tflops_candidate_products": tflops}
+        log(f"Llama-3-8B block {name} ({spec.M} x {spec.K} -> {spec.N}): {ms:.1f} ms/layer, "
+            f"{tflops:.0f} TFLOP/s in the candidate products, alpha index {res[name]['best_idx']}")
+        del xd, wd
+        torch.cuda.empty_cache()
+    res["ms_per_block"] = total
+    res["blocks_per_s"] = 1e3 / total
+    log(f"Llama-3-8B block: {total:.1f} ms per block, {1e3 / total:.2f} blocks/s")
+    return res
+
+
 def bench_pipeline(awq, dev, stream, n_blocks: int = 2, M: int = 65536, d: int = 4096,
                    F: int = 11008) -> dict:
     """The search layer after layer through synthetic feed-forward blocks at
@@ -584,7 +638,8 @@ def main() -> int:
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode-shaped GEMM figures (prints them as JSON)")
     ap.add_argument("--no-largest", action="store_true",
-                    help="skip the search on the workloads' largest layer (Llama-2-70B down)")
+                    help="skip the searches on the Llama-3-8B block and the largest layer "
+                         "(Llama-2-70B down)")
     ap.add_argument("--decode-case", default=None, metavar="LAYER:M",
                     help="only one decode case of the Llama-3-8B block, e.g. gate_up:1")
     ap.add_argument("--cpu-m", type=int, default=4096)
@@ -798,6 +853,7 @@ def main() -> int:
         result["variants"]["block_pipeline_llama2_7b_mlp"] = bench_pipeline(awq, dev, stream)
         torch.cuda.empty_cache()
     if not args.no_largest:
+        result["variants"]["search_llama3_8b_block"] = bench_llama3_block(awq, dev)
         result["variants"]["search_llama2_70b_down"] = bench_largest_layer(awq, dev)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_m} tokens x {args.cpu_n} rows")
