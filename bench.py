@@ -483,57 +483,55 @@ def bench_largest_layer(awq, dev, steps: int = 3) -> dict:
     return out
 
 
-def bench_llama3_block(awq, dev, steps: int = 2) -> dict:
-    """The search over the four layers of the Llama-3-8B-shaped decoder block
-    (32768 calibration tokens; qkv 4096 -> 6144, o_proj 4096 -> 4096, gate/up
-    4096 -> 2 x 14336, down 14336 -> 4096), reported per layer and as blocks/s.
-    The down layer's input H = silu(X . Wg^T) * (X . Wu^T) from the unquantized
-    gate/up weights is formed in fp64 on the GPU (torch) and rounded to bf16,
-    the generator's own formula, so the host does not spend a minute on it."""
+def bench_workload_layers(awq, dev, workload: str, names, steps: int = 2) -> dict:
+    """The search over the layers of one workload, each on its own synthetic
+    inputs, reported per layer and in total.  A down projection's input
+    H = silu(X . Wg^T) * (X . Wu^T), from its gate/up layer's inputs and
+    unquantized weights, is formed in fp64 on the GPU (torch) and rounded to
+    bf16, the generator's own formula, so the host does not spend a minute
+    on it."""
     import torch
 
     import synth
-    res, total = {}, 0.0
-    gate_up = None
-    for name in ("qkv", "o_proj", "gate_up", "down"):
-        spec = synth.layer_spec("llama3_8b_block", name)
+    res, total, sources = {}, 0.0, {}
+    for name in names:
+        spec = synth.layer_spec(workload, name)
         w_bits = synth.make_weight(spec, 0)
         wd = torch.from_numpy(w_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-        if name == "down":
-            xg, wg = gate_up
+        if spec.x_kind == "silu_gate_up":
+            xg, wg = sources.pop(spec.source)
             F = spec.K
-            h = torch.empty((spec.M, F), dtype=torch.bfloat16, device=dev)
+            xd = torch.empty((spec.M, F), dtype=torch.bfloat16, device=dev)
             for r0 in range(0, spec.M, 8192):
                 xc = xg[r0:r0 + 8192].double()
                 g = xc @ wg[:F].double().T
                 u = xc @ wg[F:].double().T
-                h[r0:r0 + 8192] = (g * torch.sigmoid(g) * u).float().to(torch.bfloat16)
+                xd[r0:r0 + 8192] = (g * torch.sigmoid(g) * u).float().to(torch.bfloat16)
                 del xc, g, u
-            xd = h
-            gate_up = None
         else:
             x_bits = synth.make_activations(spec, seed=0)
             xd = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-            if name == "gate_up":
-                gate_up = (xd, wd)
-        awq.search_scale(xd, wd, 4, spec.group, spec.n_grid)
+            if any(synth.layer_spec(workload, n).source == name for n in names):
+                sources[name] = (xd, wd)
+        bits = spec.bits[-1]
+        awq.search_scale(xd, wd, bits, spec.group, spec.n_grid)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
-            r = awq.search_scale(xd, wd, 4, spec.group, spec.n_grid)
+            r = awq.search_scale(xd, wd, bits, spec.group, spec.n_grid)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
         total += ms
         tflops = 2.0 * spec.M * spec.N * spec.K * spec.n_grid / (ms * 1e-3) / 1e12
-        res[name] = {"M": spec.M, "K": spec.K, "N": spec.N, "ms_per_layer": ms,
+        res[name] = {"M": spec.M, "K": spec.K, "N": spec.N, "bits": bits, "ms_per_layer": ms,
                      "best_idx": int(r["best_idx"].item()), "tflops_candidate_products": tflops}
-        log(f"Llama-3-8B block {name} ({spec.M} x {spec.K} -> {spec.N}): {ms:.1f} ms/layer, "
+        log(f"{workload} {name} ({spec.M} x {spec.K} -> {spec.N}, INT{bits}): {ms:.1f} ms/layer, "
             f"{tflops:.0f} TFLOP/s in the candidate products, alpha index {res[name]['best_idx']}")
         del xd, wd
         torch.cuda.empty_cache()
-    res["ms_per_block"] = total
-    res["blocks_per_s"] = 1e3 / total
-    log(f"Llama-3-8B block: {total:.1f} ms per block, {1e3 / total:.2f} blocks/s")
+    res["ms_total"] = total
+    res["per_s"] = 1e3 / total
+    log(f"{workload}: {total:.1f} ms for its {len(names)} layers, {1e3 / total:.2f} per second")
     return res
 
 
@@ -853,7 +851,10 @@ def main() -> int:
         result["variants"]["block_pipeline_llama2_7b_mlp"] = bench_pipeline(awq, dev, stream)
         torch.cuda.empty_cache()
     if not args.no_largest:
-        result["variants"]["search_llama3_8b_block"] = bench_llama3_block(awq, dev)
+        result["variants"]["search_llama2_7b_mlp"] = bench_workload_layers(
+            awq, dev, "llama2_7b_mlp", ("gate_up", "down"))
+        result["variants"]["search_llama3_8b_block"] = bench_workload_layers(
+            awq, dev, "llama3_8b_block", ("qkv", "o_proj", "gate_up", "down"))
         result["variants"]["search_llama2_70b_down"] = bench_largest_layer(awq, dev)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_m} tokens x {args.cpu_n} rows")
