@@ -344,6 +344,27 @@ def test_search_is_bit_reproducible(dev):
         assert torch.equal(a[k], b[k]), k
 
 
+def test_searches_on_two_streams_at_once(dev):
+    """Two searches in flight on two streams (each with its own outputs and
+    workspace) give the same results as one after the other: the library
+    keeps no mutable state between calls."""
+    announce("search on two streams")
+    layers = [layer(SHAPES[1]), layer(SHAPES[4])]
+    dl = [(to_dev_bf16(x, dev), to_dev_bf16(w, dev)) for x, w in layers]
+    seq = [awq.search_scale(xd, wd) for xd, wd in dl]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+    par = [None, None]
+    for rep in range(3):
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                par[i] = awq.search_scale(*dl[i])
+        torch.cuda.synchronize()
+        for a, b in zip(seq, par):
+            for k in a:
+                assert torch.equal(a[k], b[k]), (rep, k)
+
+
 def test_gemm_empty_and_degenerate(dev):
     announce("gemm empty")
     x = torch.zeros((0, 128), dtype=torch.bfloat16, device=dev)
