@@ -26,11 +26,12 @@
 // Work split.  At these sizes a call is dominated by fixed latency (a kernel
 // costs several microseconds before it streams a byte), so the layer should be
 // in flight at once, in as few kernels as possible.  A workgroup owns 16, 32
-// or 64 output channels and a range of at most 64 groups along K; its 4 waves
-// split that range, and each wave streams its columns' codes through a ring
-// of two groups.  The waves' partial outputs are summed through LDS in wave
-// order, so results do not depend on timing.  Only layers with K > 8192 also
-// split K across workgroups; those write fp32 partials that a second kernel
+// or 64 output channels and a range of at most 64 groups along K (32 above 16
+// tokens); its 4 waves split that range, and each wave streams its columns'
+// codes through a ring of two groups.  The waves' partial outputs are summed
+// through LDS in wave order, so results do not depend on timing.  Only layers
+// whose K exceeds that range also split K across workgroups; those write fp32
+// partials that a second kernel
 // sums in split order.  More columns per workgroup let one activation
 // fragment feed more codes, which pays when M is large or the layer is wide
 // enough to keep every CU busy anyway (the rule in decode_blocks_per_group

@@ -6,8 +6,8 @@
 //
 // Layout: 8 lanes own one 128-channel group, 16 channels (32 B of bf16) per
 // lane, so a wave covers 8 groups = 2 KiB of one row.  A block of 256 lanes
-// spans 32 groups and walks kRows rows; each lane loads its 16 scale factors
-// once.  Group min/max is reduced with three DPP steps inside each 8-lane
+// spans 32 groups and walks rows kRows at a time in a grid-stride loop; each
+// lane loads its 16 scale factors once.  Group min/max is reduced with three DPP steps inside each 8-lane
 // segment (quad swaps, then the half-row mirror); each lane writes two u32 of
 // packed nibbles.  Every arithmetic step is one IEEE fp32 operation, in the
 // order of the contract: ws = w*s; step = (max(mx,0) - min(mn,0)) / qmax
