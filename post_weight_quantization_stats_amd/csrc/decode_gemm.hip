@@ -31,8 +31,8 @@
 // codes through a ring of two groups.  The waves' partial outputs are summed
 // through LDS in wave order, so results do not depend on timing.  Only layers
 // whose K exceeds that range also split K across workgroups; those write fp32
-// partials that a second kernel
-// sums in split order.  More columns per workgroup let one activation
+// partials that a second kernel sums in split order.  More columns per
+// workgroup let one activation
 // fragment feed more codes, which pays when M is large or the layer is wide
 // enough to keep every CU busy anyway (the rule in decode_blocks_per_group
 // was measured on the Llama-3-8B block's layers).
