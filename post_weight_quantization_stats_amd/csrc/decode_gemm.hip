@@ -20,8 +20,10 @@
 //     sum A).  The products are exact in fp32, so the result is the
 //     fp32-accumulated value of sum_k A * (q - z) * step.
 //
-// Up to 64 tokens: MB 16-row blocks of A per workgroup; each group's codes
-// are turned into bf16 once and feed every row block.
+// Up to 64 tokens: MB (1 or 2) 16-row blocks of A per workgroup; each
+// group's codes are turned into bf16 once and feed every row block.  More
+// tokens than that go to further workgroups along the grid's z, each
+// re-reading the same codes (from L2 once the first has fetched them).
 //
 // Work split.  At these sizes a call is dominated by fixed latency (a kernel
 // costs several microseconds before it streams a byte), so the layer should be
@@ -32,10 +34,9 @@
 // through LDS in wave order, so results do not depend on timing.  Only layers
 // whose K exceeds that range also split K across workgroups; those write fp32
 // partials that a second kernel sums in split order.  More columns per
-// workgroup let one activation
-// fragment feed more codes, which pays when M is large or the layer is wide
-// enough to keep every CU busy anyway (the rule in decode_blocks_per_group
-// was measured on the Llama-3-8B block's layers).
+// workgroup let one activation fragment feed more codes, which pays when M is
+// large or the layer is wide enough to keep every CU busy anyway (the rule in
+// decode_blocks_per_group was measured on the Llama-3-8B block's layers).
 // Tiled weights (TL): the packed codes rearranged once so that a wave's
 // code load for one 16-column block and one group is a single contiguous
 // 1 KiB (768 B for dense INT3) piece in lane order: tile b*G + g holds rows
@@ -66,6 +67,11 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kDepth = 2;                     // groups of codes in flight per wave
 constexpr int kWaveGroups = 16;               // most groups per wave
 constexpr int kBlockGroups = kWaves * kWaveGroups;   // 64 groups = 8192 channels
+// Token blocks of 16 per workgroup: more tokens go to more workgroups along
+// the grid's z (measured on the Llama-3-8B layers at 48 and 64 tokens: two
+// blocks per workgroup beat four by up to 9%, and one block was slower on
+// the wide layers).
+constexpr int kMaxTokenBlocks = 2;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -173,8 +179,9 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
   const int64_t M = p.M, N = p.N, K = p.K;
   // A rows past M repeat row M-1 (their outputs are never stored).
   int arow[MB];
+  const int m0 = (int)blockIdx.z * 16 * MB;         // this workgroup's first token
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) arow[mb] = min(16 * mb + c16, (int)M - 1);
+  for (int mb = 0; mb < MB; ++mb) arow[mb] = min(m0 + 16 * mb + c16, (int)M - 1);
   const int64_t G = K / kGroup;
   const int64_t n_blk = (int64_t)blockIdx.x * kCols;
   // This workgroup's groups [gb0, gb1); this wave's [g0, g0 + gn).
@@ -361,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t m = 16 * mb + 4 * g4 + i;
+          const int64_t m = m0 + 16 * mb + 4 * g4 + i;
           if (m < M) out[m * N + n] = y[mb][b][i];
         }
     }
@@ -481,9 +488,11 @@ template <bool H16>
 hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* ws,
                            hipStream_t stream, bool int3_dense, bool tiled) {
   const int64_t M = p.M, N = p.N;
-  const int nb = decode_blocks_per_group(M, N, d.splits);
-  const int mb = (int)ceil_div(M, (int64_t)16);
-  dim3 grid((unsigned)ceil_div(N, (int64_t)16 * nb), (unsigned)d.splits);
+  const int mb_all = (int)ceil_div(M, (int64_t)16);
+  const int mb = std::min(mb_all, kMaxTokenBlocks);
+  const int tz = (int)ceil_div((int64_t)mb_all, (int64_t)mb);   // token groups
+  const int nb = decode_blocks_per_group(std::min(M, (int64_t)16 * mb), N, d.splits);
+  dim3 grid((unsigned)ceil_div(N, (int64_t)16 * nb), (unsigned)d.splits, (unsigned)tz);
   auto go = [&](auto NBc, auto MBc) {
     constexpr int nbv = decltype(NBc)::value, mbv = decltype(MBc)::value;
     if constexpr (H16) {
@@ -504,12 +513,11 @@ hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* 
     }
   };
   auto go_mb = [&](auto NBc) {
+    static_assert(kMaxTokenBlocks == 2, "instantiations below cover 1 or 2 token blocks");
     if (mb == 1)
       go(NBc, std::integral_constant<int, 1>{});
-    else if (mb == 2)
-      go(NBc, std::integral_constant<int, 2>{});
     else
-      go(NBc, std::integral_constant<int, 4>{});
+      go(NBc, std::integral_constant<int, 2>{});
   };
   if (nb == 4)
     go_mb(std::integral_constant<int, 4>{});
