@@ -491,8 +491,9 @@ hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* 
   const int mb_all = (int)ceil_div(M, (int64_t)16);
   // Narrow layers (fewer than 512 column blocks, K splits included) above 32
   // tokens take one token block per workgroup: more workgroups in flight
-  // there beat sharing the converted codes (Llama-3-8B qkv at M = 48 and 64,
-  // 17.2 -> 16.6 and 20.0 -> 16.8 us; the wide layers were slower so).
+  // there beat sharing the converted codes (Llama-3-8B qkv at M = 48 and 64:
+  // 17.2 -> 16.6 and 20.0 -> 16.8 us; the wide gate_up and down layers were
+  // slower with one block).
   const int64_t b1 = ceil_div(N, (int64_t)16) * d.splits;
   const int mb = (M > 32 && b1 < 512) ? 1 : std::min(mb_all, kMaxTokenBlocks);
   const int tz = (int)ceil_div((int64_t)mb_all, (int64_t)mb);   // token groups
