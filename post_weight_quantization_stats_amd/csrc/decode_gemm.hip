@@ -29,7 +29,8 @@
 // costs several microseconds before it streams a byte), so the layer should be
 // in flight at once, in as few kernels as possible.  A workgroup owns 16, 32
 // or 64 output channels and a range of at most 64 groups along K (32 above 16
-// tokens); its 4 waves split that range, and each wave streams its columns'
+// tokens; 128 at up to 4 tokens when that leaves K unsplit, with 8 waves
+// instead of 4); its waves split that range, and each wave streams its columns'
 // codes through a ring of two groups.  The waves' partial outputs are summed
 // through LDS in wave order, so results do not depend on timing.  Only layers
 // whose K exceeds that range also split K across workgroups; those write fp32
@@ -62,8 +63,8 @@ namespace awq {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = 4;                     // waves per workgroup (kWavesWide: see decode_plan)
+constexpr int kWavesWide = 8;
 constexpr int kDepth = 2;                     // groups of codes in flight per wave
 constexpr int kWaveGroups = 16;               // most groups per wave
 constexpr int kBlockGroups = kWaves * kWaveGroups;   // 64 groups = 8192 channels
@@ -164,12 +165,13 @@ struct GroupLoads {
 // NB 16-column blocks per workgroup (all of its waves work on them) and MB
 // 16-row blocks of tokens (M <= 16 * MB); I3: dense INT3 codes; TL: tiled;
 // H16: the compact metadata (binary16 steps, 4-bit zeros).
-template <int NB, int MB, bool I3, bool TL, bool H16 = false>
-__global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
+// W waves per workgroup.
+template <int NB, int MB, bool I3, bool TL, bool H16 = false, int W = kWaves>
+__global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int kCols = 16 * NB;
-  __shared__ float2 ssz[kWaves][kCols][kWaveGroups];    // (step, 128 + z), 8 to 32 KiB
-  __shared__ f32x4 red[kWaves - 1][MB][NB][64];          // partial outputs of waves 1..3
+  __shared__ float2 ssz[W][kCols][kWaveGroups];    // (step, 128 + z), 8 to 64 KiB
+  __shared__ f32x4 red[W - 1][MB][NB][64];          // partial outputs of waves 1..W-1
 
   const int lane = threadIdx.x & 63;
   // Wave index in an SGPR, so the buffer resources below are scalar.
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
   // This workgroup's groups [gb0, gb1); this wave's [g0, g0 + gn).
   const int64_t gb0 = (int64_t)blockIdx.y * p.groups_per_split;
   const int64_t gb1 = min(G, gb0 + p.groups_per_split);
-  const int64_t per = (gb1 - gb0 + kWaves - 1) / kWaves;            // <= kWaveGroups
+  const int64_t per = (gb1 - gb0 + W - 1) / W;                      // <= kWaveGroups
   const int64_t g0 = gb0 + wave * per;
   const int gn = (int)max((int64_t)0, min(gb1, g0 + per) - g0);
 
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecodeParams p) {
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w)
+  for (int w = 0; w < W - 1; ++w)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -458,7 +460,14 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
   // group), so workgroups take at most 32 groups and more of them share K:
   // measured on the Llama-3-8B down layer (K = 14336) at M = 32 and 64,
   // 22.3 -> 20.3 and 35.1 -> 29.0 us; 16 groups per workgroup was slower.
-  const int64_t max_groups = M > 16 ? kBlockGroups / 2 : kBlockGroups;
+  int64_t max_groups = M > 16 ? kBlockGroups / 2 : kBlockGroups;
+  // Up to 4 tokens, a K of 65 to 128 groups goes to one workgroup of
+  // kWavesWide waves rather than to two workgroups and a second kernel that
+  // sums their partials: measured on the Llama-3-8B down layer (K = 14336)
+  // at M = 1 and 4, 14.5 -> 10.7 and 13.1 -> 11.3 us.  At 16 tokens the
+  // wide workgroup was slower (14.9 -> 18.8 us), and 8 waves over 64 groups
+  // or fewer were slower at every M.
+  if (M <= 4 && G > kBlockGroups && G <= 2 * kBlockGroups) max_groups = 2 * kBlockGroups;
   d.splits = ceil_div(G, max_groups);
   d.groups_per_split = ceil_div(G, d.splits);
   d.ws_bytes = d.splits > 1 ? align_up((size_t)d.splits * M * N * sizeof(float)) : 0;
@@ -499,31 +508,43 @@ hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* 
   const int tz = (int)ceil_div((int64_t)mb_all, (int64_t)mb);   // token groups
   const int nb = decode_blocks_per_group(std::min(M, (int64_t)16 * mb), N, d.splits);
   dim3 grid((unsigned)ceil_div(N, (int64_t)16 * nb), (unsigned)d.splits, (unsigned)tz);
-  auto go = [&](auto NBc, auto MBc) {
+  // More groups per workgroup than kWaves waves can take: the wide
+  // workgroup (decode_plan gives it only to M <= 4, so one token block and
+  // at most 2 column blocks).
+  const bool wide = d.groups_per_split > kBlockGroups;
+  if (wide && (mb != 1 || nb > 2 || d.groups_per_split > kWavesWide * kWaveGroups))
+    return hipErrorInvalidValue;
+  auto go = [&](auto NBc, auto MBc, auto Wc) {
     constexpr int nbv = decltype(NBc)::value, mbv = decltype(MBc)::value;
+    constexpr int wv = decltype(Wc)::value;
+    const unsigned threads = 64 * wv;
     if constexpr (H16) {
       // The compact metadata is read with tiled codes only.
       if (int3_dense)
-        decode_gemm_kernel<nbv, mbv, true, true, true><<<grid, kThreads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, true, true, true, wv><<<grid, threads, 0, stream>>>(p);
       else
-        decode_gemm_kernel<nbv, mbv, false, true, true><<<grid, kThreads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, false, true, true, wv><<<grid, threads, 0, stream>>>(p);
     } else {
       if (int3_dense && tiled)
-        decode_gemm_kernel<nbv, mbv, true, true><<<grid, kThreads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, true, true, false, wv><<<grid, threads, 0, stream>>>(p);
       else if (int3_dense)
-        decode_gemm_kernel<nbv, mbv, true, false><<<grid, kThreads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, true, false, false, wv><<<grid, threads, 0, stream>>>(p);
       else if (tiled)
-        decode_gemm_kernel<nbv, mbv, false, true><<<grid, kThreads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, false, true, false, wv><<<grid, threads, 0, stream>>>(p);
       else
-        decode_gemm_kernel<nbv, mbv, false, false><<<grid, kThreads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, false, false, false, wv><<<grid, threads, 0, stream>>>(p);
     }
   };
   auto go_mb = [&](auto NBc) {
     static_assert(kMaxTokenBlocks == 2, "instantiations below cover 1 or 2 token blocks");
+    using One = std::integral_constant<int, 1>;
+    if constexpr (decltype(NBc)::value <= 2) {
+      if (wide) return go(NBc, One{}, std::integral_constant<int, kWavesWide>{});
+    }
     if (mb == 1)
-      go(NBc, std::integral_constant<int, 1>{});
+      go(NBc, One{}, std::integral_constant<int, kWaves>{});
     else
-      go(NBc, std::integral_constant<int, 2>{});
+      go(NBc, std::integral_constant<int, 2>{}, std::integral_constant<int, kWaves>{});
   };
   if (nb == 4)
     go_mb(std::integral_constant<int, 4>{});

@@ -111,7 +111,8 @@ def test_expand_meta16_exact(dev):
 
 DECODE_SHAPES = [(1, 64, 128), (2, 200, 384), (3, 1000, 1152), (16, 6144, 4096),
                  (16, 40960, 512), (2, 520, 16512), (1, 72, 32768), (33, 40, 640),
-                 (64, 4096, 4096), (48, 520, 16512), (45, 8200, 256)]
+                 (64, 4096, 4096), (48, 520, 16512), (45, 8200, 256),
+                 (3, 200, 16384)]
 
 
 @pytest.mark.parametrize("dense3", [False, True], ids=["nibble", "int3dense"])

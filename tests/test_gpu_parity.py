@@ -406,12 +406,14 @@ def run_decode(dev, M, N, K, bits, seed):
 # and split across workgroups (K > 8192), ragged N, one group, odd token
 # counts, narrow and wide layers (16-, 32- and 64-column workgroups), and
 # more than 32 tokens split over several token groups of one or two 16-token
-# blocks (the last group ragged at M = 33 and 45).
+# blocks (the last group ragged at M = 33 and 45); up to 4 tokens, 65 to 128
+# groups on one workgroup of 8 waves (the last wave's range ragged at 65).
 DECODE_SHAPES = [(1, 64, 128), (2, 200, 256), (3, 1000, 1024), (4, 4096, 4096), (8, 520, 2048),
                  (13, 4104, 384), (16, 6144, 4096), (16, 40960, 512), (5, 16, 1152),
                  (2, 520, 16512), (1, 72, 32768), (16, 8200, 16384),
                  (17, 1000, 1024), (32, 6144, 4096), (48, 520, 16512), (64, 4096, 4096),
-                 (64, 20000, 640), (33, 40, 128), (45, 8200, 256)]
+                 (64, 20000, 640), (33, 40, 128), (45, 8200, 256),
+                 (1, 4096, 14336), (3, 200, 16384), (2, 40, 8320), (4, 16392, 8320)]
 
 
 @pytest.mark.parametrize("bits", [4, 3])
@@ -481,7 +483,7 @@ def test_quantize_pack3_bit_exact(dev, shape):
 
 INT3_DECODE_SHAPES = [(1, 64, 128), (3, 1000, 1024), (16, 6144, 4096), (16, 40960, 512),
                       (2, 520, 16512), (64, 4096, 4096), (33, 40, 128), (1, 72, 32768),
-                      (45, 8200, 256)]
+                      (45, 8200, 256), (2, 40, 8320)]
 
 
 @pytest.mark.parametrize("shape", INT3_DECODE_SHAPES, ids=lambda s: f"M{s[0]}_N{s[1]}_K{s[2]}")
