@@ -96,11 +96,16 @@ KERNEL_LABELS = [
     ("decode_tiles_kernel", "decode tiles"),
     ("transpose_pad_kernel", "X^T (Gram form)"),
     ("gram_split_kernel", "G split (Gram form)"),
-    (("decode_gemm_kernel<", ", true, true>"), "decode GEMM, tiles, compact metadata"),
-    (("decode_gemm_kernel<", ", false, true, false>"), "decode GEMM, tiles"),
-    (("decode_gemm_kernel<", ", true, true, false>"), "decode GEMM, dense INT3 tiles"),
-    (("decode_gemm_kernel<", ", false, false, false>"), "decode GEMM, row-major words"),
-    (("decode_gemm_kernel<", ", true, false, false>"), "decode GEMM, dense INT3 row-major"),
+    # decode_gemm_kernel<column blocks, token blocks, INT3 dense, tiled,
+    # compact metadata, waves>
+    *[(("decode_gemm_kernel<", f", {flags}, {waves}>"), label + ("" if waves == 4 else ", 8 waves"))
+      for flags, label in (("false, true, true", "decode GEMM, tiles, compact metadata"),
+                           ("true, true, true", "decode GEMM, dense INT3 tiles, compact metadata"),
+                           ("false, true, false", "decode GEMM, tiles"),
+                           ("true, true, false", "decode GEMM, dense INT3 tiles"),
+                           ("false, false, false", "decode GEMM, row-major words"),
+                           ("true, false, false", "decode GEMM, dense INT3 row-major"))
+      for waves in (4, 8)],
     ("decode_gemm", "decode W4A16 GEMM (M <= 64)"),
     ("decode_reduce", "decode split-K reduce"),
     ("act_stats_partial", "act_stats partial sums"),
