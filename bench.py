@@ -647,8 +647,8 @@ def main() -> int:
                          "(Llama-2-70B down)")
     ap.add_argument("--decode-case", default=None, metavar="LAYER:M",
                     help="only one decode case of the Llama-3-8B block, e.g. gate_up:1")
-    ap.add_argument("--cpu-m", type=int, default=4096)
-    ap.add_argument("--cpu-n", type=int, default=2048)
+    ap.add_argument("--cpu-m", type=int, default=8192)
+    ap.add_argument("--cpu-n", type=int, default=4096)
     ap.add_argument("--summarize-trace", metavar="DIR", default=None,
                     help="write a summary of a rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
