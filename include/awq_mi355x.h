@@ -259,7 +259,7 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
  *   y       f32 [M][N] output
  *   ws      awq_workspace_size(AWQ_OP_DECODE_GEMM) bytes (fp32 partials
  *           when K is split across workgroups: K > 8192, or K > 16384 for
- *           M <= 4, or K > 4096 for M > 16; 0 otherwise, and ws may then be
+ *           M <= 6, or K > 4096 for M > 16; 0 otherwise, and ws may then be
  *           NULL).
  * M > 64 gives AWQ_ERR_SHAPE (use awq_w4a16_gemm).  M == 0 or N == 0 is a
  * no-op.  Results are bit-reproducible for a given (M, N, K).

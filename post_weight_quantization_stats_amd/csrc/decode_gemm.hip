@@ -29,7 +29,7 @@
 // costs several microseconds before it streams a byte), so the layer should be
 // in flight at once, in as few kernels as possible.  A workgroup owns 16, 32
 // or 64 output channels and a range of at most 64 groups along K (32 above 16
-// tokens; 128 at up to 4 tokens when K exceeds 64 groups, with 8 waves
+// tokens; 128 at up to 6 tokens when K exceeds 64 groups, with 8 waves
 // instead of 4); its waves split that range, and each wave streams its columns'
 // codes through a ring of two groups.  The waves' partial outputs are summed
 // through LDS in wave order, so results do not depend on timing.  Only layers
@@ -461,15 +461,17 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
   // measured on the Llama-3-8B down layer (K = 14336) at M = 32 and 64,
   // 22.3 -> 20.3 and 35.1 -> 29.0 us; 16 groups per workgroup was slower.
   int64_t max_groups = M > 16 ? kBlockGroups / 2 : kBlockGroups;
-  // Up to 4 tokens, a K of more than 64 groups goes to workgroups of
+  // Up to 6 tokens, a K of more than 64 groups goes to workgroups of
   // kWavesWide waves and up to 128 groups, which halves the K splits (none
   // at all up to 128 groups, so no second kernel sums partials).  Measured
   // on the Llama-3-8B down layer (K = 14336) at M = 1 and 4: 14.5 -> 10.7
   // and 13.1 -> 11.3 us; on the Llama-2-70B down layer (K = 28672, dense
-  // INT3) at M = 1, 2 and 4: 29.1 -> 26.6, 28.1 -> 26.8, 29.3 -> 27.4 us.
-  // At 16 tokens the wide workgroup was slower (8B down, 14.9 -> 18.8 us),
-  // and 8 waves over 64 groups or fewer were slower at every M.
-  if (M <= 4 && G > kBlockGroups) max_groups = 2 * kBlockGroups;
+  // INT3) at M = 1, 2 and 4: 29.1 -> 26.6, 28.1 -> 26.8, 29.3 -> 27.4 us;
+  // at M = 5 and 6 on 8B down 12.8 -> 11.6 and 13.3 -> 11.6 us.  At 8
+  // tokens it was mixed (8B down 12.7 -> 13.1 us, 70B down 31.9 -> 30.6 us),
+  // at 16 slower (8B down, 14.9 -> 18.8 us), and 8 waves over 64 groups or
+  // fewer were slower at every M.
+  if (M <= 6 && G > kBlockGroups) max_groups = 2 * kBlockGroups;
   d.splits = ceil_div(G, max_groups);
   d.groups_per_split = ceil_div(G, d.splits);
   d.ws_bytes = d.splits > 1 ? align_up((size_t)d.splits * M * N * sizeof(float)) : 0;
@@ -511,7 +513,7 @@ hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* 
   const int nb = decode_blocks_per_group(std::min(M, (int64_t)16 * mb), N, d.splits);
   dim3 grid((unsigned)ceil_div(N, (int64_t)16 * nb), (unsigned)d.splits, (unsigned)tz);
   // More groups per workgroup than kWaves waves can take: the wide
-  // workgroup (decode_plan gives it only to M <= 4, so one token block and
+  // workgroup (decode_plan gives it only to M <= 6, so one token block and
   // at most 2 column blocks).
   const bool wide = d.groups_per_split > kBlockGroups;
   if (wide && (mb != 1 || nb > 2 || d.groups_per_split > kWavesWide * kWaveGroups))

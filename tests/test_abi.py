@@ -188,18 +188,19 @@ def test_decode_gemm_errors_and_plan():
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 4, 128, 4096) == 0
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 4096, 8192) == 0
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 4096, 8320) > 0
-    # Up to 4 tokens, one workgroup of 8 waves covers up to 128 groups (and
+    # Up to 6 tokens, one workgroup of 8 waves covers up to 128 groups (and
     # beyond, workgroups of 128 groups halve the splits).
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 4, 4096, 14336) == 0
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 1, 4096, 16384) == 0
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 4, 4096, 16512) >= 2 * 4 * 4096 * 4
-    assert awq.workspace_size(awq.OP_DECODE_GEMM, 5, 4096, 8320) >= 2 * 5 * 4096 * 4
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 6, 4096, 14336) == 0
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 7, 4096, 8320) >= 2 * 7 * 4096 * 4
     # Above 16 tokens a workgroup takes at most 32 groups (4096 channels).
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 17, 4096, 4096) == 0
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 17, 4096, 4224) >= 2 * 17 * 4096 * 4
     need = awq.workspace_size(awq.OP_DECODE_GEMM, 4, 128, 32768)
     assert need >= 2 * 4 * 128 * 4
-    assert awq.workspace_size(awq.OP_DECODE_GEMM, 5, 128, 32768) >= 4 * 5 * 128 * 4
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 7, 128, 32768) >= 4 * 7 * 128 * 4
     assert call(K=32768) == WORKSPACE
     assert call(K=32768, ws=FAKE, wsb=need - 1) == WORKSPACE
 

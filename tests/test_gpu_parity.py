@@ -406,14 +406,16 @@ def run_decode(dev, M, N, K, bits, seed):
 # and split across workgroups (K > 8192), ragged N, one group, odd token
 # counts, narrow and wide layers (16-, 32- and 64-column workgroups), and
 # more than 32 tokens split over several token groups of one or two 16-token
-# blocks (the last group ragged at M = 33 and 45); up to 4 tokens, 65 to 128
-# groups on one workgroup of 8 waves (the last wave's range ragged at 65).
+# blocks (the last group ragged at M = 33 and 45); up to 6 tokens, 65 to 128
+# groups on one workgroup of 8 waves (the last wave's range ragged at 65),
+# and more on several such workgroups.
 DECODE_SHAPES = [(1, 64, 128), (2, 200, 256), (3, 1000, 1024), (4, 4096, 4096), (8, 520, 2048),
                  (13, 4104, 384), (16, 6144, 4096), (16, 40960, 512), (5, 16, 1152),
                  (2, 520, 16512), (1, 72, 32768), (16, 8200, 16384),
                  (17, 1000, 1024), (32, 6144, 4096), (48, 520, 16512), (64, 4096, 4096),
                  (64, 20000, 640), (33, 40, 128), (45, 8200, 256),
-                 (1, 4096, 14336), (3, 200, 16384), (2, 40, 8320), (4, 16392, 8320)]
+                 (1, 4096, 14336), (3, 200, 16384), (2, 40, 8320), (4, 16392, 8320),
+                 (6, 40, 8320), (5, 520, 16512), (7, 40, 8320)]
 
 
 @pytest.mark.parametrize("bits", [4, 3])
