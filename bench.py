@@ -2,12 +2,13 @@
 """Throughput of the AWQ per-layer scale search on one MI355X.
 
 One step = one whole search over one layer (activation statistics, 20
-candidate scales, the fp32 reference product, 20 x (quantize to the
-candidate's bf16 operand + contraction with fused squared error), loss
-reduction, argmin, final quantize + pack) with the inputs already resident
-in HBM.  Default workload: a Llama-2-7B
-shaped fused QKV layer, 65536 calibration tokens, K=4096 -> N=12288, INT4,
-group 128, 20 grid points, seeded synthetic data.
+candidate scales, 20 x (quantize to the candidate's difference operand +
+contraction with the fused sum of squares), loss reduction, argmin, final
+quantize + pack) with the inputs already resident in HBM.  Default workload:
+the workloads' largest layer, a Llama-2-70B-shaped MLP gate/up projection,
+16384 calibration tokens, K=8192 -> N=2x28672, INT4, group 128, 20 grid
+points, seeded synthetic data; the same layer at INT3, the Llama-2-7B fused
+QKV layer and every other workload layer are reported beside it.
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
 the stream the kernels are launched on; the roofline block uses the
@@ -35,7 +36,11 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "AWQ search: layers/s + W4A16 GEMM TFLOP/s (% MFMA peak), quant GB/s (% HBM)"
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "search_contraction_llama2_7b_qkv_traffic.txt")
+HEADLINE = ("llama2_70b_mlp", "gate_up", 4)
+
+
+def traffic_file(workload: str, layer: str) -> str:
+    return os.path.join(PROFILES, f"search_contraction_{workload}_{layer}_traffic.txt")
 # The search's per-candidate contraction X . D^T with the sum-of-squares epilogue.
 DOMINANT_KERNEL = "gemm_kernel<false, false, 4, false, true, false, true>"
 GEMM_SOURCES = ["w4a16_gemm.hip", "device_common.h", "awq_internal.h"]
@@ -52,13 +57,13 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
-    """HBM bytes per launch of the search's dominant contraction from the
-    committed rocprofv3 counter summary, or None when the kernel source
-    changed since it was taken."""
+def committed_traffic(workload: str, layer: str):
+    """HBM bytes per launch of the search's dominant contraction on this
+    layer from the committed rocprofv3 counter summary, or None when there is
+    none or the kernel source changed since it was taken."""
     try:
         fields = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload, layer)) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
@@ -240,10 +245,12 @@ def summarize_pmc(fetch_dir: str, write_dir: str, commands: str, M: int, K: int)
     write = _per_kernel_counter(_read_csv(_find(write_dir, "counter_collection.csv")), "WRITE_SIZE")
 
     def calib(per, nbytes):
-        cands = [(max(v), k) for k, v in per.items() if "copy" in k and "awq::" not in k]
+        # The bench's calibration copy is torch's bf16 -> fp32 conversion of
+        # X (other copies, e.g. of W, can be larger, so match it by name).
+        cands = [(v[0], k) for k, v in per.items() if "bfloat16tofloat32" in k]
         if not cands:
-            raise SystemExit("calibration copy kernel not found")
-        kib, _ = max(cands)
+            raise SystemExit("calibration copy kernel (bf16 -> fp32) not found")
+        kib, _ = cands[0]
         return nbytes / (kib * 1024.0), kib
 
     f_read, kib_r = calib(fetch, 2.0 * M * K)
@@ -600,9 +607,10 @@ def bench_pipeline(awq, dev, stream, n_blocks: int = 2, M: int = 65536, d: int =
                         "bytes": nb} for k, (nb, t) in ops.items()}}
 
 
-def cpu_baseline(x_bits, w_bits, spec, m_sample: int, n_sample: int) -> dict:
+def cpu_baseline(x_bits, w_bits, spec, bits: int, m_sample: int, n_sample: int) -> dict:
     """Oracle (numpy fp64) on a token prefix x output-row prefix; each phase is
-    scaled to the full layer by the dimension it is linear in."""
+    scaled to the full layer by the dimension it is linear in.  Records the
+    host's CPU model and the ROCm version beside the figure."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -613,16 +621,97 @@ def cpu_baseline(x_bits, w_bits, spec, m_sample: int, n_sample: int) -> dict:
     ws = np.ascontiguousarray(w_bits[:n_sample])
     t = {}
     t0 = time.perf_counter()
-    O.search(xs, ws, spec.bits[-1], spec.group, spec.n_grid, loss_form="direct", timings=t)
+    O.search(xs, ws, bits, spec.group, spec.n_grid, loss_form="direct", timings=t)
     wall = time.perf_counter() - t0
     M, N = spec.M, spec.N
     full = (t["stats_and_scales"] * (M / m_sample) + t["quantize"] * (N / n_sample) +
             t["loss"] * (M / m_sample) * (N / n_sample) + t["final_pack"] * (N / n_sample))
+    info = host_info()
     return {"value": 1.0 / full, "unit": "layers/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"full {spec.n_grid}-point search on the first {m_sample} tokens x first "
-                       f"{n_sample} output rows (K={spec.K}) in {wall:.1f} s; phases scaled to "
-                       f"M={M}, N={N} (stats by M, quantize by N, loss by M*N)"),
-            "seconds_sample": wall, "seconds_full_layer_est": full}
+            "sample": (f"full {spec.n_grid}-point INT{bits} search on the first {m_sample} tokens x "
+                       f"first {n_sample} output rows (K={spec.K}) in {wall:.1f} s; phases scaled "
+                       f"to M={M}, N={N} (stats by M, quantize by N, loss by M*N)"),
+            "seconds_sample": wall, "seconds_full_layer_est": full,
+            "cpu_model": info["cpu_model"], "host_threads": info["host_threads"],
+            "rocm": info["rocm"]}
+
+
+def host_info() -> dict:
+    """CPU model, host threads and the ROCm / torch versions of this run."""
+    info = {"cpu_model": None, "host_threads": len(os.sched_getaffinity(0)), "rocm": None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        import torch
+        info["torch"] = torch.__version__
+        info["torch_hip"] = torch.version.hip
+    except Exception:
+        pass
+    return info
+
+
+def to_dev(bits: np.ndarray, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def time_search(awq, xd, wd, bits: int, spec, steps: int, warmup: int = 1, ws=None):
+    """Wall time per layer of awq_search_scale (device-synchronised)."""
+    import torch
+    out = None
+    for _ in range(warmup):
+        out = awq.search_scale(xd, wd, bits, spec.group, spec.n_grid, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        out = awq.search_scale(xd, wd, bits, spec.group, spec.n_grid, workspace=ws)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps, out
+
+
+def bench_qkv_layer(awq, dev, stream, steps: int, reps: int, with_gram: bool) -> dict:
+    """The Llama-2-7B fused QKV layer (65536 tokens x 4096 -> 12288, INT4):
+    the search, its contraction, and the Gram-form search (which pays here,
+    since 2K < M)."""
+    import torch
+
+    import synth
+    spec = synth.layer_spec("llama2_7b_qkv")
+    x_bits, w_bits, _ = synth.make_layer(spec.workload, spec.name)
+    xd, wd = to_dev(x_bits, dev), to_dev(w_bits, dev)
+    del x_bits, w_bits
+    ms, out = time_search(awq, xd, wd, 4, spec, steps, warmup=2)
+    M, K, N, G = spec.M, spec.K, spec.N, spec.n_grid
+    s_all, inv_all = awq.candidate_scales(out["mean_abs"], G)
+    d_mid = awq.diff_operand(wd, s_all[G // 2], inv_all[G // 2], 4, spec.group)
+    gws = torch.empty(max(awq.workspace_size(awq.OP_W4A16_GEMM, M, N, K), 256), dtype=torch.uint8,
+                      device=dev)
+    t_sse = event_time_ms(lambda: awq.candidate_sse(xd, d_mid, None, workspace=gws), reps, stream)
+    flops = 2.0 * M * N * K
+    res = {"M": M, "K": K, "N": N, "bits": 4, "ms_per_layer": ms, "layers_per_s": 1e3 / ms,
+           "best_idx": int(out["best_idx"].item()),
+           "search_contraction": {"ms": t_sse, "tflops": flops / (t_sse * 1e-3) / 1e12,
+                                  "frac_mfma_peak": flops / (t_sse * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
+    log(f"llama2_7b_qkv search: {ms:.2f} ms/layer ({1e3 / ms:.2f} layers/s); contraction "
+        f"{t_sse:.3f} ms = {res['search_contraction']['tflops']:.0f} TFLOP/s")
+    del d_mid, gws
+    torch.cuda.empty_cache()
+    if with_gram:
+        res["gram_form"] = bench_gram(awq, xd, wd, spec, 4, out, steps, ms)
+    del xd, wd, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def main() -> int:
@@ -630,8 +719,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama2_7b_qkv")
-    ap.add_argument("--layer", default=None)
+    ap.add_argument("--workload", default=HEADLINE[0])
+    ap.add_argument("--layer", default=HEADLINE[1])
+    ap.add_argument("--bits", type=int, default=HEADLINE[2])
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped GEMM figures")
@@ -640,15 +730,16 @@ def main() -> int:
                     help="skip the layer-by-layer block pipeline figure")
     ap.add_argument("--no-power-probe", action="store_true",
                     help="skip the constant-operand launch (keeps profiles to the synthetic data)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="only the headline layer and its kernels (for profiler runs)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode-shaped GEMM figures (prints them as JSON)")
     ap.add_argument("--no-largest", action="store_true",
-                    help="skip the searches on the Llama-3-8B block and the largest layer "
-                         "(Llama-2-70B down)")
+                    help="skip the searches on the other workload layers")
     ap.add_argument("--decode-case", default=None, metavar="LAYER:M",
                     help="only one decode case of the Llama-3-8B block, e.g. gate_up:1")
-    ap.add_argument("--cpu-m", type=int, default=8192)
-    ap.add_argument("--cpu-n", type=int, default=4096)
+    ap.add_argument("--cpu-m", type=int, default=4096)
+    ap.add_argument("--cpu-n", type=int, default=2048)
     ap.add_argument("--summarize-trace", metavar="DIR", default=None,
                     help="write a summary of a rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
@@ -699,14 +790,15 @@ def main() -> int:
               flush=True)
         return 0
     spec = synth.layer_spec(args.workload, args.layer)
-    bits = spec.bits[-1]
+    bits = args.bits
+    if bits not in spec.bits:
+        raise SystemExit(f"{spec.workload}/{spec.name} is quantized to {spec.bits} bits")
     M, K, N, G = spec.M, spec.K, spec.N, spec.n_grid
     log(f"workload {spec.workload}/{spec.name}: M={M} K={K} N={N} bits={bits} grid={G}")
     t0 = time.perf_counter()
     x_bits, w_bits, _ = synth.make_layer(spec.workload, spec.name)
     log(f"synthetic inputs in {time.perf_counter() - t0:.1f} s")
-    xd = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    wd = torch.from_numpy(w_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    xd, wd = to_dev(x_bits, dev), to_dev(w_bits, dev)
     ws_bytes = awq.workspace_size(awq.OP_SEARCH_SCALE, M, N, K, bits, spec.group, G)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -738,37 +830,47 @@ def main() -> int:
     mean_abs = awq.act_stats(xd)
     s_all, inv_all = awq.candidate_scales(mean_abs, G)
     i_mid = G // 2
-    qw, sc, ze = awq.quantize_pack(wd, s_all[i_mid], bits, spec.group)
-    b_mid = awq.dequant_operand(wd, s_all[i_mid], inv_all[i_mid], bits, spec.group)
     d_mid = awq.diff_operand(wd, s_all[i_mid], inv_all[i_mid], bits, spec.group)
-    yref = awq.reference_gemm(xd, wd)
     gemm_ws = torch.empty(max(awq.workspace_size(awq.OP_W4A16_GEMM, M, N, K), 256),
                           dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     t_sse = event_time_ms(lambda: awq.candidate_sse(xd, d_mid, None, workspace=gemm_ws), reps,
                           stream)
-    t_sse_y = event_time_ms(lambda: awq.candidate_sse(xd, b_mid, yref, workspace=gemm_ws),
-                            max(2, reps // 2), stream)
-    # The same launch on constant operands: identical instructions and memory
-    # traffic, almost no bit toggling in the matrix cores.  The gap to the
-    # synthetic data is the chip's power limit, not the kernel's schedule.
-    # The vendor library's plain bf16 GEMM on the same operands (hipBLASLt via
-    # torch.mm, bf16 out): a yardstick for the contraction, not part of the path.
-    d_t = d_mid.t().contiguous()
-    y_mm = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    t_mm = event_time_ms(lambda: torch.mm(xd, d_t, out=y_mm), max(2, reps // 2), stream)
-    del d_t, y_mm
-    t_sse_c = None
-    if not args.no_power_probe:
-        x_one, d_one = torch.ones_like(xd), torch.ones_like(d_mid)
-        t_sse_c = event_time_ms(lambda: awq.candidate_sse(x_one, d_one, None, workspace=gemm_ws),
+    flops = 2.0 * M * N * K
+    tf = lambda ms: flops / (ms * 1e-3) / 1e12
+    log(f"search contraction {t_sse:.3f} ms = {tf(t_sse):.1f} TFLOP/s")
+    kern = {"search_contraction": None}
+    if not args.no_variants:
+        # The vendor library's plain bf16 GEMM on the same operands (hipBLASLt
+        # via torch.mm, bf16 out): a yardstick, not part of the path.
+        d_t = d_mid.t().contiguous()
+        y_mm = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        t_mm = event_time_ms(lambda: torch.mm(xd, d_t, out=y_mm), max(2, reps // 2), stream)
+        del d_t, y_mm
+        # The same launch on constant operands: identical instructions and
+        # memory traffic, almost no bit toggling in the matrix cores.
+        t_sse_c = None
+        if not args.no_power_probe:
+            x_one, d_one = torch.ones_like(xd), torch.ones_like(d_mid)
+            t_sse_c = event_time_ms(lambda: awq.candidate_sse(x_one, d_one, None, workspace=gemm_ws),
+                                    max(2, reps // 2), stream)
+            del x_one, d_one
+        qw, sc, ze = awq.quantize_pack(wd, s_all[i_mid], bits, spec.group)
+        b_mid = awq.dequant_operand(wd, s_all[i_mid], inv_all[i_mid], bits, spec.group)
+        yref = awq.reference_gemm(xd, wd)
+        t_sse_y = event_time_ms(lambda: awq.candidate_sse(xd, b_mid, yref, workspace=gemm_ws),
                                 max(2, reps // 2), stream)
-        del x_one, d_one
-    t_w4 = event_time_ms(lambda: awq.w4a16_gemm(xd, qw, sc, ze, bits, spec.group,
-                                                inv_s=inv_all[i_mid], y_ref=yref,
-                                                return_y=False, workspace=gemm_ws),
-                         max(2, reps // 2), stream)
-    t_ref = event_time_ms(lambda: awq.reference_gemm(xd, wd), max(2, reps // 2), stream)
+        t_w4 = event_time_ms(lambda: awq.w4a16_gemm(xd, qw, sc, ze, bits, spec.group,
+                                                    inv_s=inv_all[i_mid], y_ref=yref,
+                                                    return_y=False, workspace=gemm_ws),
+                             max(2, reps // 2), stream)
+        t_ref = event_time_ms(lambda: awq.reference_gemm(xd, wd), max(2, reps // 2), stream)
+        del yref, b_mid
+        torch.cuda.empty_cache()
+        log(f"against y_ref {t_sse_y:.3f} ms = {tf(t_sse_y):.1f} TFLOP/s; constant operands "
+            f"{(t_sse_c or float('nan')):.3f} ms; hipBLASLt bf16 mm {t_mm:.3f} ms = "
+            f"{tf(t_mm):.1f} TFLOP/s; packed w4a16+sse {t_w4:.3f} ms = {tf(t_w4):.1f} TFLOP/s; "
+            f"reference {t_ref:.3f} ms = {tf(t_ref):.1f} TFLOP/s")
     t_stats = event_time_ms(lambda: awq.act_stats(xd), reps, stream)
     t_quant = event_time_ms(lambda: awq.quantize_pack(wd, s_all[i_mid], bits, spec.group),
                             reps * 5, stream)
@@ -781,17 +883,10 @@ def main() -> int:
     cp_src, cp_dst = wd.clone(), torch.empty_like(wd)
     t_copy = event_time_ms(lambda: cp_dst.copy_(cp_src), reps * 5, stream)
     del cp_src, cp_dst
-    flops = 2.0 * M * N * K
-    tf = lambda ms: flops / (ms * 1e-3) / 1e12
     stats_bytes = 2.0 * M * K + 4.0 * K
     quant_bytes = 2.0 * N * K + 4.0 * K + N * K / 2 + 5.0 * N * K / spec.group
     deq_bytes = 2.0 * N * K + 8.0 * K + 2.0 * N * K
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
-    log(f"search contraction {t_sse:.3f} ms = {tf(t_sse):.1f} TFLOP/s; against y_ref "
-        f"{t_sse_y:.3f} ms = {tf(t_sse_y):.1f} TFLOP/s; on constant operands "
-        f"{(t_sse_c or float('nan')):.3f} ms; hipBLASLt bf16 mm {t_mm:.3f} ms = {tf(t_mm):.1f} "
-        f"TFLOP/s; packed w4a16+sse {t_w4:.3f} ms "
-        f"= {tf(t_w4):.1f} TFLOP/s; reference {t_ref:.3f} ms = {tf(t_ref):.1f} TFLOP/s")
     log(f"stats {t_stats * 1e3:.1f} us = {gbs(stats_bytes, t_stats):.0f} GB/s; quantize+pack "
         f"{t_quant * 1e3:.1f} us = {gbs(quant_bytes, t_quant):.0f} GB/s; dequant operand "
         f"{t_deq * 1e3:.1f} us = {gbs(deq_bytes, t_deq):.0f} GB/s; difference operand "
@@ -805,6 +900,20 @@ def main() -> int:
         return {"us": ms * 1e3, "gbs": gbs(nbytes, ms), "frac_hbm_peak": gbs(nbytes, ms) / PEAK_HBM_GBS,
                 "bytes": nbytes}
 
+    kern = {"search_contraction": mfma_entry(t_sse)}
+    if not args.no_variants:
+        kern.update({
+            "candidate_sse_vs_yref": mfma_entry(t_sse_y),
+            "search_contraction_constant_operands": mfma_entry(t_sse_c) if t_sse_c else None,
+            "vendor_bf16_gemm_same_shape": mfma_entry(t_mm),
+            "w4a16_gemm_sse": mfma_entry(t_w4),
+            "reference_gemm": mfma_entry(t_ref)})
+    kern.update({
+        "act_stats": hbm_entry(stats_bytes, t_stats),
+        "quantize_pack": hbm_entry(quant_bytes, t_quant),
+        "dequant_operand": hbm_entry(deq_bytes, t_deq),
+        "diff_operand": hbm_entry(deq_bytes, t_diff),
+        "device_copy_same_bytes": hbm_entry(4.0 * N * K, t_copy)})
     result = {
         "metric": METRIC,
         "value": 1e3 / ms_per_step,
@@ -822,42 +931,42 @@ def main() -> int:
                    "bits": bits, "group": spec.group, "n_grid": G},
         "roofline": {"bound": "mfma", "achieved": tf(t_sse), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": tf(t_sse) / PEAK_BF16_TFLOPS,
-                     "traffic": committed_traffic(),
+                     "traffic": committed_traffic(spec.workload, spec.name),
                      "kernel": "per-candidate contraction X.D^T (D = B - W) with fused sum of squares",
                      "flops_per_launch": flops, "ms_per_launch": t_sse,
                      "algorithmic_bytes_per_launch": 2.0 * M * K + 2.0 * N * K,
                      "kernel_source_hash": gemm_source_hash()},
-        "kernels": {
-            "search_contraction": mfma_entry(t_sse),
-            "candidate_sse_vs_yref": mfma_entry(t_sse_y),
-            "search_contraction_constant_operands": mfma_entry(t_sse_c) if t_sse_c else None,
-            "vendor_bf16_gemm_same_shape": mfma_entry(t_mm),
-            "w4a16_gemm_sse": mfma_entry(t_w4),
-            "reference_gemm": mfma_entry(t_ref),
-            "act_stats": hbm_entry(stats_bytes, t_stats),
-            "quantize_pack": hbm_entry(quant_bytes, t_quant),
-            "dequant_operand": hbm_entry(deq_bytes, t_deq),
-            "diff_operand": hbm_entry(deq_bytes, t_diff),
-            "device_copy_same_bytes": hbm_entry(4.0 * N * K, t_copy),
-        },
+        "kernels": kern,
+        "host": host_info(),
         "cpu_baseline": None,
     }
-    if not args.no_decode:
-        result["kernels"]["decode_gemm_llama3_8b"] = bench_decode(awq, dev, stream)
-        result["kernels"]["decode_gemm_int3_llama2_70b"] = bench_decode_int3(awq, dev, stream)
-    del ws, gemm_ws, yref, b_mid, d_mid
+    del d_mid, gemm_ws
     torch.cuda.empty_cache()
     result["variants"] = {}
-    if not args.no_gram:
-        result["variants"]["gram_form"] = bench_gram(awq, xd, wd, spec, bits, out, args.steps,
-                                                     ms_per_step)
+    if not args.no_variants:
+        other = [b for b in spec.bits if b != bits]
+        for b in other:
+            ms_b, out_b = time_search(awq, xd, wd, b, spec, args.steps, ws=None)
+            result["variants"][f"search_{spec.workload}_{spec.name}_int{b}"] = {
+                "ms_per_layer": ms_b, "layers_per_s": 1e3 / ms_b,
+                "best_idx": int(out_b["best_idx"].item()),
+                "tflops_candidate_products": flops * G / (ms_b * 1e-3) / 1e12}
+            log(f"{spec.workload}/{spec.name} INT{b} search: {ms_b:.2f} ms/layer "
+                f"({1e3 / ms_b:.2f} layers/s)")
+            del out_b
+    del ws, xd, wd, out
+    torch.cuda.empty_cache()
+    if not args.no_decode and not args.no_variants:
+        result["kernels"]["decode_gemm_llama3_8b"] = bench_decode(awq, dev, stream)
+        result["kernels"]["decode_gemm_int3_llama2_70b"] = bench_decode_int3(awq, dev, stream)
+    if not args.no_variants:
+        result["variants"]["search_llama2_7b_qkv"] = bench_qkv_layer(
+            awq, dev, stream, args.steps, reps, not args.no_gram)
         torch.cuda.empty_cache()
-    if not args.no_pipeline:
-        del xd, wd, out
-        torch.cuda.empty_cache()
+    if not args.no_pipeline and not args.no_variants:
         result["variants"]["block_pipeline_llama2_7b_mlp"] = bench_pipeline(awq, dev, stream)
         torch.cuda.empty_cache()
-    if not args.no_largest:
+    if not args.no_largest and not args.no_variants:
         result["variants"]["search_llama2_7b_mlp"] = bench_workload_layers(
             awq, dev, "llama2_7b_mlp", ("gate_up", "down"))
         result["variants"]["search_llama3_8b_block"] = bench_workload_layers(
@@ -865,7 +974,7 @@ def main() -> int:
         result["variants"]["search_llama2_70b_down"] = bench_largest_layer(awq, dev)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_m} tokens x {args.cpu_n} rows")
-        result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, spec, args.cpu_m, args.cpu_n)
+        result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, spec, bits, args.cpu_m, args.cpu_n)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -73,6 +73,7 @@ typedef enum awq_op {
   AWQ_OP_DECODE_GEMM = 4,
   AWQ_OP_CANDIDATE_SSE = 5,
   AWQ_OP_SEARCH_SCALE_GRAM = 6,
+  AWQ_OP_W4A16_GEMM_STAGED = 7,
 } awq_op;
 
 /* Packed code layouts of the deployment contraction. */
@@ -100,6 +101,8 @@ const char* awq_last_error(void);
  *                           split across workgroups).
  *   op AWQ_OP_CANDIDATE_SSE: uses M, N.
  *   op AWQ_OP_SEARCH_SCALE_GRAM: uses M, N, K, bits, group, n_grid.
+ *   op AWQ_OP_W4A16_GEMM_STAGED: uses M, N, K, bits, group (2*N*K bytes of
+ *                           dequantized operand plus per-tile partials).
  * Errors: AWQ_ERR_NULL (bytes NULL), AWQ_ERR_SHAPE, AWQ_ERR_UNSUPPORTED.
  */
 awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t bits,
@@ -243,6 +246,30 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                           const uint32_t* qweight, const float* scales, const uint8_t* zeros,
                           int32_t bits, int32_t group, const float* inv_s, const float* y_ref,
                           float* y, double* sse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The same W4A16 product for many tokens, from codes in either packed layout
+ * (builderai "About": 4-bit weights with 16-bit activations; sourcepulse AWQ
+ * project page, opening paragraph: 3- and 4-bit weights).  The operand
+ *   B[n,k] = bf16( fp32( fp32((q - z) * step) * inv_s[k] ) )
+ * (the one awq_w4a16_gemm forms in LDS) is written once per call into the
+ * workspace by a streaming kernel, then contracted on the bf16 matrix cores:
+ * each weight is dequantized once instead of once per 256-row tile of X,
+ * which pays once X has more than a few hundred rows.  Y is bit-identical
+ * to awq_w4a16_gemm's for the same codes (same operand, same accumulation
+ * order); sse agrees up to the order of its fp64 partial sums.
+ *   layout  AWQ_LAYOUT_NIBBLE: qweight u32 [N][K/8] (awq_quantize_pack, bits
+ *           3 or 4); AWQ_LAYOUT_INT3_DENSE: qweight u32 [N][3K/32]
+ *           (awq_quantize_pack3, bits 3); 4-byte aligned.
+ *   other arguments, outputs and the M == 0 / N == 0 rule as awq_w4a16_gemm
+ *   ws      awq_workspace_size(AWQ_OP_W4A16_GEMM_STAGED) bytes, always
+ *           required (it holds the 2*N*K-byte operand).
+ */
+awq_status awq_w4a16_gemm_staged(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                                 const uint32_t* qweight, const float* scales,
+                                 const uint8_t* zeros, int32_t bits, int32_t group,
+                                 int32_t layout, const float* inv_s, const float* y_ref, float* y,
+                                 double* sse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Decode-shaped W4A16 contraction for 1 <= M <= 64 tokens, the deployment

@@ -82,6 +82,13 @@ SearchLayout search_layout(int64_t M, int64_t N, int64_t K, int n_grid) {
   return L;
 }
 
+// Staged W4A16 product: the dequantized bf16 operand [N][K], then the SSE
+// partials of its contraction.
+size_t staged_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  return awq::align_up((size_t)N * (size_t)K * sizeof(uint16_t)) +
+         awq::align_up((size_t)awq::gemm_tiles(M, N) * sizeof(double));
+}
+
 struct GramLayout {
   size_t s, inv, scales_ws, stats_ws, xt, g32, gsplit, asplit, d32, partials, total;
 };
@@ -180,6 +187,15 @@ awq_status awq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32
           return fail(AWQ_ERR_SHAPE, "Gram search needs 1 <= M <= 2^22, 1 <= N <= 2^22, 2K <= 2^22");
         if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_UNSUPPORTED, "n_grid must be in [1, 64]");
         *bytes = gram_layout(M, N, K, n_grid).total;
+        return ok();
+      }
+      case AWQ_OP_W4A16_GEMM_STAGED: {
+        awq_status st = check_quant_params(bits, group);
+        if (st != AWQ_OK) return st;
+        if ((st = check_k(K, group)) != AWQ_OK) return st;
+        if (M < 0 || N < 0 || M >= kMaxDim || N > kMaxGemmN)
+          return fail(AWQ_ERR_SHAPE, "bad GEMM shape");
+        *bytes = staged_ws_bytes(M, N, K);
         return ok();
       }
       case AWQ_OP_CANDIDATE_SCALES:
@@ -426,6 +442,62 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
     AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
     if (sse != nullptr)
       AWQ_TRY_LAUNCH(awq::launch_loss_reduce((const double*)ws, awq::gemm_tiles(M, N), 1, 1.0, sse, s));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_w4a16_gemm_staged(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                                 const uint32_t* qweight, const float* scales,
+                                 const uint8_t* zeros, int32_t bits, int32_t group,
+                                 int32_t layout, const float* inv_s, const float* y_ref, float* y,
+                                 double* sse, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (layout != AWQ_LAYOUT_NIBBLE && layout != AWQ_LAYOUT_INT3_DENSE)
+      return fail(AWQ_ERR_UNSUPPORTED, "unknown layout %d", layout);
+    const bool dense = layout == AWQ_LAYOUT_INT3_DENSE;
+    if (dense && bits != 3) return fail(AWQ_ERR_UNSUPPORTED, "the dense INT3 layout holds 3-bit codes");
+    awq_status st = check_quant_params(bits, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (M < 0 || N < 0 || M >= kMaxDim || N > kMaxGemmN) return fail(AWQ_ERR_SHAPE, "M, N out of range");
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0 || N == 0) {  // empty product: only sse (if given) is written
+      if (sse != nullptr) {
+        if ((uintptr_t)sse & 7u) return fail(AWQ_ERR_ALIGN, "sse must be 8-byte aligned");
+        AWQ_TRY_LAUNCH(awq::launch_fill_f64(sse, 1, 0.0, s));
+      }
+      return ok();
+    }
+    if (x == nullptr || qweight == nullptr || scales == nullptr || zeros == nullptr)
+      return fail(AWQ_ERR_NULL, "x, qweight, scales and zeros are required");
+    if (y == nullptr && sse == nullptr) return fail(AWQ_ERR_NULL, "one of y and sse is required");
+    if (sse != nullptr && y_ref == nullptr) return fail(AWQ_ERR_NULL, "sse needs y_ref");
+    if (misaligned(x) || misaligned(y) || misaligned(y_ref) || misaligned(inv_s) ||
+        misaligned(ws) || ((uintptr_t)scales & 3u) || ((uintptr_t)sse & 7u) ||
+        ((uintptr_t)qweight & 3u))
+      return fail(AWQ_ERR_ALIGN, "x, y, y_ref, inv_s and ws must be 16-byte aligned, qweight and "
+                                 "scales 4-byte, sse 8-byte");
+    const size_t need = staged_ws_bytes(M, N, K);
+    if (ws == nullptr || ws_bytes < need)
+      return fail(AWQ_ERR_WORKSPACE, "w4a16_gemm_staged needs %zu workspace bytes", need);
+    char* base = (char*)ws;
+    uint16_t* operand = (uint16_t*)base;
+    double* partials = (double*)(base + awq::align_up((size_t)N * (size_t)K * sizeof(uint16_t)));
+    AWQ_TRY_LAUNCH(awq::launch_dequant_packed(qweight, scales, zeros, inv_s, N, K, dense, operand, s));
+    awq::GemmOperands op{};
+    op.x = x;
+    op.M = M;
+    op.N = N;
+    op.K = K;
+    op.w = operand;
+    op.y = y;
+    op.y_ref = sse != nullptr ? y_ref : nullptr;
+    op.partials = sse != nullptr ? partials : nullptr;
+    AWQ_TRY_LAUNCH(awq::launch_gemm(op, s));
+    if (sse != nullptr)
+      AWQ_TRY_LAUNCH(awq::launch_loss_reduce(partials, awq::gemm_tiles(M, N), 1, 1.0, sse, s));
     return ok();
   } catch (...) {
     return fail(AWQ_ERR_LAUNCH, "internal error");

@@ -84,6 +84,13 @@ hipError_t launch_quantize_diff(const uint16_t* w, int64_t N, int64_t K, const f
                                 const float* inv_s, int bits, uint16_t* a_split, float* d32,
                                 hipStream_t stream);
 
+// Packed codes (4-bit containers [N][K/8], or dense INT3 [N][3K/32]) -> the
+// bf16 operand b[n][k] = bf16(f32(f32((q - z) * step) * inv_s[k])) (inv_s
+// NULL: no factor), as the fused W4A16 kernel dequantizes it.
+hipError_t launch_dequant_packed(const uint32_t* qweight, const float* scales,
+                                 const uint8_t* zeros, const float* inv_s, int64_t N, int64_t K,
+                                 bool int3_dense, uint16_t* b, hipStream_t stream);
+
 // ---- Gram form: X^T (bf16 [K][Mp], zero-padded) and the split G operand ----
 int64_t gram_padded_m(int64_t M);
 hipError_t launch_transpose_pad(const uint16_t* x, int64_t M, int64_t K, uint16_t* xt,

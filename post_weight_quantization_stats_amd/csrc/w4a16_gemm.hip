@@ -610,7 +610,9 @@ hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream) {
   } else if (op.qweight == nullptr && op.dot) {
     gemm_kernel<false, false, 4, false, true, true><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
   } else if (op.qweight == nullptr) {
-    if (sse)
+    if (y && sse)
+      gemm_kernel<false, false, 4, true, true><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
+    else if (sse)
       gemm_kernel<false, false, 4, false, true><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
     else
       gemm_kernel<false, false, 4, true, false><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);

@@ -39,14 +39,14 @@ def quantize_mlp_block(x: torch.Tensor, gamma: torch.Tensor, w_gu: torch.Tensor,
     gu = search(u, w_gu, bits, group, n_grid)
     gamma_f = divide_rows(gamma, gu["best_s"])
     u_f = rmsnorm(x, gamma_f, eps)
-    y_gu = w4a16_gemm(u_f, gu["qweight"], gu["scales"], gu["zeros"], bits, group)
+    y_gu = w4a16_gemm(u_f, gu["qweight"], gu["scales"], gu["zeros"], bits, group, staged=True)
     h = silu_mul(y_gu)
     dn = search(h, w_down, bits, group, n_grid)
     scales_f = gu["scales"].clone()
     divide_rows(gu["scales"][F:], dn["best_s"], out=scales_f[F:])
-    y_gu2 = w4a16_gemm(u_f, gu["qweight"], scales_f, gu["zeros"], bits, group)
+    y_gu2 = w4a16_gemm(u_f, gu["qweight"], scales_f, gu["zeros"], bits, group, staged=True)
     h2 = silu_mul(y_gu2)
-    y_down = w4a16_gemm(h2, dn["qweight"], dn["scales"], dn["zeros"], bits, group)
+    y_down = w4a16_gemm(h2, dn["qweight"], dn["scales"], dn["zeros"], bits, group, staged=True)
     out.update(gate_up=gu, down=dn, gamma_folded=gamma_f, scales_gu_folded=scales_f,
                x_next=residual_add(x, y_down))
     if keep_intermediates:

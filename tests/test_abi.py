@@ -399,3 +399,87 @@ def test_last_error_is_per_thread():
     assert seen["shape"] is not None and seen["shape"][0] == SHAPE
     assert seen["unsupported"] is not None and seen["unsupported"][0] == UNSUPPORTED
     assert seen["shape"][1] != seen["unsupported"][1]
+
+
+def test_staged_gemm_entry_errors():
+    """awq_w4a16_gemm_staged: layout, bits, shapes, alignment and workspace
+    are rejected on the host."""
+    f = awq.lib().awq_w4a16_gemm_staged
+    st, need = ws_size(awq.OP_W4A16_GEMM_STAGED, 300, 64, 256)
+    assert st == OK and need >= 64 * 256 * 2
+    args = lambda **k: dict(dict(x=FAKE, M=300, N=64, K=256, q=FAKE, sc=FAKE, ze=FAKE, bits=4,
+                                 group=128, layout=0, inv=None, yref=None, y=FAKE, sse=None,
+                                 ws=FAKE, wsb=need), **k)
+    call = lambda a: f(a["x"], a["M"], a["N"], a["K"], a["q"], a["sc"], a["ze"], a["bits"],
+                       a["group"], a["layout"], a["inv"], a["yref"], a["y"], a["sse"], a["ws"],
+                       a["wsb"], None)
+    assert call(args(layout=2)) == UNSUPPORTED
+    assert call(args(layout=1, bits=4)) == UNSUPPORTED       # dense words hold 3-bit codes
+    assert call(args(bits=5)) == UNSUPPORTED
+    assert call(args(K=200)) == SHAPE
+    assert call(args(x=None)) == NULL
+    assert call(args(y=None)) == NULL                        # neither y nor sse
+    assert call(args(y=None, sse=FAKE)) == NULL              # sse without y_ref
+    assert call(args(x=FAKE_MIS)) == ALIGN
+    assert call(args(q=FAKE + 2)) == ALIGN
+    assert call(args(ws=None)) == WORKSPACE
+    assert call(args(wsb=need - 1)) == WORKSPACE
+
+
+def _cpu(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+@pytest.mark.parametrize("case", [
+    "decode_out", "decode_scales_dtype", "decode_zeros_shape", "decode_qweight_cols",
+    "decode3_words", "tiled_size", "tiled_scales", "tiled16_steps", "tiled16_zeros4",
+    "w4a16_inv_s", "w4a16_y_ref", "w4a16_scales", "dequant_s", "divide_rows_s", "residual_y",
+    "rmsnorm_gamma", "tiles_qweight", "noncontiguous"])
+def test_python_wrappers_check_shapes_before_the_device(case):
+    """Every wrapper checks dtype, exact shape and contiguity of each tensor
+    argument before any pointer reaches the library (the kernels size their
+    accesses from M, N and K, not from the allocations); on this GPU-less
+    machine each mistake must be reported as itself, not as "not a GPU
+    tensor"."""
+    import torch
+    bf, f32, u8, i32, f16 = torch.bfloat16, torch.float32, torch.uint8, torch.int32, torch.float16
+    M, N, K = 4, 32, 256
+    a = _cpu((M, K), bf)
+    qw, sc, ze = _cpu((N, K // 8), i32), _cpu((N, 2), f32), _cpu((N, 2), u8)
+    tiles = _cpu((awq.decode_tiles_size(N, K) // 4,), i32)
+    calls = {
+        "decode_out": (lambda: awq.decode_gemm(a, qw, sc, ze, out=_cpu((M, N - 1), f32)), "out must"),
+        "decode_scales_dtype": (lambda: awq.decode_gemm(a, qw, sc.half(), ze), "scales must"),
+        "decode_zeros_shape": (lambda: awq.decode_gemm(a, qw, sc, _cpu((N, 3), u8)), "zeros must"),
+        "decode_qweight_cols": (lambda: awq.decode_gemm(a, _cpu((N, K // 8 - 1), i32), sc, ze),
+                                "qweight must"),
+        "decode3_words": (lambda: awq.decode_gemm3(a, qw, sc, ze), "qweight3 must"),
+        "tiled_size": (lambda: awq.decode_gemm_tiled(a, tiles[:-4], sc, ze), "tiles must hold"),
+        "tiled_scales": (lambda: awq.decode_gemm_tiled(a, tiles, _cpu((N, 3), f32), ze), "scales must"),
+        "tiled16_steps": (lambda: awq.decode_gemm_tiled16(a, tiles, sc, _cpu((N, 1), u8)),
+                          "steps16 must"),
+        "tiled16_zeros4": (lambda: awq.decode_gemm_tiled16(a, tiles, _cpu((N, 2), f16),
+                                                           _cpu((N, 2), u8)), "zeros4 must"),
+        "w4a16_inv_s": (lambda: awq.w4a16_gemm(a, qw, sc, ze, inv_s=_cpu((K - 1,), f32)),
+                        "inv_s must"),
+        "w4a16_y_ref": (lambda: awq.w4a16_gemm(a, qw, sc, ze, y_ref=_cpu((M, N + 1), f32)),
+                        "y_ref must"),
+        "w4a16_scales": (lambda: awq.w4a16_gemm(a, qw, _cpu((N, 2), f16), ze), "scales must"),
+        "dequant_s": (lambda: awq.dequant_operand(_cpu((N, K), bf), _cpu((K + 1,), f32), None),
+                      "s must"),
+        "divide_rows_s": (lambda: awq.divide_rows(_cpu((N, 2), f32), _cpu((N - 1,), f32)), "s must"),
+        "residual_y": (lambda: awq.residual_add(a, _cpu((M, K - 8), f32)), "y must"),
+        "rmsnorm_gamma": (lambda: awq.rmsnorm(a, _cpu((K - 8,), f32)), "gamma must"),
+        "tiles_qweight": (lambda: awq.decode_tiles(_cpu((N, K // 8 + 1), i32), K), "qweight must"),
+        "noncontiguous": (lambda: awq.decode_gemm(a, qw, _cpu((2, N), f32).t(), ze), "contiguous"),
+    }
+    fn, msg = calls[case]
+    with pytest.raises((ValueError, TypeError), match=msg):
+        fn()
+    # with every shape right, the same call fails only on the device check
+    good = {"decode_out": lambda: awq.decode_gemm(a, qw, sc, ze, out=_cpu((M, N), f32)),
+            "tiled_size": lambda: awq.decode_gemm_tiled(a, tiles, sc, ze)}
+    if case in good:
+        with pytest.raises(ValueError, match="GPU tensor"):
+            good[case]()

@@ -37,21 +37,38 @@ def test_module_compact_format_shapes():
     assert "compact=True" in repr(m)
 
 
+def test_fold_inverse_scale_needs_gpu_tensors():
+    """The fold runs in the library (awq_divide_rows), never in torch."""
+    g = torch.ones(16, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        awq.fold_inverse_scale(g, torch.ones(16))
+    with pytest.raises(ValueError, match="16 elements"):
+        awq.fold_inverse_scale(g, torch.ones(8))
+
+
+@pytest.mark.gpu
 def test_fold_inverse_scale():
     """Folding 1/s into a gain or into a previous layer's rows makes its
-    output X / s: (diag(g) X) / s = diag(g / s) X, exactly in fp64."""
+    output X / s: (diag(g) X) / s = diag(g / s) X; each element is one IEEE
+    fp32 division, bit-exact against the oracle's divide_rows."""
+    dev = require_gpu()
+    announce("fold_inverse_scale")
     rng = np.random.default_rng(3)
     K = 16
-    g = torch.from_numpy(rng.uniform(0.5, 2.0, K)).to(torch.float32)
-    s = torch.from_numpy(rng.uniform(0.25, 4.0, K)).to(torch.float32)
-    x = torch.from_numpy(rng.standard_normal((5, K)))
-    folded = awq.fold_inverse_scale(g, s)
-    np.testing.assert_allclose((x * folded.double()).numpy(), (x * g.double() / s.double()).numpy(),
-                               rtol=1e-6)
-    Wp = torch.from_numpy(rng.standard_normal((K, 7))).to(torch.float32)   # previous layer rows
-    h = torch.from_numpy(rng.standard_normal((5, 7)))
-    np.testing.assert_allclose((h @ awq.fold_inverse_scale(Wp, s).double().T).numpy(),
-                               ((h @ Wp.double().T) / s.double()).numpy(), rtol=1e-5, atol=1e-6)
+    g = rng.uniform(0.5, 2.0, K).astype(np.float32)
+    s = rng.uniform(0.25, 4.0, K).astype(np.float32)
+    folded = awq.fold_inverse_scale(torch.from_numpy(g).to(dev), torch.from_numpy(s).to(dev))
+    assert folded.dtype == torch.float32
+    assert np.array_equal(folded.cpu().numpy().astype(np.float64), O.divide_rows(g, s))
+    Wp = rng.standard_normal((K, 7)).astype(np.float32)             # previous layer rows
+    fw = awq.fold_inverse_scale(torch.from_numpy(Wp).to(dev).to(torch.bfloat16),
+                                torch.from_numpy(s).to(dev))
+    wp_bf16 = torch.from_numpy(Wp).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(fw.cpu().numpy().astype(np.float64), O.divide_rows(wp_bf16, s))
+    h = rng.standard_normal((5, 7))
+    np.testing.assert_allclose(h @ fw.cpu().double().numpy().T,
+                               (h @ wp_bf16.astype(np.float64).T) / s.astype(np.float64),
+                               rtol=1e-5, atol=1e-6)
 
 
 @pytest.mark.gpu

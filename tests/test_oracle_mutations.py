@@ -203,6 +203,18 @@ def _mut_half_step_no_clamp(mp):
     mp.setattr(OA, "F16_MIN", 0.0)
 
 
+def _mut_block_deploys_on_unfolded_u(mp):
+    """gate/up deployed on u instead of u_f: the gain fold 1/s1 is dropped."""
+    orig = OA.divide_rows
+    mp.setattr(OA, "divide_rows", lambda v, s: np.asarray(v, np.float64) if np.ndim(v) == 1 else orig(v, s))
+
+
+def _mut_block_up_rows_not_folded(mp):
+    """The up rows' steps keep their unfolded values (1/s2 dropped)."""
+    orig = OA.divide_rows
+    mp.setattr(OA, "divide_rows", lambda v, s: np.asarray(v, np.float64) if np.ndim(v) == 2 else orig(v, s))
+
+
 MUTATIONS = [_mut_floor_instead_of_rint, _mut_drop_inv_s, _mut_alpha_grid_closed,
              _mut_scale_index_reversed, _mut_zero_added_before_rounding, _mut_loss_sign,
              _mut_no_range_extension, _mut_stats_mean_without_abs, _mut_normaliser_max_only,
@@ -210,7 +222,8 @@ MUTATIONS = [_mut_floor_instead_of_rint, _mut_drop_inv_s, _mut_alpha_grid_closed
              _mut_diff_off_by_half_ulp, _mut_pack3_code_bits_reversed, _mut_pack3_runs_of_16,
              _mut_tiles_row_major_inside, _mut_tiles_codes_in_pack_order, _mut_rmsnorm_without_mean, _mut_silu_is_sigmoid,
              _mut_fold_multiplies, _mut_f16_ties_away, _mut_quantize16_codes_with_fp32_step,
-             _mut_zero_nibbles_swapped, _mut_half_step_no_clamp]
+             _mut_zero_nibbles_swapped, _mut_half_step_no_clamp, _mut_block_deploys_on_unfolded_u,
+             _mut_block_up_rows_not_folded]
 
 PINS = [
     P.test_quantizer_worked_group,
@@ -237,6 +250,7 @@ PINS = [
     P.test_quantize16_brute_force_nearest_level,
     P.test_quantize16_clamped_and_subnormal_steps,
     P.test_meta16_pack_brute_force_and_roundtrip,
+    P.test_mlp_block_deployed_error_is_the_searched_loss,
 ]
 
 

@@ -907,3 +907,47 @@ def test_mlp_block_steps_and_fold_of_the_up_rows():
     v1, v2 = r["y_gu"][:, F:], r["y_gu2"][:, F:]
     assert np.abs(v2 * s2[None, :] - v1).max() <= 2e-2 * np.abs(v1).max()
     assert r["x_next"].shape == x.shape and r["x_next"].dtype == np.uint16
+
+
+def test_mlp_block_deployed_error_is_the_searched_loss():
+    """The block against the fp64 block with unquantized weights.  Each
+    layer's search scores candidate i by the MSE of X . B_i^T against
+    X . W^T, with 1/s folded into B (robotsatlas.com "AWQ", How it works:
+    the activation is divided by the factor that multiplies the weight, and
+    the grid search minimises the layer's output error).  Once deployed
+    (1/s1 folded into the RMSNorm gain, 1/s2 into the up rows' steps), each
+    layer computes the same product up to bf16 roundings of the folded
+    activation and weight, so its output error against the fp64 product
+    with unquantized weights must equal the search's chosen loss to within
+    those roundings (measured 0.1%; 2% allowed).  Deploying on the unfolded
+    activation or skipping a fold multiplies the error several times over.
+    End to end, the block's update error is at most the down layer's
+    searched error plus the gate/up error carried through the down weights
+    (triangle inequality)."""
+    rng = np.random.default_rng(44)
+    M, d, F = 128, 256, 256
+    x, _ = synth.random_layer(M, d, 8, seed=44, n_outlier=4, outlier_factor=20.0)
+    gamma = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    wgu = synth.to_bf16_bits((rng.standard_normal((2 * F, d)) * 0.02).astype(np.float32))
+    wd = synth.to_bf16_bits((rng.standard_normal((d, F)) * 0.02).astype(np.float32))
+    r = O.mlp_block(x, gamma, wgu, wd, n_grid=10)
+    b1, b2 = r["gate_up"]["best_idx"], r["down"]["best_idx"]
+    assert b1 > 0 and b2 > 0          # the folds are not identities here
+    u = O.bf16_bits_to_f64(O.rmsnorm(x, gamma, 1e-5)[0])
+    y_gu_fp = u @ O.bf16_bits_to_f64(wgu).T
+    ratio_gu = np.mean((r["y_gu"] - y_gu_fp) ** 2) / r["gate_up"]["losses"][b1]
+    assert abs(ratio_gu - 1.0) <= 2e-2, ratio_gu
+    h = O.bf16_bits_to_f64(r["h"])
+    Wd = O.bf16_bits_to_f64(wd)
+    y_d_fp = h @ Wd.T
+    ratio_d = np.mean((r["y_down"] - y_d_fp) ** 2) / r["down"]["losses"][b2]
+    assert abs(ratio_d - 1.0) <= 2e-2, ratio_d
+    # end to end against the unquantized block (fp64 throughout)
+    g, v = y_gu_fp[:, :F], y_gu_fp[:, F:]
+    H_fp = g / (1.0 + np.exp(-g)) * v
+    Y_fp = H_fp @ Wd.T
+    bound = 1.02 * np.sqrt(M * d * r["down"]["losses"][b2]) + np.linalg.norm((h - H_fp) @ Wd.T)
+    err = np.linalg.norm(r["y_down"] - Y_fp)
+    assert err <= bound, (err, bound)
+    x_next_fp = O.bf16_bits_to_f64(x) + Y_fp
+    assert np.linalg.norm(O.bf16_bits_to_f64(r["x_next"]) - x_next_fp) <= bound + 2e-2 * np.linalg.norm(x_next_fp)
