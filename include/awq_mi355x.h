@@ -344,6 +344,27 @@ awq_status awq_decode_gemm_tiled(const uint16_t* a, int64_t M, int64_t N, int64_
                                  size_t ws_bytes, void* stream);
 
 /*
+ * awq_decode_gemm_tiled for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, limits and results as awq_decode_gemm_tiled
+ * (bit-identical to it), without the workspace: the K-split partials go to a
+ * scratch array owned by the library, 16 MiB per GPU (a static device array,
+ * held by each GPU the library runs on until the process ends).  The call
+ * itself allocates and frees nothing.  The partials take
+ * awq_workspace_size(AWQ_OP_DECODE_GEMM) bytes (splits x M x N x 4); a shape
+ * that needs more than 16 MiB gives AWQ_ERR_WORKSPACE (the Llama-2-70B down
+ * projection at 64 tokens, 8192 x 28672, needs 14.7 MB).  Every call
+ * on one GPU shares that GPU's scratch: calls that overlap in time on one GPU
+ * (two streams, two threads) race and must be serialised by the caller.
+ * Nothing in the scratch needs clearing: each call overwrites every partial
+ * it reads.
+ */
+awq_status awq_decode_gemm_tiled_noalloc(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                         const uint32_t* tiles, const float* scales,
+                                         const uint8_t* zeros, int32_t layout, int32_t group,
+                                         float* y, void* stream);
+
+/*
  * Compact deployment format: 16-bit steps and 4-bit zeros (2.5 bytes of
  * metadata per group instead of 5; robotsatlas "Components": a scale per
  * group of 128; builderai "About": real low-bit weights are written).  The

@@ -19,7 +19,7 @@ from . import build as _build
 __all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "quantize_pack",
            "reference_gemm", "w4a16_gemm", "search_scale", "search_scale_gram", "decode_gemm",
            "dequant_operand", "diff_operand", "candidate_sse", "quantize_pack3", "decode_gemm3",
-           "decode_tiles", "decode_tiles_size", "decode_gemm_tiled", "LAYOUT_NIBBLE", "LAYOUT_INT3_DENSE",
+           "decode_tiles", "decode_tiles_size", "decode_gemm_tiled", "decode_gemm_tiled_noalloc", "LAYOUT_NIBBLE", "LAYOUT_INT3_DENSE",
            "quantize_pack16", "expand_meta16", "decode_gemm_tiled16",
            "rmsnorm", "silu_mul", "divide_rows", "residual_add", "workspace_size",
            "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES",
@@ -51,6 +51,8 @@ _SIGNATURES = {
     "awq_decode_tiles": ([_c_void_p, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p], _i32),
     "awq_decode_gemm_tiled": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
                                _i32, _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
+    "awq_decode_gemm_tiled_noalloc": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p,
+                                       _c_void_p, _i32, _i32, _c_void_p, _c_void_p], _i32),
     "awq_quantize_pack16": ([_c_void_p, _i64, _i64, _c_void_p, _i32, _i32, _i32, _c_void_p,
                              _c_void_p, _c_void_p, _c_void_p], _i32),
     "awq_expand_meta16": ([_c_void_p, _c_void_p, _i64, _i64, _i32, _c_void_p, _c_void_p,
@@ -535,6 +537,27 @@ def decode_gemm_tiled(a: torch.Tensor, tiles: torch.Tensor, scales: torch.Tensor
                                        layout, group, _ptr(y), _ptr(ws),
                                        0 if ws is None else ws.numel(), _stream(dev)),
            "awq_decode_gemm_tiled")
+    return y
+
+
+def decode_gemm_tiled_noalloc(a: torch.Tensor, tiles: torch.Tensor, scales: torch.Tensor,
+                              zeros: torch.Tensor, layout: int = LAYOUT_NIBBLE, group: int = 128,
+                              out: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_gemm_tiled without a workspace: the K-split partials go to the
+    library's static 16 MiB scratch (awq_decode_gemm_tiled_noalloc), so a
+    call with `out` given allocates nothing.  Calls that overlap on one GPU
+    race on that scratch."""
+    a = _bf16(a, "a")
+    M, K = a.shape
+    N = _rows_of(scales, "scales")
+    _meta(scales, zeros, N, K, group)
+    _tiles(tiles, N, K, layout, group)
+    y = _out(out, M, N)
+    dev = _gpu(a=a, tiles=tiles, scales=scales, zeros=zeros, out=y)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else y
+    _check(lib().awq_decode_gemm_tiled_noalloc(_ptr(a), M, N, K, _ptr(tiles), _ptr(scales),
+                                               _ptr(zeros), layout, group, _ptr(y), _stream(dev)),
+           "awq_decode_gemm_tiled_noalloc")
     return y
 
 

@@ -605,6 +605,38 @@ awq_status awq_decode_gemm_tiled(const uint16_t* a, int64_t M, int64_t N, int64_
                       ws_bytes, stream, dense, true);
 }
 
+awq_status awq_decode_gemm_tiled_noalloc(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                         const uint32_t* tiles, const float* scales,
+                                         const uint8_t* zeros, int32_t layout, int32_t group,
+                                         float* y, void* stream) {
+  try {
+    if (layout != AWQ_LAYOUT_NIBBLE && layout != AWQ_LAYOUT_INT3_DENSE)
+      return fail(AWQ_ERR_UNSUPPORTED, "unknown layout %d", layout);
+    const bool dense = layout == AWQ_LAYOUT_INT3_DENSE;
+    awq_status st = check_quant_params(dense ? 3 : 4, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (M < 0 || M > awq::kDecodeMaxM || N < 0 || N > kMaxGemmN)
+      return fail(AWQ_ERR_SHAPE, "decode GEMM needs 0 <= M <= %lld and 0 <= N <= 2^22",
+                  (long long)awq::kDecodeMaxM);
+    if (M == 0 || N == 0) return ok();
+    // Scratch needed by the K splits (partials [splits][M][N]); the static
+    // array is the only memory this call may use beyond its arguments.
+    const size_t need = awq::decode_plan(M, N, K).ws_bytes;
+    if (need > awq::kNoallocScratchBytes)
+      return fail(AWQ_ERR_WORKSPACE,
+                  "decode GEMM of M=%lld N=%lld K=%lld needs %zu scratch bytes; the static scratch "
+                  "holds %zu (use awq_decode_gemm_tiled with a workspace)",
+                  (long long)M, (long long)N, (long long)K, need, awq::kNoallocScratchBytes);
+    void* scratch = nullptr;
+    if (need > 0) AWQ_TRY_LAUNCH(awq::noalloc_scratch(&scratch));
+    return awq_decode_gemm_tiled(a, M, N, K, tiles, scales, zeros, layout, group, y, scratch,
+                                 need, stream);
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
 awq_status awq_decode_gemm_tiled16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
                                    const uint32_t* tiles, const uint16_t* steps16,
                                    const uint8_t* zeros4, int32_t layout, int32_t group, float* y,

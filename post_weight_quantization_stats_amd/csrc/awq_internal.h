@@ -149,6 +149,12 @@ size_t decode_tiles_bytes(int64_t N, int64_t K, bool int3_dense);
 hipError_t launch_decode_tiles(const uint32_t* qweight, int64_t N, int64_t K, bool int3_dense,
                                uint32_t* tiles, hipStream_t stream);
 
+// Static scratch of the entry point that allocates nothing: its size, and
+// the device address of the current device's copy (looked up once per device
+// with hipGetSymbolAddress; see noalloc.hip).
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // losses[i] = (sum_t partials[i*T + t]) / divisor, fixed summation order.
 hipError_t launch_loss_reduce(const double* partials, int64_t T, int n_grid, double divisor,
                               double* losses, hipStream_t stream);

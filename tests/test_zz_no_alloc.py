@@ -1,0 +1,73 @@
+"""awq_decode_gemm_tiled_noalloc, the decode contraction for callers that
+cannot allocate device memory (graph capture, tight serving loops): its
+K-split partials live in the library's static per-GPU scratch.  Checked
+through the C ABI against awq_decode_gemm_tiled with a caller-owned
+workspace (bit for bit) and the oracle (GEMM tolerance, sampled columns), on
+two calls in a row, the second with a smaller input, so the second reads
+nothing the first left behind."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import post_weight_quantization_stats_amd as awq
+import synth
+from gpu_util import announce, gemm_close, require_gpu, to_dev_bf16, u32
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(M, N, K, bits, dense, seed, dev):
+    rng = np.random.default_rng(seed)
+    w = synth.to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    s = np.exp(rng.uniform(-0.3, 0.3, K)).astype(np.float32)
+    wd, sd = to_dev_bf16(w, dev), torch.from_numpy(s).to(dev)
+    if dense:
+        qw, sc, ze = awq.quantize_pack3(wd, sd)
+        layout = awq.LAYOUT_INT3_DENSE
+    else:
+        qw, sc, ze = awq.quantize_pack(wd, sd, bits)
+        layout = awq.LAYOUT_NIBBLE
+    tiles = awq.decode_tiles(qw, K, layout)
+    a = synth.decode_activations(K, M, seed=seed)
+    return a, to_dev_bf16(a, dev), qw, tiles, sc, ze, layout
+
+
+def test_noalloc_matches_workspace_entry_two_calls():
+    dev = require_gpu()
+    # First call: the largest scratch of the workloads (Llama-2-70B down at
+    # 64 tokens: 7 K splits, 14.7 MB of partials); second: smaller (2 splits).
+    for M, N, K, bits, dense, seed in ((64, 8192, 28672, 4, False, 1),
+                                       (8, 1000, 9216, 3, True, 2)):
+        announce("decode noalloc", M, N, K, bits, dense)
+        need = awq.workspace_size(awq.OP_DECODE_GEMM, M, N, K, bits)
+        assert 0 < need <= 16 << 20
+        a, ad, qw, tiles, sc, ze, layout = _layer(M, N, K, bits, dense, seed, dev)
+        y_ref = awq.decode_gemm_tiled(ad, tiles, sc, ze, layout)
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+        awq.decode_gemm_tiled_noalloc(ad, tiles, sc, ze, layout, out=y)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), (M, N, K)
+        cols = np.sort(np.random.default_rng(seed).choice(N, 16, replace=False))
+        qwn, scn, zen = u32(qw)[cols], sc.cpu().numpy()[cols], ze.cpu().numpy()[cols]
+        ref = O.decode_gemm3(a, qwn, scn, zen, 128) if dense else O.decode_gemm(a, qwn, scn, zen, 128)
+        gemm_close(y.cpu().numpy()[:, cols], ref)
+
+
+def test_noalloc_without_splits_and_too_large():
+    dev = require_gpu()
+    announce("decode noalloc, no split and over the limit")
+    a, ad, qw, tiles, sc, ze, layout = _layer(3, 520, 2048, 4, False, 3, dev)
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 3, 520, 2048) == 0
+    y = awq.decode_gemm_tiled_noalloc(ad, tiles, sc, ze, layout)
+    assert torch.equal(y, awq.decode_gemm_tiled(ad, tiles, sc, ze, layout))
+    # partials of 7 splits x 64 x 16384 x 4 B = 29 MB exceed the 16 MiB scratch:
+    # rejected on the host before anything is enqueued
+    N, K = 16384, 28672
+    tl = torch.zeros(awq.decode_tiles_size(N, K) // 4, dtype=torch.int32, device=dev)
+    scz = torch.ones((N, K // 128), dtype=torch.float32, device=dev)
+    zez = torch.zeros((N, K // 128), dtype=torch.uint8, device=dev)
+    a64 = torch.zeros((64, K), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(awq.AwqError, match="static scratch"):
+        awq.decode_gemm_tiled_noalloc(a64, tl, scz, zez)
