@@ -123,6 +123,7 @@ KERNEL_LABELS = [
     ("select_row_kernel", "select s*"),
     ("fill_f64_kernel", "fill"),
     ("Cijk_", "hipBLASLt bf16 GEMM (vendor yardstick, same operands)"),
+    ("FillFunctor<float>", "one-element fill (launch floor; also torch fills)"),
 ]
 
 
@@ -203,7 +204,7 @@ def summarize_trace(trace_dir: str, command: str, log_path: str | None) -> str:
     out.append(f"{'kernel':<62} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}")
     for r in rows:
         name = r["Name"]
-        if "awq::" not in name and "Cijk_" not in name:
+        if "awq::" not in name and "Cijk_" not in name and "FillFunctor<float>" not in name:
             continue
         out.append(f"{_label(name):<62} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.1f} "
                    f"{float(r['MinNs']) / 1e3:>10.1f} {float(r['MaxNs']) / 1e3:>10.1f} "
@@ -212,6 +213,9 @@ def summarize_trace(trace_dir: str, command: str, log_path: str | None) -> str:
     if line and "int4" in line:
         out += ["", "# same run, bench.py figures (HIP-graph replays, weights rotated beyond the LLC):"]
         for case, v in line["int4"].items():
+            if not isinstance(v, dict):
+                out.append(f"{case}: {v:.2f}")
+                continue
             out.append(f"{case}: tiles {v['us']:.2f} us ({v['gbs']:.0f} GB/s), row-major "
                        f"{v['row_major_us']:.2f} us, compact metadata {v['compact_us']:.2f} us "
                        f"({v['compact_gbs']:.0f} GB/s)")
@@ -224,6 +228,37 @@ def summarize_trace(trace_dir: str, command: str, log_path: str | None) -> str:
         for k, v in line["kernels"].items():
             if isinstance(v, dict) and all(isinstance(b, (int, float)) for b in v.values()):
                 out.append(f"{k}: " + ", ".join(f"{a}={b:.4g}" for a, b in v.items()))
+    return "\n".join(out) + "\n"
+
+
+def summarize_counters(dirs, command: str) -> str:
+    """Per-kernel medians of every counter in one or more rocprofv3 --pmc
+    runs, with the dispatch's grid, workgroup and register counts.  FETCH_SIZE
+    is in KiB per dispatch and reads half the bytes moved (the calibration of
+    the search-contraction traffic summary), so bytes = 2 x 1024 x FETCH_SIZE;
+    SQ_WAVES counts the waves launched."""
+    per = {}
+    for d in dirs:
+        for r in _read_csv(_find(d, "counter_collection.csv")):
+            name = r["Kernel_Name"]
+            if "awq::" not in name and "FillFunctor<float>" not in name:
+                continue
+            key = _label(name) if "awq::" in name else "one-element fill (launch floor)"
+            e = per.setdefault(key, {"dur": [], "meta": (r["Grid_Size"], r["Workgroup_Size"],
+                                                         r["VGPR_Count"], r["LDS_Block_Size"])})
+            e.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == sorted({x for x in e if x not in ("dur", "meta")})[0]:
+                e["dur"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    out = ["# rocprofv3 counters per kernel (medians over dispatches)", f"# commands: {command}", ""]
+    for key, e in sorted(per.items()):
+        grid, wg, vgpr, lds = e["meta"]
+        out.append(f"{key}: grid {grid} threads, workgroup {wg}, {vgpr} VGPRs, {lds} B LDS, "
+                   f"waves {int(grid) // 64}; duration in the counter run {np.median(e['dur']):.2f} us")
+        for c, v in sorted(e.items()):
+            if c in ("dur", "meta"):
+                continue
+            extra = f"  (= {2 * 1024 * np.median(v) / 1e6:.2f} MB)" if c == "FETCH_SIZE" else ""
+            out.append(f"    {c:<24} {np.median(v):>14.6g}{extra}")
     return "\n".join(out) + "\n"
 
 
@@ -328,6 +363,12 @@ def bench_decode(awq, dev, stream, reps: int = 96, layers=("qkv", "o_proj", "gat
 
     import synth
     out = {}
+    # Fixed per-launch floor: a kernel with no work to speak of (a one-element
+    # fill), replayed from a graph exactly like the decode calls.
+    z1 = torch.zeros(1, device=dev)
+    floor_ms = _graph_time_ms(lambda i: z1.fill_(float(i) + 1.0), reps, stream)
+    out["empty_kernel_us"] = floor_ms * 1e3
+    log(f"one-element kernel (launch floor) in a graph replay: {floor_ms * 1e3:.2f} us")
     for name in layers:
         spec = synth.layer_spec("llama3_8b_block", name)
         N, K = spec.N, spec.K
@@ -746,15 +787,19 @@ def main() -> int:
                     help="write HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE runs and exit")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR", default=None,
                     help="write clock / matrix-core occupancy from a counter pass and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR", default=None,
+                    help="write per-kernel medians of the counters of --pmc runs and exit")
     ap.add_argument("--bench-log", default=None, help="log of the profiled bench run")
     ap.add_argument("--profile-command", default="", help="command text recorded in a summary")
     ap.add_argument("--summary-out", default=None)
     args = ap.parse_args()
 
-    if args.summarize_trace or args.summarize_pmc or args.summarize_mfma:
+    if args.summarize_trace or args.summarize_pmc or args.summarize_mfma or args.summarize_counters:
         import synth
         spec = synth.layer_spec(args.workload, args.layer)
-        if args.summarize_mfma:
+        if args.summarize_counters:
+            text = summarize_counters(args.summarize_counters, args.profile_command)
+        elif args.summarize_mfma:
             text = summarize_mfma(args.summarize_mfma, args.profile_command)
         elif args.summarize_trace:
             text = summarize_trace(args.summarize_trace, args.profile_command, args.bench_log)
