@@ -42,7 +42,7 @@ HEADLINE = ("llama2_70b_mlp", "gate_up", 4)
 def traffic_file(workload: str, layer: str) -> str:
     return os.path.join(PROFILES, f"search_contraction_{workload}_{layer}_traffic.txt")
 # The search's per-candidate contraction X . D^T with the sum-of-squares epilogue.
-DOMINANT_KERNEL = "gemm_kernel<false, false, 4, false, true, false, true>"
+DOMINANT_KERNEL = "diff_sq_kernel"
 GEMM_SOURCES = ["w4a16_gemm.hip", "device_common.h", "awq_internal.h"]
 
 
@@ -78,13 +78,13 @@ def committed_traffic(workload: str, layer: str):
 # ---- rocprofv3 output summaries (run on the host after a profiled bench) ----
 
 KERNEL_LABELS = [
-    ("gemm_kernel<false, false, 4, false, true, false, true>",
-     "search contraction X.D^T (difference operand, sum of squares)"),
-    ("gemm_kernel<false, false, 4, false, true, true, false>",
+    ("diff_sq_kernel", "search contraction X.D^T (difference operand, sum of squares)"),
+    ("gemm_kernel<false, false, 4, false, true, true>",
      "Gram-form contraction (split D . split G, dot epilogue)"),
-    ("gemm_kernel<false, false, 4, false, true, false, false>",
+    ("gemm_kernel<false, false, 4, false, true, false>",
      "candidate_sse vs y_ref (bf16 operand, squared-error epilogue)"),
-    ("gemm_kernel<false, false, 4, true, false", "reference_gemm / Gram matrix (bf16, fp32 out)"),
+    ("gemm_kernel<false, false, 4, true, true", "staged W4A16 product with SSE (bf16 operand, Y and SSE)"),
+    ("gemm_kernel<false, false, 4, true, false", "reference_gemm / Gram matrix / staged W4A16 (bf16, fp32 out)"),
     ("gemm_kernel<true, true, 2, false, true", "w4a16_gemm_sse (INT4 operand, 1/s folded, SSE epilogue)"),
     ("gemm_kernel<true", "w4a16_gemm (INT4 operand, other epilogues)"),
     ("quantize_kernel<4, 1,", "dequant_operand (quantize -> bf16 B)"),
@@ -97,6 +97,8 @@ KERNEL_LABELS = [
     ("quantize_kernel<3, 0, true>", "quantize_pack16 (compact format)"),
     ("quantize_kernel<3, 4, true>", "quantize_pack16 (compact format, dense INT3)"),
     ("quantize_kernel<3, 4,", "quantize_pack3 (dense INT3)"),
+    ("dequant_nibble_kernel", "staged operand from 4-bit containers"),
+    ("dequant_int3_kernel", "staged operand from dense INT3"),
     ("expand_meta16", "compact metadata expansion"),
     ("decode_tiles_kernel", "decode tiles"),
     ("transpose_pad_kernel", "X^T (Gram form)"),
