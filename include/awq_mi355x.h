@@ -407,6 +407,34 @@ awq_status awq_decode_gemm_tiled16(const uint16_t* a, int64_t M, int64_t N, int6
                                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Metadata tiles: the compact metadata (awq_quantize_pack16) rearranged like
+ * the decode tiles, so that the decode contraction reads each row's step and
+ * zero with its codes (robotsatlas "Implementation pitfalls": the benefit
+ * needs matched INT4 kernels).  u32 [ceil(N/16)][K/group][16]: word r of
+ * tile b*G + g holds the binary16 step of row 16b + r and group g in bits
+ * 0..15 and its zero in bits 16..19, bits 20..31 clear; rows past N are 0.
+ *   awq_decode_meta_size: *bytes = ceil(N/16) * 16 * (K/group) * 4.
+ *   awq_decode_meta: steps16 (2-byte aligned) and zeros4 as written by
+ *     awq_quantize_pack16; meta output of that size, 4-byte aligned.
+ *     N == 0 is a no-op.
+ */
+awq_status awq_decode_meta_size(int64_t N, int64_t K, int32_t group, size_t* bytes);
+awq_status awq_decode_meta(const uint16_t* steps16, const uint8_t* zeros4, int64_t N, int64_t K,
+                           int32_t group, uint32_t* meta, void* stream);
+
+/*
+ * The decode-shaped contraction on decode tiles and metadata tiles:
+ * arguments, limits, workspace and results as awq_decode_gemm_tiled16, with
+ * meta (awq_decode_meta, 4-byte aligned) in place of steps16 and zeros4.
+ * Bit-identical to awq_decode_gemm_tiled16 on the compact metadata the tiles
+ * were made from.
+ */
+awq_status awq_decode_gemm_tiled_meta(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                      const uint32_t* tiles, const uint32_t* meta, int32_t layout,
+                                      int32_t group, float* y, void* ws, size_t ws_bytes,
+                                      void* stream);
+
+/*
  * The whole per-layer search (robotsatlas "How it works", "Key mechanisms";
  * "Computational complexity": cost grows with layers x grid points x
  * calibration tokens).  Steps, all on `stream` with no host synchronisation:

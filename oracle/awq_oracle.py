@@ -412,6 +412,22 @@ def decode_tiles(qweight, K: int, dense3: bool = False, group: int = 128) -> np.
     return np.ascontiguousarray(t.astype("<u4")).reshape(-1).view(np.uint8)
 
 
+def decode_meta(steps16, zeros4, K: int, group: int = 128) -> np.ndarray:
+    """The compact metadata rearranged like decode_tiles (a layout of this
+    library, for the deployment contraction): one u32 per row and group,
+    the binary16 step bits in bits 0..15 and the 4-bit zero in bits 16..19;
+    word r of tile b*G + g belongs to row 16b + r and group g, rows past N
+    give 0.  Returns uint32 [ceil(N/16) * G * 16]."""
+    G = K // group
+    st = np.asarray(steps16, dtype=np.uint16).astype(np.uint64)
+    N = st.shape[0]
+    _, z = unpack_meta16(steps16, zeros4, G)
+    NB = -(-N // 16)
+    w = np.zeros((NB * 16, G), dtype=np.uint64)
+    w[:N] = st | (z.astype(np.uint64) << np.uint64(16))
+    return np.ascontiguousarray(w.reshape(NB, 16, G).transpose(0, 2, 1)).reshape(-1).astype(np.uint32)
+
+
 def packed3_bytes(N: int, K: int, group: int) -> int:
     """Storage of the dense INT3 form: 3-bit codes + fp32 scale + u8 zero per group."""
     return N * 3 * K // 8 + N * (K // group) * (4 + 1)

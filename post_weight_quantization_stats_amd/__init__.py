@@ -20,7 +20,8 @@ __all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "
            "reference_gemm", "w4a16_gemm", "search_scale", "search_scale_gram", "decode_gemm",
            "dequant_operand", "diff_operand", "candidate_sse", "quantize_pack3", "decode_gemm3",
            "decode_tiles", "decode_tiles_size", "decode_gemm_tiled", "decode_gemm_tiled_noalloc", "LAYOUT_NIBBLE", "LAYOUT_INT3_DENSE",
-           "quantize_pack16", "expand_meta16", "decode_gemm_tiled16",
+           "quantize_pack16", "expand_meta16", "decode_gemm_tiled16", "decode_meta_size",
+           "decode_meta", "decode_gemm_tiled_meta",
            "rmsnorm", "silu_mul", "divide_rows", "residual_add", "workspace_size",
            "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES",
            "OP_DECODE_GEMM", "OP_CANDIDATE_SSE", "OP_SEARCH_SCALE_GRAM", "OP_W4A16_GEMM_STAGED"]
@@ -59,6 +60,10 @@ _SIGNATURES = {
                            _c_void_p], _i32),
     "awq_decode_gemm_tiled16": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                  _i32, _i32, _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
+    "awq_decode_meta_size": ([_i64, _i64, _i32, _c_void_p], _i32),
+    "awq_decode_meta": ([_c_void_p, _c_void_p, _i64, _i64, _i32, _c_void_p, _c_void_p], _i32),
+    "awq_decode_gemm_tiled_meta": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _i32, _i32,
+                                    _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
     "awq_rmsnorm": ([_c_void_p, _i64, _i64, _c_void_p, ctypes.c_double, _c_void_p, _c_void_p,
                      _c_void_p], _i32),
     "awq_silu_mul": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p], _i32),
@@ -618,6 +623,49 @@ def decode_gemm_tiled16(a: torch.Tensor, tiles: torch.Tensor, steps16: torch.Ten
                                          _ptr(zeros4), layout, group, _ptr(y),
                                          _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)),
            "awq_decode_gemm_tiled16")
+    return y
+
+
+def decode_meta_size(N: int, K: int, group: int = 128) -> int:
+    """Bytes of the metadata tiles of an N x K layer."""
+    nbytes = _size_t(0)
+    _check(lib().awq_decode_meta_size(N, K, group, ctypes.byref(nbytes)), "awq_decode_meta_size")
+    return int(nbytes.value)
+
+
+def decode_meta(steps16: torch.Tensor, zeros4: torch.Tensor, group: int = 128) -> torch.Tensor:
+    """The compact metadata as metadata tiles (int32, flat), for
+    decode_gemm_tiled_meta."""
+    N = _rows_of(steps16, "steps16")
+    G = steps16.shape[1]
+    _meta16(steps16, zeros4, N, G)
+    dev = _gpu(steps16=steps16, zeros4=zeros4)
+    meta = torch.empty(decode_meta_size(N, G * group, group) // 4, dtype=torch.int32, device=dev)
+    _check(lib().awq_decode_meta(_ptr(steps16), _ptr(zeros4), N, G * group, group, _ptr(meta),
+                                 _stream(dev)), "awq_decode_meta")
+    return meta
+
+
+def decode_gemm_tiled_meta(a: torch.Tensor, tiles: torch.Tensor, meta: torch.Tensor, N: int,
+                           layout: int = LAYOUT_NIBBLE, group: int = 128,
+                           out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_gemm_tiled16 reading metadata tiles (fp32 [M][N]); N is the
+    layer's output width (the tiles round it up to 16)."""
+    a = _bf16(a, "a")
+    M, K = a.shape
+    if group <= 0 or K % group:
+        raise ValueError(f"K={K} must be a multiple of the group size {group}")
+    _tiles(tiles, N, K, layout, group)
+    _tensor(meta, "meta", _WORDS, (decode_meta_size(N, K, group) // 4,))
+    y = _out(out, M, N)
+    dev = _gpu(a=a, tiles=tiles, meta=meta, out=y)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else y
+    ws = _decode_ws(M, N, K, 3 if layout == LAYOUT_INT3_DENSE else 4, group, dev, workspace)
+    _check(lib().awq_decode_gemm_tiled_meta(_ptr(a), M, N, K, _ptr(tiles), _ptr(meta), layout,
+                                            group, _ptr(y), _ptr(ws),
+                                            0 if ws is None else ws.numel(), _stream(dev)),
+           "awq_decode_gemm_tiled_meta")
     return y
 
 

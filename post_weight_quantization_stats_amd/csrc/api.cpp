@@ -649,6 +649,68 @@ awq_status awq_decode_gemm_tiled16(const uint16_t* a, int64_t M, int64_t N, int6
                       ws_bytes, stream, dense, true);
 }
 
+awq_status awq_decode_meta_size(int64_t N, int64_t K, int32_t group, size_t* bytes) {
+  if (bytes == nullptr) return fail(AWQ_ERR_NULL, "bytes is required");
+  awq_status st = check_quant_params(4, group);
+  if (st != AWQ_OK) return st;
+  if ((st = check_k(K, group)) != AWQ_OK) return st;
+  if (N < 0 || N > kMaxGemmN) return fail(AWQ_ERR_SHAPE, "N out of range");
+  *bytes = awq::decode_meta_bytes(N, K);
+  return ok();
+}
+
+awq_status awq_decode_meta(const uint16_t* steps16, const uint8_t* zeros4, int64_t N, int64_t K,
+                           int32_t group, uint32_t* meta, void* stream) {
+  try {
+    size_t bytes = 0;
+    awq_status st = awq_decode_meta_size(N, K, group, &bytes);
+    if (st != AWQ_OK) return st;
+    if (N == 0) return ok();
+    if (steps16 == nullptr || zeros4 == nullptr || meta == nullptr)
+      return fail(AWQ_ERR_NULL, "steps16, zeros4 and meta are required");
+    if (((uintptr_t)steps16 & 1u) || ((uintptr_t)meta & 3u))
+      return fail(AWQ_ERR_ALIGN, "steps16 must be 2-byte aligned, meta 4-byte");
+    AWQ_TRY_LAUNCH(awq::launch_decode_meta(steps16, zeros4, N, K, meta, (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_decode_gemm_tiled_meta(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                      const uint32_t* tiles, const uint32_t* meta, int32_t layout,
+                                      int32_t group, float* y, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  try {
+    if (layout != AWQ_LAYOUT_NIBBLE && layout != AWQ_LAYOUT_INT3_DENSE)
+      return fail(AWQ_ERR_UNSUPPORTED, "unknown layout %d", layout);
+    const bool dense = layout == AWQ_LAYOUT_INT3_DENSE;
+    awq_status st = check_quant_params(dense ? 3 : 4, group);
+    if (st != AWQ_OK) return st;
+    if ((st = check_k(K, group)) != AWQ_OK) return st;
+    if (M < 0 || M > awq::kDecodeMaxM || N < 0 || N > kMaxGemmN)
+      return fail(AWQ_ERR_SHAPE, "decode GEMM needs 0 <= M <= %lld and 0 <= N <= 2^22",
+                  (long long)awq::kDecodeMaxM);
+    if (M == 0 || N == 0) return ok();
+    if (a == nullptr || tiles == nullptr || meta == nullptr || y == nullptr)
+      return fail(AWQ_ERR_NULL, "a, tiles, meta and y are required");
+    if (misaligned(a) || misaligned(y) || misaligned(ws) ||
+        (dense ? ((uintptr_t)tiles & 3u) != 0 : misaligned(tiles)) || ((uintptr_t)meta & 3u))
+      return fail(AWQ_ERR_ALIGN, "a, y and ws must be 16-byte aligned, tiles 16-byte (4-byte for "
+                                 "dense INT3), meta 4-byte");
+    const awq::DecodePlan plan = awq::decode_plan(M, N, K);
+    if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes))
+      return fail(AWQ_ERR_WORKSPACE, "decode GEMM needs %zu workspace bytes", plan.ws_bytes);
+    if (awq::decode_tiles_bytes(N, K, dense) > 0xFFFFFFFFull)
+      return fail(AWQ_ERR_SHAPE, "decode tiles are addressed with 32-bit offsets: at most 4 GiB");
+    AWQ_TRY_LAUNCH(awq::launch_decode_gemm_meta(a, M, N, K, tiles, meta, y, ws,
+                                                (hipStream_t)stream, dense));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
 awq_status awq_candidate_sse(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint16_t* b,
                              const float* y_ref, double* sse, void* ws, size_t ws_bytes,
                              void* stream) {

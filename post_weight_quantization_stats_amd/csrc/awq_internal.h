@@ -123,7 +123,7 @@ struct GemmOperands {
 };
 hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream);
 
-// ---- decode-shaped W4A16 contraction (M <= 16) ----
+// ---- decode-shaped W4A16 contraction (M <= 64) ----
 constexpr int64_t kDecodeMaxM = 64;
 struct DecodePlan {
   int64_t groups_per_split;
@@ -143,6 +143,16 @@ hipError_t launch_decode_gemm16(const uint16_t* a, int64_t M, int64_t N, int64_t
                                 const uint32_t* tiles, const uint16_t* steps16,
                                 const uint8_t* zeros4, float* y, void* ws, hipStream_t stream,
                                 bool int3_dense);
+// The decode contraction on decode tiles with metadata tiles (launch_decode_meta).
+hipError_t launch_decode_gemm_meta(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                   const uint32_t* tiles, const uint32_t* meta, float* y, void* ws,
+                                   hipStream_t stream, bool int3_dense);
+// Metadata tiles: u32 [ceil(N/16)][G][16], word r of tile b*G + g = binary16
+// step of row 16b + r, group g, in bits 0..15 and its zero in bits 16..19
+// (0 past N), from the compact metadata.
+size_t decode_meta_bytes(int64_t N, int64_t K);
+hipError_t launch_decode_meta(const uint16_t* steps16, const uint8_t* zeros4, int64_t N,
+                              int64_t K, uint32_t* meta, hipStream_t stream);
 // Decode tiles: rows 16b .. 16b+15 (zero past N) x group g as tile b*G + g,
 // row r's piece for channels 32q .. 32q+31 at byte P*(r + 16q) (P = 16 or 12).
 size_t decode_tiles_bytes(int64_t N, int64_t K, bool int3_dense);

@@ -49,10 +49,22 @@
 // of word p/4; dense INT3: bits 3t and 16+3t of word p/5, t = p%5, pair 15
 // in bits 15 and 31 of the three words), so the MFMA slots hold channels in
 // their natural order and the activations are used as loaded.
-// The activations come from L2 (every workgroup reads the same few KiB).  The
-// (step, 128 + zero) pairs of a wave's rows and groups are loaded into an LDS
-// table up front, one distinct element per lane: loaded per group and per
-// lane they would touch 16 cache lines for 64 useful bytes per instruction.
+// The activations come from L2 (every workgroup reads the same few KiB); the
+// codes are read once, with the non-temporal hint (3-7% faster on the
+// Llama-3-8B layers).  The (step, 128 + zero) pairs of a wave's rows and
+// groups come one of two ways:
+//   * From the row-major metadata (fp32 steps and u8 zeros, or the compact
+//     binary16 steps and 4-bit zeros): loaded into an LDS table up front, one
+//     distinct element per lane (loaded per group they would touch 16 cache
+//     lines for 64 useful bytes per instruction).
+//   * From metadata tiles (META == kMetaTiles): the compact metadata
+//     rearranged like the code tiles, one u32 per row and group (binary16
+//     step in bits 0..15, zero in bits 16..19), the 16 rows of tile b*G + g
+//     in 64 contiguous bytes.  Each lane then loads its row's word with the
+//     group's codes, in the same ring: no table, no barrier before the loop,
+//     one load per group and column block (7-19% faster at M = 1 than the
+//     table on the Llama-3-8B layers).  Values equal the compact table's, so
+//     the results are bit-identical to it.
 #include <algorithm>
 #include <type_traits>
 
@@ -74,14 +86,18 @@ constexpr int kBlockGroups = kWaves * kWaveGroups;   // 64 groups = 8192 channel
 // the wide layers).
 constexpr int kMaxTokenBlocks = 2;
 
+// Where the steps and zeros come from.
+enum MetaSource { kMetaF32 = 0, kMetaH16 = 1, kMetaTiles = 2 };
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 struct DecodeParams {
   const uint16_t* a;
   const uint32_t* qweight;
-  const float* scales;        // fp32 steps [N][G] (unless H16)
-  const uint16_t* steps16;    // H16: binary16 steps [N][G]
-  const uint8_t* zeros;       // u8 [N][G], or H16: two per byte [N][ceil(G/2)]
+  const float* scales;        // fp32 steps [N][G] (kMetaF32)
+  const uint16_t* steps16;    // kMetaH16: binary16 steps [N][G]
+  const uint8_t* zeros;       // u8 [N][G], or kMetaH16: two per byte [N][ceil(G/2)]
+  const uint32_t* meta;       // kMetaTiles: u32 [ceil(N/16)][G][16]
   float* out;                 // y, or partials [splits][M][N]
   int64_t M, N, K;
   int64_t groups_per_split;
@@ -94,6 +110,15 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
 
 __device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t voff) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Cache-policy bit of a buffer load: non-temporal (streamed once).
+constexpr int kNonTemporal = 2;
+
+// Codes: 16 bytes (4-bit containers) or 12 (dense INT3), read once.
+__device__ __forceinline__ uint4 ld_codes16(rsrc_t r, uint32_t voff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kNonTemporal);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -147,9 +172,9 @@ __device__ __forceinline__ void lift_pairs3(uint4 v, bf16x8 (&out)[4], uint32_t 
     out[j] = __builtin_bit_cast(bf16x8, u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]});
 }
 
-__device__ __forceinline__ uint4 ld12(rsrc_t r, uint32_t voff) {
+__device__ __forceinline__ uint4 ld_codes12(rsrc_t r, uint32_t voff) {
   typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-  const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, 0);
+  const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, kNonTemporal);
   return make_uint4(v.x, v.y, v.z, 0u);
 }
 
@@ -158,19 +183,23 @@ __device__ __forceinline__ uint4 ld12(rsrc_t r, uint32_t voff) {
 // 32*g4 .. 32*g4+31 of the group).
 template <int NB, int MB>
 struct GroupLoads {
+  uint32_t m[NB];       // kMetaTiles: the lane's (step, zero) word per column block
   uint4 q[NB];
   uint4 a[MB][4];
 };
 
 // NB 16-column blocks per workgroup (all of its waves work on them) and MB
 // 16-row blocks of tokens (M <= 16 * MB); I3: dense INT3 codes; TL: tiled;
-// H16: the compact metadata (binary16 steps, 4-bit zeros).
-// W waves per workgroup.
-template <int NB, int MB, bool I3, bool TL, bool H16 = false, int W = kWaves>
+// META: where the steps and zeros come from (MetaSource; the compact
+// metadata and its tiles go with tiled codes only).  W waves per workgroup.
+template <int NB, int MB, bool I3, bool TL, int META = kMetaF32, int W = kWaves>
 __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool H16 = META == kMetaH16, MT = META == kMetaTiles;
+  static_assert(META == kMetaF32 || TL, "the compact metadata goes with tiled codes");
   constexpr int kCols = 16 * NB;
-  __shared__ float2 ssz[W][kCols][kWaveGroups];    // (step, 128 + z), 8 to 64 KiB
+  // (step, 128 + z) table, 8 to 64 KiB (none with metadata tiles).
+  __shared__ float2 ssz[MT ? 1 : W][MT ? 1 : kCols][MT ? 1 : kWaveGroups];
   __shared__ f32x4 red[W - 1][MB][NB][64];          // partial outputs of waves 1..W-1
 
   const int lane = threadIdx.x & 63;
@@ -203,15 +232,17 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
   const rsrc_t rs = H16 ? make_rsrc(p.steps16 + n_blk * G, (N - n_blk) * G * 2)
                         : make_rsrc(p.scales + n_blk * G, (N - n_blk) * G * 4);
   const rsrc_t rz = make_rsrc(p.zeros + n_blk * zrow, (N - n_blk) * zrow);
+  const rsrc_t rm = make_rsrc(p.meta, MT ? row_blocks * G * 64 : 0);
 
   // (step, zero) of the workgroup's kCols rows x this wave's gn groups:
   // element e -> row e / gn, group e % gn (consecutive lanes read consecutive
   // groups of a row).  Past the rows, or for a wave without groups, the
   // offsets point outside the buffers and the loads return 0.
-  constexpr int kSzIters = kCols * kWaveGroups / 64;
+  constexpr int kSzIters = MT ? 1 : kCols * kWaveGroups / 64;
   uint32_t sz_step[kSzIters], sz_zero[kSzIters];
 #pragma unroll
   for (int i = 0; i < kSzIters; ++i) {
+    if constexpr (MT) break;
     const int e = i * 64 + lane;
     const int row = gn > 0 ? e / gn : kCols, gl = gn > 0 ? e - row * gn : 0;
     const bool ok = row < kCols;
@@ -245,10 +276,18 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
   // outside the buffer: the load returns zeros without a memory access.
   auto load = [&](GroupLoads<NB, MB>& L, int gl) {
     const bool in = gl < gn;
+    if constexpr (MT) {
+      // Word c16 of metadata tile (row block, group): this lane's row.
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        L.m[b] = __builtin_amdgcn_raw_buffer_load_b32(
+            rm, in ? (uint32_t)((((n_blk / 16 + b) * G + g0 + gl) * 16 + c16) * 4) : 0xFFFFFFF0u,
+            0, 0);
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const uint32_t off = in ? q_off[b] + (uint32_t)gl * kStride : 0xFFFFFFF0u;
-      L.q[b] = I3 ? ld12(rq, off) : ld16(rq, off);
+      L.q[b] = I3 ? ld_codes12(rq, off) : ld_codes16(rq, off);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -261,21 +300,23 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) load(R[d], d);
 
+  if constexpr (!MT) {
 #pragma unroll
-  for (int i = 0; i < kSzIters; ++i) {
-    const int e = i * 64 + lane;
-    const int row = gn > 0 ? e / gn : kCols, gl = gn > 0 ? e - row * gn : 0;
-    if (row < kCols) {
-      if constexpr (H16) {
-        const uint32_t zq = (sz_zero[i] >> (4 * ((g0 + gl) & 1))) & 15u;
-        ssz[wave][row][gl] = make_float2(
-            (float)__builtin_bit_cast(_Float16, (uint16_t)sz_step[i]), 128.f + (float)zq);
-      } else {
-        ssz[wave][row][gl] = make_float2(__uint_as_float(sz_step[i]), 128.f + (float)sz_zero[i]);
+    for (int i = 0; i < kSzIters; ++i) {
+      const int e = i * 64 + lane;
+      const int row = gn > 0 ? e / gn : kCols, gl = gn > 0 ? e - row * gn : 0;
+      if (row < kCols) {
+        if constexpr (H16) {
+          const uint32_t zq = (sz_zero[i] >> (4 * ((g0 + gl) & 1))) & 15u;
+          ssz[wave][row][gl] = make_float2(
+              (float)__builtin_bit_cast(_Float16, (uint16_t)sz_step[i]), 128.f + (float)zq);
+        } else {
+          ssz[wave][row][gl] = make_float2(__uint_as_float(sz_step[i]), 128.f + (float)sz_zero[i]);
+        }
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   uint32_t kc;   // see codes_b; an opaque VGPR value, so it is not folded back into a literal
   asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(kc));
@@ -304,7 +345,13 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) bq[b][j] = codes_b(words[j], kc);
       }
-      sz[b] = ssz[wave][b * 16 + c16][gl];
+      if constexpr (MT) {
+        const uint32_t m = L.m[b];
+        sz[b] = make_float2((float)__builtin_bit_cast(_Float16, (uint16_t)(m & 0xFFFFu)),
+                            128.f + (float)((m >> 16) & 15u));
+      } else {
+        sz[b] = ssz[wave][b * 16 + c16][gl];
+      }
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -428,6 +475,24 @@ __global__ __launch_bounds__(256) void decode_tiles_kernel(const uint32_t* __res
   for (int i = 0; i < W; ++i) tiles[e * W + i] = o[i];
 }
 
+// Metadata tiles from the compact metadata: word r of tile b*G + g holds the
+// binary16 step of row 16b + r and group g in bits 0..15 and its zero in
+// bits 16..19; rows past N give 0.  One thread per word.
+__global__ __launch_bounds__(256) void meta_tiles_kernel(const uint16_t* __restrict__ steps16,
+                                                         const uint8_t* __restrict__ zeros4,
+                                                         int64_t N, int64_t G,
+                                                         uint32_t* __restrict__ meta) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (N + 15) / 16 * G * 16) return;
+  const int64_t t = e / 16, b = t / G, g = t - b * G, n = 16 * b + e % 16;
+  uint32_t word = 0u;
+  if (n < N) {
+    const uint32_t z = (zeros4[n * ((G + 1) / 2) + g / 2] >> (4 * (g & 1))) & 15u;
+    word = (uint32_t)steps16[n * G + g] | (z << 16);
+  }
+  meta[e] = word;
+}
+
 // y[i] = sum over s of part[s][i], s ascending.
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ part,
                                                             int64_t count, int splits,
@@ -478,6 +543,20 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
   return d;
 }
 
+size_t decode_meta_bytes(int64_t N, int64_t K) {
+  return (size_t)((N + 15) / 16) * 16 * (size_t)(K / kGroup) * 4;
+}
+
+hipError_t launch_decode_meta(const uint16_t* steps16, const uint8_t* zeros4, int64_t N,
+                              int64_t K, uint32_t* meta, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int64_t G = K / kGroup;
+  const int64_t words = (N + 15) / 16 * G * 16;
+  meta_tiles_kernel<<<(unsigned)ceil_div(words, (int64_t)256), 256, 0, stream>>>(steps16, zeros4,
+                                                                                 N, G, meta);
+  return hipGetLastError();
+}
+
 size_t decode_tiles_bytes(int64_t N, int64_t K, bool int3_dense) {
   return (size_t)((N + 15) / 16) * 16 * (size_t)(int3_dense ? 3 * K / 8 : K / 2);
 }
@@ -497,7 +576,7 @@ hipError_t launch_decode_tiles(const uint32_t* qweight, int64_t N, int64_t K, bo
 
 namespace {
 
-template <bool H16>
+template <int META>
 hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* ws,
                            hipStream_t stream, bool int3_dense, bool tiled) {
   const int64_t M = p.M, N = p.N;
@@ -514,29 +593,34 @@ hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* 
   dim3 grid((unsigned)ceil_div(N, (int64_t)16 * nb), (unsigned)d.splits, (unsigned)tz);
   // More groups per workgroup than kWaves waves can take: the wide
   // workgroup (decode_plan gives it only to M <= 6, so one token block and
-  // at most 2 column blocks).
-  const bool wide = d.groups_per_split > kBlockGroups;
+  // at most 2 column blocks).  Up to 8 tokens, layers with fewer than 320
+  // column blocks (one workgroup per CU or less) take it too, with half the
+  // groups per wave: more loads in flight per CU.  Measured on the
+  // Llama-3-8B o_proj layer (4096 x 4096) at M = 1 and 4: 5.69 -> 5.35 and
+  // 5.95 -> 5.72 us (LDS table), 5.67 -> 4.73 and 6.02 -> 5.06 us (metadata
+  // tiles); at 16 tokens no faster.
+  const bool wide = d.groups_per_split > kBlockGroups || (M <= 8 && b1 < 320 && mb == 1 && nb <= 2);
   if (wide && (mb != 1 || nb > 2 || d.groups_per_split > kWavesWide * kWaveGroups))
     return hipErrorInvalidValue;
   auto go = [&](auto NBc, auto MBc, auto Wc) {
     constexpr int nbv = decltype(NBc)::value, mbv = decltype(MBc)::value;
     constexpr int wv = decltype(Wc)::value;
     const unsigned threads = 64 * wv;
-    if constexpr (H16) {
-      // The compact metadata is read with tiled codes only.
+    if constexpr (META != kMetaF32) {
+      // The compact metadata and its tiles are read with tiled codes only.
       if (int3_dense)
-        decode_gemm_kernel<nbv, mbv, true, true, true, wv><<<grid, threads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, true, true, META, wv><<<grid, threads, 0, stream>>>(p);
       else
-        decode_gemm_kernel<nbv, mbv, false, true, true, wv><<<grid, threads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, false, true, META, wv><<<grid, threads, 0, stream>>>(p);
     } else {
       if (int3_dense && tiled)
-        decode_gemm_kernel<nbv, mbv, true, true, false, wv><<<grid, threads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, true, true, kMetaF32, wv><<<grid, threads, 0, stream>>>(p);
       else if (int3_dense)
-        decode_gemm_kernel<nbv, mbv, true, false, false, wv><<<grid, threads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, true, false, kMetaF32, wv><<<grid, threads, 0, stream>>>(p);
       else if (tiled)
-        decode_gemm_kernel<nbv, mbv, false, true, false, wv><<<grid, threads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, false, true, kMetaF32, wv><<<grid, threads, 0, stream>>>(p);
       else
-        decode_gemm_kernel<nbv, mbv, false, false, false, wv><<<grid, threads, 0, stream>>>(p);
+        decode_gemm_kernel<nbv, mbv, false, false, kMetaF32, wv><<<grid, threads, 0, stream>>>(p);
     }
   };
   auto go_mb = [&](auto NBc) {
@@ -572,6 +656,7 @@ DecodeParams decode_params(const uint16_t* a, int64_t M, int64_t N, int64_t K,
   p.scales = nullptr;
   p.steps16 = nullptr;
   p.zeros = nullptr;
+  p.meta = nullptr;
   p.out = d.splits > 1 ? (float*)ws : y;
   p.M = M;
   p.N = N;
@@ -591,7 +676,7 @@ hipError_t launch_decode_gemm(const uint16_t* a, int64_t M, int64_t N, int64_t K
   DecodeParams p = decode_params(a, M, N, K, qweight, d, y, ws);
   p.scales = scales;
   p.zeros = zeros;
-  return decode_dispatch<false>(p, d, y, ws, stream, int3_dense, tiled);
+  return decode_dispatch<kMetaF32>(p, d, y, ws, stream, int3_dense, tiled);
 }
 
 hipError_t launch_decode_gemm16(const uint16_t* a, int64_t M, int64_t N, int64_t K,
@@ -603,7 +688,17 @@ hipError_t launch_decode_gemm16(const uint16_t* a, int64_t M, int64_t N, int64_t
   DecodeParams p = decode_params(a, M, N, K, tiles, d, y, ws);
   p.steps16 = steps16;
   p.zeros = zeros4;
-  return decode_dispatch<true>(p, d, y, ws, stream, int3_dense, true);
+  return decode_dispatch<kMetaH16>(p, d, y, ws, stream, int3_dense, true);
+}
+
+hipError_t launch_decode_gemm_meta(const uint16_t* a, int64_t M, int64_t N, int64_t K,
+                                   const uint32_t* tiles, const uint32_t* meta, float* y, void* ws,
+                                   hipStream_t stream, bool int3_dense) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const DecodePlan d = decode_plan(M, N, K);
+  DecodeParams p = decode_params(a, M, N, K, tiles, d, y, ws);
+  p.meta = meta;
+  return decode_dispatch<kMetaTiles>(p, d, y, ws, stream, int3_dense, true);
 }
 
 }  // namespace awq

@@ -146,6 +146,21 @@ int main(void) {
   EXPECT(awq_decode_gemm_tiled16(F, 4, 8, 128, F, (void*)0x10001, F, AWQ_LAYOUT_NIBBLE, 128, F, NULL,
                                  0, NULL), AWQ_ERR_ALIGN);
 
+  /* metadata tiles */
+  EXPECT(awq_decode_meta_size(big - 1, k22, 128, &b), AWQ_ERR_SHAPE);
+  EXPECT(awq_decode_meta_size(k22, k22, 128, &b), AWQ_OK);
+  EXPECT(awq_decode_meta_size(8, 128, 128, NULL), AWQ_ERR_NULL);
+  EXPECT(awq_decode_meta(NULL, F, 8, 128, 128, F, NULL), AWQ_ERR_NULL);
+  EXPECT(awq_decode_meta(F, F, 8, 128, 128, (void*)0x10002, NULL), AWQ_ERR_ALIGN);
+  EXPECT(awq_decode_gemm_tiled_meta(F, 4, 8, 128, F, NULL, AWQ_LAYOUT_NIBBLE, 128, F, NULL, 0, NULL),
+         AWQ_ERR_NULL);
+  EXPECT(awq_decode_gemm_tiled_meta(F, 4, 8, 128, F, (void*)0x10002, AWQ_LAYOUT_NIBBLE, 128, F, NULL,
+                                    0, NULL), AWQ_ERR_ALIGN);
+  EXPECT(awq_decode_gemm_tiled_meta(F, 65, 8, 128, F, F, AWQ_LAYOUT_NIBBLE, 128, F, NULL, 0, NULL),
+         AWQ_ERR_SHAPE);
+  EXPECT(awq_decode_gemm_tiled_meta(F, 4, 8, 32768, F, F, AWQ_LAYOUT_NIBBLE, 128, F, NULL, 0, NULL),
+         AWQ_ERR_WORKSPACE);
+
   /* the searches */
   EXPECT(awq_search_scale(F, 0, 128, F, 8, 4, 128, 20, F, F, F, F, F, F, F, F, 0, NULL),
          AWQ_ERR_SHAPE);

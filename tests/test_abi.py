@@ -372,6 +372,39 @@ def test_compact_format_entry_errors():
     assert dec(M=0) == OK and dec(N=0) == OK
 
 
+def test_metadata_tiles_entry_errors():
+    lib = awq.lib()
+    out = ctypes.c_size_t(0)
+    size = lib.awq_decode_meta_size
+    assert size(40, 384, 128, None) == NULL
+    assert size(40, 100, 128, ctypes.byref(out)) == SHAPE
+    assert size(40, 384, 64, ctypes.byref(out)) == UNSUPPORTED
+    assert size(-1, 384, 128, ctypes.byref(out)) == SHAPE
+    assert size(40, 384, 128, ctypes.byref(out)) == OK and out.value == 3 * 16 * 3 * 4
+    assert size(0, 384, 128, ctypes.byref(out)) == OK and out.value == 0
+    mk = lib.awq_decode_meta
+    assert mk(None, FAKE, 40, 384, 128, FAKE, None) == NULL
+    assert mk(FAKE, FAKE, 40, 384, 128, None, None) == NULL
+    assert mk(FAKE + 1, FAKE, 40, 384, 128, FAKE, None) == ALIGN
+    assert mk(FAKE, FAKE, 40, 384, 128, FAKE + 2, None) == ALIGN
+    assert mk(FAKE, FAKE, 40, 100, 128, FAKE, None) == SHAPE
+    assert mk(None, None, 0, 384, 128, None, None) == OK
+    f = lib.awq_decode_gemm_tiled_meta
+
+    def dec(a=FAKE, M=4, N=128, K=4096, t=FAKE, m=FAKE, layout=0, group=128, y=FAKE, ws=None,
+            wsb=0):
+        return f(a, M, N, K, t, m, layout, group, y, ws, wsb, None)
+
+    assert dec(layout=5) == UNSUPPORTED and dec(group=64) == UNSUPPORTED
+    assert dec(m=None) == NULL and dec(a=None) == NULL and dec(t=None) == NULL and dec(y=None) == NULL
+    assert dec(M=65) == SHAPE and dec(K=100) == SHAPE and dec(N=-1) == SHAPE
+    assert dec(m=FAKE + 2) == ALIGN and dec(t=FAKE + 4) == ALIGN and dec(a=FAKE_MIS) == ALIGN
+    assert dec(layout=1, t=FAKE + 2) == ALIGN                        # dense INT3 tiles: 4-byte
+    assert dec(K=32768) == WORKSPACE
+    assert dec(N=1 << 22, K=1 << 13, ws=FAKE, wsb=1 << 40) == SHAPE
+    assert dec(M=0) == OK and dec(N=0) == OK
+
+
 def test_last_error_is_per_thread():
     """Each thread sees the message of its own last failing call."""
     import threading
@@ -434,6 +467,7 @@ def _cpu(shape, dtype):
 @pytest.mark.parametrize("case", [
     "decode_out", "decode_scales_dtype", "decode_zeros_shape", "decode_qweight_cols",
     "decode3_words", "tiled_size", "tiled_scales", "tiled16_steps", "tiled16_zeros4",
+    "meta_steps", "tiled_meta_size", "tiled_meta_tiles",
     "w4a16_inv_s", "w4a16_y_ref", "w4a16_scales", "dequant_s", "divide_rows_s", "residual_y",
     "rmsnorm_gamma", "tiles_qweight", "noncontiguous"])
 def test_python_wrappers_check_shapes_before_the_device(case):
@@ -461,6 +495,12 @@ def test_python_wrappers_check_shapes_before_the_device(case):
                           "steps16 must"),
         "tiled16_zeros4": (lambda: awq.decode_gemm_tiled16(a, tiles, _cpu((N, 2), f16),
                                                            _cpu((N, 2), u8)), "zeros4 must"),
+        "meta_steps": (lambda: awq.decode_meta(_cpu((N, 2), f32), _cpu((N, 1), u8)),
+                       "steps16 must"),
+        "tiled_meta_size": (lambda: awq.decode_gemm_tiled_meta(
+            a, tiles, _cpu((awq.decode_meta_size(N, K) // 4 - 1,), i32), N), "meta must"),
+        "tiled_meta_tiles": (lambda: awq.decode_gemm_tiled_meta(
+            a, tiles[:-4], _cpu((awq.decode_meta_size(N, K) // 4,), i32), N), "tiles must hold"),
         "w4a16_inv_s": (lambda: awq.w4a16_gemm(a, qw, sc, ze, inv_s=_cpu((K - 1,), f32)),
                         "inv_s must"),
         "w4a16_y_ref": (lambda: awq.w4a16_gemm(a, qw, sc, ze, y_ref=_cpu((M, N + 1), f32)),
@@ -479,6 +519,8 @@ def test_python_wrappers_check_shapes_before_the_device(case):
         fn()
     # with every shape right, the same call fails only on the device check
     good = {"decode_out": lambda: awq.decode_gemm(a, qw, sc, ze, out=_cpu((M, N), f32)),
+            "tiled_meta_size": lambda: awq.decode_gemm_tiled_meta(
+                a, tiles, _cpu((awq.decode_meta_size(N, K) // 4,), i32), N),
             "tiled_size": lambda: awq.decode_gemm_tiled(a, tiles, sc, ze)}
     if case in good:
         with pytest.raises(ValueError, match="GPU tensor"):

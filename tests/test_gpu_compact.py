@@ -1,8 +1,9 @@
 """The compact deployment format (binary16 steps, two 4-bit zeros per byte)
 on the GPU against the oracle: the final pack bit for bit, the metadata
-expansion bit for bit, and the decode contraction on decode tiles reading
-the compact metadata (bit-identical to the fp32-metadata kernel on the
-expanded metadata, and within the contraction tolerance of the oracle)."""
+expansion bit for bit, the metadata tiles bit for bit, and the decode
+contraction on decode tiles reading the compact metadata or its tiles
+(bit-identical to each other and to the fp32-metadata kernel on the expanded
+metadata, and within the contraction tolerance of the oracle)."""
 
 import numpy as np
 import pytest
@@ -135,8 +136,12 @@ def test_decode_gemm_tiled16(dev, shape, dense3):
     y16 = awq.decode_gemm_tiled16(ad, tiles, st_d, zb_d, layout)
     sc, ze = awq.expand_meta16(st_d, zb_d)
     y32 = awq.decode_gemm_tiled(ad, tiles, sc, ze, layout)
+    meta = awq.decode_meta(st_d, zb_d)
+    ymt = awq.decode_gemm_tiled_meta(ad, tiles, meta, N, layout)
     torch.cuda.synchronize()
+    assert np.array_equal(meta.cpu().numpy().view(np.uint32), O.decode_meta(sb, zb, K))
     assert torch.equal(y16, y32)
+    assert torch.equal(ymt, y16)
     _, fro = gemm_close(y16.cpu().numpy(), O.decode_gemm16(a, words, sb, zb, 128, dense3=dense3))
     assert fro <= 1e-5
 

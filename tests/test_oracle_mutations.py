@@ -209,6 +209,29 @@ def _mut_block_deploys_on_unfolded_u(mp):
     mp.setattr(OA, "divide_rows", lambda v, s: np.asarray(v, np.float64) if np.ndim(v) == 1 else orig(v, s))
 
 
+def _mut_meta_zero_at_bit_20(mp):
+    """Metadata tiles with the zero one nibble too high (bits 20..23)."""
+    orig = OA.decode_meta
+
+    def meta(steps16, zeros4, K, group=128):
+        m = orig(steps16, zeros4, K, group).astype(np.uint64)
+        return ((m & np.uint64(0xFFFF)) | ((m >> np.uint64(16)) << np.uint64(20))).astype(np.uint32)
+    mp.setattr(oracle, "decode_meta", meta)
+
+
+def _mut_meta_row_major(mp):
+    """Metadata in row-major order [row][group] instead of tile order."""
+    def meta(steps16, zeros4, K, group=128):
+        G = K // group
+        st = np.asarray(steps16, dtype=np.uint16).astype(np.uint64)
+        N = st.shape[0]
+        _, z = OA.unpack_meta16(steps16, zeros4, G)
+        w = np.zeros((-(-N // 16) * 16, G), dtype=np.uint64)
+        w[:N] = st | (z.astype(np.uint64) << np.uint64(16))
+        return w.reshape(-1).astype(np.uint32)
+    mp.setattr(oracle, "decode_meta", meta)
+
+
 def _mut_block_up_rows_not_folded(mp):
     """The up rows' steps keep their unfolded values (1/s2 dropped)."""
     orig = OA.divide_rows
@@ -223,7 +246,7 @@ MUTATIONS = [_mut_floor_instead_of_rint, _mut_drop_inv_s, _mut_alpha_grid_closed
              _mut_tiles_row_major_inside, _mut_tiles_codes_in_pack_order, _mut_rmsnorm_without_mean, _mut_silu_is_sigmoid,
              _mut_fold_multiplies, _mut_f16_ties_away, _mut_quantize16_codes_with_fp32_step,
              _mut_zero_nibbles_swapped, _mut_half_step_no_clamp, _mut_block_deploys_on_unfolded_u,
-             _mut_block_up_rows_not_folded]
+             _mut_block_up_rows_not_folded, _mut_meta_zero_at_bit_20, _mut_meta_row_major]
 
 PINS = [
     P.test_quantizer_worked_group,
@@ -242,6 +265,7 @@ PINS = [
     P.test_pack3_big_integer_brute_force,
     lambda: P.test_decode_tiles_brute_force(False),
     lambda: P.test_decode_tiles_brute_force(True),
+    P.test_decode_meta_brute_force,
     P.test_rmsnorm_closed_form_and_scaling,
     P.test_silu_mul_against_torch_and_identities,
     P.test_divide_rows_and_residual_against_library,

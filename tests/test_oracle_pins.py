@@ -327,6 +327,32 @@ def test_pack3_big_integer_brute_force():
         O.pack3(np.full((1, 32), 8))
 
 
+def test_decode_meta_brute_force():
+    """Every word of the metadata tiles, found by walking the definition in
+    pure Python: word r of tile b*G + g is row 16b + r's binary16 step bits
+    for group g, plus its zero (the nibble of byte g // 2, low for even g)
+    shifted to bit 16; rows past N give 0."""
+    rng = np.random.default_rng(43)
+    N, K = 37, 640
+    G = K // 128
+    steps16 = rng.integers(0, 2 ** 16, size=(N, G), dtype=np.uint64).astype(np.uint16)
+    zeros4 = rng.integers(0, 256, size=(N, (G + 1) // 2), dtype=np.uint64).astype(np.uint8)
+    zeros4[:, -1] &= 0x0F                  # G odd: the high nibble past the last group is 0
+    meta = O.decode_meta(steps16, zeros4, K)
+    NB = -(-N // 16)
+    assert meta.dtype == np.uint32 and meta.size == NB * G * 16
+    for b in range(NB):
+        for g in range(G):
+            for r in range(16):
+                n = 16 * b + r
+                want = 0
+                if n < N:
+                    byte = int(zeros4[n, g // 2])
+                    z = (byte >> 4) if g % 2 else (byte & 15)
+                    want = int(steps16[n, g]) + z * 65536
+                assert int(meta[(b * G + g) * 16 + r]) == want, (b, g, r)
+
+
 def test_dense_int3_storage_and_product():
     """Dense INT3 takes 3 bits per weight plus 40 bits per group (3.31 bits,
     4.83x smaller than bf16), and the product from its words equals the
