@@ -104,15 +104,18 @@ KERNEL_LABELS = [
     ("transpose_pad_kernel", "X^T (Gram form)"),
     ("gram_split_kernel", "G split (Gram form)"),
     # decode_gemm_kernel<column blocks, token blocks, INT3 dense, tiled,
-    # compact metadata, waves>
+    # metadata source (0 fp32 table, 1 compact table, 2 metadata tiles), waves>
     *[(("decode_gemm_kernel<", f", {flags}, {waves}>"), label + ("" if waves == 4 else ", 8 waves"))
-      for flags, label in (("false, true, true", "decode GEMM, tiles, compact metadata"),
-                           ("true, true, true", "decode GEMM, dense INT3 tiles, compact metadata"),
-                           ("false, true, false", "decode GEMM, tiles"),
-                           ("true, true, false", "decode GEMM, dense INT3 tiles"),
-                           ("false, false, false", "decode GEMM, row-major words"),
-                           ("true, false, false", "decode GEMM, dense INT3 row-major"))
+      for flags, label in (("false, true, 2", "decode GEMM, tiles, metadata tiles"),
+                           ("true, true, 2", "decode GEMM, dense INT3 tiles, metadata tiles"),
+                           ("false, true, 1", "decode GEMM, tiles, compact metadata"),
+                           ("true, true, 1", "decode GEMM, dense INT3 tiles, compact metadata"),
+                           ("false, true, 0", "decode GEMM, tiles"),
+                           ("true, true, 0", "decode GEMM, dense INT3 tiles"),
+                           ("false, false, 0", "decode GEMM, row-major words"),
+                           ("true, false, 0", "decode GEMM, dense INT3 row-major"))
       for waves in (4, 8)],
+    ("meta_tiles_kernel", "metadata tiles"),
     ("decode_gemm", "decode W4A16 GEMM (M <= 64)"),
     ("decode_reduce", "decode split-K reduce"),
     ("act_stats_partial", "act_stats partial sums"),
@@ -357,8 +360,10 @@ def bench_decode(awq, dev, stream, reps: int = 96, layers=("qkv", "o_proj", "gat
                  token_counts=(1, 2, 4, 8, 16, 64)) -> dict:
     """Decode-shaped W4A16 contraction on the Llama-3-8B block's layers
     (M = 1, 2, 4, 8, 16 and 64 tokens, random packed INT4 weights), on decode tiles
-    (the deployment path), on the row-major packed words, and on decode
-    tiles with the compact metadata (binary16 steps, 4-bit zeros).  Launches cycle
+    with fp32 steps and u8 zeros, on the row-major packed words, on decode
+    tiles with the compact metadata (binary16 steps, 4-bit zeros) and on
+    decode tiles with metadata tiles (the compact metadata as one u32 per row
+    and group, the deployment module's path).  Launches cycle
     through enough copies of the packed weights (>= 768 MiB in all) that each
     one streams from HBM rather than the 256 MiB last-level cache."""
     import torch
@@ -385,7 +390,8 @@ def bench_decode(awq, dev, stream, reps: int = 96, layers=("qkv", "o_proj", "gat
             ze = torch.randint(0, 16, (N, K // 128), dtype=torch.uint8, device=dev, generator=gen)
             z4 = torch.randint(0, 256, (N, (K // 128 + 1) // 2), dtype=torch.uint8, device=dev,
                                generator=gen)
-            packs.append((qw, awq.decode_tiles(qw, K), sc, ze, sc.half(), z4))
+            st16 = sc.half()
+            packs.append((qw, awq.decode_tiles(qw, K), sc, ze, st16, z4, awq.decode_meta(st16, z4)))
         for M in token_counts:
             a = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -393,34 +399,45 @@ def bench_decode(awq, dev, stream, reps: int = 96, layers=("qkv", "o_proj", "gat
             ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
             def tiled(i):
-                _, tl, sc, ze, _, _ = packs[i % copies]
+                _, tl, sc, ze, _, _, _ = packs[i % copies]
                 awq.decode_gemm_tiled(a, tl, sc, ze, awq.LAYOUT_NIBBLE, out=y, workspace=ws)
 
             def row_major(i):
-                qw, _, sc, ze, _, _ = packs[i % copies]
+                qw, _, sc, ze, _, _, _ = packs[i % copies]
                 awq.decode_gemm(a, qw, sc, ze, 4, out=y, workspace=ws)
 
             def compact(i):
-                _, tl, _, _, st16, z4 = packs[i % copies]
+                _, tl, _, _, st16, z4, _ = packs[i % copies]
                 awq.decode_gemm_tiled16(a, tl, st16, z4, awq.LAYOUT_NIBBLE, out=y, workspace=ws)
+
+            def meta_tiles(i):
+                _, tl, _, _, _, _, mt = packs[i % copies]
+                awq.decode_gemm_tiled_meta(a, tl, mt, N, awq.LAYOUT_NIBBLE, out=y, workspace=ws)
             if M == token_counts[0]:
                 _graph_time_ms(tiled, reps, stream)   # untimed: first touch of this layer's copies
             ms = _graph_time_ms(tiled, reps, stream)
             ms_rm = _graph_time_ms(row_major, reps, stream)
             ms_c = _graph_time_ms(compact, reps, stream)
+            ms_m = _graph_time_ms(meta_tiles, reps, stream)
             io = 2.0 * M * K + 4.0 * M * N
             nbytes = wbytes + io
             gbs = nbytes / (ms * 1e-3) / 1e9
             cbytes = N * K / 2 + 2.5 * N * K / 128 + io
             cgbs = cbytes / (ms_c * 1e-3) / 1e9
+            mbytes = N * K / 2 + 4.0 * N * K / 128 + io
+            mgbs = mbytes / (ms_m * 1e-3) / 1e9
             out[f"{name}_M{M}"] = {"N": N, "K": K, "us": ms * 1e3, "gbs": gbs,
                                    "frac_hbm_peak": gbs / PEAK_HBM_GBS, "bytes": nbytes,
                                    "row_major_us": ms_rm * 1e3, "compact_us": ms_c * 1e3,
                                    "compact_bytes": cbytes, "compact_gbs": cgbs,
+                                   "meta_tiles_us": ms_m * 1e3, "meta_tiles_bytes": mbytes,
+                                   "meta_tiles_gbs": mgbs,
+                                   "meta_tiles_frac_hbm_peak": mgbs / PEAK_HBM_GBS,
                                    "weight_copies": copies}
             log(f"decode {name} M={M} N={N} K={K}: tiles {ms * 1e3:.2f} us = {gbs:.0f} GB/s; "
                 f"row-major {ms_rm * 1e3:.2f} us; compact metadata {ms_c * 1e3:.2f} us = "
-                f"{cgbs:.0f} GB/s ({copies} weight copies)")
+                f"{cgbs:.0f} GB/s; metadata tiles {ms_m * 1e3:.2f} us = {mgbs:.0f} GB/s "
+                f"({copies} weight copies)")
         del packs
         torch.cuda.empty_cache()
     return out
