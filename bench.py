@@ -42,7 +42,7 @@ HEADLINE = ("llama2_70b_mlp", "gate_up", 4)
 def traffic_file(workload: str, layer: str) -> str:
     return os.path.join(PROFILES, f"search_contraction_{workload}_{layer}_traffic.txt")
 # The search's per-candidate contraction X . D^T with the sum-of-squares epilogue.
-DOMINANT_KERNEL = "diff_sq_kernel"
+DOMINANT_KERNEL = "mfma16_kernel<false, 1>"
 GEMM_SOURCES = ["w4a16_gemm.hip", "device_common.h", "awq_internal.h"]
 
 
@@ -78,13 +78,12 @@ def committed_traffic(workload: str, layer: str):
 # ---- rocprofv3 output summaries (run on the host after a profiled bench) ----
 
 KERNEL_LABELS = [
-    ("diff_sq_kernel", "search contraction X.D^T (difference operand, sum of squares)"),
-    ("gemm_kernel<false, false, 4, false, true, true>",
-     "Gram-form contraction (split D . split G, dot epilogue)"),
-    ("gemm_kernel<false, false, 4, false, true, false>",
-     "candidate_sse vs y_ref (bf16 operand, squared-error epilogue)"),
-    ("gemm_kernel<false, false, 4, true, true", "staged W4A16 product with SSE (bf16 operand, Y and SSE)"),
-    ("gemm_kernel<false, false, 4, true, false", "reference_gemm / Gram matrix / staged W4A16 (bf16, fp32 out)"),
+    # mfma16_kernel<store Y, epilogue (0 none, 1 sum of squares, 2 SSE vs Y_ref, 3 dot with Y_ref)>
+    ("mfma16_kernel<false, 1>", "search contraction X.D^T (difference operand, sum of squares)"),
+    ("mfma16_kernel<false, 3>", "Gram-form contraction (split D . split G, dot epilogue)"),
+    ("mfma16_kernel<false, 2>", "candidate_sse vs y_ref (bf16 operand, squared-error epilogue)"),
+    ("mfma16_kernel<true, 2>", "staged W4A16 product with SSE (bf16 operand, Y and SSE)"),
+    ("mfma16_kernel<true, 0>", "reference_gemm / Gram matrix / staged W4A16 (bf16, fp32 out)"),
     ("gemm_kernel<true, true, 2, false, true", "w4a16_gemm_sse (INT4 operand, 1/s folded, SSE epilogue)"),
     ("gemm_kernel<true", "w4a16_gemm (INT4 operand, other epilogues)"),
     ("quantize_kernel<4, 1,", "dequant_operand (quantize -> bf16 B)"),

@@ -255,9 +255,11 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
  * (the one awq_w4a16_gemm forms in LDS) is written once per call into the
  * workspace by a streaming kernel, then contracted on the bf16 matrix cores:
  * each weight is dequantized once instead of once per 256-row tile of X,
- * which pays once X has more than a few hundred rows.  Y is bit-identical
- * to awq_w4a16_gemm's for the same codes (same operand, same accumulation
- * order); sse agrees up to the order of its fp64 partial sums.
+ * which pays once X has more than a few hundred rows.  Same operand as
+ * awq_w4a16_gemm, contracted on the 16x16x32 matrix-core form (that one
+ * uses 32x32x16): Y agrees with it to fp32 rounding of the sums, not bit
+ * for bit; dense INT3 and the same codes in 4-bit containers give the same
+ * Y bit for bit.
  *   layout  AWQ_LAYOUT_NIBBLE: qweight u32 [N][K/8] (awq_quantize_pack, bits
  *           3 or 4); AWQ_LAYOUT_INT3_DENSE: qweight u32 [N][3K/32]
  *           (awq_quantize_pack3, bits 3); 4-byte aligned.

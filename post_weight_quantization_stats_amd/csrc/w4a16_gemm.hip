@@ -41,8 +41,10 @@
 //   * Epilogue: optional fp32 store of Y; optional fp64 sum of (Y - Y_ref)^2
 //     per tile written to a partial slot (partials are reduced later in a
 //     fixed order, so results are bit-reproducible).
-//   * The search's own contraction, the sum of squares of X . D^T for a
-//     difference operand D, is diff_sq_kernel below: the same tiles, ring and
+//   * Every product with a bf16 weight operand (the search's sum of squares
+//     of X . D^T for a difference operand D, the reference product, the
+//     staged W4A16 product, the Gram form's contractions, the candidate SSE
+//     against Y_ref) runs mfma16_kernel below: the same tiles, ring and
 //     publication, with v_mfma_f32_16x16x32_bf16 instead of 32x32x16.
 #include <type_traits>
 
@@ -554,13 +556,18 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// The search's contraction: the fp64 sum of squares of Y = X . D^T per
-// 256x256 tile, for a bf16 difference operand D (so Y is the candidate's
-// output error itself; robotsatlas AWQ page, "How it works": the scale
-// minimises the layer's output error).  Same tiles, XCD-aware order, LDS
-// layout, DMA ring and publication two k-steps ahead as gemm_kernel<bf16>,
-// but on v_mfma_f32_16x16x32_bf16: per k-step one k32 substep of 8 A and 4 B
-// fragments per wave (128x64) and 32 MFMAs.  Under the chip's power limit
+// Epilogues of mfma16_kernel beside the optional fp32 store of Y.
+enum Epilogue { kEpiNone = 0, kEpiSq = 1, kEpiSse = 2, kEpiDot = 3 };
+
+// The contractions with a bf16 weight operand, Y = X . B^T per 256x256 tile
+// (B: the search's difference operand D, so Y is the candidate's output
+// error itself, robotsatlas AWQ page, "How it works": the scale minimises the
+// layer's output error; or W, a staged dequantized operand, a Gram factor).
+// kStoreY writes fp32 Y; kEpi adds per tile the fp64 sum of Y^2 (kEpiSq), of
+// (Y - Y_ref)^2 (kEpiSse) or of Y * Y_ref (kEpiDot) to a partial slot.  Same
+// tiles, XCD-aware order, LDS layout, DMA ring and publication two k-steps
+// ahead as gemm_kernel, but on v_mfma_f32_16x16x32_bf16: per k-step one k32
+// substep of 8 A and 4 B fragments per wave (128x64) and 32 MFMAs.  Under the chip's power limit
 // the 16x16x32 form sustains more flops than 32x32x16 on random operands
 // (measured with operands in registers: 78% against 74% of the 2.5 PFLOP/s
 // spec; zero operands reach 91% and 98%); on the search's operands this
@@ -568,7 +575,8 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
 // (128 per lane) stay in VGPRs; the next step's fragments are read into the
 // registers each row block frees right after its MFMAs, so two fragment sets
 // never coexist in full (238 VGPRs, two waves per SIMD, no spills).
-__global__ __launch_bounds__(512, 1) void diff_sq_kernel(Params p) {
+template <bool kStoreY, int kEpi>
+__global__ __launch_bounds__(512, 1) void mfma16_kernel(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int WN = 4, NW = 8, DPW = Cfg<WN>::kDma;
   static_assert(DPW == 2, "the vmcnt below assumes 2 copies per operand per step");
@@ -686,21 +694,111 @@ __global__ __launch_bounds__(512, 1) void diff_sq_kernel(Params p) {
     step(k + 3, std::integral_constant<int, 3>{});
   }
 
-  // Sum of squares in fp64 (each square exact); lane holds column l16 of
-  // each 16x16 block.  Columns past N are masked; rows past M are zero.
-  double sse = 0.0;
+  // Lane holds column l16 of each 16x16 block (r, j) and its rows 4*lq + e,
+  // e = 0..3: tile row wm*128 + 16r + 4lq + e, tile column wn*64 + 16j + l16.
+  // Rows past M fall outside the buffer resources (stores dropped, Y_ref
+  // reads 0; their accumulators are 0); columns past N are masked.
+  const uint32_t lane_off = (uint32_t)(((int64_t)(wm * 128 + 4 * lq) * N + wn * 64 + l16) * 4);
+  if constexpr (kStoreY) {
+    // The wave's 128 x 64 block goes out through LDS, 64 rows at a time, so
+    // that each store writes 4 whole rows of 256 bytes (one 16-byte piece per
+    // lane) instead of 4 x 64 scattered bytes.  The k-loop's stage arrays are
+    // free once every wave has passed the barrier and the prefetches past the
+    // last step have landed; each wave then uses one 16 KiB array of its own.
+    // Inside a row the 16-column block index is XOR-ed with the row's quad
+    // ((row >> 2) & 3), so the fragment-order writes hit 64 distinct banks.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    float* lw;
+    switch (wave) {                       // a switch keeps every pointer in LDS space
+      case 0: lw = (float*)sa0; break;
+      case 1: lw = (float*)sa1; break;
+      case 2: lw = (float*)sa2; break;
+      case 3: lw = (float*)sa3; break;
+      case 4: lw = (float*)sb0; break;
+      case 5: lw = (float*)sb1; break;
+      case 6: lw = (float*)sb2; break;
+      default: lw = (float*)sb3; break;
+    }
+    const rsrc_t ro = make_rsrc(p.y + m0 * N + n0, ((uint64_t)(M - m0) * N - n0) * 4);
+    const int pc = lane & 15, pr = lane >> 4;             // piece column, row in a group of 4
+    const int64_t col = wn * 64 + 4 * pc;                 // within the tile
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bool ok = n0 + wn * 64 + j * 16 + l16 < N;
-    double dpart = 0.0;
+    for (int ph = 0; ph < 2; ++ph) {
+      if (ph == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // phase 0's reads done
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
+      for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const double a = (double)acc[r][j][e];
-        dpart = fma(a, a, dpart);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * rr + 4 * lq + e;         // within the phase
+            lw[row * 64 + 16 * (j ^ lq) + l16] = acc[4 * ph + rr][j][e];
+          }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = 4 * q + pr;
+        const float4 v = *(const float4*)&lw[row * 64 + 16 * ((pc >> 2) ^ ((row >> 2) & 3)) +
+                                             4 * (pc & 3)];
+        const uint32_t off =
+            (uint32_t)((((int64_t)wm * 128 + 64 * ph + row) * N + col) * 4);
+        if (n0 + col + 3 < N) {
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                    __float_as_uint(v.w)}, ro, off, 0, 0);
+        } else {
+          const float vs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (n0 + col + i < N)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vs[i]), ro, off + 4 * i, 0, 0);
+        }
       }
-    sse += ok ? dpart : 0.0;
+    }
+  }
+  if constexpr (kEpi == kEpiNone) return;
+  // fp64 sums: each square and each product of two fp32 values is exact.
+  double sse = 0.0;
+  if constexpr (kEpi == kEpiSq) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = n0 + wn * 64 + j * 16 + l16 < N;
+      double dpart = 0.0;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double a = (double)acc[r][j][e];
+          dpart = fma(a, a, dpart);
+        }
+      sse += ok ? dpart : 0.0;
+    }
+  } else {
+    const rsrc_t ry = make_rsrc(p.y_ref + m0 * N + n0, ((uint64_t)(M - m0) * N - n0) * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = n0 + wn * 64 + j * 16 + l16 < N;
+      float yv[8][4];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          yv[r][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              ry, lane_off + (uint32_t)(((int64_t)(16 * r + e) * N + 16 * j) * 4), 0, 0));
+      double dpart = 0.0;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (kEpi == kEpiDot) {
+            dpart = fma((double)acc[r][j][e], (double)yv[r][e], dpart);
+          } else {
+            const double d = (double)(acc[r][j][e] - yv[r][e]);
+            dpart = fma(d, d, dpart);
+          }
+        }
+      sse += ok ? dpart : 0.0;
+    }
   }
   sse = wave_sum_f64(sse);
   __shared__ double wsq[NW];
@@ -739,17 +837,18 @@ hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream) {
   // bf16 operand: 8 waves (two per SIMD) measured faster; INT4: the dequant
   // VALU work favours 4 waves with 128x128 tiles each.
   const bool y = op.y != nullptr, sse = op.partials != nullptr;
+  constexpr unsigned kThreads16 = 512;
   if (op.qweight == nullptr && op.sq) {
-    diff_sq_kernel<<<blocks, Cfg<4>::kThreads, 0, stream>>>(p);
+    mfma16_kernel<false, kEpiSq><<<blocks, kThreads16, 0, stream>>>(p);
   } else if (op.qweight == nullptr && op.dot) {
-    gemm_kernel<false, false, 4, false, true, true><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
+    mfma16_kernel<false, kEpiDot><<<blocks, kThreads16, 0, stream>>>(p);
   } else if (op.qweight == nullptr) {
     if (y && sse)
-      gemm_kernel<false, false, 4, true, true><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
+      mfma16_kernel<true, kEpiSse><<<blocks, kThreads16, 0, stream>>>(p);
     else if (sse)
-      gemm_kernel<false, false, 4, false, true><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
+      mfma16_kernel<false, kEpiSse><<<blocks, kThreads16, 0, stream>>>(p);
     else
-      gemm_kernel<false, false, 4, true, false><<<blocks, Cfg<4>::kThreads, 0, stream>>>(p, nullptr);
+      mfma16_kernel<true, kEpiNone><<<blocks, kThreads16, 0, stream>>>(p);
   } else {
     auto go = [&](auto kInv) {
       constexpr bool inv = decltype(kInv)::value;

@@ -9,7 +9,7 @@ nothing of the product runs in PyTorch.
     (q - z) * step exactly).
   * M > 64: the staged W4A16 product (the operand bf16(f32((q - z) * step))
     written once per call into a cached workspace, then the bf16
-    matrix-core contraction; bit-identical to the fused kernel that
+    matrix-core contraction; the same operand as the fused kernel that
     dequantizes in LDS, and faster once many tokens reuse each weight).
 
 Both agree with the unrounded product to the contraction tolerance; they are

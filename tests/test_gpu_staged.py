@@ -5,8 +5,9 @@ weights with 16-bit activations; sourcepulse AWQ project page, opening
 paragraph: 3- and 4-bit weights).
 
 Checked against the oracle's deploy product (elementwise, the GEMM
-tolerance) and against the fused W4A16 kernel, whose output it must equal
-bit for bit (same operand, same accumulation order); dense INT3 codes must
+tolerance), beside the fused W4A16 kernel on the same codes (same operand,
+contracted on the 32x32x16 matrix-core form instead of 16x16x32, so the two
+agree to the contraction tolerance, not bit for bit); dense INT3 codes must
 give exactly the result of the same codes in 4-bit containers.  The
 deployment module runs dense INT3 layers at every token count.
 """
@@ -63,10 +64,10 @@ def test_staged_matches_fused_and_oracle(dev, shape, use_inv_s):
     y_f, sse_f = awq.w4a16_gemm(xd, qwd, scd, zed, 4, 128, inv_s=invd, y_ref=yrd)
     torch.cuda.synchronize()
     gemm_close(y_s.cpu().numpy(), y_oracle)
-    assert torch.equal(y_s, y_f)
+    gemm_close(y_f.cpu().numpy(), y_oracle)
     sse_ref = float(np.sum((y_oracle - y_ref32) ** 2))
     assert float(sse_s.item()) == pytest.approx(sse_ref, rel=1e-4)
-    assert float(sse_s.item()) == pytest.approx(float(sse_f.item()), rel=1e-12)
+    assert float(sse_f.item()) == pytest.approx(sse_ref, rel=1e-4)
     # y only, and sse only, give the same numbers as the call with both
     assert torch.equal(awq.w4a16_gemm(xd, qwd, scd, zed, 4, 128, inv_s=invd, staged=True), y_s)
     _, sse_only = awq.w4a16_gemm(xd, qwd, scd, zed, 4, 128, inv_s=invd, y_ref=yrd,
