@@ -115,6 +115,10 @@ KERNEL_LABELS = [
                            ("true, false, 0", "decode GEMM, dense INT3 row-major"))
       for waves in (4, 8)],
     ("meta_tiles_kernel", "metadata tiles"),
+    ("mfma_ceiling_kernel", "ceiling: matrix cores from registers"),
+    ("copy_ceiling_kernel", "ceiling: copy"),
+    ("read_ceiling_kernel", "ceiling: read"),
+    ("write_ceiling_kernel", "ceiling: write"),
     ("decode_gemm", "decode W4A16 GEMM (M <= 64)"),
     ("decode_reduce", "decode split-K reduce"),
     ("act_stats_partial", "act_stats partial sums"),
@@ -336,6 +340,39 @@ def event_time_ms(fn, reps: int, stream) -> float:
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / reps
+
+
+def measure_ceilings(awq, dev, stream, src) -> dict:
+    """What this GPU sustains, from the library's ceiling kernels: the
+    matrix cores fed from registers (bf16 16x16x32, random and zero
+    operands) and streaming copy / read / write over the bytes of `src`
+    (larger than the last-level cache).  Kernels are reported as fractions
+    of these beside their fractions of the spec."""
+    import torch
+    nbytes = src.numel() * src.element_size() // 16 * 16
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    gbs = lambda nb, ms: nb / (ms * 1e-3) / 1e9
+    grids = (1024, 4096, 16384, 65536)
+    # The best grid of each kernel (it differs by kernel and part).
+    t_copy, t_read, t_write = (min(event_time_ms(
+        lambda: awq.ceiling_stream(mode, a, b, nbytes, g), 5, stream) for g in grids)
+        for mode, a, b in ((awq.CEILING_COPY, src, dst), (awq.CEILING_READ, src, sink),
+                           (awq.CEILING_WRITE, None, dst)))
+    blocks, iters = 1024, 5000
+    flops = awq.ceiling_mfma(sink, blocks, iters)
+    t_mfma = event_time_ms(lambda: awq.ceiling_mfma(sink, blocks, iters), 3, stream)
+    t_mfma0 = event_time_ms(lambda: awq.ceiling_mfma(sink, blocks, iters, zero=True), 3, stream)
+    out = {"copy_gbs": gbs(2.0 * nbytes, t_copy), "read_gbs": gbs(nbytes, t_read),
+           "write_gbs": gbs(nbytes, t_write), "stream_bytes": nbytes, "stream_grids": grids,
+           "mfma_bf16_tflops": flops / (t_mfma * 1e-3) / 1e12,
+           "mfma_bf16_zero_operands_tflops": flops / (t_mfma0 * 1e-3) / 1e12,
+           "mfma_flops_per_launch": flops}
+    log(f"measured ceilings: copy {out['copy_gbs']:.0f} GB/s, read {out['read_gbs']:.0f} GB/s, "
+        f"write {out['write_gbs']:.0f} GB/s; bf16 matrix cores from registers "
+        f"{out['mfma_bf16_tflops']:.0f} TFLOP/s (zero operands {out['mfma_bf16_zero_operands_tflops']:.0f})")
+    del dst, sink
+    return out
 
 
 def _graph_time_ms(fn, reps: int, stream) -> float:
@@ -946,6 +983,7 @@ def main() -> int:
     cp_src, cp_dst = wd.clone(), torch.empty_like(wd)
     t_copy = event_time_ms(lambda: cp_dst.copy_(cp_src), reps * 5, stream)
     del cp_src, cp_dst
+    ceil = measure_ceilings(awq, dev, stream, wd)
     stats_bytes = 2.0 * M * K + 4.0 * K
     quant_bytes = 2.0 * N * K + 4.0 * K + N * K / 2 + 5.0 * N * K / spec.group
     deq_bytes = 2.0 * N * K + 8.0 * K + 2.0 * N * K
@@ -957,10 +995,12 @@ def main() -> int:
         f"{t_copy * 1e3:.1f} us = {gbs(4.0 * N * K, t_copy):.0f} GB/s")
 
     def mfma_entry(ms):
-        return {"ms": ms, "tflops": tf(ms), "frac_mfma_peak": tf(ms) / PEAK_BF16_TFLOPS}
+        return {"ms": ms, "tflops": tf(ms), "frac_mfma_peak": tf(ms) / PEAK_BF16_TFLOPS,
+                "frac_measured_mfma": tf(ms) / ceil["mfma_bf16_tflops"]}
 
-    def hbm_entry(nbytes, ms):
+    def hbm_entry(nbytes, ms, ceiling="copy_gbs"):
         return {"us": ms * 1e3, "gbs": gbs(nbytes, ms), "frac_hbm_peak": gbs(nbytes, ms) / PEAK_HBM_GBS,
+                "frac_measured_ceiling": gbs(nbytes, ms) / ceil[ceiling], "ceiling": ceiling,
                 "bytes": nbytes}
 
     kern = {"search_contraction": mfma_entry(t_sse)}
@@ -972,7 +1012,7 @@ def main() -> int:
             "w4a16_gemm_sse": mfma_entry(t_w4),
             "reference_gemm": mfma_entry(t_ref)})
     kern.update({
-        "act_stats": hbm_entry(stats_bytes, t_stats),
+        "act_stats": hbm_entry(stats_bytes, t_stats, "read_gbs"),
         "quantize_pack": hbm_entry(quant_bytes, t_quant),
         "dequant_operand": hbm_entry(deq_bytes, t_deq),
         "diff_operand": hbm_entry(deq_bytes, t_diff),
@@ -998,7 +1038,10 @@ def main() -> int:
                      "kernel": "per-candidate contraction X.D^T (D = B - W) with fused sum of squares",
                      "flops_per_launch": flops, "ms_per_launch": t_sse,
                      "algorithmic_bytes_per_launch": 2.0 * M * K + 2.0 * N * K,
-                     "kernel_source_hash": gemm_source_hash()},
+                     "kernel_source_hash": gemm_source_hash(),
+                     "measured_peak": ceil["mfma_bf16_tflops"],
+                     "frac_measured_peak": tf(t_sse) / ceil["mfma_bf16_tflops"]},
+        "ceilings": ceil,
         "kernels": kern,
         "host": host_info(),
         "cpu_baseline": None,

@@ -437,6 +437,38 @@ awq_status awq_decode_gemm_tiled_meta(const uint16_t* a, int64_t M, int64_t N, i
                                       void* stream);
 
 /*
+ * Measured ceilings of the GPU, so that each kernel can be reported as a
+ * fraction of what the part sustains as well as of its spec (the
+ * measurement of the path: GEMM TFLOP/s against the matrix cores' peak,
+ * streaming kernels against the copy ceiling).  Not steps of the method;
+ * time them with events on the given stream.
+ *   awq_ceiling_mfma: `blocks` workgroups of 8 waves, each wave issuing
+ *     iters x 32 v_mfma_f32_16x16x32_bf16 on operands held in registers (the
+ *     search contraction's 128x64 wave tile), pseudo-random bf16 operands
+ *     of magnitude 1..2, or zeros when zero_operands != 0 (the part is
+ *     power-limited, so data sets the clock).  *flops (host) receives the
+ *     flops of the launch.  sink: a device float, never written in
+ *     practice.  1 <= blocks <= 65536, 1 <= iters <= 2^20.
+ *   awq_ceiling_stream: mode AWQ_CEILING_COPY copies `bytes` from src to
+ *     dst; AWQ_CEILING_READ reads src (dst: a device u32 sink, never written
+ *     in practice); AWQ_CEILING_WRITE writes dst (16-byte element i gets the
+ *     u32 values i, i^1, i^2, i^3 of its low 32 bits; src unused).  16 bytes
+ *     per lane in a grid-stride loop over `blocks` workgroups of 256 threads
+ *     (1 <= blocks <= 65536; the fastest grid differs by mode and part, so
+ *     sweep it).  bytes: a positive multiple of 16; the buffers used 16-byte
+ *     aligned.
+ */
+typedef enum {
+  AWQ_CEILING_COPY = 0,
+  AWQ_CEILING_READ = 1,
+  AWQ_CEILING_WRITE = 2
+} awq_ceiling_mode;
+awq_status awq_ceiling_mfma(int32_t blocks, int32_t iters, int32_t zero_operands, float* sink,
+                            int64_t* flops, void* stream);
+awq_status awq_ceiling_stream(int32_t mode, const void* src, void* dst, size_t bytes,
+                              int32_t blocks, void* stream);
+
+/*
  * The whole per-layer search (robotsatlas "How it works", "Key mechanisms";
  * "Computational complexity": cost grows with layers x grid points x
  * calibration tokens).  Steps, all on `stream` with no host synchronisation:

@@ -21,13 +21,16 @@ __all__ = ["AwqError", "lib", "library_path", "act_stats", "candidate_scales", "
            "dequant_operand", "diff_operand", "candidate_sse", "quantize_pack3", "decode_gemm3",
            "decode_tiles", "decode_tiles_size", "decode_gemm_tiled", "decode_gemm_tiled_noalloc", "LAYOUT_NIBBLE", "LAYOUT_INT3_DENSE",
            "quantize_pack16", "expand_meta16", "decode_gemm_tiled16", "decode_meta_size",
-           "decode_meta", "decode_gemm_tiled_meta",
+           "decode_meta", "decode_gemm_tiled_meta", "ceiling_mfma", "ceiling_stream",
+           "CEILING_COPY", "CEILING_READ", "CEILING_WRITE",
            "rmsnorm", "silu_mul", "divide_rows", "residual_add", "workspace_size",
            "OP_ACT_STATS", "OP_W4A16_GEMM", "OP_SEARCH_SCALE", "OP_CANDIDATE_SCALES",
            "OP_DECODE_GEMM", "OP_CANDIDATE_SSE", "OP_SEARCH_SCALE_GRAM", "OP_W4A16_GEMM_STAGED"]
 
 (OP_ACT_STATS, OP_W4A16_GEMM, OP_SEARCH_SCALE, OP_CANDIDATE_SCALES, OP_DECODE_GEMM,
  OP_CANDIDATE_SSE, OP_SEARCH_SCALE_GRAM, OP_W4A16_GEMM_STAGED) = 0, 1, 2, 3, 4, 5, 6, 7
+
+CEILING_COPY, CEILING_READ, CEILING_WRITE = 0, 1, 2
 
 _c_void_p, _i64, _i32, _size_t = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 
@@ -64,6 +67,8 @@ _SIGNATURES = {
     "awq_decode_meta": ([_c_void_p, _c_void_p, _i64, _i64, _i32, _c_void_p, _c_void_p], _i32),
     "awq_decode_gemm_tiled_meta": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _i32, _i32,
                                     _c_void_p, _c_void_p, _size_t, _c_void_p], _i32),
+    "awq_ceiling_mfma": ([_i32, _i32, _i32, _c_void_p, ctypes.POINTER(_i64), _c_void_p], _i32),
+    "awq_ceiling_stream": ([_i32, _c_void_p, _c_void_p, _size_t, _i32, _c_void_p], _i32),
     "awq_rmsnorm": ([_c_void_p, _i64, _i64, _c_void_p, ctypes.c_double, _c_void_p, _c_void_p,
                      _c_void_p], _i32),
     "awq_silu_mul": ([_c_void_p, _i64, _i64, _c_void_p, _c_void_p], _i32),
@@ -667,6 +672,33 @@ def decode_gemm_tiled_meta(a: torch.Tensor, tiles: torch.Tensor, meta: torch.Ten
                                             0 if ws is None else ws.numel(), _stream(dev)),
            "awq_decode_gemm_tiled_meta")
     return y
+
+
+def ceiling_mfma(sink: torch.Tensor, blocks: int, iters: int, zero: bool = False) -> int:
+    """Launch the matrix-core ceiling kernel (awq_ceiling_mfma) on the
+    current stream; returns the launch's flops.  sink: one float on the GPU."""
+    _tensor(sink, "sink", torch.float32)
+    dev = _gpu(sink=sink)
+    flops = ctypes.c_int64(0)
+    _check(lib().awq_ceiling_mfma(blocks, iters, int(bool(zero)), _ptr(sink), ctypes.byref(flops),
+                                  _stream(dev)), "awq_ceiling_mfma")
+    return int(flops.value)
+
+
+def ceiling_stream(mode: int, src: torch.Tensor | None, dst: torch.Tensor, nbytes: int,
+                   blocks: int = 4096) -> None:
+    """Launch a streaming ceiling kernel (awq_ceiling_stream) over nbytes on
+    the current stream with `blocks` workgroups: CEILING_COPY src -> dst,
+    CEILING_READ src (dst a sink), CEILING_WRITE dst."""
+    need_dst = 4 if mode == CEILING_READ else nbytes
+    if dst.numel() * dst.element_size() < need_dst or not dst.is_contiguous():
+        raise ValueError(f"dst must be a contiguous buffer of at least {need_dst} bytes")
+    if mode != CEILING_WRITE and (src is None or src.numel() * src.element_size() < nbytes
+                                  or not src.is_contiguous()):
+        raise ValueError(f"src must be a contiguous buffer of at least {nbytes} bytes")
+    dev = _gpu(src=src, dst=dst)
+    _check(lib().awq_ceiling_stream(mode, _ptr(src), _ptr(dst), nbytes, blocks, _stream(dev)),
+           "awq_ceiling_stream")
 
 
 def _search_outputs(K: int, N: int, n_grid: int, group: int, dev) -> dict:

@@ -711,6 +711,44 @@ awq_status awq_decode_gemm_tiled_meta(const uint16_t* a, int64_t M, int64_t N, i
   }
 }
 
+awq_status awq_ceiling_mfma(int32_t blocks, int32_t iters, int32_t zero_operands, float* sink,
+                            int64_t* flops, void* stream) {
+  try {
+    if (blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 20))
+      return fail(AWQ_ERR_SHAPE, "ceiling_mfma needs 1 <= blocks <= 65536 and 1 <= iters <= 2^20");
+    if (sink == nullptr || flops == nullptr) return fail(AWQ_ERR_NULL, "sink and flops are required");
+    if ((uintptr_t)sink & 3u) return fail(AWQ_ERR_ALIGN, "sink must be 4-byte aligned");
+    *flops = awq::mfma_ceiling_flops(blocks, iters);
+    AWQ_TRY_LAUNCH(awq::launch_mfma_ceiling(blocks, iters, zero_operands != 0, sink,
+                                            (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
+awq_status awq_ceiling_stream(int32_t mode, const void* src, void* dst, size_t bytes,
+                              int32_t blocks, void* stream) {
+  try {
+    if (mode != AWQ_CEILING_COPY && mode != AWQ_CEILING_READ && mode != AWQ_CEILING_WRITE)
+      return fail(AWQ_ERR_UNSUPPORTED, "unknown ceiling mode %d", mode);
+    if (bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 40))
+      return fail(AWQ_ERR_SHAPE, "bytes must be a positive multiple of 16, at most 2^40");
+    if (blocks < 1 || blocks > 65536)
+      return fail(AWQ_ERR_SHAPE, "blocks must lie in [1, 65536]");
+    const bool uses_src = mode != AWQ_CEILING_WRITE;
+    if ((uses_src && src == nullptr) || dst == nullptr)
+      return fail(AWQ_ERR_NULL, "%s", uses_src ? "src and dst are required" : "dst is required");
+    if ((uses_src && misaligned(src)) || (mode == AWQ_CEILING_READ ? ((uintptr_t)dst & 3u) != 0
+                                                                    : misaligned(dst)))
+      return fail(AWQ_ERR_ALIGN, "src and dst must be 16-byte aligned (the read sink 4-byte)");
+    AWQ_TRY_LAUNCH(awq::launch_stream_ceiling(mode, src, dst, bytes, blocks, (hipStream_t)stream));
+    return ok();
+  } catch (...) {
+    return fail(AWQ_ERR_LAUNCH, "internal error");
+  }
+}
+
 awq_status awq_candidate_sse(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint16_t* b,
                              const float* y_ref, double* sse, void* ws, size_t ws_bytes,
                              void* stream) {

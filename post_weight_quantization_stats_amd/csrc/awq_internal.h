@@ -159,6 +159,13 @@ size_t decode_tiles_bytes(int64_t N, int64_t K, bool int3_dense);
 hipError_t launch_decode_tiles(const uint32_t* qweight, int64_t N, int64_t K, bool int3_dense,
                                uint32_t* tiles, hipStream_t stream);
 
+// Measured ceilings (ceilings.hip): matrix cores fed from registers, and
+// streaming copy (mode 0), read (1) and write (2) kernels.
+hipError_t launch_mfma_ceiling(int blocks, int iters, bool zero, float* sink, hipStream_t stream);
+int64_t mfma_ceiling_flops(int blocks, int iters);
+hipError_t launch_stream_ceiling(int mode, const void* src, void* dst, size_t bytes, int blocks,
+                                 hipStream_t stream);
+
 // Static scratch of the entry point that allocates nothing: its size, and
 // the device address of the current device's copy (looked up once per device
 // with hipGetSymbolAddress; see noalloc.hip).

@@ -1,0 +1,148 @@
+// Measured ceilings of the part, for reporting each kernel against what the
+// chip sustains beside its spec (the measurement of the method's hot path:
+// GEMM TFLOP/s as a fraction of the measured matrix-core peak, streaming
+// kernels as a fraction of the measured copy ceiling).  Not a step of the
+// method; the bench times these launches with HIP events.
+//
+//   * mfma_ceiling_kernel: each wave holds the operands and the 32
+//     accumulators of the search contraction's 128x64 wave tile in registers
+//     and issues v_mfma_f32_16x16x32_bf16 back to back, with no memory
+//     traffic.  Operands are pseudo-random bf16 values of magnitude 1..2 with
+//     random signs (the chip is power-limited, so the switching activity of
+//     the data sets the clock), or all zero.
+//   * stream kernels: 16 bytes per lane in a grid-stride loop over a grid the
+//     caller picks (the best grid differs by kernel, so a caller sweeps it);
+//     copy (one load and one store per step), read-only (non-temporal, four
+//     loads in flight) and write-only.  These were the fastest forms in a
+//     sweep of unroll depth, cache hints and grid size on 896 MiB buffers.
+#include "awq_internal.h"
+#include "device_common.h"
+
+namespace awq {
+
+namespace {
+
+constexpr int kCeilThreads = 512;              // 8 waves: two per SIMD, as the contraction
+constexpr int kStreamThreads = 256;
+constexpr int kUnroll = 4;
+
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// Eight bf16 values 1 <= |v| < 2 with random mantissas and signs (or zeros).
+__device__ __forceinline__ bf16x8 ceiling_operand(uint32_t seed, bool zero) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h = mix32(seed * 4u + (uint32_t)i);
+    const uint32_t lo = 0x3F80u | (h & 0x807Fu), hi = 0x3F80u | ((h >> 16) & 0x807Fu);
+    r[i] = zero ? 0u : (lo | (hi << 16));
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__global__ __launch_bounds__(kCeilThreads) void mfma_ceiling_kernel(float* __restrict__ sink,
+                                                                    int iters, int zero) {
+  const uint32_t t = blockIdx.x * kCeilThreads + threadIdx.x;
+  bf16x8 a[8], b[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = ceiling_operand(t * 16u + i, zero != 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = ceiling_operand(t * 16u + 8u + j, zero != 0);
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    // Rotate the A operands so consecutive steps multiply different data.
+    const bf16x8 first = a[0];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) a[i] = a[i + 1];
+    a[7] = first;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += acc[i][j][0] + acc[i][j][1] + acc[i][j][2] + acc[i][j][3];
+  if (s == 1234.5f) sink[0] = s;      // practically never: keeps the products live
+}
+
+__global__ __launch_bounds__(kStreamThreads) void copy_ceiling_kernel(const u32x4* __restrict__ src,
+                                                                      u32x4* __restrict__ dst,
+                                                                      int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride)
+    dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(kStreamThreads) void read_ceiling_kernel(const u32x4* __restrict__ src,
+                                                                      uint32_t* __restrict__ sink,
+                                                                      int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+  uint32_t acc = 0u;
+  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n; i += stride) acc ^= src[i].x;
+  if (acc == 0x9E3779B9u) sink[0] = acc;   // practically never: keeps the loads live
+}
+
+// dst[i] = (i, i ^ 1, i ^ 2, i ^ 3) for 16-byte element i (low 32 bits of i).
+__global__ __launch_bounds__(kStreamThreads) void write_ceiling_kernel(u32x4* __restrict__ dst,
+                                                                       int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride) {
+    const uint32_t v = (uint32_t)i;
+    dst[i] = u32x4{v, v ^ 1u, v ^ 2u, v ^ 3u};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mfma_ceiling(int blocks, int iters, bool zero, float* sink, hipStream_t stream) {
+  mfma_ceiling_kernel<<<blocks, kCeilThreads, 0, stream>>>(sink, iters, zero ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_ceiling(int mode, const void* src, void* dst, size_t bytes, int blocks,
+                                 hipStream_t stream) {
+  const int64_t n = (int64_t)(bytes / 16);
+  switch (mode) {
+    case 0:
+      copy_ceiling_kernel<<<blocks, kStreamThreads, 0, stream>>>((const u32x4*)src, (u32x4*)dst, n);
+      break;
+    case 1:
+      read_ceiling_kernel<<<blocks, kStreamThreads, 0, stream>>>((const u32x4*)src,
+                                                                 (uint32_t*)dst, n);
+      break;
+    default:
+      write_ceiling_kernel<<<blocks, kStreamThreads, 0, stream>>>((u32x4*)dst, n);
+      break;
+  }
+  return hipGetLastError();
+}
+
+int64_t mfma_ceiling_flops(int blocks, int iters) {
+  // Per wave and iteration 32 MFMAs of 16 x 16 x 32 (2 flops each).
+  return (int64_t)blocks * (kCeilThreads / 64) * iters * 32 * (16 * 16 * 32 * 2);
+}
+
+}  // namespace awq

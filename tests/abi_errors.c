@@ -161,6 +161,17 @@ int main(void) {
   EXPECT(awq_decode_gemm_tiled_meta(F, 4, 8, 32768, F, F, AWQ_LAYOUT_NIBBLE, 128, F, NULL, 0, NULL),
          AWQ_ERR_WORKSPACE);
 
+  /* measured ceilings */
+  {
+    int64_t fl = 0;
+    EXPECT(awq_ceiling_mfma(0, 10, 0, F, &fl, NULL), AWQ_ERR_SHAPE);
+    EXPECT(awq_ceiling_mfma(4, 10, 0, NULL, &fl, NULL), AWQ_ERR_NULL);
+    EXPECT(awq_ceiling_stream(7, F, F, 4096, 1024, NULL), AWQ_ERR_UNSUPPORTED);
+    EXPECT(awq_ceiling_stream(AWQ_CEILING_COPY, F, F, 4100, 1024, NULL), AWQ_ERR_SHAPE);
+    EXPECT(awq_ceiling_stream(AWQ_CEILING_COPY, F, F, 4096, 0, NULL), AWQ_ERR_SHAPE);
+    EXPECT(awq_ceiling_stream(AWQ_CEILING_READ, F, (void*)0x10002, 4096, 1024, NULL), AWQ_ERR_ALIGN);
+  }
+
   /* the searches */
   EXPECT(awq_search_scale(F, 0, 128, F, 8, 4, 128, 20, F, F, F, F, F, F, F, F, 0, NULL),
          AWQ_ERR_SHAPE);

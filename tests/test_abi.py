@@ -405,6 +405,32 @@ def test_metadata_tiles_entry_errors():
     assert dec(M=0) == OK and dec(N=0) == OK
 
 
+def test_ceiling_entry_errors():
+    lib = awq.lib()
+    flops = ctypes.c_int64(0)
+    m = lib.awq_ceiling_mfma
+    assert m(0, 10, 0, FAKE, ctypes.byref(flops), None) == SHAPE
+    assert m(65537, 10, 0, FAKE, ctypes.byref(flops), None) == SHAPE
+    assert m(4, 0, 0, FAKE, ctypes.byref(flops), None) == SHAPE
+    assert m(4, (1 << 20) + 1, 0, FAKE, ctypes.byref(flops), None) == SHAPE
+    assert m(4, 10, 0, None, ctypes.byref(flops), None) == NULL
+    assert m(4, 10, 0, FAKE, None, None) == NULL
+    assert m(4, 10, 0, FAKE + 2, ctypes.byref(flops), None) == ALIGN
+    f = lib.awq_ceiling_stream
+
+    def s(mode, src, dst, nbytes, blocks=1024):
+        return f(mode, src, dst, nbytes, blocks, None)
+
+    assert s(3, FAKE, FAKE, 4096) == UNSUPPORTED
+    assert s(0, FAKE, FAKE, 0) == SHAPE and s(0, FAKE, FAKE, 4100) == SHAPE
+    assert s(0, FAKE, FAKE, 4096, 0) == SHAPE and s(0, FAKE, FAKE, 4096, 65537) == SHAPE
+    assert s(0, None, FAKE, 4096) == NULL and s(1, None, FAKE, 4096) == NULL
+    assert s(2, None, None, 4096) == NULL
+    assert s(0, FAKE + 4, FAKE, 4096) == ALIGN and s(0, FAKE, FAKE + 4, 4096) == ALIGN
+    assert s(1, FAKE, FAKE + 2, 4096) == ALIGN                  # the read sink: 4-byte
+    assert s(2, None, FAKE + 8, 4096) == ALIGN
+
+
 def test_last_error_is_per_thread():
     """Each thread sees the message of its own last failing call."""
     import threading
