@@ -103,8 +103,10 @@ KERNEL_LABELS = [
     ("transpose_pad_kernel", "X^T (Gram form)"),
     ("gram_split_kernel", "G split (Gram form)"),
     # decode_gemm_kernel<column blocks, token blocks, INT3 dense, tiled,
-    # metadata source (0 fp32 table, 1 compact table, 2 metadata tiles), waves>
-    *[(("decode_gemm_kernel<", f", {flags}, {waves}>"), label + ("" if waves == 4 else ", 8 waves"))
+    # metadata source (0 fp32 table, 1 compact table, 2 metadata tiles), waves,
+    # one token>
+    *[(("decode_gemm_kernel<", f", {flags}, {waves}, {one}>"),
+       label + ("" if waves == 4 else ", 8 waves") + (", one token" if one == "true" else ""))
       for flags, label in (("false, true, 2", "decode GEMM, tiles, metadata tiles"),
                            ("true, true, 2", "decode GEMM, dense INT3 tiles, metadata tiles"),
                            ("false, true, 1", "decode GEMM, tiles, compact metadata"),
@@ -113,7 +115,7 @@ KERNEL_LABELS = [
                            ("true, true, 0", "decode GEMM, dense INT3 tiles"),
                            ("false, false, 0", "decode GEMM, row-major words"),
                            ("true, false, 0", "decode GEMM, dense INT3 row-major"))
-      for waves in (4, 8)],
+      for waves in (4, 8) for one in ("false", "true")],
     ("meta_tiles_kernel", "metadata tiles"),
     ("mfma_ceiling_kernel", "ceiling: matrix cores from registers"),
     ("copy_ceiling_kernel", "ceiling: copy"),
