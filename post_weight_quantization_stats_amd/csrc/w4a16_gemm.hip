@@ -574,7 +574,7 @@ enum Epilogue { kEpiNone = 0, kEpiSq = 1, kEpiSse = 2, kEpiDot = 3 };
 // kernel is 4-5% faster than gemm_kernel's 32x32x16 form.  The accumulators
 // (128 per lane) stay in VGPRs; the next step's fragments are read into the
 // registers each row block frees right after its MFMAs, so two fragment sets
-// never coexist in full (238 VGPRs, two waves per SIMD, no spills).
+// never coexist in full (230-236 VGPRs, two waves per SIMD, no spills).
 template <bool kStoreY, int kEpi>
 __global__ __launch_bounds__(512, 1) void mfma16_kernel(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
