@@ -678,6 +678,8 @@ def ceiling_mfma(sink: torch.Tensor, blocks: int, iters: int, zero: bool = False
     """Launch the matrix-core ceiling kernel (awq_ceiling_mfma) on the
     current stream; returns the launch's flops.  sink: one float on the GPU."""
     _tensor(sink, "sink", torch.float32)
+    if sink.numel() < 1:
+        raise ValueError("sink must hold at least one float")
     dev = _gpu(sink=sink)
     flops = ctypes.c_int64(0)
     _check(lib().awq_ceiling_mfma(blocks, iters, int(bool(zero)), _ptr(sink), ctypes.byref(flops),
