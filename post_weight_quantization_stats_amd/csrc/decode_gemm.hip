@@ -78,6 +78,12 @@ namespace {
 constexpr int kWaves = 4;                     // waves per workgroup (kWavesWide: see decode_plan)
 constexpr int kWavesWide = 8;
 constexpr int kDepth = 2;                     // groups of codes in flight per wave
+// At one token (A1) a ring slot holds one activation load instead of four,
+// and a ring of 4 groups measured fastest (Llama-3-8B layers at M = 1: qkv
+// 6.72 -> 5.99 us, o_proj 4.74 -> 4.62, gate_up 15.9 -> 14.9, down 11.6 ->
+// 8.8; 6 and 8 were slower).  With four activation loads per group deeper
+// rings were slower at every M.
+constexpr int kDepthOne = 4;
 constexpr int kWaveGroups = 16;               // most groups per wave
 constexpr int kBlockGroups = kWaves * kWaveGroups;   // 64 groups = 8192 channels
 // Token blocks of 16 per workgroup: more tokens go to more workgroups along
@@ -318,9 +324,10 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
     }
   };
 
-  GroupLoads<NB, MB> R[kDepth];
+  constexpr int kRing = A1 ? kDepthOne : kDepth;
+  GroupLoads<NB, MB> R[kRing];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) load(R[d], d);
+  for (int d = 0; d < kRing; ++d) load(R[d], d);
 
   if constexpr (!MT) {
 #pragma unroll
@@ -414,13 +421,13 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
     }
   };
 
-  // Ring of kDepth register sets, unrolled so every index is static.  Loads
+  // Ring of kRing register sets, unrolled so every index is static.  Loads
   // are unconditional, so the compiler's wait counts stay exact.
-  for (int gl = 0; gl < gn; gl += kDepth) {
+  for (int gl = 0; gl < gn; gl += kRing) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
+    for (int d = 0; d < kRing; ++d) {
       if (gl + d < gn) compute(R[d], gl + d);
-      load(R[d], gl + d + kDepth);
+      load(R[d], gl + d + kRing);
     }
   }
 
