@@ -104,9 +104,10 @@ KERNEL_LABELS = [
     ("gram_split_kernel", "G split (Gram form)"),
     # decode_gemm_kernel<column blocks, token blocks, INT3 dense, tiled,
     # metadata source (0 fp32 table, 1 compact table, 2 metadata tiles), waves,
-    # one token>
-    *[(("decode_gemm_kernel<", f", {flags}, {waves}, {one}>"),
-       label + ("" if waves == 4 else ", 8 waves") + (", one token" if one == "true" else ""))
+    # one token, two to four tokens>
+    *[(("decode_gemm_kernel<", f", {flags}, {waves}, {few}>"),
+       label + ("" if waves == 4 else ", 8 waves") +
+       {"false, false": "", "true, false": ", one token", "false, true": ", 2-4 tokens"}[few])
       for flags, label in (("false, true, 2", "decode GEMM, tiles, metadata tiles"),
                            ("true, true, 2", "decode GEMM, dense INT3 tiles, metadata tiles"),
                            ("false, true, 1", "decode GEMM, tiles, compact metadata"),
@@ -115,7 +116,7 @@ KERNEL_LABELS = [
                            ("true, true, 0", "decode GEMM, dense INT3 tiles"),
                            ("false, false, 0", "decode GEMM, row-major words"),
                            ("true, false, 0", "decode GEMM, dense INT3 row-major"))
-      for waves in (4, 8) for one in ("false", "true")],
+      for waves in (4, 8) for few in ("false, false", "true, false", "false, true")],
     ("meta_tiles_kernel", "metadata tiles"),
     ("mfma_ceiling_kernel", "ceiling: matrix cores from registers"),
     ("copy_ceiling_kernel", "ceiling: copy"),

@@ -78,7 +78,7 @@ namespace {
 constexpr int kWaves = 4;                     // waves per workgroup (kWavesWide: see decode_plan)
 constexpr int kWavesWide = 8;
 constexpr int kDepth = 2;                     // groups of codes in flight per wave
-// At one token (A1) a ring slot holds one activation load instead of four,
+// At one to four tokens (A1, A4) a ring slot holds one activation load instead of four,
 // and a ring of 4 groups measured fastest (Llama-3-8B layers at M = 1: qkv
 // 6.72 -> 5.99 us, o_proj 4.74 -> 4.62, gate_up 15.9 -> 14.9, down 11.6 ->
 // 8.8; 6 and 8 were slower).  With four activation loads per group deeper
@@ -208,13 +208,15 @@ struct GroupLoads {
 // 16-row blocks of tokens (M <= 16 * MB); I3: dense INT3 codes; TL: tiled;
 // META: where the steps and zeros come from (MetaSource; the compact
 // metadata and its tiles go with tiled codes only).  W waves per workgroup.
-// A1: exactly one token (tiled codes, MB = 1).
-template <int NB, int MB, bool I3, bool TL, int META = kMetaF32, int W = kWaves, bool A1 = false>
+// A1: exactly one token; A4: two to four tokens (both: tiled codes, MB = 1).
+template <int NB, int MB, bool I3, bool TL, int META = kMetaF32, int W = kWaves, bool A1 = false,
+          bool A4 = false>
 __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr bool H16 = META == kMetaH16, MT = META == kMetaTiles;
   static_assert(META == kMetaF32 || TL, "the compact metadata goes with tiled codes");
-  static_assert(!A1 || (TL && MB == 1), "the one-token form takes tiled codes, one token block");
+  static_assert(!(A1 || A4) || (TL && MB == 1 && !(A1 && A4)),
+                "the few-token forms take tiled codes and one token block");
   constexpr int kCols = 16 * NB;
   // (step, 128 + z) table, 8 to 64 KiB (none with metadata tiles).
   __shared__ float2 ssz[MT ? 1 : W][MT ? 1 : kCols][MT ? 1 : kWaveGroups];
@@ -296,6 +298,16 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
   // four pieces are broadcast along the row: one load per group instead of
   // four (gate_up at M = 1: 16.35 -> 15.32 us; the others 1%).
   const uint32_t a1_off = (uint32_t)((g0 * kGroup + 32 * g4 + 8 * (lane & 3)) * 2);
+  // Two to four tokens (A4): the 16 pieces a quarter-row of the fragments
+  // holds (4 tokens x 4 pieces) are loaded once, lane p of the row taking
+  // token p / 4's piece p % 4 (tokens past M repeat token M - 1), and each
+  // lane gathers its row's four pieces with ds_bpermute: one activation load
+  // per group instead of four, and the ring of 4 then pays (Llama-3-8B at 2
+  // and 4 tokens: qkv 6.78 -> 6.45 and 7.10 -> 6.57 us, gate_up 16.15 ->
+  // 14.87 and 16.57 -> 15.16, down 10.41 -> 9.24 and 10.39 -> 9.36).
+  const uint32_t a4_off = (uint32_t)(((int64_t)min(c16 >> 2, (int)M - 1) * K + g0 * kGroup +
+                                      32 * g4 + 8 * (lane & 3)) * 2);
+  const int a4_src = ((lane & 48) | (4 * (c16 & 3))) * 4;    // byte address of piece 0's lane
   // Loads of local group gl.  Past the wave's last group the offset points
   // outside the buffer: the load returns zeros without a memory access.
   auto load = [&](GroupLoads<NB, MB>& L, int gl) {
@@ -315,6 +327,8 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
     }
     if constexpr (A1) {
       L.a[0][0] = ld16(ra, in ? a1_off + (uint32_t)gl * (kGroup * 2) : 0xFFFFFFF0u);
+    } else if constexpr (A4) {
+      L.a[0][0] = ld16(ra, in ? a4_off + (uint32_t)gl * (kGroup * 2) : 0xFFFFFFF0u);
     } else {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -324,7 +338,7 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
     }
   };
 
-  constexpr int kRing = A1 ? kDepthOne : kDepth;
+  constexpr int kRing = (A1 || A4) ? kDepthOne : kDepth;
   GroupLoads<NB, MB> R[kRing];
 #pragma unroll
   for (int d = 0; d < kRing; ++d) load(R[d], d);
@@ -392,6 +406,14 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
         ad[1] = row_bcast<1>(v);
         ad[2] = row_bcast<2>(v);
         ad[3] = row_bcast<3>(v);
+      } else if constexpr (A4) {
+        const uint4 v = L.a[0][0];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ad[j] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(a4_src + 4 * j, (int)v.x),
+                             (uint32_t)__builtin_amdgcn_ds_bpermute(a4_src + 4 * j, (int)v.y),
+                             (uint32_t)__builtin_amdgcn_ds_bpermute(a4_src + 4 * j, (int)v.z),
+                             (uint32_t)__builtin_amdgcn_ds_bpermute(a4_src + 4 * j, (int)v.w));
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) ad[j] = L.a[mb][j];
@@ -653,6 +675,20 @@ hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* 
         else
           decode_gemm_kernel<nbv, 1, false, true, META, wv, true><<<grid, threads, 0, stream>>>(p);
         return;
+      }
+      // Two to four tokens: one load and a gather, with metadata tiles only
+      // (with the LDS table it was slower on gate_up at 2 and 4 tokens:
+      // 16.4 -> 18.6 and 16.6 -> 19.0 us).
+      if constexpr (META == kMetaTiles) {
+        if (M <= 4) {
+          if (int3_dense)
+            decode_gemm_kernel<nbv, 1, true, true, META, wv, false, true>
+                <<<grid, threads, 0, stream>>>(p);
+          else
+            decode_gemm_kernel<nbv, 1, false, true, META, wv, false, true>
+                <<<grid, threads, 0, stream>>>(p);
+          return;
+        }
       }
     }
     if constexpr (META != kMetaF32) {
