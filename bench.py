@@ -77,6 +77,11 @@ def committed_traffic(workload: str, layer: str):
 
 # ---- rocprofv3 output summaries (run on the host after a profiled bench) ----
 
+# The decode kernel's few-token template flags (one token, two to four, five
+# to eight), as the demangled name spells them, and their labels.
+FEW_TOKENS = {"false, false, false": "", "true, false, false": ", one token",
+              "false, true, false": ", 2-4 tokens", "false, false, true": ", 5-8 tokens"}
+
 KERNEL_LABELS = [
     # mfma16_kernel<store Y, epilogue (0 none, 1 sum of squares, 2 SSE vs Y_ref, 3 dot with Y_ref)>
     ("mfma16_kernel<false, 1>", "search contraction X.D^T (difference operand, sum of squares)"),
@@ -104,10 +109,9 @@ KERNEL_LABELS = [
     ("gram_split_kernel", "G split (Gram form)"),
     # decode_gemm_kernel<column blocks, token blocks, INT3 dense, tiled,
     # metadata source (0 fp32 table, 1 compact table, 2 metadata tiles), waves,
-    # one token, two to four tokens>
+    # one token, two to four tokens, five to eight tokens>
     *[(("decode_gemm_kernel<", f", {flags}, {waves}, {few}>"),
-       label + ("" if waves == 4 else ", 8 waves") +
-       {"false, false": "", "true, false": ", one token", "false, true": ", 2-4 tokens"}[few])
+       label + ("" if waves == 4 else ", 8 waves") + FEW_TOKENS[few])
       for flags, label in (("false, true, 2", "decode GEMM, tiles, metadata tiles"),
                            ("true, true, 2", "decode GEMM, dense INT3 tiles, metadata tiles"),
                            ("false, true, 1", "decode GEMM, tiles, compact metadata"),
@@ -116,7 +120,7 @@ KERNEL_LABELS = [
                            ("true, true, 0", "decode GEMM, dense INT3 tiles"),
                            ("false, false, 0", "decode GEMM, row-major words"),
                            ("true, false, 0", "decode GEMM, dense INT3 row-major"))
-      for waves in (4, 8) for few in ("false, false", "true, false", "false, true")],
+      for waves in (4, 8) for few in FEW_TOKENS],
     ("meta_tiles_kernel", "metadata tiles"),
     ("mfma_ceiling_kernel", "ceiling: matrix cores from registers"),
     ("copy_ceiling_kernel", "ceiling: copy"),

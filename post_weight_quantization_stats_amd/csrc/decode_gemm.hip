@@ -78,8 +78,8 @@ namespace {
 constexpr int kWaves = 4;                     // waves per workgroup (kWavesWide: see decode_plan)
 constexpr int kWavesWide = 8;
 constexpr int kDepth = 2;                     // groups of codes in flight per wave
-// At one to four tokens (A1, A4) a ring slot holds one activation load instead of four,
-// and a ring of 4 groups measured fastest (Llama-3-8B layers at M = 1: qkv
+// At one to eight tokens (A1, A4, A8) a ring slot holds one or two activation
+// loads instead of four, and a ring of 4 groups measured fastest (Llama-3-8B layers at M = 1: qkv
 // 6.72 -> 5.99 us, o_proj 4.74 -> 4.62, gate_up 15.9 -> 14.9, down 11.6 ->
 // 8.8; 6 and 8 were slower).  With four activation loads per group deeper
 // rings were slower at every M.
@@ -123,6 +123,17 @@ __device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t voff) {
 template <int n>
 __device__ __forceinline__ uint4 row_bcast(uint4 v) {
   constexpr int ctl = 0x150 + n;
+  return make_uint4((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, ctl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, ctl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, ctl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, ctl, 0xF, 0xF, false));
+}
+
+// The value of lane i + n of the lane's 16-lane row (DPP row_shl); lanes
+// past the row's end get 0.
+template <int n>
+__device__ __forceinline__ uint4 row_shl(uint4 v) {
+  constexpr int ctl = 0x100 + n;
   return make_uint4((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, ctl, 0xF, 0xF, false),
                     (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, ctl, 0xF, 0xF, false),
                     (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, ctl, 0xF, 0xF, false),
@@ -208,14 +219,15 @@ struct GroupLoads {
 // 16-row blocks of tokens (M <= 16 * MB); I3: dense INT3 codes; TL: tiled;
 // META: where the steps and zeros come from (MetaSource; the compact
 // metadata and its tiles go with tiled codes only).  W waves per workgroup.
-// A1: exactly one token; A4: two to four tokens (both: tiled codes, MB = 1).
+// A1: exactly one token; A4: two to four tokens; A8: five to eight tokens
+// (each: tiled codes, MB = 1).
 template <int NB, int MB, bool I3, bool TL, int META = kMetaF32, int W = kWaves, bool A1 = false,
-          bool A4 = false>
+          bool A4 = false, bool A8 = false>
 __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr bool H16 = META == kMetaH16, MT = META == kMetaTiles;
   static_assert(META == kMetaF32 || TL, "the compact metadata goes with tiled codes");
-  static_assert(!(A1 || A4) || (TL && MB == 1 && !(A1 && A4)),
+  static_assert(!(A1 || A4 || A8) || (TL && MB == 1 && (int)A1 + (int)A4 + (int)A8 == 1),
                 "the few-token forms take tiled codes and one token block");
   constexpr int kCols = 16 * NB;
   // (step, 128 + z) table, 8 to 64 KiB (none with metadata tiles).
@@ -299,15 +311,20 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
   // four (gate_up at M = 1: 16.35 -> 15.32 us; the others 1%).
   const uint32_t a1_off = (uint32_t)((g0 * kGroup + 32 * g4 + 8 * (lane & 3)) * 2);
   // Two to four tokens (A4): the 16 pieces a quarter-row of the fragments
-  // holds (4 tokens x 4 pieces) are loaded once, lane p of the row taking
-  // token p / 4's piece p % 4 (tokens past M repeat token M - 1), and each
-  // lane gathers its row's four pieces with ds_bpermute: one activation load
-  // per group instead of four, and the ring of 4 then pays (Llama-3-8B at 2
-  // and 4 tokens: qkv 6.78 -> 6.45 and 7.10 -> 6.57 us, gate_up 16.15 ->
-  // 14.87 and 16.57 -> 15.16, down 10.41 -> 9.24 and 10.39 -> 9.36).
-  const uint32_t a4_off = (uint32_t)(((int64_t)min(c16 >> 2, (int)M - 1) * K + g0 * kGroup +
-                                      32 * g4 + 8 * (lane & 3)) * 2);
-  const int a4_src = ((lane & 48) | (4 * (c16 & 3))) * 4;    // byte address of piece 0's lane
+  // holds (4 tokens x 4 pieces) are loaded once, lane r + 4q of the row
+  // taking token r's piece q (tokens past M repeat token M - 1), and row
+  // r < 4 takes piece j from lane r + 4j with a DPP row shift: one
+  // activation load per group instead of four, and the ring of 4 then pays.
+  // Five to eight tokens (A8): lane r < 8 loads pieces 0 and 1 of token r,
+  // lane r + 8 pieces 2 and 3, and row r takes those two from lane r + 8:
+  // two loads instead of four.  Llama-3-8B, us at 2 / 4 / 6 / 8 tokens:
+  // qkv 6.48 / 6.45 / 7.22 / 7.35 -> 5.82 / 6.06 / 6.08 / 6.32, down 9.56 /
+  // 10.62 / 10.68 / 13.04 -> 8.60 / 9.04 / 10.44 / 10.98 (the gather by
+  // ds_bpermute it replaces was 0.3-0.6 us slower at 2 and 4 tokens).
+  const uint32_t a4_off = (uint32_t)(((int64_t)min(c16 & 3, (int)M - 1) * K + g0 * kGroup +
+                                      32 * g4 + 8 * (c16 >> 2)) * 2);
+  const uint32_t a8_off = (uint32_t)(((int64_t)min(c16 & 7, (int)M - 1) * K + g0 * kGroup +
+                                      32 * g4 + 16 * (c16 >> 3)) * 2);
   // Loads of local group gl.  Past the wave's last group the offset points
   // outside the buffer: the load returns zeros without a memory access.
   auto load = [&](GroupLoads<NB, MB>& L, int gl) {
@@ -329,6 +346,9 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
       L.a[0][0] = ld16(ra, in ? a1_off + (uint32_t)gl * (kGroup * 2) : 0xFFFFFFF0u);
     } else if constexpr (A4) {
       L.a[0][0] = ld16(ra, in ? a4_off + (uint32_t)gl * (kGroup * 2) : 0xFFFFFFF0u);
+    } else if constexpr (A8) {
+      L.a[0][0] = ld16(ra, in ? a8_off + (uint32_t)gl * (kGroup * 2) : 0xFFFFFFF0u);
+      L.a[0][1] = ld16(ra, in ? a8_off + (uint32_t)gl * (kGroup * 2) + 16 : 0xFFFFFFF0u);
     } else {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -338,7 +358,7 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
     }
   };
 
-  constexpr int kRing = (A1 || A4) ? kDepthOne : kDepth;
+  constexpr int kRing = (A1 || A4 || A8) ? kDepthOne : kDepth;
   GroupLoads<NB, MB> R[kRing];
 #pragma unroll
   for (int d = 0; d < kRing; ++d) load(R[d], d);
@@ -408,12 +428,15 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
         ad[3] = row_bcast<3>(v);
       } else if constexpr (A4) {
         const uint4 v = L.a[0][0];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          ad[j] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(a4_src + 4 * j, (int)v.x),
-                             (uint32_t)__builtin_amdgcn_ds_bpermute(a4_src + 4 * j, (int)v.y),
-                             (uint32_t)__builtin_amdgcn_ds_bpermute(a4_src + 4 * j, (int)v.z),
-                             (uint32_t)__builtin_amdgcn_ds_bpermute(a4_src + 4 * j, (int)v.w));
+        ad[0] = v;
+        ad[1] = row_shl<4>(v);
+        ad[2] = row_shl<8>(v);
+        ad[3] = row_shl<12>(v);
+      } else if constexpr (A8) {
+        ad[0] = L.a[0][0];
+        ad[1] = L.a[0][1];
+        ad[2] = row_shl<8>(L.a[0][0]);
+        ad[3] = row_shl<8>(L.a[0][1]);
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) ad[j] = L.a[mb][j];
@@ -676,9 +699,10 @@ hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* 
           decode_gemm_kernel<nbv, 1, false, true, META, wv, true><<<grid, threads, 0, stream>>>(p);
         return;
       }
-      // Two to four tokens: one load and a gather, with metadata tiles only
-      // (with the LDS table it was slower on gate_up at 2 and 4 tokens:
-      // 16.4 -> 18.6 and 16.6 -> 19.0 us).
+      // Two to eight tokens: one or two loads and row shifts, with metadata
+      // tiles only (with the LDS table, the few-token form, then a gather by
+      // ds_bpermute, was slower on gate_up at 2 and 4 tokens: 16.4 -> 18.6
+      // and 16.6 -> 19.0 us).
       if constexpr (META == kMetaTiles) {
         if (M <= 4) {
           if (int3_dense)
@@ -686,6 +710,15 @@ hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* 
                 <<<grid, threads, 0, stream>>>(p);
           else
             decode_gemm_kernel<nbv, 1, false, true, META, wv, false, true>
+                <<<grid, threads, 0, stream>>>(p);
+          return;
+        }
+        if (M <= 8) {
+          if (int3_dense)
+            decode_gemm_kernel<nbv, 1, true, true, META, wv, false, false, true>
+                <<<grid, threads, 0, stream>>>(p);
+          else
+            decode_gemm_kernel<nbv, 1, false, true, META, wv, false, false, true>
                 <<<grid, threads, 0, stream>>>(p);
           return;
         }
