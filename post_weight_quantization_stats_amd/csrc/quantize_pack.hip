@@ -4,14 +4,18 @@
 // "Hyperparameters": 4 or 3 bits; builderai AWQ page, "About": the real
 // integer weights are written).
 //
-// Layout: 8 lanes own one 128-channel group, 16 channels (32 B of bf16) per
-// lane, so a wave covers 8 groups = 2 KiB of one row.  A block of 256 lanes
-// spans 32 groups and walks rows kRows at a time in a grid-stride loop; each
-// lane loads its 16 scale factors once.  Group min/max is reduced with three DPP steps inside each 8-lane
-// segment (quad swaps, then the half-row mirror); each lane writes two u32 of
-// packed nibbles.  Every arithmetic step is one IEEE fp32 operation, in the
-// order of the contract: ws = w*s; step = (max(mx,0) - min(mn,0)) / qmax
-// (1 if 0); z = clamp(rint(-mn/step)); q = clamp(rint(ws/step) + z).
+// Layout: a block of 256 lanes owns 32 groups (4096 channels) of a row, in
+// two halves of 2048 channels; lane l holds channels 8l .. 8l+7 of each
+// half, so every load and store instruction of a wave covers one contiguous
+// span (two 16-byte pieces 16 bytes apart per lane, the previous layout, ran
+// about 10% slower in a plain copy of the same bytes).  The 16 lanes of a
+// DPP row hold one group per half; its min/max is reduced in four DPP steps
+// (quad swaps, half-row mirror, row mirror) on the values' bit patterns.
+// Rows run in a grid-stride loop, kRows at a time, the next rows' loads
+// issued before the current ones are quantized.  Every arithmetic step is one
+// IEEE fp32 operation, in the order of the contract: ws = w*s;
+// step = (max(mx,0) - min(mn,0)) / qmax (1 if 0); z = clamp(rint(-mn/step));
+// q = clamp(rint(ws/step) + z).
 //
 // The quotients must be the correctly rounded ones (the codes are their rint).
 // With y = RN(1/b), q0 = RN(a*y) and the exact residual r = a - b*q0 (one
@@ -24,7 +28,11 @@
 // above the subnormal range, and for |a| < step/2 both quotients round to a
 // code of 0 (checked exhaustively for the constant divisors 15 and 7 and on
 // 2e8 random (a, step) pairs).  Other groups (zero, tiny, huge or non-finite
-// ranges) take plain IEEE divisions.
+// ranges) take plain IEEE divisions.  y = RN(1/step) is the hardware
+// reciprocal refined by one Newton step with a fused residual; that equals
+// the IEEE quotient 1/b for every binary32 b with exponent -100 .. 100
+// (checked exhaustively on the device, 1.69e9 values), which holds every
+// step of the fast path.
 #include <math.h>
 
 #include <algorithm>
@@ -37,13 +45,33 @@ namespace awq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLanesPerGroup = 8;
-constexpr int kGroupsPerBlock = kThreads / kLanesPerGroup;
+constexpr int kLanesPerGroup = 16;
+constexpr int kGroupsPerBlock = 32;
+constexpr int kHalfGroups = kGroupsPerBlock / 2;
 constexpr int kRows = 4;
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t row_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t voff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+// RN(1 / b) for b with exponent -100 .. 100: the hardware reciprocal and one
+// Newton step with a fused residual (equal to the IEEE quotient there).
+__device__ __forceinline__ float rcp_rn(float b) {
+  const float y0 = __builtin_amdgcn_rcpf(b);
+  return fmaf(fmaf(-b, y0, 1.0f), y0, y0);
 }
 
 __device__ __forceinline__ float markstein_div(float a, float b, float y) {
@@ -52,30 +80,40 @@ __device__ __forceinline__ float markstein_div(float a, float b, float y) {
   return fmaf(r, y, q0);                        // RN(a / b)
 }
 
-// One lane's 16 channels of a group: their codes (as floats) and the group's
-// step and zero (identical in all 8 lanes of the group).  kCentred: q[j] holds
-// the centred code q - z instead, formed as clamp(rint(ws/step), -z, qmax - z)
-// (equal to clamp(rint(ws/step) + z, 0, qmax) - z: every value is a small
-// integer), one median instead of an add, a clamp and a subtract.
+// One lane's 8 channels of a group: their codes (as floats) and the group's
+// step and zero (identical in all 16 lanes of the group).  kCentred: q[j]
+// holds the centred code q - z instead, formed as clamp(rint(ws/step), -z,
+// qmax - z) (equal to clamp(rint(ws/step) + z, 0, qmax) - z: every value is a
+// small integer), one median instead of an add, a clamp and a subtract.
 template <int BITS, bool kHalf = false, bool kCentred = false>
-__device__ __forceinline__ void quantize16(const float (&ws)[16], float (&q)[16],
-                                           float& step_out, float& z_out) {
+__device__ __forceinline__ void quantize8(const float (&ws)[8], float (&q)[8],
+                                          float& step_out, float& z_out) {
   constexpr float qmax = (float)((1 << BITS) - 1);
   constexpr float inv_qmax = 1.0f / qmax;       // RN(1/qmax), folded by the compiler
-  float mx = fmaxf(ws[0], ws[1]), mn = fminf(ws[0], ws[1]);
+  // max(0, max ws) and min(0, min ws) on the bit patterns (finite inputs):
+  // as signed integers, non-negative floats order like their values and
+  // every negative float is below 0; as unsigned integers, negative floats
+  // order by magnitude above every non-negative one.  So the signed max
+  // with 0 is max(0, max ws), and the unsigned max is the most negative
+  // member (or a non-negative value, which the signed min with 0 turns into
+  // +0).  Integer max needs no canonicalisation and folds into the DPP moves.
+  int32_t mxi = 0;
+  uint32_t mnu = 0u;
 #pragma unroll
-  for (int j = 2; j < 16; ++j) {
-    mx = fmaxf(mx, ws[j]);
-    mn = fminf(mn, ws[j]);
+  for (int j = 0; j < 8; ++j) {
+    mxi = max(mxi, (int32_t)__float_as_uint(ws[j]));
+    mnu = max(mnu, __float_as_uint(ws[j]));
   }
-  mx = fmaxf(mx, dpp<0xB1>(mx));                // lanes ^1
-  mn = fminf(mn, dpp<0xB1>(mn));
-  mx = fmaxf(mx, dpp<0x4E>(mx));                // lanes ^2
-  mn = fminf(mn, dpp<0x4E>(mn));
-  mx = fmaxf(mx, dpp<0x141>(mx));               // lane i <-> 7-i of each half row
-  mn = fminf(mn, dpp<0x141>(mn));
-  mx = fmaxf(mx, 0.f);
-  mn = fminf(mn, 0.f);
+  mxi = max(mxi, (int32_t)dpp<0xB1>((uint32_t)mxi));    // lanes ^1
+  mnu = max(mnu, dpp<0xB1>(mnu));
+  mxi = max(mxi, (int32_t)dpp<0x4E>((uint32_t)mxi));    // lanes ^2
+  mnu = max(mnu, dpp<0x4E>(mnu));
+  mxi = max(mxi, (int32_t)dpp<0x141>((uint32_t)mxi));   // lane i <-> 7-i of each half row
+  mnu = max(mnu, dpp<0x141>(mnu));
+  mxi = max(mxi, (int32_t)dpp<0x140>((uint32_t)mxi));   // lane i <-> 15-i of the row
+  mnu = max(mnu, dpp<0x140>(mnu));
+  const float mx = __int_as_float(mxi);
+  const float mn = __int_as_float(min((int32_t)mnu, 0));
   const float range = mx - mn;
   const bool fast = range >= 0x1p-90f && range <= 0x1p100f;
 
@@ -88,32 +126,32 @@ __device__ __forceinline__ void quantize16(const float (&ws)[16], float (&q)[16]
     float step = fast ? markstein_div(range, qmax, inv_qmax) : range / qmax;
     if (!(step > 0.f)) step = 1.f;
     step = (float)(_Float16)fminf(fmaxf(step, 0x1p-24f), 65504.f);
-    const float y = 1.0f / step;
+    const float y = rcp_rn(step);
     float zq = markstein_div(-mn, step, y);
-    float qt[16];
+    float qt[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) qt[j] = markstein_div(ws[j], step, y);
+    for (int j = 0; j < 8; ++j) qt[j] = markstein_div(ws[j], step, y);
     if (__builtin_expect(!fast, 0)) {
       asm volatile("" ::: "memory");
       zq = -mn / step;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) qt[j] = ws[j] / step;
+      for (int j = 0; j < 8; ++j) qt[j] = ws[j] / step;
     }
     static_assert(!kCentred, "the compact format writes codes");
     const float z = fminf(fmaxf(rintf(zq), 0.f), qmax);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) q[j] = fminf(fmaxf(rintf(qt[j]) + z, 0.f), qmax);
+    for (int j = 0; j < 8; ++j) q[j] = fminf(fmaxf(rintf(qt[j]) + z, 0.f), qmax);
     step_out = step;
     z_out = z;
     return;
   }
 
   float step = markstein_div(range, qmax, inv_qmax);
-  float y = 1.0f / step;
+  float y = rcp_rn(step);
   float zq = markstein_div(-mn, step, y);
-  float qt[16];
+  float qt[8];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) qt[j] = markstein_div(ws[j], step, y);
+  for (int j = 0; j < 8; ++j) qt[j] = markstein_div(ws[j], step, y);
   if (__builtin_expect(!fast, 0)) {
     // Outside the proven range: plain correctly rounded divides.  The empty
     // asm keeps this a real branch (no speculated divides on the fast path).
@@ -122,16 +160,16 @@ __device__ __forceinline__ void quantize16(const float (&ws)[16], float (&q)[16]
     if (!(step > 0.f)) step = 1.f;
     zq = -mn / step;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) qt[j] = ws[j] / step;
+    for (int j = 0; j < 8; ++j) qt[j] = ws[j] / step;
   }
   const float z = fminf(fmaxf(rintf(zq), 0.f), qmax);
   if constexpr (kCentred) {
     const float lo = -z, hi = qmax - z;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) q[j] = __builtin_amdgcn_fmed3f(rintf(qt[j]), lo, hi);
+    for (int j = 0; j < 8; ++j) q[j] = __builtin_amdgcn_fmed3f(rintf(qt[j]), lo, hi);
   } else {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) q[j] = fminf(fmaxf(rintf(qt[j]) + z, 0.f), qmax);
+    for (int j = 0; j < 8; ++j) q[j] = fminf(fmaxf(rintf(qt[j]) + z, 0.f), qmax);
   }
   step_out = step;
   z_out = z;
@@ -139,11 +177,19 @@ __device__ __forceinline__ void quantize16(const float (&ws)[16], float (&q)[16]
 
 // Eight codes -> one u32 (code j at bits 4j).  Codes are small integers, so
 // a pair packs exactly as lo + 16*hi into one byte with v_cvt_pk_u8_f32.
-__device__ __forceinline__ uint32_t pack8(const float* q) {
+__device__ __forceinline__ uint32_t pack8(const float (&q)[8]) {
   uint32_t w = 0u;
 #pragma unroll
   for (int b = 0; b < 4; ++b) w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[2 * b + 1], 16.f, q[2 * b]), b, w);
   return w;
+}
+
+// Eight 3-bit codes (as floats) -> the 24-bit value sum q_i << 3i.
+__device__ __forceinline__ uint32_t pack24(const float (&q)[8]) {
+  uint32_t c = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c |= (uint32_t)q[i] << (3 * i);
+  return c;
 }
 
 // Output modes.  kPack: packed codes, steps and zeros.  kOperand: the
@@ -163,26 +209,6 @@ enum QuantMode { kPack = 0, kOperand = 1, kDiff = 2, kDiffOp = 3, kPack3 = 4 };
 // Modes that write codes (the rest write a dequantized operand).
 constexpr bool writes_codes(int mode) { return mode == kPack || mode == kPack3; }
 
-// Sixteen 3-bit codes (as floats) -> the 48-bit value sum q_i << 3i, split
-// into bits 0..31 and 32..47.
-__device__ __forceinline__ void pack48(const float (&q)[16], uint32_t& lo, uint32_t& hi) {
-  lo = 0;
-  hi = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t c = (uint32_t)q[i];
-    const int b = 3 * i;
-    if (b + 3 <= 32) {
-      lo |= c << b;
-    } else if (b >= 32) {
-      hi |= c << (b - 32);
-    } else {
-      lo |= c << b;
-      hi |= c >> (32 - b);
-    }
-  }
-}
-
 // kHalf (code modes only): the compact format, binary16 steps in steps16
 // [N][G] and zeros two per byte in zeros [N][ceil(G/2)] (even group in the
 // low nibble; the high nibble past the last group is 0).
@@ -194,159 +220,166 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     uint16_t* __restrict__ bout, float* __restrict__ dout, uint16_t* __restrict__ steps16) {
   static_assert(!kHalf || writes_codes(kMode), "the compact format is a code mode");
   const int64_t G = K / kGroup;
-  const int64_t g = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x / kLanesPerGroup);
-  const int t8 = threadIdx.x % kLanesPerGroup;
-  const bool gvalid = g < G;
-  const int64_t k0 = (gvalid ? g : 0) * kGroup + t8 * 16;
-
-  auto load16 = [&](const float* row, float (&v)[16]) {
+  const int lane = threadIdx.x;
+  const int j16 = lane % kLanesPerGroup;        // position inside the group
+  // Half h: group g[h], the lane's channels k[h] .. k[h] + 7 (an invalid
+  // group past G reads the last group's channels and stores nothing).
+  int64_t g[2], k[2];
+  bool gvalid[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float4 t = *(const float4*)(row + k0 + 4 * c);
-      v[4 * c] = t.x; v[4 * c + 1] = t.y; v[4 * c + 2] = t.z; v[4 * c + 3] = t.w;
-    }
+  for (int h = 0; h < 2; ++h) {
+    g[h] = (int64_t)blockIdx.x * kGroupsPerBlock + h * kHalfGroups + lane / kLanesPerGroup;
+    gvalid[h] = g[h] < G;
+    k[h] = (gvalid[h] ? g[h] : G - 1) * kGroup + 8 * j16;
+  }
+
+  auto load8 = [&](const float* row, float (&v)[2][8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float4 t = *(const float4*)(row + k[h] + 4 * c);
+        v[h][4 * c] = t.x; v[h][4 * c + 1] = t.y; v[h][4 * c + 2] = t.z; v[h][4 * c + 3] = t.w;
+      }
   };
-  float sv[16], iv[16];
+  float sv[2][8], iv[2][8];
   const float* srow = s;
   if (s != nullptr && s_sel != nullptr) srow = s + (int64_t)max(*s_sel, 0) * K;
-  if (srow != nullptr) load16(srow, sv);
+  if (srow != nullptr) load8(srow, sv);
   if constexpr (!writes_codes(kMode)) {
     // No inverse scale: a factor of 1, which every multiply keeps exactly,
     // so the loop below multiplies unconditionally (no per-element select).
     if (inv_s != nullptr) {
-      load16(inv_s, iv);
+      load8(inv_s, iv);
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) iv[j] = 1.0f;
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) iv[h][j] = 1.0f;
     }
   }
 
-  // Rows in a grid-stride loop: each block takes kRows rows at a time and
-  // issues the loads of its next kRows before quantizing the current ones,
-  // so the memory pipe stays busy through the arithmetic (a block that loads,
-  // then computes, then stores leaves it idle for much of its life).
-  auto load_rows = [&](uint4 (&v)[kRows][2], int64_t nb) {
+  // Row indices are 32-bit (N < 2^31) and uniform, so each row's base lives
+  // in scalar registers (one buffer resource per row) and the lane's offsets
+  // in the row are fixed: no per-row vector address arithmetic, whose
+  // temporaries would otherwise share registers with loads in flight and
+  // make the wave wait for its own prefetch.  Rows past N re-read row N - 1
+  // (never stored).
+  const uint32_t n_last = (uint32_t)N - 1u;
+  const uint32_t off0 = (uint32_t)(k[0] * 2), off1 = (uint32_t)(k[1] * 2);
+  auto load_rows = [&](uint4 (&v)[kRows][2], uint32_t nb) {
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-      const int64_t n = nb + r;
-      const bool ok = gvalid && n < N;
-      const uint16_t* src = w + (ok ? n : 0) * K + k0;
-      v[r][0] = ok ? load_stream16(src) : make_uint4(0, 0, 0, 0);
-      v[r][1] = ok ? load_stream16(src + 8) : make_uint4(0, 0, 0, 0);
+      const uint32_t n = min(nb + (uint32_t)r, n_last);
+      const rsrc_t rw = row_rsrc(w + (int64_t)n * K, K * 2);
+      v[r][0] = ld16(rw, off0);
+      v[r][1] = ld16(rw, off1);
     }
   };
-  auto process_rows = [&](const uint4 (&v)[kRows][2], int64_t n_begin) {
+  auto process_rows = [&](const uint4 (&v)[kRows][2], uint32_t n_begin) {
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-      const int64_t n = n_begin + r;
-      float ws[16];
+      const int64_t n = (int64_t)n_begin + r;
+      const bool row_ok = n_begin + (uint32_t)r < (uint32_t)N;   // scalar compare
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        ws[8 * c + 0] = bf16_lo(v[r][c].x); ws[8 * c + 1] = bf16_hi(v[r][c].x);
-        ws[8 * c + 2] = bf16_lo(v[r][c].y); ws[8 * c + 3] = bf16_hi(v[r][c].y);
-        ws[8 * c + 4] = bf16_lo(v[r][c].z); ws[8 * c + 5] = bf16_hi(v[r][c].z);
-        ws[8 * c + 6] = bf16_lo(v[r][c].w); ws[8 * c + 7] = bf16_hi(v[r][c].w);
-      }
-      float wv[16];
+      for (int h = 0; h < 2; ++h) {
+        float ws[8];
+        ws[0] = bf16_lo(v[r][h].x); ws[1] = bf16_hi(v[r][h].x);
+        ws[2] = bf16_lo(v[r][h].y); ws[3] = bf16_hi(v[r][h].y);
+        ws[4] = bf16_lo(v[r][h].z); ws[5] = bf16_hi(v[r][h].z);
+        ws[6] = bf16_lo(v[r][h].w); ws[7] = bf16_hi(v[r][h].w);
+        float wv[8];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) wv[j] = ws[j];
-      if (srow != nullptr) {
+        for (int j = 0; j < 8; ++j) wv[j] = ws[j];
+        if (srow != nullptr) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) ws[j] *= sv[j];
-      }
-      float q[16], step, z;
-      quantize16<BITS, kHalf, !writes_codes(kMode)>(ws, q, step, z);
-      // The zero of the neighbouring group (lanes ^ 8: same row, group g ^ 1).
-      uint32_t z_next = 0u;
-      if constexpr (kHalf) z_next = (uint32_t)__shfl_xor((int)z, kLanesPerGroup);
-      uint32_t p_lo = 0, p_hi = 0, o_lo = 0, o_hi = 0;
-      if constexpr (kMode == kPack3) {
-        // Lanes 2m and 2m+1 hold the two halves of one 32-code run; the even
-        // lane takes its neighbour's 48 bits (quad_perm [1,0,3,2]) and writes
-        // the run's three words.  Both lanes of a pair are active or inactive
-        // together (same group and row).
-        pack48(q, p_lo, p_hi);
-        o_lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p_lo, 0xB1, 0xF, 0xF, false);
-        o_hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p_hi, 0xB1, 0xF, 0xF, false);
-      }
-      if (!(gvalid && n < N)) continue;
-      if constexpr (!writes_codes(kMode)) {
-        float bv[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          bv[j] = q[j] * step * iv[j];                // q holds q - z: two roundings
+          for (int j = 0; j < 8; ++j) ws[j] *= sv[h][j];
         }
-        uint32_t d[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) d[j] = pack_bf16x2(bv[2 * j], bv[2 * j + 1]);
-        if constexpr (kMode == kOperand) {
-          uint4* dst = (uint4*)(bout + n * K + k0);
-          dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
-          dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
-        } else if constexpr (kMode == kDiffOp) {
-          uint32_t e[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            e[j] = pack_bf16x2(bf16_lo(d[j]) - wv[2 * j], bf16_hi(d[j]) - wv[2 * j + 1]);
-          uint4* dst = (uint4*)(bout + n * K + k0);
-          dst[0] = make_uint4(e[0], e[1], e[2], e[3]);
-          dst[1] = make_uint4(e[4], e[5], e[6], e[7]);
-        } else {
-          static_assert(kMode == kDiff, "unhandled operand mode");
-          float dd[16];
-          uint32_t e[8];
+        float q[8], step, z;
+        quantize8<BITS, kHalf, !writes_codes(kMode)>(ws, q, step, z);
+        // The zero of the neighbouring group (lanes ^ 16: same row and half,
+        // group g ^ 1).
+        uint32_t z_next = 0u;
+        if constexpr (kHalf) z_next = (uint32_t)__shfl_xor((int)z, kLanesPerGroup);
+        // Dense INT3: lanes 4m .. 4m+3 of a row hold one run of 32 codes,
+        // 24 bits each; lane 4m+i (i < 3) writes the run's word i from its
+        // own bits and its right neighbour's (quad_perm [1,2,3,3]).
+        uint32_t c24 = 0u, c24_next = 0u;
+        if constexpr (kMode == kPack3) {
+          c24 = pack24(q);
+          c24_next = dpp<0xF9>(c24);
+        }
+        if (!(gvalid[h] && row_ok)) continue;
+        if constexpr (!writes_codes(kMode)) {
+          float bv[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            dd[2 * j] = bf16_lo(d[j]) - wv[2 * j];
-            dd[2 * j + 1] = bf16_hi(d[j]) - wv[2 * j + 1];
-            e[j] = pack_bf16x2(dd[2 * j], dd[2 * j + 1]);
+            bv[j] = q[j] * step * iv[h][j];           // q holds q - z: two roundings
           }
-          float4* df = (float4*)(dout + n * K + k0);
+          uint32_t d[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            df[c] = make_float4(dd[4 * c], dd[4 * c + 1], dd[4 * c + 2], dd[4 * c + 3]);
-          uint16_t* arow = bout + n * 2 * K;
-          const uint4 e0 = make_uint4(e[0], e[1], e[2], e[3]);
-          const uint4 e1 = make_uint4(e[4], e[5], e[6], e[7]);
-          ((uint4*)(arow + k0))[0] = e0;
-          ((uint4*)(arow + k0))[1] = e1;
-          ((uint4*)(arow + K + k0))[0] = e0;
-          ((uint4*)(arow + K + k0))[1] = e1;
-        }
-      } else {
-        static_assert(writes_codes(kMode), "unhandled code mode");
-        if constexpr (kMode == kPack3) {
-          if ((t8 & 1) == 0) {
-            uint32_t* dst = qweight + n * (3 * K / 32) + (k0 / 32) * 3;
-            dst[0] = p_lo;
-            dst[1] = p_hi | (o_lo << 16);
-            dst[2] = (o_lo >> 16) | (o_hi << 16);
+          for (int j = 0; j < 4; ++j) d[j] = pack_bf16x2(bv[2 * j], bv[2 * j + 1]);
+          if constexpr (kMode == kOperand) {
+            *(uint4*)(bout + n * K + k[h]) = make_uint4(d[0], d[1], d[2], d[3]);
+          } else if constexpr (kMode == kDiffOp) {
+            uint32_t e[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              e[j] = pack_bf16x2(bf16_lo(d[j]) - wv[2 * j], bf16_hi(d[j]) - wv[2 * j + 1]);
+            *(uint4*)(bout + n * K + k[h]) = make_uint4(e[0], e[1], e[2], e[3]);
+          } else {
+            static_assert(kMode == kDiff, "unhandled operand mode");
+            float dd[8];
+            uint32_t e[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              dd[2 * j] = bf16_lo(d[j]) - wv[2 * j];
+              dd[2 * j + 1] = bf16_hi(d[j]) - wv[2 * j + 1];
+              e[j] = pack_bf16x2(dd[2 * j], dd[2 * j + 1]);
+            }
+            float4* df = (float4*)(dout + n * K + k[h]);
+            df[0] = make_float4(dd[0], dd[1], dd[2], dd[3]);
+            df[1] = make_float4(dd[4], dd[5], dd[6], dd[7]);
+            uint16_t* arow = bout + n * 2 * K;
+            const uint4 ev = make_uint4(e[0], e[1], e[2], e[3]);
+            *(uint4*)(arow + k[h]) = ev;
+            *(uint4*)(arow + K + k[h]) = ev;
           }
         } else {
-          *(uint2*)(qweight + n * (K / 8) + k0 / 8) = make_uint2(pack8(q), pack8(q + 8));
-        }
-        if (t8 == 0) {
-          if constexpr (kHalf) {
-            steps16[n * G + g] = __builtin_bit_cast(uint16_t, (_Float16)step);   // exact
-            if ((g & 1) == 0)
-              zeros[n * ((G + 1) / 2) + g / 2] = (uint8_t)((uint32_t)z | (g + 1 < G ? z_next << 4 : 0u));
+          static_assert(writes_codes(kMode), "unhandled code mode");
+          if constexpr (kMode == kPack3) {
+            const int i = j16 & 3;
+            if (i < 3)
+              qweight[n * (3 * K / 32) + (k[h] / 32) * 3 + i] =
+                  (c24 >> (8 * i)) | (c24_next << (24 - 8 * i));
           } else {
-            scales[n * G + g] = step;
-            zeros[n * G + g] = (uint8_t)z;
+            qweight[n * (K / 8) + k[h] / 8] = pack8(q);
+          }
+          if (j16 == 0) {
+            const int64_t gh = g[h];
+            if constexpr (kHalf) {
+              steps16[n * G + gh] = __builtin_bit_cast(uint16_t, (_Float16)step);   // exact
+              if ((gh & 1) == 0)
+                zeros[n * ((G + 1) / 2) + gh / 2] =
+                    (uint8_t)((uint32_t)z | (gh + 1 < G ? z_next << 4 : 0u));
+            } else {
+              scales[n * G + gh] = step;
+              zeros[n * G + gh] = (uint8_t)z;
+            }
           }
         }
       }
     }
   };
-  const int64_t stride = (int64_t)gridDim.y * kRows;
-  int64_t nb = (int64_t)blockIdx.y * kRows;
+  const uint32_t stride = gridDim.y * kRows, n_rows = (uint32_t)N;
+  uint32_t nb = blockIdx.y * kRows;
   uint4 va[kRows][2], vb[kRows][2];
   load_rows(va, nb);
-  while (nb < N) {                       // uniform across the block
+  while (nb < n_rows) {                  // uniform across the block
     load_rows(vb, nb + stride);
     process_rows(va, nb);
     nb += stride;
-    if (nb >= N) break;
+    if (nb >= n_rows) break;
     load_rows(va, nb + stride);
     process_rows(vb, nb);
     nb += stride;
