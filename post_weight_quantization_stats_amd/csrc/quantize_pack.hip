@@ -57,8 +57,10 @@ __device__ __forceinline__ rsrc_t row_rsrc(const void* base, int64_t bytes) {
                                            0x00020000);
 }
 
+// 16 bytes at voff; kAux 2: non-temporal.
+template <int kAux>
 __device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t voff) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kAux);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -265,6 +267,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   // temporaries would otherwise share registers with loads in flight and
   // make the wave wait for its own prefetch.  Rows past N re-read row N - 1
   // (never stored).
+  // Non-temporal loads where the weight is only read (the code modes: pack
+  // 230 -> 208 us on the 57344 x 8192 weight); the operand modes, which
+  // write as much as they read, were 1-2% slower with them.
+  constexpr int kLoadAux = writes_codes(kMode) ? 2 : 0;
   const uint32_t n_last = (uint32_t)N - 1u;
   const uint32_t off0 = (uint32_t)(k[0] * 2), off1 = (uint32_t)(k[1] * 2);
   auto load_rows = [&](uint4 (&v)[kRows][2], uint32_t nb) {
@@ -272,8 +278,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     for (int r = 0; r < kRows; ++r) {
       const uint32_t n = min(nb + (uint32_t)r, n_last);
       const rsrc_t rw = row_rsrc(w + (int64_t)n * K, K * 2);
-      v[r][0] = ld16(rw, off0);
-      v[r][1] = ld16(rw, off1);
+      v[r][0] = ld16<kLoadAux>(rw, off0);
+      v[r][1] = ld16<kLoadAux>(rw, off1);
     }
   };
   auto process_rows = [&](const uint4 (&v)[kRows][2], uint32_t n_begin) {
@@ -400,10 +406,13 @@ __global__ __launch_bounds__(256) void expand_meta16_kernel(const uint16_t* __re
 }
 
 // Blocks along K cover kGroupsPerBlock groups each; along N, enough row
-// slots for about eight blocks per CU (the rest is the grid-stride loop).
+// slots for about sixteen blocks per CU (the rest is the grid-stride loop).
+// On the 57344 x 8192 weight this grid beat half of it by 1-2% (difference
+// operand 355 -> 350 us); a quarter and a double of the rows per step were
+// slower (kRows 2: pack 230 -> 240 us; kRows 8: difference 355 -> 372 us).
 dim3 quant_grid(int64_t N, int64_t K) {
   const int64_t gx = ceil_div(K / kGroup, (int64_t)kGroupsPerBlock);
-  const int64_t gy = std::min(ceil_div(N, (int64_t)kRows), std::max((int64_t)1, (int64_t)2048 / gx));
+  const int64_t gy = std::min(ceil_div(N, (int64_t)kRows), std::max((int64_t)1, (int64_t)4096 / gx));
   return dim3((unsigned)gx, (unsigned)gy);
 }
 
