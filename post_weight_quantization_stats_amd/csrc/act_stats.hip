@@ -7,6 +7,8 @@
 // columns in fp64 (the partial sums of bf16 magnitudes stay exact in
 // practice), the four waves of a block are combined in a fixed order, and a
 // second kernel adds the per-block partials in a fixed order.
+#include <algorithm>
+
 #include "awq_internal.h"
 #include "device_common.h"
 
@@ -40,16 +42,13 @@ __global__ __launch_bounds__(kThreads) void act_stats_partial_kernel(
   if (col0 < K) {
     const uint16_t* p = x + col0;
     int64_t r = r_begin + wave;
-    // four rows in flight per lane
-    for (; r + 12 < r_end; r += 16) {
-      const uint4 v0 = load_stream16(p + r * K);
-      const uint4 v1 = load_stream16(p + (r + 4) * K);
-      const uint4 v2 = load_stream16(p + (r + 8) * K);
-      const uint4 v3 = load_stream16(p + (r + 12) * K);
-      acc_abs8(acc, v0);
-      acc_abs8(acc, v1);
-      acc_abs8(acc, v2);
-      acc_abs8(acc, v3);
+    // eight rows in flight per lane
+    for (; r + 28 < r_end; r += 32) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = load_stream16(p + (r + 4 * u) * K);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc_abs8(acc, v[u]);
     }
     for (; r < r_end; r += 4) acc_abs8(acc, *(const uint4*)(p + r * K));
   }
@@ -86,14 +85,16 @@ __global__ __launch_bounds__(kThreads) void act_stats_finalize_kernel(
 }  // namespace
 
 StatsPlan stats_plan(int64_t M, int64_t K) {
-  // About 512 blocks in all (two per CU), each streaming long runs of rows:
-  // measured on X 65536 x 4096, 64 row blocks of 1024 rows stream at
-  // 6.4 TB/s against 5.3 TB/s for 256 blocks of 256 rows (the short loops
-  // spend much of each wave's life ramping up and draining) and 5.3 TB/s
-  // for 32 blocks of 2048 (too few waves in flight).  At least 64 rows per
-  // block, at most 1024 row blocks.
+  // At most one block per CU (256 in all, rounded down so that no second
+  // round of blocks trails), each wave with eight rows in flight and a long
+  // run of rows.  Measured against two blocks per CU with four rows in
+  // flight: X 16384 x 8192 49.4 -> 45.1 us (5.96 TB/s), 65536 x 4096 85.7
+  // -> 83.4, 32768 x 14336 163.3 -> 142.2, 65536 x 11008 253.2 -> 217.1;
+  // rounding the count up instead (280 blocks for K = 14336) cost 24% there,
+  // and two blocks per CU with eight rows in flight 3-14%.  At least 64 rows
+  // per block, at most 1024 row blocks.
   const int64_t col_blocks = ceil_div(K, (int64_t)kColsPerBlock);
-  int64_t R = ceil_div((int64_t)512, col_blocks);
+  int64_t R = std::max((int64_t)1, (int64_t)256 / col_blocks);
   if (R > ceil_div(M, (int64_t)64)) R = ceil_div(M, (int64_t)64);
   if (R > 1024) R = 1024;
   if (R < 1) R = 1;
