@@ -360,8 +360,11 @@ def measure_ceilings(awq, dev, stream, src) -> dict:
     dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.zeros(4, dtype=torch.float32, device=dev)
     gbs = lambda nb, ms: nb / (ms * 1e-3) / 1e9
-    grids = (1024, 4096, 16384, 65536)
-    # The best grid of each kernel (it differs by kernel and part).
+    # The best grid of each kernel (it differs by kernel and part), up to one
+    # pass over the bytes (one 16-byte step per lane; the read kernel's
+    # unrolled step covers four).
+    n16 = nbytes // 16
+    grids = (1024, 4096, 16384, 65536, n16 // 1024, n16 // 256)
     t_copy, t_read, t_write = (min(event_time_ms(
         lambda: awq.ceiling_stream(mode, a, b, nbytes, g), 5, stream) for g in grids)
         for mode, a, b in ((awq.CEILING_COPY, src, dst), (awq.CEILING_READ, src, sink),

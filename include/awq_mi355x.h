@@ -454,8 +454,8 @@ awq_status awq_decode_gemm_tiled_meta(const uint16_t* a, int64_t M, int64_t N, i
  *     in practice); AWQ_CEILING_WRITE writes dst (16-byte element i gets the
  *     u32 values i, i^1, i^2, i^3 of its low 32 bits; src unused).  16 bytes
  *     per lane in a grid-stride loop over `blocks` workgroups of 256 threads
- *     (1 <= blocks <= 65536; the fastest grid differs by mode and part, so
- *     sweep it).  bytes: a positive multiple of 16; the buffers used 16-byte
+ *     (1 <= blocks <= 2^24; the fastest grid differs by mode and part, up to
+ *     one pass over the bytes, so sweep it).  bytes: a positive multiple of 16; the buffers used 16-byte
  *     aligned.
  */
 typedef enum {

@@ -734,8 +734,8 @@ awq_status awq_ceiling_stream(int32_t mode, const void* src, void* dst, size_t b
       return fail(AWQ_ERR_UNSUPPORTED, "unknown ceiling mode %d", mode);
     if (bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 40))
       return fail(AWQ_ERR_SHAPE, "bytes must be a positive multiple of 16, at most 2^40");
-    if (blocks < 1 || blocks > 65536)
-      return fail(AWQ_ERR_SHAPE, "blocks must lie in [1, 65536]");
+    if (blocks < 1 || blocks > (1 << 24))
+      return fail(AWQ_ERR_SHAPE, "blocks must lie in [1, 2^24]");
     const bool uses_src = mode != AWQ_CEILING_WRITE;
     if ((uses_src && src == nullptr) || dst == nullptr)
       return fail(AWQ_ERR_NULL, "%s", uses_src ? "src and dst are required" : "dst is required");

@@ -11,7 +11,8 @@
 //     random signs (the chip is power-limited, so the switching activity of
 //     the data sets the clock), or all zero.
 //   * stream kernels: 16 bytes per lane in a grid-stride loop over a grid the
-//     caller picks (the best grid differs by kernel, so a caller sweeps it);
+//     caller picks (the best grid differs by kernel, so a caller sweeps it,
+//     up to one pass: one step per lane);
 //     copy (one load and one store per step), read-only (non-temporal, four
 //     loads in flight) and write-only.  These were the fastest forms in a
 //     sweep of unroll depth, cache hints and grid size on 896 MiB buffers.
@@ -101,7 +102,10 @@ __global__ __launch_bounds__(kStreamThreads) void read_ceiling_kernel(const u32x
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n; i += stride) acc ^= src[i].x;
+  for (; i < n; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
   if (acc == 0x9E3779B9u) sink[0] = acc;   // practically never: keeps the loads live
 }
 

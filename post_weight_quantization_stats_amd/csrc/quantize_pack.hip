@@ -11,8 +11,10 @@
 // about 10% slower in a plain copy of the same bytes).  The 16 lanes of a
 // DPP row hold one group per half; its min/max is reduced in four DPP steps
 // (quad swaps, half-row mirror, row mirror) on the values' bit patterns.
-// Rows run in a grid-stride loop, kRows at a time, the next rows' loads
-// issued before the current ones are quantized.  Every arithmetic step is one
+// Each block takes 4 rows per step.  The operand modes launch one block per
+// step (every row read once, no loop); the code modes run a grid-stride loop
+// over about 32 blocks per CU, the next rows' loads issued before the
+// current ones are quantized.  Every arithmetic step is one
 // IEEE fp32 operation, in the order of the contract: ws = w*s;
 // step = (max(mx,0) - min(mn,0)) / qmax (1 if 0); z = clamp(rint(-mn/step));
 // q = clamp(rint(ws/step) + z).
@@ -48,7 +50,8 @@ constexpr int kThreads = 256;
 constexpr int kLanesPerGroup = 16;
 constexpr int kGroupsPerBlock = 32;
 constexpr int kHalfGroups = kGroupsPerBlock / 2;
-constexpr int kRows = 4;
+constexpr int kRowsCodes = 4;         // rows per step: the code modes
+constexpr int kRowsOperand = 4;       // the operand modes
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -210,6 +213,7 @@ __device__ __forceinline__ uint32_t pack24(const float (&q)[8]) {
 enum QuantMode { kPack = 0, kOperand = 1, kDiff = 2, kDiffOp = 3, kPack3 = 4 };
 // Modes that write codes (the rest write a dequantized operand).
 constexpr bool writes_codes(int mode) { return mode == kPack || mode == kPack3; }
+constexpr int rows_per_step(int mode) { return writes_codes(mode) ? kRowsCodes : kRowsOperand; }
 
 // kHalf (code modes only): the compact format, binary16 steps in steps16
 // [N][G] and zeros two per byte in zeros [N][ceil(G/2)] (even group in the
@@ -273,6 +277,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   constexpr int kLoadAux = writes_codes(kMode) ? 2 : 0;
   const uint32_t n_last = (uint32_t)N - 1u;
   const uint32_t off0 = (uint32_t)(k[0] * 2), off1 = (uint32_t)(k[1] * 2);
+  constexpr int kRows = rows_per_step(kMode);
   auto load_rows = [&](uint4 (&v)[kRows][2], uint32_t nb) {
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
@@ -359,7 +364,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
               qweight[n * (3 * K / 32) + (k[h] / 32) * 3 + i] =
                   (c24 >> (8 * i)) | (c24_next << (24 - 8 * i));
           } else {
-            qweight[n * (K / 8) + k[h] / 8] = pack8(q);
+            // Non-temporal: the codes are not read back here (pack 206 -> 203 us).
+            __builtin_nontemporal_store(pack8(q), qweight + n * (K / 8) + k[h] / 8);
           }
           if (j16 == 0) {
             const int64_t gh = g[h];
@@ -381,6 +387,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   uint32_t nb = blockIdx.y * kRows;
   uint4 va[kRows][2], vb[kRows][2];
   load_rows(va, nb);
+  if (stride >= n_rows) {                // one step per block: nothing to prefetch
+    // (skipping the loads of the row past the end: dequant operand 329 -> 321 us)
+    process_rows(va, nb);
+    return;
+  }
   while (nb < n_rows) {                  // uniform across the block
     load_rows(vb, nb + stride);
     process_rows(va, nb);
@@ -405,14 +416,18 @@ __global__ __launch_bounds__(256) void expand_meta16_kernel(const uint16_t* __re
   zeros[i] = (uint8_t)((zeros4[n * ((G + 1) / 2) + g / 2] >> (4 * (g & 1))) & 15);
 }
 
-// Blocks along K cover kGroupsPerBlock groups each; along N, enough row
-// slots for about sixteen blocks per CU (the rest is the grid-stride loop).
-// On the 57344 x 8192 weight this grid beat half of it by 1-2% (difference
-// operand 355 -> 350 us); a quarter and a double of the rows per step were
-// slower (kRows 2: pack 230 -> 240 us; kRows 8: difference 355 -> 372 us).
-dim3 quant_grid(int64_t N, int64_t K) {
+// Blocks along K cover kGroupsPerBlock groups each.  Along N: the operand
+// modes, which write as much as they read, one block per 4-row step (up to
+// 65535 row slots, then the grid-stride loop); the code modes enough row
+// slots for about 32 blocks per CU.  Measured on the 57344 x 8192 weight
+// (us, difference operand / pack): 8 blocks per CU 355 / 230, 16: 350 / 208,
+// 32: 341 / 206, 64: 329 / 207, one pass: 315 / 218; one pass with 1, 2 or 8
+// rows per step: 426, 347, 341 for the difference operand.
+dim3 quant_grid(int64_t N, int64_t K, int mode) {
   const int64_t gx = ceil_div(K / kGroup, (int64_t)kGroupsPerBlock);
-  const int64_t gy = std::min(ceil_div(N, (int64_t)kRows), std::max((int64_t)1, (int64_t)4096 / gx));
+  const int64_t rows = ceil_div(N, (int64_t)rows_per_step(mode));
+  const int64_t gy = writes_codes(mode) ? std::min(rows, std::max((int64_t)1, (int64_t)8192 / gx))
+                                        : std::min(rows, (int64_t)65535);
   return dim3((unsigned)gx, (unsigned)gy);
 }
 
@@ -422,7 +437,7 @@ hipError_t launch_quantize_pack16(const uint16_t* w, int64_t N, int64_t K, const
                                   int bits, bool int3_dense, uint32_t* qweight, uint16_t* steps16,
                                   uint8_t* zeros4, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  const dim3 grid = quant_grid(N, K);
+  const dim3 grid = quant_grid(N, K, kPack);
   if (int3_dense)
     quantize_kernel<3, kPack3, true><<<grid, kThreads, 0, stream>>>(
         w, N, K, s, nullptr, nullptr, qweight, nullptr, zeros4, nullptr, nullptr, steps16);
@@ -447,7 +462,7 @@ hipError_t launch_quantize_pack(const uint16_t* w, int64_t N, int64_t K, const f
                                 const int32_t* s_sel, int bits, uint32_t* qweight,
                                 float* scales, uint8_t* zeros, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  const dim3 grid = quant_grid(N, K);
+  const dim3 grid = quant_grid(N, K, kPack);
   if (bits == 4)
     quantize_kernel<4, kPack><<<grid, kThreads, 0, stream>>>(w, N, K, s, s_sel, nullptr, qweight,
                                                              scales, zeros, nullptr, nullptr, nullptr);
@@ -461,7 +476,7 @@ hipError_t launch_quantize_pack3(const uint16_t* w, int64_t N, int64_t K, const 
                                  uint32_t* qweight3, float* scales, uint8_t* zeros,
                                  hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  const dim3 grid = quant_grid(N, K);
+  const dim3 grid = quant_grid(N, K, kPack);
   quantize_kernel<3, kPack3><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, nullptr, qweight3,
                                                             scales, zeros, nullptr, nullptr, nullptr);
   return hipGetLastError();
@@ -471,7 +486,7 @@ hipError_t launch_quantize_dequant(const uint16_t* w, int64_t N, int64_t K, cons
                                    const float* inv_s, int bits, uint16_t* b_out,
                                    hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  const dim3 grid = quant_grid(N, K);
+  const dim3 grid = quant_grid(N, K, kOperand);
   if (bits == 4)
     quantize_kernel<4, kOperand><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
                                                                 nullptr, nullptr, b_out, nullptr, nullptr);
@@ -485,7 +500,7 @@ hipError_t launch_quantize_diff_operand(const uint16_t* w, int64_t N, int64_t K,
                                         const float* inv_s, int bits, uint16_t* d_out,
                                         hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  const dim3 grid = quant_grid(N, K);
+  const dim3 grid = quant_grid(N, K, kDiffOp);
   if (bits == 4)
     quantize_kernel<4, kDiffOp><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
                                                                nullptr, nullptr, d_out, nullptr, nullptr);
@@ -499,7 +514,7 @@ hipError_t launch_quantize_diff(const uint16_t* w, int64_t N, int64_t K, const f
                                 const float* inv_s, int bits, uint16_t* a_split, float* d32,
                                 hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  const dim3 grid = quant_grid(N, K);
+  const dim3 grid = quant_grid(N, K, kDiff);
   if (bits == 4)
     quantize_kernel<4, kDiff><<<grid, kThreads, 0, stream>>>(w, N, K, s, nullptr, inv_s, nullptr,
                                                              nullptr, nullptr, a_split, d32, nullptr);

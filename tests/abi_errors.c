@@ -169,6 +169,7 @@ int main(void) {
     EXPECT(awq_ceiling_stream(7, F, F, 4096, 1024, NULL), AWQ_ERR_UNSUPPORTED);
     EXPECT(awq_ceiling_stream(AWQ_CEILING_COPY, F, F, 4100, 1024, NULL), AWQ_ERR_SHAPE);
     EXPECT(awq_ceiling_stream(AWQ_CEILING_COPY, F, F, 4096, 0, NULL), AWQ_ERR_SHAPE);
+    EXPECT(awq_ceiling_stream(AWQ_CEILING_COPY, F, F, 4096, (1 << 24) + 1, NULL), AWQ_ERR_SHAPE);
     EXPECT(awq_ceiling_stream(AWQ_CEILING_READ, F, (void*)0x10002, 4096, 1024, NULL), AWQ_ERR_ALIGN);
   }
 

@@ -423,7 +423,7 @@ def test_ceiling_entry_errors():
 
     assert s(3, FAKE, FAKE, 4096) == UNSUPPORTED
     assert s(0, FAKE, FAKE, 0) == SHAPE and s(0, FAKE, FAKE, 4100) == SHAPE
-    assert s(0, FAKE, FAKE, 4096, 0) == SHAPE and s(0, FAKE, FAKE, 4096, 65537) == SHAPE
+    assert s(0, FAKE, FAKE, 4096, 0) == SHAPE and s(0, FAKE, FAKE, 4096, (1 << 24) + 1) == SHAPE
     assert s(0, None, FAKE, 4096) == NULL and s(1, None, FAKE, 4096) == NULL
     assert s(2, None, None, 4096) == NULL
     assert s(0, FAKE + 4, FAKE, 4096) == ALIGN and s(0, FAKE, FAKE + 4, 4096) == ALIGN

@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 def test_stream_ceilings_move_the_bytes():
     dev = require_gpu()
     announce("ceiling kernels: copy, read, write")
-    for nbytes, blocks in ((16, 1), (4096 + 16, 1024), ((1 << 24) + 48, 65536), ((1 << 24) + 48, 7)):
+    for nbytes, blocks in ((16, 1), (4096 + 16, 1024), ((1 << 24) + 48, 65536), ((1 << 24) + 48, 7),
+                           ((1 << 24) + 48, (1 << 22) + 3)):
         src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev)
         dst = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         awq.ceiling_stream(awq.CEILING_COPY, src, dst, nbytes, blocks)
