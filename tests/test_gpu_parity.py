@@ -199,6 +199,30 @@ def test_diff_operand_bit_exact(dev, shape, bits):
                           O.diff_operand(w, O.dequant_operand(q, z, st, 128, None)))
 
 
+def test_operands_and_pack_many_rows(dev):
+    """More rows than one pass of the operand modes' grid covers (65535 row
+    slots of 4 rows), so their grid-stride loop runs, with a ragged tail of
+    rows; the pack at the same shape.  Operands and codes bit for bit."""
+    N, K = 4 * 65535 + 7, 256
+    announce("quantize many rows", N, K)
+    rng = np.random.default_rng(17)
+    w = synth.to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    s = np.exp(rng.uniform(-0.5, 0.5, K)).astype(np.float32)
+    inv = (1.0 / s.astype(np.float64)).astype(np.float32)
+    wd = to_dev_bf16(w, dev)
+    q, z, st = O.quantize(w, s, 4, 128)
+    b_ref = O.dequant_operand(q, z, st, 128, inv)
+    b = awq.dequant_operand(wd, to_dev_f32(s, dev), to_dev_f32(inv, dev), 4)
+    assert np.array_equal(b.float().cpu().numpy().astype(np.float64), b_ref)
+    d = awq.diff_operand(wd, to_dev_f32(s, dev), to_dev_f32(inv, dev), 4)
+    assert np.array_equal(d.float().cpu().numpy().astype(np.float64), O.diff_operand(w, b_ref))
+    qw, sc, ze = awq.quantize_pack(wd, to_dev_f32(s, dev), 4)
+    rq, rs, rz = O.pack(q, z, st)
+    assert np.array_equal(u32(qw), rq)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(ze.cpu().numpy(), rz)
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=ids)
 def test_candidate_sse_difference_form(dev, shape):
     """sum (X . D^T)^2 with the difference operand: the search's loss numerator."""
