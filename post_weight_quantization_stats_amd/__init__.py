@@ -306,7 +306,9 @@ def w4a16_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zer
     layout LAYOUT_NIBBLE (default; qweight [N][K/8]) or LAYOUT_INT3_DENSE
     (bits 3, qweight [N][3K/32]).  staged=True, or the dense INT3 layout,
     runs awq_w4a16_gemm_staged (the operand dequantized once into the
-    workspace, then the bf16 matrix-core contraction; Y bit-identical);
+    workspace, then the bf16 matrix-core contraction: the same operand, Y
+    equal to the fused kernel's up to fp32 rounding of the sums, and bit for
+    bit the same for dense INT3 and the same codes in 4-bit containers);
     otherwise awq_w4a16_gemm (dequantized in LDS per tile)."""
     x = _bf16(x, "x")
     M, K = x.shape
