@@ -89,8 +89,12 @@ KERNEL_LABELS = [
     ("mfma16_kernel<false, 2>", "candidate_sse vs y_ref (bf16 operand, squared-error epilogue)"),
     ("mfma16_kernel<true, 2>", "staged W4A16 product with SSE (bf16 operand, Y and SSE)"),
     ("mfma16_kernel<true, 0>", "reference_gemm / Gram matrix / staged W4A16 (bf16, fp32 out)"),
-    ("gemm_kernel<true, true, 2, false, true", "w4a16_gemm_sse (INT4 operand, 1/s folded, SSE epilogue)"),
-    ("gemm_kernel<true", "w4a16_gemm (INT4 operand, other epilogues)"),
+    # gemm_kernel<packed, 1/s, waves/2, store Y, SSE, dot, dense INT3>
+    ("gemm_kernel<true, true, 2, false, true, false, false>",
+     "w4a16_gemm_sse (INT4 operand, 1/s folded, SSE epilogue)"),
+    ("gemm_kernel<true, true, 2, false, true, false, true>",
+     "w3a16_gemm_sse (dense INT3 operand, 1/s folded, SSE epilogue)"),
+    ("gemm_kernel<true", "w4a16_gemm / w3a16_gemm (packed operand, other epilogues)"),
     ("quantize_kernel<4, 1,", "dequant_operand (quantize -> bf16 B)"),
     ("quantize_kernel<3, 1,", "dequant_operand (quantize -> bf16 B)"),
     ("quantize_kernel<4, 2,", "Gram-form quantize (split D, fp32 D)"),
@@ -974,12 +978,21 @@ def main() -> int:
                                                     inv_s=inv_all[i_mid], y_ref=yref,
                                                     return_y=False, workspace=gemm_ws),
                              max(2, reps // 2), stream)
+        # The same fused product on dense INT3 codes (awq_w3a16_gemm).
+        qw3, sc3, ze3 = awq.quantize_pack3(wd, s_all[i_mid], spec.group)
+        t_w3 = event_time_ms(lambda: awq.w4a16_gemm(xd, qw3, sc3, ze3, 3, spec.group,
+                                                    inv_s=inv_all[i_mid], y_ref=yref,
+                                                    return_y=False, workspace=gemm_ws,
+                                                    layout=awq.LAYOUT_INT3_DENSE),
+                             max(2, reps // 2), stream)
+        del qw3, sc3, ze3
         t_ref = event_time_ms(lambda: awq.reference_gemm(xd, wd), max(2, reps // 2), stream)
         del yref, b_mid
         torch.cuda.empty_cache()
         log(f"against y_ref {t_sse_y:.3f} ms = {tf(t_sse_y):.1f} TFLOP/s; constant operands "
             f"{(t_sse_c or float('nan')):.3f} ms; hipBLASLt bf16 mm {t_mm:.3f} ms = "
-            f"{tf(t_mm):.1f} TFLOP/s; packed w4a16+sse {t_w4:.3f} ms = {tf(t_w4):.1f} TFLOP/s; "
+            f"{tf(t_mm):.1f} TFLOP/s; packed w4a16+sse {t_w4:.3f} ms = {tf(t_w4):.1f} TFLOP/s "
+            f"(dense INT3 {t_w3:.3f} ms = {tf(t_w3):.1f} TFLOP/s); "
             f"reference {t_ref:.3f} ms = {tf(t_ref):.1f} TFLOP/s")
     t_stats = event_time_ms(lambda: awq.act_stats(xd), reps, stream)
     t_quant = event_time_ms(lambda: awq.quantize_pack(wd, s_all[i_mid], bits, spec.group),
@@ -1020,6 +1033,7 @@ def main() -> int:
             "search_contraction_constant_operands": mfma_entry(t_sse_c) if t_sse_c else None,
             "vendor_bf16_gemm_same_shape": mfma_entry(t_mm),
             "w4a16_gemm_sse": mfma_entry(t_w4),
+            "w3a16_gemm_sse": mfma_entry(t_w3),
             "reference_gemm": mfma_entry(t_ref)})
     kern.update({
         "act_stats": hbm_entry(stats_bytes, t_stats, "read_gbs"),

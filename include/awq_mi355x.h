@@ -248,6 +248,24 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                           float* y, double* sse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The same fused contraction on dense INT3 codes (sourcepulse AWQ project
+ * page, opening paragraph: 3- and 4-bit weights; robotsatlas "Implementation
+ * pitfalls": dequantization stays inside the kernel).  Each k-step's 32 codes
+ * of a weight row come as one 12-byte run and are widened on chip to the
+ * 4-bit fields the dequantization reads, so for the same codes Y and sse are
+ * bit-identical to awq_w4a16_gemm on the 4-bit containers.
+ *   qweight3  u32 [N][3K/32] as from awq_quantize_pack3 (each run of 32 codes
+ *             along K one 96-bit little-endian value, code i at bits 3i),
+ *             4-byte aligned; scales/zeros f32/u8 [N][K/group]
+ *   other arguments, outputs, workspace (awq_workspace_size(AWQ_OP_W4A16_GEMM))
+ *   and the M == 0 / N == 0 rule as awq_w4a16_gemm with bits = 3
+ */
+awq_status awq_w3a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                          const uint32_t* qweight3, const float* scales, const uint8_t* zeros,
+                          int32_t group, const float* inv_s, const float* y_ref, float* y,
+                          double* sse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * The same W4A16 product for many tokens, from codes in either packed layout
  * (builderai "About": 4-bit weights with 16-bit activations; sourcepulse AWQ
  * project page, opening paragraph: 3- and 4-bit weights).  The operand

@@ -82,6 +82,9 @@ _SIGNATURES = {
     "awq_w4a16_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
                         _c_void_p], _i32),
+    "awq_w3a16_gemm": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
+                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
+                        _c_void_p], _i32),
     "awq_w4a16_gemm_staged": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
                                _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                _size_t, _c_void_p], _i32),
@@ -304,18 +307,20 @@ def w4a16_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zer
     as a float64 [1] device tensor: returns (y or None, sse).
 
     layout LAYOUT_NIBBLE (default; qweight [N][K/8]) or LAYOUT_INT3_DENSE
-    (bits 3, qweight [N][3K/32]).  staged=True, or the dense INT3 layout,
-    runs awq_w4a16_gemm_staged (the operand dequantized once into the
-    workspace, then the bf16 matrix-core contraction: the same operand, Y
-    equal to the fused kernel's up to fp32 rounding of the sums, and bit for
-    bit the same for dense INT3 and the same codes in 4-bit containers);
-    otherwise awq_w4a16_gemm (dequantized in LDS per tile)."""
+    (bits 3, qweight [N][3K/32]).  staged=True runs awq_w4a16_gemm_staged
+    (the operand dequantized once into the workspace, then the bf16
+    matrix-core contraction: the same operand, Y equal to the fused kernel's
+    up to fp32 rounding of the sums); otherwise the fused product,
+    dequantized in LDS per tile: awq_w4a16_gemm, or awq_w3a16_gemm for the
+    dense INT3 layout.  Either way dense INT3 gives the product of the same
+    codes in 4-bit containers bit for bit."""
     x = _bf16(x, "x")
     M, K = x.shape
     layout = LAYOUT_NIBBLE if layout is None else layout
-    staged = staged or layout == LAYOUT_INT3_DENSE
     N = _rows_of(qweight, "qweight")
     _packed_words(qweight, N, K, layout)
+    if layout == LAYOUT_INT3_DENSE and bits != 3:
+        raise ValueError("the dense INT3 layout holds 3-bit codes (bits=3)")
     _meta(scales, zeros, N, K, group)
     inv_s = _vec_f32(inv_s, "inv_s", K)
     if y_ref is not None:
@@ -335,10 +340,16 @@ def w4a16_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zer
         ws = None
         if y_ref is not None:
             ws = _workspace(workspace_size(OP_W4A16_GEMM, M, N, K), dev, workspace)
-        _check(lib().awq_w4a16_gemm(_ptr(x), M, N, K, _ptr(qweight), _ptr(scales), _ptr(zeros),
-                                    bits, group, _ptr(inv_s), _ptr(y_ref), _ptr(y), _ptr(sse),
-                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)),
-               "awq_w4a16_gemm")
+        nws = 0 if ws is None else ws.numel()
+        if layout == LAYOUT_INT3_DENSE:
+            _check(lib().awq_w3a16_gemm(_ptr(x), M, N, K, _ptr(qweight), _ptr(scales),
+                                        _ptr(zeros), group, _ptr(inv_s), _ptr(y_ref), _ptr(y),
+                                        _ptr(sse), _ptr(ws), nws, _stream(dev)), "awq_w3a16_gemm")
+        else:
+            _check(lib().awq_w4a16_gemm(_ptr(x), M, N, K, _ptr(qweight), _ptr(scales),
+                                        _ptr(zeros), bits, group, _ptr(inv_s), _ptr(y_ref),
+                                        _ptr(y), _ptr(sse), _ptr(ws), nws, _stream(dev)),
+                   "awq_w4a16_gemm")
     if y_ref is None:
         return y
     return y, sse

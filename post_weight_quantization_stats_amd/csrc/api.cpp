@@ -400,10 +400,14 @@ awq_status awq_reference_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K
   }
 }
 
-awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
-                          const uint32_t* qweight, const float* scales, const uint8_t* zeros,
-                          int32_t bits, int32_t group, const float* inv_s, const float* y_ref,
-                          float* y, double* sse, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// The fused W4A16 product on 4-bit containers or dense INT3 codes; the
+// entry points below differ only in the code layout.
+awq_status w4a16_fused(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint32_t* qweight,
+                       const float* scales, const uint8_t* zeros, int32_t bits, int32_t group,
+                       bool int3_dense, const float* inv_s, const float* y_ref, float* y,
+                       double* sse, void* ws, size_t ws_bytes, void* stream) {
   try {
     awq_status st = check_quant_params(bits, group);
     if (st != AWQ_OK) return st;
@@ -421,9 +425,10 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
       return fail(AWQ_ERR_NULL, "x, qweight, scales and zeros are required");
     if (y == nullptr && sse == nullptr) return fail(AWQ_ERR_NULL, "one of y and sse is required");
     if (sse != nullptr && y_ref == nullptr) return fail(AWQ_ERR_NULL, "sse needs y_ref");
-    if (misaligned(x) || misaligned(qweight) || misaligned(y) || misaligned(y_ref) ||
+    const bool q_misaligned = int3_dense ? ((uintptr_t)qweight & 3u) != 0 : misaligned(qweight);
+    if (misaligned(x) || q_misaligned || misaligned(y) || misaligned(y_ref) ||
         misaligned(inv_s) || misaligned(ws) || ((uintptr_t)scales & 3u) || ((uintptr_t)sse & 7u))
-      return fail(AWQ_ERR_ALIGN, "tensor pointers must be 16-byte aligned (scales 4, sse 8)");
+      return fail(AWQ_ERR_ALIGN, "tensor pointers must be 16-byte aligned (qweight3 and scales 4, sse 8)");
     const size_t need = awq::align_up((size_t)awq::gemm_tiles(M, N) * sizeof(double));
     if (sse != nullptr && (ws == nullptr || ws_bytes < need))
       return fail(AWQ_ERR_WORKSPACE, "w4a16_gemm with sse needs %zu workspace bytes", need);
@@ -435,6 +440,7 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
     op.qweight = qweight;
     op.scales = scales;
     op.zeros = zeros;
+    op.int3_dense = int3_dense;
     op.inv_s = inv_s;
     op.y_ref = sse != nullptr ? y_ref : nullptr;
     op.y = y;
@@ -446,6 +452,24 @@ awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
   } catch (...) {
     return fail(AWQ_ERR_LAUNCH, "internal error");
   }
+}
+
+}  // namespace
+
+awq_status awq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                          const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                          int32_t bits, int32_t group, const float* inv_s, const float* y_ref,
+                          float* y, double* sse, void* ws, size_t ws_bytes, void* stream) {
+  return w4a16_fused(x, M, N, K, qweight, scales, zeros, bits, group, false, inv_s, y_ref, y, sse,
+                     ws, ws_bytes, stream);
+}
+
+awq_status awq_w3a16_gemm(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                          const uint32_t* qweight3, const float* scales, const uint8_t* zeros,
+                          int32_t group, const float* inv_s, const float* y_ref, float* y,
+                          double* sse, void* ws, size_t ws_bytes, void* stream) {
+  return w4a16_fused(x, M, N, K, qweight3, scales, zeros, 3, group, true, inv_s, y_ref, y, sse, ws,
+                     ws_bytes, stream);
 }
 
 awq_status awq_w4a16_gemm_staged(const uint16_t* x, int64_t M, int64_t N, int64_t K,

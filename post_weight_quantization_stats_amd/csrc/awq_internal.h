@@ -111,9 +111,10 @@ struct GemmOperands {
   int64_t M, N, K;
   // exactly one of: w (bf16 [N][K]) or the packed triple
   const uint16_t* w;
-  const uint32_t* qweight;
+  const uint32_t* qweight;   // u32 [N][K/8], or with int3_dense u32 [N][3K/32]
   const float* scales;
   const uint8_t* zeros;
+  bool int3_dense;          // packed codes in the dense INT3 layout
   const float* inv_s;       // [K] or NULL
   const float* y_ref;       // [M][N] or NULL
   float* y;                 // [M][N] or NULL

@@ -172,18 +172,9 @@ __device__ __forceinline__ bf16x8 codes_b(uint32_t w, uint32_t kc) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Dense INT3 (32 codes in three u32 words, code i at bit 3i): the lane's 32
-// codes of a group come as 12 bytes; each 24-bit run of 8 codes is spread to
-// 4-bit fields (code i at bit 4i) so the 4-bit path below applies unchanged.
-__device__ __forceinline__ uint32_t spread3(uint32_t f) {
-  const uint32_t y = (f & 0xFFFu) | ((f & 0xFFF000u) << 4);   // codes 0-3 | codes 4-7 << 16
-  return (y & 0x00070007u) | ((y & 0x00380038u) << 1) | ((y & 0x01C001C0u) << 2) |
-         ((y & 0x0E000E00u) << 3);
-}
-__device__ __forceinline__ uint4 nibbles_from_int3(uint4 v) {
-  return make_uint4(spread3(v.x & 0xFFFFFFu), spread3((v.x >> 24) | ((v.y & 0xFFFFu) << 8)),
-                    spread3((v.y >> 16) | ((v.z & 0xFFu) << 16)), spread3(v.z >> 8));
-}
+// Dense INT3 (32 codes in three u32 words): the lane's 32 codes of a group
+// come as 12 bytes and are widened to 4-bit fields (nibbles_from_int3) so the
+// 4-bit path below applies unchanged.
 
 // A dense-INT3 tile piece (three words) -> the four bf16x8 operands of its
 // 32 channels in natural order: pair p as bf16 (128 + code) halves.

@@ -30,6 +30,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// Dense INT3 (each run of 32 codes along K one 96-bit little-endian value in
+// three u32 words, code i at bit 3i) widened to 4-bit fields: each 24-bit
+// run of 8 codes is spread so that code i lands at bit 4i of one u32.
+__device__ __forceinline__ uint32_t spread3(uint32_t f) {
+  const uint32_t y = (f & 0xFFFu) | ((f & 0xFFF000u) << 4);   // codes 0-3 | codes 4-7 << 16
+  return (y & 0x00070007u) | ((y & 0x00380038u) << 1) | ((y & 0x01C001C0u) << 2) |
+         ((y & 0x0E000E00u) << 3);
+}
+// The three words of one 32-code run (v.w unused) -> four words of nibbles.
+__device__ __forceinline__ uint4 nibbles_from_int3(uint4 v) {
+  return make_uint4(spread3(v.x & 0xFFFFFFu), spread3((v.x >> 24) | ((v.y & 0xFFFFu) << 8)),
+                    spread3((v.y >> 16) | ((v.z & 0xFFu) << 16)), spread3(v.z >> 8));
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -206,7 +206,11 @@ struct CodeRegs {
 
 // kStoreY: write the fp32 product; kSse: fp64 sum of (Y - Y_ref)^2 per tile,
 // or with kDot the fp64 sum of Y * Y_ref (a quadratic form's last factor).
-template <bool kInt4, bool kInvS, int WN, bool kStoreY, bool kSse, bool kDot = false>
+// kI3: the packed codes in the dense INT3 layout (32 codes of a row in three
+// u32 words per k-step), widened to the 4-bit fields the dequantization reads;
+// for the same codes Y is the same bit for bit.
+template <bool kInt4, bool kInvS, int WN, bool kStoreY, bool kSse, bool kDot = false,
+          bool kI3 = false>
 __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
                                                                     const float* __restrict__ inv_s) {
   // The body exists only in the device pass; the host pass needs just the
@@ -215,6 +219,7 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
   using C_ = Cfg<WN>;
   constexpr int NW = C_::kWaves, BJ = C_::kBJ, TN = C_::kTN, DPW = C_::kDma;
   constexpr int TPR = C_::kTPR, WPT = C_::kWPT;
+  static_assert(!kI3 || (kInt4 && WPT == 4), "dense INT3: one thread per row, a whole run per k-step");
   // Separate objects per stage: the compiler tracks LDS-DMA writes per object.
   __shared__ uint4 sa0[kSlots], sa1[kSlots], sa2[kSlots], sa3[kSlots];
   __shared__ uint4 sb0[kSlots], sb1[kSlots], sb2[kSlots], sb3[kSlots];
@@ -247,7 +252,8 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
   const rsrc_t ra = make_rsrc(p.x + m0 * K, (uint64_t)(M - m0) * K * 2);
   rsrc_t rb, rq, rsc, rz;
   if constexpr (kInt4) {
-    rq = make_rsrc(p.qweight + n0 * (K / 8), (uint64_t)(N - n0) * (K / 2));
+    rq = kI3 ? make_rsrc(p.qweight + n0 * (3 * K / 32), (uint64_t)(N - n0) * (3 * K / 8))
+             : make_rsrc(p.qweight + n0 * (K / 8), (uint64_t)(N - n0) * (K / 2));
     rsc = make_rsrc(p.scales + n0 * G, (uint64_t)(N - n0) * G * 4);
     rz = make_rsrc(p.zeros + n0 * G, (uint64_t)(N - n0) * G);
   } else {
@@ -256,7 +262,8 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
   // INT4 dequant mapping: thread t owns words [wq0, wq0 + WPT) of row brow.
   const int brow = t / TPR;
   const int wq0 = (t % TPR) * WPT;
-  const uint32_t q_off = (uint32_t)(brow * (K / 2) + wq0 * 4);
+  const uint32_t q_off = kI3 ? (uint32_t)(brow * (3 * K / 8))
+                             : (uint32_t)(brow * (K / 2) + wq0 * 4);
   const uint32_t sc_off = (uint32_t)(brow * G * 4);
   const uint32_t z_off = (uint32_t)(brow * G);
 
@@ -264,7 +271,12 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
     dma_tile_wave<DPW>(r, stage + dma_slot, dma_off, (uint32_t)(k0 * 2));
   };
   auto load_codes = [&](CodeRegs<WPT>& C, int64_t k0) {
-    if constexpr (WPT == 4) {
+    if constexpr (kI3) {
+      // The k-step's 32 codes of the row: one 12-byte run.
+      typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+      const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rq, q_off, (uint32_t)(k0 / 32 * 12), 0);
+      C.q[0] = v.x; C.q[1] = v.y; C.q[2] = v.z; C.q[3] = 0u;
+    } else if constexpr (WPT == 4) {
       const uint4 v = ld16(rq, q_off, (uint32_t)(k0 / 2));
       C.q[0] = v.x; C.q[1] = v.y; C.q[2] = v.z; C.q[3] = v.w;
     } else {
@@ -291,7 +303,11 @@ __global__ __launch_bounds__(Cfg<WN>::kThreads, 1) void gemm_kernel(Params p,
     for (int w = 0; w < WPT; ++w) U.words[w] = C.q[w];
     asm volatile("" : "+v"(sbits), "+v"(zraw));
 #pragma unroll
-    for (int w = 0; w < WPT; ++w) asm volatile("" : "+v"(U.words[w]));
+    for (int w = 0; w < (kI3 ? 3 : WPT); ++w) asm volatile("" : "+v"(U.words[w]));
+    if constexpr (kI3) {
+      const uint4 n = nibbles_from_int3(make_uint4(U.words[0], U.words[1], U.words[2], 0u));
+      U.words[0] = n.x; U.words[1] = n.y; U.words[2] = n.z; U.words[3] = n.w;
+    }
     U.step = __uint_as_float(sbits);
     U.zero = (float)zraw;
     return U;
@@ -850,20 +866,24 @@ hipError_t launch_gemm(const GemmOperands& op, hipStream_t stream) {
     else
       mfma16_kernel<true, kEpiNone><<<blocks, kThreads16, 0, stream>>>(p);
   } else {
-    auto go = [&](auto kInv) {
-      constexpr bool inv = decltype(kInv)::value;
+    auto go = [&](auto kInv, auto kI3c) {
+      constexpr bool inv = decltype(kInv)::value, i3 = decltype(kI3c)::value;
       const float* is = inv ? op.inv_s : nullptr;
       if (y && sse)
-        gemm_kernel<true, inv, 2, true, true><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, is);
+        gemm_kernel<true, inv, 2, true, true, false, i3><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, is);
       else if (sse)
-        gemm_kernel<true, inv, 2, false, true><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, is);
+        gemm_kernel<true, inv, 2, false, true, false, i3><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, is);
       else
-        gemm_kernel<true, inv, 2, true, false><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, is);
+        gemm_kernel<true, inv, 2, true, false, false, i3><<<blocks, Cfg<2>::kThreads, 0, stream>>>(p, is);
     };
-    if (op.inv_s != nullptr)
-      go(std::true_type{});
+    if (op.inv_s != nullptr && op.int3_dense)
+      go(std::true_type{}, std::true_type{});
+    else if (op.inv_s != nullptr)
+      go(std::true_type{}, std::false_type{});
+    else if (op.int3_dense)
+      go(std::false_type{}, std::true_type{});
     else
-      go(std::false_type{});
+      go(std::false_type{}, std::false_type{});
   }
   return hipGetLastError();
 }

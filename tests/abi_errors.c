@@ -112,6 +112,20 @@ int main(void) {
          AWQ_ERR_WORKSPACE);
   EXPECT(awq_w4a16_gemm(F, 4, 8, 128, F, F, F, 4, 128, FM, NULL, F, NULL, NULL, 0, NULL),
          AWQ_ERR_ALIGN);
+  EXPECT(awq_w3a16_gemm(F, 4, 8, 128, F, F, F, 128, NULL, NULL, NULL, NULL, NULL, 0, NULL),
+         AWQ_ERR_NULL);
+  EXPECT(awq_w3a16_gemm(F, 4, 8, 128, NULL, F, F, 128, NULL, NULL, F, NULL, NULL, 0, NULL),
+         AWQ_ERR_NULL);
+  EXPECT(awq_w3a16_gemm(F, 4, 8, 128, F, F, F, 128, NULL, F, NULL, F, NULL, 0, NULL),
+         AWQ_ERR_WORKSPACE);
+  EXPECT(awq_w3a16_gemm(F, 4, 8, 128, (void*)0x10002, F, F, 128, NULL, NULL, F, NULL, NULL, 0,
+                        NULL), AWQ_ERR_ALIGN);
+  EXPECT(awq_w3a16_gemm(F, 4, 8, 100, F, F, F, 128, NULL, NULL, F, NULL, NULL, 0, NULL),
+         AWQ_ERR_SHAPE);
+  EXPECT(awq_w3a16_gemm(F, 4, 8, 128, F, F, F, 64, NULL, NULL, F, NULL, NULL, 0, NULL),
+         AWQ_ERR_UNSUPPORTED);
+  EXPECT(awq_w3a16_gemm(F, 0, 8, 128, NULL, NULL, NULL, 128, NULL, NULL, NULL, NULL, NULL, 0, NULL),
+         AWQ_OK);
   EXPECT(awq_w4a16_gemm_staged(F, 4, 8, 128, F, F, F, 4, 128, 3, NULL, NULL, F, NULL, F, 1 << 20,
                                NULL), AWQ_ERR_UNSUPPORTED);
   EXPECT(awq_w4a16_gemm_staged(F, 4, 8, 128, F, F, F, 4, 128, AWQ_LAYOUT_INT3_DENSE, NULL, NULL, F,

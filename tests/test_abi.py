@@ -494,7 +494,7 @@ def _cpu(shape, dtype):
     "decode_out", "decode_scales_dtype", "decode_zeros_shape", "decode_qweight_cols",
     "decode3_words", "tiled_size", "tiled_scales", "tiled16_steps", "tiled16_zeros4",
     "meta_steps", "tiled_meta_size", "tiled_meta_tiles",
-    "w4a16_inv_s", "w4a16_y_ref", "w4a16_scales", "dequant_s", "divide_rows_s", "residual_y",
+    "w4a16_inv_s", "w4a16_y_ref", "w4a16_scales", "w3a16_bits", "w3a16_words", "dequant_s", "divide_rows_s", "residual_y",
     "rmsnorm_gamma", "tiles_qweight", "noncontiguous"])
 def test_python_wrappers_check_shapes_before_the_device(case):
     """Every wrapper checks dtype, exact shape and contiguity of each tensor
@@ -532,6 +532,10 @@ def test_python_wrappers_check_shapes_before_the_device(case):
         "w4a16_y_ref": (lambda: awq.w4a16_gemm(a, qw, sc, ze, y_ref=_cpu((M, N + 1), f32)),
                         "y_ref must"),
         "w4a16_scales": (lambda: awq.w4a16_gemm(a, qw, _cpu((N, 2), f16), ze), "scales must"),
+        "w3a16_bits": (lambda: awq.w4a16_gemm(a, _cpu((N, 3 * K // 32), i32), sc, ze, 4,
+                                              layout=awq.LAYOUT_INT3_DENSE), "holds 3-bit codes"),
+        "w3a16_words": (lambda: awq.w4a16_gemm(a, qw, sc, ze, 3, layout=awq.LAYOUT_INT3_DENSE),
+                        "qweight must"),
         "dequant_s": (lambda: awq.dequant_operand(_cpu((N, K), bf), _cpu((K + 1,), f32), None),
                       "s must"),
         "divide_rows_s": (lambda: awq.divide_rows(_cpu((N, 2), f32), _cpu((N - 1,), f32)), "s must"),
@@ -547,7 +551,9 @@ def test_python_wrappers_check_shapes_before_the_device(case):
     good = {"decode_out": lambda: awq.decode_gemm(a, qw, sc, ze, out=_cpu((M, N), f32)),
             "tiled_meta_size": lambda: awq.decode_gemm_tiled_meta(
                 a, tiles, _cpu((awq.decode_meta_size(N, K) // 4,), i32), N),
-            "tiled_size": lambda: awq.decode_gemm_tiled(a, tiles, sc, ze)}
+            "tiled_size": lambda: awq.decode_gemm_tiled(a, tiles, sc, ze),
+            "w3a16_bits": lambda: awq.w4a16_gemm(a, _cpu((N, 3 * K // 32), i32), sc, ze, 3,
+                                                 layout=awq.LAYOUT_INT3_DENSE)}
     if case in good:
         with pytest.raises(ValueError, match="GPU tensor"):
             good[case]()

@@ -86,7 +86,7 @@ def test_staged_dense_int3(dev, shape):
     wd, sd, xd = to_dev_bf16(w, dev), to_dev_f32(s, dev), to_dev_bf16(x, dev)
     qw3, sc3, ze3 = awq.quantize_pack3(wd, sd)
     qw4, sc4, ze4 = awq.quantize_pack(wd, sd, 3)
-    y3 = awq.w4a16_gemm(xd, qw3, sc3, ze3, 3, 128, layout=awq.LAYOUT_INT3_DENSE)
+    y3 = awq.w4a16_gemm(xd, qw3, sc3, ze3, 3, 128, layout=awq.LAYOUT_INT3_DENSE, staged=True)
     y4 = awq.w4a16_gemm(xd, qw4, sc4, ze4, 3, 128, staged=True)
     torch.cuda.synchronize()
     assert torch.equal(y3, y4)
@@ -94,6 +94,40 @@ def test_staged_dense_int3(dev, shape):
     assert np.array_equal(q3, O.unpack(u32(qw4)))
     ref = O.gemm(x, O.dequant_operand(q3, ze3.cpu().numpy(), sc3.cpu().numpy(), 128))
     gemm_close(y3.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=ids)
+def test_fused_dense_int3(dev, shape):
+    """The fused product on dense INT3 words (awq_w3a16_gemm) equals the fused
+    product of the same codes in 4-bit containers bit for bit, with and
+    without the inverse scale and the SSE epilogue, and matches the oracle's
+    product of the unpacked codes."""
+    announce("w3a16_gemm fused dense INT3", ids(shape))
+    M, K, N, seed = shape
+    x, w = synth.random_layer(M, K, N, seed=seed + 70, n_outlier=4, outlier_factor=20.0)
+    rng = np.random.default_rng(seed + 7)
+    s = np.exp(rng.uniform(-0.5, 0.5, K)).astype(np.float32)
+    inv = (1.0 / s.astype(np.float64)).astype(np.float32)
+    wd, sd, xd, invd = to_dev_bf16(w, dev), to_dev_f32(s, dev), to_dev_bf16(x, dev), to_dev_f32(inv, dev)
+    qw3, sc3, ze3 = awq.quantize_pack3(wd, sd)
+    qw4, sc4, ze4 = awq.quantize_pack(wd, sd, 3)
+    y_ref = rng.standard_normal((M, N)).astype(np.float32) * 0.1
+    yrd = to_dev_f32(y_ref, dev)
+    y3, sse3 = awq.w4a16_gemm(xd, qw3, sc3, ze3, 3, 128, inv_s=invd, y_ref=yrd,
+                              layout=awq.LAYOUT_INT3_DENSE)
+    y4, sse4 = awq.w4a16_gemm(xd, qw4, sc4, ze4, 3, 128, inv_s=invd, y_ref=yrd)
+    _, sse_only = awq.w4a16_gemm(xd, qw3, sc3, ze3, 3, 128, inv_s=invd, y_ref=yrd, return_y=False,
+                                 layout=awq.LAYOUT_INT3_DENSE)
+    y3n = awq.w4a16_gemm(xd, qw3, sc3, ze3, 3, 128, layout=awq.LAYOUT_INT3_DENSE)
+    y4n = awq.w4a16_gemm(xd, qw4, sc4, ze4, 3, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(y3, y4) and torch.equal(sse3, sse4) and torch.equal(sse_only, sse3)
+    assert torch.equal(y3n, y4n)
+    q3 = O.unpack3(u32(qw3))
+    ref = O.gemm(x, O.dequant_operand(q3, ze3.cpu().numpy(), sc3.cpu().numpy(), 128, inv))
+    gemm_close(y3.cpu().numpy(), ref)
+    d = y3.cpu().numpy().astype(np.float64) - y_ref.astype(np.float64)
+    assert abs(sse3.item() - float((d * d).sum())) <= 1e-6 * float((d * d).sum())
 
 
 def test_staged_empty_and_errors(dev):
@@ -104,7 +138,8 @@ def test_staged_empty_and_errors(dev):
     ze = torch.zeros((64, 2), dtype=torch.uint8, device=dev)
     y = awq.w4a16_gemm(x, qw, sc, ze, staged=True)
     assert tuple(y.shape) == (0, 64)
-    with pytest.raises(awq.AwqError, match="dense INT3 layout holds 3-bit codes"):
+    # refused by the wrapper before any call (the library refuses it too: ABI tests)
+    with pytest.raises(ValueError, match="dense INT3 layout holds 3-bit codes"):
         awq.w4a16_gemm(torch.zeros((4, 256), dtype=torch.bfloat16, device=dev),
                        torch.zeros((64, 24), dtype=torch.int32, device=dev), sc, ze, 4,
                        layout=awq.LAYOUT_INT3_DENSE)
