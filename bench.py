@@ -881,7 +881,7 @@ def main() -> int:
         return 0
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this implementation runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         return 2
 
