@@ -26,7 +26,8 @@
  *     until then.  Calls on different streams that share an output race.
  *   - On any validation error nothing is enqueued and no HIP call is made.
  *   - Pointers to bf16/f32/u32 tensors with more than one element must be
- *     16-byte aligned (AWQ_ERR_ALIGN otherwise).
+ *     16-byte aligned (AWQ_ERR_ALIGN otherwise), except where a call states
+ *     a weaker requirement (dense INT3 words, scales, sse).
  *   - group must be 128 and bits 3 or 4 (AWQ_ERR_UNSUPPORTED otherwise); K must
  *     be a positive multiple of group, at most 2^22, and the contractions
  *     take N <= 2^22 (AWQ_ERR_SHAPE otherwise: tiles are addressed with 32-bit
@@ -42,6 +43,11 @@
  *   scales  f32 [N][K/group]: quantization step of each group.
  *   zeros   u8  [N][K/group]: integer zero point of each group.
  *   Dequantized weight: (code - zero) * step.
+ *   Dense INT3 (awq_quantize_pack3; sourcepulse AWQ project page: 3-bit
+ *   weights): qweight3 u32 [N][3K/32], each run of 32 codes along K one
+ *   96-bit little-endian value with code i at bits 3i, in three words.
+ *   Compact deployment metadata (awq_quantize_pack16): binary16 steps and
+ *   two 4-bit zeros per byte.
  */
 #ifndef AWQ_MI355X_H
 #define AWQ_MI355X_H
