@@ -49,6 +49,19 @@ def test_rmsnorm(dev):
         assert np.array_equal(bits(u), ru)
 
 
+@pytest.mark.parametrize("K", [2048, 2056, 6152, 8192, 8200, 14336, 16384, 16392])
+def test_rmsnorm_row_lengths(dev, K):
+    # one to eight register pieces per thread, ragged last pieces, and rows past
+    # the register-resident length (read twice)
+    announce(f"rmsnorm K={K}")
+    x, _ = synth.random_layer(5, K, 8, seed=K, n_outlier=4, outlier_factor=30.0)
+    gamma = np.random.default_rng(K).uniform(0.5, 1.5, K).astype(np.float32)
+    u, r = awq.rmsnorm(to_dev_bf16(x, dev), to_dev_f32(gamma, dev), 1e-6, return_r=True)
+    ru, rr = O.rmsnorm(x, gamma, 1e-6)
+    assert np.array_equal(r.cpu().numpy(), rr)
+    assert np.array_equal(bits(u), ru)
+
+
 def test_silu_mul_divide_residual(dev):
     announce("silu_mul, divide_rows, residual_add")
     rng = np.random.default_rng(6)
