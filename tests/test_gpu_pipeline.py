@@ -79,6 +79,14 @@ def test_silu_mul_divide_residual(dev):
                           O.residual_add(x, yy))
 
 
+@pytest.mark.parametrize("M,F", [(1, 4), (3, 12), (1000, 1028), (257, 2048)])
+def test_silu_mul_shapes(dev, M, F):
+    # one quad, a few quads, several workgroups with a ragged last one, whole workgroups
+    announce(f"silu_mul M={M} F={F}")
+    y = (np.random.default_rng(M + F).standard_normal((M, 2 * F)) * 6).astype(np.float32)
+    close_bf16(bits(awq.silu_mul(to_dev_f32(y, dev))), O.silu_mul(y, F))
+
+
 def check_block_steps(dev, x, gamma, wgu, wd, n_grid, F, gram=False):
     """Run one block on the GPU and check each step against the oracle on the
     GPU's own inputs; returns the GPU's x_next (bit patterns)."""
