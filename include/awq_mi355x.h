@@ -379,7 +379,7 @@ awq_status awq_decode_gemm_tiled(const uint16_t* a, int64_t M, int64_t N, int64_
  * itself allocates and frees nothing.  The partials take
  * awq_workspace_size(AWQ_OP_DECODE_GEMM) bytes (splits x M x N x 4); a shape
  * that needs more than 16 MiB gives AWQ_ERR_WORKSPACE (the Llama-2-70B down
- * projection at 64 tokens, 8192 x 28672, needs 14.7 MB).  Every call
+ * projection at 64 tokens, 8192 x 28672, needs 8 MiB).  Every call
  * on one GPU shares that GPU's scratch: calls that overlap in time on one GPU
  * (two streams, two threads) race and must be serialised by the caller.
  * Nothing in the scratch needs clearing: each call overwrites every partial

@@ -28,16 +28,19 @@
 // Work split.  At these sizes a call is dominated by fixed latency (a kernel
 // costs several microseconds before it streams a byte), so the layer should be
 // in flight at once, in as few kernels as possible.  A workgroup owns 16, 32
-// or 64 output channels and a range of at most 64 groups along K (32 above 16
-// tokens; 128 at up to 6 tokens when K exceeds 64 groups, with 8 waves
-// instead of 4); its waves split that range, and each wave streams its columns'
-// codes through a ring of two groups.  The waves' partial outputs are summed
-// through LDS in wave order, so results do not depend on timing.  Only layers
-// whose K exceeds that range also split K across workgroups; those write fp32
-// partials that a second kernel sums in split order.  More columns per
-// workgroup let one activation fragment feed more codes, which pays when M is
-// large or the layer is wide enough to keep every CU busy anyway (the rule in
-// decode_blocks_per_group was measured on the Llama-3-8B block's layers).
+// or 64 output channels and a range of at most 64 groups along K (128 at up
+// to 6 tokens when K exceeds 64 groups, with 8 waves instead of 4); its waves
+// split that range, and each wave streams its columns' codes through a ring
+// of groups.  The waves' partial outputs are summed through LDS in wave
+// order, so results do not depend on timing.  Layers whose K exceeds that
+// range, and above 8 tokens layers too narrow to fill the chip otherwise,
+// also split K across workgroups; those write fp32 partials that a second
+// kernel sums in split order.  More columns per workgroup let one activation
+// fragment feed more codes: up to 8 tokens that pays when the layer is wide
+// enough to keep every CU busy anyway (decode_blocks_per_group); above 8
+// tokens the activation traffic dominates and the plan takes the fewest
+// workgroups that still fill the chip (many_token_shape).  Both rules were
+// measured on the Llama-3-8B block's layers.
 // Tiled weights (TL): the packed codes rearranged once so that a wave's
 // code load for one 16-column block and one group is a single contiguous
 // 1 KiB (768 B for dense INT3) piece in lane order: tile b*G + g holds rows
@@ -580,16 +583,71 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
   y[i] = acc;
 }
 
-// 16-column blocks per workgroup, from the number of workgroups one block
-// each would give (b1, K splits included).  Measured (4 waves, ring of 2) on
-// the Llama-3-8B layers at M = 1, 16, 32 and 64: more columns let an
-// activation fragment feed more codes, which pays once M > 4 if at least 192
-// workgroups remain, and at any M on the widest layers.
+// Up to 8 tokens: 16-column blocks per workgroup, from the number of
+// workgroups one block each would give (b1, K splits included).  Measured
+// (4 waves, ring of 2) on the Llama-3-8B layers: more columns let an
+// activation fragment feed more codes, which pays once M > 4 if at least 384
+// column blocks remain, and at any M on the widest layers.
 int decode_blocks_per_group(int64_t M, int64_t N, int64_t splits) {
   const int64_t b1 = ceil_div(N, (int64_t)16) * splits;
-  if (M > 8 && b1 >= 1024) return 4;
   if ((M > 4 && b1 >= 384) || b1 >= 1024) return 2;
   return 1;
+}
+
+// Above 8 tokens every workgroup reads its token blocks' activations once per
+// group for each 16-column block it does not share them with, so the
+// activation traffic is (N / columns per workgroup) x M x K x 2 bytes, and at
+// 64 tokens it outweighs the codes many times over (128 MiB against 8.9 MB on
+// a 4096 x 4096 layer).  The plan therefore takes the fewest workgroups that
+// still fill the chip: of the column blocks {1, 2, 4}, token blocks {1, 2}
+// and K splits {s, 2s, 4s} (s the fewest with at most 64 groups per
+// workgroup), the one with the fewest workgroups not below kMinWorkgroups
+// (else the most workgroups); ties go to no K split (a second kernel and the
+// partials cost more than a little parallelism), then more columns, then
+// more tokens per workgroup.  Measured on the four Llama-3-8B layers at 16,
+// 32 and 64 tokens against a sweep of all those combinations, the rule
+// picks the fastest in 10 of 12 cases and is within 1% in the others; at
+// 32 and 64 tokens it takes o_proj (4096 x 4096) from 10.3 and 20.0 us to
+// 7.8 and 9.7, qkv (6144 x 4096) from 11.5 and 18.1 to 10.0 and 13.8, and
+// down (4096 x 14336) at 64 tokens from 27.5 to 23.1 us.
+constexpr int64_t kMinWorkgroups = 192;
+
+struct Shape3 {
+  int nb, mb;
+  int64_t splits, groups_per_split, workgroups;
+};
+
+Shape3 many_token_shape(int64_t M, int64_t N, int64_t G) {
+  const int64_t mb_all = ceil_div(M, (int64_t)16);
+  const int64_t s_min = ceil_div(G, (int64_t)kBlockGroups);
+  Shape3 best{0, 0, 0, 0, 0};
+  auto key_better = [&](const Shape3& a, const Shape3& b) {
+    // a before b among equal workgroup counts
+    if ((a.splits > 1) != (b.splits > 1)) return a.splits == 1;
+    if (a.nb != b.nb) return a.nb > b.nb;
+    if (a.mb != b.mb) return a.mb > b.mb;
+    return a.splits < b.splits;
+  };
+  for (int64_t f = 1; f <= 4; f *= 2) {
+    int64_t s = std::min(G, s_min * f);
+    const int64_t gps = ceil_div(G, s);
+    s = ceil_div(G, gps);                     // no split without groups
+    for (int nb = 1; nb <= 4; nb *= 2) {
+      for (int mb = 1; mb <= kMaxTokenBlocks && mb <= mb_all; ++mb) {
+        const Shape3 c{nb, mb, s, gps,
+                       ceil_div(N, (int64_t)16 * nb) * s * ceil_div(mb_all, (int64_t)mb)};
+        if (best.nb == 0) { best = c; continue; }
+        const bool c_ok = c.workgroups >= kMinWorkgroups, b_ok = best.workgroups >= kMinWorkgroups;
+        bool take;
+        if (c_ok != b_ok) take = c_ok;
+        else if (c.workgroups != best.workgroups)
+          take = c_ok ? c.workgroups < best.workgroups : c.workgroups > best.workgroups;
+        else take = key_better(c, best);
+        if (take) best = c;
+      }
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -597,24 +655,28 @@ int decode_blocks_per_group(int64_t M, int64_t N, int64_t splits) {
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
   DecodePlan d;
   const int64_t G = K / kGroup;
-  // Above 16 tokens each wave's groups cost more (more token blocks per
-  // group), so workgroups take at most 32 groups and more of them share K:
-  // measured on the Llama-3-8B down layer (K = 14336) at M = 32 and 64,
-  // 22.3 -> 20.3 and 35.1 -> 29.0 us; 16 groups per workgroup was slower.
-  int64_t max_groups = M > 16 ? kBlockGroups / 2 : kBlockGroups;
-  // Up to 6 tokens, a K of more than 64 groups goes to workgroups of
-  // kWavesWide waves and up to 128 groups, which halves the K splits (none
-  // at all up to 128 groups, so no second kernel sums partials).  Measured
-  // on the Llama-3-8B down layer (K = 14336) at M = 1 and 4: 14.5 -> 10.7
-  // and 13.1 -> 11.3 us; on the Llama-2-70B down layer (K = 28672, dense
-  // INT3) at M = 1, 2 and 4: 29.1 -> 26.6, 28.1 -> 26.8, 29.3 -> 27.4 us;
-  // at M = 5 and 6 on 8B down 12.8 -> 11.6 and 13.3 -> 11.6 us.  At 8
-  // tokens it was mixed (8B down 12.7 -> 13.1 us, 70B down 31.9 -> 30.6 us),
-  // at 16 slower (8B down, 14.9 -> 18.8 us), and 8 waves over 64 groups or
-  // fewer were slower at every M.
-  if (M <= 6 && G > kBlockGroups) max_groups = 2 * kBlockGroups;
-  d.splits = ceil_div(G, max_groups);
-  d.groups_per_split = ceil_div(G, d.splits);
+  if (M > 8) {
+    const Shape3 c = many_token_shape(M, N, G);
+    d.splits = c.splits;
+    d.groups_per_split = c.groups_per_split;
+    d.col_blocks = c.nb;
+    d.token_blocks = c.mb;
+  } else {
+    // Up to 6 tokens, a K of more than 64 groups goes to workgroups of
+    // kWavesWide waves and up to 128 groups, which halves the K splits (none
+    // at all up to 128 groups, so no second kernel sums partials).  Measured
+    // on the Llama-3-8B down layer (K = 14336) at M = 1 and 4: 14.5 -> 10.7
+    // and 13.1 -> 11.3 us; on the Llama-2-70B down layer (K = 28672, dense
+    // INT3) at M = 1, 2 and 4: 29.1 -> 26.6, 28.1 -> 26.8, 29.3 -> 27.4 us;
+    // at M = 5 and 6 on 8B down 12.8 -> 11.6 and 13.3 -> 11.6 us.  At 8
+    // tokens it was mixed (8B down 12.7 -> 13.1 us, 70B down 31.9 -> 30.6
+    // us), and 8 waves over 64 groups or fewer were slower at every M.
+    const int64_t max_groups = (M <= 6 && G > kBlockGroups) ? 2 * kBlockGroups : kBlockGroups;
+    d.splits = ceil_div(G, max_groups);
+    d.groups_per_split = ceil_div(G, d.splits);
+    d.col_blocks = decode_blocks_per_group(M, N, d.splits);
+    d.token_blocks = 1;
+  }
   d.ws_bytes = d.splits > 1 ? align_up((size_t)d.splits * M * N * sizeof(float)) : 0;
   return d;
 }
@@ -657,15 +719,9 @@ hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* 
                            hipStream_t stream, bool int3_dense, bool tiled) {
   const int64_t M = p.M, N = p.N;
   const int mb_all = (int)ceil_div(M, (int64_t)16);
-  // Narrow layers (fewer than 512 column blocks, K splits included) above 32
-  // tokens take one token block per workgroup: more workgroups in flight
-  // there beat sharing the converted codes (Llama-3-8B qkv at M = 48 and 64:
-  // 17.2 -> 16.6 and 20.0 -> 16.8 us; the wide gate_up and down layers were
-  // slower with one block).
   const int64_t b1 = ceil_div(N, (int64_t)16) * d.splits;
-  const int mb = (M > 32 && b1 < 512) ? 1 : std::min(mb_all, kMaxTokenBlocks);
+  const int mb = d.token_blocks, nb = d.col_blocks;
   const int tz = (int)ceil_div((int64_t)mb_all, (int64_t)mb);   // token groups
-  const int nb = decode_blocks_per_group(std::min(M, (int64_t)16 * mb), N, d.splits);
   dim3 grid((unsigned)ceil_div(N, (int64_t)16 * nb), (unsigned)d.splits, (unsigned)tz);
   // More groups per workgroup than kWaves waves can take: the wide
   // workgroup (decode_plan gives it only to M <= 6, so one token block and

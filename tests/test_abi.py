@@ -195,9 +195,14 @@ def test_decode_gemm_errors_and_plan():
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 4, 4096, 16512) >= 2 * 4 * 4096 * 4
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 6, 4096, 14336) == 0
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 7, 4096, 8320) >= 2 * 7 * 4096 * 4
-    # Above 16 tokens a workgroup takes at most 32 groups (4096 channels).
+    # Above 8 tokens the plan takes the fewest workgroups that fill the chip,
+    # with no K split where one workgroup's 64 groups can cover K.
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 17, 4096, 4096) == 0
-    assert awq.workspace_size(awq.OP_DECODE_GEMM, 17, 4096, 4224) >= 2 * 17 * 4096 * 4
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 64, 4096, 8192) == 0
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 17, 4096, 8320) >= 2 * 17 * 4096 * 4
+    # A layer too narrow to fill the chip splits K further: 4096 x 14336 at
+    # 16 tokens takes 4 splits of 28 groups (64 workgroups of 64 columns each).
+    assert awq.workspace_size(awq.OP_DECODE_GEMM, 16, 4096, 14336) >= 4 * 16 * 4096 * 4
     need = awq.workspace_size(awq.OP_DECODE_GEMM, 4, 128, 32768)
     assert need >= 2 * 4 * 128 * 4
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 7, 128, 32768) >= 4 * 7 * 128 * 4

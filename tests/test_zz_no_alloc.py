@@ -37,7 +37,7 @@ def _layer(M, N, K, bits, dense, seed, dev):
 def test_noalloc_matches_workspace_entry_two_calls():
     dev = require_gpu()
     # First call: the largest scratch of the workloads (Llama-2-70B down at
-    # 64 tokens: 7 K splits, 14.7 MB of partials); second: smaller (2 splits).
+    # 64 tokens: 4 K splits, 8 MiB of partials); second: smaller (2 splits).
     for M, N, K, bits, dense, seed in ((64, 8192, 28672, 4, False, 1),
                                        (8, 1000, 9216, 3, True, 2)):
         announce("decode noalloc", M, N, K, bits, dense)
@@ -62,9 +62,9 @@ def test_noalloc_without_splits_and_too_large():
     assert awq.workspace_size(awq.OP_DECODE_GEMM, 3, 520, 2048) == 0
     y = awq.decode_gemm_tiled_noalloc(ad, tiles, sc, ze, layout)
     assert torch.equal(y, awq.decode_gemm_tiled(ad, tiles, sc, ze, layout))
-    # partials of 7 splits x 64 x 16384 x 4 B = 29 MB exceed the 16 MiB scratch:
+    # partials of 4 splits x 64 x 24576 x 4 B = 24 MiB exceed the 16 MiB scratch:
     # rejected on the host before anything is enqueued
-    N, K = 16384, 28672
+    N, K = 24576, 28672
     tl = torch.zeros(awq.decode_tiles_size(N, K) // 4, dtype=torch.int32, device=dev)
     scz = torch.ones((N, K // 128), dtype=torch.float32, device=dev)
     zez = torch.zeros((N, K // 128), dtype=torch.uint8, device=dev)
