@@ -407,9 +407,9 @@ def _graph_time_ms(fn, reps: int, stream) -> float:
 
 
 def bench_decode(awq, dev, stream, reps: int = 96, layers=("qkv", "o_proj", "gate_up", "down"),
-                 token_counts=(1, 2, 4, 8, 16, 64)) -> dict:
+                 token_counts=(1, 2, 4, 8, 16, 32, 64)) -> dict:
     """Decode-shaped W4A16 contraction on the Llama-3-8B block's layers
-    (M = 1, 2, 4, 8, 16 and 64 tokens, random packed INT4 weights), on decode tiles
+    (M = 1, 2, 4, 8, 16, 32 and 64 tokens, random packed INT4 weights), on decode tiles
     with fp32 steps and u8 zeros, on the row-major packed words, on decode
     tiles with the compact metadata (binary16 steps, 4-bit zeros) and on
     decode tiles with metadata tiles (the compact metadata as one u32 per row

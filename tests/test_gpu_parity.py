@@ -439,7 +439,10 @@ DECODE_SHAPES = [(1, 64, 128), (2, 200, 256), (3, 1000, 1024), (4, 4096, 4096), 
                  (17, 1000, 1024), (32, 6144, 4096), (48, 520, 16512), (64, 4096, 4096),
                  (64, 20000, 640), (33, 40, 128), (45, 8200, 256),
                  (1, 4096, 14336), (3, 200, 16384), (2, 40, 8320), (4, 16392, 8320),
-                 (6, 40, 8320), (5, 520, 16512), (7, 40, 8320)]
+                 (6, 40, 8320), (5, 520, 16512), (7, 40, 8320),
+                 # above 8 tokens: 64 columns and two token blocks per
+                 # workgroup with K splits, a ragged last column block
+                 (40, 4104, 14336), (24, 4104, 11008)]
 
 
 @pytest.mark.parametrize("bits", [4, 3])
