@@ -129,8 +129,9 @@ constexpr int64_t kDecodeMaxM = 64;
 struct DecodePlan {
   int64_t groups_per_split;
   int64_t splits;
-  int col_blocks;           // 16-column blocks per workgroup: 1, 2 or 4
-  int token_blocks;         // 16-token blocks per workgroup: 1 or 2
+  bool cols;                // the column-split kernel (waves split columns, not K)
+  int col_blocks;           // 16-column blocks per workgroup (1, 2 or 4), or per wave (cols: 2)
+  int token_blocks;         // 16-token blocks per workgroup: 1 or 2 (cols: 2 or 4)
   size_t ws_bytes;          // fp32 partials [splits][M][N] when splits > 1
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K);

@@ -40,7 +40,10 @@
 // enough to keep every CU busy anyway (decode_blocks_per_group); above 8
 // tokens the activation traffic dominates and the plan takes the fewest
 // workgroups that still fill the chip (many_token_shape).  Both rules were
-// measured on the Llama-3-8B block's layers.
+// measured on the Llama-3-8B block's layers.  Above 32 tokens on layers of
+// 96 Mi weights or more, decode_cols_kernel instead splits a workgroup's
+// columns across its waves and stages each group's activations once in LDS
+// for all of them.
 // Tiled weights (TL): the packed codes rearranged once so that a wave's
 // code load for one 16-column block and one group is a single contiguous
 // 1 KiB (768 B for dense INT3) piece in lane order: tile b*G + g holds rows
@@ -94,6 +97,8 @@ constexpr int kBlockGroups = kWaves * kWaveGroups;   // 64 groups = 8192 channel
 // blocks per workgroup beat four by up to 9%, and one block was slower on
 // the wide layers).
 constexpr int kMaxTokenBlocks = 2;
+// Code ring of the column-split kernel (groups in flight per wave).
+constexpr int kColsDepth = 4;
 
 // Where the steps and zeros come from.
 enum MetaSource { kMetaF32 = 0, kMetaH16 = 1, kMetaTiles = 2 };
@@ -504,6 +509,227 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
 #endif
 }
 
+// Above 8 tokens: the waves of a workgroup split its columns instead of K.
+// Every wave walks the same groups, so each group's activations (MB token
+// blocks x 128 channels, 4 KiB per block) are loaded once per workgroup,
+// 16 bytes per lane, staged in LDS and read by all four waves as MFMA
+// fragments: the activation traffic through L2 falls by the number of waves
+// against decode_gemm_kernel, where each wave reads its own groups'
+// activations for its columns.  Each wave owns NBW 16-column blocks and folds
+// every group of the workgroup's range into its outputs in group order, so
+// no cross-wave reduction is needed.  LDS ring of two stages: at step g the
+// workgroup writes group g+1's activations (loaded two steps ahead into
+// registers), computes group g, and ends with one barrier.  The codes stream
+// through a per-wave register ring of CD groups as in decode_gemm_kernel.
+// Row r's piece p (channels 8p .. 8p+7) of a token block sits at LDS slot
+// 16r + (p ^ r): the 16 lanes of one fragment read (rows 0..15, one piece
+// each) and of one write (one row, 16 pieces) then hit 64 distinct banks.
+template <int NBW, int MB, int CD, bool I3, bool TL, int META>
+__global__ __launch_bounds__(256) void decode_cols_kernel(DecodeParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int W = 4;
+  constexpr bool H16 = META == kMetaH16, MT = META == kMetaTiles;
+  static_assert(META == kMetaF32 || TL, "the compact metadata goes with tiled codes");
+  static_assert(CD % 2 == 0, "the activation stage follows the parity of the group");
+  constexpr int kCols = 16 * NBW;                     // per wave
+  __shared__ uint4 As[2][MB][256];
+  __shared__ float2 ssz[MT ? 1 : W][MT ? 1 : kCols][MT ? 1 : kBlockGroups];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t G = K / kGroup;
+  const int m0 = (int)blockIdx.z * 16 * MB;
+  const int64_t n_wave = (int64_t)blockIdx.x * (W * kCols) + wave * kCols;
+  const int64_t g0 = (int64_t)blockIdx.y * p.groups_per_split;
+  const int gn = (int)max((int64_t)0, min(G, g0 + p.groups_per_split) - g0);   // <= 64
+
+  const rsrc_t ra = make_rsrc(p.a, M * K * 2);
+  const int64_t row_words = I3 ? 3 * K / 32 : K / 8;
+  const int64_t row_blocks = (N + 15) / 16;
+  const rsrc_t rq = TL ? make_rsrc(p.qweight, row_blocks * 16 * row_words * 4)
+                       : make_rsrc(p.qweight + n_wave * row_words, (N - n_wave) * row_words * 4);
+  const int64_t zrow = H16 ? (G + 1) / 2 : G;
+  const rsrc_t rs = H16 ? make_rsrc(p.steps16 + n_wave * G, (N - n_wave) * G * 2)
+                        : make_rsrc(p.scales + n_wave * G, (N - n_wave) * G * 4);
+  const rsrc_t rz = make_rsrc(p.zeros + n_wave * zrow, (N - n_wave) * zrow);
+  const rsrc_t rm = make_rsrc(p.meta, MT ? row_blocks * G * 64 : 0);
+
+  // (step, 128 + zero) of this wave's kCols rows x the gn groups, into the
+  // wave's LDS table (rows past N read as zero).
+  if constexpr (!MT) {
+    constexpr int kSzIters = kCols * kBlockGroups / 64;
+#pragma unroll 4
+    for (int i = 0; i < kSzIters; ++i) {
+      const int e = i * 64 + lane;
+      const int row = gn > 0 ? e / gn : kCols, gl = gn > 0 ? e - row * gn : 0;
+      if (row < kCols) {
+        if constexpr (H16) {
+          const uint32_t st = __builtin_amdgcn_raw_buffer_load_b16(
+              rs, (uint32_t)((row * G + g0 + gl) * 2), 0, 0);
+          const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(
+              rz, (uint32_t)(row * zrow + (g0 + gl) / 2), 0, 0);
+          const uint32_t zq = (zb >> (4 * ((g0 + gl) & 1))) & 15u;
+          ssz[wave][row][gl] =
+              make_float2((float)__builtin_bit_cast(_Float16, (uint16_t)st), 128.f + (float)zq);
+        } else {
+          const uint32_t st = __builtin_amdgcn_raw_buffer_load_b32(
+              rs, (uint32_t)((row * G + g0 + gl) * 4), 0, 0);
+          const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(
+              rz, (uint32_t)(row * G + g0 + gl), 0, 0);
+          ssz[wave][row][gl] = make_float2(__uint_as_float(st), 128.f + (float)zb);
+        }
+      }
+    }
+  }
+
+  // Codes of group gl for this wave's blocks (as decode_gemm_kernel).
+  constexpr uint32_t kGroupBytes = I3 ? 48 : 64, kLaneBytes = I3 ? 12 : 16;
+  constexpr uint32_t kStride = TL ? 16 * kGroupBytes : kGroupBytes;
+  uint32_t q_off[NBW];
+#pragma unroll
+  for (int b = 0; b < NBW; ++b)
+    q_off[b] = TL ? (uint32_t)(((n_wave / 16 + b) * G + g0) * kStride + kLaneBytes * lane)
+                  : (uint32_t)((b * 16 + c16) * row_words * 4 + g0 * kGroupBytes + g4 * kLaneBytes);
+  struct CodeLoads {
+    uint32_t m[NBW];
+    uint4 q[NBW];
+  };
+  auto load_codes = [&](CodeLoads& L, int gl) {
+    const bool in = gl < gn;
+    if constexpr (MT) {
+#pragma unroll
+      for (int b = 0; b < NBW; ++b)
+        L.m[b] = __builtin_amdgcn_raw_buffer_load_b32(
+            rm, in ? (uint32_t)((((n_wave / 16 + b) * G + g0 + gl) * 16 + c16) * 4) : 0xFFFFFFF0u,
+            0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+      const uint32_t off = in ? q_off[b] + (uint32_t)gl * kStride : 0xFFFFFFF0u;
+      L.q[b] = I3 ? ld_codes12(rq, off) : ld_codes16(rq, off);
+    }
+  };
+
+  // The workgroup's activations of group gl: thread t loads row t >> 4
+  // (tokens past M repeat token M - 1, whose outputs are never stored),
+  // piece t & 15, of each token block.
+  const int ar = t >> 4, ap = t & 15;
+  uint32_t a_off[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    a_off[mb] = (uint32_t)(((int64_t)min(m0 + 16 * mb + ar, (int)M - 1) * K + g0 * kGroup + 8 * ap) * 2);
+  auto load_a = [&](uint4 (&P)[MB], int gl) {
+    const bool in = gl < gn;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      P[mb] = ld16(ra, in ? a_off[mb] + (uint32_t)gl * (kGroup * 2) : 0xFFFFFFF0u);
+  };
+  auto write_a = [&](int stage, const uint4 (&P)[MB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) As[stage][mb][ar * 16 + (ap ^ ar)] = P[mb];
+  };
+
+  uint32_t kc;   // bf16 128 in both halves, in a VGPR (see codes_b)
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(kc));
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
+                                                       0x3F803F80u});
+  f32x4 y[MB][NBW];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) y[mb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const CodeLoads& L, int stage, int gl) {
+    bf16x8 bq[NBW][4];
+    float2 sz[NBW];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+      if constexpr (I3 && TL) {
+        lift_pairs3(L.q[b], bq[b], kc);
+      } else {
+        const uint4 qw = I3 ? nibbles_from_int3(L.q[b]) : L.q[b];
+        const uint32_t words[4] = {qw.x, qw.y, qw.z, qw.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bq[b][j] = codes_b(words[j], kc);
+      }
+      if constexpr (MT) {
+        const uint32_t m = L.m[b];
+        sz[b] = make_float2((float)__builtin_bit_cast(_Float16, (uint16_t)(m & 0xFFFFu)),
+                            128.f + (float)((m >> 16) & 15u));
+      } else {
+        sz[b] = ssz[wave][b * 16 + c16][gl];
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      bf16x8 af[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 d = As[stage][mb][c16 * 16 + ((4 * g4 + j) ^ c16)];
+        af[j] = TL ? __builtin_bit_cast(bf16x8, u32x4{d.x, d.y, d.z, d.w}) : permute_a(d);
+      }
+      f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], ones, sa, 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bq[b][j], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          y[mb][b][i] = fmaf(sz[b].x, fmaf(-sz[b].y, sa[i], acc[i]), y[mb][b][i]);
+      }
+    }
+  };
+
+  CodeLoads R[CD];
+#pragma unroll
+  for (int d = 0; d < CD; ++d) load_codes(R[d], d);
+  uint4 P[2][MB];
+  load_a(P[0], 0);
+  load_a(P[1], 1);
+  write_a(0, P[0]);
+  load_a(P[0], 2);
+  __syncthreads();
+  // Step g: group g+1's activations into stage (g+1)&1 (read last at step
+  // g-1, before that step's barrier), group g+3's into registers, group g
+  // computed from stage g&1, then the barrier that publishes stage (g+1)&1.
+  // gn is the same for every wave, so every wave passes every barrier.
+  for (int gl = 0; gl < gn; gl += CD) {
+#pragma unroll
+    for (int d = 0; d < CD; ++d) {
+      if (gl + d < gn) {
+        write_a((d + 1) & 1, P[(d + 1) & 1]);
+        load_a(P[(d + 1) & 1], gl + d + 3);
+        compute(R[d], d & 1, gl + d);
+        load_codes(R[d], gl + d + CD);
+        __syncthreads();
+      }
+    }
+  }
+
+  float* out = p.out + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) {
+    const int64_t n = n_wave + b * 16 + c16;
+    if (n < N) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = m0 + 16 * mb + 4 * g4 + i;
+          if (m < M) out[m * N + n] = y[mb][b][i];
+        }
+    }
+  }
+#endif
+}
+
 // Decode tiles from row-major packed words: one thread per W-word piece.
 // 4-bit containers (W = 4): each word's nibbles 0..7 (channels 8j .. 8j+7)
 // go to nibbles 0,4,1,5,2,6,3,7, so channels 2p, 2p+1 land in nibbles t,
@@ -612,6 +838,21 @@ int decode_blocks_per_group(int64_t M, int64_t N, int64_t splits) {
 // down (4096 x 14336) at 64 tokens from 27.5 to 23.1 us.
 constexpr int64_t kMinWorkgroups = 192;
 
+// Above 32 tokens, layers of at least kColsMinWeights weights (48 MiB of
+// 4-bit codes) take the column-split kernel (decode_cols_kernel).  Measured
+// against the plan above (graph replays, weights from HBM, us): Llama-3-8B
+// gate_up 28672 x 4096 at 33 / 48 / 64 tokens 37.3 / 39.3 / 44.0 -> 33.0 /
+// 33.1 / 34.3; Llama-2-70B gate_up 57344 x 8192 at 48 / 64 tokens 125.6 /
+// 139.1 -> 94.4 / 98.2 (four token blocks; 125.2 at 64 with two) and down
+// 8192 x 28672 at 48 / 64 tokens 74.0 / 81.4 -> 63.7 / 64.4.  On smaller
+// layers it was as fast or slower at every token count from 16 to 64
+// (Llama-2-7B gate_up 22016 x 4096 at 48 tokens 31.7 -> 36.0; 4096 x 4096
+// to 4096 x 14336 and 12288 x 4096 up to 1.6x slower): their workgroups wait
+// at one barrier per group, and the plan above already keeps their
+// activation traffic small.
+constexpr int64_t kColsMinWeights = int64_t(96) << 20;
+constexpr int64_t kColsOnePassBytes = int64_t(96) << 20;
+
 struct Shape3 {
   int nb, mb;
   int64_t splits, groups_per_split, workgroups;
@@ -655,12 +896,30 @@ Shape3 many_token_shape(int64_t M, int64_t N, int64_t G) {
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
   DecodePlan d;
   const int64_t G = K / kGroup;
-  if (M > 8) {
+  if (M > 32 && N * K >= kColsMinWeights) {
+    // Large layers at many tokens: the column-split kernel, 128 columns per
+    // workgroup, two token blocks, or four (one pass over the codes) when
+    // the 4-bit codes exceed kColsOnePassBytes (a second pass would no longer
+    // come from the last-level cache), and the fewest K splits that keep
+    // kMinWorkgroups workgroups.
+    const int64_t mb_all = ceil_div(M, (int64_t)16);
+    d.cols = true;
+    d.col_blocks = 2;
+    d.token_blocks = N * K / 2 > kColsOnePassBytes ? 4 : 2;
+    const int64_t s_min = ceil_div(G, (int64_t)kBlockGroups);
+    int64_t s = s_min;
+    while (ceil_div(N, (int64_t)128) * s * ceil_div(mb_all, (int64_t)d.token_blocks) <
+               kMinWorkgroups && s < 4 * s_min && s < G)
+      s *= 2;
+    d.groups_per_split = ceil_div(G, s);
+    d.splits = ceil_div(G, d.groups_per_split);
+  } else if (M > 8) {
     const Shape3 c = many_token_shape(M, N, G);
     d.splits = c.splits;
     d.groups_per_split = c.groups_per_split;
     d.col_blocks = c.nb;
     d.token_blocks = c.mb;
+    d.cols = false;
   } else {
     // Up to 6 tokens, a K of more than 64 groups goes to workgroups of
     // kWavesWide waves and up to 128 groups, which halves the K splits (none
@@ -676,6 +935,7 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K) {
     d.groups_per_split = ceil_div(G, d.splits);
     d.col_blocks = decode_blocks_per_group(M, N, d.splits);
     d.token_blocks = 1;
+    d.cols = false;
   }
   d.ws_bytes = d.splits > 1 ? align_up((size_t)d.splits * M * N * sizeof(float)) : 0;
   return d;
@@ -714,9 +974,56 @@ hipError_t launch_decode_tiles(const uint32_t* qweight, int64_t N, int64_t K, bo
 
 namespace {
 
+// The column-split kernel: 2 16-column blocks per wave, 2 or 4 token blocks
+// per workgroup, a code ring of kColsDepth groups.
+template <int META>
+hipError_t cols_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* ws,
+                         hipStream_t stream, bool int3_dense, bool tiled) {
+  const int64_t M = p.M, N = p.N;
+  const int mb_all = (int)ceil_div(M, (int64_t)16);
+  const int mb = d.token_blocks, nbw = d.col_blocks;
+  // The LDS table of steps and zeros holds at most kBlockGroups groups.
+  if (d.groups_per_split > kBlockGroups || nbw != 2 || (mb != 2 && mb != 4))
+    return hipErrorInvalidValue;
+  dim3 grid((unsigned)ceil_div(N, (int64_t)64 * nbw), (unsigned)d.splits,
+            (unsigned)ceil_div((int64_t)mb_all, (int64_t)mb));
+  auto go = [&](auto NBc, auto MBc) {
+    constexpr int nbv = decltype(NBc)::value, mbv = decltype(MBc)::value;
+    constexpr int cd = kColsDepth;
+    if constexpr (META != kMetaF32) {
+      if (int3_dense)
+        decode_cols_kernel<nbv, mbv, cd, true, true, META><<<grid, 256, 0, stream>>>(p);
+      else
+        decode_cols_kernel<nbv, mbv, cd, false, true, META><<<grid, 256, 0, stream>>>(p);
+    } else {
+      if (int3_dense && tiled)
+        decode_cols_kernel<nbv, mbv, cd, true, true, kMetaF32><<<grid, 256, 0, stream>>>(p);
+      else if (int3_dense)
+        decode_cols_kernel<nbv, mbv, cd, true, false, kMetaF32><<<grid, 256, 0, stream>>>(p);
+      else if (tiled)
+        decode_cols_kernel<nbv, mbv, cd, false, true, kMetaF32><<<grid, 256, 0, stream>>>(p);
+      else
+        decode_cols_kernel<nbv, mbv, cd, false, false, kMetaF32><<<grid, 256, 0, stream>>>(p);
+    }
+  };
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  if (mb == 4)
+    go(I2{}, I4{});
+  else
+    go(I2{}, I2{});
+  if (d.splits > 1) {
+    const int64_t count = M * N;
+    decode_reduce_kernel<<<(unsigned)ceil_div(count, (int64_t)256), 256, 0, stream>>>(
+        (const float*)ws, count, (int)d.splits, y);
+  }
+  return hipGetLastError();
+}
+
 template <int META>
 hipError_t decode_dispatch(DecodeParams p, const DecodePlan& d, float* y, void* ws,
                            hipStream_t stream, bool int3_dense, bool tiled) {
+  if (d.cols) return cols_dispatch<META>(p, d, y, ws, stream, int3_dense, tiled);
   const int64_t M = p.M, N = p.N;
   const int mb_all = (int)ceil_div(M, (int64_t)16);
   const int64_t b1 = ceil_div(N, (int64_t)16) * d.splits;

@@ -150,7 +150,7 @@ int main(void) {
          AWQ_ERR_NULL);
   EXPECT(awq_decode_gemm_tiled(F, 4, k22, k22, F, F, F, AWQ_LAYOUT_NIBBLE, 128, F, F, (size_t)-1,
                                NULL), AWQ_ERR_SHAPE);      /* tiles beyond 4 GiB */
-  EXPECT(awq_decode_gemm_tiled_noalloc(F, 64, 16384, 28672, F, F, F, AWQ_LAYOUT_NIBBLE, 128, F,
+  EXPECT(awq_decode_gemm_tiled_noalloc(F, 64, 24576, 28672, F, F, F, AWQ_LAYOUT_NIBBLE, 128, F,
                                        NULL), AWQ_ERR_WORKSPACE);   /* beyond the static scratch */
   EXPECT(awq_decode_gemm_tiled_noalloc(F, 4, 8, 128, F, F, F, 2, 128, F, NULL), AWQ_ERR_UNSUPPORTED);
   EXPECT(awq_decode_gemm_tiled_noalloc(F, 0, 8, 128, NULL, NULL, NULL, AWQ_LAYOUT_NIBBLE, 128, NULL,

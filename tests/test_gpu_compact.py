@@ -114,7 +114,7 @@ DECODE_SHAPES = [(1, 64, 128), (2, 200, 384), (3, 1000, 1152), (16, 6144, 4096),
                  (16, 40960, 512), (2, 520, 16512), (1, 72, 32768), (33, 40, 640),
                  (64, 4096, 4096), (48, 520, 16512), (45, 8200, 256),
                  (3, 200, 16384), (4, 4096, 4096), (5, 200, 384), (6, 1000, 1152),
-                 (7, 520, 16512), (8, 6144, 4096), (8, 72, 32768)]
+                 (7, 520, 16512), (8, 6144, 4096), (8, 72, 32768), (64, 12296, 8320)]
 
 
 @pytest.mark.parametrize("dense3", [False, True], ids=["nibble", "int3dense"])

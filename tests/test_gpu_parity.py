@@ -442,7 +442,11 @@ DECODE_SHAPES = [(1, 64, 128), (2, 200, 256), (3, 1000, 1024), (4, 4096, 4096), 
                  (6, 40, 8320), (5, 520, 16512), (7, 40, 8320),
                  # above 8 tokens: 64 columns and two token blocks per
                  # workgroup with K splits, a ragged last column block
-                 (40, 4104, 14336), (24, 4104, 11008)]
+                 (40, 4104, 14336), (24, 4104, 11008),
+                 # above 32 tokens on at least 96 Mi weights: the column-split
+                 # kernel, with K splits and ragged column and token blocks,
+                 # two token blocks and four (codes beyond 96 MiB)
+                 (64, 12296, 8320), (36, 24584, 4224), (33, 8200, 24704)]
 
 
 @pytest.mark.parametrize("bits", [4, 3])
@@ -512,7 +516,7 @@ def test_quantize_pack3_bit_exact(dev, shape):
 
 INT3_DECODE_SHAPES = [(1, 64, 128), (3, 1000, 1024), (16, 6144, 4096), (16, 40960, 512),
                       (2, 520, 16512), (64, 4096, 4096), (33, 40, 128), (1, 72, 32768),
-                      (45, 8200, 256), (2, 40, 8320)]
+                      (45, 8200, 256), (2, 40, 8320), (64, 12296, 8320)]
 
 
 @pytest.mark.parametrize("shape", INT3_DECODE_SHAPES, ids=lambda s: f"M{s[0]}_N{s[1]}_K{s[2]}")
