@@ -20,7 +20,10 @@ pytestmark = pytest.mark.gpu
 
 # (M, N, K): no split (K = 4096, 32 groups); K split in 2 (M = 8, 128
 # groups); 8 waves per workgroup, no split (M = 1, 128 groups, 4096 columns).
-SHAPES = [(1, 6144, 4096), (8, 1000, 16384), (1, 4096, 16384)]
+SHAPES = [(1, 6144, 4096), (8, 1000, 16384), (1, 4096, 16384),
+          # above 8 tokens with K splits; above 32 tokens on a large layer
+          # (the column-split kernel, two K splits)
+          (40, 4104, 14336), (48, 12296, 8320)]
 
 
 def _compact_layer(N, K, seed, dev):
