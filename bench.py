@@ -496,8 +496,8 @@ def bench_decode(awq, dev, stream, reps: int = 96, layers=("qkv", "o_proj", "gat
 def bench_decode_int3(awq, dev, stream, reps: int = 64) -> dict:
     """Decode-shaped contraction on the Llama-2-70B MLP's INT3 layers, dense
     INT3 words (3 bits per weight) beside the same codes in 4-bit containers,
-    both as decode tiles, M = 1 and 16, weights rotated beyond the last-level
-    cache."""
+    both as decode tiles, M = 1, 16 and 64 (at 64 tokens both layers take the
+    column-split kernel), weights rotated beyond the last-level cache."""
     import torch
 
     import synth
@@ -523,7 +523,7 @@ def bench_decode_int3(awq, dev, stream, reps: int = 64) -> dict:
                 lay = awq.LAYOUT_INT3_DENSE if layout == "dense" else awq.LAYOUT_NIBBLE
                 packs.append((awq.decode_tiles(qw, K, lay), sc, ze))
                 del qw
-            for M in (1, 16):
+            for M in (1, 16, 64):
                 a = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
                 y = torch.empty((M, N), dtype=torch.float32, device=dev)
                 need = awq.workspace_size(awq.OP_DECODE_GEMM, M, N, K, 3)

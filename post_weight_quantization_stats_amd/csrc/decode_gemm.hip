@@ -533,7 +533,11 @@ __global__ __launch_bounds__(256) void decode_cols_kernel(DecodeParams p) {
   static_assert(CD % 2 == 0, "the activation stage follows the parity of the group");
   constexpr int kCols = 16 * NBW;                     // per wave
   __shared__ uint4 As[2][MB][256];
-  __shared__ float2 ssz[MT ? 1 : W][MT ? 1 : kCols][MT ? 1 : kBlockGroups];
+  // Steps (fp32) and zeros (u8) of each wave's rows and the workgroup's
+  // groups: 40 KiB with two column blocks per wave, so that two workgroups
+  // of four token blocks (32 KiB of activation stages each) share a CU.
+  __shared__ float sst[MT ? 1 : W][MT ? 1 : kCols][MT ? 1 : kBlockGroups];
+  __shared__ uint8_t szb[MT ? 1 : W][MT ? 1 : kCols][MT ? 1 : kBlockGroups];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -571,15 +575,15 @@ __global__ __launch_bounds__(256) void decode_cols_kernel(DecodeParams p) {
               rs, (uint32_t)((row * G + g0 + gl) * 2), 0, 0);
           const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(
               rz, (uint32_t)(row * zrow + (g0 + gl) / 2), 0, 0);
-          const uint32_t zq = (zb >> (4 * ((g0 + gl) & 1))) & 15u;
-          ssz[wave][row][gl] =
-              make_float2((float)__builtin_bit_cast(_Float16, (uint16_t)st), 128.f + (float)zq);
+          sst[wave][row][gl] = (float)__builtin_bit_cast(_Float16, (uint16_t)st);
+          szb[wave][row][gl] = (uint8_t)((zb >> (4 * ((g0 + gl) & 1))) & 15u);
         } else {
           const uint32_t st = __builtin_amdgcn_raw_buffer_load_b32(
               rs, (uint32_t)((row * G + g0 + gl) * 4), 0, 0);
           const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(
               rz, (uint32_t)(row * G + g0 + gl), 0, 0);
-          ssz[wave][row][gl] = make_float2(__uint_as_float(st), 128.f + (float)zb);
+          sst[wave][row][gl] = __uint_as_float(st);
+          szb[wave][row][gl] = (uint8_t)zb;
         }
       }
     }
@@ -660,7 +664,7 @@ __global__ __launch_bounds__(256) void decode_cols_kernel(DecodeParams p) {
         sz[b] = make_float2((float)__builtin_bit_cast(_Float16, (uint16_t)(m & 0xFFFFu)),
                             128.f + (float)((m >> 16) & 15u));
       } else {
-        sz[b] = ssz[wave][b * 16 + c16][gl];
+        sz[b] = make_float2(sst[wave][b * 16 + c16][gl], 128.f + (float)szb[wave][b * 16 + c16][gl]);
       }
     }
 #pragma unroll
