@@ -509,13 +509,14 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
 #endif
 }
 
-// Above 8 tokens: the waves of a workgroup split its columns instead of K.
-// Every wave walks the same groups, so each group's activations (MB token
-// blocks x 128 channels, 4 KiB per block) are loaded once per workgroup,
-// 16 bytes per lane, staged in LDS and read by all four waves as MFMA
-// fragments: the activation traffic through L2 falls by the number of waves
-// against decode_gemm_kernel, where each wave reads its own groups'
-// activations for its columns.  Each wave owns NBW 16-column blocks and folds
+// Large layers above 32 tokens: the waves of a workgroup split its columns
+// instead of K.  Every wave walks the same groups, so each group's
+// activations (MB token blocks x 128 channels, 4 KiB per block) are loaded
+// once per workgroup, 16 bytes per lane, staged in LDS and read by all four
+// waves as MFMA fragments.  A workgroup so covers 128 columns, twice what
+// decode_gemm_kernel's waves hold in registers, which halves the activation
+// traffic through L2, and with four token blocks it reads the codes once
+// for up to 64 tokens.  Each wave owns NBW 16-column blocks and folds
 // every group of the workgroup's range into its outputs in group order, so
 // no cross-wave reduction is needed.  LDS ring of two stages: at step g the
 // workgroup writes group g+1's activations (loaded two steps ahead into
