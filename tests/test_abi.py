@@ -562,3 +562,21 @@ def test_python_wrappers_check_shapes_before_the_device(case):
     if case in good:
         with pytest.raises(ValueError, match="GPU tensor"):
             good[case]()
+
+
+def test_noalloc_scratch_covers_every_workload_layer():
+    """The entry point that allocates nothing keeps the decode contraction's
+    K-split partials in a 16 MiB static scratch; the header states that this
+    covers every workload layer at 1 to 64 tokens.  The partials' size is
+    the decode workspace size, a host-side function of the plan."""
+    import synth
+    worst, where = 0, None
+    for workload, layers in synth.WORKLOADS.items():
+        for spec in layers:
+            for M in range(1, 65):
+                need = awq.workspace_size(awq.OP_DECODE_GEMM, M, spec.N, spec.K)
+                assert need <= 16 << 20, (workload, spec.name, M, need)
+                if need > worst:
+                    worst, where = need, (workload, spec.name, M)
+    # the largest is the Llama-2-70B down projection at 64 tokens: 4 K splits
+    assert where == ("llama2_70b_mlp", "down", 64) and worst == 4 * 64 * 8192 * 4
