@@ -311,9 +311,10 @@ awq_status awq_w4a16_gemm_staged(const uint16_t* x, int64_t M, int64_t N, int64_
  *   qweight/scales/zeros as from awq_quantize_pack, bits 3 or 4
  *   y       f32 [M][N] output
  *   ws      awq_workspace_size(AWQ_OP_DECODE_GEMM) bytes (fp32 partials
- *           when K is split across workgroups: K > 8192, or K > 16384 for
- *           M <= 6, or K > 4096 for M > 16; 0 otherwise, and ws may then be
- *           NULL).
+ *           when K is split across workgroups: up to 8 tokens when
+ *           K > 8192, or K > 16384 for M <= 6; above 8 tokens when K > 8192
+ *           or the layer is too narrow to fill the chip without a split;
+ *           0 otherwise, and ws may then be NULL).
  * M > 64 gives AWQ_ERR_SHAPE (use awq_w4a16_gemm).  M == 0 or N == 0 is a
  * no-op.  Results are bit-reproducible for a given (M, N, K).
  */
