@@ -125,6 +125,19 @@ KERNEL_LABELS = [
                            ("false, false, 0", "decode GEMM, row-major words"),
                            ("true, false, 0", "decode GEMM, dense INT3 row-major"))
       for waves in (4, 8) for few in FEW_TOKENS],
+    # decode_cols_kernel<column blocks per wave, token blocks, code ring,
+    # INT3 dense, tiled, metadata source>: large layers above 32 tokens
+    *[(("decode_cols_kernel<", f", {mb}, 4, {flags}>"),
+       f"decode GEMM, column split, {16 * mb} tokens per workgroup, " + label)
+      for flags, label in (("false, true, 2", "tiles, metadata tiles"),
+                           ("true, true, 2", "dense INT3 tiles, metadata tiles"),
+                           ("false, true, 1", "tiles, compact metadata"),
+                           ("true, true, 1", "dense INT3 tiles, compact metadata"),
+                           ("false, true, 0", "tiles"),
+                           ("true, true, 0", "dense INT3 tiles"),
+                           ("false, false, 0", "row-major words"),
+                           ("true, false, 0", "dense INT3 row-major"))
+      for mb in (2, 4)],
     ("meta_tiles_kernel", "metadata tiles"),
     ("mfma_ceiling_kernel", "ceiling: matrix cores from registers"),
     ("copy_ceiling_kernel", "ceiling: copy"),
