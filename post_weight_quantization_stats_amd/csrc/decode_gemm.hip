@@ -562,7 +562,7 @@ __global__ __launch_bounds__(256) void decode_cols_kernel(DecodeParams p) {
   const rsrc_t rz = make_rsrc(p.zeros + n_wave * zrow, (N - n_wave) * zrow);
   const rsrc_t rm = make_rsrc(p.meta, MT ? row_blocks * G * 64 : 0);
 
-  // (step, 128 + zero) of this wave's kCols rows x the gn groups, into the
+  // Steps and zeros of this wave's kCols rows x the gn groups, into the
   // wave's LDS table (rows past N read as zero).
   if constexpr (!MT) {
     constexpr int kSzIters = kCols * kBlockGroups / 64;
