@@ -193,7 +193,9 @@ def test_fullsize_search_llama2_70b_down(dev, bits):
 def test_fullsize_int3_dense_llama2_70b(dev, name):
     """The 70B-shaped INT3 layers at full size: dense words on sampled rows
     against the oracle, and the dense-INT3 decode contraction bit-identical to
-    the 4-bit-container one at M = 1 and 16, with a sampled oracle block."""
+    the 4-bit-container one at M = 1, 16 and 64 (at 64 tokens both layers take
+    the column-split kernel with four token blocks), with a sampled oracle
+    block."""
     announce("full-size dense INT3", name)
     spec = synth.layer_spec("llama2_70b_mlp", name)
     w = synth.make_weight(spec, 0)
@@ -205,7 +207,7 @@ def test_fullsize_int3_dense_llama2_70b(dev, name):
     rows = sample_rows(spec.N, 16, 5)
     q, z, st = O.quantize(w[rows], s, 3, 128)
     assert np.array_equal(u32(qw3)[rows], O.pack3(q))
-    for M in (1, 16):
+    for M in (1, 16, 64):
         a = synth.decode_activations(spec.K, M, seed=M)
         ad = to_dev_bf16(a, dev)
         y3 = awq.decode_gemm3(ad, qw3, sc, ze)
@@ -221,7 +223,7 @@ def test_fullsize_compact_format_llama2_70b(dev, name, bits, dense3):
     """The compact deployment format on the 70B-shaped layers at full size:
     codes, binary16 steps and zero nibbles on sampled rows against the
     oracle, and the compact decode contraction on tiles bit-identical to the
-    fp32-metadata one on the expanded metadata (M = 1 and 16)."""
+    fp32-metadata one on the expanded metadata (M = 1, 16 and 64)."""
     announce("full-size compact format", name, bits, dense3)
     spec = synth.layer_spec("llama2_70b_mlp", name)
     w = synth.make_weight(spec, 0)
@@ -239,7 +241,7 @@ def test_fullsize_compact_format_llama2_70b(dev, name, bits, dense3):
     tiles = awq.decode_tiles(qw, spec.K, layout)
     sc, ze = awq.expand_meta16(st, z4)
     del wd, qw
-    for M in (1, 16):
+    for M in (1, 16, 64):
         ad = to_dev_bf16(synth.decode_activations(spec.K, M, seed=M), dev)
         y16 = awq.decode_gemm_tiled16(ad, tiles, st, z4, layout)
         y32 = awq.decode_gemm_tiled(ad, tiles, sc, ze, layout)

@@ -462,7 +462,8 @@ def test_decode_gemm(dev, shape, bits):
 
 @pytest.mark.parametrize("name", ["qkv", "o_proj", "gate_up", "down"])
 def test_decode_gemm_llama3_block_shapes(dev, name):
-    """The Llama-3-8B block's layers at their full sizes, M = 1 and 16."""
+    """The Llama-3-8B block's layers at their full sizes, M = 1, 16 and 64
+    (gate_up at 64 tokens takes the column-split kernel)."""
     spec = synth.layer_spec("llama3_8b_block", name)
     for M in (1, 16, 64):
         announce("decode_gemm full size", name, M)
