@@ -377,7 +377,8 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
         }
       }
     }
-    __syncthreads();
+    // No barrier: each wave reads only its own table, and a wave's LDS
+    // accesses complete in order.
   }
 
   uint32_t kc;   // see codes_b; an opaque VGPR value, so it is not folded back into a literal
