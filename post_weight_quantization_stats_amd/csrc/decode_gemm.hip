@@ -231,7 +231,10 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
   constexpr int kCols = 16 * NB;
   // (step, 128 + z) table, 8 to 64 KiB (none with metadata tiles).
   __shared__ float2 ssz[MT ? 1 : W][MT ? 1 : kCols][MT ? 1 : kWaveGroups];
-  __shared__ f32x4 red[W - 1][MB][NB][64];          // partial outputs of waves 1..W-1
+  // Partial outputs of waves 1..W-1; with one token only lanes 0..15 hold
+  // an output (row 0 of each 16-row fragment), so only their first element.
+  __shared__ f32x4 red[A1 ? 1 : W - 1][MB][NB][A1 ? 1 : 64];
+  __shared__ float red1[A1 ? W - 1 : 1][NB][16];
 
   const int lane = threadIdx.x & 63;
   // Wave index in an SGPR, so the buffer resources below are scalar.
@@ -477,20 +480,33 @@ __global__ __launch_bounds__(64 * W) void decode_gemm_kernel(DecodeParams p) {
   }
 
   // Sum the waves' partial outputs in wave order.
-  if (wave > 0) {
+  if constexpr (A1) {
+    if (wave > 0 && lane < 16) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int b = 0; b < NB; ++b) red1[wave - 1][b][lane] = y[0][b][0];
+    }
+    __syncthreads();
+    if (wave != 0 || lane >= 16) return;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) red[wave - 1][mb][b][lane] = y[mb][b];
+    for (int w = 0; w < W - 1; ++w)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) y[0][b][0] += red1[w][b][lane];
+  } else {
+    if (wave > 0) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) red[wave - 1][mb][b][lane] = y[mb][b];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < W - 1; ++w)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) y[mb][b] += red[w][mb][b][lane];
   }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int w = 0; w < W - 1; ++w)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) y[mb][b] += red[w][mb][b][lane];
 
   // Output: lane holds column c16 of each block and rows 16mb + 4*g4 + i.
   float* out = p.out + (int64_t)blockIdx.y * M * N;
